@@ -1,0 +1,380 @@
+/*
+ * oracle.c -- CPU oracle for the PATCH hybrid tile-sparse GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark may load this file's library.  The product
+ * path (the HIP library and its Python binding) never calls it, and it shares
+ * no code, header, table or constant generator with that path.
+ *
+ * What it computes (sources: "PATCH: Learnable Tile-level Hybrid Sparsity for
+ * LLMs", arXiv 2509.23410; pages: the arXiv abstract, and the gist.science
+ * explainer, section "2. Methodology: PATCH"):
+ *
+ *   - A weight matrix W (N x K, row-major, N = output features, K = input
+ *     features) is partitioned into tiles of b1 x b2 (tile_n x tile_k).
+ *     (gist.science explainer, section 2, "Core Mechanism".)
+ *   - Each tile is either dense (keeps every weight) or 2:4 sparse (in every
+ *     group of four consecutive weights, two are kept).
+ *     (same section; section 1 "Problem Statement" defines the 2:4 rule.)
+ *   - At inference the tile choice is hard: the effective mask E is 1 in
+ *     dense tiles and the supplied 2:4 mask in sparse tiles.  The explainer
+ *     calls the mask a weighted combination of the dense and the 2:4 option;
+ *     with a hard 0/1 weight that combination is exactly this selection.
+ *   - The product is Y = X * (W o E)^T, X being M x K.
+ *
+ * Readings where the pages are silent (each is listed with its reason in the
+ * design notes of the repository):
+ *   - the groups of four run along K (the reduction dimension) inside a row;
+ *   - a tile-map byte != 0 marks a sparse tile; a mask byte != 0 marks "keep";
+ *   - the mask inside dense tiles is ignored and not validated;
+ *   - a sparse-tile group whose mask does not keep exactly two positions is an
+ *     error (ORACLE_ERR_MASK);
+ *   - kept values are stored bit-exactly (a kept -0.0 stays -0.0).
+ *
+ * Arithmetic: every product of two binary16/bfloat16 values is exact in
+ * binary64 (11x11 or 8x8 significand bits), and the sum runs over k in
+ * ascending order in binary64, so the result does not depend on the number
+ * of threads (OpenMP splits the work over output rows n only).
+ *
+ * The packed format is the repository's own (format version 1): the pages fix
+ * only the tile shape (128 x 128 execution tiles, gist.science explainer,
+ * section 4 "Ablation Studies"), the six 2:4 patterns (section 2, "Pattern
+ * Selection") and nothing about bytes.  oracle_pack() writes it from its
+ * written definition, restated next to the function.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <math.h>
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG 1
+#define ORACLE_ERR_SHAPE 2
+#define ORACLE_ERR_MASK 3
+#define ORACLE_ERR_SMALL 4
+
+#define ORACLE_F16 0
+#define ORACLE_BF16 1
+
+/* ---------------------------------------------------------------------------
+ * Element decoding, written from the IEEE 754-2008 binary16 definition and the
+ * bfloat16 definition (the upper 16 bits of an IEEE binary32).
+ * ------------------------------------------------------------------------- */
+double oracle_f16_to_double(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 0x1f;
+  int f = h & 0x3ff;
+  double v;
+  if (e == 0) {
+    v = ldexp((double)f, -24); /* subnormal: f * 2^-24 */
+  } else if (e == 31) {
+    v = f ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(1024 + f), e - 25); /* (1 + f/1024) * 2^(e-15) */
+  }
+  return sign ? -v : v;
+}
+
+double oracle_bf16_to_double(uint16_t b) {
+  int sign = (b >> 15) & 1;
+  int e = (b >> 7) & 0xff;
+  int f = b & 0x7f;
+  double v;
+  if (e == 0) {
+    v = ldexp((double)f, -133); /* subnormal: f * 2^-7 * 2^-126 */
+  } else if (e == 255) {
+    v = f ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(128 + f), e - 134); /* (1 + f/128) * 2^(e-127) */
+  }
+  return sign ? -v : v;
+}
+
+static double decode(uint16_t bits, int dtype) {
+  return dtype == ORACLE_F16 ? oracle_f16_to_double(bits) : oracle_bf16_to_double(bits);
+}
+
+/* Round a binary64 value to the nearest bfloat16 / binary16 (ties to even).
+ * Used only to measure the rounding floor of a 16-bit output. */
+static uint16_t round_to_bits(double v, int mant_bits, int emin, int emax, int ebias, int expbits) {
+  uint16_t sign = 0;
+  if (signbit(v)) { sign = 1; v = -v; }
+  uint16_t out;
+  if (isnan(v)) {
+    out = (uint16_t)(((1u << expbits) - 1) << mant_bits | (1u << (mant_bits - 1)));
+  } else if (isinf(v)) {
+    out = (uint16_t)(((1u << expbits) - 1) << mant_bits);
+  } else if (v == 0.0) {
+    out = 0;
+  } else {
+    int e;
+    frexp(v, &e); /* v = m * 2^e, m in [0.5, 1) -> unbiased exponent e-1 */
+    int ue = e - 1;
+    if (ue < emin) ue = emin; /* subnormal range shares the minimum exponent */
+    /* quantum = 2^(ue - mant_bits) */
+    double q = ldexp(1.0, ue - mant_bits);
+    double n = v / q;           /* exact: q is a power of two */
+    double r = nearbyint(n);    /* default rounding mode: to nearest, ties even */
+    double rv = r * q;
+    /* re-derive exponent after rounding (may carry into the next binade) */
+    if (rv == 0.0) {
+      out = 0; /* underflow to zero keeps the sign below */
+    } else if (rv >= ldexp(1.0, emax + 1)) {
+      out = (uint16_t)(((1u << expbits) - 1) << mant_bits);
+    } else {
+      int e2;
+      frexp(rv, &e2);
+      int ue2 = e2 - 1;
+      if (ue2 < emin) { /* subnormal */
+        uint32_t frac = (uint32_t)(rv / ldexp(1.0, emin - mant_bits));
+        out = (uint16_t)frac;
+      } else {
+        uint32_t frac = (uint32_t)(rv / ldexp(1.0, ue2 - mant_bits)) - (1u << mant_bits);
+        out = (uint16_t)(((uint32_t)(ue2 + ebias) << mant_bits) | frac);
+      }
+    }
+  }
+  return (uint16_t)(out | (sign << 15));
+}
+
+uint16_t oracle_double_to_bf16(double v) { return round_to_bits(v, 7, -126, 127, 127, 8); }
+uint16_t oracle_double_to_f16(double v) { return round_to_bits(v, 10, -14, 15, 15, 5); }
+
+/* ---------------------------------------------------------------------------
+ * Validation and the effective mask (gist.science explainer, section 2,
+ * "Core Mechanism" and "Hybrid Mask Generation").
+ * ------------------------------------------------------------------------- */
+static int check_shape(int64_t N, int64_t K, int64_t tn, int64_t tk) {
+  if (N <= 0 || K <= 0 || tn <= 0 || tk <= 0) return ORACLE_ERR_ARG;
+  if (N % tn != 0 || K % tk != 0 || tk % 4 != 0) return ORACLE_ERR_SHAPE;
+  return ORACLE_OK;
+}
+
+/* Returns ORACLE_ERR_MASK if a group of four inside a sparse tile does not
+ * keep exactly two positions; *bad_row / *bad_group receive the first one. */
+int oracle_validate(int64_t N, int64_t K, int64_t tn, int64_t tk, const uint8_t* tile_map,
+                    const uint8_t* mask, int64_t* bad_row, int64_t* bad_group) {
+  int rc = check_shape(N, K, tn, tk);
+  if (rc) return rc;
+  int64_t KT = K / tk;
+  for (int64_t n = 0; n < N; n++) {
+    for (int64_t g = 0; g < K / 4; g++) {
+      int64_t k0 = 4 * g;
+      if (!tile_map[(n / tn) * KT + k0 / tk]) continue; /* dense tile: mask not read */
+      int kept = 0;
+      for (int d = 0; d < 4; d++) kept += mask[n * K + k0 + d] != 0;
+      if (kept != 2) {
+        if (bad_row) *bad_row = n;
+        if (bad_group) *bad_group = g;
+        return ORACLE_ERR_MASK;
+      }
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* E[n][k] = 1 in dense tiles, (mask != 0) in sparse tiles. */
+int oracle_effective_mask(int64_t N, int64_t K, int64_t tn, int64_t tk, const uint8_t* tile_map,
+                          const uint8_t* mask, uint8_t* E) {
+  int rc = check_shape(N, K, tn, tk);
+  if (rc) return rc;
+  int64_t KT = K / tk;
+  for (int64_t n = 0; n < N; n++)
+    for (int64_t k = 0; k < K; k++) {
+      int sparse = tile_map[(n / tn) * KT + k / tk] != 0;
+      E[n * K + k] = sparse ? (mask[n * K + k] != 0) : 1;
+    }
+  return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * The GEMM: Y[m][n] = sum_k X[m][k] * W[n][k] * E[n][k], fp64, k ascending.
+ * X: M x K element bits, W: N x K element bits, Y: M x N doubles.
+ * ------------------------------------------------------------------------- */
+int oracle_gemm_f64(int dtype, int64_t M, int64_t N, int64_t K, int64_t tn, int64_t tk,
+                    const uint16_t* X, const uint16_t* W, const uint8_t* tile_map, const uint8_t* mask,
+                    double* Y) {
+  if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return ORACLE_ERR_ARG;
+  if (M < 0) return ORACLE_ERR_ARG;
+  int rc = oracle_validate(N, K, tn, tk, tile_map, mask, NULL, NULL);
+  if (rc) return rc;
+  if (M == 0) return ORACLE_OK;
+  int64_t KT = K / tk;
+  double* Xd = (double*)malloc(sizeof(double) * (size_t)(M * K));
+  if (!Xd) return ORACLE_ERR_ARG;
+  for (int64_t i = 0; i < M * K; i++) Xd[i] = decode(X[i], dtype);
+  int fail = 0;
+#pragma omp parallel
+  {
+    double* w = (double*)malloc(sizeof(double) * (size_t)K);
+    if (!w) {
+#pragma omp atomic write
+      fail = 1;
+    }
+#pragma omp for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+      if (!w) continue;
+      /* masked row: W_eff[n][k] = W[n][k] where kept, +0 elsewhere */
+      for (int64_t k = 0; k < K; k++) {
+        int sparse = tile_map[(n / tn) * KT + k / tk] != 0;
+        int keep = sparse ? (mask[n * K + k] != 0) : 1;
+        w[k] = keep ? decode(W[n * K + k], dtype) : 0.0;
+      }
+      for (int64_t m = 0; m < M; m++) {
+        const double* x = Xd + m * K;
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; k++) acc += x[k] * w[k];
+        Y[m * N + n] = acc;
+      }
+    }
+    free(w);
+  }
+  free(Xd);
+  return fail ? ORACLE_ERR_ARG : ORACLE_OK;
+}
+
+/* Round an fp64 result to the 16-bit output type (RNE) -- used to measure the
+ * error floor that any 16-bit output must carry. */
+void oracle_round_f64(int dtype, int64_t n, const double* in, uint16_t* out) {
+  for (int64_t i = 0; i < n; i++)
+    out[i] = dtype == ORACLE_F16 ? oracle_double_to_f16(in[i]) : oracle_double_to_bf16(in[i]);
+}
+
+/* ---------------------------------------------------------------------------
+ * Packed format, version 1 (the repository's own format; restated here).
+ *
+ * Tile edge b = 128 in both directions; NT = N/128, KT = K/128, T = NT*KT.
+ * Little-endian.  All bytes not written below are zero.
+ *
+ * Header, 256 bytes at offset 0:
+ *   u32 magic 0x48435450, u32 version 1, u32 dtype (0 f16, 1 bf16),
+ *   u32 tile_n 128, u32 tile_k 128, u32 N, u32 K, u32 NT, u32 KT,
+ *   u32 n_sparse, u64 table_offset (= 256), u64 data_offset,
+ *   u64 data_bytes, u64 total_bytes.
+ * Tile table at 256: T entries of 16 bytes, tile (i, j) at index i*KT + j:
+ *   u64 byte offset of the tile's data from the start of the blob,
+ *   u32 kind (0 dense, 1 sparse), u32 zero.
+ * Data at data_offset = round_up(256 + 16*T, 256): tiles in table order,
+ * back to back; a dense tile takes 32768 bytes, a sparse one 18432 bytes.
+ *
+ * Inside a tile, a "band" is 16 consecutive rows (b = 0..7) and a "lane" is
+ * a number l = 0..63 with row-in-band r = l mod 16 and column group h = l / 16.
+ *
+ * Dense tile: 4 slices q of 32 columns; chunk (q, band, l) holds the 8
+ *   elements of row 16*band + (l mod 16), columns 32*q + 8*(l/16) + t for
+ *   t = 0..7, in that order.  Chunk index = (q*8 + band)*64 + l, 16 bytes each.
+ * Sparse tile: groups of four columns g = 0..31 (columns 4g..4g+3).
+ *   Values: 2 slices q of 16 groups; chunk (q, band, l) holds, for
+ *   p = 0..3 and group g = 16*q + 4*(l/16) + p, the two kept elements of row
+ *   16*band + (l mod 16) in ascending column order -- 8 elements, 16 bytes.
+ *   Chunk index = (q*8 + band)*64 + l; 16384 bytes in all.
+ *   Metadata, 2048 bytes after the values: a u32 per (band, l) at
+ *   index band*64 + l.  Bits 16*q + 4*p .. +3 hold the code of group
+ *   g = 16*q + 4*(l/16) + p of that row; code = i0 | (i1 << 2), i0 < i1 the
+ *   positions (0..3) of the two kept elements inside the group.
+ * ------------------------------------------------------------------------- */
+#define PT_B 128
+#define PT_DENSE_BYTES 32768u
+#define PT_SPARSE_BYTES 18432u
+
+static uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+uint64_t oracle_packed_bytes(int64_t N, int64_t K, const uint8_t* tile_map) {
+  if (N <= 0 || K <= 0 || N % PT_B || K % PT_B) return 0;
+  int64_t T = (N / PT_B) * (K / PT_B);
+  uint64_t ns = 0;
+  for (int64_t t = 0; t < T; t++) ns += tile_map[t] != 0;
+  return round_up(256 + 16 * (uint64_t)T, 256) + PT_DENSE_BYTES * (uint64_t)(T - (int64_t)ns) +
+         PT_SPARSE_BYTES * ns;
+}
+
+static void put32(uint8_t* p, uint32_t v) {
+  for (int i = 0; i < 4; i++) p[i] = (uint8_t)(v >> (8 * i));
+}
+static void put64(uint8_t* p, uint64_t v) {
+  for (int i = 0; i < 8; i++) p[i] = (uint8_t)(v >> (8 * i));
+}
+static void put16(uint8_t* p, uint16_t v) {
+  p[0] = (uint8_t)v;
+  p[1] = (uint8_t)(v >> 8);
+}
+
+int oracle_pack(int dtype, int64_t N, int64_t K, const uint16_t* W, const uint8_t* tile_map,
+                const uint8_t* mask, uint8_t* out, uint64_t out_bytes) {
+  if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return ORACLE_ERR_ARG;
+  if (N <= 0 || K <= 0) return ORACLE_ERR_ARG;
+  if (N % PT_B || K % PT_B) return ORACLE_ERR_SHAPE;
+  int rc = oracle_validate(N, K, PT_B, PT_B, tile_map, mask, NULL, NULL);
+  if (rc) return rc;
+  uint64_t total = oracle_packed_bytes(N, K, tile_map);
+  if (out_bytes < total) return ORACLE_ERR_SMALL;
+  memset(out, 0, (size_t)total);
+  int64_t NT = N / PT_B, KT = K / PT_B, T = NT * KT;
+  uint32_t ns = 0;
+  for (int64_t t = 0; t < T; t++) ns += tile_map[t] != 0;
+  uint64_t data_off = round_up(256 + 16 * (uint64_t)T, 256);
+  put32(out + 0, 0x48435450u);
+  put32(out + 4, 1);
+  put32(out + 8, (uint32_t)dtype);
+  put32(out + 12, PT_B);
+  put32(out + 16, PT_B);
+  put32(out + 20, (uint32_t)N);
+  put32(out + 24, (uint32_t)K);
+  put32(out + 28, (uint32_t)NT);
+  put32(out + 32, (uint32_t)KT);
+  put32(out + 36, ns);
+  put64(out + 40, 256);
+  put64(out + 48, data_off);
+  put64(out + 56, total - data_off);
+  put64(out + 64, total);
+
+  uint64_t off = data_off;
+  for (int64_t i = 0; i < NT; i++) {
+    for (int64_t j = 0; j < KT; j++) {
+      int64_t t = i * KT + j;
+      int sparse = tile_map[t] != 0;
+      put64(out + 256 + 16 * t, off);
+      put32(out + 256 + 16 * t + 8, (uint32_t)sparse);
+      uint8_t* tile = out + off;
+      if (!sparse) {
+        for (int q = 0; q < 4; q++)
+          for (int band = 0; band < 8; band++)
+            for (int l = 0; l < 64; l++)
+              for (int e = 0; e < 8; e++) {
+                int64_t row = i * PT_B + 16 * band + (l % 16);
+                int64_t col = j * PT_B + 32 * q + 8 * (l / 16) + e;
+                int64_t chunk = ((int64_t)q * 8 + band) * 64 + l;
+                put16(tile + 16 * chunk + 2 * e, W[row * K + col]);
+              }
+        off += PT_DENSE_BYTES;
+      } else {
+        for (int q = 0; q < 2; q++)
+          for (int band = 0; band < 8; band++)
+            for (int l = 0; l < 64; l++) {
+              int64_t row = i * PT_B + 16 * band + (l % 16);
+              int64_t chunk = ((int64_t)q * 8 + band) * 64 + l;
+              for (int p = 0; p < 4; p++) {
+                int g = 16 * q + 4 * (l / 16) + p;
+                int64_t c0 = j * PT_B + 4 * g;
+                int s = 0;
+                int pos[2] = {0, 0};
+                for (int d = 0; d < 4; d++)
+                  if (mask[row * K + c0 + d]) {
+                    put16(tile + 16 * chunk + 2 * (2 * p + s), W[row * K + c0 + d]);
+                    pos[s] = d;
+                    s++;
+                  }
+                uint32_t code = (uint32_t)pos[0] | ((uint32_t)pos[1] << 2);
+                uint8_t* meta = tile + 16384 + 4 * (band * 64 + l);
+                uint32_t word = (uint32_t)meta[0] | ((uint32_t)meta[1] << 8) | ((uint32_t)meta[2] << 16) |
+                                ((uint32_t)meta[3] << 24);
+                word |= code << (16 * q + 4 * p);
+                put32(meta, word);
+              }
+            }
+        off += PT_SPARSE_BYTES;
+      }
+    }
+  }
+  return ORACLE_OK;
+}

@@ -1,0 +1,156 @@
+"""ctypes marshalling for the C oracle (test infrastructure only)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+F16, BF16 = 0, 1
+_DT = {"f16": F16, "bf16": BF16, F16: F16, BF16: BF16}
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_ERRS = {1: "invalid argument", 2: "shape not a multiple of the tile", 3: "mask: a sparse group does not keep exactly 2",
+         4: "buffer too small"}
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code: int):
+        super().__init__(f"oracle error {code}: {_ERRS.get(code, '?')}")
+        self.code = code
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (plain C, OpenMP, IEEE arithmetic)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+                               "-Wall", "-Wextra", "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    lib.oracle_f16_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_f16_to_double.restype = ctypes.c_double
+    lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_double.restype = ctypes.c_double
+    lib.oracle_validate.argtypes = [I64, I64, I64, I64, P, P, P, P]
+    lib.oracle_validate.restype = ctypes.c_int
+    lib.oracle_effective_mask.argtypes = [I64, I64, I64, I64, P, P, P]
+    lib.oracle_effective_mask.restype = ctypes.c_int
+    lib.oracle_gemm_f64.argtypes = [ctypes.c_int, I64, I64, I64, I64, I64, P, P, P, P, P]
+    lib.oracle_gemm_f64.restype = ctypes.c_int
+    lib.oracle_round_f64.argtypes = [ctypes.c_int, I64, P, P]
+    lib.oracle_round_f64.restype = None
+    lib.oracle_packed_bytes.argtypes = [I64, I64, P]
+    lib.oracle_packed_bytes.restype = ctypes.c_uint64
+    lib.oracle_pack.argtypes = [ctypes.c_int, I64, I64, P, P, P, P, ctypes.c_uint64]
+    lib.oracle_pack.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u16(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.uint16)
+
+
+def _u8(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.uint8)
+
+
+def f16_to_double(bits: int) -> float:
+    return load().oracle_f16_to_double(int(bits))
+
+
+def bf16_to_double(bits: int) -> float:
+    return load().oracle_bf16_to_double(int(bits))
+
+
+def validate(N, K, tile_map, mask, tile_n=128, tile_k=128):
+    """Returns None if valid, else (row, group) of the first bad sparse group."""
+    lib = load()
+    tm, mk = _u8(tile_map), _u8(mask)
+    r = ctypes.c_int64(-1)
+    g = ctypes.c_int64(-1)
+    rc = lib.oracle_validate(N, K, tile_n, tile_k, _p(tm), _p(mk), ctypes.byref(r), ctypes.byref(g))
+    if rc == 3:
+        return (r.value, g.value)
+    if rc:
+        raise OracleError(rc)
+    return None
+
+
+def effective_mask(N, K, tile_map, mask, tile_n=128, tile_k=128) -> np.ndarray:
+    lib = load()
+    tm, mk = _u8(tile_map), _u8(mask)
+    E = np.zeros((N, K), dtype=np.uint8)
+    rc = lib.oracle_effective_mask(N, K, tile_n, tile_k, _p(tm), _p(mk), _p(E))
+    if rc:
+        raise OracleError(rc)
+    return E
+
+
+def gemm_f64(dtype, X, W, tile_map, mask, tile_n=128, tile_k=128) -> np.ndarray:
+    """Y = X (W o E)^T in fp64; X (M, K) and W (N, K) are 16-bit patterns."""
+    lib = load()
+    X, W = _u16(X), _u16(W)
+    M, K = X.shape
+    N, K2 = W.shape
+    if K != K2:
+        raise ValueError("K mismatch")
+    tm, mk = _u8(tile_map), _u8(mask)
+    Y = np.zeros((M, N), dtype=np.float64)
+    rc = lib.oracle_gemm_f64(_DT[dtype], M, N, K, tile_n, tile_k, _p(X), _p(W), _p(tm), _p(mk), _p(Y))
+    if rc:
+        raise OracleError(rc)
+    return Y
+
+
+def round_f64(dtype, Y: np.ndarray) -> np.ndarray:
+    """fp64 -> 16-bit patterns with round-to-nearest-even."""
+    lib = load()
+    Y = np.ascontiguousarray(Y, dtype=np.float64)
+    out = np.zeros(Y.shape, dtype=np.uint16)
+    lib.oracle_round_f64(_DT[dtype], Y.size, _p(Y), _p(out))
+    return out
+
+
+def packed_bytes(N, K, tile_map) -> int:
+    return int(load().oracle_packed_bytes(N, K, _p(_u8(tile_map))))
+
+
+def pack(dtype, W, tile_map, mask) -> np.ndarray:
+    """The format-1 blob as a uint8 array."""
+    lib = load()
+    W = _u16(W)
+    N, K = W.shape
+    tm, mk = _u8(tile_map), _u8(mask)
+    nbytes = lib.oracle_packed_bytes(N, K, _p(tm))
+    if nbytes == 0:
+        raise OracleError(2)
+    out = np.zeros(nbytes, dtype=np.uint8)
+    rc = lib.oracle_pack(_DT[dtype], N, K, _p(W), _p(tm), _p(mk), _p(out), nbytes)
+    if rc:
+        raise OracleError(rc)
+    return out

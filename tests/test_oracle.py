@@ -1,0 +1,360 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself.
+
+Each test names what pins it: a library routine or textbook special case, an
+exact invariant stated by the pages, brute force on tiny inputs, or a
+hand-worked example of the byte format.  Page citations refer to PATCH
+(arXiv 2509.23410): the arXiv abstract, and the gist.science explainer
+sections "1. Problem Statement", "2. Methodology: PATCH" and
+"4. Experimental Results".
+"""
+import itertools
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from sparse_gemm_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- element codecs
+def test_f16_decode_all_patterns_match_numpy():
+    """binary16 decoding: every one of the 65536 patterns against numpy's
+    float16 -> float64 conversion (library routine)."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.f16_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_bf16_decode_all_patterns_match_torch():
+    """bfloat16 decoding: all 65536 patterns against torch's bfloat16 -> float64."""
+    import torch
+
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([oracle.bf16_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_round_to_f16_matches_numpy_rne():
+    """fp64 -> binary16 rounding against numpy (direct RNE), with exact ties."""
+    rng = np.random.default_rng(1)
+    v = np.concatenate([
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-8, 6, 20000),
+        # exact halfway cases between adjacent binary16 values
+        (np.arange(1, 4000, dtype=np.float64) + 0.5) * 2.0 ** -10,
+        (np.arange(1, 400, dtype=np.float64) + 0.5) * 2.0 ** -24,  # subnormal ties
+        np.array([65504.0, 65519.99, 65520.0, -65520.0, 0.0, -0.0, 1e-9, -1e-9]),
+    ])
+    with np.errstate(over="ignore"):
+        ref = v.astype(np.float16).view(np.uint16)
+    got = oracle.round_f64("f16", v)
+    assert np.array_equal(got, ref)
+
+
+def test_round_to_bf16_matches_torch_rne():
+    """fp64 -> bfloat16 rounding against torch's float32 -> bfloat16 (RNE), on
+    values exactly representable in float32 so torch's route is exact."""
+    import torch
+
+    rng = np.random.default_rng(2)
+    f32 = (rng.standard_normal(50000) * 10.0 ** rng.integers(-30, 30, 50000)).astype(np.float32)
+    ties = ((rng.integers(0, 1 << 16, 5000).astype(np.uint32) << 16) | 0x8000).view(np.float32)
+    ties = ties[np.isfinite(ties)]
+    f32 = np.concatenate([f32, ties, np.array([3.3895314e38, -3.3895314e38, 0.0, -0.0], np.float32)])
+    ref = torch.from_numpy(f32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.round_f64("bf16", f32.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+# ---------------------------------------------------------------- effective mask
+def _problem(N, K, kind, frac, dtype="bf16", seed=0, mask="top2"):
+    return inputs.make_custom(dtype, N, K, seed, kind, frac, mask)
+
+
+def test_effective_mask_two_of_four_in_sparse_tiles_one_in_dense():
+    """S2: in a 2:4 tile every group of four keeps exactly two (explainer
+    section 1, '2:4 ... two non-zero values per four elements'); a dense tile
+    keeps everything (section 2, 'remain dense (0% sparsity)')."""
+    p = _problem(512, 384, "bernoulli", 0.5, seed=3)
+    E = oracle.effective_mask(p.N, p.K, p.tile_map, p.mask)
+    tm = np.repeat(np.repeat(p.tile_map, 128, 0), 128, 1).astype(bool)
+    groups = E.reshape(p.N, p.K // 4, 4).sum(-1)
+    gsparse = tm.reshape(p.N, p.K // 4, 4)[..., 0]
+    assert np.all(groups[gsparse] == 2)
+    assert np.all(E[~tm] == 1)
+    assert 0 < p.tile_map.sum() < p.tile_map.size
+
+
+@pytest.mark.parametrize("frac", [0.0, 0.25, 0.5, 0.75, 1.0])
+def test_sparsity_is_half_the_sparse_tile_fraction(frac):
+    """S3: overall sparsity = 0.5 x (fraction of sparse tiles), exactly, which
+    spans 0%..50% (abstract: 'continuous sparsity ratio between 0% and 50%')."""
+    p = _problem(512, 512, "exact", frac, seed=4)
+    E = oracle.effective_mask(p.N, p.K, p.tile_map, p.mask)
+    zeros = int((E == 0).sum())
+    T = p.tile_map.size
+    n_sparse = int(p.tile_map.sum())
+    assert n_sparse == int(np.round(frac * T))
+    # zeros / (N K) == 0.5 * n_sparse / T, compared as exact rationals
+    assert zeros * 2 * T == n_sparse * p.N * p.K
+
+
+def test_mask_in_dense_tiles_is_ignored_and_not_validated():
+    p = _problem(256, 256, "exact", 0.5, seed=5)
+    mask = p.mask.copy()
+    dense_i, dense_j = np.argwhere(p.tile_map == 0)[0]
+    mask[dense_i * 128:(dense_i + 1) * 128, dense_j * 128:(dense_j + 1) * 128] = 0  # illegal, but dense
+    assert oracle.validate(p.N, p.K, p.tile_map, mask) is None
+    X = inputs.make_custom_x("bf16", 8, 256, 1)
+    assert np.array_equal(oracle.gemm_f64("bf16", X, p.w, p.tile_map, mask),
+                          oracle.gemm_f64("bf16", X, p.w, p.tile_map, p.mask))
+
+
+@pytest.mark.parametrize("keep", [(0,), (0, 1, 2), (), (0, 1, 2, 3)])
+def test_illegal_sparse_group_is_rejected(keep):
+    p = _problem(256, 256, "sparse", 1.0, seed=6)
+    mask = p.mask.copy()
+    mask[37, 4 * 9:4 * 9 + 4] = 0
+    for d in keep:
+        mask[37, 4 * 9 + d] = 1
+    assert oracle.validate(p.N, p.K, p.tile_map, mask) == (37, 9)
+    with pytest.raises(oracle.OracleError):
+        oracle.gemm_f64("bf16", np.zeros((1, 256), np.uint16), p.w, p.tile_map, mask)
+    with pytest.raises(oracle.OracleError):
+        oracle.pack("bf16", p.w, p.tile_map, mask)
+
+
+# ---------------------------------------------------------------- the GEMM
+def test_all_dense_map_equals_numpy_matmul():
+    """S1: with an all-dense tile map the method is a plain GEMM; against
+    numpy.matmul in float64 (library routine) to 1e-12 relative."""
+    for dtype in ("bf16", "f16"):
+        p = _problem(256, 384, "dense", 0.0, dtype=dtype, seed=7)
+        X = inputs.make_custom_x(dtype, 33, 384, 2)
+        Y = oracle.gemm_f64(dtype, X, p.w, p.tile_map, p.mask)
+        Xf = inputs.bits_to_f32(X, dtype).astype(np.float64)
+        Wf = inputs.bits_to_f32(p.w, dtype).astype(np.float64)
+        ref = Xf @ Wf.T
+        np.testing.assert_allclose(Y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_all_sparse_map_equals_numpy_matmul_of_masked_weights():
+    """Uniform 2:4 special case: every tile sparse, so Y = X (W o mask)^T with
+    the mask applied by numpy (library matmul of the masked matrix)."""
+    p = _problem(256, 256, "sparse", 1.0, seed=8, mask="uniform")
+    X = inputs.make_custom_x("bf16", 16, 256, 3)
+    Y = oracle.gemm_f64("bf16", X, p.w, p.tile_map, p.mask)
+    Wf = inputs.bits_to_f32(p.w, "bf16").astype(np.float64) * (p.mask != 0)
+    ref = inputs.bits_to_f32(X, "bf16").astype(np.float64) @ Wf.T
+    np.testing.assert_allclose(Y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def _int_bits(vals, dtype):
+    return inputs.to_bits(np.asarray(vals, dtype=np.float64), dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_brute_force_8x8_all_tile_maps(dtype):
+    """S4: 8 x 8 weights with 4 x 4 tiles (the pages' finest tile, section 4
+    'Tile Size'), all 16 tile maps, integer-valued X and W in -3..3.  A second
+    formulation sums only over the two kept positions of each group, read from
+    the six-pattern table, and must agree exactly."""
+    rng = np.random.default_rng(11)
+    M, N, K = 5, 8, 8
+    Xi = rng.integers(-3, 4, (M, K))
+    Wi = rng.integers(-3, 4, (N, K))
+    X, W = _int_bits(Xi, dtype), _int_bits(Wi, dtype)
+    pats = rng.integers(0, 6, (N, K // 4))
+    mask = np.zeros((N, K), np.uint8)
+    for n in range(N):
+        for g in range(K // 4):
+            for d in inputs.PATTERNS[pats[n, g]]:
+                mask[n, 4 * g + d] = 1
+    for bitsmap in range(16):
+        tmap = np.array([(bitsmap >> b) & 1 for b in range(4)], np.uint8).reshape(2, 2)
+        Y = oracle.gemm_f64(dtype, X, W, tmap, mask, tile_n=4, tile_k=4)
+        ref = np.zeros((M, N), dtype=np.int64)
+        for m in range(M):
+            for n in range(N):
+                s = 0
+                for g in range(K // 4):
+                    if tmap[n // 4, (4 * g) // 4]:
+                        for d in inputs.PATTERNS[pats[n, g]]:
+                            s += Xi[m, 4 * g + d] * Wi[n, 4 * g + d]
+                    else:
+                        for d in range(4):
+                            s += Xi[m, 4 * g + d] * Wi[n, 4 * g + d]
+                ref[m, n] = s
+        assert np.array_equal(Y, ref.astype(np.float64)), bitsmap
+
+
+def test_identity_x_recovers_masked_weights():
+    """With X = identity rows, Y^T is W o E exactly (one product per output)."""
+    p = _problem(256, 256, "bernoulli", 0.5, seed=9)
+    X = inputs.to_bits(np.eye(256), "bf16")
+    Y = oracle.gemm_f64("bf16", X, p.w, p.tile_map, p.mask)
+    E = oracle.effective_mask(p.N, p.K, p.tile_map, p.mask)
+    Wf = inputs.bits_to_f32(p.w, "bf16").astype(np.float64) * E
+    assert np.array_equal(Y.T, Wf)
+
+
+def test_six_patterns_each_select_their_columns():
+    """Each of the six 2:4 patterns (section 2 'Pattern Selection') keeps its two
+    columns: with W = 1 and X = one-hot columns, Y reads back the pattern."""
+    for pi, (a, b) in enumerate(inputs.PATTERNS):
+        N = K = 128
+        W = inputs.to_bits(np.ones((N, K)), "bf16")
+        mask = np.zeros((N, K), np.uint8)
+        mask[:, a::4] = 1
+        mask[:, b::4] = 1
+        X = inputs.to_bits(np.eye(K)[:4], "bf16")
+        Y = oracle.gemm_f64("bf16", X, W, np.ones((1, 1), np.uint8), mask)
+        expect = np.zeros((4, N))
+        expect[a] = 1
+        expect[b] = 1
+        assert np.array_equal(Y, expect), pi
+
+
+def test_oracle_result_independent_of_thread_count():
+    import subprocess
+    import sys
+    code = ("import numpy as np, oracle; from sparse_gemm_amd import inputs;"
+            "p = inputs.make_custom('bf16', 384, 256, 1, 'bernoulli', 0.5, 'top2');"
+            "X = inputs.make_custom_x('bf16', 7, 256, 1);"
+            "print(oracle.gemm_f64('bf16', X, p.w, p.tile_map, p.mask).tobytes().hex()[:4000])")
+    outs = []
+    for t in ("1", "5"):
+        env = dict(os.environ, OMP_NUM_THREADS=t)
+        outs.append(subprocess.check_output([sys.executable, "-c", code], env=env,
+                                            cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__)))))
+    assert outs[0] == outs[1]
+
+
+# ---------------------------------------------------------------- packed format
+def _golden(name):
+    kv = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, v = line.split()
+            kv[k] = int(v, 0)
+    return kv
+
+
+def test_pack_hand_worked_example():
+    g = _golden("pack_format_example.txt")
+    N, K = 128, 256
+    W = np.full((N, K), 0x3F80, np.uint16)
+    W[g["dense.row"], g["dense.col"]] = g["dense.bits"]
+    W[g["sparse.row"], g["sparse.col"]] = g["sparse.bits"]
+    mask = np.zeros((N, K), np.uint8)
+    mask[:, 0::4] = 1
+    mask[:, 1::4] = 1
+    r, c = g["sparse.row"], g["sparse.col"]
+    g0 = c - c % 4
+    mask[r, g0:g0 + 4] = [1, 0, 1, 0]
+    tmap = np.array([[0, 1]], np.uint8)
+    blob = oracle.pack("bf16", W, tmap, mask)
+    u64 = lambda o: int.from_bytes(blob[o:o + 8].tobytes(), "little")
+    u32 = lambda o: int.from_bytes(blob[o:o + 4].tobytes(), "little")
+    u16 = lambda o: int.from_bytes(blob[o:o + 2].tobytes(), "little")
+    assert blob.size == g["header.total_bytes"]
+    assert u32(0) == 0x48435450 and u32(4) == 1 and u32(8) == 1
+    assert (u32(12), u32(16), u32(20), u32(24), u32(28), u32(32)) == (128, 128, N, K, 1, 2)
+    assert u32(36) == g["header.n_sparse"]
+    assert u64(40) == 256 and u64(48) == g["header.data_offset"] and u64(64) == g["header.total_bytes"]
+    assert u64(56) == g["header.total_bytes"] - g["header.data_offset"]
+    assert u64(256) == g["table.0.offset"] and u32(264) == g["table.0.kind"]
+    assert u64(272) == g["table.1.offset"] and u32(280) == g["table.1.kind"]
+    assert u16(g["dense.byte_offset"]) == g["dense.bits"]
+    assert u16(g["sparse.byte_offset"]) == g["sparse.bits"]
+    assert blob[g["sparse.meta_byte_offset"]] == g["sparse.meta_byte_value"]
+    # every other metadata nibble of the sparse tile is code 4 (keeps 0 and 1)
+    meta = blob[g["table.1.offset"] + 16384:g["table.1.offset"] + 18432]
+    nib = np.stack([meta & 15, meta >> 4], -1).ravel()
+    assert (nib == 4).sum() == nib.size - 1 and (nib == 8).sum() == 1
+
+
+def test_packed_size_closed_form():
+    for frac in (0.0, 0.3, 1.0):
+        p = _problem(384, 640, "exact", frac, seed=12)
+        T = p.tile_map.size
+        ns = int(p.tile_map.sum())
+        expect = -(-(256 + 16 * T) // 256) * 256 + 32768 * (T - ns) + 18432 * ns
+        assert oracle.packed_bytes(p.N, p.K, p.tile_map) == expect
+        assert oracle.pack("bf16", p.w, p.tile_map, p.mask).size == expect
+
+
+def _unpack(blob, N, K):
+    """Independent reader of the format (written from the format definition)."""
+    NT, KT = N // 128, K // 128
+    W = np.zeros((N, K), np.uint16)
+    codes = []
+    for i in range(NT):
+        for j in range(KT):
+            e = 256 + 16 * (i * KT + j)
+            off = int.from_bytes(blob[e:e + 8].tobytes(), "little")
+            kind = int.from_bytes(blob[e + 8:e + 12].tobytes(), "little")
+            tile = blob[off:off + (32768 if kind == 0 else 18432)]
+            if kind == 0:
+                ch = tile.view(np.uint16).reshape(4, 8, 64, 8)  # q, band, lane, e
+                for q in range(4):
+                    for band in range(8):
+                        for l in range(64):
+                            r = i * 128 + band * 16 + l % 16
+                            c = j * 128 + 32 * q + 8 * (l // 16)
+                            W[r, c:c + 8] = ch[q, band, l]
+            else:
+                vals = tile[:16384].view(np.uint16).reshape(2, 8, 64, 8)
+                meta = tile[16384:].view(np.uint32).reshape(8, 64)
+                for q in range(2):
+                    for band in range(8):
+                        for l in range(64):
+                            r = i * 128 + band * 16 + l % 16
+                            for p in range(4):
+                                g = 16 * q + 4 * (l // 16) + p
+                                code = (int(meta[band, l]) >> (16 * q + 4 * p)) & 15
+                                codes.append(code)
+                                i0, i1 = code & 3, code >> 2
+                                W[r, j * 128 + 4 * g + i0] = vals[q, band, l, 2 * p]
+                                W[r, j * 128 + 4 * g + i1] = vals[q, band, l, 2 * p + 1]
+    return W, np.array(codes)
+
+
+@pytest.mark.parametrize("mask_kind", ["top2", "uniform"])
+def test_pack_round_trip_and_legal_codes(mask_kind):
+    """unpack(pack(W)) == W o E bit-exactly; every code is one of the six
+    patterns i0 | i1 << 2 with i0 < i1: {4, 8, 12, 9, 13, 14}."""
+    p = _problem(256, 384, "bernoulli", 0.5, seed=13, mask=mask_kind)
+    blob = oracle.pack("bf16", p.w, p.tile_map, p.mask)
+    W2, codes = _unpack(blob, p.N, p.K)
+    E = oracle.effective_mask(p.N, p.K, p.tile_map, p.mask)
+    assert np.array_equal(W2, np.where(E != 0, p.w, 0).astype(np.uint16))
+    assert set(np.unique(codes)) <= {4, 8, 12, 9, 13, 14}
+    if mask_kind == "uniform":
+        assert set(np.unique(codes)) == {4, 8, 12, 9, 13, 14}
+
+
+def test_pack_keeps_negative_zero_bits():
+    N = K = 128
+    W = np.full((N, K), 0x8000, np.uint16)  # -0.0 everywhere
+    mask = np.zeros((N, K), np.uint8)
+    mask[:, 1::4] = 1
+    mask[:, 3::4] = 1
+    blob = oracle.pack("bf16", W, np.ones((1, 1), np.uint8), mask)
+    vals = blob[512:512 + 16384].view(np.uint16)
+    assert np.all(vals == 0x8000)
+    meta = blob[512 + 16384:512 + 18432]
+    assert np.all(meta == (13 | (13 << 4)))  # code (1,3) = 1 | 3 << 2 = 13
