@@ -1,0 +1,164 @@
+/*
+ * patch.h -- C ABI of the MI355X (gfx950) hybrid tile-sparse GEMM library.
+ *
+ * The method: PATCH, "Learnable Tile-level Hybrid Sparsity for LLMs"
+ * (arXiv 2509.23410).  A weight matrix W (N x K) is cut into tiles; every
+ * tile is either dense or 2:4 sparse (two kept weights in every four
+ * consecutive ones), which gives an overall sparsity anywhere between 0% and
+ * 50% (arXiv abstract; gist.science explainer, section 2 "Methodology:
+ * PATCH", "Core Mechanism").  Dense tiles run on dense matrix units and 2:4
+ * tiles on the sparse matrix path (same explainer, "Inference &
+ * Deployment"); execution tiles are 128 x 128 (section 4, "Ablation
+ * Studies").  This library computes Y = X * (W o E)^T on one GPU, with E the
+ * effective mask: 1 inside dense tiles, the 2:4 mask inside sparse tiles.
+ *
+ * Conventions for every entry point:
+ *   - Matrices are row-major with the last index contiguous: W is N x K
+ *     (output features x input features, the layout of a linear layer's
+ *     weight), X is M x K, Y is M x N.  Elements are IEEE binary16 (PATCH_F16)
+ *     or bfloat16 (PATCH_BF16); Y may also be binary32 (PATCH_F32).
+ *   - "_dev" pointers are device memory on the current HIP device, owned by
+ *     the caller, 16-byte aligned.  "_host" pointers are host memory.  The
+ *     library allocates no device memory and keeps no pointer after return.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     GEMM calls are asynchronous on that stream; patch_pack synchronises it.
+ *   - Errors are returned as patch_status; nothing is thrown.  On an error
+ *     found on the host nothing is launched and no output is written.
+ *     patch_last_error() returns a thread-local description of the last
+ *     failure on the calling thread.
+ *   - N and K must be positive multiples of 128 (else PATCH_ERR_SHAPE).
+ *     M >= 0; M == 0 is a no-op returning PATCH_OK.
+ */
+#ifndef PATCH_H
+#define PATCH_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PATCH_OK = 0,
+  PATCH_ERR_INVALID_ARG = 1,      /* null/unaligned pointer, bad dtype, M < 0, bad descriptor */
+  PATCH_ERR_SHAPE = 2,            /* N or K not a positive multiple of 128, or too large */
+  PATCH_ERR_MASK = 3,             /* a group of four inside a sparse tile does not keep exactly 2 */
+  PATCH_ERR_BUFFER_TOO_SMALL = 4, /* packed buffer or workspace smaller than required */
+  PATCH_ERR_UNSUPPORTED = 5,      /* valid request this build does not implement */
+  PATCH_ERR_HIP = 6               /* a HIP runtime call failed; see patch_last_error() */
+} patch_status;
+
+typedef enum { PATCH_F16 = 0, PATCH_BF16 = 1, PATCH_F32 = 2 } patch_dtype;
+
+/* GEMM variant selection for patch_gemm_ex (patch_gemm uses PATCH_VARIANT_AUTO). */
+typedef enum {
+  PATCH_VARIANT_AUTO = 0,    /* decode for M <= 16, prefill otherwise */
+  PATCH_VARIANT_DECODE = 1,  /* W-streaming kernel; valid for 1 <= M <= 16 */
+  PATCH_VARIANT_PREFILL = 2  /* output-tiled MFMA kernel; any M >= 1 */
+} patch_variant;
+
+/* Host-side mirror of the packed blob's header (format version 1). */
+typedef struct {
+  uint32_t version;   /* 1 */
+  uint32_t dtype;     /* PATCH_F16 or PATCH_BF16 */
+  uint32_t tile_n;    /* 128 */
+  uint32_t tile_k;    /* 128 */
+  uint32_t N, K;      /* matrix shape */
+  uint32_t nt_n;      /* N / 128 */
+  uint32_t nt_k;      /* K / 128 */
+  uint32_t n_sparse;  /* number of 2:4 tiles */
+  uint64_t table_offset; /* 256 */
+  uint64_t data_offset;  /* round_up(256 + 16 * nt_n * nt_k, 256) */
+  uint64_t total_bytes;  /* size of the whole blob */
+} patch_packed_desc;
+
+/* ABI version of this header (incremented on any incompatible change). */
+int32_t patch_abi_version(void);
+
+/*
+ * Size in bytes of the packed blob for a tile map (PATCH "tile-level
+ * assignment", gist.science explainer, section 2 "Core Mechanism"):
+ *   round_up(256 + 16*T, 256) + 32768 * n_dense + 18432 * n_sparse,
+ * T = (N/128)*(K/128).  tile_map_host: T bytes, row-block-major (tile (i, j)
+ * at i*(K/128) + j), nonzero = 2:4 sparse.  Returns 0 if the arguments are
+ * invalid (dtype, shape, null map).
+ */
+uint64_t patch_packed_bytes(patch_dtype dtype, int64_t N, int64_t K, const uint8_t* tile_map_host);
+
+/*
+ * Pack dense W plus a tile map and a 2:4 mask into the blob (format
+ * version 1): a 256-byte header, a 16-byte-per-tile table (data offset, kind)
+ * and the tile data.  A dense tile keeps its 128 x 128 values; a sparse tile
+ * keeps, for every group of four consecutive weights along K, the two kept
+ * values plus a 4-bit code i0 | i1 << 2 (2 bits per kept value), laid out in
+ * the order the sparse matrix instructions consume them.  The 2:4 rule:
+ * gist.science explainer, section 1 "Problem Statement"; the six patterns:
+ * section 2 "Pattern Selection".
+ *
+ *   W_dev          N x K elements of `dtype`, row-major, device.
+ *   tile_map_host  T bytes on the host, nonzero = sparse tile.
+ *   mask_dev       N x K bytes on the device, nonzero = keep.  Read only
+ *                  inside sparse tiles (ignored in dense tiles).
+ *   packed_dev     output, device, at least patch_packed_bytes() bytes.
+ *   desc_out       host descriptor of the result (written on success only).
+ *
+ * Synchronises `stream` (to report PATCH_ERR_MASK).  On PATCH_ERR_MASK the
+ * blob contents are undefined.  The blob is immutable afterwards and may be
+ * shared by any number of concurrent GEMM calls.
+ */
+patch_status patch_pack(patch_dtype dtype, int64_t N, int64_t K, const void* W_dev, const uint8_t* tile_map_host,
+                        const uint8_t* mask_dev, void* packed_dev, uint64_t packed_bytes,
+                        patch_packed_desc* desc_out, void* stream);
+
+/* Parse a blob header already copied to the host (for reloading a saved blob).
+ * Checks magic, version, dtype, tile shape and that the sizes agree. */
+patch_status patch_desc_from_header(const void* header_host, uint64_t header_bytes, patch_packed_desc* desc_out);
+
+/* Device workspace bytes patch_gemm needs for this M (0 in this version:
+ * every reduction happens inside a workgroup). */
+uint64_t patch_gemm_workspace_bytes(const patch_packed_desc* desc, int64_t M);
+
+/*
+ * Hybrid GEMM: Y = X * (W o E)^T from the packed blob.  Dense tiles use
+ * v_mfma_f32_16x16x32 (bf16/f16); 2:4 tiles use v_smfmac_f32_16x16x64 with
+ * the packed codes as sparse indices; accumulation is fp32; a 16-bit Y is
+ * rounded to nearest even.
+ *
+ *   desc        descriptor from patch_pack / patch_desc_from_header.
+ *   packed_dev  the blob (device).
+ *   X_dev       M x K elements of desc->dtype (device).
+ *   Y_dev       M x N elements of y_dtype (device), y_dtype in {desc->dtype, PATCH_F32}.
+ *   workspace   may be NULL when patch_gemm_workspace_bytes() is 0.
+ * Asynchronous on `stream`.
+ */
+patch_status patch_gemm(const patch_packed_desc* desc, const void* packed_dev, const void* X_dev, int64_t M,
+                        void* Y_dev, patch_dtype y_dtype, void* workspace_dev, uint64_t workspace_bytes,
+                        void* stream);
+
+/* patch_gemm with an explicit kernel variant (patch_variant); used by tests to
+ * run both kernels on the same shapes. */
+patch_status patch_gemm_ex(const patch_packed_desc* desc, const void* packed_dev, const void* X_dev, int64_t M,
+                           void* Y_dev, patch_dtype y_dtype, void* workspace_dev, uint64_t workspace_bytes,
+                           int32_t variant, void* stream);
+
+/*
+ * Same-shape dense baseline: Y = X * W^T from plain row-major W (N x K), on
+ * the same MFMA machinery as patch_gemm with every tile dense.
+ */
+patch_status patch_dense_gemm(patch_dtype dtype, int64_t M, int64_t N, int64_t K, const void* X_dev,
+                              const void* W_dev, void* Y_dev, patch_dtype y_dtype, void* workspace_dev,
+                              uint64_t workspace_bytes, void* stream);
+
+/* patch_dense_gemm with an explicit kernel variant (patch_variant). */
+patch_status patch_dense_gemm_ex(patch_dtype dtype, int64_t M, int64_t N, int64_t K, const void* X_dev,
+                                 const void* W_dev, void* Y_dev, patch_dtype y_dtype, void* workspace_dev,
+                                 uint64_t workspace_bytes, int32_t variant, void* stream);
+
+const char* patch_status_string(patch_status s);
+const char* patch_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PATCH_H */

@@ -1,0 +1,102 @@
+// device_common.h -- vector types, fragment loads and matrix-core wrappers
+// shared by the gfx950 kernels of the hybrid tile-sparse GEMM.
+//
+// Matrix-core operand layouts used throughout (checked on gfx950 against a
+// CPU model for every lane and every 2:4 pattern before any kernel was
+// written):
+//   v_mfma_f32_16x16x32_{bf16,f16}:  A lane l = row l%16, K 8*(l/16)+t (t<8);
+//                                    B lane l = col l%16, K 8*(l/16)+t;
+//                                    D lane l, reg r = row 4*(l/16)+r, col l%16.
+//   v_smfmac_f32_16x16x64_{bf16,f16}: A lane l = row l%16, 8 stored values
+//                                    covering logical K 16*(l/16) .. +15, value
+//                                    v in the group of four v/2, its position
+//                                    in that group = index bits [2v+1:2v] of
+//                                    the 16-bit half selected by ABID;
+//                                    B lane l = col l%16, regs 0..7 = K
+//                                    8*(l/16)+t, regs 8..15 = K 32+8*(l/16)+t
+//                                    (two stacked 16x16x32 B fragments);
+//                                    D as for the dense instruction.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace patch {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 128;             // execution tile edge (N and K)
+constexpr int kDenseTileBytes = 32768; // 128 x 128 x 2
+constexpr int kSparseValBytes = 16384; // 128 x 64 x 2
+constexpr int kSparseTileBytes = 18432;
+constexpr int kHeaderBytes = 256;
+constexpr int kErrFlagOffset = 252;    // reserved header word used by pack to report a bad mask
+
+// A 16-byte chunk loaded by one lane.
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x4 ld16_pred(const void* p, bool ok) {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return ok ? *reinterpret_cast<const u32x4*>(p) : z;
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Dense 16x16x32 step: acc += A(16x32) * B(32x16).
+template <bool BF16>
+__device__ __forceinline__ f32x4 mma_dense(u32x4 a, u32x4 b, f32x4 acc) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc,
+                                                   0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc, 0,
+                                                  0, 0);
+  }
+}
+
+// 2:4 sparse 16x16x64 step: acc += A_sparse(16x64, 8 stored values a lane) * B(64x16).
+// b_lo covers logical K 8h..8h+7, b_hi covers 32+8h..32+8h+7 (h = lane/16).
+// ABID selects which 16-bit half of `idx` holds this step's 2-bit positions.
+template <bool BF16, int ABID>
+__device__ __forceinline__ f32x4 mma_sparse(u32x4 a, u32x4 b_lo, u32x4 b_hi, f32x4 acc, uint32_t idx) {
+  u32x8 b = {b_lo[0], b_lo[1], b_lo[2], b_lo[3], b_hi[0], b_hi[1], b_hi[2], b_hi[3]};
+  if constexpr (BF16) {
+    return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x16, b),
+                                                     acc, (int)idx, 0, ABID);
+  } else {
+    return __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x16, b), acc,
+                                                    (int)idx, 0, ABID);
+  }
+}
+
+// Store four consecutive outputs Y[row][n..n+3] of one accumulator lane.
+// 16-bit outputs are rounded to nearest even (v_cvt_pk_bf16_f32 /
+// v_cvt_f16_f32 round to nearest even on gfx950).
+template <bool BF16, bool OUT_F32>
+__device__ __forceinline__ void store4(void* Y, int64_t elem_off, f32x4 v) {
+  if constexpr (OUT_F32) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(Y) + elem_off) = v;
+  } else if constexpr (BF16) {
+    bf16x4 o = __builtin_convertvector(v, bf16x4);
+    *reinterpret_cast<bf16x4*>(reinterpret_cast<uint16_t*>(Y) + elem_off) = o;
+  } else {
+    f16x4 o = __builtin_convertvector(v, f16x4);
+    *reinterpret_cast<f16x4*>(reinterpret_cast<uint16_t*>(Y) + elem_off) = o;
+  }
+}
+
+// One tile-table entry of the packed blob.
+struct TileEntry {
+  uint64_t offset;  // byte offset of the tile's data from the blob start
+  uint32_t kind;    // 0 dense, 1 sparse
+  uint32_t zero;
+};
+
+}  // namespace patch

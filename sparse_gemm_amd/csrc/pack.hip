@@ -1,0 +1,97 @@
+// pack.hip -- dense W + tile map + 2:4 mask -> packed blob (format version 1).
+//
+// PATCH (arXiv 2509.23410), gist.science explainer, section 2 "Core
+// Mechanism": every 128 x 128 tile of W is dense or 2:4 sparse; section 1
+// "Problem Statement": a 2:4 group keeps two of four consecutive weights;
+// section 2 "Pattern Selection": six possible patterns per group.
+//
+// Tile data layout (the host writes the header and the tile table before
+// this kernel runs):
+//   dense tile : 2048 chunks of 16 bytes; chunk c = (q*8 + band)*64 + l holds
+//                row 16*band + l%16, columns 32*q + 8*(l/16) .. +7.
+//   sparse tile: 1024 value chunks, chunk c = (q*8 + band)*64 + l holds the two
+//                kept values (ascending column) of the groups
+//                g = 16*q + 4*(l/16) + p, p = 0..3, of row 16*band + l%16;
+//                then 512 metadata words, word band*64 + l holding group g's
+//                code i0 | i1 << 2 at bits 16*q + 4*p.
+// This is exactly the lane order of the matrix-core operands (dense A of
+// v_mfma_f32_16x16x32, sparse A and index of v_smfmac_f32_16x16x64), so the
+// GEMM kernels load each 1 KB fragment with one coalesced 16-byte load a lane.
+#include "device_common.h"
+
+namespace patch {
+
+// grid: T * 8 workgroups of 256 threads; workgroup (t, part) packs part of tile t.
+__global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, const uint8_t* __restrict__ mask,
+                                              int K, int KT, uint8_t* __restrict__ blob) {
+  const int t = blockIdx.x >> 3;
+  const int part = blockIdx.x & 7;
+  const TileEntry e = reinterpret_cast<const TileEntry*>(blob + kHeaderBytes)[t];
+  const int i = t / KT, j = t - (t / KT) * KT;
+  uint8_t* tile = blob + e.offset;
+  if (e.kind == 0) {
+    const int c = part * 256 + threadIdx.x;  // 0 .. 2047
+    const int q = c >> 9, band = (c >> 6) & 7, l = c & 63;
+    const int64_t row = (int64_t)i * kTile + 16 * band + (l & 15);
+    const int64_t col = (int64_t)j * kTile + 32 * q + 8 * (l >> 4);
+    st16(tile + 16 * c, ld16(W + row * K + col));
+    return;
+  }
+  if (part >= 2) return;
+  const int pair = part * 256 + threadIdx.x;  // (band, l), 0 .. 511
+  const int band = pair >> 6, l = pair & 63;
+  const int64_t row = (int64_t)i * kTile + 16 * band + (l & 15);
+  uint32_t meta = 0;
+  bool bad = false;
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    const int64_t col0 = (int64_t)j * kTile + 64 * q + 16 * (l >> 4);
+    const uint16_t* wp = W + row * K + col0;
+    const uint8_t* mp = mask + row * K + col0;
+    u32x4 w0 = ld16(wp), w1 = ld16(wp + 8);
+    u32x4 m4 = ld16(mp);
+    uint16_t wv[16];
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+      wv[2 * d] = (uint16_t)(w0[d] & 0xffffu);
+      wv[2 * d + 1] = (uint16_t)(w0[d] >> 16);
+      wv[8 + 2 * d] = (uint16_t)(w1[d] & 0xffffu);
+      wv[8 + 2 * d + 1] = (uint16_t)(w1[d] >> 16);
+    }
+    uint32_t outv[4];
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+      const uint32_t mword = m4[p];  // mask bytes of group p (4 columns)
+      uint32_t kept[2] = {0u, 0u};
+      uint32_t pos[2] = {0u, 0u};
+      int n = 0;
+#pragma unroll
+      for (int d = 0; d < 4; d++) {
+        if ((mword >> (8 * d)) & 0xffu) {
+          if (n < 2) {
+            kept[n] = wv[4 * p + d];
+            pos[n] = (uint32_t)d;
+          }
+          n++;
+        }
+      }
+      bad |= (n != 2);
+      outv[p] = kept[0] | (kept[1] << 16);
+      meta |= (pos[0] | (pos[1] << 2)) << (16 * q + 4 * p);
+    }
+    u32x4 o = {outv[0], outv[1], outv[2], outv[3]};
+    st16(tile + 16 * ((q * 8 + band) * 64 + l), o);
+  }
+  reinterpret_cast<uint32_t*>(tile + kSparseValBytes)[pair] = meta;
+  if (bad) atomicOr(reinterpret_cast<uint32_t*>(blob + kErrFlagOffset), 1u);
+}
+
+hipError_t launch_pack(const void* W, const uint8_t* mask, int64_t N, int64_t K, uint8_t* blob, hipStream_t s) {
+  const int KT = (int)(K / kTile);
+  const int64_t T = (N / kTile) * KT;
+  hipLaunchKernelGGL(k_pack, dim3((unsigned)(T * 8)), dim3(256), 0, s, reinterpret_cast<const uint16_t*>(W), mask,
+                     (int)K, KT, blob);
+  return hipGetLastError();
+}
+
+}  // namespace patch

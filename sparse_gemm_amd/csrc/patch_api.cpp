@@ -1,0 +1,283 @@
+// patch_api.cpp -- host side of the C ABI declared in include/patch.h:
+// argument validation, the packed header and tile table, kernel selection.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "patch.h"
+
+namespace patch {
+hipError_t launch_pack(const void* W, const uint8_t* mask, int64_t N, int64_t K, uint8_t* blob, hipStream_t s);
+hipError_t launch_decode(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* X, int64_t M, int64_t N,
+                         int64_t K, void* Y, hipStream_t s);
+hipError_t launch_prefill(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* X, int64_t M, int64_t N,
+                          int64_t K, void* Y, hipStream_t s);
+}  // namespace patch
+
+namespace {
+
+constexpr uint32_t kMagic = 0x48435450u;  // "PTCH"
+constexpr uint32_t kVersion = 1;
+constexpr int64_t kTile = 128;
+constexpr uint64_t kDenseBytes = 32768;
+constexpr uint64_t kSparseBytes = 18432;
+constexpr int64_t kMaxDim = int64_t(1) << 20;  // N, K upper bound (int32 indexing inside kernels)
+constexpr int64_t kMaxKT = 1024;              // decode kernel's per-workgroup tile list
+constexpr uint64_t kErrFlagOffset = 252;
+
+thread_local std::string g_err;
+
+patch_status fail(patch_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+patch_status hip_fail(hipError_t e, const char* what) {
+  return fail(PATCH_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+patch_status check_nk(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || N % kTile || K % kTile)
+    return fail(PATCH_ERR_SHAPE, "N=%lld K=%lld must be positive multiples of 128", (long long)N, (long long)K);
+  if (N > kMaxDim || K > kMaxDim || K / kTile > kMaxKT)
+    return fail(PATCH_ERR_SHAPE, "N=%lld K=%lld exceed the supported maximum (%lld, K/128 <= %lld)", (long long)N,
+                (long long)K, (long long)kMaxDim, (long long)kMaxKT);
+  return PATCH_OK;
+}
+
+patch_status check_dtype(patch_dtype dt) {
+  if (dt != PATCH_F16 && dt != PATCH_BF16) return fail(PATCH_ERR_INVALID_ARG, "dtype %d is not F16 or BF16", (int)dt);
+  return PATCH_OK;
+}
+
+patch_status check_ydtype(patch_dtype in, patch_dtype y) {
+  if (y != in && y != PATCH_F32)
+    return fail(PATCH_ERR_INVALID_ARG, "y_dtype %d must equal the input dtype %d or be F32", (int)y, (int)in);
+  return PATCH_OK;
+}
+
+patch_status check_desc(const patch_packed_desc* d) {
+  if (!d) return fail(PATCH_ERR_INVALID_ARG, "null descriptor");
+  if (d->version != kVersion || d->tile_n != kTile || d->tile_k != kTile)
+    return fail(PATCH_ERR_INVALID_ARG, "descriptor version/tile mismatch");
+  if (check_dtype((patch_dtype)d->dtype)) return PATCH_ERR_INVALID_ARG;
+  patch_status s = check_nk(d->N, d->K);
+  if (s) return s;
+  const uint64_t T = (uint64_t)d->nt_n * d->nt_k;
+  if (d->nt_n != d->N / kTile || d->nt_k != d->K / kTile || d->n_sparse > T || d->table_offset != 256 ||
+      d->data_offset != round_up(256 + 16 * T, 256) ||
+      d->total_bytes != d->data_offset + kDenseBytes * (T - d->n_sparse) + kSparseBytes * d->n_sparse)
+    return fail(PATCH_ERR_INVALID_ARG, "inconsistent descriptor");
+  return PATCH_OK;
+}
+
+void put32(uint8_t* p, uint32_t v) { std::memcpy(p, &v, 4); }
+void put64(uint8_t* p, uint64_t v) { std::memcpy(p, &v, 8); }
+
+}  // namespace
+
+extern "C" {
+
+int32_t patch_abi_version(void) { return 1; }
+
+const char* patch_status_string(patch_status s) {
+  switch (s) {
+    case PATCH_OK: return "ok";
+    case PATCH_ERR_INVALID_ARG: return "invalid argument";
+    case PATCH_ERR_SHAPE: return "unsupported shape";
+    case PATCH_ERR_MASK: return "mask does not keep exactly two of four in a sparse tile";
+    case PATCH_ERR_BUFFER_TOO_SMALL: return "buffer too small";
+    case PATCH_ERR_UNSUPPORTED: return "unsupported";
+    case PATCH_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* patch_last_error(void) { return g_err.c_str(); }
+
+uint64_t patch_packed_bytes(patch_dtype dtype, int64_t N, int64_t K, const uint8_t* tile_map_host) {
+  if (check_dtype(dtype) || check_nk(N, K) || !tile_map_host) return 0;
+  const int64_t T = (N / kTile) * (K / kTile);
+  uint64_t ns = 0;
+  for (int64_t t = 0; t < T; t++) ns += tile_map_host[t] != 0;
+  return round_up(256 + 16 * (uint64_t)T, 256) + kDenseBytes * (uint64_t)(T - (int64_t)ns) + kSparseBytes * ns;
+}
+
+patch_status patch_pack(patch_dtype dtype, int64_t N, int64_t K, const void* W_dev, const uint8_t* tile_map_host,
+                        const uint8_t* mask_dev, void* packed_dev, uint64_t packed_bytes,
+                        patch_packed_desc* desc_out, void* stream) {
+  patch_status s;
+  if ((s = check_dtype(dtype))) return s;
+  if ((s = check_nk(N, K))) return s;
+  if (!W_dev || !tile_map_host || !mask_dev || !packed_dev || !desc_out)
+    return fail(PATCH_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(W_dev) || !aligned16(mask_dev) || !aligned16(packed_dev))
+    return fail(PATCH_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  const int64_t NT = N / kTile, KT = K / kTile, T = NT * KT;
+  const uint64_t need = patch_packed_bytes(dtype, N, K, tile_map_host);
+  if (packed_bytes < need)
+    return fail(PATCH_ERR_BUFFER_TOO_SMALL, "packed buffer %llu < %llu bytes", (unsigned long long)packed_bytes,
+                (unsigned long long)need);
+
+  // header + tile table, built on the host
+  const uint64_t data_off = round_up(256 + 16 * (uint64_t)T, 256);
+  std::vector<uint8_t> head(data_off, 0);
+  uint32_t ns = 0;
+  uint64_t off = data_off;
+  for (int64_t t = 0; t < T; t++) {
+    const uint32_t kind = tile_map_host[t] != 0;
+    put64(&head[256 + 16 * t], off);
+    put32(&head[256 + 16 * t + 8], kind);
+    off += kind ? kSparseBytes : kDenseBytes;
+    ns += kind;
+  }
+  put32(&head[0], kMagic);
+  put32(&head[4], kVersion);
+  put32(&head[8], (uint32_t)dtype);
+  put32(&head[12], (uint32_t)kTile);
+  put32(&head[16], (uint32_t)kTile);
+  put32(&head[20], (uint32_t)N);
+  put32(&head[24], (uint32_t)K);
+  put32(&head[28], (uint32_t)NT);
+  put32(&head[32], (uint32_t)KT);
+  put32(&head[36], ns);
+  put64(&head[40], 256);
+  put64(&head[48], data_off);
+  put64(&head[56], need - data_off);
+  put64(&head[64], need);
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(packed_dev, head.data(), head.size(), hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(header)");
+  e = patch::launch_pack(W_dev, mask_dev, N, K, reinterpret_cast<uint8_t*>(packed_dev), st);
+  if (e != hipSuccess) return hip_fail(e, "launch pack");
+  uint32_t flag = 0;
+  e = hipMemcpyAsync(&flag, reinterpret_cast<uint8_t*>(packed_dev) + kErrFlagOffset, 4, hipMemcpyDeviceToHost, st);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(flag)");
+  e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  if (flag) return fail(PATCH_ERR_MASK, "a group of four inside a sparse tile does not keep exactly two weights");
+
+  patch_packed_desc d;
+  d.version = kVersion;
+  d.dtype = (uint32_t)dtype;
+  d.tile_n = d.tile_k = (uint32_t)kTile;
+  d.N = (uint32_t)N;
+  d.K = (uint32_t)K;
+  d.nt_n = (uint32_t)NT;
+  d.nt_k = (uint32_t)KT;
+  d.n_sparse = ns;
+  d.table_offset = 256;
+  d.data_offset = data_off;
+  d.total_bytes = need;
+  *desc_out = d;
+  return PATCH_OK;
+}
+
+patch_status patch_desc_from_header(const void* header_host, uint64_t header_bytes, patch_packed_desc* desc_out) {
+  if (!header_host || !desc_out) return fail(PATCH_ERR_INVALID_ARG, "null pointer argument");
+  if (header_bytes < 72) return fail(PATCH_ERR_BUFFER_TOO_SMALL, "header needs at least 72 bytes");
+  const uint8_t* h = reinterpret_cast<const uint8_t*>(header_host);
+  uint32_t u[10];
+  uint64_t v[4];
+  std::memcpy(u, h, 40);
+  std::memcpy(v, h + 40, 32);
+  if (u[0] != kMagic) return fail(PATCH_ERR_INVALID_ARG, "bad magic");
+  patch_packed_desc d;
+  d.version = u[1];
+  d.dtype = u[2];
+  d.tile_n = u[3];
+  d.tile_k = u[4];
+  d.N = u[5];
+  d.K = u[6];
+  d.nt_n = u[7];
+  d.nt_k = u[8];
+  d.n_sparse = u[9];
+  d.table_offset = v[0];
+  d.data_offset = v[1];
+  d.total_bytes = v[3];
+  if (v[2] != d.total_bytes - d.data_offset) return fail(PATCH_ERR_INVALID_ARG, "inconsistent data size");
+  patch_status s = check_desc(&d);
+  if (s) return s;
+  *desc_out = d;
+  return PATCH_OK;
+}
+
+uint64_t patch_gemm_workspace_bytes(const patch_packed_desc* desc, int64_t M) {
+  (void)desc;
+  (void)M;
+  return 0;
+}
+
+static patch_status gemm_common(bool rowmajor, patch_dtype dt, int64_t M, int64_t N, int64_t K, const void* src,
+                                const void* X_dev, void* Y_dev, patch_dtype y_dtype, int32_t variant, void* stream) {
+  patch_status s;
+  if ((s = check_ydtype(dt, y_dtype))) return s;
+  if (M < 0 || M > (int64_t)0x7fffffff) return fail(PATCH_ERR_INVALID_ARG, "M=%lld out of range", (long long)M);
+  if (variant < PATCH_VARIANT_AUTO || variant > PATCH_VARIANT_PREFILL)
+    return fail(PATCH_ERR_INVALID_ARG, "unknown variant %d", (int)variant);
+  if (variant == PATCH_VARIANT_DECODE && M > 16)
+    return fail(PATCH_ERR_INVALID_ARG, "decode variant needs M <= 16 (M=%lld)", (long long)M);
+  if (M == 0) return PATCH_OK;
+  if (!src || !X_dev || !Y_dev) return fail(PATCH_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(src) || !aligned16(X_dev) || !aligned16(Y_dev))
+    return fail(PATCH_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  const bool decode = variant == PATCH_VARIANT_DECODE || (variant == PATCH_VARIANT_AUTO && M <= 16);
+  const bool bf16 = dt == PATCH_BF16, f32out = y_dtype == PATCH_F32;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = decode ? patch::launch_decode(bf16, rowmajor, f32out, src, X_dev, M, N, K, Y_dev, st)
+                        : patch::launch_prefill(bf16, rowmajor, f32out, src, X_dev, M, N, K, Y_dev, st);
+  if (e != hipSuccess) return hip_fail(e, decode ? "launch decode" : "launch prefill");
+  return PATCH_OK;
+}
+
+patch_status patch_gemm_ex(const patch_packed_desc* desc, const void* packed_dev, const void* X_dev, int64_t M,
+                           void* Y_dev, patch_dtype y_dtype, void* workspace_dev, uint64_t workspace_bytes,
+                           int32_t variant, void* stream) {
+  (void)workspace_dev;
+  (void)workspace_bytes;
+  patch_status s = check_desc(desc);
+  if (s) return s;
+  return gemm_common(false, (patch_dtype)desc->dtype, M, desc->N, desc->K, packed_dev, X_dev, Y_dev, y_dtype, variant,
+                     stream);
+}
+
+patch_status patch_gemm(const patch_packed_desc* desc, const void* packed_dev, const void* X_dev, int64_t M,
+                        void* Y_dev, patch_dtype y_dtype, void* workspace_dev, uint64_t workspace_bytes,
+                        void* stream) {
+  return patch_gemm_ex(desc, packed_dev, X_dev, M, Y_dev, y_dtype, workspace_dev, workspace_bytes,
+                       PATCH_VARIANT_AUTO, stream);
+}
+
+patch_status patch_dense_gemm_ex(patch_dtype dtype, int64_t M, int64_t N, int64_t K, const void* X_dev,
+                                 const void* W_dev, void* Y_dev, patch_dtype y_dtype, void* workspace_dev,
+                                 uint64_t workspace_bytes, int32_t variant, void* stream) {
+  (void)workspace_dev;
+  (void)workspace_bytes;
+  patch_status s;
+  if ((s = check_dtype(dtype))) return s;
+  if ((s = check_nk(N, K))) return s;
+  return gemm_common(true, dtype, M, N, K, W_dev, X_dev, Y_dev, y_dtype, variant, stream);
+}
+
+patch_status patch_dense_gemm(patch_dtype dtype, int64_t M, int64_t N, int64_t K, const void* X_dev,
+                              const void* W_dev, void* Y_dev, patch_dtype y_dtype, void* workspace_dev,
+                              uint64_t workspace_bytes, void* stream) {
+  return patch_dense_gemm_ex(dtype, M, N, K, X_dev, W_dev, Y_dev, y_dtype, workspace_dev, workspace_bytes,
+                             PATCH_VARIANT_AUTO, stream);
+}
+
+}  // extern "C"

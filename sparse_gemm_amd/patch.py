@@ -1,0 +1,192 @@
+"""Python binding of libpatch.so (C ABI in include/patch.h).
+
+Argument marshalling only: every step of the hybrid GEMM runs in the HIP
+kernels behind the C ABI.  torch provides device memory and the current HIP
+stream; nothing here computes on the CPU, and there is no fallback -- if the
+library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpatch.so")
+
+PATCH_F16, PATCH_BF16, PATCH_F32 = 0, 1, 2
+VARIANTS = {"auto": 0, "decode": 1, "prefill": 2}
+STATUS = {0: "PATCH_OK", 1: "PATCH_ERR_INVALID_ARG", 2: "PATCH_ERR_SHAPE", 3: "PATCH_ERR_MASK",
+          4: "PATCH_ERR_BUFFER_TOO_SMALL", 5: "PATCH_ERR_UNSUPPORTED", 6: "PATCH_ERR_HIP"}
+
+_TORCH_DT = {torch.float16: PATCH_F16, torch.bfloat16: PATCH_BF16, torch.float32: PATCH_F32}
+_DT_TORCH = {PATCH_F16: torch.float16, PATCH_BF16: torch.bfloat16, PATCH_F32: torch.float32}
+
+
+class PatchError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("version", ctypes.c_uint32), ("dtype", ctypes.c_uint32), ("tile_n", ctypes.c_uint32),
+                ("tile_k", ctypes.c_uint32), ("N", ctypes.c_uint32), ("K", ctypes.c_uint32),
+                ("nt_n", ctypes.c_uint32), ("nt_k", ctypes.c_uint32), ("n_sparse", ctypes.c_uint32),
+                ("table_offset", ctypes.c_uint64), ("data_offset", ctypes.c_uint64),
+                ("total_bytes", ctypes.c_uint64)]
+
+
+EXPORTS = ("patch_abi_version", "patch_packed_bytes", "patch_pack", "patch_desc_from_header",
+           "patch_gemm_workspace_bytes", "patch_gemm", "patch_gemm_ex", "patch_dense_gemm", "patch_dense_gemm_ex",
+           "patch_status_string", "patch_last_error")
+
+_lib = None
+
+
+def load():
+    """Load libpatch.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_gemm_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, U64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_int32
+    DP = ctypes.POINTER(Desc)
+    lib.patch_abi_version.argtypes = []
+    lib.patch_abi_version.restype = I32
+    lib.patch_packed_bytes.argtypes = [ctypes.c_int, I64, I64, P]
+    lib.patch_packed_bytes.restype = U64
+    lib.patch_pack.argtypes = [ctypes.c_int, I64, I64, P, P, P, P, U64, DP, P]
+    lib.patch_pack.restype = ctypes.c_int
+    lib.patch_desc_from_header.argtypes = [P, U64, DP]
+    lib.patch_desc_from_header.restype = ctypes.c_int
+    lib.patch_gemm_workspace_bytes.argtypes = [DP, I64]
+    lib.patch_gemm_workspace_bytes.restype = U64
+    lib.patch_gemm.argtypes = [DP, P, P, I64, P, ctypes.c_int, P, U64, P]
+    lib.patch_gemm.restype = ctypes.c_int
+    lib.patch_gemm_ex.argtypes = [DP, P, P, I64, P, ctypes.c_int, P, U64, I32, P]
+    lib.patch_gemm_ex.restype = ctypes.c_int
+    lib.patch_dense_gemm.argtypes = [ctypes.c_int, I64, I64, I64, P, P, P, ctypes.c_int, P, U64, P]
+    lib.patch_dense_gemm.restype = ctypes.c_int
+    lib.patch_dense_gemm_ex.argtypes = [ctypes.c_int, I64, I64, I64, P, P, P, ctypes.c_int, P, U64, I32, P]
+    lib.patch_dense_gemm_ex.restype = ctypes.c_int
+    lib.patch_status_string.argtypes = [ctypes.c_int]
+    lib.patch_status_string.restype = ctypes.c_char_p
+    lib.patch_last_error.argtypes = []
+    lib.patch_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise PatchError(rc, load().patch_last_error().decode())
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _dt(dtype: torch.dtype) -> int:
+    if dtype not in _TORCH_DT:
+        raise TypeError(f"unsupported dtype {dtype}")
+    return _TORCH_DT[dtype]
+
+
+def _host_map(tile_map) -> np.ndarray:
+    if isinstance(tile_map, torch.Tensor):
+        tile_map = tile_map.detach().cpu().numpy()
+    return np.ascontiguousarray(tile_map, dtype=np.uint8)
+
+
+@dataclasses.dataclass
+class PackedWeight:
+    blob: torch.Tensor  # uint8, device
+    desc: Desc
+
+    @property
+    def N(self) -> int:
+        return self.desc.N
+
+    @property
+    def K(self) -> int:
+        return self.desc.K
+
+    @property
+    def dtype(self) -> torch.dtype:
+        return _DT_TORCH[self.desc.dtype]
+
+    @property
+    def n_sparse(self) -> int:
+        return self.desc.n_sparse
+
+    @property
+    def nbytes(self) -> int:
+        return self.desc.total_bytes
+
+
+def packed_bytes(dtype: torch.dtype, N: int, K: int, tile_map) -> int:
+    tm = _host_map(tile_map)
+    return int(load().patch_packed_bytes(_dt(dtype), N, K, tm.ctypes.data_as(ctypes.c_void_p)))
+
+
+def pack(W: torch.Tensor, tile_map, mask: torch.Tensor, out: Optional[torch.Tensor] = None) -> PackedWeight:
+    """Pack W (N x K, f16/bf16, device), a host tile map (nonzero = 2:4 tile)
+    and a device byte mask (nonzero = keep) into a blob (patch_pack)."""
+    lib = load()
+    N, K = W.shape
+    tm = _host_map(tile_map)
+    nbytes = packed_bytes(W.dtype, N, K, tm)
+    if nbytes == 0:
+        raise PatchError(2, f"invalid shape/dtype for pack: {tuple(W.shape)} {W.dtype}")
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
+    desc = Desc()
+    _check(lib.patch_pack(_dt(W.dtype), N, K, _ptr(W), tm.ctypes.data_as(ctypes.c_void_p), _ptr(mask), _ptr(out),
+                          out.numel(), ctypes.byref(desc), _stream()))
+    return PackedWeight(out, desc)
+
+
+def desc_from_header(header: bytes) -> Desc:
+    buf = (ctypes.c_uint8 * len(header)).from_buffer_copy(header)
+    d = Desc()
+    _check(load().patch_desc_from_header(ctypes.cast(buf, ctypes.c_void_p), len(header), ctypes.byref(d)))
+    return d
+
+
+def gemm(X: torch.Tensor, packed: PackedWeight, out_dtype: Optional[torch.dtype] = None, variant: str = "auto",
+         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X (W o E)^T from a packed blob (patch_gemm_ex)."""
+    lib = load()
+    M = X.shape[0]
+    od = out_dtype or X.dtype
+    if out is None:
+        out = torch.empty((M, packed.N), dtype=od, device=X.device)
+    _check(lib.patch_gemm_ex(ctypes.byref(packed.desc), _ptr(packed.blob), _ptr(X), M, _ptr(out), _dt(od), None, 0,
+                             VARIANTS[variant], _stream()))
+    return out
+
+
+def dense_gemm(X: torch.Tensor, W: torch.Tensor, out_dtype: Optional[torch.dtype] = None, variant: str = "auto",
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Same-shape dense baseline Y = X W^T from row-major W (patch_dense_gemm_ex)."""
+    lib = load()
+    M, K = X.shape
+    N = W.shape[0]
+    od = out_dtype or X.dtype
+    if out is None:
+        out = torch.empty((M, N), dtype=od, device=X.device)
+    _check(lib.patch_dense_gemm_ex(_dt(X.dtype), M, N, K, _ptr(X), _ptr(W), _ptr(out), _dt(od), None, 0,
+                                   VARIANTS[variant], _stream()))
+    return out

@@ -1,0 +1,310 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Pages: PATCH (arXiv 2509.23410), gist.science explainer, section 2 "Core
+Mechanism" (dense or 2:4 tiles), "Inference & Deployment" (dense tiles on dense
+kernels, 2:4 tiles on the sparse path), section 4 "Ablation Studies" (128 x
+128 execution tiles).
+
+Bars: the packed blob is bit-exact with the oracle's; a GEMM with a 16-bit
+output is within relative Frobenius 2e-3 and max error 1e-2 * max|Y_ref| of
+the fp64 oracle (tests/gpu_util.py); cases whose exact result is
+representable (identity X, small integers with a float32 output) must match
+exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_gemm_amd import inputs, patch
+from tests.gpu_util import assert_close, dev_bits, dev_u8, host_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    patch.load()
+    torch.cuda.set_device(0)
+
+
+def _pack(p):
+    W = dev_bits(p.w, p.dtype)
+    return patch.pack(W, p.tile_map, dev_u8(p.mask)), W
+
+
+def _ref(p, X, rows=None):
+    Xs = X if rows is None else X[rows]
+    return oracle.gemm_f64(p.dtype, Xs, p.w, p.tile_map, p.mask)
+
+
+# ------------------------------------------------------------------ pack
+PACK_CASES = [
+    ("tiny_seed0", lambda: inputs.make_weights(inputs.CONFIGS["tiny"], 0, 0, seed=0)),
+    ("tiny_seed1", lambda: inputs.make_weights(inputs.CONFIGS["tiny"], 0, 0, seed=1)),
+    ("tiny_all_dense", lambda: inputs.make_weights(inputs.CONFIGS["tiny"], 0, 0, map_kind="dense")),
+    ("tiny_all_sparse", lambda: inputs.make_weights(inputs.CONFIGS["tiny"], 0, 0, map_kind="sparse")),
+    ("single_tile_sparse_bf16", lambda: inputs.make_custom("bf16", 128, 128, 3, "sparse", 1.0, "uniform")),
+    ("single_tile_dense_f16", lambda: inputs.make_custom("f16", 128, 128, 3, "dense", 0.0, "top2")),
+    ("ragged_384x640", lambda: inputs.make_custom("bf16", 384, 640, 4, "bernoulli", 0.5, "uniform")),
+    ("decode_q_proj", lambda: inputs.make_weights(inputs.CONFIGS["decode"], 0, 0)),
+]
+
+
+@pytest.mark.parametrize("name,make", PACK_CASES, ids=[c[0] for c in PACK_CASES])
+def test_pack_bit_exact(name, make):
+    p = make()
+    pw, _ = _pack(p)
+    torch.cuda.synchronize()
+    got = pw.blob.cpu().numpy()
+    ref = oracle.pack(p.dtype, p.w, p.tile_map, p.mask)
+    assert got.size == ref.size
+    diff = np.flatnonzero(got != ref)
+    assert diff.size == 0, f"{name}: {diff.size} bytes differ, first at {diff[:8]}"
+    assert pw.n_sparse == int(p.tile_map.sum())
+
+
+@pytest.mark.parametrize("mi", [0, 1])
+def test_pack_bit_exact_prefill_mlp_and_13b(mi):
+    for cfg in ("prefill_mlp", "imbalanced_13b"):
+        p = inputs.make_weights(inputs.CONFIGS[cfg], mi, 0)
+        pw, _ = _pack(p)
+        torch.cuda.synchronize()
+        got = pw.blob.cpu().numpy()
+        ref = oracle.pack(p.dtype, p.w, p.tile_map, p.mask)
+        assert np.array_equal(got, ref), cfg
+
+
+def test_pack_rejects_illegal_mask_on_gpu():
+    p = inputs.make_custom("bf16", 256, 256, 5, "sparse", 1.0, "top2")
+    mask = p.mask.copy()
+    mask[200, 4 * 40:4 * 40 + 4] = [1, 1, 1, 0]
+    with pytest.raises(patch.PatchError) as e:
+        patch.pack(dev_bits(p.w, "bf16"), p.tile_map, dev_u8(mask))
+    assert e.value.name == "PATCH_ERR_MASK"
+    # the same bad group inside a dense tile is ignored
+    tm = p.tile_map.copy()
+    tm[1, 1] = 0
+    pw = patch.pack(dev_bits(p.w, "bf16"), tm, dev_u8(mask))
+    torch.cuda.synchronize()
+    assert np.array_equal(pw.blob.cpu().numpy(), oracle.pack("bf16", p.w, tm, mask))
+
+
+# ------------------------------------------------------------------ GEMM, small shapes
+SMALL_M = [1, 2, 3, 4, 7, 15, 16, 17, 31, 100, 255, 256, 257, 300]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("M", SMALL_M)
+def test_gemm_small_ragged(dtype, M):
+    """384 x 640 (3 x 5 tiles, random map), every M edge, every variant, both
+    output types."""
+    p = inputs.make_custom(dtype, 384, 640, 7, "bernoulli", 0.5, "top2")
+    assert 0 < p.tile_map.sum() < p.tile_map.size
+    pw, _ = _pack(p)
+    Xb = inputs.make_custom_x(dtype, M, 640, M)
+    X = dev_bits(Xb, dtype)
+    ref = _ref(p, Xb)
+    variants = ["auto", "prefill"] + (["decode"] if M <= 16 else [])
+    for v in variants:
+        y = patch.gemm(X, pw, variant=v)
+        assert_close(y, ref, what=f"{dtype} M={M} {v}")
+        y32 = patch.gemm(X, pw, out_dtype=torch.float32, variant=v)
+        assert_close(y32, ref, f32=True, what=f"{dtype} M={M} {v} f32")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("M", [1, 16, 17, 300])
+def test_dense_baseline_small(dtype, M):
+    p = inputs.make_custom(dtype, 384, 640, 8, "dense", 0.0, "top2")
+    W = dev_bits(p.w, dtype)
+    Xb = inputs.make_custom_x(dtype, M, 640, M + 1)
+    X = dev_bits(Xb, dtype)
+    ref = _ref(p, Xb)
+    for v in ["auto", "prefill"] + (["decode"] if M <= 16 else []):
+        assert_close(patch.dense_gemm(X, W, variant=v), ref, what=f"dense {dtype} M={M} {v}")
+        assert_close(patch.dense_gemm(X, W, out_dtype=torch.float32, variant=v), ref, f32=True,
+                     what=f"dense {dtype} M={M} {v} f32")
+
+
+@pytest.mark.parametrize("M", [5, 16, 64, 300])
+def test_all_dense_map_equals_dense_baseline_bitwise(M):
+    """An all-dense tile map runs the same arithmetic in the same order as the
+    dense baseline, so the two must agree bit for bit."""
+    p = inputs.make_custom("bf16", 256, 512, 9, "dense", 0.0, "top2")
+    pw, W = _pack(p)
+    X = dev_bits(inputs.make_custom_x("bf16", M, 512, 3), "bf16")
+    for v in ["prefill"] + (["decode"] if M <= 16 else []):
+        a = patch.gemm(X, pw, out_dtype=torch.float32, variant=v)
+        b = patch.dense_gemm(X, W, out_dtype=torch.float32, variant=v)
+        assert torch.equal(a, b), v
+
+
+# ------------------------------------------------------------------ exact cases
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_identity_x_gives_masked_weights_exactly(dtype):
+    """X = rows of the identity: every output is one product w * 1, exact in
+    any precision, so Y^T == W o E bit for bit.  This pins every metadata
+    position of every lane for both variants."""
+    p = inputs.make_custom(dtype, 256, 384, 10, "bernoulli", 0.5, "uniform")
+    pw, _ = _pack(p)
+    E = oracle.effective_mask(p.N, p.K, p.tile_map, p.mask)
+    Weff = np.where(E != 0, inputs.bits_to_f32(p.w, dtype), 0.0).astype(np.float64)
+    eye = inputs.to_bits(np.eye(p.K), dtype)
+    # prefill: all K rows at once
+    y = patch.gemm(dev_bits(eye, dtype), pw, variant="prefill")
+    assert np.array_equal(host_f64(y).T, Weff)
+    # decode: 16 rows at a time
+    for k0 in range(0, p.K, 16):
+        y = patch.gemm(dev_bits(eye[k0:k0 + 16], dtype), pw, variant="decode")
+        assert np.array_equal(host_f64(y).T, Weff[:, k0:k0 + 16]), k0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("M", [3, 16, 200])
+def test_small_integers_exact_in_f32(dtype, M):
+    """|x|, |w| <= 2 and K <= 4096: every partial sum is an integer below 2^24,
+    so any fp32 summation order is exact and must equal the oracle."""
+    rng = np.random.default_rng(M)
+    N, K = 256, 1024
+    p = inputs.make_custom(dtype, N, K, 11, "bernoulli", 0.5, "uniform")
+    p.w = inputs.to_bits(rng.integers(-2, 3, (N, K)).astype(np.float64), dtype)
+    Xb = inputs.to_bits(rng.integers(-2, 3, (M, K)).astype(np.float64), dtype)
+    pw, _ = _pack(p)
+    ref = _ref(p, Xb)
+    for v in ["prefill"] + (["decode"] if M <= 16 else []):
+        y = patch.gemm(dev_bits(Xb, dtype), pw, out_dtype=torch.float32, variant=v)
+        assert np.array_equal(host_f64(y), ref), v
+
+
+def test_six_patterns_every_lane_slot():
+    """Each of the six patterns in every group of a full tile, with X = ones on
+    one column at a time."""
+    N = K = 128
+    rng = np.random.default_rng(5)
+    w = inputs.to_bits(rng.integers(1, 8, (N, K)).astype(np.float64), "bf16")
+    pat = (np.arange(N)[:, None] + np.arange(K // 4)[None, :]) % 6
+    mask = np.zeros((N, K // 4, 4), np.uint8)
+    np.put_along_axis(mask, inputs.PATTERNS[pat], 1, axis=-1)
+    mask = mask.reshape(N, K)
+    tm = np.ones((1, 1), np.uint8)
+    pw = patch.pack(dev_bits(w, "bf16"), tm, dev_u8(mask))
+    eye = inputs.to_bits(np.eye(K), "bf16")
+    ref = oracle.gemm_f64("bf16", eye, w, tm, mask)
+    y = patch.gemm(dev_bits(eye, "bf16"), pw, out_dtype=torch.float32, variant="prefill")
+    assert np.array_equal(host_f64(y), ref)
+    for k0 in range(0, K, 16):
+        y = patch.gemm(dev_bits(eye[k0:k0 + 16], "bf16"), pw, out_dtype=torch.float32, variant="decode")
+        assert np.array_equal(host_f64(y), ref[k0:k0 + 16])
+
+
+# ------------------------------------------------------------------ robustness
+def test_output_guard_bands_untouched():
+    p = inputs.make_custom("bf16", 384, 640, 12, "bernoulli", 0.5, "top2")
+    pw, _ = _pack(p)
+    for M in (7, 300):
+        X = dev_bits(inputs.make_custom_x("bf16", M, 640, 1), "bf16")
+        for v in ["prefill"] + (["decode"] if M <= 16 else []):
+            pad = 4096
+            buf = torch.full((M * 384 + 2 * pad,), 12345.0, dtype=torch.float32, device="cuda")
+            y = buf[pad:pad + M * 384].view(M, 384)
+            patch.gemm(X, pw, out_dtype=torch.float32, variant=v, out=y)
+            torch.cuda.synchronize()
+            assert torch.all(buf[:pad] == 12345.0) and torch.all(buf[pad + M * 384:] == 12345.0), v
+
+
+def test_blob_guard_bands_untouched():
+    p = inputs.make_custom("bf16", 256, 384, 13, "bernoulli", 0.5, "top2")
+    n = oracle.packed_bytes(p.N, p.K, p.tile_map)
+    pad = 4096
+    buf = torch.full((n + 2 * pad,), 0xA5, dtype=torch.uint8, device="cuda")
+    pw = patch.pack(dev_bits(p.w, "bf16"), p.tile_map, dev_u8(p.mask), out=buf[pad:pad + n])
+    torch.cuda.synchronize()
+    assert torch.all(buf[:pad] == 0xA5) and torch.all(buf[pad + n:] == 0xA5)
+    assert np.array_equal(pw.blob.cpu().numpy(), oracle.pack("bf16", p.w, p.tile_map, p.mask))
+
+
+def test_deterministic_repeat():
+    p = inputs.make_weights(inputs.CONFIGS["decode"], 0, 0)
+    pw, _ = _pack(p)
+    for M in (16, 512):
+        X = dev_bits(inputs.make_x(inputs.CONFIGS["decode"], M, p.K), "bf16")
+        a = patch.gemm(X, pw, out_dtype=torch.float32)
+        b = patch.gemm(X, pw, out_dtype=torch.float32)
+        assert torch.equal(a, b), M
+
+
+# ------------------------------------------------------------------ the named workloads
+def test_config_tiny_all_seeds():
+    cfg = inputs.CONFIGS["tiny"]
+    for seed in range(6):
+        p = inputs.make_weights(cfg, 0, 0, seed=seed)
+        pw, _ = _pack(p)
+        Xb = inputs.make_x(cfg, 16, p.K, seed=seed)
+        ref = _ref(p, Xb)
+        for v in ("auto", "decode", "prefill"):
+            assert_close(patch.gemm(dev_bits(Xb, "f16"), pw, variant=v), ref, what=f"tiny seed {seed} {v}")
+
+
+def test_config_decode_q_proj_full():
+    cfg = inputs.CONFIGS["decode"]
+    p = inputs.make_weights(cfg, 0, 0)
+    assert p.tile_map.sum() == 512
+    pw, W = _pack(p)
+    for M in cfg.Ms:
+        Xb = inputs.make_x(cfg, M, p.K)
+        X = dev_bits(Xb, "bf16")
+        ref = _ref(p, Xb)
+        assert_close(patch.gemm(X, pw), ref, what=f"decode M={M}")
+        assert_close(patch.gemm(X, pw, out_dtype=torch.float32), ref, f32=True, what=f"decode M={M} f32")
+
+
+def _sampled_rows(M, n=24, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, size=min(M, n), replace=False)]))
+    return rows
+
+
+@pytest.mark.parametrize("mi", [0, 1])
+def test_config_prefill_mlp_sampled(mi):
+    cfg = inputs.CONFIGS["prefill_mlp"]
+    p = inputs.make_weights(cfg, mi, 0)
+    assert p.tile_map.sum() == 2202
+    pw, _ = _pack(p)
+    M = cfg.Ms[0]
+    Xb = inputs.make_x(cfg, M, p.K, matrix_index=mi)
+    y = patch.gemm(dev_bits(Xb, "bf16"), pw)
+    rows = _sampled_rows(M)
+    assert_close(y[torch.from_numpy(rows).cuda()], _ref(p, Xb, rows), what=f"prefill_mlp {cfg.matrices[mi].name}")
+
+
+@pytest.mark.parametrize("mi", [0, 1])
+def test_config_imbalanced_13b_sampled(mi):
+    cfg = inputs.CONFIGS["imbalanced_13b"]
+    p = inputs.make_weights(cfg, mi, 0)
+    NT = p.N // 128
+    assert np.all(p.tile_map[:NT // 2] == 0) and np.all(p.tile_map[NT // 2:] == 1)
+    pw, _ = _pack(p)
+    M = cfg.Ms[0]
+    Xb = inputs.make_x(cfg, M, p.K, matrix_index=mi)
+    y = patch.gemm(dev_bits(Xb, "bf16"), pw)
+    rows = _sampled_rows(M, seed=mi)
+    assert_close(y[torch.from_numpy(rows).cuda()], _ref(p, Xb, rows), what=f"13b {cfg.matrices[mi].name}")
+
+
+@pytest.mark.parametrize("mi", [0, 4, 6])
+def test_config_sweep_sampled(mi):
+    """Sparsity sweep (q_proj, gate_proj, down_proj) at every sparse-tile
+    fraction and every M of the sweep, on sampled output rows."""
+    cfg = inputs.CONFIGS["sweep"]
+    for si, frac in enumerate(cfg.fractions):
+        p = inputs.make_weights(cfg, mi, si)
+        assert p.tile_map.sum() == int(np.round(frac * p.tile_map.size))
+        pw, _ = _pack(p)
+        for M in cfg.Ms:
+            Xb = inputs.make_x(cfg, M, p.K, matrix_index=mi)
+            y = patch.gemm(dev_bits(Xb, "bf16"), pw)
+            rows = _sampled_rows(M, n=8, seed=si)
+            assert_close(y[torch.from_numpy(rows).cuda()], _ref(p, Xb, rows),
+                         what=f"sweep {cfg.matrices[mi].name} s={frac} M={M}")
