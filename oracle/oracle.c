@@ -46,6 +46,9 @@
 #include <stdlib.h>
 #include <string.h>
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORACLE_OK 0
 #define ORACLE_ERR_ARG 1
@@ -55,6 +58,15 @@
 
 #define ORACLE_F16 0
 #define ORACLE_BF16 1
+
+/* Number of OpenMP threads oracle_gemm_f64 runs on (1 without OpenMP). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
 
 /* ---------------------------------------------------------------------------
  * Element decoding, written from the IEEE 754-2008 binary16 definition and the

@@ -63,6 +63,8 @@ def load():
     lib.oracle_packed_bytes.restype = ctypes.c_uint64
     lib.oracle_pack.argtypes = [ctypes.c_int, I64, I64, P, P, P, P, ctypes.c_uint64]
     lib.oracle_pack.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -77,6 +79,10 @@ def _u16(a) -> np.ndarray:
 
 def _u8(a) -> np.ndarray:
     return np.ascontiguousarray(a, dtype=np.uint8)
+
+
+def num_threads() -> int:
+    return int(load().oracle_num_threads())
 
 
 def f16_to_double(bits: int) -> float:

@@ -6,10 +6,10 @@
 // kernel streams each tile's packed bytes exactly once:
 //
 //   * one workgroup per 16-row band of W (N/16 workgroups) and all of K;
-//   * the workgroup first splits the band's row-block into a list of dense
-//     and a list of sparse tiles (from the tile table), then its waves take
-//     tiles round-robin from each list, so every wave gets an equal share of
-//     each kind;
+//     wave w of the workgroup takes the tile columns j = w, w+8, w+16, ...
+//     of the band's row-block, reading each tile's offset and kind from the
+//     tile table with a scalar load (no list building, no barrier before the
+//     first weight load);
 //   * a tile's 16 x 128 band is 4 (dense) or 2 (sparse) 1 KB fragments that a
 //     wave loads with one 16-byte load per lane each, straight into the A
 //     operand registers; X (at most 16 rows) is read from L2 into the B
@@ -26,61 +26,70 @@
 namespace patch {
 
 constexpr int kDecodeWaves = 8;
-constexpr int kDecodeMaxKT = 1024;  // K <= 131072
+constexpr int kDecodeMaxKT = 512;  // 64 tiles per wave
 
+// Registers of one tile in flight.  Both kinds issue the same eight 16-byte
+// loads (4 for X, 4 for W), so the wait counts the compiler derives stay
+// exact whatever mix of kinds a wave meets:
+//   dense : a[c] = the band's fragment of slice c (c = 0..3);
+//   sparse: a[0], a[1] = value fragments of slices 0 and 1, a[2] = the 16-byte
+//           aligned chunk of the band's metadata holding this lane's word
+//           (word l & 3), a[3] = the same chunk again (unused).
 struct DecodeFrag {
   u32x4 x[4];  // B operand chunks: X[m][k0 + 32c + 8h .. +7], c = 0..3
-  u32x4 a[4];  // A operand chunks (dense: 4 slices; sparse: 2 slices in a[0..1])
-  uint32_t meta;
+  u32x4 a[4];
+  uint32_t kind;
 };
 
+// Lanes whose X row is >= M only feed output columns >= M, which are never
+// stored, so they need no X at all: they re-read their own W chunk (same
+// cache lines as the A load) instead of a predicated load (which would make
+// the compiler wait for it right away) or all hitting row 0 of X (a hot spot
+// when M is 1).
 template <bool SRC_ROWMAJOR>
-__device__ __forceinline__ void decode_load_dense(DecodeFrag& f, const uint8_t* __restrict__ src, uint64_t tile_off,
-                                                  const uint16_t* __restrict__ X, int K, int M, int i, int b, int j,
-                                                  int l) {
+__device__ __forceinline__ void decode_load(DecodeFrag& f, const uint8_t* __restrict__ src, uint64_t off,
+                                            uint32_t kind, const uint16_t* __restrict__ X, int K, int M, int i, int b,
+                                            int j, int l) {
   const int m = l & 15, h = l >> 4;
   const bool mok = m < M;
-  const uint16_t* xr = X + (int64_t)(mok ? m : 0) * K + (int64_t)j * kTile + 8 * h;
-#pragma unroll
-  for (int c = 0; c < 4; c++) f.x[c] = ld16_pred(xr + 32 * c, mok);
+  const uint16_t* xr = X + (int64_t)m * K + (int64_t)j * kTile + 8 * h;
   if constexpr (SRC_ROWMAJOR) {
     const uint16_t* W = reinterpret_cast<const uint16_t*>(src);
     const uint16_t* wr = W + ((int64_t)i * kTile + 16 * b + m) * K + (int64_t)j * kTile + 8 * h;
 #pragma unroll
-    for (int c = 0; c < 4; c++) f.a[c] = ld16(wr + 32 * c);
-  } else {
-    const uint8_t* tp = src + tile_off + 1024 * b + 16 * l;
+    for (int c = 0; c < 4; c++) f.x[c] = ld16(mok ? xr + 32 * c : wr + 32 * c);
 #pragma unroll
-    for (int c = 0; c < 4; c++) f.a[c] = ld16(tp + 8192 * c);
+    for (int c = 0; c < 4; c++) f.a[c] = ld16(wr + 32 * c);
+    f.kind = 0;
+  } else {
+    const uint8_t* tp = src + off + 1024 * b + 16 * l;
+    const uint8_t* mp = src + off + kSparseValBytes + ((4 * (64 * b + l)) & ~15);
+    const uint8_t* ap[4] = {tp, tp + 8192, kind ? mp : tp + 16384, kind ? mp : tp + 24576};
+#pragma unroll
+    for (int c = 0; c < 4; c++)
+      f.x[c] = ld16(mok ? reinterpret_cast<const uint8_t*>(xr + 32 * c) : ap[c]);
+    f.kind = kind;
+#pragma unroll
+    for (int c = 0; c < 4; c++) f.a[c] = ld16(ap[c]);
   }
 }
 
-__device__ __forceinline__ void decode_load_sparse(DecodeFrag& f, const uint8_t* __restrict__ src, uint64_t tile_off,
-                                                   const uint16_t* __restrict__ X, int K, int M, int b, int j, int l) {
-  const int m = l & 15, h = l >> 4;
-  const bool mok = m < M;
-  const uint16_t* xr = X + (int64_t)(mok ? m : 0) * K + (int64_t)j * kTile + 8 * h;
+template <bool BF16, bool SRC_ROWMAJOR>
+__device__ __forceinline__ f32x4 decode_mma(const DecodeFrag& f, f32x4 acc, int l) {
+  if (SRC_ROWMAJOR || f.kind == 0) {
 #pragma unroll
-  for (int c = 0; c < 4; c++) f.x[c] = ld16_pred(xr + 32 * c, mok);
-  const uint8_t* tp = src + tile_off + 1024 * b + 16 * l;
-  f.a[0] = ld16(tp);
-  f.a[1] = ld16(tp + 8192);
-  f.meta = *reinterpret_cast<const uint32_t*>(src + tile_off + kSparseValBytes + 4 * (64 * b + l));
-}
-
-template <bool BF16>
-__device__ __forceinline__ f32x4 decode_mma_dense(const DecodeFrag& f, f32x4 acc) {
-#pragma unroll
-  for (int c = 0; c < 4; c++) acc = mma_dense<BF16>(f.a[c], f.x[c], acc);
-  return acc;
-}
-
-template <bool BF16>
-__device__ __forceinline__ f32x4 decode_mma_sparse(const DecodeFrag& f, f32x4 acc) {
-  // slice 0: logical K 0..63 of the tile -> B chunks 0 (K 8h..) and 1 (K 32+8h..)
-  acc = mma_sparse<BF16, 0>(f.a[0], f.x[0], f.x[1], acc, f.meta);
-  // slice 1: logical K 64..127 -> B chunks 2 and 3
-  acc = mma_sparse<BF16, 1>(f.a[1], f.x[2], f.x[3], acc, f.meta);
+    for (int c = 0; c < 4; c++) acc = mma_dense<BF16>(f.a[c], f.x[c], acc);
+  } else {
+    // this lane's word of the 16-byte metadata chunk (selects, not a dynamic
+    // vector index, which would put the fragment array in scratch memory)
+    const int sel = l & 3;
+    const u32x4 mc = f.a[2];
+    const uint32_t meta = sel == 0 ? mc[0] : sel == 1 ? mc[1] : sel == 2 ? mc[2] : mc[3];
+    // slice 0: logical K 0..63 of the tile -> B chunks 0 (K 8h..) and 1 (K 32+8h..)
+    acc = mma_sparse<BF16, 0>(f.a[0], f.x[0], f.x[1], acc, meta);
+    // slice 1: logical K 64..127 -> B chunks 2 and 3
+    acc = mma_sparse<BF16, 1>(f.a[1], f.x[2], f.x[3], acc, meta);
+  }
   return acc;
 }
 
@@ -91,97 +100,59 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void k_decode(const uint8_t* __r
   const int KT = K / kTile;
   const int band_g = blockIdx.x;  // 16-row band of W
   const int i = band_g >> 3, b = band_g & 7;
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  const TileEntry* table = reinterpret_cast<const TileEntry*>(src + kHeaderBytes) + (int64_t)i * KT;
 
-  __shared__ uint32_t s_list[2][kDecodeMaxKT];  // [0] dense tiles, [1] sparse tiles: (j << 0), offsets below
-  __shared__ uint64_t s_off[2][kDecodeMaxKT];
-  __shared__ int s_count[2];
   __shared__ f32x4 s_red[kDecodeWaves][64];
 
-  int nd, ns;
-  if constexpr (SRC_ROWMAJOR) {
-    nd = KT;
-    ns = 0;
-  } else {
-    // Split this row-block's tiles into a dense and a sparse list (in column order).
-    const TileEntry* table = reinterpret_cast<const TileEntry*>(src + kHeaderBytes) + (int64_t)i * KT;
-    if (w == 0) {
-      int base_d = 0, base_s = 0;
-      for (int c0 = 0; c0 < KT; c0 += 64) {
-        const int jj = c0 + l;
-        const bool valid = jj < KT;
-        TileEntry e = {0, 0, 0};
-        if (valid) e = table[jj];
-        const bool sp = valid && e.kind != 0;
-        const bool de = valid && e.kind == 0;
-        const uint64_t bs = __ballot(sp), bd = __ballot(de);
-        const uint64_t lt = (l == 0) ? 0ull : (~0ull >> (64 - l));
-        if (de) {
-          const int r = base_d + __popcll(bd & lt);
-          s_list[0][r] = (uint32_t)jj;
-          s_off[0][r] = e.offset;
-        }
-        if (sp) {
-          const int r = base_s + __popcll(bs & lt);
-          s_list[1][r] = (uint32_t)jj;
-          s_off[1][r] = e.offset;
-        }
-        base_d += __popcll(bd);
-        base_s += __popcll(bs);
-      }
-      if (l == 0) {
-        s_count[0] = base_d;
-        s_count[1] = base_s;
-      }
-    }
-    __syncthreads();
-    nd = s_count[0];
-    ns = s_count[1];
-  }
-
+  // wave w takes tile columns j = w, w + 8, w + 16, ... of its row-block
+  // (at most 64 of them: K <= 65536).  Their table entries arrive with one
+  // vector load (lane t holds the entry of the wave's t-th tile) and are read
+  // with v_readlane.
+  const int n_mine = (KT - w + kDecodeWaves - 1) / kDecodeWaves;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-
-  // ---- dense tiles: wave w takes list entries w, w + 8, ...
-  if (w < nd) {
+  if (n_mine > 0) {
+    u32x4 ents = {0u, 0u, 0u, 0u};
+    if constexpr (!SRC_ROWMAJOR) ents = ld16(table + w + kDecodeWaves * min(l, n_mine - 1));
+    auto entry = [&](int t, uint64_t& off, uint32_t& kind) {
+      if constexpr (SRC_ROWMAJOR) {
+        off = 0;
+        kind = 0;
+      } else {
+        const int lane = t;
+        off = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ents[0], lane) |
+              ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ents[1], lane) << 32);
+        kind = (uint32_t)__builtin_amdgcn_readlane((int)ents[2], lane);
+      }
+    };
     DecodeFrag f[DEPTH];
 #pragma unroll
     for (int s = 0; s < DEPTH; s++) {
-      const int e = min(w + s * kDecodeWaves, nd - 1);
-      const int j = SRC_ROWMAJOR ? e : (int)s_list[0][e];
-      const uint64_t off = SRC_ROWMAJOR ? 0 : s_off[0][e];
-      decode_load_dense<SRC_ROWMAJOR>(f[s], src, off, X, K, M, i, b, j, l);
+      const int t = min(s, n_mine - 1);
+      uint64_t off;
+      uint32_t kind;
+      entry(t, off, kind);
+      decode_load<SRC_ROWMAJOR>(f[s], src, off, kind, X, K, M, i, b, w + kDecodeWaves * t, l);
     }
-    for (int base = w; base < nd; base += DEPTH * kDecodeWaves) {
+    // steady state: compute the DEPTH slots, refilling each with the tile
+    // DEPTH further on (clamped to the last tile: a redundant, cached load)
+    int t0 = 0;
+    for (; t0 + DEPTH < n_mine; t0 += DEPTH) {
 #pragma unroll
       for (int s = 0; s < DEPTH; s++) {
-        const int e = base + s * kDecodeWaves;
-        if (e < nd) acc = decode_mma_dense<BF16>(f[s], acc);
-        const int en = min(e + DEPTH * kDecodeWaves, nd - 1);
-        const int j = SRC_ROWMAJOR ? en : (int)s_list[0][en];
-        const uint64_t off = SRC_ROWMAJOR ? 0 : s_off[0][en];
-        decode_load_dense<SRC_ROWMAJOR>(f[s], src, off, X, K, M, i, b, j, l);
+        acc = decode_mma<BF16, SRC_ROWMAJOR>(f[s], acc, l);
+        const int tn = min(t0 + s + DEPTH, n_mine - 1);
+        uint64_t off;
+        uint32_t kind;
+        entry(tn, off, kind);
+        decode_load<SRC_ROWMAJOR>(f[s], src, off, kind, X, K, M, i, b, w + kDecodeWaves * tn, l);
       }
     }
-  }
-  // ---- sparse tiles
-  if constexpr (!SRC_ROWMAJOR) {
-    if (w < ns) {
-      DecodeFrag f[DEPTH];
+    // last round: no refills
 #pragma unroll
-      for (int s = 0; s < DEPTH; s++) {
-        const int e = min(w + s * kDecodeWaves, ns - 1);
-        decode_load_sparse(f[s], src, s_off[1][e], X, K, M, b, (int)s_list[1][e], l);
-      }
-      for (int base = w; base < ns; base += DEPTH * kDecodeWaves) {
-#pragma unroll
-        for (int s = 0; s < DEPTH; s++) {
-          const int e = base + s * kDecodeWaves;
-          if (e < ns) acc = decode_mma_sparse<BF16>(f[s], acc);
-          const int en = min(e + DEPTH * kDecodeWaves, ns - 1);
-          decode_load_sparse(f[s], src, s_off[1][en], X, K, M, b, (int)s_list[1][en], l);
-        }
-      }
-    }
+    for (int s = 0; s < DEPTH; s++)
+      if (t0 + s < n_mine) acc = decode_mma<BF16, SRC_ROWMAJOR>(f[s], acc, l);
   }
 
   // ---- fixed-order reduction over waves, then round and store
@@ -203,7 +174,7 @@ template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32>
 static hipError_t launch_decode_t(const void* src, const void* X, int64_t M, int64_t N, int64_t K, void* Y,
                                   hipStream_t s) {
   const unsigned grid = (unsigned)(N / 16);
-  hipLaunchKernelGGL((k_decode<BF16, SRC_ROWMAJOR, OUT_F32, 2>), dim3(grid), dim3(kDecodeWaves * 64), 0, s,
+  hipLaunchKernelGGL((k_decode<BF16, SRC_ROWMAJOR, OUT_F32, 4>), dim3(grid), dim3(kDecodeWaves * 64), 0, s,
                      reinterpret_cast<const uint8_t*>(src), reinterpret_cast<const uint16_t*>(X), (int)M, (int)N,
                      (int)K, Y);
   return hipGetLastError();

@@ -26,7 +26,8 @@ constexpr int64_t kTile = 128;
 constexpr uint64_t kDenseBytes = 32768;
 constexpr uint64_t kSparseBytes = 18432;
 constexpr int64_t kMaxDim = int64_t(1) << 20;  // N, K upper bound (int32 indexing inside kernels)
-constexpr int64_t kMaxKT = 1024;              // decode kernel's per-workgroup tile list
+constexpr int64_t kMaxKT = 1024;              // prefill kernel's per-workgroup tile lists
+constexpr int64_t kDecodeMaxK = 65536;        // decode kernel: <= 64 tile columns per wave
 constexpr uint64_t kErrFlagOffset = 252;
 
 thread_local std::string g_err;
@@ -235,7 +236,10 @@ static patch_status gemm_common(bool rowmajor, patch_dtype dt, int64_t M, int64_
   if (!src || !X_dev || !Y_dev) return fail(PATCH_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned16(src) || !aligned16(X_dev) || !aligned16(Y_dev))
     return fail(PATCH_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
-  const bool decode = variant == PATCH_VARIANT_DECODE || (variant == PATCH_VARIANT_AUTO && M <= 16);
+  if (variant == PATCH_VARIANT_DECODE && K > kDecodeMaxK)
+    return fail(PATCH_ERR_UNSUPPORTED, "decode variant needs K <= %lld (K=%lld)", (long long)kDecodeMaxK, (long long)K);
+  const bool decode =
+      variant == PATCH_VARIANT_DECODE || (variant == PATCH_VARIANT_AUTO && M <= 16 && K <= kDecodeMaxK);
   const bool bf16 = dt == PATCH_BF16, f32out = y_dtype == PATCH_F32;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = decode ? patch::launch_decode(bf16, rowmajor, f32out, src, X_dev, M, N, K, Y_dev, st)

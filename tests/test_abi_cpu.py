@@ -80,6 +80,9 @@ def test_bad_arguments_rejected_before_launch():
         "PATCH_ERR_INVALID_ARG"
     assert patch.STATUS[lib.patch_dense_gemm_ex(1, 4, 256, 256, V(16), V(16), V(16), 1, None, 0, 9, None)] == \
         "PATCH_ERR_INVALID_ARG"
+    # the decode kernel serves K <= 65536 only
+    assert patch.STATUS[lib.patch_dense_gemm_ex(1, 4, 256, 65536 + 128, V(16), V(16), V(16), 1, None, 0, 1, None)] == \
+        "PATCH_ERR_UNSUPPORTED"
     # M == 0 is a no-op that launches nothing (valid on a machine without a GPU)
     assert lib.patch_dense_gemm(1, 0, 256, 256, V(16), V(16), V(16), 1, None, 0, None) == 0
 
