@@ -255,6 +255,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--report", default=None, help="also write the full sweep as JSON lines to this path")
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill_mlp", "imbalanced_13b"],
+                    help="decode (default: the q_proj decode GEMM) or a prefill workload, for profiling")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (reference for rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 (the multi-GPU sharding "
@@ -269,6 +273,17 @@ def main():
     torch.cuda.set_device(0)
     patch.load()
 
+    if args.calibrate_copy:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": src.numel(), "copies": 3}), file=sys.stderr, flush=True)
+        del src, dst
+    if args.workload != "decode":
+        run_prefill_workload(args)
+        return
     cfg = inputs.CONFIGS["decode"]
     Ms = cfg.Ms
     res = gemm_set("decode", 0, 0, Ms, args.steps, args.warmup)
@@ -328,6 +343,22 @@ def main():
 
     if args.report:
         write_report(args.report, args.steps, args.warmup)
+
+
+def run_prefill_workload(args):
+    """One prefill workload (both matrices) as JSON lines: for profiling the
+    prefill kernel; not the headline line."""
+    from sparse_gemm_amd import inputs
+
+    cfg = inputs.CONFIGS[args.workload]
+    for mi in range(len(cfg.matrices)):
+        res = gemm_set(args.workload, mi, 0, cfg.Ms, args.steps, args.warmup)
+        summ = summarize(res, cfg.Ms)
+        p = res["p"]
+        for M in cfg.Ms:
+            print(json.dumps(dict(workload=args.workload, matrix=cfg.matrices[mi].name, N=p.N, K=p.K, M=M,
+                                  sparse_tiles=int(p.tile_map.sum()), tiles=int(p.tile_map.size), **summ[M])),
+                  flush=True)
 
 
 def write_report(path, steps, warmup):
