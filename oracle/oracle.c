@@ -36,7 +36,7 @@
  * ascending order in binary64, so the result does not depend on the number
  * of threads (OpenMP splits the work over output rows n only).
  *
- * The packed format is the repository's own (format version 1): the pages fix
+ * The packed format is the repository's own (format version 2): the pages fix
  * only the tile shape (128 x 128 execution tiles, gist.science explainer,
  * section 4 "Ablation Studies"), the six 2:4 patterns (section 2, "Pattern
  * Selection") and nothing about bytes.  oracle_pack() writes it from its
@@ -253,13 +253,13 @@ void oracle_round_f64(int dtype, int64_t n, const double* in, uint16_t* out) {
 }
 
 /* ---------------------------------------------------------------------------
- * Packed format, version 1 (the repository's own format; restated here).
+ * Packed format, version 2 (the repository's own format; restated here).
  *
  * Tile edge b = 128 in both directions; NT = N/128, KT = K/128, T = NT*KT.
  * Little-endian.  All bytes not written below are zero.
  *
  * Header, 256 bytes at offset 0:
- *   u32 magic 0x48435450, u32 version 1, u32 dtype (0 f16, 1 bf16),
+ *   u32 magic 0x48435450, u32 version 2, u32 dtype (0 f16, 1 bf16),
  *   u32 tile_n 128, u32 tile_k 128, u32 N, u32 K, u32 NT, u32 KT,
  *   u32 n_sparse, u64 table_offset (= 256), u64 data_offset,
  *   u64 data_bytes, u64 total_bytes.
@@ -272,9 +272,14 @@ void oracle_round_f64(int dtype, int64_t n, const double* in, uint16_t* out) {
  * Inside a tile, a "band" is 16 consecutive rows (b = 0..7) and a "lane" is
  * a number l = 0..63 with row-in-band r = l mod 16 and column group h = l / 16.
  *
- * Dense tile: 4 slices q of 32 columns; chunk (q, band, l) holds the 8
- *   elements of row 16*band + (l mod 16), columns 32*q + 8*(l/16) + t for
- *   t = 0..7, in that order.  Chunk index = (q*8 + band)*64 + l, 16 bytes each.
+ * Dense tile: 2 slices q of 64 columns; lane l covers the 16 columns
+ *   64*q + 16*(l/16) .. +15 of row 16*band + (l mod 16), i.e. four groups of
+ *   four g = 0..3.  Chunk (q, band, e, l), e = 0 or 1, holds the elements at
+ *   positions 2e and 2e+1 of those four groups: element 2*g + u (u = 0, 1) is
+ *   column 64*q + 16*(l/16) + 4*g + 2*e + u.  Chunk index
+ *   = ((q*8 + band)*2 + e)*64 + l, 16 bytes each.  (Each half is a 2:4 operand
+ *   with the fixed pattern (0,1) or (2,3), so a dense tile runs on the same
+ *   sparse matrix instruction as a 2:4 tile.)
  * Sparse tile: groups of four columns g = 0..31 (columns 4g..4g+3).
  *   Values: 2 slices q of 16 groups; chunk (q, band, l) holds, for
  *   p = 0..3 and group g = 16*q + 4*(l/16) + p, the two kept elements of row
@@ -326,7 +331,7 @@ int oracle_pack(int dtype, int64_t N, int64_t K, const uint16_t* W, const uint8_
   for (int64_t t = 0; t < T; t++) ns += tile_map[t] != 0;
   uint64_t data_off = round_up(256 + 16 * (uint64_t)T, 256);
   put32(out + 0, 0x48435450u);
-  put32(out + 4, 1);
+  put32(out + 4, 2);
   put32(out + 8, (uint32_t)dtype);
   put32(out + 12, PT_B);
   put32(out + 16, PT_B);
@@ -349,15 +354,17 @@ int oracle_pack(int dtype, int64_t N, int64_t K, const uint16_t* W, const uint8_
       put32(out + 256 + 16 * t + 8, (uint32_t)sparse);
       uint8_t* tile = out + off;
       if (!sparse) {
-        for (int q = 0; q < 4; q++)
+        for (int q = 0; q < 2; q++)
           for (int band = 0; band < 8; band++)
-            for (int l = 0; l < 64; l++)
-              for (int e = 0; e < 8; e++) {
-                int64_t row = i * PT_B + 16 * band + (l % 16);
-                int64_t col = j * PT_B + 32 * q + 8 * (l / 16) + e;
-                int64_t chunk = ((int64_t)q * 8 + band) * 64 + l;
-                put16(tile + 16 * chunk + 2 * e, W[row * K + col]);
-              }
+            for (int e = 0; e < 2; e++)
+              for (int l = 0; l < 64; l++)
+                for (int g = 0; g < 4; g++)
+                  for (int u = 0; u < 2; u++) {
+                    int64_t row = i * PT_B + 16 * band + (l % 16);
+                    int64_t col = j * PT_B + 64 * q + 16 * (l / 16) + 4 * g + 2 * e + u;
+                    int64_t chunk = (((int64_t)q * 8 + band) * 2 + e) * 64 + l;
+                    put16(tile + 16 * chunk + 2 * (2 * g + u), W[row * K + col]);
+                  }
         off += PT_DENSE_BYTES;
       } else {
         for (int q = 0; q < 2; q++)

@@ -258,6 +258,7 @@ def test_pack_hand_worked_example():
     N, K = 128, 256
     W = np.full((N, K), 0x3F80, np.uint16)
     W[g["dense.row"], g["dense.col"]] = g["dense.bits"]
+    W[g["dense2.row"], g["dense2.col"]] = g["dense2.bits"]
     W[g["sparse.row"], g["sparse.col"]] = g["sparse.bits"]
     mask = np.zeros((N, K), np.uint8)
     mask[:, 0::4] = 1
@@ -271,7 +272,7 @@ def test_pack_hand_worked_example():
     u32 = lambda o: int.from_bytes(blob[o:o + 4].tobytes(), "little")
     u16 = lambda o: int.from_bytes(blob[o:o + 2].tobytes(), "little")
     assert blob.size == g["header.total_bytes"]
-    assert u32(0) == 0x48435450 and u32(4) == 1 and u32(8) == 1
+    assert u32(0) == 0x48435450 and u32(4) == g["header.version"] and u32(8) == 1
     assert (u32(12), u32(16), u32(20), u32(24), u32(28), u32(32)) == (128, 128, N, K, 1, 2)
     assert u32(36) == g["header.n_sparse"]
     assert u64(40) == 256 and u64(48) == g["header.data_offset"] and u64(64) == g["header.total_bytes"]
@@ -279,6 +280,7 @@ def test_pack_hand_worked_example():
     assert u64(256) == g["table.0.offset"] and u32(264) == g["table.0.kind"]
     assert u64(272) == g["table.1.offset"] and u32(280) == g["table.1.kind"]
     assert u16(g["dense.byte_offset"]) == g["dense.bits"]
+    assert u16(g["dense2.byte_offset"]) == g["dense2.bits"]
     assert u16(g["sparse.byte_offset"]) == g["sparse.bits"]
     assert blob[g["sparse.meta_byte_offset"]] == g["sparse.meta_byte_value"]
     # every other metadata nibble of the sparse tile is code 4 (keeps 0 and 1)
@@ -309,13 +311,17 @@ def _unpack(blob, N, K):
             kind = int.from_bytes(blob[e + 8:e + 12].tobytes(), "little")
             tile = blob[off:off + (32768 if kind == 0 else 18432)]
             if kind == 0:
-                ch = tile.view(np.uint16).reshape(4, 8, 64, 8)  # q, band, lane, e
-                for q in range(4):
+                # q (64-column slice), band, half e, lane, element 2*g + u
+                ch = tile.view(np.uint16).reshape(2, 8, 2, 64, 8)
+                for q in range(2):
                     for band in range(8):
-                        for l in range(64):
-                            r = i * 128 + band * 16 + l % 16
-                            c = j * 128 + 32 * q + 8 * (l // 16)
-                            W[r, c:c + 8] = ch[q, band, l]
+                        for e in range(2):
+                            for l in range(64):
+                                r = i * 128 + band * 16 + l % 16
+                                for g in range(4):
+                                    for u in range(2):
+                                        c = j * 128 + 64 * q + 16 * (l // 16) + 4 * g + 2 * e + u
+                                        W[r, c] = ch[q, band, e, l, 2 * g + u]
             else:
                 vals = tile[:16384].view(np.uint16).reshape(2, 8, 64, 8)
                 meta = tile[16384:].view(np.uint32).reshape(8, 64)
