@@ -286,7 +286,9 @@ void oracle_round_f64(int dtype, int64_t n, const double* in, uint16_t* out) {
  *   16*band + (l mod 16) in ascending column order -- 8 elements, 16 bytes.
  *   Chunk index = (q*8 + band)*64 + l; 16384 bytes in all.
  *   Metadata, 2048 bytes after the values: a u32 per (band, l) at
- *   index band*64 + l.  Bits 16*q + 4*p .. +3 hold the code of group
+ *   index (band/4)*256 + 4*l + (band mod 4), so the 16 bytes at
+ *   (band/4)*1024 + 16*l hold lane l's words of four consecutive bands.
+ *   Bits 16*q + 4*p .. +3 hold the code of group
  *   g = 16*q + 4*(l/16) + p of that row; code = i0 | (i1 << 2), i0 < i1 the
  *   positions (0..3) of the two kept elements inside the group.
  * ------------------------------------------------------------------------- */
@@ -384,7 +386,7 @@ int oracle_pack(int dtype, int64_t N, int64_t K, const uint16_t* W, const uint8_
                     s++;
                   }
                 uint32_t code = (uint32_t)pos[0] | ((uint32_t)pos[1] << 2);
-                uint8_t* meta = tile + 16384 + 4 * (band * 64 + l);
+                uint8_t* meta = tile + 16384 + 4 * ((band / 4) * 256 + 4 * l + band % 4);
                 uint32_t word = (uint32_t)meta[0] | ((uint32_t)meta[1] << 8) | ((uint32_t)meta[2] << 16) |
                                 ((uint32_t)meta[3] << 24);
                 word |= code << (16 * q + 4 * p);

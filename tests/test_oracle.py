@@ -324,14 +324,15 @@ def _unpack(blob, N, K):
                                         W[r, c] = ch[q, band, e, l, 2 * g + u]
             else:
                 vals = tile[:16384].view(np.uint16).reshape(2, 8, 64, 8)
-                meta = tile[16384:].view(np.uint32).reshape(8, 64)
+                # word (band, l) at (band // 4) * 256 + 4 * l + band % 4
+                meta = tile[16384:].view(np.uint32).reshape(2, 64, 4)
                 for q in range(2):
                     for band in range(8):
                         for l in range(64):
                             r = i * 128 + band * 16 + l % 16
                             for p in range(4):
                                 g = 16 * q + 4 * (l // 16) + p
-                                code = (int(meta[band, l]) >> (16 * q + 4 * p)) & 15
+                                code = (int(meta[band // 4, l, band % 4]) >> (16 * q + 4 * p)) & 15
                                 codes.append(code)
                                 i0, i1 = code & 3, code >> 2
                                 W[r, j * 128 + 4 * g + i0] = vals[q, band, l, 2 * p]
