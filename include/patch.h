@@ -58,9 +58,9 @@ typedef enum {
   PATCH_VARIANT_PREFILL = 2  /* output-tiled MFMA kernel; any M >= 1 */
 } patch_variant;
 
-/* Host-side mirror of the packed blob's header (format version 1). */
+/* Host-side mirror of the packed blob's header (format version 2). */
 typedef struct {
-  uint32_t version;   /* 1 */
+  uint32_t version;   /* 2 */
   uint32_t dtype;     /* PATCH_F16 or PATCH_BF16 */
   uint32_t tile_n;    /* 128 */
   uint32_t tile_k;    /* 128 */
@@ -88,11 +88,14 @@ uint64_t patch_packed_bytes(patch_dtype dtype, int64_t N, int64_t K, const uint8
 
 /*
  * Pack dense W plus a tile map and a 2:4 mask into the blob (format
- * version 1): a 256-byte header, a 16-byte-per-tile table (data offset, kind)
- * and the tile data.  A dense tile keeps its 128 x 128 values; a sparse tile
- * keeps, for every group of four consecutive weights along K, the two kept
- * values plus a 4-bit code i0 | i1 << 2 (2 bits per kept value), laid out in
- * the order the sparse matrix instructions consume them.  The 2:4 rule:
+ * version 2): a 256-byte header, a 16-byte-per-tile table (data offset, kind)
+ * and the tile data.  A sparse tile keeps, for every group of four
+ * consecutive weights along K, the two kept values plus a 4-bit code
+ * i0 | i1 << 2 (2 bits per kept value); a dense tile keeps all 128 x 128
+ * values, each 64-column slice stored as two halves holding positions (0,1)
+ * and (2,3) of every group of four.  Both are laid out in the lane order of
+ * the sparse matrix instruction's operands, which then runs both kinds (a
+ * dense half is a 2:4 operand with a fixed code).  The 2:4 rule:
  * gist.science explainer, section 1 "Problem Statement"; the six patterns:
  * section 2 "Pattern Selection".
  *
@@ -120,10 +123,10 @@ patch_status patch_desc_from_header(const void* header_host, uint64_t header_byt
 uint64_t patch_gemm_workspace_bytes(const patch_packed_desc* desc, int64_t M);
 
 /*
- * Hybrid GEMM: Y = X * (W o E)^T from the packed blob.  Dense tiles use
- * v_mfma_f32_16x16x32 (bf16/f16); 2:4 tiles use v_smfmac_f32_16x16x64 with
- * the packed codes as sparse indices; accumulation is fp32; a 16-bit Y is
- * rounded to nearest even.
+ * Hybrid GEMM: Y = X * (W o E)^T from the packed blob.  Both tile kinds run
+ * on v_smfmac_f32_16x16x64 (bf16/f16): a 2:4 slice once with its packed
+ * codes, a dense slice as its two fixed-pattern halves; accumulation is
+ * fp32; a 16-bit Y is rounded to nearest even.
  *
  *   desc        descriptor from patch_pack / patch_desc_from_header.
  *   packed_dev  the blob (device).
@@ -143,8 +146,9 @@ patch_status patch_gemm_ex(const patch_packed_desc* desc, const void* packed_dev
                            int32_t variant, void* stream);
 
 /*
- * Same-shape dense baseline: Y = X * W^T from plain row-major W (N x K), on
- * the same MFMA machinery as patch_gemm with every tile dense.
+ * Same-shape dense baseline: Y = X * W^T from plain row-major W (N x K), with
+ * the same tiling and staging as patch_gemm, every tile dense, on
+ * v_mfma_f32_16x16x32.
  */
 patch_status patch_dense_gemm(patch_dtype dtype, int64_t M, int64_t N, int64_t K, const void* X_dev,
                               const void* W_dev, void* Y_dev, patch_dtype y_dtype, void* workspace_dev,

@@ -13,8 +13,10 @@
 //   * a tile's 16 x 128 band is 4 (dense) or 2 (sparse) 1 KB fragments that a
 //     wave loads with one 16-byte load per lane each, straight into the A
 //     operand registers; X (at most 16 rows) is read from L2 into the B
-//     operand registers, zero for rows >= M;
-//   * dense: 4 x v_mfma_f32_16x16x32; sparse: 2 x v_smfmac_f32_16x16x64;
+//     operand registers;
+//   * both kinds run on v_smfmac_f32_16x16x64: a 2:4 tile is 2 of them (one
+//     per 64-column slice, its own index codes), a dense tile 4 (each slice
+//     as two halves with the fixed patterns (0,1) and (2,3));
 //   * loads run DEPTH tiles ahead of the matrix instructions;
 //   * the waves' fp32 partial sums are added in LDS in wave order (fixed, so
 //     results are deterministic) and rounded to the output type.
@@ -26,15 +28,15 @@
 namespace patch {
 
 constexpr int kDecodeWaves = 8;
-constexpr int kDecodeMaxKT = 512;  // 64 tiles per wave
 
 // Registers of one tile in flight.  Both kinds issue the same eight 16-byte
 // loads (4 for X, 4 for W), so the wait counts the compiler derives stay
 // exact whatever mix of kinds a wave meets:
-//   dense : a[c] = the band's fragment of slice c (c = 0..3);
-//   sparse: a[0], a[1] = value fragments of slices 0 and 1, a[2] = the 16-byte
-//           aligned chunk of the band's metadata holding this lane's word
-//           (word l & 3), a[3] = the same chunk again (unused).
+//   dense : a[2q + e] = the band's half e of 64-column slice q (packed W), or
+//           the row-major chunk of columns 32c + 8*(l/16) (dense baseline);
+//   sparse: a[0], a[1] = value fragments of slices 0 and 1, a[2] = this
+//           lane's 16 bytes of metadata for bands 4*(b/4) .. +3 (word b & 3
+//           is the band's), a[3] = the same chunk again (unused).
 struct DecodeFrag {
   u32x4 x[4];  // B operand chunks: X[m][k0 + 32c + 8h .. +7], c = 0..3
   u32x4 a[4];
@@ -62,9 +64,11 @@ __device__ __forceinline__ void decode_load(DecodeFrag& f, const uint8_t* __rest
     for (int c = 0; c < 4; c++) f.a[c] = ld16(wr + 32 * c);
     f.kind = 0;
   } else {
-    const uint8_t* tp = src + off + 1024 * b + 16 * l;
-    const uint8_t* mp = src + off + kSparseValBytes + ((4 * (64 * b + l)) & ~15);
-    const uint8_t* ap[4] = {tp, tp + 8192, kind ? mp : tp + 16384, kind ? mp : tp + 24576};
+    const uint8_t* tp = src + off + 16 * l;
+    const uint8_t* mp = src + off + kSparseValBytes + 1024 * (b >> 2) + 16 * l;
+    const uint8_t* dp = tp + 2048 * b;  // dense: halves of slice 0, then slice 1
+    const uint8_t* ap[4] = {kind ? tp + 1024 * b : dp, kind ? tp + 8192 + 1024 * b : dp + 1024, kind ? mp : dp + 16384,
+                            kind ? mp : dp + 17408};
 #pragma unroll
     for (int c = 0; c < 4; c++)
       f.x[c] = ld16(mok ? reinterpret_cast<const uint8_t*>(xr + 32 * c) : ap[c]);
@@ -75,16 +79,23 @@ __device__ __forceinline__ void decode_load(DecodeFrag& f, const uint8_t* __rest
 }
 
 template <bool BF16, bool SRC_ROWMAJOR>
-__device__ __forceinline__ f32x4 decode_mma(const DecodeFrag& f, f32x4 acc, int l) {
-  if (SRC_ROWMAJOR || f.kind == 0) {
+__device__ __forceinline__ f32x4 decode_mma(const DecodeFrag& f, f32x4 acc, int b) {
+  if constexpr (SRC_ROWMAJOR) {
 #pragma unroll
     for (int c = 0; c < 4; c++) acc = mma_dense<BF16>(f.a[c], f.x[c], acc);
+  } else if (f.kind == 0) {
+    // slice q: halves with positions (0,1) (code 4) and (2,3) (code 14)
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      acc = mma_sparse<BF16, 0>(f.a[2 * q], f.x[2 * q], f.x[2 * q + 1], acc, 0x4444u);
+      acc = mma_sparse<BF16, 0>(f.a[2 * q + 1], f.x[2 * q], f.x[2 * q + 1], acc, 0xEEEEu);
+    }
   } else {
-    // this lane's word of the 16-byte metadata chunk (selects, not a dynamic
-    // vector index, which would put the fragment array in scratch memory)
-    const int sel = l & 3;
+    // the band's word of the lane's metadata chunk (b is the same in every
+    // lane: uniform selects, not a dynamic vector index, which would put the
+    // fragment array in scratch memory)
     const u32x4 mc = f.a[2];
-    const uint32_t meta = sel == 0 ? mc[0] : sel == 1 ? mc[1] : sel == 2 ? mc[2] : mc[3];
+    const uint32_t meta = (b & 2) ? ((b & 1) ? mc[3] : mc[2]) : ((b & 1) ? mc[1] : mc[0]);
     // slice 0: logical K 0..63 of the tile -> B chunks 0 (K 8h..) and 1 (K 32+8h..)
     acc = mma_sparse<BF16, 0>(f.a[0], f.x[0], f.x[1], acc, meta);
     // slice 1: logical K 64..127 -> B chunks 2 and 3
@@ -141,7 +152,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void k_decode(const uint8_t* __r
     for (; t0 + DEPTH < n_mine; t0 += DEPTH) {
 #pragma unroll
       for (int s = 0; s < DEPTH; s++) {
-        acc = decode_mma<BF16, SRC_ROWMAJOR>(f[s], acc, l);
+        acc = decode_mma<BF16, SRC_ROWMAJOR>(f[s], acc, b);
         const int tn = min(t0 + s + DEPTH, n_mine - 1);
         uint64_t off;
         uint32_t kind;
@@ -152,7 +163,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void k_decode(const uint8_t* __r
     // last round: no refills
 #pragma unroll
     for (int s = 0; s < DEPTH; s++)
-      if (t0 + s < n_mine) acc = decode_mma<BF16, SRC_ROWMAJOR>(f[s], acc, l);
+      if (t0 + s < n_mine) acc = decode_mma<BF16, SRC_ROWMAJOR>(f[s], acc, b);
   }
 
   // ---- fixed-order reduction over waves, then round and store

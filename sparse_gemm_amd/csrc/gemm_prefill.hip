@@ -3,37 +3,55 @@
 // PATCH (arXiv 2509.23410), gist.science explainer, section 2 "Inference &
 // Deployment": each tile runs on the dense matrix units or, when it is 2:4,
 // on the sparse ones.  With M >= 512 the product is bound by the matrix
-// cores.  A workgroup owns one 128-row tile row of W (row-block i) and 256
-// columns of M, and keeps that 128 x 256 block of Y^T in fp32 accumulators:
+// cores, so the kernel is built around feeding them:
 //
-//   * 4 waves in a 2 x 2 arrangement; wave (wn, wm) owns bands 4wn..4wn+3 of
-//     the row-block (64 rows of W) and 128 columns of M: 4 x 8 accumulators
-//     of 16 x 16;
-//   * every wave of the workgroup sees the same tile kind at each step (one
-//     row-block per workgroup), so the K loop is split into two loops: first
-//     the row-block's dense tiles, then its 2:4 tiles (the tile table gives the
-//     two lists).  A step covers 64 columns of K: half a dense tile (2 x
-//     v_mfma_f32_16x16x32 deep) or one sparse slice (1 x
-//     v_smfmac_f32_16x16x64 deep, half the matrix-core time);
-//   * X[m0 .. m0+255][64 columns] is copied global -> LDS directly
-//     (global_load_lds_dwordx4, no registers), double-buffered, its 16-byte
-//     chunks XOR-swizzled by row so the B-operand reads hit distinct banks;
+//   * A workgroup (8 waves, one per CU) owns TWO row-blocks of W -- row-block
+//     p and row-block NT-1-p -- and BM columns of M (BM = 128, 192 or 256,
+//     chosen per shape so the grid fills the GPU): a 256 x BM block of Y^T.
+//     Both row-blocks read the same X[m0 .. m0+BM-1][k] slices, so every X
+//     byte brought into the CU feeds 256 rows of W.
+//   * Wave w: row-block r = w/4, bands 4*((w/2)&1) .. +3 of it (64 rows of W)
+//     and BM/2 columns of M (w&1): 4 x BM/32 fp32 accumulators of 16 x 16.
+//     Waves w and w+4 -- one per row-block -- share a SIMD, so when one
+//     row-block's tile is dense and the other's is 2:4 the SIMD's matrix
+//     core is busy for the sum of the two, with no wave idling on the other's
+//     kind.  Pairing row-block p with NT-1-p also evens out maps whose dense
+//     tiles cluster in a band of rows.
+//   * The K loop walks the tile columns in order, 64 columns a step, and
+//     runs both kinds on v_smfmac_f32_16x16x64: a 2:4 slice once with its
+//     own index codes, a dense slice twice (its halves holding positions
+//     (0,1) and (2,3) of every group, fixed codes) -- so both kinds share one
+//     instruction, one B fragment set and one accumulator layout, and the
+//     per-wave choice of kind is just a trip count.
+//   * X[m0 .. m0+BM-1][64 columns] of the next step is loaded into registers
+//     while the current step computes, then written to the other of two LDS
+//     buffers; 16-byte chunks are XOR-swizzled by row so the B-operand reads
+//     hit distinct banks.  Every memory operation in the loop is an ordinary
+//     vector load, so the compiler's wait counts stay exact (mixing in
+//     global -> LDS copies makes it wait for everything before each LDS
+//     read).  Where registers allow, B fragments for the next 32 columns of
+//     M are read from LDS while the current ones feed the matrix cores.
 //   * W comes straight from the packed blob into A-operand registers (a 1 KB
-//     fragment = one 16-byte load a lane), fetched one step ahead;
-//   * workgroups are numbered so that each of the 8 XCDs gets a contiguous
-//     run of output blocks (the M-blocks of a row-block share its W tiles in
-//     that XCD's L2).
+//     fragment is one 16-byte load a lane), one step ahead; eight loads a
+//     lane per step for either kind.
+//   * All loads are buffer loads: a scalar descriptor (tile or X block base)
+//     plus a 32-bit lane offset, so addresses cost no 64-bit vector
+//     arithmetic; X rows past M fall outside the X descriptor's range and
+//     read as zero.
+//   * Workgroups are numbered so that each of the 8 XCDs gets a contiguous
+//     run of output blocks (the M-blocks of a row-block pair share its W
+//     tiles in that XCD's L2; the pairs share the X slices).
 //
 // With SRC_ROWMAJOR the same kernel reads plain row-major W with every tile
-// dense: the same-shape dense baseline.
+// dense, on v_mfma_f32_16x16x32: the same-shape dense baseline.
 #include "device_common.h"
 
 namespace patch {
 
-constexpr int kPfBM = 256;                        // M columns of a workgroup block
-constexpr int kPfRowBytes = 128;                  // one staged X row: 64 elements
-constexpr int kPfBufBytes = kPfBM * kPfRowBytes;  // 32 KB per stage
+constexpr int kPfWaves = 8;
+constexpr int kPfRowBytes = 128;  // one staged X row: 64 elements
 constexpr int kPfMaxKT = 1024;
+constexpr int kPfMGroup = 2;      // 16-column blocks of M whose B fragments are read together
 
 // Chunk position of 16-byte chunk c (0..7) of staged row r.  The XOR keeps the
 // 16 rows read by one B-fragment load on distinct bank groups for both 32- and
@@ -41,265 +59,371 @@ constexpr int kPfMaxKT = 1024;
 __device__ __forceinline__ int swz_f(int r) { return (((r ^ (r >> 3)) & 1) << 2) | ((r >> 1) & 3); }
 __device__ __forceinline__ int swz(int r, int c) { return r * kPfRowBytes + ((c ^ swz_f(r)) << 4); }
 
-// 16 bytes per lane, global -> LDS without registers: lane l's chunk lands at
-// LDS byte lds_base + 16*l (global_load_lds_dwordx4, M0 = LDS base).  Written
-// as inline asm so the compiler does not order every later LDS read behind
-// it; the kernel waits for these copies itself (vmcnt(0) before the barrier
-// that publishes a stage).
-// M0 is saved and restored around the copy, so the compiler's own use of M0
-// is unaffected.
-__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %2, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds_base), "v"(gptr)
-      : "memory");
+// Workgroup barrier without the fences __syncthreads adds (they would wait
+// for every load in flight); callers wait for what they need first.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-// s_waitcnt vmcnt(0) as a real instruction (not inline asm), so the compiler's
-// own wait-count tracking knows every vector-memory load has landed here.
-__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Raw buffer descriptor: byte addressing from `base`, loads at offsets >=
+// `bytes` return zero (word 3 = the gfx9-family raw-buffer format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
 
-struct DenseA {
-  u32x4 a[2][4];  // [slice in step][band]
-};
-struct SparseA {
-  u32x4 a[4];        // [band]
-  uint32_t meta[4];  // [band] both slices' index halves
-  uint32_t shift;    // 16 * slice: moves this slice's half to bits 0..15
+// A operands of one step, [.][band]: packed dense tile: a[e] = half e
+// (positions 2e, 2e+1 of every group of four); 2:4 tile: a[0] = values,
+// a[1][0] = this lane's metadata words of the wave's four bands, a[1][1..3]
+// unused; row-major W (dense baseline): a[qq] = 32-column slice qq in the
+// v_mfma_f32_16x16x32 layout.
+struct StepA {
+  u32x4 a[2][4];
 };
 
-template <bool SRC_ROWMAJOR>
-__device__ __forceinline__ void load_dense_step(DenseA& A, const uint8_t* __restrict__ src, uint64_t off, int64_t K,
-                                                int i, int j, int half, int wn, int l) {
-#pragma unroll
-  for (int qq = 0; qq < 2; qq++) {
-    const int q = 2 * half + qq;
-#pragma unroll
-    for (int bnd = 0; bnd < 4; bnd++) {
-      const int band = 4 * wn + bnd;
-      if constexpr (SRC_ROWMAJOR) {
-        const uint16_t* W = reinterpret_cast<const uint16_t*>(src);
-        A.a[qq][bnd] = ld16(W + ((int64_t)i * kTile + 16 * band + (l & 15)) * K + (int64_t)j * kTile + 32 * q +
-                            8 * (l >> 4));
-      } else {
-        A.a[qq][bnd] = ld16(src + off + (q * 8 + band) * 1024 + 16 * l);
-      }
-    }
-  }
-}
+struct PfArgs {
+  const uint8_t* src;
+  const uint16_t* X;
+  void* Y;
+  int M, N, K, NT, KT, n_mblk, n_blocks, per_xcd;
+};
 
-__device__ __forceinline__ void load_sparse_step(SparseA& A, const uint8_t* __restrict__ src, uint64_t off, int q,
-                                                 int wn, int l) {
-#pragma unroll
-  for (int bnd = 0; bnd < 4; bnd++) {
-    const int band = 4 * wn + bnd;
-    A.a[bnd] = ld16(src + off + (q * 8 + band) * 1024 + 16 * l);
-    A.meta[bnd] = *reinterpret_cast<const uint32_t*>(src + off + kSparseValBytes + 4 * (64 * band + l));
-  }
-  A.shift = 16 * q;
-}
+template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, int BM, int DIST>
+__global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
+  constexpr int kNMB = BM / 32;                       // 16-column M blocks per wave
+  constexpr int kStageBytes = BM * kPfRowBytes;       // one X stage
+  constexpr int kXChunks = kStageBytes / 16 / (kPfWaves * 64);  // 16-byte chunks a lane stages per step
+  static_assert(kNMB % kPfMGroup == 0 && kXChunks * 16 * kPfWaves * 64 == kStageBytes, "tile shape");
 
-template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32>
-__global__ __launch_bounds__(256, 2) void k_prefill(const uint8_t* __restrict__ src, const uint16_t* __restrict__ X,
-                                                    int M, int N, int K, void* __restrict__ Y, int n_mblk,
-                                                    int n_tiles, int per_xcd) {
+  static_assert(DIST == 1 || DIST == 2, "prefetch distance");
+  __shared__ __attribute__((aligned(16))) uint8_t s_x0[kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_x1[kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_x2[DIST == 2 ? kStageBytes : 16];
+  // per row-block of the pair and tile column: (byte offset >> 8) | kind << 31
+  __shared__ uint32_t s_ent[2][kPfMaxKT];
+
   const int id = blockIdx.x;
-  const int t = (id & 7) * per_xcd + (id >> 3);
-  if (t >= n_tiles) return;
-  const int i = t / n_mblk, mb = t - (t / n_mblk) * n_mblk;
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int wn = w >> 1, wm = w & 1;
-  const int KT = K / kTile;
-  const int m0 = mb * kPfBM;
-  const int h = l >> 4;
+  const int t = (id & 7) * P.per_xcd + (id >> 3);
+  if (t >= P.n_blocks) return;  // whole workgroup
+  const int p = t / P.n_mblk, mb = t - (t / P.n_mblk) * P.n_mblk;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int l = threadIdx.x & 63;
+  const int r = w >> 2, wn = (w >> 1) & 1, wm = w & 1;
+  const int hl = l >> 4;
+  const int KT = P.KT, K = P.K;
+  const int m0 = mb * BM;
+  const int i0 = p, i1 = P.NT - 1 - p;
+  const int i_mine = r == 0 ? i0 : i1;
+  const bool active = r == 0 || i1 != i0;  // a lone middle row-block has no second half
+  const int n_steps = 2 * KT;
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kPfBufBytes];
-  __shared__ uint16_t s_list[2][kPfMaxKT];
-  __shared__ int s_count[2];
-
-  const TileEntry* table = reinterpret_cast<const TileEntry*>(src + kHeaderBytes) + (int64_t)i * KT;
-  int nd, ns;
-  if constexpr (SRC_ROWMAJOR) {
-    nd = KT;
-    ns = 0;
-  } else {
-    if (w == 0) {
-      int base_d = 0, base_s = 0;
-      for (int c0 = 0; c0 < KT; c0 += 64) {
-        const int jj = c0 + l;
-        const bool valid = jj < KT;
-        const uint32_t kind = valid ? table[jj].kind : 0u;
-        const bool sp = valid && kind != 0;
-        const bool de = valid && kind == 0;
-        const uint64_t bs = __ballot(sp), bd = __ballot(de);
-        const uint64_t lt = (l == 0) ? 0ull : (~0ull >> (64 - l));
-        if (de) s_list[0][base_d + __popcll(bd & lt)] = (uint16_t)jj;
-        if (sp) s_list[1][base_s + __popcll(bs & lt)] = (uint16_t)jj;
-        base_d += __popcll(bd);
-        base_s += __popcll(bs);
-      }
-      if (l == 0) {
-        s_count[0] = base_d;
-        s_count[1] = base_s;
-      }
+  if constexpr (!SRC_ROWMAJOR) {
+    const TileEntry* table = reinterpret_cast<const TileEntry*>(P.src + kHeaderBytes);
+    for (int e = threadIdx.x; e < 2 * KT; e += kPfWaves * 64) {
+      const int rr = e >= KT ? 1 : 0;
+      const int j = e - rr * KT;
+      const TileEntry te = table[(int64_t)(rr ? i1 : i0) * KT + j];
+      s_ent[rr][j] = (uint32_t)(te.offset >> 8) | (te.kind ? 0x80000000u : 0u);
     }
     __syncthreads();
-    nd = s_count[0];
-    ns = s_count[1];
   }
-  const int n_steps = 2 * (nd + ns);
 
-  // tile column of step s (dense tiles first, then sparse ones); the K range
-  // of step s is columns 64*(s&1) .. +63 of that tile in both cases.
-  auto step_tile = [&](int s) -> int {
+  const uint32_t lane16 = 16u * (uint32_t)l;
+
+  // A operands of step s (tile column s/2, half s&1) for this wave; returns
+  // the tile kind (0 dense, 1 2:4), wave-uniform.  Both kinds issue the same
+  // eight 16-byte loads (only offsets differ), so registers and wait counts
+  // are identical on both paths.
+  auto load_a = [&](int s, StepA& A) -> uint32_t {
+    const int j = s >> 1, h = s & 1;
     if constexpr (SRC_ROWMAJOR) {
-      return s >> 1;
-    } else {
-      const int e = s >> 1;
-      return e < nd ? (int)s_list[0][e] : (int)s_list[1][e - nd];
-    }
-  };
-
-  // X stage of step s into buffer buf: 256 rows x 64 columns = 32 blocks of
-  // 1 KB (8 rows); wave w fills blocks 8w .. 8w+7.  Lane l lands at row
-  // 8*blk + l/8, chunk position l%8, so it fetches the source chunk whose
-  // swizzled position is l%8.  Rows past M repeat row M-1 (never stored).
-  auto issue_stage = [&](int s, int buf) {
-    const int j = step_tile(s);
-    const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem) + buf * kPfBufBytes;
+      // rows 64wn + 16b + (l & 15) of row-block i_mine, columns 128j + 64h + 32qq + 8hl
+      const uint8_t* W = P.src + (((int64_t)i_mine * kTile + 64 * wn) * K + (int64_t)j * kTile + 64 * h) * 2;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(W, 0xffffffffu);
+      const uint32_t lane_rm = ((uint32_t)(l & 15) * (uint32_t)K + 8u * (uint32_t)hl) * 2u;
 #pragma unroll
-    for (int u = 0; u < 8; u++) {
-      const int blk = 8 * w + u;
-      const int r = 8 * blk + (l >> 3);
-      const int c = (l & 7) ^ swz_f(r);
-      const int gm = min(m0 + r, M - 1);
-      const uint16_t* g = X + (int64_t)gm * K + (int64_t)j * kTile + 64 * (s & 1) + 8 * c;
-      lds_dma16(g, __builtin_amdgcn_readfirstlane(lds0 + 1024 * blk));
+      for (int qq = 0; qq < 2; qq++)
+#pragma unroll
+        for (int b = 0; b < 4; b++) A.a[qq][b] = bload16(rs, lane_rm, (uint32_t)(16 * b * K + 32 * qq) * 2u);
+      return 0u;
+    } else {
+      const uint32_t e = __builtin_amdgcn_readfirstlane(s_ent[r][j]);
+      const uint32_t kind = e >> 31;
+      const uint8_t* tile = P.src + ((uint64_t)(e & 0x7fffffffu) << 8);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile, kDenseTileBytes);
+      // dense: a[e][b] = half e of band 4wn+b in 64-column slice h, at
+      //        ((h*8 + 4wn + b)*2 + e) KB;
+      // 2:4  : a[0][b] = values of band 4wn+b in slice h, at (h*8 + 4wn + b) KB;
+      //        a[1][0] = metadata words of bands 4wn .. 4wn+3, at 16 KB + wn KB;
+      //        a[1][1..3] go through a zero-length descriptor (they read as
+      //        zero and move no data) at that same in-tile offset.
+      const __amdgpu_buffer_rsrc_t rz = make_rsrc(tile, kind ? 0u : (uint32_t)kDenseTileBytes);
+      const uint32_t b0 = kind ? (uint32_t)(h * 8 + 4 * wn) * 1024u : (uint32_t)(h * 8 + 4 * wn) * 2048u;
+      const uint32_t bm = (uint32_t)kSparseValBytes + 1024u * wn;
+      const uint32_t s0 = kind ? 1024u : 2048u;
+#pragma unroll
+      for (int b = 0; b < 4; b++) A.a[0][b] = bload16(rs, lane16, b0 + s0 * b);
+      A.a[1][0] = bload16(rs, lane16, kind ? bm : b0 + 1024u);
+#pragma unroll
+      for (int b = 1; b < 4; b++) A.a[1][b] = bload16(rz, lane16, kind ? bm : b0 + 1024u + 2048u * b);
+      return kind;
     }
   };
 
-  f32x4 acc[4][8];
+  // X of step s, BM rows x 64 columns = BM*8 chunks of 16 bytes: lane chunk
+  // c = u * 512 + threadIdx.x is row c / 8, stored at chunk position c % 8 of
+  // that row, so it holds the source chunk whose swizzled position is c % 8.
+  // Rows past M are outside the descriptor's range and load as zero (never
+  // stored).  Lane offsets stay below BM * K * 2 bytes (< 2^31).
+  uint32_t lane_x[kXChunks];
+#pragma unroll
+  for (int u = 0; u < kXChunks; u++) {
+    const int c = u * kPfWaves * 64 + (int)threadIdx.x;
+    const int row = c >> 3;
+    lane_x[u] = ((uint32_t)row * (uint32_t)K + 8u * (uint32_t)((c & 7) ^ swz_f(row))) * 2u;
+  }
+  const __amdgpu_buffer_rsrc_t rx =
+      make_rsrc(P.X + (int64_t)m0 * K, (uint32_t)min(BM, P.M - m0) * (uint32_t)K * 2u);
+  auto load_x = [&](int s, u32x4 (&xr)[kXChunks]) {
+    const uint32_t col = (uint32_t)((s >> 1) * kTile + 64 * (s & 1)) * 2u;
+#pragma unroll
+    for (int u = 0; u < kXChunks; u++) xr[u] = bload16(rx, lane_x[u], col);
+  };
+  auto store_x = [&](const u32x4 (&xr)[kXChunks], uint8_t* dst) {
+#pragma unroll
+    for (int u = 0; u < kXChunks; u++)
+      *reinterpret_cast<u32x4*>(dst + 16 * (u * kPfWaves * 64 + (int)threadIdx.x)) = xr[u];
+  };
+
+  f32x4 acc[4][kNMB];
 #pragma unroll
   for (int a = 0; a < 4; a++)
 #pragma unroll
-    for (int c = 0; c < 8; c++) acc[a][c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < kNMB; c++) acc[a][c] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  if (n_steps > 0) {
-    issue_stage(0, 0);
-    wait_vmem_all();
-    __syncthreads();
-  }
-
-  // ---- dense steps: s = 0 .. 2*nd-1
-  if (nd > 0) {
-    DenseA cur, nxt;
-    {
-      const int j = step_tile(0);
-      load_dense_step<SRC_ROWMAJOR>(cur, src, SRC_ROWMAJOR ? 0 : table[j].offset, K, i, j, 0, wn, l);
-      wait_vmem_all();
+  // B fragments of M blocks kPfMGroup*g .. +kPfMGroup-1: chunks hl (K 8hl..)
+  // and 4+hl (K 32+8hl..) of their rows.
+  auto read_b = [&](const uint8_t* xs, int g, u32x4 (&blo)[kPfMGroup], u32x4 (&bhi)[kPfMGroup]) {
+#pragma unroll
+    for (int mm = 0; mm < kPfMGroup; mm++) {
+      const int row = wm * (BM / 2) + (kPfMGroup * g + mm) * 16 + (l & 15);
+      blo[mm] = *reinterpret_cast<const u32x4*>(xs + swz(row, hl));
+      bhi[mm] = *reinterpret_cast<const u32x4*>(xs + swz(row, 4 + hl));
     }
-    for (int s = 0; s < 2 * nd; s++) {
-      const int buf = s & 1;
-      const bool more_dense = s + 1 < 2 * nd;
-      if (more_dense) {
-        const int j = step_tile(s + 1);
-        load_dense_step<SRC_ROWMAJOR>(nxt, src, SRC_ROWMAJOR ? 0 : table[j].offset, K, i, j, (s + 1) & 1, wn, l);
-      }
-      if (s + 1 < n_steps) issue_stage(s + 1, buf ^ 1);
-      const uint8_t* xs = smem + buf * kPfBufBytes;
+  };
+
+  // One step from stage buffer xs.
+  auto compute = [&](const StepA& A, uint32_t kind, int h, const uint8_t* xs) {
+    if (!active) return;
+    if constexpr (SRC_ROWMAJOR) {
 #pragma unroll
       for (int qq = 0; qq < 2; qq++) {
-        u32x4 bf[8];
+        u32x4 bf[kNMB];
 #pragma unroll
-        for (int mblk = 0; mblk < 8; mblk++)
-          bf[mblk] = *reinterpret_cast<const u32x4*>(xs + swz(wm * 128 + mblk * 16 + (l & 15), 4 * qq + h));
+        for (int mblk = 0; mblk < kNMB; mblk++)
+          bf[mblk] = *reinterpret_cast<const u32x4*>(xs + swz(wm * (BM / 2) + mblk * 16 + (l & 15), 4 * qq + hl));
 #pragma unroll
-        for (int mblk = 0; mblk < 8; mblk++)
+        for (int mblk = 0; mblk < kNMB; mblk++)
 #pragma unroll
-          for (int bnd = 0; bnd < 4; bnd++) acc[bnd][mblk] = mma_dense<BF16>(cur.a[qq][bnd], bf[mblk], acc[bnd][mblk]);
+          for (int b = 0; b < 4; b++) acc[b][mblk] = mma_dense<BF16>(A.a[qq][b], bf[mblk], acc[b][mblk]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      wait_vmem_all();
-      __syncthreads();
-      if (more_dense) cur = nxt;
+    } else {
+      // Both kinds on v_smfmac_f32_16x16x64 with the same B fragments: a 2:4
+      // slice once with its own codes, a dense slice twice -- half (0,1) with
+      // code 4 in every group, half (2,3) with code 14.
+      const int nsub = kind == 0 ? 2 : 1;
+      uint32_t idx0[4];
+#pragma unroll
+      for (int b = 0; b < 4; b++) idx0[b] = kind == 0 ? 0x4444u : (A.a[1][0][b] >> (16 * h));
+      // B fragments double-buffered across groups where registers allow
+      // (the 256-wide tile has no room for the second set).
+      constexpr int kGroups = kNMB / kPfMGroup;
+      constexpr bool kPipeB = BM < 256;
+      u32x4 blo[2][kPfMGroup], bhi[2][kPfMGroup];
+      if (kPipeB) read_b(xs, 0, blo[0], bhi[0]);
+#pragma unroll
+      for (int g = 0; g < kGroups; g++) {
+        if (!kPipeB) read_b(xs, g, blo[g & 1], bhi[g & 1]);
+        if (kPipeB && g + 1 < kGroups) read_b(xs, g + 1, blo[(g + 1) & 1], bhi[(g + 1) & 1]);
+        for (int sub = 0; sub < nsub; sub++) {
+#pragma unroll
+          for (int mm = 0; mm < kPfMGroup; mm++)
+#pragma unroll
+            for (int b = 0; b < 4; b++)
+              acc[b][kPfMGroup * g + mm] =
+                  mma_sparse<BF16, 0>(sub ? A.a[1][b] : A.a[0][b], blo[g & 1][mm], bhi[g & 1][mm],
+                                      acc[b][kPfMGroup * g + mm], sub ? 0xEEEEu : idx0[b]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-  }
+  };
 
-  // ---- 2:4 steps: s = 2*nd .. n_steps-1
-  if constexpr (!SRC_ROWMAJOR) {
-    if (ns > 0) {
-      SparseA cur, nxt;
-      {
-        const int j = step_tile(2 * nd);
-        load_sparse_step(cur, src, table[j].offset, 0, wn, l);
-        wait_vmem_all();
-      }
-      for (int s = 2 * nd; s < n_steps; s++) {
-        const int buf = s & 1;
-        const bool more = s + 1 < n_steps;
-        if (more) {
-          const int j = step_tile(s + 1);
-          load_sparse_step(nxt, src, table[j].offset, (s + 1) & 1, wn, l);
-          issue_stage(s + 1, buf ^ 1);
-        }
-        const uint8_t* xs = smem + buf * kPfBufBytes;
-#pragma unroll
-        for (int g4 = 0; g4 < 2; g4++) {
-          u32x4 blo[4], bhi[4];
-#pragma unroll
-          for (int mm = 0; mm < 4; mm++) {
-            const int row = wm * 128 + (4 * g4 + mm) * 16 + (l & 15);
-            blo[mm] = *reinterpret_cast<const u32x4*>(xs + swz(row, h));
-            bhi[mm] = *reinterpret_cast<const u32x4*>(xs + swz(row, 4 + h));
-          }
-#pragma unroll
-          for (int mm = 0; mm < 4; mm++)
-#pragma unroll
-            for (int bnd = 0; bnd < 4; bnd++)
-              acc[bnd][4 * g4 + mm] =
-                  mma_sparse<BF16, 0>(cur.a[bnd], blo[mm], bhi[mm], acc[bnd][4 * g4 + mm], cur.meta[bnd] >> cur.shift);
-        }
-        wait_vmem_all();
-        __syncthreads();
-        if (more) cur = nxt;
+  const int last = n_steps - 1;
+  if constexpr (DIST == 1) {
+    // ---- prologue: X of step 0 into buffer 0, A of step 0.  Every step
+    // issues the same loads (X of the next step, then its A); past the last
+    // step they repeat the last step's offsets and land in registers and a
+    // buffer nobody reads again, so the wait counts hold on every path.
+    u32x4 xr[kXChunks];
+    StepA A0, A1;
+    load_x(0, xr);
+    uint32_t k0 = load_a(0, A0), k1 = 0;
+    store_x(xr, s_x0);
+    __syncthreads();
+
+    // Step s (X buffer s % 2, A buffer s % 2): load X and A of step s+1 into
+    // registers, compute step s, write X of s+1 into the other buffer (read
+    // at step s-1; every wave has passed the barrier after it), and meet at
+    // the barrier once the LDS writes are done.
+    auto step = [&](int s, StepA& cur, uint32_t kc, StepA& nxt, uint32_t& kn, const uint8_t* xs, uint8_t* xo) {
+      load_x(min(s + 1, last), xr);
+      kn = load_a(min(s + 1, last), nxt);
+      compute(cur, kc, s & 1, xs);
+      store_x(xr, xo);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+      wg_barrier();
+    };
+    for (int s = 0; s < n_steps; s += 2) {  // n_steps is even
+      step(s, A0, k0, A1, k1, s_x0, s_x1);
+      step(s + 1, A1, k1, A0, k0, s_x1, s_x0);
+    }
+  } else {
+    // ---- two steps ahead: A of step s+2 and X of step s+2 are loaded at
+    // step s; X of s+1 (loaded at step s-1) is written to LDS at the end of
+    // step s.  Three A register sets, three X buffers, two X register sets:
+    // the pattern repeats every 6 steps.
+    u32x4 xr0[kXChunks], xr1[kXChunks];
+    StepA A0, A1, A2;
+    uint32_t k0, k1, k2 = 0;
+    load_x(0, xr0);
+    k0 = load_a(0, A0);
+    load_x(min(1, last), xr1);
+    k1 = load_a(min(1, last), A1);
+    store_x(xr0, s_x0);
+    __syncthreads();
+
+    // xl: registers receiving X of s+2; xw: registers holding X of s+1.
+    auto step = [&](int s, StepA& cur, uint32_t kc, StepA& ahead, uint32_t& ka, u32x4 (&xl)[kXChunks],
+                    const u32x4 (&xw)[kXChunks], const uint8_t* xs, uint8_t* xo) {
+      load_x(min(s + 2, last), xl);
+      ka = load_a(min(s + 2, last), ahead);
+      compute(cur, kc, s & 1, xs);
+      store_x(xw, xo);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+      wg_barrier();
+    };
+    int s = 0;
+    for (; s + 6 <= n_steps; s += 6) {
+      step(s + 0, A0, k0, A2, k2, xr0, xr1, s_x0, s_x1);
+      step(s + 1, A1, k1, A0, k0, xr1, xr0, s_x1, s_x2);
+      step(s + 2, A2, k2, A1, k1, xr0, xr1, s_x2, s_x0);
+      step(s + 3, A0, k0, A2, k2, xr1, xr0, s_x0, s_x1);
+      step(s + 4, A1, k1, A0, k0, xr0, xr1, s_x1, s_x2);
+      step(s + 5, A2, k2, A1, k1, xr1, xr0, s_x2, s_x0);
+    }
+    if (s < n_steps) {  // n_steps = 2 or 4 (mod 6): the first steps of the pattern
+      step(s + 0, A0, k0, A2, k2, xr0, xr1, s_x0, s_x1);
+      step(s + 1, A1, k1, A0, k0, xr1, xr0, s_x1, s_x2);
+      if (s + 2 < n_steps) {
+        step(s + 2, A2, k2, A1, k1, xr0, xr1, s_x2, s_x0);
+        step(s + 3, A0, k0, A2, k2, xr1, xr0, s_x0, s_x1);
       }
     }
   }
 
   // ---- epilogue: round and store Y[m][n .. n+3]
+  if (active) {
 #pragma unroll
-  for (int mblk = 0; mblk < 8; mblk++) {
-    const int m = m0 + wm * 128 + mblk * 16 + (l & 15);
-    if (m < M) {
+    for (int mblk = 0; mblk < kNMB; mblk++) {
+      const int m = m0 + wm * (BM / 2) + mblk * 16 + (l & 15);
+      if (m < P.M) {
 #pragma unroll
-      for (int bnd = 0; bnd < 4; bnd++) {
-        const int64_t n = (int64_t)i * kTile + 16 * (4 * wn + bnd) + 4 * h;
-        store4<BF16, OUT_F32>(Y, (int64_t)m * N + n, acc[bnd][mblk]);
+        for (int b = 0; b < 4; b++) {
+          const int64_t n = (int64_t)i_mine * kTile + 16 * (4 * wn + b) + 4 * hl;
+          store4<BF16, OUT_F32>(P.Y, (int64_t)m * P.N + n, acc[b][mblk]);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// Number of compute units, read once per device.
+static int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// M-block width: the grid runs in rounds of one workgroup per CU, so pick the
+// width whose last round is fullest, weighted by how well each width reuses
+// W (a narrower block re-reads W for more blocks of M).
+static int choose_bm(int64_t M, int64_t N) {
+  const int64_t pairs = (N / kTile + 1) / 2;
+  const int cus = cu_count();
+  const int widths[3] = {256, 192, 128};
+  const double reuse[3] = {1.0, 0.94, 0.85};
+  int best = 256;
+  double best_score = -1.0;
+  for (int c = 0; c < 3; c++) {
+    const int64_t mblk = (M + widths[c] - 1) / widths[c];
+    const int64_t blocks = pairs * mblk;
+    const int64_t rounds = (blocks + cus - 1) / cus;
+    const double useful = (double)M / (double)(mblk * widths[c]);
+    const double score = reuse[c] * useful * (double)blocks / (double)(rounds * cus);
+    if (score > best_score + 1e-9) {
+      best_score = score;
+      best = widths[c];
+    }
+  }
+  return best;
+}
+
+template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, int BM, int DIST>
+static hipError_t launch_prefill_bm(const void* src, const void* X, int64_t M, int64_t N, int64_t K, void* Y,
+                                    hipStream_t s) {
+  PfArgs a;
+  a.src = reinterpret_cast<const uint8_t*>(src);
+  a.X = reinterpret_cast<const uint16_t*>(X);
+  a.Y = Y;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.NT = (int)(N / kTile);
+  a.KT = (int)(K / kTile);
+  a.n_mblk = (int)((M + BM - 1) / BM);
+  a.n_blocks = ((a.NT + 1) / 2) * a.n_mblk;
+  a.per_xcd = (a.n_blocks + 7) / 8;
+  hipLaunchKernelGGL((k_prefill<BF16, SRC_ROWMAJOR, OUT_F32, BM, DIST>), dim3((unsigned)(8 * a.per_xcd)),
+                     dim3(kPfWaves * 64), 0, s, a);
+  return hipGetLastError();
 }
 
 template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32>
 static hipError_t launch_prefill_t(const void* src, const void* X, int64_t M, int64_t N, int64_t K, void* Y,
                                    hipStream_t s) {
-  const int NT = (int)(N / kTile);
-  const int n_mblk = (int)((M + kPfBM - 1) / kPfBM);
-  const int n_tiles = NT * n_mblk;
-  const int per_xcd = (n_tiles + 7) / 8;
-  hipLaunchKernelGGL((k_prefill<BF16, SRC_ROWMAJOR, OUT_F32>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s,
-                     reinterpret_cast<const uint8_t*>(src), reinterpret_cast<const uint16_t*>(X), (int)M, (int)N,
-                     (int)K, Y, n_mblk, n_tiles, per_xcd);
-  return hipGetLastError();
+  switch (choose_bm(M, N)) {
+    case 128: return launch_prefill_bm<BF16, SRC_ROWMAJOR, OUT_F32, 128, 2>(src, X, M, N, K, Y, s);
+    case 192: return launch_prefill_bm<BF16, SRC_ROWMAJOR, OUT_F32, 192, 1>(src, X, M, N, K, Y, s);
+    default: return launch_prefill_bm<BF16, SRC_ROWMAJOR, OUT_F32, 256, 1>(src, X, M, N, K, Y, s);
+  }
 }
 
 hipError_t launch_prefill(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* X, int64_t M, int64_t N,
                           int64_t K, void* Y, hipStream_t s) {
+  if (K / kTile > kPfMaxKT) return hipErrorInvalidValue;
   if (bf16) {
     if (rowmajor) return out_f32 ? launch_prefill_t<true, true, true>(src, X, M, N, K, Y, s)
                                  : launch_prefill_t<true, true, false>(src, X, M, N, K, Y, s);

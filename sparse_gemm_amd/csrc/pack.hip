@@ -1,4 +1,4 @@
-// pack.hip -- dense W + tile map + 2:4 mask -> packed blob (format version 1).
+// pack.hip -- dense W + tile map + 2:4 mask -> packed blob (format version 2).
 //
 // PATCH (arXiv 2509.23410), gist.science explainer, section 2 "Core
 // Mechanism": every 128 x 128 tile of W is dense or 2:4 sparse; section 1
@@ -7,16 +7,22 @@
 //
 // Tile data layout (the host writes the header and the tile table before
 // this kernel runs):
-//   dense tile : 2048 chunks of 16 bytes; chunk c = (q*8 + band)*64 + l holds
-//                row 16*band + l%16, columns 32*q + 8*(l/16) .. +7.
+//   dense tile : 2048 chunks of 16 bytes; chunk c = ((q*8 + band)*2 + e)*64 + l
+//                holds, of row 16*band + l%16 and the four groups of four at
+//                columns 64*q + 16*(l/16) .. +15, the elements at positions
+//                2e and 2e+1 of each group (group order, then column order):
+//                two halves that are 2:4 operands with the fixed patterns
+//                (0,1) and (2,3).
 //   sparse tile: 1024 value chunks, chunk c = (q*8 + band)*64 + l holds the two
 //                kept values (ascending column) of the groups
 //                g = 16*q + 4*(l/16) + p, p = 0..3, of row 16*band + l%16;
-//                then 512 metadata words, word band*64 + l holding group g's
-//                code i0 | i1 << 2 at bits 16*q + 4*p.
-// This is exactly the lane order of the matrix-core operands (dense A of
-// v_mfma_f32_16x16x32, sparse A and index of v_smfmac_f32_16x16x64), so the
-// GEMM kernels load each 1 KB fragment with one coalesced 16-byte load a lane.
+//                then 512 metadata words, word (band/4)*256 + 4*l + band%4
+//                holding group g's code i0 | i1 << 2 at bits 16*q + 4*p (so
+//                one 16-byte load gives lane l its words of four bands).
+// This is exactly the lane order of the A operand and index of
+// v_smfmac_f32_16x16x64, for both tile kinds, so the GEMM kernels load each
+// 1 KB fragment with one coalesced 16-byte load a lane and run dense and 2:4
+// tiles on the same instruction.
 #include "device_common.h"
 
 namespace patch {
@@ -30,11 +36,19 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, co
   const int i = t / KT, j = t - (t / KT) * KT;
   uint8_t* tile = blob + e.offset;
   if (e.kind == 0) {
-    const int c = part * 256 + threadIdx.x;  // 0 .. 2047
+    if (part >= 4) return;
+    const int c = part * 256 + threadIdx.x;  // (q, band, l), 0 .. 1023
     const int q = c >> 9, band = (c >> 6) & 7, l = c & 63;
     const int64_t row = (int64_t)i * kTile + 16 * band + (l & 15);
-    const int64_t col = (int64_t)j * kTile + 32 * q + 8 * (l >> 4);
-    st16(tile + 16 * c, ld16(W + row * K + col));
+    const int64_t col = (int64_t)j * kTile + 64 * q + 16 * (l >> 4);
+    // 16 elements = 8 words of two; group g is words 2g (positions 0, 1) and
+    // 2g+1 (positions 2, 3)
+    const u32x4 w0 = ld16(W + row * K + col), w1 = ld16(W + row * K + col + 8);
+    const u32x4 h0 = {w0[0], w0[2], w1[0], w1[2]};
+    const u32x4 h1 = {w0[1], w0[3], w1[1], w1[3]};
+    uint8_t* dst = tile + 16 * ((q * 8 + band) * 2 * 64 + l);
+    st16(dst, h0);
+    st16(dst + 1024, h1);
     return;
   }
   if (part >= 2) return;
@@ -82,7 +96,7 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, co
     u32x4 o = {outv[0], outv[1], outv[2], outv[3]};
     st16(tile + 16 * ((q * 8 + band) * 64 + l), o);
   }
-  reinterpret_cast<uint32_t*>(tile + kSparseValBytes)[pair] = meta;
+  reinterpret_cast<uint32_t*>(tile + kSparseValBytes)[(band >> 2) * 256 + 4 * l + (band & 3)] = meta;
   if (bad) atomicOr(reinterpret_cast<uint32_t*>(blob + kErrFlagOffset), 1u);
 }
 

@@ -21,7 +21,7 @@ hipError_t launch_prefill(bool bf16, bool rowmajor, bool out_f32, const void* sr
 namespace {
 
 constexpr uint32_t kMagic = 0x48435450u;  // "PTCH"
-constexpr uint32_t kVersion = 1;
+constexpr uint32_t kVersion = 2;
 constexpr int64_t kTile = 128;
 constexpr uint64_t kDenseBytes = 32768;
 constexpr uint64_t kSparseBytes = 18432;
@@ -92,7 +92,7 @@ void put64(uint8_t* p, uint64_t v) { std::memcpy(p, &v, 8); }
 
 extern "C" {
 
-int32_t patch_abi_version(void) { return 1; }
+int32_t patch_abi_version(void) { return 2; }
 
 const char* patch_status_string(patch_status s) {
   switch (s) {

@@ -129,16 +129,23 @@ def test_dense_baseline_small(dtype, M):
 
 
 @pytest.mark.parametrize("M", [5, 16, 64, 300])
-def test_all_dense_map_equals_dense_baseline_bitwise(M):
-    """An all-dense tile map runs the same arithmetic in the same order as the
-    dense baseline, so the two must agree bit for bit."""
+def test_all_dense_map_matches_dense_baseline(M):
+    """An all-dense tile map computes the same products as the dense baseline
+    (packed dense tiles run as two fixed-pattern halves on the sparse
+    instruction, the baseline on the dense one), so with fp32 output the two
+    agree to fp32 accumulation-order rounding, and both match the oracle."""
     p = inputs.make_custom("bf16", 256, 512, 9, "dense", 0.0, "top2")
     pw, W = _pack(p)
-    X = dev_bits(inputs.make_custom_x("bf16", M, 512, 3), "bf16")
+    Xb = inputs.make_custom_x("bf16", M, 512, 3)
+    X = dev_bits(Xb, "bf16")
+    ref = _ref(p, Xb)
     for v in ["prefill"] + (["decode"] if M <= 16 else []):
         a = patch.gemm(X, pw, out_dtype=torch.float32, variant=v)
         b = patch.dense_gemm(X, W, out_dtype=torch.float32, variant=v)
-        assert torch.equal(a, b), v
+        assert_close(a, ref, f32=True, what=f"hybrid all-dense M={M} {v}")
+        assert_close(b, ref, f32=True, what=f"dense M={M} {v}")
+        scale = float(b.abs().max())
+        assert float((a - b).abs().max()) <= 1e-5 * scale, v
 
 
 # ------------------------------------------------------------------ exact cases
