@@ -52,8 +52,8 @@ typedef enum { PATCH_F16 = 0, PATCH_BF16 = 1, PATCH_F32 = 2 } patch_dtype;
 
 /* GEMM variant selection for patch_gemm_ex (patch_gemm uses PATCH_VARIANT_AUTO). */
 typedef enum {
-  PATCH_VARIANT_AUTO = 0,    /* decode for M <= 16 and K <= 65536, prefill otherwise */
-  PATCH_VARIANT_DECODE = 1,  /* W-streaming kernel; valid for 1 <= M <= 16, K <= 65536
+  PATCH_VARIANT_AUTO = 0,    /* decode for M <= 128 and K <= 65536, prefill otherwise */
+  PATCH_VARIANT_DECODE = 1,  /* W-streaming kernel; valid for 1 <= M <= 128, K <= 65536
                                 (else PATCH_ERR_INVALID_ARG / PATCH_ERR_UNSUPPORTED) */
   PATCH_VARIANT_PREFILL = 2  /* output-tiled MFMA kernel; any M >= 1 */
 } patch_variant;

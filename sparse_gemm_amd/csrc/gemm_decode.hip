@@ -6,10 +6,11 @@
 // kernel streams each tile's packed bytes exactly once:
 //
 //   * one workgroup per 16-row band of W (N/16 workgroups) and all of K;
-//     wave w of the workgroup takes the tile columns j = w, w+8, w+16, ...
-//     of the band's row-block, reading each tile's offset and kind from the
-//     tile table with a scalar load (no list building, no barrier before the
-//     first weight load);
+//     wave w of the workgroup's WAVES takes the tile columns j = w,
+//     w+WAVES, ... of the band's row-block; its tile-table entries arrive
+//     with one vector load and are read with v_readlane (no list building,
+//     no barrier before the first weight load); the 8 bands of a row-block
+//     run on one XCD, so the lines they share sit in one L2;
 //   * a tile's 16 x 128 band is 4 (dense) or 2 (sparse) 1 KB fragments that a
 //     wave loads with one 16-byte load per lane each, straight into the A
 //     operand registers; X (at most 16 rows) is read from L2 into the B
@@ -17,7 +18,8 @@
 //   * both kinds run on v_smfmac_f32_16x16x64: a 2:4 tile is 2 of them (one
 //     per 64-column slice, its own index codes), a dense tile 4 (each slice
 //     as two halves with the fixed patterns (0,1) and (2,3));
-//   * loads run DEPTH tiles ahead of the matrix instructions;
+//   * loads run DEPTH tiles ahead of the matrix instructions (at K = 4096
+//     every tile of a wave is in flight at once);
 //   * the waves' fp32 partial sums are added in LDS in wave order (fixed, so
 //     results are deterministic) and rounded to the output type.
 //
@@ -27,7 +29,6 @@
 
 namespace patch {
 
-constexpr int kDecodeWaves = 8;
 
 // Registers of one tile in flight.  Both kinds issue the same eight 16-byte
 // loads (4 for X, 4 for W), so the wait counts the compiler derives stay
@@ -37,8 +38,9 @@ constexpr int kDecodeWaves = 8;
 //   sparse: a[0], a[1] = value fragments of slices 0 and 1, a[2] = this
 //           lane's 16 bytes of metadata for bands 4*(b/4) .. +3 (word b & 3
 //           is the band's), a[3] = the same chunk again (unused).
+template <int MB>
 struct DecodeFrag {
-  u32x4 x[4];  // B operand chunks: X[m][k0 + 32c + 8h .. +7], c = 0..3
+  u32x4 x[MB][4];  // B operand chunks of M block mb: X[16mb + m][k0 + 32c + 8h .. +7], c = 0..3
   u32x4 a[4];
   uint32_t kind;
 };
@@ -48,81 +50,105 @@ struct DecodeFrag {
 // cache lines as the A load) instead of a predicated load (which would make
 // the compiler wait for it right away) or all hitting row 0 of X (a hot spot
 // when M is 1).
-template <bool SRC_ROWMAJOR>
-__device__ __forceinline__ void decode_load(DecodeFrag& f, const uint8_t* __restrict__ src, uint64_t off,
+template <bool SRC_ROWMAJOR, int MB>
+__device__ __forceinline__ void decode_load(DecodeFrag<MB>& f, const uint8_t* __restrict__ src, uint64_t off,
                                             uint32_t kind, const uint16_t* __restrict__ X, int K, int M, int i, int b,
                                             int j, int l) {
-  const int m = l & 15, h = l >> 4;
-  const bool mok = m < M;
-  const uint16_t* xr = X + (int64_t)m * K + (int64_t)j * kTile + 8 * h;
+  const int h = l >> 4;
+  const uint8_t* ap[4];
   if constexpr (SRC_ROWMAJOR) {
     const uint16_t* W = reinterpret_cast<const uint16_t*>(src);
-    const uint16_t* wr = W + ((int64_t)i * kTile + 16 * b + m) * K + (int64_t)j * kTile + 8 * h;
+    const uint8_t* wr = reinterpret_cast<const uint8_t*>(W + ((int64_t)i * kTile + 16 * b + (l & 15)) * K +
+                                                         (int64_t)j * kTile + 8 * h);
 #pragma unroll
-    for (int c = 0; c < 4; c++) f.x[c] = ld16(mok ? xr + 32 * c : wr + 32 * c);
-#pragma unroll
-    for (int c = 0; c < 4; c++) f.a[c] = ld16(wr + 32 * c);
+    for (int c = 0; c < 4; c++) ap[c] = wr + 64 * c;
     f.kind = 0;
   } else {
     const uint8_t* tp = src + off + 16 * l;
     const uint8_t* mp = src + off + kSparseValBytes + 1024 * (b >> 2) + 16 * l;
     const uint8_t* dp = tp + 2048 * b;  // dense: halves of slice 0, then slice 1
-    const uint8_t* ap[4] = {kind ? tp + 1024 * b : dp, kind ? tp + 8192 + 1024 * b : dp + 1024, kind ? mp : dp + 16384,
-                            kind ? mp : dp + 17408};
-#pragma unroll
-    for (int c = 0; c < 4; c++)
-      f.x[c] = ld16(mok ? reinterpret_cast<const uint8_t*>(xr + 32 * c) : ap[c]);
+    ap[0] = kind ? tp + 1024 * b : dp;
+    ap[1] = kind ? tp + 8192 + 1024 * b : dp + 1024;
+    ap[2] = kind ? mp : dp + 16384;
+    ap[3] = kind ? mp : dp + 17408;
     f.kind = kind;
-#pragma unroll
-    for (int c = 0; c < 4; c++) f.a[c] = ld16(ap[c]);
   }
+#pragma unroll
+  for (int mb = 0; mb < MB; mb++) {
+    const int m = 16 * mb + (l & 15);
+    const uint8_t* xr = reinterpret_cast<const uint8_t*>(X + (int64_t)m * K + (int64_t)j * kTile + 8 * h);
+#pragma unroll
+    for (int c = 0; c < 4; c++) f.x[mb][c] = ld16(m < M ? xr + 64 * c : ap[c]);
+  }
+#pragma unroll
+  for (int c = 0; c < 4; c++) f.a[c] = ld16(ap[c]);
 }
 
-template <bool BF16, bool SRC_ROWMAJOR>
-__device__ __forceinline__ f32x4 decode_mma(const DecodeFrag& f, f32x4 acc, int b) {
+template <bool BF16, bool SRC_ROWMAJOR, int MB>
+__device__ __forceinline__ void decode_mma(const DecodeFrag<MB>& f, f32x4 (&acc)[MB], int b) {
   if constexpr (SRC_ROWMAJOR) {
 #pragma unroll
-    for (int c = 0; c < 4; c++) acc = mma_dense<BF16>(f.a[c], f.x[c], acc);
+    for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+      for (int c = 0; c < 4; c++) acc[mb] = mma_dense<BF16>(f.a[c], f.x[mb][c], acc[mb]);
   } else if (f.kind == 0) {
     // slice q: halves with positions (0,1) (code 4) and (2,3) (code 14)
 #pragma unroll
-    for (int q = 0; q < 2; q++) {
-      acc = mma_sparse<BF16, 0>(f.a[2 * q], f.x[2 * q], f.x[2 * q + 1], acc, 0x4444u);
-      acc = mma_sparse<BF16, 0>(f.a[2 * q + 1], f.x[2 * q], f.x[2 * q + 1], acc, 0xEEEEu);
-    }
+    for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+      for (int q = 0; q < 2; q++) {
+        acc[mb] = mma_sparse<BF16, 0>(f.a[2 * q], f.x[mb][2 * q], f.x[mb][2 * q + 1], acc[mb], 0x4444u);
+        acc[mb] = mma_sparse<BF16, 0>(f.a[2 * q + 1], f.x[mb][2 * q], f.x[mb][2 * q + 1], acc[mb], 0xEEEEu);
+      }
   } else {
     // the band's word of the lane's metadata chunk (b is the same in every
     // lane: uniform selects, not a dynamic vector index, which would put the
     // fragment array in scratch memory)
     const u32x4 mc = f.a[2];
     const uint32_t meta = (b & 2) ? ((b & 1) ? mc[3] : mc[2]) : ((b & 1) ? mc[1] : mc[0]);
-    // slice 0: logical K 0..63 of the tile -> B chunks 0 (K 8h..) and 1 (K 32+8h..)
-    acc = mma_sparse<BF16, 0>(f.a[0], f.x[0], f.x[1], acc, meta);
-    // slice 1: logical K 64..127 -> B chunks 2 and 3
-    acc = mma_sparse<BF16, 1>(f.a[1], f.x[2], f.x[3], acc, meta);
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++) {
+      // slice 0: logical K 0..63 of the tile -> B chunks 0 (K 8h..) and 1 (K 32+8h..)
+      acc[mb] = mma_sparse<BF16, 0>(f.a[0], f.x[mb][0], f.x[mb][1], acc[mb], meta);
+      // slice 1: logical K 64..127 -> B chunks 2 and 3
+      acc[mb] = mma_sparse<BF16, 1>(f.a[1], f.x[mb][2], f.x[mb][3], acc[mb], meta);
+    }
   }
-  return acc;
 }
 
-template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, int DEPTH>
-__global__ __launch_bounds__(kDecodeWaves * 64) void k_decode(const uint8_t* __restrict__ src,
-                                                               const uint16_t* __restrict__ X, int M, int N, int K,
-                                                               void* __restrict__ Y) {
+// WAVES waves per workgroup (tile columns split between them); XCD_MAP puts
+// the 8 bands of a row-block on one XCD (blocks are dealt to the 8 XCDs in
+// turn), so lines they share -- the 2:4 metadata, X -- are fetched into one L2.
+template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, int WAVES, int DEPTH, bool XCD_MAP, int MB>
+__global__ __launch_bounds__(WAVES * 64) void k_decode(const uint8_t* __restrict__ src,
+                                                        const uint16_t* __restrict__ X, int M, int N, int K,
+                                                        void* __restrict__ Y) {
+  constexpr int kDecodeWaves = WAVES;
   const int KT = K / kTile;
-  const int band_g = blockIdx.x;  // 16-row band of W
-  const int i = band_g >> 3, b = band_g & 7;
+  const int bid = blockIdx.x;
+  const int full = (N / kTile / 8) * 64;  // blocks in complete groups of 8 row-blocks
+  int i, b;                               // row-block and 16-row band of W
+  if (XCD_MAP && bid < full) {
+    i = (bid & 7) + 8 * (bid >> 6);
+    b = (bid >> 3) & 7;
+  } else {
+    i = bid >> 3;
+    b = bid & 7;
+  }
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = threadIdx.x & 63;
   const TileEntry* table = reinterpret_cast<const TileEntry*>(src + kHeaderBytes) + (int64_t)i * KT;
 
-  __shared__ f32x4 s_red[kDecodeWaves][64];
+  __shared__ f32x4 s_red[kDecodeWaves * MB][64];
 
   // wave w takes tile columns j = w, w + 8, w + 16, ... of its row-block
   // (at most 64 of them: K <= 65536).  Their table entries arrive with one
   // vector load (lane t holds the entry of the wave's t-th tile) and are read
   // with v_readlane.
   const int n_mine = (KT - w + kDecodeWaves - 1) / kDecodeWaves;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; mb++) acc[mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
   if (n_mine > 0) {
     u32x4 ents = {0u, 0u, 0u, 0u};
     if constexpr (!SRC_ROWMAJOR) ents = ld16(table + w + kDecodeWaves * min(l, n_mine - 1));
@@ -137,14 +163,14 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void k_decode(const uint8_t* __r
         kind = (uint32_t)__builtin_amdgcn_readlane((int)ents[2], lane);
       }
     };
-    DecodeFrag f[DEPTH];
+    DecodeFrag<MB> f[DEPTH];
 #pragma unroll
     for (int s = 0; s < DEPTH; s++) {
       const int t = min(s, n_mine - 1);
       uint64_t off;
       uint32_t kind;
       entry(t, off, kind);
-      decode_load<SRC_ROWMAJOR>(f[s], src, off, kind, X, K, M, i, b, w + kDecodeWaves * t, l);
+      decode_load<SRC_ROWMAJOR, MB>(f[s], src, off, kind, X, K, M, i, b, w + kDecodeWaves * t, l);
     }
     // steady state: compute the DEPTH slots, refilling each with the tile
     // DEPTH further on (clamped to the last tile: a redundant, cached load)
@@ -152,28 +178,30 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void k_decode(const uint8_t* __r
     for (; t0 + DEPTH < n_mine; t0 += DEPTH) {
 #pragma unroll
       for (int s = 0; s < DEPTH; s++) {
-        acc = decode_mma<BF16, SRC_ROWMAJOR>(f[s], acc, b);
+        decode_mma<BF16, SRC_ROWMAJOR, MB>(f[s], acc, b);
         const int tn = min(t0 + s + DEPTH, n_mine - 1);
         uint64_t off;
         uint32_t kind;
         entry(tn, off, kind);
-        decode_load<SRC_ROWMAJOR>(f[s], src, off, kind, X, K, M, i, b, w + kDecodeWaves * tn, l);
+        decode_load<SRC_ROWMAJOR, MB>(f[s], src, off, kind, X, K, M, i, b, w + kDecodeWaves * tn, l);
       }
     }
     // last round: no refills
 #pragma unroll
     for (int s = 0; s < DEPTH; s++)
-      if (t0 + s < n_mine) acc = decode_mma<BF16, SRC_ROWMAJOR>(f[s], acc, b);
+      if (t0 + s < n_mine) decode_mma<BF16, SRC_ROWMAJOR, MB>(f[s], acc, b);
   }
 
-  // ---- fixed-order reduction over waves, then round and store
-  s_red[w][l] = acc;
-  __syncthreads();
-  if (w == 0) {
-    f32x4 sum = s_red[0][l];
+  // ---- fixed-order reduction over waves (wave w < MB adds up M block w),
+  // then round and store
 #pragma unroll
-    for (int ww = 1; ww < kDecodeWaves; ww++) sum += s_red[ww][l];
-    const int m = l & 15;
+  for (int mb = 0; mb < MB; mb++) s_red[w * MB + mb][l] = acc[mb];
+  __syncthreads();
+  if (w < MB) {
+    f32x4 sum = s_red[w][l];
+#pragma unroll
+    for (int ww = 1; ww < kDecodeWaves; ww++) sum += s_red[ww * MB + w][l];
+    const int m = 16 * w + (l & 15);
     if (m < M) {
       const int64_t n = (int64_t)i * kTile + 16 * b + 4 * (l >> 4);
       store4<BF16, OUT_F32>(Y, (int64_t)m * N + n, sum);
@@ -181,14 +209,28 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void k_decode(const uint8_t* __r
   }
 }
 
+template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, int WAVES, int DEPTH, bool XCD_MAP, int MB>
+static hipError_t launch_decode_v(const void* src, const void* X, int64_t M, int64_t N, int64_t K, void* Y,
+                                  hipStream_t s) {
+  const unsigned grid = (unsigned)(N / 16);
+  hipLaunchKernelGGL((k_decode<BF16, SRC_ROWMAJOR, OUT_F32, WAVES, DEPTH, XCD_MAP, MB>), dim3(grid),
+                     dim3(WAVES * 64), 0, s, reinterpret_cast<const uint8_t*>(src),
+                     reinterpret_cast<const uint16_t*>(X), (int)M, (int)N, (int)K, Y);
+  return hipGetLastError();
+}
+
 template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32>
 static hipError_t launch_decode_t(const void* src, const void* X, int64_t M, int64_t N, int64_t K, void* Y,
                                   hipStream_t s) {
-  const unsigned grid = (unsigned)(N / 16);
-  hipLaunchKernelGGL((k_decode<BF16, SRC_ROWMAJOR, OUT_F32, 4>), dim3(grid), dim3(kDecodeWaves * 64), 0, s,
-                     reinterpret_cast<const uint8_t*>(src), reinterpret_cast<const uint16_t*>(X), (int)M, (int)N,
-                     (int)K, Y);
-  return hipGetLastError();
+  // M <= 16: 16 waves (two tile columns each at K = 4096, all in flight at
+  // once) and the 8 bands of a row-block on one XCD -- the fastest of the
+  // measured arrangements on the q_proj decode shape.  More tokens: MB column
+  // blocks of 16 per wave on 8 waves, one tile ahead (X is re-read from L2 by
+  // every band, which the 16 < M <= 128 range affords).
+  if (M <= 16) return launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, 16, 2, true, 1>(src, X, M, N, K, Y, s);
+  if (M <= 32) return launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, 8, 2, true, 2>(src, X, M, N, K, Y, s);
+  if (M <= 64) return launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, 8, 1, true, 4>(src, X, M, N, K, Y, s);
+  return launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, 8, 1, true, 8>(src, X, M, N, K, Y, s);
 }
 
 hipError_t launch_decode(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* X, int64_t M, int64_t N,

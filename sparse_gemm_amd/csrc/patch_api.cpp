@@ -28,6 +28,7 @@ constexpr uint64_t kSparseBytes = 18432;
 constexpr int64_t kMaxDim = int64_t(1) << 20;  // N, K upper bound (int32 indexing inside kernels)
 constexpr int64_t kMaxKT = 1024;              // prefill kernel's per-workgroup tile lists
 constexpr int64_t kDecodeMaxK = 65536;        // decode kernel: <= 64 tile columns per wave
+constexpr int64_t kDecodeMaxM = 128;          // decode kernel: <= 8 blocks of 16 columns of M
 constexpr uint64_t kErrFlagOffset = 252;
 
 thread_local std::string g_err;
@@ -230,8 +231,8 @@ static patch_status gemm_common(bool rowmajor, patch_dtype dt, int64_t M, int64_
   if (M < 0 || M > (int64_t)0x7fffffff) return fail(PATCH_ERR_INVALID_ARG, "M=%lld out of range", (long long)M);
   if (variant < PATCH_VARIANT_AUTO || variant > PATCH_VARIANT_PREFILL)
     return fail(PATCH_ERR_INVALID_ARG, "unknown variant %d", (int)variant);
-  if (variant == PATCH_VARIANT_DECODE && M > 16)
-    return fail(PATCH_ERR_INVALID_ARG, "decode variant needs M <= 16 (M=%lld)", (long long)M);
+  if (variant == PATCH_VARIANT_DECODE && M > kDecodeMaxM)
+    return fail(PATCH_ERR_INVALID_ARG, "decode variant needs M <= %lld (M=%lld)", (long long)kDecodeMaxM, (long long)M);
   if (M == 0) return PATCH_OK;
   if (!src || !X_dev || !Y_dev) return fail(PATCH_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned16(src) || !aligned16(X_dev) || !aligned16(Y_dev))
@@ -239,7 +240,7 @@ static patch_status gemm_common(bool rowmajor, patch_dtype dt, int64_t M, int64_
   if (variant == PATCH_VARIANT_DECODE && K > kDecodeMaxK)
     return fail(PATCH_ERR_UNSUPPORTED, "decode variant needs K <= %lld (K=%lld)", (long long)kDecodeMaxK, (long long)K);
   const bool decode =
-      variant == PATCH_VARIANT_DECODE || (variant == PATCH_VARIANT_AUTO && M <= 16 && K <= kDecodeMaxK);
+      variant == PATCH_VARIANT_DECODE || (variant == PATCH_VARIANT_AUTO && M <= kDecodeMaxM && K <= kDecodeMaxK);
   const bool bf16 = dt == PATCH_BF16, f32out = y_dtype == PATCH_F32;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = decode ? patch::launch_decode(bf16, rowmajor, f32out, src, X_dev, M, N, K, Y_dev, st)

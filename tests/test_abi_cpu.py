@@ -73,10 +73,10 @@ def test_bad_arguments_rejected_before_launch():
     # dense gemm: y dtype must be the input dtype or F32
     assert patch.STATUS[lib.patch_dense_gemm(1, 4, 256, 256, V(16), V(16), V(16), 0, None, 0, None)] == \
         "PATCH_ERR_INVALID_ARG"
-    # M < 0, decode variant with M > 16, unknown variant
+    # M < 0, decode variant with M > 128, unknown variant
     assert patch.STATUS[lib.patch_dense_gemm(1, -1, 256, 256, V(16), V(16), V(16), 1, None, 0, None)] == \
         "PATCH_ERR_INVALID_ARG"
-    assert patch.STATUS[lib.patch_dense_gemm_ex(1, 17, 256, 256, V(16), V(16), V(16), 1, None, 0, 1, None)] == \
+    assert patch.STATUS[lib.patch_dense_gemm_ex(1, 129, 256, 256, V(16), V(16), V(16), 1, None, 0, 1, None)] == \
         "PATCH_ERR_INVALID_ARG"
     assert patch.STATUS[lib.patch_dense_gemm_ex(1, 4, 256, 256, V(16), V(16), V(16), 1, None, 0, 9, None)] == \
         "PATCH_ERR_INVALID_ARG"

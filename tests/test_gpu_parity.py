@@ -92,7 +92,7 @@ def test_pack_rejects_illegal_mask_on_gpu():
 
 
 # ------------------------------------------------------------------ GEMM, small shapes
-SMALL_M = [1, 2, 3, 4, 7, 15, 16, 17, 31, 100, 255, 256, 257, 300]
+SMALL_M = [1, 2, 3, 4, 7, 15, 16, 17, 31, 33, 48, 64, 65, 100, 128, 129, 255, 256, 257, 300]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
@@ -106,7 +106,7 @@ def test_gemm_small_ragged(dtype, M):
     Xb = inputs.make_custom_x(dtype, M, 640, M)
     X = dev_bits(Xb, dtype)
     ref = _ref(p, Xb)
-    variants = ["auto", "prefill"] + (["decode"] if M <= 16 else [])
+    variants = ["auto", "prefill"] + (["decode"] if M <= 128 else [])
     for v in variants:
         y = patch.gemm(X, pw, variant=v)
         assert_close(y, ref, what=f"{dtype} M={M} {v}")
@@ -122,7 +122,7 @@ def test_dense_baseline_small(dtype, M):
     Xb = inputs.make_custom_x(dtype, M, 640, M + 1)
     X = dev_bits(Xb, dtype)
     ref = _ref(p, Xb)
-    for v in ["auto", "prefill"] + (["decode"] if M <= 16 else []):
+    for v in ["auto", "prefill"] + (["decode"] if M <= 128 else []):
         assert_close(patch.dense_gemm(X, W, variant=v), ref, what=f"dense {dtype} M={M} {v}")
         assert_close(patch.dense_gemm(X, W, out_dtype=torch.float32, variant=v), ref, f32=True,
                      what=f"dense {dtype} M={M} {v} f32")
@@ -139,7 +139,7 @@ def test_all_dense_map_matches_dense_baseline(M):
     Xb = inputs.make_custom_x("bf16", M, 512, 3)
     X = dev_bits(Xb, "bf16")
     ref = _ref(p, Xb)
-    for v in ["prefill"] + (["decode"] if M <= 16 else []):
+    for v in ["prefill"] + (["decode"] if M <= 128 else []):
         a = patch.gemm(X, pw, out_dtype=torch.float32, variant=v)
         b = patch.dense_gemm(X, W, out_dtype=torch.float32, variant=v)
         assert_close(a, ref, f32=True, what=f"hybrid all-dense M={M} {v}")
@@ -162,14 +162,15 @@ def test_identity_x_gives_masked_weights_exactly(dtype):
     # prefill: all K rows at once
     y = patch.gemm(dev_bits(eye, dtype), pw, variant="prefill")
     assert np.array_equal(host_f64(y).T, Weff)
-    # decode: 16 rows at a time
-    for k0 in range(0, p.K, 16):
-        y = patch.gemm(dev_bits(eye[k0:k0 + 16], dtype), pw, variant="decode")
-        assert np.array_equal(host_f64(y).T, Weff[:, k0:k0 + 16]), k0
+    # decode: 16 rows at a time (one block of M), then 128 (eight blocks)
+    for rows in (16, 128):
+        for k0 in range(0, p.K, rows):
+            y = patch.gemm(dev_bits(eye[k0:k0 + rows], dtype), pw, variant="decode")
+            assert np.array_equal(host_f64(y).T, Weff[:, k0:k0 + rows]), (rows, k0)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("M", [3, 16, 200])
+@pytest.mark.parametrize("M", [3, 16, 40, 128, 200])
 def test_small_integers_exact_in_f32(dtype, M):
     """|x|, |w| <= 2 and K <= 4096: every partial sum is an integer below 2^24,
     so any fp32 summation order is exact and must equal the oracle."""
@@ -180,7 +181,7 @@ def test_small_integers_exact_in_f32(dtype, M):
     Xb = inputs.to_bits(rng.integers(-2, 3, (M, K)).astype(np.float64), dtype)
     pw, _ = _pack(p)
     ref = _ref(p, Xb)
-    for v in ["prefill"] + (["decode"] if M <= 16 else []):
+    for v in ["prefill"] + (["decode"] if M <= 128 else []):
         y = patch.gemm(dev_bits(Xb, dtype), pw, out_dtype=torch.float32, variant=v)
         assert np.array_equal(host_f64(y), ref), v
 
@@ -201,18 +202,19 @@ def test_six_patterns_every_lane_slot():
     ref = oracle.gemm_f64("bf16", eye, w, tm, mask)
     y = patch.gemm(dev_bits(eye, "bf16"), pw, out_dtype=torch.float32, variant="prefill")
     assert np.array_equal(host_f64(y), ref)
-    for k0 in range(0, K, 16):
-        y = patch.gemm(dev_bits(eye[k0:k0 + 16], "bf16"), pw, out_dtype=torch.float32, variant="decode")
-        assert np.array_equal(host_f64(y), ref[k0:k0 + 16])
+    for rows in (16, 32, 64, 128):
+        for k0 in range(0, K, rows):
+            y = patch.gemm(dev_bits(eye[k0:k0 + rows], "bf16"), pw, out_dtype=torch.float32, variant="decode")
+            assert np.array_equal(host_f64(y), ref[k0:k0 + rows]), (rows, k0)
 
 
 # ------------------------------------------------------------------ robustness
 def test_output_guard_bands_untouched():
     p = inputs.make_custom("bf16", 384, 640, 12, "bernoulli", 0.5, "top2")
     pw, _ = _pack(p)
-    for M in (7, 300):
+    for M in (7, 70, 300):
         X = dev_bits(inputs.make_custom_x("bf16", M, 640, 1), "bf16")
-        for v in ["prefill"] + (["decode"] if M <= 16 else []):
+        for v in ["prefill"] + (["decode"] if M <= 128 else []):
             pad = 4096
             buf = torch.full((M * 384 + 2 * pad,), 12345.0, dtype=torch.float32, device="cuda")
             y = buf[pad:pad + M * 384].view(M, 384)
@@ -235,7 +237,7 @@ def test_blob_guard_bands_untouched():
 def test_deterministic_repeat():
     p = inputs.make_weights(inputs.CONFIGS["decode"], 0, 0)
     pw, _ = _pack(p)
-    for M in (16, 512):
+    for M in (16, 128, 512):
         X = dev_bits(inputs.make_x(inputs.CONFIGS["decode"], M, p.K), "bf16")
         a = patch.gemm(X, pw, out_dtype=torch.float32)
         b = patch.gemm(X, pw, out_dtype=torch.float32)
