@@ -36,7 +36,7 @@
  * ascending order in binary64, so the result does not depend on the number
  * of threads (OpenMP splits the work over output rows n only).
  *
- * The packed format is the repository's own (format version 2): the pages fix
+ * The packed format is the repository's own (format version 3): the pages fix
  * only the tile shape (128 x 128 execution tiles, gist.science explainer,
  * section 4 "Ablation Studies"), the six 2:4 patterns (section 2, "Pattern
  * Selection") and nothing about bytes.  oracle_pack() writes it from its
@@ -253,48 +253,54 @@ void oracle_round_f64(int dtype, int64_t n, const double* in, uint16_t* out) {
 }
 
 /* ---------------------------------------------------------------------------
- * Packed format, version 2 (the repository's own format; restated here).
+ * Packed format, version 3 (the repository's own format; restated here).
  *
  * Tile edge b = 128 in both directions; NT = N/128, KT = K/128, T = NT*KT.
  * Little-endian.  All bytes not written below are zero.
  *
  * Header, 256 bytes at offset 0:
- *   u32 magic 0x48435450, u32 version 2, u32 dtype (0 f16, 1 bf16),
+ *   u32 magic 0x48435450, u32 version 3, u32 dtype (0 f16, 1 bf16),
  *   u32 tile_n 128, u32 tile_k 128, u32 N, u32 K, u32 NT, u32 KT,
  *   u32 n_sparse, u64 table_offset (= 256), u64 data_offset,
  *   u64 data_bytes, u64 total_bytes.
+ * Data at data_offset = round_up(256 + 16*T, 256).
+ *
+ * A "band" is 16 consecutive rows of a row-block (b = 0..7); a "piece" is
+ * one band of one tile: 4096 bytes for a dense tile, 2304 for a sparse one.
+ * Row-block i takes 8 * S_i bytes, S_i = sum over its tiles of the piece
+ * sizes (the band stride); row-blocks follow each other.  Inside row-block
+ * i, band b's pieces of tiles j = 0 .. KT-1 are back to back, and band b
+ * starts S_i bytes after band b-1.
  * Tile table at 256: T entries of 16 bytes, tile (i, j) at index i*KT + j:
- *   u64 byte offset of the tile's data from the start of the blob,
- *   u32 kind (0 dense, 1 sparse), u32 zero.
- * Data at data_offset = round_up(256 + 16*T, 256): tiles in table order,
- * back to back; a dense tile takes 32768 bytes, a sparse one 18432 bytes.
+ *   u64 byte offset (from the start of the blob) of the tile's band-0 piece,
+ *   u32 kind (0 dense, 1 sparse), u32 S_i.
+ * So band b's piece of tile (i, j) starts at entry offset + b * S_i.
  *
- * Inside a tile, a "band" is 16 consecutive rows (b = 0..7) and a "lane" is
- * a number l = 0..63 with row-in-band r = l mod 16 and column group h = l / 16.
+ * Inside a piece a "lane" is a number l = 0..63 with row-in-band
+ * r = l mod 16 and column group h = l / 16; a chunk is 16 bytes, lane l's
+ * chunk of a 1024-byte block sits at byte 16*l.
  *
- * Dense tile: 2 slices q of 64 columns; lane l covers the 16 columns
- *   64*q + 16*(l/16) .. +15 of row 16*band + (l mod 16), i.e. four groups of
- *   four g = 0..3.  Chunk (q, band, e, l), e = 0 or 1, holds the elements at
- *   positions 2e and 2e+1 of those four groups: element 2*g + u (u = 0, 1) is
- *   column 64*q + 16*(l/16) + 4*g + 2*e + u.  Chunk index
- *   = ((q*8 + band)*2 + e)*64 + l, 16 bytes each.  (Each half is a 2:4 operand
- *   with the fixed pattern (0,1) or (2,3), so a dense tile runs on the same
- *   sparse matrix instruction as a 2:4 tile.)
- * Sparse tile: groups of four columns g = 0..31 (columns 4g..4g+3).
- *   Values: 2 slices q of 16 groups; chunk (q, band, l) holds, for
- *   p = 0..3 and group g = 16*q + 4*(l/16) + p, the two kept elements of row
- *   16*band + (l mod 16) in ascending column order -- 8 elements, 16 bytes.
- *   Chunk index = (q*8 + band)*64 + l; 16384 bytes in all.
- *   Metadata, 2048 bytes after the values: a u32 per (band, l) at
- *   index (band/4)*256 + 4*l + (band mod 4), so the 16 bytes at
- *   (band/4)*1024 + 16*l hold lane l's words of four consecutive bands.
- *   Bits 16*q + 4*p .. +3 hold the code of group
- *   g = 16*q + 4*(l/16) + p of that row; code = i0 | (i1 << 2), i0 < i1 the
- *   positions (0..3) of the two kept elements inside the group.
+ * Dense piece: blocks (q, e) at byte 2048*q + 1024*e, q = 0, 1 (64-column
+ *   slice), e = 0, 1 (half).  Lane l of block (q, e) holds, of row
+ *   16*band + r and the four groups of four g = 0..3 at columns
+ *   64*q + 16*h .. +15, the elements at positions 2e and 2e+1: element
+ *   2*g + u (u = 0, 1) is column 64*q + 16*h + 4*g + 2*e + u.  (Each half is
+ *   a 2:4 operand with the fixed pattern (0,1) or (2,3), so a dense tile runs
+ *   on the same sparse matrix instruction as a 2:4 tile.)
+ * Sparse piece: groups of four columns g = 0..31 (columns 4g..4g+3).
+ *   Values: block q (q = 0, 1) at byte 1024*q; lane l holds, for p = 0..3
+ *   and group g = 16*q + 4*h + p, the two kept elements of row 16*band + r in
+ *   ascending column order -- 8 elements, 16 bytes.
+ *   Metadata at byte 2048: a u32 per lane l at 2048 + 4*l.  Bits
+ *   16*q + 4*p .. +3 hold the code of group g = 16*q + 4*h + p of that row;
+ *   code = i0 | (i1 << 2), i0 < i1 the positions (0..3) of the two kept
+ *   elements inside the group.
  * ------------------------------------------------------------------------- */
 #define PT_B 128
 #define PT_DENSE_BYTES 32768u
 #define PT_SPARSE_BYTES 18432u
+#define PT_DENSE_PIECE 4096u
+#define PT_SPARSE_PIECE 2304u
 
 static uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
@@ -333,7 +339,7 @@ int oracle_pack(int dtype, int64_t N, int64_t K, const uint16_t* W, const uint8_
   for (int64_t t = 0; t < T; t++) ns += tile_map[t] != 0;
   uint64_t data_off = round_up(256 + 16 * (uint64_t)T, 256);
   put32(out + 0, 0x48435450u);
-  put32(out + 4, 2);
+  put32(out + 4, 3);
   put32(out + 8, (uint32_t)dtype);
   put32(out + 12, PT_B);
   put32(out + 16, PT_B);
@@ -347,33 +353,33 @@ int oracle_pack(int dtype, int64_t N, int64_t K, const uint16_t* W, const uint8_
   put64(out + 56, total - data_off);
   put64(out + 64, total);
 
-  uint64_t off = data_off;
+  uint64_t rb = data_off;  /* start of the current row-block */
   for (int64_t i = 0; i < NT; i++) {
+    uint64_t stride = 0;     /* S_i */
+    for (int64_t j = 0; j < KT; j++) stride += tile_map[i * KT + j] ? PT_SPARSE_PIECE : PT_DENSE_PIECE;
+    uint64_t prefix = 0;     /* offset of tile j's piece inside a band */
     for (int64_t j = 0; j < KT; j++) {
       int64_t t = i * KT + j;
       int sparse = tile_map[t] != 0;
-      put64(out + 256 + 16 * t, off);
+      put64(out + 256 + 16 * t, rb + prefix);
       put32(out + 256 + 16 * t + 8, (uint32_t)sparse);
-      uint8_t* tile = out + off;
-      if (!sparse) {
-        for (int q = 0; q < 2; q++)
-          for (int band = 0; band < 8; band++)
+      put32(out + 256 + 16 * t + 12, (uint32_t)stride);
+      for (int band = 0; band < 8; band++) {
+        uint8_t* piece = out + rb + (uint64_t)band * stride + prefix;
+        if (!sparse) {
+          for (int q = 0; q < 2; q++)
             for (int e = 0; e < 2; e++)
               for (int l = 0; l < 64; l++)
                 for (int g = 0; g < 4; g++)
                   for (int u = 0; u < 2; u++) {
                     int64_t row = i * PT_B + 16 * band + (l % 16);
                     int64_t col = j * PT_B + 64 * q + 16 * (l / 16) + 4 * g + 2 * e + u;
-                    int64_t chunk = (((int64_t)q * 8 + band) * 2 + e) * 64 + l;
-                    put16(tile + 16 * chunk + 2 * (2 * g + u), W[row * K + col]);
+                    put16(piece + 2048 * q + 1024 * e + 16 * l + 2 * (2 * g + u), W[row * K + col]);
                   }
-        off += PT_DENSE_BYTES;
-      } else {
-        for (int q = 0; q < 2; q++)
-          for (int band = 0; band < 8; band++)
+        } else {
+          for (int q = 0; q < 2; q++)
             for (int l = 0; l < 64; l++) {
               int64_t row = i * PT_B + 16 * band + (l % 16);
-              int64_t chunk = ((int64_t)q * 8 + band) * 64 + l;
               for (int p = 0; p < 4; p++) {
                 int g = 16 * q + 4 * (l / 16) + p;
                 int64_t c0 = j * PT_B + 4 * g;
@@ -381,21 +387,23 @@ int oracle_pack(int dtype, int64_t N, int64_t K, const uint16_t* W, const uint8_
                 int pos[2] = {0, 0};
                 for (int d = 0; d < 4; d++)
                   if (mask[row * K + c0 + d]) {
-                    put16(tile + 16 * chunk + 2 * (2 * p + s), W[row * K + c0 + d]);
+                    put16(piece + 1024 * q + 16 * l + 2 * (2 * p + s), W[row * K + c0 + d]);
                     pos[s] = d;
                     s++;
                   }
                 uint32_t code = (uint32_t)pos[0] | ((uint32_t)pos[1] << 2);
-                uint8_t* meta = tile + 16384 + 4 * ((band / 4) * 256 + 4 * l + band % 4);
+                uint8_t* meta = piece + 2048 + 4 * l;
                 uint32_t word = (uint32_t)meta[0] | ((uint32_t)meta[1] << 8) | ((uint32_t)meta[2] << 16) |
                                 ((uint32_t)meta[3] << 24);
                 word |= code << (16 * q + 4 * p);
                 put32(meta, word);
               }
             }
-        off += PT_SPARSE_BYTES;
+        }
       }
+      prefix += sparse ? PT_SPARSE_PIECE : PT_DENSE_PIECE;
     }
+    rb += 8 * stride;
   }
   return ORACLE_OK;
 }

@@ -283,8 +283,10 @@ def test_pack_hand_worked_example():
     assert u16(g["dense2.byte_offset"]) == g["dense2.bits"]
     assert u16(g["sparse.byte_offset"]) == g["sparse.bits"]
     assert blob[g["sparse.meta_byte_offset"]] == g["sparse.meta_byte_value"]
+    assert u32(268) == g["table.0.stride"] and u32(284) == g["table.1.stride"]
     # every other metadata nibble of the sparse tile is code 4 (keeps 0 and 1)
-    meta = blob[g["table.1.offset"] + 16384:g["table.1.offset"] + 18432]
+    meta = np.concatenate([blob[g["table.1.offset"] + b * g["table.1.stride"] + 2048:
+                                g["table.1.offset"] + b * g["table.1.stride"] + 2304] for b in range(8)])
     nib = np.stack([meta & 15, meta >> 4], -1).ravel()
     assert (nib == 4).sum() == nib.size - 1 and (nib == 8).sum() == 1
 
@@ -304,39 +306,38 @@ def _unpack(blob, N, K):
     NT, KT = N // 128, K // 128
     W = np.zeros((N, K), np.uint16)
     codes = []
+    u64 = lambda o: int.from_bytes(blob[o:o + 8].tobytes(), "little")
+    u32 = lambda o: int.from_bytes(blob[o:o + 4].tobytes(), "little")
     for i in range(NT):
         for j in range(KT):
             e = 256 + 16 * (i * KT + j)
-            off = int.from_bytes(blob[e:e + 8].tobytes(), "little")
-            kind = int.from_bytes(blob[e + 8:e + 12].tobytes(), "little")
-            tile = blob[off:off + (32768 if kind == 0 else 18432)]
-            if kind == 0:
-                # q (64-column slice), band, half e, lane, element 2*g + u
-                ch = tile.view(np.uint16).reshape(2, 8, 2, 64, 8)
-                for q in range(2):
-                    for band in range(8):
-                        for e in range(2):
+            off, kind, stride = u64(e), u32(e + 8), u32(e + 12)
+            for band in range(8):
+                piece = blob[off + band * stride:off + band * stride + (4096 if kind == 0 else 2304)]
+                if kind == 0:
+                    # blocks (q, e) of 1 KB, lane l's 16 bytes at 16*l: element 2*g + u
+                    ch = piece.view(np.uint16).reshape(2, 2, 64, 8)
+                    for q in range(2):
+                        for half in range(2):
                             for l in range(64):
                                 r = i * 128 + band * 16 + l % 16
                                 for g in range(4):
                                     for u in range(2):
-                                        c = j * 128 + 64 * q + 16 * (l // 16) + 4 * g + 2 * e + u
-                                        W[r, c] = ch[q, band, e, l, 2 * g + u]
-            else:
-                vals = tile[:16384].view(np.uint16).reshape(2, 8, 64, 8)
-                # word (band, l) at (band // 4) * 256 + 4 * l + band % 4
-                meta = tile[16384:].view(np.uint32).reshape(2, 64, 4)
-                for q in range(2):
-                    for band in range(8):
+                                        c = j * 128 + 64 * q + 16 * (l // 16) + 4 * g + 2 * half + u
+                                        W[r, c] = ch[q, half, l, 2 * g + u]
+                else:
+                    vals = piece[:2048].view(np.uint16).reshape(2, 64, 8)
+                    meta = piece[2048:2304].view(np.uint32)
+                    for q in range(2):
                         for l in range(64):
                             r = i * 128 + band * 16 + l % 16
                             for p in range(4):
                                 g = 16 * q + 4 * (l // 16) + p
-                                code = (int(meta[band // 4, l, band % 4]) >> (16 * q + 4 * p)) & 15
+                                code = (int(meta[l]) >> (16 * q + 4 * p)) & 15
                                 codes.append(code)
                                 i0, i1 = code & 3, code >> 2
-                                W[r, j * 128 + 4 * g + i0] = vals[q, band, l, 2 * p]
-                                W[r, j * 128 + 4 * g + i1] = vals[q, band, l, 2 * p + 1]
+                                W[r, j * 128 + 4 * g + i0] = vals[q, l, 2 * p]
+                                W[r, j * 128 + 4 * g + i1] = vals[q, l, 2 * p + 1]
     return W, np.array(codes)
 
 
@@ -361,7 +362,7 @@ def test_pack_keeps_negative_zero_bits():
     mask[:, 1::4] = 1
     mask[:, 3::4] = 1
     blob = oracle.pack("bf16", W, np.ones((1, 1), np.uint8), mask)
-    vals = blob[512:512 + 16384].view(np.uint16)
-    assert np.all(vals == 0x8000)
-    meta = blob[512 + 16384:512 + 18432]
-    assert np.all(meta == (13 | (13 << 4)))  # code (1,3) = 1 | 3 << 2 = 13
+    # one sparse tile: 8 band pieces of 2304 bytes (2048 of values, 256 of codes) from byte 512
+    pieces = blob[512:512 + 8 * 2304].reshape(8, 2304)
+    assert np.all(pieces[:, :2048].copy().view(np.uint16) == 0x8000)
+    assert np.all(pieces[:, 2048:] == (13 | (13 << 4)))  # code (1,3) = 1 | 3 << 2 = 13
