@@ -58,9 +58,9 @@ typedef enum {
   PATCH_VARIANT_PREFILL = 2  /* output-tiled MFMA kernel; any M >= 1 */
 } patch_variant;
 
-/* Host-side mirror of the packed blob's header (format version 2). */
+/* Host-side mirror of the packed blob's header (format version 3). */
 typedef struct {
-  uint32_t version;   /* 2 */
+  uint32_t version;   /* 3 */
   uint32_t dtype;     /* PATCH_F16 or PATCH_BF16 */
   uint32_t tile_n;    /* 128 */
   uint32_t tile_k;    /* 128 */
@@ -88,16 +88,19 @@ uint64_t patch_packed_bytes(patch_dtype dtype, int64_t N, int64_t K, const uint8
 
 /*
  * Pack dense W plus a tile map and a 2:4 mask into the blob (format
- * version 2): a 256-byte header, a 16-byte-per-tile table (data offset, kind)
- * and the tile data.  A sparse tile keeps, for every group of four
- * consecutive weights along K, the two kept values plus a 4-bit code
- * i0 | i1 << 2 (2 bits per kept value); a dense tile keeps all 128 x 128
- * values, each 64-column slice stored as two halves holding positions (0,1)
- * and (2,3) of every group of four.  Both are laid out in the lane order of
- * the sparse matrix instruction's operands, which then runs both kinds (a
- * dense half is a 2:4 operand with a fixed code).  The 2:4 rule:
- * gist.science explainer, section 1 "Problem Statement"; the six patterns:
- * section 2 "Pattern Selection".
+ * version 3): a 256-byte header, a 16-byte-per-tile table (data offset,
+ * kind, band stride) and the tile data.  A sparse tile keeps, for every
+ * group of four consecutive weights along K, the two kept values plus a
+ * 4-bit code i0 | i1 << 2 (2 bits per kept value); a dense tile keeps all
+ * 128 x 128 values, each 64-column slice stored as two halves holding
+ * positions (0,1) and (2,3) of every group of four.  A tile is stored as
+ * eight pieces, one per 16-row band (4096 bytes dense, 2304 bytes 2:4);
+ * within a row-block the pieces of one band for all its tiles lie back to
+ * back, so band b of a tile sits at the tile's offset + b * band stride.
+ * Pieces are laid out in the lane order of the sparse matrix instruction's
+ * operands, which then runs both kinds (a dense half is a 2:4 operand with a
+ * fixed code).  The 2:4 rule: gist.science explainer, section 1 "Problem
+ * Statement"; the six patterns: section 2 "Pattern Selection".
  *
  *   W_dev          N x K elements of `dtype`, row-major, device.
  *   tile_map_host  T bytes on the host, nonzero = sparse tile.

@@ -35,9 +35,6 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 128;             // execution tile edge (N and K)
-constexpr int kDenseTileBytes = 32768; // 128 x 128 x 2
-constexpr int kSparseValBytes = 16384; // 128 x 64 x 2
-constexpr int kSparseTileBytes = 18432;
 constexpr int kHeaderBytes = 256;
 constexpr int kErrFlagOffset = 252;    // reserved header word used by pack to report a bad mask
 
@@ -92,11 +89,16 @@ __device__ __forceinline__ void store4(void* Y, int64_t elem_off, f32x4 v) {
   }
 }
 
-// One tile-table entry of the packed blob.
+constexpr int kDensePieceBytes = 4096;   // one 16-row band of a dense tile
+constexpr int kSparsePieceBytes = 2304;  // one band of a 2:4 tile: 2048 of values, 256 of codes
+constexpr int kSparseMetaOffset = 2048;  // codes after the values in a 2:4 piece
+
+// One tile-table entry of the packed blob.  Band b's piece of the tile
+// starts at offset + b * band_stride.
 struct TileEntry {
-  uint64_t offset;  // byte offset of the tile's data from the blob start
-  uint32_t kind;    // 0 dense, 1 sparse
-  uint32_t zero;
+  uint64_t offset;       // byte offset of the tile's band-0 piece from the blob start
+  uint32_t kind;         // 0 dense, 1 sparse
+  uint32_t band_stride;  // bytes from one band's pieces to the next in this row-block
 };
 
 }  // namespace patch

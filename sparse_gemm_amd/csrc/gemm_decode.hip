@@ -35,9 +35,9 @@ namespace patch {
 // exact whatever mix of kinds a wave meets:
 //   dense : a[2q + e] = the band's half e of 64-column slice q (packed W), or
 //           the row-major chunk of columns 32c + 8*(l/16) (dense baseline);
-//   sparse: a[0], a[1] = value fragments of slices 0 and 1, a[2] = this
-//           lane's 16 bytes of metadata for bands 4*(b/4) .. +3 (word b & 3
-//           is the band's), a[3] = the same chunk again (unused).
+//   sparse: a[0], a[1] = value fragments of slices 0 and 1, a[2] = the
+//           16 bytes of the band's codes holding this lane's word (word l & 3),
+//           a[3] = the same chunk again (unused).
 template <int MB>
 struct DecodeFrag {
   u32x4 x[MB][4];  // B operand chunks of M block mb: X[16mb + m][k0 + 32c + 8h .. +7], c = 0..3
@@ -52,8 +52,8 @@ struct DecodeFrag {
 // when M is 1).
 template <bool SRC_ROWMAJOR, int MB>
 __device__ __forceinline__ void decode_load(DecodeFrag<MB>& f, const uint8_t* __restrict__ src, uint64_t off,
-                                            uint32_t kind, const uint16_t* __restrict__ X, int K, int M, int i, int b,
-                                            int j, int l) {
+                                            uint32_t kind, uint32_t stride, const uint16_t* __restrict__ X, int K,
+                                            int M, int i, int b, int j, int l) {
   const int h = l >> 4;
   const uint8_t* ap[4];
   if constexpr (SRC_ROWMAJOR) {
@@ -64,13 +64,14 @@ __device__ __forceinline__ void decode_load(DecodeFrag<MB>& f, const uint8_t* __
     for (int c = 0; c < 4; c++) ap[c] = wr + 64 * c;
     f.kind = 0;
   } else {
-    const uint8_t* tp = src + off + 16 * l;
-    const uint8_t* mp = src + off + kSparseValBytes + 1024 * (b >> 2) + 16 * l;
-    const uint8_t* dp = tp + 2048 * b;  // dense: halves of slice 0, then slice 1
-    ap[0] = kind ? tp + 1024 * b : dp;
-    ap[1] = kind ? tp + 8192 + 1024 * b : dp + 1024;
-    ap[2] = kind ? mp : dp + 16384;
-    ap[3] = kind ? mp : dp + 17408;
+    // band b's piece of the tile: dense = blocks (slice 0, half 0/1), (slice
+    // 1, half 0/1); 2:4 = value blocks of slices 0 and 1, then the codes
+    const uint8_t* pb = src + off + (uint64_t)b * stride;
+    const uint8_t* mp = pb + kSparseMetaOffset + 16 * (l >> 2);
+    ap[0] = pb + 16 * l;
+    ap[1] = pb + 1024 + 16 * l;
+    ap[2] = kind ? mp : pb + 2048 + 16 * l;
+    ap[3] = kind ? mp : pb + 3072 + 16 * l;
     f.kind = kind;
   }
 #pragma unroll
@@ -85,7 +86,7 @@ __device__ __forceinline__ void decode_load(DecodeFrag<MB>& f, const uint8_t* __
 }
 
 template <bool BF16, bool SRC_ROWMAJOR, int MB>
-__device__ __forceinline__ void decode_mma(const DecodeFrag<MB>& f, f32x4 (&acc)[MB], int b) {
+__device__ __forceinline__ void decode_mma(const DecodeFrag<MB>& f, f32x4 (&acc)[MB], int l) {
   if constexpr (SRC_ROWMAJOR) {
 #pragma unroll
     for (int mb = 0; mb < MB; mb++)
@@ -101,11 +102,11 @@ __device__ __forceinline__ void decode_mma(const DecodeFrag<MB>& f, f32x4 (&acc)
         acc[mb] = mma_sparse<BF16, 0>(f.a[2 * q + 1], f.x[mb][2 * q], f.x[mb][2 * q + 1], acc[mb], 0xEEEEu);
       }
   } else {
-    // the band's word of the lane's metadata chunk (b is the same in every
-    // lane: uniform selects, not a dynamic vector index, which would put the
-    // fragment array in scratch memory)
+    // word l & 3 of the codes chunk, by two bit tests (plain selects; a
+    // dynamic vector index would put the fragment array in scratch memory)
     const u32x4 mc = f.a[2];
-    const uint32_t meta = (b & 2) ? ((b & 1) ? mc[3] : mc[2]) : ((b & 1) ? mc[1] : mc[0]);
+    const uint32_t lo = (l & 1) ? mc[1] : mc[0], hi = (l & 1) ? mc[3] : mc[2];
+    const uint32_t meta = (l & 2) ? hi : lo;
 #pragma unroll
     for (int mb = 0; mb < MB; mb++) {
       // slice 0: logical K 0..63 of the tile -> B chunks 0 (K 8h..) and 1 (K 32+8h..)
@@ -152,15 +153,17 @@ __global__ __launch_bounds__(WAVES * 64) void k_decode(const uint8_t* __restrict
   if (n_mine > 0) {
     u32x4 ents = {0u, 0u, 0u, 0u};
     if constexpr (!SRC_ROWMAJOR) ents = ld16(table + w + kDecodeWaves * min(l, n_mine - 1));
-    auto entry = [&](int t, uint64_t& off, uint32_t& kind) {
+    auto entry = [&](int t, uint64_t& off, uint32_t& kind, uint32_t& stride) {
       if constexpr (SRC_ROWMAJOR) {
         off = 0;
         kind = 0;
+        stride = 0;
       } else {
         const int lane = t;
         off = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ents[0], lane) |
               ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ents[1], lane) << 32);
         kind = (uint32_t)__builtin_amdgcn_readlane((int)ents[2], lane);
+        stride = (uint32_t)__builtin_amdgcn_readlane((int)ents[3], lane);
       }
     };
     DecodeFrag<MB> f[DEPTH];
@@ -168,9 +171,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_decode(const uint8_t* __restrict
     for (int s = 0; s < DEPTH; s++) {
       const int t = min(s, n_mine - 1);
       uint64_t off;
-      uint32_t kind;
-      entry(t, off, kind);
-      decode_load<SRC_ROWMAJOR, MB>(f[s], src, off, kind, X, K, M, i, b, w + kDecodeWaves * t, l);
+      uint32_t kind, stride;
+      entry(t, off, kind, stride);
+      decode_load<SRC_ROWMAJOR, MB>(f[s], src, off, kind, stride, X, K, M, i, b, w + kDecodeWaves * t, l);
     }
     // steady state: compute the DEPTH slots, refilling each with the tile
     // DEPTH further on (clamped to the last tile: a redundant, cached load)
@@ -178,18 +181,18 @@ __global__ __launch_bounds__(WAVES * 64) void k_decode(const uint8_t* __restrict
     for (; t0 + DEPTH < n_mine; t0 += DEPTH) {
 #pragma unroll
       for (int s = 0; s < DEPTH; s++) {
-        decode_mma<BF16, SRC_ROWMAJOR, MB>(f[s], acc, b);
+        decode_mma<BF16, SRC_ROWMAJOR, MB>(f[s], acc, l);
         const int tn = min(t0 + s + DEPTH, n_mine - 1);
         uint64_t off;
-        uint32_t kind;
-        entry(tn, off, kind);
-        decode_load<SRC_ROWMAJOR, MB>(f[s], src, off, kind, X, K, M, i, b, w + kDecodeWaves * tn, l);
+        uint32_t kind, stride;
+        entry(tn, off, kind, stride);
+        decode_load<SRC_ROWMAJOR, MB>(f[s], src, off, kind, stride, X, K, M, i, b, w + kDecodeWaves * tn, l);
       }
     }
     // last round: no refills
 #pragma unroll
     for (int s = 0; s < DEPTH; s++)
-      if (t0 + s < n_mine) decode_mma<BF16, SRC_ROWMAJOR, MB>(f[s], acc, b);
+      if (t0 + s < n_mine) decode_mma<BF16, SRC_ROWMAJOR, MB>(f[s], acc, l);
   }
 
   // ---- fixed-order reduction over waves (wave w < MB adds up M block w),

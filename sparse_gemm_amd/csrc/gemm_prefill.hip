@@ -33,7 +33,9 @@
 //     M are read from LDS while the current ones feed the matrix cores.
 //   * W comes straight from the packed blob into A-operand registers (a 1 KB
 //     fragment is one 16-byte load a lane), one step ahead; eight loads a
-//     lane per step for either kind.
+//     lane per step for either kind.  A wave's four bands of a tile are four
+//     pieces one band stride apart, so one descriptor and four scalar
+//     offsets address them.
 //   * All loads are buffer loads: a scalar descriptor (tile or X block base)
 //     plus a 32-bit lane offset, so addresses cost no 64-bit vector
 //     arithmetic; X rows past M fall outside the X descriptor's range and
@@ -78,8 +80,8 @@ __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff
 
 // A operands of one step, [.][band]: packed dense tile: a[e] = half e
 // (positions 2e, 2e+1 of every group of four); 2:4 tile: a[0] = values,
-// a[1][0] = this lane's metadata words of the wave's four bands, a[1][1..3]
-// unused; row-major W (dense baseline): a[qq] = 32-column slice qq in the
+// a[1] = the 16 bytes of the band's codes that hold this lane's word (word
+// l & 3); row-major W (dense baseline): a[qq] = 32-column slice qq in the
 // v_mfma_f32_16x16x32 layout.
 struct StepA {
   u32x4 a[2][4];
@@ -105,6 +107,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
   __shared__ __attribute__((aligned(16))) uint8_t s_x2[DIST == 2 ? kStageBytes : 16];
   // per row-block of the pair and tile column: (byte offset >> 8) | kind << 31
   __shared__ uint32_t s_ent[2][kPfMaxKT];
+  __shared__ uint32_t s_stride[2];  // band stride of each row-block of the pair
 
   const int id = blockIdx.x;
   const int t = (id & 7) * P.per_xcd + (id >> 3);
@@ -128,9 +131,11 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
       const int j = e - rr * KT;
       const TileEntry te = table[(int64_t)(rr ? i1 : i0) * KT + j];
       s_ent[rr][j] = (uint32_t)(te.offset >> 8) | (te.kind ? 0x80000000u : 0u);
+      if (j == 0) s_stride[rr] = te.band_stride;
     }
     __syncthreads();
   }
+  const uint32_t stride = SRC_ROWMAJOR ? 0u : (uint32_t)__builtin_amdgcn_readfirstlane((int)s_stride[r]);
 
   const uint32_t lane16 = 16u * (uint32_t)l;
 
@@ -153,23 +158,20 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
     } else {
       const uint32_t e = __builtin_amdgcn_readfirstlane(s_ent[r][j]);
       const uint32_t kind = e >> 31;
-      const uint8_t* tile = P.src + ((uint64_t)(e & 0x7fffffffu) << 8);
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile, kDenseTileBytes);
+      // the wave's first band piece; band 4wn+b is b * stride further on
+      const uint8_t* piece = P.src + ((uint64_t)(e & 0x7fffffffu) << 8) + (uint64_t)(4 * wn) * stride;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(piece, 3u * stride + (uint32_t)kDensePieceBytes);
       // dense: a[e][b] = half e of band 4wn+b in 64-column slice h, at
-      //        ((h*8 + 4wn + b)*2 + e) KB;
-      // 2:4  : a[0][b] = values of band 4wn+b in slice h, at (h*8 + 4wn + b) KB;
-      //        a[1][0] = metadata words of bands 4wn .. 4wn+3, at 16 KB + wn KB;
-      //        a[1][1..3] go through a zero-length descriptor (they read as
-      //        zero and move no data) at that same in-tile offset.
-      const __amdgpu_buffer_rsrc_t rz = make_rsrc(tile, kind ? 0u : (uint32_t)kDenseTileBytes);
-      const uint32_t b0 = kind ? (uint32_t)(h * 8 + 4 * wn) * 1024u : (uint32_t)(h * 8 + 4 * wn) * 2048u;
-      const uint32_t bm = (uint32_t)kSparseValBytes + 1024u * wn;
-      const uint32_t s0 = kind ? 1024u : 2048u;
+      //        2048h + 1024e in its piece;
+      // 2:4  : a[0][b] = values of band 4wn+b in slice h, at 1024h;
+      //        a[1][b] = its codes chunk 16 * (l/4) past the values.
+      const uint32_t v1 = kind ? 16u * (uint32_t)(l >> 2) : lane16;
+      const uint32_t o0 = kind ? 1024u * (uint32_t)h : 2048u * (uint32_t)h;
+      const uint32_t o1 = kind ? (uint32_t)kSparseMetaOffset : 2048u * (uint32_t)h + 1024u;
 #pragma unroll
-      for (int b = 0; b < 4; b++) A.a[0][b] = bload16(rs, lane16, b0 + s0 * b);
-      A.a[1][0] = bload16(rs, lane16, kind ? bm : b0 + 1024u);
+      for (int b = 0; b < 4; b++) A.a[0][b] = bload16(rs, lane16, o0 + stride * b);
 #pragma unroll
-      for (int b = 1; b < 4; b++) A.a[1][b] = bload16(rz, lane16, kind ? bm : b0 + 1024u + 2048u * b);
+      for (int b = 0; b < 4; b++) A.a[1][b] = bload16(rs, v1, o1 + stride * b);
       return kind;
     }
   };
@@ -237,9 +239,15 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
       // slice once with its own codes, a dense slice twice -- half (0,1) with
       // code 4 in every group, half (2,3) with code 14.
       const int nsub = kind == 0 ? 2 : 1;
+      // 2:4: word l & 3 of the chunk by two bit tests (plain selects; a
+      // dynamic vector index would put the fragments in scratch memory)
       uint32_t idx0[4];
 #pragma unroll
-      for (int b = 0; b < 4; b++) idx0[b] = kind == 0 ? 0x4444u : (A.a[1][0][b] >> (16 * h));
+      for (int b = 0; b < 4; b++) {
+        const u32x4 mc = A.a[1][b];
+        const uint32_t lo = (l & 1) ? mc[1] : mc[0], hi = (l & 1) ? mc[3] : mc[2];
+        idx0[b] = kind == 0 ? 0x4444u : (((l & 2) ? hi : lo) >> (16 * h));
+      }
       // B fragments double-buffered across groups where registers allow
       // (the 256-wide tile has no room for the second set).
       constexpr int kGroups = kNMB / kPfMGroup;

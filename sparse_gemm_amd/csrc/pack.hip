@@ -1,28 +1,28 @@
-// pack.hip -- dense W + tile map + 2:4 mask -> packed blob (format version 2).
+// pack.hip -- dense W + tile map + 2:4 mask -> packed blob (format version 3).
 //
 // PATCH (arXiv 2509.23410), gist.science explainer, section 2 "Core
 // Mechanism": every 128 x 128 tile of W is dense or 2:4 sparse; section 1
 // "Problem Statement": a 2:4 group keeps two of four consecutive weights;
 // section 2 "Pattern Selection": six possible patterns per group.
 //
-// Tile data layout (the host writes the header and the tile table before
-// this kernel runs):
-//   dense tile : 2048 chunks of 16 bytes; chunk c = ((q*8 + band)*2 + e)*64 + l
-//                holds, of row 16*band + l%16 and the four groups of four at
-//                columns 64*q + 16*(l/16) .. +15, the elements at positions
-//                2e and 2e+1 of each group (group order, then column order):
-//                two halves that are 2:4 operands with the fixed patterns
-//                (0,1) and (2,3).
-//   sparse tile: 1024 value chunks, chunk c = (q*8 + band)*64 + l holds the two
-//                kept values (ascending column) of the groups
-//                g = 16*q + 4*(l/16) + p, p = 0..3, of row 16*band + l%16;
-//                then 512 metadata words, word (band/4)*256 + 4*l + band%4
-//                holding group g's code i0 | i1 << 2 at bits 16*q + 4*p (so
-//                one 16-byte load gives lane l its words of four bands).
-// This is exactly the lane order of the A operand and index of
+// Layout (the host writes the header and the tile table before this kernel
+// runs): a piece is one 16-row band of one tile; inside a row-block each
+// band's pieces of all tiles are back to back (band b of tile (i, j) at the
+// table entry's offset + b * band_stride).  Lane l (row l%16 of the band,
+// column group l/16) owns 16 bytes at 16*l of each 1 KB block of a piece:
+//   dense piece (4096 B): blocks (q, e) at 2048*q + 1024*e hold, of the four
+//       groups of four at columns 64*q + 16*(l/16) .. +15, the elements at
+//       positions 2e and 2e+1 of each group (group order, then column order):
+//       two halves that are 2:4 operands with the fixed patterns (0,1) and
+//       (2,3);
+//   2:4 piece (2304 B): block q at 1024*q holds the two kept values
+//       (ascending column) of groups g = 16*q + 4*(l/16) + p, p = 0..3; then
+//       at 2048 + 4*l the lane's word of codes i0 | i1 << 2 (bits 16*q + 4*p).
+// These are the lane orders of the A operand and index of
 // v_smfmac_f32_16x16x64, for both tile kinds, so the GEMM kernels load each
-// 1 KB fragment with one coalesced 16-byte load a lane and run dense and 2:4
-// tiles on the same instruction.
+// 1 KB fragment with one coalesced 16-byte load a lane, run dense and 2:4
+// tiles on the same instruction, and a kernel that owns one band of a
+// row-block streams one contiguous range.
 #include "device_common.h"
 
 namespace patch {
@@ -34,7 +34,6 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, co
   const int part = blockIdx.x & 7;
   const TileEntry e = reinterpret_cast<const TileEntry*>(blob + kHeaderBytes)[t];
   const int i = t / KT, j = t - (t / KT) * KT;
-  uint8_t* tile = blob + e.offset;
   if (e.kind == 0) {
     if (part >= 4) return;
     const int c = part * 256 + threadIdx.x;  // (q, band, l), 0 .. 1023
@@ -46,7 +45,7 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, co
     const u32x4 w0 = ld16(W + row * K + col), w1 = ld16(W + row * K + col + 8);
     const u32x4 h0 = {w0[0], w0[2], w1[0], w1[2]};
     const u32x4 h1 = {w0[1], w0[3], w1[1], w1[3]};
-    uint8_t* dst = tile + 16 * ((q * 8 + band) * 2 * 64 + l);
+    uint8_t* dst = blob + e.offset + (uint64_t)band * e.band_stride + 2048 * q + 16 * l;
     st16(dst, h0);
     st16(dst + 1024, h1);
     return;
@@ -55,6 +54,7 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, co
   const int pair = part * 256 + threadIdx.x;  // (band, l), 0 .. 511
   const int band = pair >> 6, l = pair & 63;
   const int64_t row = (int64_t)i * kTile + 16 * band + (l & 15);
+  uint8_t* piece = blob + e.offset + (uint64_t)band * e.band_stride;
   uint32_t meta = 0;
   bool bad = false;
 #pragma unroll
@@ -94,9 +94,9 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, co
       meta |= (pos[0] | (pos[1] << 2)) << (16 * q + 4 * p);
     }
     u32x4 o = {outv[0], outv[1], outv[2], outv[3]};
-    st16(tile + 16 * ((q * 8 + band) * 64 + l), o);
+    st16(piece + 1024 * q + 16 * l, o);
   }
-  reinterpret_cast<uint32_t*>(tile + kSparseValBytes)[(band >> 2) * 256 + 4 * l + (band & 3)] = meta;
+  reinterpret_cast<uint32_t*>(piece + kSparseMetaOffset)[l] = meta;
   if (bad) atomicOr(reinterpret_cast<uint32_t*>(blob + kErrFlagOffset), 1u);
 }
 

@@ -21,10 +21,12 @@ hipError_t launch_prefill(bool bf16, bool rowmajor, bool out_f32, const void* sr
 namespace {
 
 constexpr uint32_t kMagic = 0x48435450u;  // "PTCH"
-constexpr uint32_t kVersion = 2;
+constexpr uint32_t kVersion = 3;
 constexpr int64_t kTile = 128;
 constexpr uint64_t kDenseBytes = 32768;
 constexpr uint64_t kSparseBytes = 18432;
+constexpr uint64_t kDensePiece = 4096;   // one 16-row band of a dense tile
+constexpr uint64_t kSparsePiece = 2304;  // one band of a 2:4 tile: values + codes
 constexpr int64_t kMaxDim = int64_t(1) << 20;  // N, K upper bound (int32 indexing inside kernels)
 constexpr int64_t kMaxKT = 1024;              // prefill kernel's per-workgroup tile lists
 constexpr int64_t kDecodeMaxK = 65536;        // decode kernel: <= 64 tile columns per wave
@@ -93,7 +95,7 @@ void put64(uint8_t* p, uint64_t v) { std::memcpy(p, &v, 8); }
 
 extern "C" {
 
-int32_t patch_abi_version(void) { return 2; }
+int32_t patch_abi_version(void) { return 3; }
 
 const char* patch_status_string(patch_status s) {
   switch (s) {
@@ -137,14 +139,25 @@ patch_status patch_pack(patch_dtype dtype, int64_t N, int64_t K, const void* W_d
   // header + tile table, built on the host
   const uint64_t data_off = round_up(256 + 16 * (uint64_t)T, 256);
   std::vector<uint8_t> head(data_off, 0);
+  // Row-block i: 8 bands of S_i bytes, band b holding its piece of every
+  // tile in order; an entry holds the offset of the tile's band-0 piece, its
+  // kind and S_i.
   uint32_t ns = 0;
-  uint64_t off = data_off;
-  for (int64_t t = 0; t < T; t++) {
-    const uint32_t kind = tile_map_host[t] != 0;
-    put64(&head[256 + 16 * t], off);
-    put32(&head[256 + 16 * t + 8], kind);
-    off += kind ? kSparseBytes : kDenseBytes;
-    ns += kind;
+  uint64_t rb = data_off;
+  for (int64_t i = 0; i < NT; i++) {
+    uint64_t stride = 0;
+    for (int64_t j = 0; j < KT; j++) stride += tile_map_host[i * KT + j] ? kSparsePiece : kDensePiece;
+    uint64_t prefix = 0;
+    for (int64_t j = 0; j < KT; j++) {
+      const int64_t t = i * KT + j;
+      const uint32_t kind = tile_map_host[t] != 0;
+      put64(&head[256 + 16 * t], rb + prefix);
+      put32(&head[256 + 16 * t + 8], kind);
+      put32(&head[256 + 16 * t + 12], (uint32_t)stride);
+      prefix += kind ? kSparsePiece : kDensePiece;
+      ns += kind;
+    }
+    rb += 8 * stride;
   }
   put32(&head[0], kMagic);
   put32(&head[4], kVersion);

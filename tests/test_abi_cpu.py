@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(patch.EXPORTS)
-    assert patch.load().patch_abi_version() == 2
+    assert patch.load().patch_abi_version() == 3
 
 
 def test_packed_bytes_matches_oracle_closed_form():
@@ -91,7 +91,7 @@ def test_desc_from_oracle_header_and_gemm_checks():
     p = inputs.make_custom("bf16", 256, 384, 2, "bernoulli", 0.5, "top2")
     blob = oracle.pack("bf16", p.w, p.tile_map, p.mask)
     d = patch.desc_from_header(blob[:256].tobytes())
-    assert (d.version, d.dtype, d.N, d.K, d.nt_n, d.nt_k) == (2, 1, 256, 384, 2, 3)
+    assert (d.version, d.dtype, d.N, d.K, d.nt_n, d.nt_k) == (3, 1, 256, 384, 2, 3)
     assert d.n_sparse == int(p.tile_map.sum()) and d.total_bytes == blob.size
     lib = patch.load()
     assert lib.patch_gemm_workspace_bytes(ctypes.byref(d), 2048) == 0
