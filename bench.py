@@ -75,12 +75,13 @@ def _event():
     return e
 
 
-def time_launches(calls, steps, warmup):
+def time_launches(calls, steps, warmup, batches=1):
     """calls: list of (key, fn(k)).  Returns
       * ms per step, a step running every call once, back to back (one event
         pair around all `steps` steps), and
-      * {key: ms per launch}, each call timed on its own: `steps` launches
-        back to back between one event pair, divided by `steps`.
+      * {key: [ms per launch of each batch]}, each call timed on its own:
+        `batches` batches of `steps` launches back to back, one event pair
+        around each batch, divided by `steps`.
     Events are recorded on the current stream, the one the launches use."""
     import torch
 
@@ -99,12 +100,14 @@ def time_launches(calls, steps, warmup):
     for key, fn in calls:
         for k in range(warmup):
             fn(k)
-        a = _event()
-        for k in range(steps):
-            fn(warmup + k)
-        b = _event()
-        torch.cuda.synchronize()
-        per[key] = a.elapsed_time(b) / steps
+        per[key] = []
+        for _ in range(batches):
+            a = _event()
+            for k in range(steps):
+                fn(warmup + k)
+            b = _event()
+            torch.cuda.synchronize()
+            per[key].append(a.elapsed_time(b) / steps)
     return ms_step, per
 
 
@@ -135,7 +138,7 @@ def pack_timed(W, tile_map, mask):
     return pw, best
 
 
-def gemm_set(cfg_name, mi, si, Ms, steps, warmup, with_hipblaslt=True, fraction=None, map_kind=None):
+def gemm_set(cfg_name, mi, si, Ms, steps, warmup, with_hipblaslt=True, fraction=None, map_kind=None, batches=1):
     """Time patch_gemm, patch_dense_gemm and torch.matmul for one weight matrix."""
     import torch
 
@@ -169,11 +172,11 @@ def gemm_set(cfg_name, mi, si, Ms, steps, warmup, with_hipblaslt=True, fraction=
             torch.matmul(Xs[M], Ws[k % len(Ws)].t(), out=Ys[M])
         return f
 
-    ms_h, per_h = time_launches([(M, hyb(M)) for M in Ms], steps, warmup)
-    ms_d, per_d = time_launches([(M, dense(M)) for M in Ms], steps, warmup)
+    ms_h, per_h = time_launches([(M, hyb(M)) for M in Ms], steps, warmup, batches)
+    ms_d, per_d = time_launches([(M, dense(M)) for M in Ms], steps, warmup, batches)
     per_b = None
     if with_hipblaslt:
-        _, per_b = time_launches([(M, blas(M)) for M in Ms], steps, warmup)
+        _, per_b = time_launches([(M, blas(M)) for M in Ms], steps, warmup, batches)
     res = dict(p=p, pw=pw, pack_ms=pack_ms, ms_step=ms_h, ms_step_dense=ms_d, per=per_h, per_dense=per_d,
                per_blas=per_b, n_copies=len(blobs))
     del blobs, Ws
@@ -185,6 +188,10 @@ def mean(x):
     return float(np.mean(x))
 
 
+def median(x):
+    return float(np.median(x))
+
+
 def summarize(res, Ms):
     p = res["p"]
     N, K, ns = p.N, p.K, int(p.tile_map.sum())
@@ -192,14 +199,15 @@ def summarize(res, Ms):
     s = ns / T
     out = {}
     for M in Ms:
-        t = mean(res["per"][M]) * 1e-3
-        td = mean(res["per_dense"][M]) * 1e-3
+        t = median(res["per"][M]) * 1e-3
+        td = median(res["per_dense"][M]) * 1e-3
         fl = 2.0 * M * N * K
         eff = 2.0 * M * N * K * (1 - 0.5 * s)
-        e = dict(us=t * 1e6, dense_us=td * 1e6, tflops_dense_equiv=fl / t / 1e12, tflops_effective=eff / t / 1e12,
+        e = dict(us=t * 1e6, us_min=min(res["per"][M]) * 1e3, us_max=max(res["per"][M]) * 1e3,
+                 batches=len(res["per"][M]), dense_us=td * 1e6, tflops_dense_equiv=fl / t / 1e12, tflops_effective=eff / t / 1e12,
                  gbps=algo_bytes(N, K, M, ns) / t / 1e9, speedup_vs_dense=td / t)
         if res["per_blas"] is not None:
-            tb = mean(res["per_blas"][M]) * 1e-3
+            tb = median(res["per_blas"][M]) * 1e-3
             e["hipblaslt_us"] = tb * 1e6
             e["speedup_vs_hipblaslt"] = tb / t
         # roofline: max of HBM time and blended matrix-core time
@@ -227,14 +235,18 @@ def traffic_for(kernel, M):
     return float(ent["fetch_bytes"] + ent["write_bytes"])
 
 
-def ingest_counters(fetch_dir, write_dir):
-    """Write profiles/traffic_counters.json from two rocprofv3 counter runs of
-    this script with --calibrate-copy (one with --pmc FETCH_SIZE, one with
-    --pmc WRITE_SIZE, CSV output in fetch_dir / write_dir).  Per-dispatch KiB
-    are averaged per kernel and scaled by what the same counter reads for the
-    256 MiB device copy of known size in the same run."""
+def ingest_counters(dirs):
+    """Write profiles/traffic_counters.json from rocprofv3 counter runs of this
+    script with --calibrate-copy: dirs = [fetch_dir, write_dir, ...], pairs of
+    one --pmc FETCH_SIZE run and one --pmc WRITE_SIZE run of the same command
+    (CSV output).  Per-dispatch KiB are averaged per kernel and scaled by what
+    the same counter reads for the 256 MiB device copy of known size in the
+    same run."""
     import csv
     import glob
+
+    if len(dirs) % 2:
+        raise SystemExit("--ingest-counters takes FETCH_DIR WRITE_DIR pairs")
 
     def per_kernel(d, counter):
         files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
@@ -257,21 +269,27 @@ def ingest_counters(fetch_dir, write_dir):
                 vals.setdefault(key, []).append(float(r["Counter_Value"]))
         return vals
 
-    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
     copy_kib = 256 * 1024.0
-    # the copy reads and writes 256 MiB; take the largest copy dispatch (the calibration one)
-    f_scale = copy_kib / max(fetch["copy"])
-    w_scale = copy_kib / max(write["copy"])
-    kernels = {}
-    for key in sorted(set(fetch) & set(write) - {"copy"}):
-        fb = mean(fetch[key]) * 1024.0 * f_scale
-        wb = mean(write[key]) * 1024.0 * w_scale
-        kernels[key] = {str(M): {"fetch_bytes": fb, "write_bytes": wb} for M in (1, 4, 16)}
+    kernels, scales = {}, []
+    for fetch_dir, write_dir in zip(dirs[0::2], dirs[1::2]):
+        fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+        # the copy reads and writes 256 MiB; take the largest copy dispatch (the calibration one)
+        f_scale = copy_kib / max(fetch["copy"])
+        w_scale = copy_kib / max(write["copy"])
+        scales.append((f_scale, w_scale))
+        for key in sorted(set(fetch) & set(write) - {"copy"}):
+            fb = mean(fetch[key]) * 1024.0 * f_scale
+            wb = mean(write[key]) * 1024.0 * w_scale
+            Ms = (1, 4, 16) if key.startswith("decode") else (2048,)
+            kernels[key] = {str(M): {"fetch_bytes": fb, "write_bytes": wb} for M in Ms}
+            kernels[key]["raw_kib"] = {"fetch": mean(fetch[key]), "write": mean(write[key]),
+                                       "dispatches": len(fetch[key])}
     out = {"kernel_sha": kernel_sha(),
-           "note": f"rocprofv3 FETCH_SIZE / WRITE_SIZE per dispatch, averaged over all dispatches of each kernel "
-                   f"(M = 1, 4, 16 launches alike), scaled by a 256 MiB device copy measured in the same runs "
-                   f"(fetch x{f_scale:.4f}, write x{w_scale:.4f})",
-           "fetch_scale": f_scale, "write_scale": w_scale, "kernels": kernels}
+           "note": "rocprofv3 FETCH_SIZE / WRITE_SIZE per dispatch, averaged over all dispatches of each kernel "
+                   "in its run (decode: M = 1, 4, 16 launches alike; prefill: both matrices of the prefill MLP "
+                   "workload), scaled by a 256 MiB device copy measured in the same run (fetch, write scales: " +
+                   ", ".join(f"x{a:.4f} x{b:.4f}" for a, b in scales) + ")",
+           "scales": scales, "kernels": kernels}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
@@ -305,15 +323,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--report", default=None, help="also write the full sweep as JSON lines to this path")
+    ap.add_argument("--report-steps", type=int, default=100, help="launches per timed batch in the report")
+    ap.add_argument("--report-batches", type=int, default=10, help="timed batches per point in the report (median)")
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill_mlp", "imbalanced_13b"],
                     help="decode (default: the q_proj decode GEMM) or a prefill workload, for profiling")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for rocprofv3 byte counters)")
-    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
-                    help="write profiles/traffic_counters.json from rocprofv3 FETCH_SIZE / WRITE_SIZE runs and exit")
+    ap.add_argument("--ingest-counters", nargs="+", metavar="DIR", default=None,
+                    help="FETCH_DIR WRITE_DIR [FETCH_DIR WRITE_DIR ...]: write profiles/traffic_counters.json from "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE runs and exit")
     args = ap.parse_args()
     if args.ingest_counters:
-        ingest_counters(*args.ingest_counters)
+        ingest_counters(args.ingest_counters)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 (the multi-GPU sharding "
@@ -397,7 +418,7 @@ def main():
     print(json.dumps(line), flush=True)
 
     if args.report:
-        write_report(args.report, args.steps, args.warmup)
+        write_report(args.report, args.report_steps, args.warmup, args.report_batches)
 
 
 def run_prefill_workload(args):
@@ -412,21 +433,24 @@ def run_prefill_workload(args):
         p = res["p"]
         for M in cfg.Ms:
             print(json.dumps(dict(workload=args.workload, matrix=cfg.matrices[mi].name, N=p.N, K=p.K, M=M,
-                                  sparse_tiles=int(p.tile_map.sum()), tiles=int(p.tile_map.size), **summ[M])),
+                                  sparse_tiles=int(p.tile_map.sum()), tiles=int(p.tile_map.size),
+                                  algorithmic_bytes=algo_bytes(p.N, p.K, M, int(p.tile_map.sum())),
+                                  traffic_counters_bytes=traffic_for("prefill", M) if args.workload == "prefill_mlp"
+                                  else None, **summ[M])),
                   flush=True)
 
 
-def write_report(path, steps, warmup):
+def write_report(path, steps, warmup, batches):
     """Every workload: decode, prefill MLP, the sparsity sweep and the 13B
-    imbalanced shapes; one JSON line per (matrix, s, M)."""
+    imbalanced shapes; one JSON line per (matrix, s, M).  Each time is the
+    median of `batches` batches of `steps` launches (min and max beside it)."""
     from sparse_gemm_amd import inputs
 
-    steps = max(20, steps // 4)
-    warmup = max(5, warmup // 4)
     with open(path, "w") as f:
         def emit(cfg_name, mi, si, Ms, fraction=None, map_kind=None):
             cfg = inputs.CONFIGS[cfg_name]
-            res = gemm_set(cfg_name, mi, si, Ms, steps, warmup, fraction=fraction, map_kind=map_kind)
+            res = gemm_set(cfg_name, mi, si, Ms, steps, warmup, fraction=fraction, map_kind=map_kind,
+                           batches=batches)
             summ = summarize(res, Ms)
             p = res["p"]
             for M in Ms:

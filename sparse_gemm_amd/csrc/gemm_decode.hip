@@ -6,11 +6,12 @@
 // kernel streams each tile's packed bytes exactly once:
 //
 //   * one workgroup per 16-row band of W (N/16 workgroups) and all of K;
-//     wave w of the workgroup's WAVES takes the tile columns j = w,
-//     w+WAVES, ... of the band's row-block; its tile-table entries arrive
-//     with one vector load and are read with v_readlane (no list building,
-//     no barrier before the first weight load); the 8 bands of a row-block
-//     run on one XCD, so the lines they share sit in one L2;
+//     wave w of the workgroup's WAVES (2 to 8, fewer where K allows) takes
+//     the tile columns j = w, w+WAVES, ... of the band's row-block; its
+//     tile-table entries arrive with one vector load and are read with
+//     v_readlane (no list building, no barrier before the first weight
+//     load); the 8 bands of a row-block run on one XCD, so the lines they
+//     share sit in one L2;
 //   * a tile's 16 x 128 band is 4 (dense) or 2 (sparse) 1 KB fragments that a
 //     wave loads with one 16-byte load per lane each, straight into the A
 //     operand registers; X (at most 16 rows) is read from L2 into the B
@@ -18,8 +19,7 @@
 //   * both kinds run on v_smfmac_f32_16x16x64: a 2:4 tile is 2 of them (one
 //     per 64-column slice, its own index codes), a dense tile 4 (each slice
 //     as two halves with the fixed patterns (0,1) and (2,3));
-//   * loads run DEPTH tiles ahead of the matrix instructions (at K = 4096
-//     every tile of a wave is in flight at once);
+//   * loads run DEPTH tiles ahead of the matrix instructions;
 //   * the waves' fp32 partial sums are added in LDS in wave order (fixed, so
 //     results are deterministic) and rounded to the output type.
 //
@@ -142,8 +142,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_decode(const uint8_t* __restrict
 
   __shared__ f32x4 s_red[kDecodeWaves * MB][64];
 
-  // wave w takes tile columns j = w, w + 8, w + 16, ... of its row-block
-  // (at most 64 of them: K <= 65536).  Their table entries arrive with one
+  // wave w takes tile columns j = w, w + WAVES, ... of its row-block (at
+  // most 64 of them, which the launch guarantees).  Their table entries arrive with one
   // vector load (lane t holds the entry of the wave's t-th tile) and are read
   // with v_readlane.
   const int n_mine = (KT - w + kDecodeWaves - 1) / kDecodeWaves;
@@ -195,16 +195,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_decode(const uint8_t* __restrict
       if (t0 + s < n_mine) decode_mma<BF16, SRC_ROWMAJOR, MB>(f[s], acc, l);
   }
 
-  // ---- fixed-order reduction over waves (wave w < MB adds up M block w),
-  // then round and store
+  // ---- fixed-order reduction over waves (wave w adds up M blocks w,
+  // w + WAVES, ...), then round and store
 #pragma unroll
   for (int mb = 0; mb < MB; mb++) s_red[w * MB + mb][l] = acc[mb];
   __syncthreads();
-  if (w < MB) {
-    f32x4 sum = s_red[w][l];
+  for (int mb = w; mb < MB; mb += kDecodeWaves) {
+    f32x4 sum = s_red[mb][l];
 #pragma unroll
-    for (int ww = 1; ww < kDecodeWaves; ww++) sum += s_red[ww * MB + w][l];
-    const int m = 16 * w + (l & 15);
+    for (int ww = 1; ww < kDecodeWaves; ww++) sum += s_red[ww * MB + mb][l];
+    const int m = 16 * mb + (l & 15);
     if (m < M) {
       const int64_t n = (int64_t)i * kTile + 16 * b + 4 * (l >> 4);
       store4<BF16, OUT_F32>(Y, (int64_t)m * N + n, sum);
@@ -225,12 +225,24 @@ static hipError_t launch_decode_v(const void* src, const void* X, int64_t M, int
 template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32>
 static hipError_t launch_decode_t(const void* src, const void* X, int64_t M, int64_t N, int64_t K, void* Y,
                                   hipStream_t s) {
-  // M <= 16: 16 waves (two tile columns each at K = 4096, all in flight at
-  // once) and the 8 bands of a row-block on one XCD -- the fastest of the
-  // measured arrangements on the q_proj decode shape.  More tokens: MB column
-  // blocks of 16 per wave on 8 waves, one tile ahead (X is re-read from L2 by
+  // Few waves a workgroup, several tiles in flight a wave: small workgroups
+  // fill every CU several times over and keep starting while others drain,
+  // which measured faster than 8 or 16 waves on the q_proj, gate_proj and
+  // down_proj shapes.  A wave reads its table entries with one vector load,
+  // so it may own at most 64 tile columns: larger K takes more waves.
+  const int64_t KT = K / kTile;
+  if (M <= 16) {
+    if (KT <= 2 * 64) return launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, 2, 4, true, 1>(src, X, M, N, K, Y, s);
+    if (KT <= 4 * 64) return launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, 4, 4, true, 1>(src, X, M, N, K, Y, s);
+    return launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, 8, 2, true, 1>(src, X, M, N, K, Y, s);
+  }
+  // More tokens: MB column blocks of 16 per wave (X is re-read from L2 by
   // every band, which the 16 < M <= 128 range affords).
-  if (M <= 16) return launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, 16, 2, true, 1>(src, X, M, N, K, Y, s);
+  if (KT <= 4 * 64) {
+    if (M <= 32) return launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, 4, 2, true, 2>(src, X, M, N, K, Y, s);
+    if (M <= 64) return launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, 4, 1, true, 4>(src, X, M, N, K, Y, s);
+    return launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, 4, 1, true, 8>(src, X, M, N, K, Y, s);
+  }
   if (M <= 32) return launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, 8, 2, true, 2>(src, X, M, N, K, Y, s);
   if (M <= 64) return launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, 8, 1, true, 4>(src, X, M, N, K, Y, s);
   return launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, 8, 1, true, 8>(src, X, M, N, K, Y, s);

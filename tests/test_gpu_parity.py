@@ -148,6 +148,23 @@ def test_all_dense_map_matches_dense_baseline(M):
         assert float((a - b).abs().max()) <= 1e-5 * scale, v
 
 
+@pytest.mark.parametrize("K", [16384, 16512, 32768, 32896, 65536])
+def test_decode_long_k(K):
+    """The decode kernel splits a band's tile columns over 2, 4 or 8 waves by
+    K (each wave may own at most 64 of them): both sides of every switch,
+    the largest K, and M on both sides of each column-block count."""
+    p = inputs.make_custom("bf16", 256, K, 14, "bernoulli", 0.5, "uniform")
+    pw, W = _pack(p)
+    Xb = inputs.make_custom_x("bf16", 128, K, 15)
+    ref = _ref(p, Xb)
+    pd = inputs.make_custom("bf16", 256, K, 14, "dense", 0.0, "top2")
+    ref_d = _ref(pd, Xb)
+    for M in (1, 16, 17, 33, 64, 65, 128):
+        X = dev_bits(Xb[:M], "bf16")
+        assert_close(patch.gemm(X, pw, variant="decode"), ref[:M], what=f"K={K} M={M}")
+        assert_close(patch.dense_gemm(X, W, variant="decode"), ref_d[:M], what=f"dense K={K} M={M}")
+
+
 # ------------------------------------------------------------------ exact cases
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_identity_x_gives_masked_weights_exactly(dtype):
