@@ -165,6 +165,20 @@ def test_decode_long_k(K):
         assert_close(patch.dense_gemm(X, W, variant="decode"), ref_d[:M], what=f"dense K={K} M={M}")
 
 
+@pytest.mark.parametrize("M", [520, 1061, 1500])
+def test_prefill_m_groups(M):
+    """Prefill orders its output blocks by groups of M-blocks (2 to 4 groups
+    at these M, the last one short) over an odd number of row-blocks (a lone
+    middle row-block): every output against the oracle."""
+    p = inputs.make_custom("bf16", 640, 384, 16, "bernoulli", 0.5, "uniform")
+    pw, _ = _pack(p)
+    Xb = inputs.make_custom_x("bf16", M, 384, 17)
+    ref = _ref(p, Xb)
+    X = dev_bits(Xb, "bf16")
+    assert_close(patch.gemm(X, pw, variant="prefill"), ref, what=f"M={M}")
+    assert_close(patch.gemm(X, pw, out_dtype=torch.float32, variant="prefill"), ref, f32=True, what=f"M={M} f32")
+
+
 # ------------------------------------------------------------------ exact cases
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_identity_x_gives_masked_weights_exactly(dtype):
