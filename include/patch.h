@@ -52,10 +52,13 @@ typedef enum { PATCH_F16 = 0, PATCH_BF16 = 1, PATCH_F32 = 2 } patch_dtype;
 
 /* GEMM variant selection for patch_gemm_ex (patch_gemm uses PATCH_VARIANT_AUTO). */
 typedef enum {
-  PATCH_VARIANT_AUTO = 0,    /* decode for M <= 128 and K <= 65536, prefill otherwise */
+  PATCH_VARIANT_AUTO = 0,    /* decode for M <= 16 (K <= 65536), prefill otherwise; for
+                                M <= 128 also decode when the workspace passed is smaller
+                                than the GEMM's workspace query asks for */
   PATCH_VARIANT_DECODE = 1,  /* W-streaming kernel; valid for 1 <= M <= 128, K <= 65536
                                 (else PATCH_ERR_INVALID_ARG / PATCH_ERR_UNSUPPORTED) */
-  PATCH_VARIANT_PREFILL = 2  /* output-tiled MFMA kernel; any M >= 1 */
+  PATCH_VARIANT_PREFILL = 2  /* output-tiled MFMA kernel; any M >= 1; splits K when the
+                                output blocks cannot fill the GPU and workspace allows */
 } patch_variant;
 
 /* Host-side mirror of the packed blob's header (format version 3). */
@@ -121,9 +124,22 @@ patch_status patch_pack(patch_dtype dtype, int64_t N, int64_t K, const void* W_d
  * Checks magic, version, dtype, tile shape and that the sizes agree. */
 patch_status patch_desc_from_header(const void* header_host, uint64_t header_bytes, patch_packed_desc* desc_out);
 
-/* Device workspace bytes patch_gemm needs for this M (0 in this version:
- * every reduction happens inside a workgroup). */
+/*
+ * Device workspace bytes the prefill kernel can use for this M: when its
+ * output blocks alone cannot fill the GPU (few tokens or few row-blocks) it
+ * splits K into ranges, writes each range's fp32 partial sums to the
+ * workspace ([splits][M][N] floats) and adds them in range order in a
+ * second kernel on the same stream, so results do not depend on timing.
+ * 0 when no split is wanted.  A smaller workspace only means fewer ranges
+ * (none below two planes of M*N floats).  The workspace is scratch owned by
+ * the call: its contents need no initialisation and are undefined after;
+ * calls that run concurrently need distinct workspaces.
+ */
 uint64_t patch_gemm_workspace_bytes(const patch_packed_desc* desc, int64_t M);
+
+/* The same for patch_dense_gemm on an N x K weight (it uses the same kernel
+ * shapes). */
+uint64_t patch_dense_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
  * Hybrid GEMM: Y = X * (W o E)^T from the packed blob.  Both tile kinds run
@@ -135,7 +151,8 @@ uint64_t patch_gemm_workspace_bytes(const patch_packed_desc* desc, int64_t M);
  *   packed_dev  the blob (device).
  *   X_dev       M x K elements of desc->dtype (device).
  *   Y_dev       M x N elements of y_dtype (device), y_dtype in {desc->dtype, PATCH_F32}.
- *   workspace   may be NULL when patch_gemm_workspace_bytes() is 0.
+ *   workspace   device scratch of workspace_bytes (16-byte aligned), or NULL
+ *               with workspace_bytes = 0; see patch_gemm_workspace_bytes().
  * Asynchronous on `stream`.
  */
 patch_status patch_gemm(const patch_packed_desc* desc, const void* packed_dev, const void* X_dev, int64_t M,

@@ -50,6 +50,8 @@
 // dense, on v_mfma_f32_16x16x32: the same-shape dense baseline.
 #include "device_common.h"
 
+#include <algorithm>
+
 namespace patch {
 
 constexpr int kPfWaves = 8;
@@ -95,6 +97,8 @@ struct PfArgs {
   void* Y;
   int M, N, K, NT, KT, n_mblk, n_pairs;
   int mg;       // M-blocks per group (the output blocks are ordered group-major)
+  int splits;   // K ranges; above 1, Y is the fp32 partial buffer [splits][M][N]
+  int kt_split; // tile columns per K range
   int n_blocks, per_xcd;
 };
 
@@ -113,14 +117,16 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
   __shared__ uint32_t s_ent[2][kPfMaxKT];
   __shared__ uint32_t s_stride[2];  // band stride of each row-block of the pair
 
-  // Output blocks in order: M-group (mg M-blocks each), then row-block
-  // pair, then M-block; XCD x (workgroups are dealt to the 8 XCDs in turn)
-  // takes the x-th eighth of that order, so its blocks are a few pairs times
-  // one group's M-blocks.
+  // Output blocks in order: K range, M-group (mg M-blocks each), row-block
+  // pair, M-block; XCD x (workgroups are dealt to the 8 XCDs in turn) takes
+  // the x-th eighth of that order, so its blocks are a few pairs times one
+  // group's M-blocks, mostly in one K range.
   const int t = (blockIdx.x & 7) * P.per_xcd + (blockIdx.x >> 3);
   if (t >= P.n_blocks) return;  // whole workgroup
+  const int per_split = P.n_pairs * P.n_mblk;
+  const int ks = t / per_split, tk = t - (t / per_split) * per_split;
   const int grp = P.n_pairs * P.mg;
-  const int gi = t / grp, rem = t - (t / grp) * grp;
+  const int gi = tk / grp, rem = tk - (tk / grp) * grp;
   const int m_cnt = min(P.mg, P.n_mblk - gi * P.mg);
   const int p = rem / m_cnt, mb = gi * P.mg + rem % m_cnt;
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -132,14 +138,17 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
   const int i0 = p, i1 = P.NT - 1 - p;
   const int i_mine = r == 0 ? i0 : i1;
   const bool active = r == 0 || i1 != i0;  // a lone middle row-block has no second half
-  const int n_steps = 2 * KT;
+  // this workgroup's tile columns j0 .. j0 + nt - 1 (all of them unless split)
+  const int j0 = ks * P.kt_split;
+  const int nt = min(P.kt_split, KT - j0);
+  const int n_steps = 2 * nt;
 
   if constexpr (!SRC_ROWMAJOR) {
     const TileEntry* table = reinterpret_cast<const TileEntry*>(P.src + kHeaderBytes);
-    for (int e = threadIdx.x; e < 2 * KT; e += kPfWaves * 64) {
-      const int rr = e >= KT ? 1 : 0;
-      const int j = e - rr * KT;
-      const TileEntry te = table[(int64_t)(rr ? i1 : i0) * KT + j];
+    for (int e = threadIdx.x; e < 2 * nt; e += kPfWaves * 64) {
+      const int rr = e >= nt ? 1 : 0;
+      const int j = e - rr * nt;
+      const TileEntry te = table[(int64_t)(rr ? i1 : i0) * KT + j0 + j];
       s_ent[rr][j] = (uint32_t)(te.offset >> 8) | (te.kind ? 0x80000000u : 0u);
       if (j == 0) s_stride[rr] = te.band_stride;
     }
@@ -154,7 +163,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
   // eight 16-byte loads (only offsets differ), so registers and wait counts
   // are identical on both paths.
   auto load_a = [&](int s, StepA& A) -> uint32_t {
-    const int j = s >> 1, h = s & 1;
+    const int jl = s >> 1, h = s & 1, j = j0 + jl;
     if constexpr (SRC_ROWMAJOR) {
       // rows 64wn + 16b + (l & 15) of row-block i_mine, columns 128j + 64h + 32qq + 8hl
       const uint8_t* W = P.src + (((int64_t)i_mine * kTile + 64 * wn) * K + (int64_t)j * kTile + 64 * h) * 2;
@@ -166,7 +175,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
         for (int b = 0; b < 4; b++) A.a[qq][b] = bload16(rs, lane_rm, (uint32_t)(16 * b * K + 32 * qq) * 2u);
       return 0u;
     } else {
-      const uint32_t e = __builtin_amdgcn_readfirstlane(s_ent[r][j]);
+      const uint32_t e = __builtin_amdgcn_readfirstlane(s_ent[r][jl]);
       const uint32_t kind = e >> 31;
       // the wave's first band piece; band 4wn+b is b * stride further on
       const uint8_t* piece = P.src + ((uint64_t)(e & 0x7fffffffu) << 8) + (uint64_t)(4 * wn) * stride;
@@ -201,7 +210,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
   const __amdgpu_buffer_rsrc_t rx =
       make_rsrc(P.X + (int64_t)m0 * K, (uint32_t)min(BM, P.M - m0) * (uint32_t)K * 2u);
   auto load_x = [&](int s, u32x4 (&xr)[kXChunks]) {
-    const uint32_t col = (uint32_t)((s >> 1) * kTile + 64 * (s & 1)) * 2u;
+    const uint32_t col = (uint32_t)((j0 + (s >> 1)) * kTile + 64 * (s & 1)) * 2u;
 #pragma unroll
     for (int u = 0; u < kXChunks; u++) xr[u] = bload16(rx, lane_x[u], col);
   };
@@ -355,7 +364,10 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
     }
   }
 
-  // ---- epilogue: round and store Y[m][n .. n+3]
+  // ---- epilogue: round and store Y[m][n .. n+3] (split: the fp32 partial
+  // of K range ks, at plane ks of the partial buffer)
+  void* Yp = P.Y;
+  if (P.splits > 1) Yp = reinterpret_cast<float*>(P.Y) + (int64_t)ks * P.M * P.N;
   if (active) {
 #pragma unroll
     for (int mblk = 0; mblk < kNMB; mblk++) {
@@ -364,7 +376,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
 #pragma unroll
         for (int b = 0; b < 4; b++) {
           const int64_t n = (int64_t)i_mine * kTile + 16 * (4 * wn + b) + 4 * hl;
-          store4<BF16, OUT_F32>(P.Y, (int64_t)m * P.N + n, acc[b][mblk]);
+          store4<BF16, OUT_F32>(Yp, (int64_t)m * P.N + n, acc[b][mblk]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -385,49 +397,75 @@ static int cu_count() {
   return cached[dev];
 }
 
-// Launch shape.  The M-block width: the grid runs in rounds of one
-// workgroup per CU, so pick the width whose last round is fullest, weighted
-// by how well each width reuses W (a narrower block re-reads W for more
-// blocks of M).  Then the number of M-groups: each XCD (one L2) works on
-// about 1/8 of the output blocks in the group-major order.  Four groups (so
-// an XCD holds some 2/8 of W's row-blocks and 1/4 of X) measured fastest or
-// within 2% of it on the LLaMA-2 7B and 13B prefill shapes, against 3-10%
-// slower with one group (every XCD reading all of X); with fewer than 8
-// M-blocks, groups of at least two M-blocks.
+// Launch shape: the M-block width BM and the number of K ranges, chosen
+// by a cost model of this kernel fitted to its measured times on the
+// LLaMA-2 7B q_proj, gate_proj and down_proj shapes (64 <= M <= 512, every
+// width, 1 to 12 ranges; 4% rms error, and its pick is within 2% of the
+// fastest measured choice on each shape):
+//   t = rounds * (3.0 + tiles * (0.93 + 0.0082 * BM)) us
+//       + with a split: 6.8 us + partial bytes / 3.5 TB/s (second kernel),
+// rounds = ceil(workgroups / CUs), tiles = tile columns per K range.  A K
+// range holds at least two tile columns, and the partial sums (ranges * M *
+// N * 4 bytes) stay within 2 * N * K bytes.  Then the number of M-groups:
+// each XCD (one L2) works on about 1/8 of the output blocks in the
+// group-major order.  Four groups (so an XCD holds some 2/8 of W's
+// row-blocks and 1/4 of X) measured fastest or within 2% of it on the
+// LLaMA-2 7B and 13B prefill shapes, against 3-10% slower with one group
+// (every XCD reading all of X); with fewer than 8 M-blocks, groups of at
+// least two M-blocks.
 struct PfShape {
-  int bm, groups;
+  int bm, groups, splits, kt_split;
 };
-static PfShape choose_shape(int64_t M, int64_t N) {
+static double shape_cost_us(int64_t M, int64_t N, int64_t K, int bm, int64_t splits, int64_t kt_split) {
   const int64_t pairs = (N / kTile + 1) / 2;
-  const int cus = cu_count();
-  const int widths[3] = {256, 192, 128};
-  const double reuse[3] = {1.0, 0.94, 0.85};
-  PfShape best = {256, 1};
-  double best_score = -1.0;
-  for (int c = 0; c < 3; c++) {
-    const int64_t mblk = (M + widths[c] - 1) / widths[c];
-    const int64_t blocks = pairs * mblk;
-    const int64_t rounds = (blocks + cus - 1) / cus;
-    const double useful = (double)M / (double)(mblk * widths[c]);
-    const double score = reuse[c] * useful * (double)blocks / (double)(rounds * cus);
-    if (score > best_score + 1e-9) {
-      best_score = score;
-      best.bm = widths[c];
+  const int64_t blocks = pairs * ((M + bm - 1) / bm) * splits;
+  const int64_t rounds = (blocks + cu_count() - 1) / cu_count();
+  double t = (double)rounds * (3.0 + (double)kt_split * (0.93 + 0.0082 * bm));
+  if (splits > 1) t += 6.8 + (double)splits * (double)M * (double)N * 4.0 / 3.5e6;
+  return t;
+}
+static PfShape choose_shape(int64_t M, int64_t N, int64_t K) {
+  const int64_t KT = K / kTile;
+  const int widths[4] = {256, 192, 128, 64};
+  const int wants[10] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
+  const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(KT / 2, K / (2 * M)));
+  PfShape best = {256, 1, 1, (int)KT};
+  double best_t = -1.0;
+  for (int c = 0; c < 4; c++) {
+    for (int w = 0; w < 10 && wants[w] <= smax; w++) {
+      const int64_t kt_split = (KT + wants[w] - 1) / wants[w];
+      const int64_t splits = (KT + kt_split - 1) / kt_split;
+      const double t = shape_cost_us(M, N, K, widths[c], splits, kt_split);
+      if (best_t < 0 || t < best_t) {
+        best_t = t;
+        best = {widths[c], 1, (int)splits, (int)kt_split};
+      }
     }
   }
   const int64_t mblk = (M + best.bm - 1) / best.bm;
-  best.groups = 1;
   while (best.groups < 4 && 2 * best.groups * 2 <= mblk) best.groups *= 2;
   return best;
 }
 
+// Adds the fp32 partial sums of the K ranges in range order (so the result
+// does not depend on which workgroup finished first) and rounds to Y.
+template <bool BF16, bool OUT_F32>
+__global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ part, int splits, int64_t mn,
+                                                      void* __restrict__ Y) {
+  const int64_t q = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
+  if (q >= mn) return;
+  f32x4 sum = *reinterpret_cast<const f32x4*>(part + q);
+  for (int k = 1; k < splits; k++) sum += *reinterpret_cast<const f32x4*>(part + (int64_t)k * mn + q);
+  store4<BF16, OUT_F32>(Y, q, sum);
+}
+
 template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, int BM, int DIST>
 static hipError_t launch_prefill_bm(const void* src, const void* X, int64_t M, int64_t N, int64_t K, void* Y,
-                                    int groups, hipStream_t s) {
+                                    const PfShape& sh, float* part, hipStream_t s) {
   PfArgs a;
   a.src = reinterpret_cast<const uint8_t*>(src);
   a.X = reinterpret_cast<const uint16_t*>(X);
-  a.Y = Y;
+  a.Y = sh.splits > 1 ? static_cast<void*>(part) : Y;
   a.M = (int)M;
   a.N = (int)N;
   a.K = (int)K;
@@ -435,38 +473,80 @@ static hipError_t launch_prefill_bm(const void* src, const void* X, int64_t M, i
   a.KT = (int)(K / kTile);
   a.n_mblk = (int)((M + BM - 1) / BM);
   a.n_pairs = (a.NT + 1) / 2;
-  a.mg = (a.n_mblk + groups - 1) / groups;
-  a.n_blocks = a.n_pairs * a.n_mblk;
+  a.mg = (a.n_mblk + sh.groups - 1) / sh.groups;
+  a.splits = sh.splits;
+  a.kt_split = sh.kt_split;
+  a.n_blocks = a.n_pairs * a.n_mblk * sh.splits;
   a.per_xcd = (a.n_blocks + 7) / 8;
-  hipLaunchKernelGGL((k_prefill<BF16, SRC_ROWMAJOR, OUT_F32, BM, DIST>), dim3((unsigned)(8 * a.per_xcd)),
-                     dim3(kPfWaves * 64), 0, s, a);
+  if (sh.splits > 1) {
+    hipLaunchKernelGGL((k_prefill<BF16, SRC_ROWMAJOR, true, BM, DIST>), dim3((unsigned)(8 * a.per_xcd)),
+                       dim3(kPfWaves * 64), 0, s, a);
+    const int64_t mn = M * N;
+    hipLaunchKernelGGL((k_split_reduce<BF16, OUT_F32>), dim3((unsigned)((mn / 4 + 255) / 256)), dim3(256), 0, s,
+                       part, sh.splits, mn, Y);
+  } else {
+    hipLaunchKernelGGL((k_prefill<BF16, SRC_ROWMAJOR, OUT_F32, BM, DIST>), dim3((unsigned)(8 * a.per_xcd)),
+                       dim3(kPfWaves * 64), 0, s, a);
+  }
   return hipGetLastError();
+}
+
+// The shape for these sizes with the split limited to what the workspace
+// holds (no workspace: no split).
+static PfShape shape_for(int64_t M, int64_t N, int64_t K, uint64_t ws_bytes) {
+  PfShape sh = choose_shape(M, N, K);
+  const uint64_t plane = (uint64_t)M * (uint64_t)N * 4u;
+  const int64_t KT = K / kTile;
+  if (sh.splits > 1 && (uint64_t)sh.splits * plane > ws_bytes) {
+    int64_t fit = (int64_t)(ws_bytes / plane);
+    if (fit < 2) {
+      sh.splits = 1;
+      sh.kt_split = (int)KT;
+    } else {
+      sh.kt_split = (int)((KT + fit - 1) / fit);
+      sh.splits = (int)((KT + sh.kt_split - 1) / sh.kt_split);
+    }
+  }
+  return sh;
+}
+
+uint64_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const PfShape sh = choose_shape(M, N, K);
+  return sh.splits > 1 ? (uint64_t)sh.splits * (uint64_t)M * (uint64_t)N * 4u : 0u;
+}
+
+// The cost model's time for the shape this workspace allows.
+double prefill_estimate_us(int64_t M, int64_t N, int64_t K, uint64_t ws_bytes) {
+  const PfShape sh = shape_for(M, N, K, ws_bytes);
+  return shape_cost_us(M, N, K, sh.bm, sh.splits, sh.kt_split);
 }
 
 template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32>
 static hipError_t launch_prefill_t(const void* src, const void* X, int64_t M, int64_t N, int64_t K, void* Y,
-                                   hipStream_t s) {
-  const PfShape sh = choose_shape(M, N);
+                                   void* ws, uint64_t ws_bytes, hipStream_t s) {
+  const PfShape sh = shape_for(M, N, K, ws ? ws_bytes : 0u);
+  float* part = reinterpret_cast<float*>(ws);
   switch (sh.bm) {
-    case 128: return launch_prefill_bm<BF16, SRC_ROWMAJOR, OUT_F32, 128, 2>(src, X, M, N, K, Y, sh.groups, s);
-    case 192: return launch_prefill_bm<BF16, SRC_ROWMAJOR, OUT_F32, 192, 1>(src, X, M, N, K, Y, sh.groups, s);
-    default: return launch_prefill_bm<BF16, SRC_ROWMAJOR, OUT_F32, 256, 1>(src, X, M, N, K, Y, sh.groups, s);
+    case 64: return launch_prefill_bm<BF16, SRC_ROWMAJOR, OUT_F32, 64, 2>(src, X, M, N, K, Y, sh, part, s);
+    case 128: return launch_prefill_bm<BF16, SRC_ROWMAJOR, OUT_F32, 128, 2>(src, X, M, N, K, Y, sh, part, s);
+    case 192: return launch_prefill_bm<BF16, SRC_ROWMAJOR, OUT_F32, 192, 1>(src, X, M, N, K, Y, sh, part, s);
+    default: return launch_prefill_bm<BF16, SRC_ROWMAJOR, OUT_F32, 256, 1>(src, X, M, N, K, Y, sh, part, s);
   }
 }
 
 hipError_t launch_prefill(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* X, int64_t M, int64_t N,
-                          int64_t K, void* Y, hipStream_t s) {
+                          int64_t K, void* Y, void* ws, uint64_t ws_bytes, hipStream_t s) {
   if (K / kTile > kPfMaxKT) return hipErrorInvalidValue;
   if (bf16) {
-    if (rowmajor) return out_f32 ? launch_prefill_t<true, true, true>(src, X, M, N, K, Y, s)
-                                 : launch_prefill_t<true, true, false>(src, X, M, N, K, Y, s);
-    return out_f32 ? launch_prefill_t<true, false, true>(src, X, M, N, K, Y, s)
-                   : launch_prefill_t<true, false, false>(src, X, M, N, K, Y, s);
+    if (rowmajor) return out_f32 ? launch_prefill_t<true, true, true>(src, X, M, N, K, Y, ws, ws_bytes, s)
+                                 : launch_prefill_t<true, true, false>(src, X, M, N, K, Y, ws, ws_bytes, s);
+    return out_f32 ? launch_prefill_t<true, false, true>(src, X, M, N, K, Y, ws, ws_bytes, s)
+                   : launch_prefill_t<true, false, false>(src, X, M, N, K, Y, ws, ws_bytes, s);
   }
-  if (rowmajor) return out_f32 ? launch_prefill_t<false, true, true>(src, X, M, N, K, Y, s)
-                               : launch_prefill_t<false, true, false>(src, X, M, N, K, Y, s);
-  return out_f32 ? launch_prefill_t<false, false, true>(src, X, M, N, K, Y, s)
-                 : launch_prefill_t<false, false, false>(src, X, M, N, K, Y, s);
+  if (rowmajor) return out_f32 ? launch_prefill_t<false, true, true>(src, X, M, N, K, Y, ws, ws_bytes, s)
+                               : launch_prefill_t<false, true, false>(src, X, M, N, K, Y, ws, ws_bytes, s);
+  return out_f32 ? launch_prefill_t<false, false, true>(src, X, M, N, K, Y, ws, ws_bytes, s)
+                 : launch_prefill_t<false, false, false>(src, X, M, N, K, Y, ws, ws_bytes, s);
 }
 
 }  // namespace patch

@@ -15,7 +15,10 @@ hipError_t launch_pack(const void* W, const uint8_t* mask, int64_t N, int64_t K,
 hipError_t launch_decode(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* X, int64_t M, int64_t N,
                          int64_t K, void* Y, hipStream_t s);
 hipError_t launch_prefill(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* X, int64_t M, int64_t N,
-                          int64_t K, void* Y, hipStream_t s);
+                          int64_t K, void* Y, void* ws, uint64_t ws_bytes, hipStream_t s);
+uint64_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K);
+double prefill_estimate_us(int64_t M, int64_t N, int64_t K, uint64_t ws_bytes);
+double decode_estimate_us(int64_t M, int64_t N, int64_t K, double w_bytes);
 }  // namespace patch
 
 namespace {
@@ -31,6 +34,7 @@ constexpr int64_t kMaxDim = int64_t(1) << 20;  // N, K upper bound (int32 indexi
 constexpr int64_t kMaxKT = 1024;              // prefill kernel's per-workgroup tile lists
 constexpr int64_t kDecodeMaxK = 65536;        // decode kernel: <= 64 tile columns per wave
 constexpr int64_t kDecodeMaxM = 128;          // decode kernel: <= 8 blocks of 16 columns of M
+constexpr int64_t kDecodeAutoM = 16;          // AUTO: always decode up to here
 constexpr uint64_t kErrFlagOffset = 252;
 
 thread_local std::string g_err;
@@ -231,14 +235,23 @@ patch_status patch_desc_from_header(const void* header_host, uint64_t header_byt
   return PATCH_OK;
 }
 
-uint64_t patch_gemm_workspace_bytes(const patch_packed_desc* desc, int64_t M) {
-  (void)desc;
-  (void)M;
-  return 0;
+static uint64_t workspace_for(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || M > (int64_t)0x7fffffff || N <= 0 || K <= 0 || N % kTile || K % kTile || N > kMaxDim || K > kMaxDim ||
+      K / kTile > kMaxKT)
+    return 0;
+  return patch::prefill_workspace_bytes(M, N, K);
 }
 
+uint64_t patch_gemm_workspace_bytes(const patch_packed_desc* desc, int64_t M) {
+  if (!desc) return 0;
+  return workspace_for(M, desc->N, desc->K);
+}
+
+uint64_t patch_dense_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) { return workspace_for(M, N, K); }
+
 static patch_status gemm_common(bool rowmajor, patch_dtype dt, int64_t M, int64_t N, int64_t K, const void* src,
-                                const void* X_dev, void* Y_dev, patch_dtype y_dtype, int32_t variant, void* stream) {
+                                uint64_t w_bytes, const void* X_dev, void* Y_dev, patch_dtype y_dtype, void* ws,
+                                uint64_t ws_bytes, int32_t variant, void* stream) {
   patch_status s;
   if ((s = check_ydtype(dt, y_dtype))) return s;
   if (M < 0 || M > (int64_t)0x7fffffff) return fail(PATCH_ERR_INVALID_ARG, "M=%lld out of range", (long long)M);
@@ -250,14 +263,20 @@ static patch_status gemm_common(bool rowmajor, patch_dtype dt, int64_t M, int64_
   if (!src || !X_dev || !Y_dev) return fail(PATCH_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned16(src) || !aligned16(X_dev) || !aligned16(Y_dev))
     return fail(PATCH_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  if (ws_bytes > 0 && (!ws || !aligned16(ws)))
+    return fail(PATCH_ERR_INVALID_ARG, "workspace must be non-null and 16-byte aligned when workspace_bytes > 0");
   if (variant == PATCH_VARIANT_DECODE && K > kDecodeMaxK)
     return fail(PATCH_ERR_UNSUPPORTED, "decode variant needs K <= %lld (K=%lld)", (long long)kDecodeMaxK, (long long)K);
-  const bool decode =
-      variant == PATCH_VARIANT_DECODE || (variant == PATCH_VARIANT_AUTO && M <= kDecodeMaxM && K <= kDecodeMaxK);
+  // AUTO: decode for up to 16 tokens; up to 128, whichever kernel's time
+  // model is lower (the prefill one for the split the workspace allows).
+  bool decode = variant == PATCH_VARIANT_DECODE;
+  if (variant == PATCH_VARIANT_AUTO && K <= kDecodeMaxK && M <= kDecodeMaxM)
+    decode = M <= kDecodeAutoM || patch::decode_estimate_us(M, N, K, (double)w_bytes) <=
+                                      patch::prefill_estimate_us(M, N, K, ws ? ws_bytes : 0);
   const bool bf16 = dt == PATCH_BF16, f32out = y_dtype == PATCH_F32;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = decode ? patch::launch_decode(bf16, rowmajor, f32out, src, X_dev, M, N, K, Y_dev, st)
-                        : patch::launch_prefill(bf16, rowmajor, f32out, src, X_dev, M, N, K, Y_dev, st);
+                        : patch::launch_prefill(bf16, rowmajor, f32out, src, X_dev, M, N, K, Y_dev, ws, ws_bytes, st);
   if (e != hipSuccess) return hip_fail(e, decode ? "launch decode" : "launch prefill");
   return PATCH_OK;
 }
@@ -265,12 +284,11 @@ static patch_status gemm_common(bool rowmajor, patch_dtype dt, int64_t M, int64_
 patch_status patch_gemm_ex(const patch_packed_desc* desc, const void* packed_dev, const void* X_dev, int64_t M,
                            void* Y_dev, patch_dtype y_dtype, void* workspace_dev, uint64_t workspace_bytes,
                            int32_t variant, void* stream) {
-  (void)workspace_dev;
-  (void)workspace_bytes;
   patch_status s = check_desc(desc);
   if (s) return s;
-  return gemm_common(false, (patch_dtype)desc->dtype, M, desc->N, desc->K, packed_dev, X_dev, Y_dev, y_dtype, variant,
-                     stream);
+  return gemm_common(false, (patch_dtype)desc->dtype, M, desc->N, desc->K, packed_dev,
+                     desc->total_bytes - desc->data_offset, X_dev, Y_dev, y_dtype, workspace_dev, workspace_bytes,
+                     variant, stream);
 }
 
 patch_status patch_gemm(const patch_packed_desc* desc, const void* packed_dev, const void* X_dev, int64_t M,
@@ -283,12 +301,11 @@ patch_status patch_gemm(const patch_packed_desc* desc, const void* packed_dev, c
 patch_status patch_dense_gemm_ex(patch_dtype dtype, int64_t M, int64_t N, int64_t K, const void* X_dev,
                                  const void* W_dev, void* Y_dev, patch_dtype y_dtype, void* workspace_dev,
                                  uint64_t workspace_bytes, int32_t variant, void* stream) {
-  (void)workspace_dev;
-  (void)workspace_bytes;
   patch_status s;
   if ((s = check_dtype(dtype))) return s;
   if ((s = check_nk(N, K))) return s;
-  return gemm_common(true, dtype, M, N, K, W_dev, X_dev, Y_dev, y_dtype, variant, stream);
+  return gemm_common(true, dtype, M, N, K, W_dev, (uint64_t)(N * K * 2), X_dev, Y_dev, y_dtype, workspace_dev,
+                     workspace_bytes, variant, stream);
 }
 
 patch_status patch_dense_gemm(patch_dtype dtype, int64_t M, int64_t N, int64_t K, const void* X_dev,

@@ -43,7 +43,8 @@ class Desc(ctypes.Structure):
 
 
 EXPORTS = ("patch_abi_version", "patch_packed_bytes", "patch_pack", "patch_desc_from_header",
-           "patch_gemm_workspace_bytes", "patch_gemm", "patch_gemm_ex", "patch_dense_gemm", "patch_dense_gemm_ex",
+           "patch_gemm_workspace_bytes", "patch_dense_gemm_workspace_bytes", "patch_gemm", "patch_gemm_ex",
+           "patch_dense_gemm", "patch_dense_gemm_ex",
            "patch_status_string", "patch_last_error")
 
 _lib = None
@@ -69,6 +70,8 @@ def load():
     lib.patch_desc_from_header.restype = ctypes.c_int
     lib.patch_gemm_workspace_bytes.argtypes = [DP, I64]
     lib.patch_gemm_workspace_bytes.restype = U64
+    lib.patch_dense_gemm_workspace_bytes.argtypes = [I64, I64, I64]
+    lib.patch_dense_gemm_workspace_bytes.restype = U64
     lib.patch_gemm.argtypes = [DP, P, P, I64, P, ctypes.c_int, P, U64, P]
     lib.patch_gemm.restype = ctypes.c_int
     lib.patch_gemm_ex.argtypes = [DP, P, P, I64, P, ctypes.c_int, P, U64, I32, P]
@@ -165,21 +168,33 @@ def desc_from_header(header: bytes) -> Desc:
     return d
 
 
+def _workspace(nbytes: int, workspace, device):
+    """workspace="auto": a fresh buffer of the size the library asks for
+    (from torch's caching allocator); None: no workspace; a tensor: used as
+    given."""
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError(f"workspace must be 'auto', None or a tensor, not {workspace!r}")
+        return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes > 0 else None
+    return workspace
+
+
 def gemm(X: torch.Tensor, packed: PackedWeight, out_dtype: Optional[torch.dtype] = None, variant: str = "auto",
-         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+         out: Optional[torch.Tensor] = None, workspace="auto") -> torch.Tensor:
     """Y = X (W o E)^T from a packed blob (patch_gemm_ex)."""
     lib = load()
     M = X.shape[0]
     od = out_dtype or X.dtype
     if out is None:
         out = torch.empty((M, packed.N), dtype=od, device=X.device)
-    _check(lib.patch_gemm_ex(ctypes.byref(packed.desc), _ptr(packed.blob), _ptr(X), M, _ptr(out), _dt(od), None, 0,
-                             VARIANTS[variant], _stream()))
+    ws = _workspace(int(lib.patch_gemm_workspace_bytes(ctypes.byref(packed.desc), M)), workspace, X.device)
+    _check(lib.patch_gemm_ex(ctypes.byref(packed.desc), _ptr(packed.blob), _ptr(X), M, _ptr(out), _dt(od), _ptr(ws),
+                             0 if ws is None else ws.numel() * ws.element_size(), VARIANTS[variant], _stream()))
     return out
 
 
 def dense_gemm(X: torch.Tensor, W: torch.Tensor, out_dtype: Optional[torch.dtype] = None, variant: str = "auto",
-               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+               out: Optional[torch.Tensor] = None, workspace="auto") -> torch.Tensor:
     """Same-shape dense baseline Y = X W^T from row-major W (patch_dense_gemm_ex)."""
     lib = load()
     M, K = X.shape
@@ -187,6 +202,8 @@ def dense_gemm(X: torch.Tensor, W: torch.Tensor, out_dtype: Optional[torch.dtype
     od = out_dtype or X.dtype
     if out is None:
         out = torch.empty((M, N), dtype=od, device=X.device)
-    _check(lib.patch_dense_gemm_ex(_dt(X.dtype), M, N, K, _ptr(X), _ptr(W), _ptr(out), _dt(od), None, 0,
-                                   VARIANTS[variant], _stream()))
+    ws = _workspace(int(lib.patch_dense_gemm_workspace_bytes(M, N, K)), workspace, X.device)
+    _check(lib.patch_dense_gemm_ex(_dt(X.dtype), M, N, K, _ptr(X), _ptr(W), _ptr(out), _dt(od), _ptr(ws),
+                                   0 if ws is None else ws.numel() * ws.element_size(), VARIANTS[variant],
+                                   _stream()))
     return out

@@ -110,3 +110,18 @@ def test_desc_from_oracle_header_and_gemm_checks():
     d.n_sparse += 1  # descriptor no longer matches its sizes
     assert patch.STATUS[lib.patch_gemm(ctypes.byref(d), ctypes.c_void_p(16), ctypes.c_void_p(16), 4,
                                        ctypes.c_void_p(16), 1, None, 0, None)] == "PATCH_ERR_INVALID_ARG"
+
+
+def test_workspace_query_host_logic():
+    """The workspace query is host logic: K is split only when the output
+    blocks cannot fill the GPU, into whole M x N fp32 planes, never more
+    bytes than 2 * N * K, and nothing for invalid shapes."""
+    lib = patch.load()
+    ws = lambda M, N, K: int(lib.patch_dense_gemm_workspace_bytes(M, N, K))
+    assert ws(2048, 11008, 4096) == 0  # 43 row-block pairs x 8+ M-blocks fill the GPU
+    for M, N, K in [(128, 4096, 4096), (64, 4096, 11008), (17, 512, 4096), (300, 384, 4096)]:
+        b = ws(M, N, K)
+        assert b > 0 and b % (M * N * 4) == 0 and b <= 2 * N * K, (M, N, K, b)
+        assert b // (M * N * 4) <= K // 256  # at least two tile columns a range
+    for bad in [(0, 4096, 4096), (-1, 4096, 4096), (16, 100, 4096), (16, 4096, 100), (16, 4096, 128 * 1025)]:
+        assert ws(*bad) == 0, bad

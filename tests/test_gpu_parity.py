@@ -11,6 +11,8 @@ the fp64 oracle (tests/gpu_util.py); cases whose exact result is
 representable (identity X, small integers with a float32 output) must match
 exactly.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -177,6 +179,39 @@ def test_prefill_m_groups(M):
     X = dev_bits(Xb, "bf16")
     assert_close(patch.gemm(X, pw, variant="prefill"), ref, what=f"M={M}")
     assert_close(patch.gemm(X, pw, out_dtype=torch.float32, variant="prefill"), ref, f32=True, what=f"M={M} f32")
+
+
+@pytest.mark.parametrize("N,K", [(512, 4096), (256, 2688), (384, 4096)])
+@pytest.mark.parametrize("M", [17, 64, 128, 200, 300])
+def test_prefill_split_k(N, K, M):
+    """Few output blocks: prefill splits K into ranges (the last one short
+    where the tile count does not divide) and adds the fp32 partials in range
+    order in a second kernel.  Every output against the oracle with the
+    workspace the library asks for, with a workspace of two planes (fewer
+    ranges) and with none (no split); the dense baseline takes the same
+    path."""
+    lib = patch.load()
+    p = inputs.make_custom("bf16", N, K, 18, "bernoulli", 0.5, "uniform")
+    pw, W = _pack(p)
+    Xb = inputs.make_custom_x("bf16", M, K, 19)
+    X = dev_bits(Xb, "bf16")
+    ref = _ref(p, Xb)
+    need = int(lib.patch_gemm_workspace_bytes(ctypes.byref(pw.desc), M))
+    assert need > 0 and need % (M * N * 4) == 0, need
+    two = torch.empty(2 * M * N * 4, dtype=torch.uint8, device="cuda")
+    for ws in ("auto", two, None):
+        tag = ws if isinstance(ws, str) or ws is None else "two planes"
+        assert_close(patch.gemm(X, pw, variant="prefill", workspace=ws), ref, what=f"M={M} ws={tag}")
+        assert_close(patch.gemm(X, pw, out_dtype=torch.float32, variant="prefill", workspace=ws), ref, f32=True,
+                     what=f"M={M} ws={tag} f32")
+    pd = inputs.make_custom("bf16", N, K, 18, "dense", 0.0, "top2")
+    assert_close(patch.dense_gemm(X, W, variant="prefill"), _ref(pd, Xb), what=f"dense M={M}")
+    # AUTO with the workspace takes the split prefill path for M > 16, and is
+    # deterministic run to run
+    a = patch.gemm(X, pw, out_dtype=torch.float32)
+    b = patch.gemm(X, pw, out_dtype=torch.float32)
+    assert torch.equal(a, b)
+    assert_close(a, ref, f32=True, what=f"auto M={M}")
 
 
 # ------------------------------------------------------------------ exact cases
