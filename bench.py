@@ -111,6 +111,67 @@ def time_launches(calls, steps, warmup, batches=1):
     return ms_step, per
 
 
+def _capture(fns):
+    """One HIP graph that runs fns in order (each a no-argument launch on
+    the current stream).  Every fn runs once eagerly first, on the capture
+    side stream, so lazy set-up happens outside the graph."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for f in fns[: min(len(fns), 8)]:
+            f()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graphs(calls, steps, warmup, batches=1):
+    """As time_launches, but the launches are captured in HIP graphs and the
+    graphs replayed, so host launch overhead is out of the timed region:
+      * ms per step: one graph of `steps` steps (every call once a step, back
+        to back), replayed once untimed and once between one event pair;
+      * {key: [ms per launch of each batch]}: per call, one graph of `steps`
+        launches, replayed `batches` times, each between one event pair.
+    Step k of either uses rotation index warmup + k, as the eager timing."""
+    import torch
+
+    for k in range(warmup):
+        for _, fn in calls:
+            fn(k)
+    torch.cuda.synchronize()
+    g = _capture([(lambda fn=fn, k=k: fn(warmup + k)) for k in range(steps) for _, fn in calls])
+    g.replay()
+    torch.cuda.synchronize()
+    a = _event()
+    g.replay()
+    b = _event()
+    torch.cuda.synchronize()
+    ms_step = a.elapsed_time(b) / steps
+    del g
+    per = {}
+    for key, fn in calls:
+        g = _capture([(lambda k=k: fn(warmup + k)) for k in range(steps)])
+        g.replay()
+        torch.cuda.synchronize()
+        per[key] = []
+        for _ in range(batches):
+            a = _event()
+            g.replay()
+            b = _event()
+            torch.cuda.synchronize()
+            per[key].append(a.elapsed_time(b) / steps)
+        del g
+    torch.cuda.empty_cache()
+    return ms_step, per
+
+
 def rotate(t, nbytes_each):
     import torch
 
@@ -172,13 +233,18 @@ def gemm_set(cfg_name, mi, si, Ms, steps, warmup, with_hipblaslt=True, fraction=
             torch.matmul(Xs[M], Ws[k % len(Ws)].t(), out=Ys[M])
         return f
 
-    ms_h, per_h = time_launches([(M, hyb(M)) for M in Ms], steps, warmup, batches)
-    ms_d, per_d = time_launches([(M, dense(M)) for M in Ms], steps, warmup, batches)
+    # our kernels: graph replays (launch overhead out of the timed region)
+    # and eager back-to-back launches; hipBLASLt (torch.matmul): eager only,
+    # since a library call may record work that graph replays do not repeat
+    # faithfully
+    ms_h, per_h = time_graphs([(M, hyb(M)) for M in Ms], steps, warmup, batches)
+    ms_d, per_d = time_graphs([(M, dense(M)) for M in Ms], steps, warmup, batches)
+    ms_he, per_he = time_launches([(M, hyb(M)) for M in Ms], steps, warmup, batches)
     per_b = None
     if with_hipblaslt:
         _, per_b = time_launches([(M, blas(M)) for M in Ms], steps, warmup, batches)
     res = dict(p=p, pw=pw, pack_ms=pack_ms, ms_step=ms_h, ms_step_dense=ms_d, per=per_h, per_dense=per_d,
-               per_blas=per_b, n_copies=len(blobs))
+               ms_step_eager=ms_he, per_eager=per_he, per_blas=per_b, n_copies=len(blobs))
     del blobs, Ws
     torch.cuda.empty_cache()
     return res
@@ -204,12 +270,13 @@ def summarize(res, Ms):
         fl = 2.0 * M * N * K
         eff = 2.0 * M * N * K * (1 - 0.5 * s)
         e = dict(us=t * 1e6, us_min=min(res["per"][M]) * 1e3, us_max=max(res["per"][M]) * 1e3,
-                 batches=len(res["per"][M]), dense_us=td * 1e6, tflops_dense_equiv=fl / t / 1e12, tflops_effective=eff / t / 1e12,
+                 batches=len(res["per"][M]), us_eager=median(res["per_eager"][M]) * 1e3, dense_us=td * 1e6, tflops_dense_equiv=fl / t / 1e12, tflops_effective=eff / t / 1e12,
                  gbps=algo_bytes(N, K, M, ns) / t / 1e9, speedup_vs_dense=td / t)
         if res["per_blas"] is not None:
+            # eager against eager: both include the host's launch cost
             tb = median(res["per_blas"][M]) * 1e-3
-            e["hipblaslt_us"] = tb * 1e6
-            e["speedup_vs_hipblaslt"] = tb / t
+            e["hipblaslt_us_eager"] = tb * 1e6
+            e["speedup_vs_hipblaslt_eager"] = tb / (e["us_eager"] * 1e-6)
         # roofline: max of HBM time and blended matrix-core time
         t_hbm = algo_bytes(N, K, M, ns) / (HBM_PEAK_GBS * 1e9)
         t_mma = 2.0 * M * 128 * 128 * ((T - ns) / MFMA_PEAK_BF16_TFLOPS + ns / (2 * MFMA_PEAK_BF16_TFLOPS)) / 1e12
@@ -396,6 +463,10 @@ def main():
             "N": p.N, "K": p.K, "Ms": list(Ms), "sparse_tiles": ns, "tiles": int(p.tile_map.size),
             "weight_copies_rotated": res["n_copies"],
         },
+        "ms_per_step_eager": res["ms_step_eager"],
+        "timing": "value and ms_per_step: one HIP graph of the K steps (3 patch_gemm launches each, cycling the "
+                  "weight copies), replayed between one event pair; ms_per_step_eager: the same launches issued "
+                  "from Python back to back",
         "speedup_vs_dense_step": res["ms_step_dense"] / res["ms_step"],
         "per_M": {str(M): summ[M] for M in Ms},
         "pack": {"us": res["pack_ms"] * 1e3,

@@ -416,15 +416,15 @@ static int cu_count() {
 struct PfShape {
   int bm, groups, splits, kt_split;
 };
-static double shape_cost_us(int64_t M, int64_t N, int64_t K, int bm, int64_t splits, int64_t kt_split) {
+static double shape_cost_us(int64_t M, int64_t N, int64_t K, int bm, int64_t splits, int64_t kt_split, int cus) {
   const int64_t pairs = (N / kTile + 1) / 2;
   const int64_t blocks = pairs * ((M + bm - 1) / bm) * splits;
-  const int64_t rounds = (blocks + cu_count() - 1) / cu_count();
+  const int64_t rounds = (blocks + cus - 1) / cus;
   double t = (double)rounds * (3.0 + (double)kt_split * (0.93 + 0.0082 * bm));
   if (splits > 1) t += 6.8 + (double)splits * (double)M * (double)N * 4.0 / 3.5e6;
   return t;
 }
-static PfShape choose_shape(int64_t M, int64_t N, int64_t K) {
+static PfShape choose_shape_uncached(int64_t M, int64_t N, int64_t K, int cus) {
   const int64_t KT = K / kTile;
   const int widths[4] = {256, 192, 128, 64};
   const int wants[10] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
@@ -435,7 +435,7 @@ static PfShape choose_shape(int64_t M, int64_t N, int64_t K) {
     for (int w = 0; w < 10 && wants[w] <= smax; w++) {
       const int64_t kt_split = (KT + wants[w] - 1) / wants[w];
       const int64_t splits = (KT + kt_split - 1) / kt_split;
-      const double t = shape_cost_us(M, N, K, widths[c], splits, kt_split);
+      const double t = shape_cost_us(M, N, K, widths[c], splits, kt_split, cus);
       if (best_t < 0 || t < best_t) {
         best_t = t;
         best = {widths[c], 1, (int)splits, (int)kt_split};
@@ -445,6 +445,27 @@ static PfShape choose_shape(int64_t M, int64_t N, int64_t K) {
   const int64_t mblk = (M + best.bm - 1) / best.bm;
   while (best.groups < 4 && 2 * best.groups * 2 <= mblk) best.groups *= 2;
   return best;
+}
+
+// The same, remembered for the last few shapes of this thread (a GEMM call
+// asks for it twice: the workspace query and the launch).
+static PfShape choose_shape(int64_t M, int64_t N, int64_t K) {
+  struct Entry {
+    int64_t M, N, K;
+    int cus;
+    PfShape sh;
+  };
+  constexpr int kSlots = 8;
+  thread_local Entry cache[kSlots];
+  thread_local int filled = 0, next = 0;
+  const int cus = cu_count();
+  for (int i = 0; i < filled; i++)
+    if (cache[i].M == M && cache[i].N == N && cache[i].K == K && cache[i].cus == cus) return cache[i].sh;
+  const PfShape sh = choose_shape_uncached(M, N, K, cus);
+  cache[next] = {M, N, K, cus, sh};
+  next = (next + 1) % kSlots;
+  if (filled < kSlots) filled++;
+  return sh;
 }
 
 // Adds the fp32 partial sums of the K ranges in range order (so the result
@@ -518,7 +539,7 @@ uint64_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 // The cost model's time for the shape this workspace allows.
 double prefill_estimate_us(int64_t M, int64_t N, int64_t K, uint64_t ws_bytes) {
   const PfShape sh = shape_for(M, N, K, ws_bytes);
-  return shape_cost_us(M, N, K, sh.bm, sh.splits, sh.kt_split);
+  return shape_cost_us(M, N, K, sh.bm, sh.splits, sh.kt_split, cu_count());
 }
 
 template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32>

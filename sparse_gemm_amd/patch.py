@@ -93,8 +93,14 @@ def _check(rc: int):
         raise PatchError(rc, load().patch_last_error().decode())
 
 
-def _stream() -> ctypes.c_void_p:
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(device_index: Optional[int] = None) -> int:
+    """The current HIP stream of the device, as an integer handle."""
+    if _raw_stream is not None:
+        return _raw_stream(torch.cuda.current_device() if device_index is None else device_index)
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
@@ -168,6 +174,22 @@ def desc_from_header(header: bytes) -> Desc:
     return d
 
 
+_WS_BYTES = {}
+
+
+def _ws_bytes(kind: str, M: int, N: int, K: int, dev: int, query) -> int:
+    """The library's workspace query, remembered per shape (it is a pure
+    function of the shape on a given device)."""
+    key = (kind, M, N, K, dev)
+    nb = _WS_BYTES.get(key)
+    if nb is None:
+        nb = int(query())
+        if len(_WS_BYTES) > 4096:
+            _WS_BYTES.clear()
+        _WS_BYTES[key] = nb
+    return nb
+
+
 def _workspace(nbytes: int, workspace, device):
     """workspace="auto": a fresh buffer of the size the library asks for
     (from torch's caching allocator); None: no workspace; a tensor: used as
@@ -182,28 +204,39 @@ def _workspace(nbytes: int, workspace, device):
 def gemm(X: torch.Tensor, packed: PackedWeight, out_dtype: Optional[torch.dtype] = None, variant: str = "auto",
          out: Optional[torch.Tensor] = None, workspace="auto") -> torch.Tensor:
     """Y = X (W o E)^T from a packed blob (patch_gemm_ex)."""
-    lib = load()
+    lib = _lib or load()
     M = X.shape[0]
     od = out_dtype or X.dtype
+    dev = X.get_device()
     if out is None:
         out = torch.empty((M, packed.N), dtype=od, device=X.device)
-    ws = _workspace(int(lib.patch_gemm_workspace_bytes(ctypes.byref(packed.desc), M)), workspace, X.device)
-    _check(lib.patch_gemm_ex(ctypes.byref(packed.desc), _ptr(packed.blob), _ptr(X), M, _ptr(out), _dt(od), _ptr(ws),
-                             0 if ws is None else ws.numel() * ws.element_size(), VARIANTS[variant], _stream()))
+    ws, nb = None, 0
+    if workspace is not None:
+        nb = _ws_bytes("packed", M, packed.N, packed.K, dev,
+                       lambda: lib.patch_gemm_workspace_bytes(ctypes.byref(packed.desc), M))
+        ws = _workspace(nb, workspace, X.device)
+        nb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.patch_gemm_ex(ctypes.byref(packed.desc), packed.blob.data_ptr(), X.data_ptr(), M, out.data_ptr(),
+                             _dt(od), None if ws is None else ws.data_ptr(), nb, VARIANTS[variant],
+                             _stream(dev)))
     return out
 
 
 def dense_gemm(X: torch.Tensor, W: torch.Tensor, out_dtype: Optional[torch.dtype] = None, variant: str = "auto",
                out: Optional[torch.Tensor] = None, workspace="auto") -> torch.Tensor:
     """Same-shape dense baseline Y = X W^T from row-major W (patch_dense_gemm_ex)."""
-    lib = load()
+    lib = _lib or load()
     M, K = X.shape
     N = W.shape[0]
     od = out_dtype or X.dtype
+    dev = X.get_device()
     if out is None:
         out = torch.empty((M, N), dtype=od, device=X.device)
-    ws = _workspace(int(lib.patch_dense_gemm_workspace_bytes(M, N, K)), workspace, X.device)
-    _check(lib.patch_dense_gemm_ex(_dt(X.dtype), M, N, K, _ptr(X), _ptr(W), _ptr(out), _dt(od), _ptr(ws),
-                                   0 if ws is None else ws.numel() * ws.element_size(), VARIANTS[variant],
-                                   _stream()))
+    ws, nb = None, 0
+    if workspace is not None:
+        nb = _ws_bytes("dense", M, N, K, dev, lambda: lib.patch_dense_gemm_workspace_bytes(M, N, K))
+        ws = _workspace(nb, workspace, X.device)
+        nb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.patch_dense_gemm_ex(_dt(X.dtype), M, N, K, X.data_ptr(), W.data_ptr(), out.data_ptr(), _dt(od),
+                                   None if ws is None else ws.data_ptr(), nb, VARIANTS[variant], _stream(dev)))
     return out

@@ -310,6 +310,50 @@ def test_deterministic_repeat():
         assert torch.equal(a, b), M
 
 
+def test_graph_replays_match_eager():
+    """The GEMM calls can be captured in a HIP graph (the bench times them
+    that way): decode, split-K prefill (with its workspace from the graph's
+    pool) and the dense baseline in one graph, replayed three times with
+    other eager GEMMs and synchronisations in between; every replay must
+    equal the eager results bit for bit (the kernels are deterministic)."""
+    p = inputs.make_custom("bf16", 512, 4096, 20, "bernoulli", 0.5, "uniform")
+    pw, W = _pack(p)
+    X4 = dev_bits(inputs.make_custom_x("bf16", 4, 4096, 21), "bf16")
+    X128 = dev_bits(inputs.make_custom_x("bf16", 128, 4096, 22), "bf16")
+    Xo = dev_bits(inputs.make_custom_x("bf16", 64, 4096, 23), "bf16")
+    outs = [torch.empty((4, 512), dtype=torch.bfloat16, device="cuda"),
+            torch.empty((128, 512), dtype=torch.float32, device="cuda"),
+            torch.empty((128, 512), dtype=torch.bfloat16, device="cuda")]
+
+    def run():
+        patch.gemm(X4, pw, out=outs[0])
+        patch.gemm(X128, pw, out_dtype=torch.float32, variant="prefill", out=outs[1])
+        patch.dense_gemm(X128, W, variant="prefill", out=outs[2])
+
+    run()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    assert int(patch.load().patch_gemm_workspace_bytes(ctypes.byref(pw.desc), 128)) > 0  # the split path
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(7.0)
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, eager):
+            assert torch.equal(a, b), f"replay {rep}"
+        other = patch.gemm(Xo, pw, variant="prefill")  # eager work between replays
+        torch.cuda.synchronize()
+        assert other.shape == (64, 512)
+
+
 # ------------------------------------------------------------------ the named workloads
 def test_config_tiny_all_seeds():
     cfg = inputs.CONFIGS["tiny"]
