@@ -57,8 +57,16 @@ typedef enum {
                                 than the GEMM's workspace query asks for */
   PATCH_VARIANT_DECODE = 1,  /* W-streaming kernel; valid for 1 <= M <= 128, K <= 65536
                                 (else PATCH_ERR_INVALID_ARG / PATCH_ERR_UNSUPPORTED) */
-  PATCH_VARIANT_PREFILL = 2  /* output-tiled MFMA kernel; any M >= 1; splits K when the
+  PATCH_VARIANT_PREFILL = 2, /* output-tiled MFMA kernel; any M >= 1; splits K when the
                                 output blocks cannot fill the GPU and workspace allows */
+  /* The prefill kernel at one M-block width and staging (K split as its
+   * cost model decides for that width, within the workspace passed): for
+   * tests and measurements that must run every kernel on the same shapes. */
+  PATCH_VARIANT_PREFILL_W64 = 3,      /* registers, 64 columns of M a workgroup */
+  PATCH_VARIANT_PREFILL_W128 = 4,     /* registers, 128 */
+  PATCH_VARIANT_PREFILL_W192 = 5,     /* registers, 192 */
+  PATCH_VARIANT_PREFILL_W256 = 6,     /* registers, 256 */
+  PATCH_VARIANT_PREFILL_W128_LDS = 7  /* W and X staged through LDS, 128 */
 } patch_variant;
 
 /* Host-side mirror of the packed blob's header (format version 3). */
@@ -137,8 +145,8 @@ patch_status patch_desc_from_header(const void* header_host, uint64_t header_byt
  */
 uint64_t patch_gemm_workspace_bytes(const patch_packed_desc* desc, int64_t M);
 
-/* The same for patch_dense_gemm on an N x K weight (it uses the same kernel
- * shapes). */
+/* The same for patch_dense_gemm on an N x K weight (its shape choice differs:
+ * it takes the LDS-staged kernel wherever the width would be 128 or more). */
 uint64_t patch_dense_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
@@ -167,7 +175,7 @@ patch_status patch_gemm_ex(const patch_packed_desc* desc, const void* packed_dev
 
 /*
  * Same-shape dense baseline: Y = X * W^T from plain row-major W (N x K), with
- * the same tiling and staging as patch_gemm, every tile dense, on
+ * the same kernels and tiling as patch_gemm, every tile dense, on
  * v_mfma_f32_16x16x32.
  */
 patch_status patch_dense_gemm(patch_dtype dtype, int64_t M, int64_t N, int64_t K, const void* X_dev,

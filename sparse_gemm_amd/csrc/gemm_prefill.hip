@@ -384,6 +384,264 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// k_prefill_lds: the same output tiling at BM = 128 with W and X staged
+// through LDS by global -> LDS copies, three steps deep.
+//
+//   * Per step every wave issues exactly six 1 KB copies (16 bytes a lane,
+//     straight into LDS, no registers): two 8-row chunks of the X stage and
+//     four W fragments -- wave (r, wn, wm) copies half wm of bands 4wn..4wn+3
+//     of row-block r (a 2:4 tile: the values if wm = 0, the band's codes if
+//     wm = 1), so each W byte enters the CU once, where the register-staged
+//     kernel loads every W fragment into both M-halves' waves.
+//   * Copies for step s+2 go out while step s computes; a wave waits for its
+//     own copies of step s with vmcnt (six newer copies may stay in flight)
+//     and the barrier after it publishes everyone's.  The copies are inline
+//     asm, so the compiler neither waits for them nor for anything else before
+//     LDS reads; the wait counts are exact because every wave issues the same
+//     six copies every step.
+//   * Fragments are then read from LDS with one 16-byte read a lane (the
+//     2:4 codes chunk holding the lane's word likewise) and fed to the same
+//     v_smfmac_f32_16x16x64 sequence as the register-staged kernel.
+// LDS: 3 x (32 KB of W + 16 KB of X) + the tile entries = 152 KB, one
+// workgroup per CU.
+// ---------------------------------------------------------------------------
+constexpr int kLdsBM = 128;
+constexpr int kLdsStages = 3;
+constexpr int kLdsWStage = 32768;                // 2 row-blocks x 8 bands x 2 fragments of 1 KB
+constexpr int kLdsXStage = kLdsBM * kPfRowBytes;  // 16 KB
+constexpr int kLdsCopies = 6;                    // copies a wave issues per step
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+// 16 bytes a lane, global -> LDS: lane l's bytes land at LDS byte lds + 16 l
+// (M0 holds the LDS base; it is saved and restored around the copy).
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(g)
+      : "memory");
+}
+// 4 bytes a lane, global -> LDS: lane l's bytes land at LDS byte lds + 4 l.
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dword %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(g)
+      : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32>
+__global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
+  constexpr int BM = kLdsBM;
+  constexpr int kNMB = BM / 32;  // 16-column M blocks per wave
+  __shared__ __attribute__((aligned(1024))) uint8_t s_w[kLdsStages * kLdsWStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_x[kLdsStages * kLdsXStage];
+  __shared__ uint32_t s_ent[2][kPfMaxKT];
+  __shared__ uint32_t s_stride[2];
+
+  const int t = (blockIdx.x & 7) * P.per_xcd + (blockIdx.x >> 3);
+  if (t >= P.n_blocks) return;  // whole workgroup
+  const int per_split = P.n_pairs * P.n_mblk;
+  const int ks = t / per_split, tk = t - (t / per_split) * per_split;
+  const int grp = P.n_pairs * P.mg;
+  const int gi = tk / grp, rem = tk - (tk / grp) * grp;
+  const int m_cnt = min(P.mg, P.n_mblk - gi * P.mg);
+  const int p = rem / m_cnt, mb = gi * P.mg + rem % m_cnt;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int l = threadIdx.x & 63;
+  const int r = w >> 2, wn = (w >> 1) & 1, wm = w & 1;
+  const int hl = l >> 4;
+  const int KT = P.KT, K = P.K, M = P.M;
+  const int m0 = mb * BM;
+  const int i0 = p, i1 = P.NT - 1 - p;
+  const bool active = r == 0 || i1 != i0;  // a lone middle row-block has no second half
+  const int i_mine = r == 0 ? i0 : i1;
+  // a wave with no row-block of its own copies row-block i0's fragments into
+  // its own (never read) LDS slots, so every wave issues the same copies
+  const int r_src = active ? r : 0;
+  const int i_src = active ? i_mine : i0;
+  const int j0 = ks * P.kt_split;
+  const int nt = min(P.kt_split, KT - j0);
+  const int n_steps = 2 * nt;
+
+  if constexpr (!SRC_ROWMAJOR) {
+    const TileEntry* table = reinterpret_cast<const TileEntry*>(P.src + kHeaderBytes);
+    for (int e = threadIdx.x; e < 2 * nt; e += kPfWaves * 64) {
+      const int rr = e >= nt ? 1 : 0;
+      const int j = e - rr * nt;
+      const TileEntry te = table[(int64_t)(rr ? i1 : i0) * KT + j0 + j];
+      s_ent[rr][j] = (uint32_t)(te.offset >> 8) | (te.kind ? 0x80000000u : 0u);
+      if (j == 0) s_stride[rr] = te.band_stride;
+    }
+    __syncthreads();
+  }
+  const uint32_t stride = SRC_ROWMAJOR ? 0u : (uint32_t)__builtin_amdgcn_readfirstlane((int)s_stride[r_src]);
+
+  // this wave's two 8-row chunks of each X stage: rows 8 (2w + u) + l/8, the
+  // lane fetching the source chunk whose swizzled position is l % 8; rows
+  // past M read row M - 1 (their outputs are never stored)
+  const uint16_t* xsrc[2];
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    const int row = 8 * (2 * w + u) + (l >> 3);
+    const int gm = min(m0 + row, M - 1);
+    xsrc[u] = P.X + (int64_t)gm * K + 8 * ((l & 7) ^ swz_f(row));
+  }
+  const uint32_t w_lds = lds_addr(s_w), x_lds = lds_addr(s_x);
+
+  // the six copies of step s into stage s % 3
+  auto issue = [&](int s) {
+    const int st = s % kLdsStages;
+    const int jl = s >> 1, h = s & 1, j = j0 + jl;
+    const uint32_t wb = w_lds + (uint32_t)(st * kLdsWStage), xb = x_lds + (uint32_t)(st * kLdsXStage);
+    const int col = j * kTile + 64 * h;
+#pragma unroll
+    for (int u = 0; u < 2; u++) dma16(xsrc[u] + col, xb + 1024u * (uint32_t)(2 * w + u));
+    // fragment slot of band 4wn + b, half e of row-block r: ((r*8 + 4wn + b)*2 + e) KB
+    const uint32_t slot0 = wb + 1024u * (uint32_t)((r * 8 + 4 * wn) * 2);
+    if constexpr (SRC_ROWMAJOR) {
+      // rows 16 (4wn + b) + l % 16 of row-block i_src, columns 64h + 32wm + 8(l/16) of tile j
+      const uint16_t* W = reinterpret_cast<const uint16_t*>(P.src) +
+                          ((int64_t)i_src * kTile + 64 * wn + (l & 15)) * K + (int64_t)col + 32 * wm + 8 * hl;
+#pragma unroll
+      for (int b = 0; b < 4; b++) dma16(W + (int64_t)16 * b * K, slot0 + 2048u * b + 1024u * wm);
+    } else {
+      const uint32_t e = __builtin_amdgcn_readfirstlane(s_ent[r_src][jl]);
+      const uint8_t* piece = P.src + ((uint64_t)(e & 0x7fffffffu) << 8) + (uint64_t)(4 * wn) * stride;
+      if ((e >> 31) == 0) {
+#pragma unroll
+        for (int b = 0; b < 4; b++)
+          dma16(piece + (uint64_t)b * stride + 2048 * h + 1024 * wm + 16 * l, slot0 + 2048u * b + 1024u * wm);
+      } else if (wm == 0) {
+#pragma unroll
+        for (int b = 0; b < 4; b++) dma16(piece + (uint64_t)b * stride + 1024 * h + 16 * l, slot0 + 2048u * b);
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; b++)
+          dma4(piece + (uint64_t)b * stride + kSparseMetaOffset + 4 * l, slot0 + 2048u * b + 1024u);
+      }
+    }
+  };
+
+  f32x4 acc[4][kNMB];
+#pragma unroll
+  for (int a = 0; a < 4; a++)
+#pragma unroll
+    for (int c = 0; c < kNMB; c++) acc[a][c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  auto read_b = [&](const uint8_t* xs, int g, u32x4 (&blo)[kPfMGroup], u32x4 (&bhi)[kPfMGroup]) {
+#pragma unroll
+    for (int mm = 0; mm < kPfMGroup; mm++) {
+      const int row = wm * (BM / 2) + (kPfMGroup * g + mm) * 16 + (l & 15);
+      blo[mm] = *reinterpret_cast<const u32x4*>(xs + swz(row, hl));
+      bhi[mm] = *reinterpret_cast<const u32x4*>(xs + swz(row, 4 + hl));
+    }
+  };
+
+  // step s from stage s % 3: this wave's A fragments from LDS, then the
+  // matrix instructions (as in k_prefill)
+  auto compute = [&](int s) {
+    const int st = s % kLdsStages;
+    const int jl = s >> 1, h = s & 1;
+    const uint8_t* ws = s_w + st * kLdsWStage + 1024 * ((r * 8 + 4 * wn) * 2);
+    const uint8_t* xs = s_x + st * kLdsXStage;
+    uint32_t kind = 0;
+    if constexpr (!SRC_ROWMAJOR) kind = __builtin_amdgcn_readfirstlane(s_ent[r_src][jl]) >> 31;
+    u32x4 a0[4], a1[4];
+    const int off1 = kind ? 16 * (l >> 2) : 16 * l;
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      a0[b] = *reinterpret_cast<const u32x4*>(ws + 2048 * b + 16 * l);
+      a1[b] = *reinterpret_cast<const u32x4*>(ws + 2048 * b + 1024 + off1);
+    }
+    if (!active) return;
+    if constexpr (SRC_ROWMAJOR) {
+#pragma unroll
+      for (int qq = 0; qq < 2; qq++) {
+        u32x4 bf[kNMB];
+#pragma unroll
+        for (int mblk = 0; mblk < kNMB; mblk++)
+          bf[mblk] = *reinterpret_cast<const u32x4*>(xs + swz(wm * (BM / 2) + mblk * 16 + (l & 15), 4 * qq + hl));
+#pragma unroll
+        for (int mblk = 0; mblk < kNMB; mblk++)
+#pragma unroll
+          for (int b = 0; b < 4; b++) acc[b][mblk] = mma_dense<BF16>(qq ? a1[b] : a0[b], bf[mblk], acc[b][mblk]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      const int nsub = kind == 0 ? 2 : 1;
+      uint32_t idx0[4];
+#pragma unroll
+      for (int b = 0; b < 4; b++) {
+        const u32x4 mc = a1[b];
+        const uint32_t lo = (l & 1) ? mc[1] : mc[0], hi = (l & 1) ? mc[3] : mc[2];
+        idx0[b] = kind == 0 ? 0x4444u : (((l & 2) ? hi : lo) >> (16 * h));
+      }
+      constexpr int kGroups = kNMB / kPfMGroup;
+      u32x4 blo[2][kPfMGroup], bhi[2][kPfMGroup];
+      read_b(xs, 0, blo[0], bhi[0]);
+#pragma unroll
+      for (int g = 0; g < kGroups; g++) {
+        if (g + 1 < kGroups) read_b(xs, g + 1, blo[(g + 1) & 1], bhi[(g + 1) & 1]);
+        for (int sub = 0; sub < nsub; sub++) {
+#pragma unroll
+          for (int mm = 0; mm < kPfMGroup; mm++)
+#pragma unroll
+            for (int b = 0; b < 4; b++)
+              acc[b][kPfMGroup * g + mm] =
+                  mma_sparse<BF16, 0>(sub ? a1[b] : a0[b], blo[g & 1][mm], bhi[g & 1][mm],
+                                      acc[b][kPfMGroup * g + mm], sub ? 0xEEEEu : idx0[b]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // ---- pipeline: copies two steps ahead
+  issue(0);
+  issue(1);  // n_steps >= 2
+  for (int s = 0; s < n_steps; s++) {
+    if (s + 1 < n_steps)
+      wait_copies<kLdsCopies>();  // this wave's copies of step s have landed
+    else
+      wait_copies<0>();
+    wg_barrier();  // everyone's have; everyone is done reading stage (s + 2) % 3
+    if (s + 2 < n_steps) issue(s + 2);
+    compute(s);
+  }
+
+  void* Yp = P.Y;
+  if (P.splits > 1) Yp = reinterpret_cast<float*>(P.Y) + (int64_t)ks * P.M * P.N;
+  if (active) {
+#pragma unroll
+    for (int mblk = 0; mblk < kNMB; mblk++) {
+      const int m = m0 + wm * (BM / 2) + mblk * 16 + (l & 15);
+      if (m < M) {
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+          const int64_t n = (int64_t)i_mine * kTile + 16 * (4 * wn + b) + 4 * hl;
+          store4<BF16, OUT_F32>(Yp, (int64_t)m * P.N + n, acc[b][mblk]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 // Number of compute units, read once per device.
 static int cu_count() {
   static int cached[64] = {0};
@@ -415,6 +673,7 @@ static int cu_count() {
 // least two M-blocks.
 struct PfShape {
   int bm, groups, splits, kt_split;
+  bool lds;  // BM = 128 with W and X staged through LDS (k_prefill_lds)
 };
 static double shape_cost_us(int64_t M, int64_t N, int64_t K, int bm, int64_t splits, int64_t kt_split, int cus) {
   const int64_t pairs = (N / kTile + 1) / 2;
@@ -424,21 +683,23 @@ static double shape_cost_us(int64_t M, int64_t N, int64_t K, int bm, int64_t spl
   if (splits > 1) t += 6.8 + (double)splits * (double)M * (double)N * 4.0 / 3.5e6;
   return t;
 }
-static PfShape choose_shape_uncached(int64_t M, int64_t N, int64_t K, int cus) {
+// only_bm: consider that width alone (0: every width).
+static PfShape choose_shape_uncached(int64_t M, int64_t N, int64_t K, int cus, int only_bm = 0) {
   const int64_t KT = K / kTile;
   const int widths[4] = {256, 192, 128, 64};
   const int wants[10] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
   const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(KT / 2, K / (2 * M)));
-  PfShape best = {256, 1, 1, (int)KT};
+  PfShape best = {256, 1, 1, (int)KT, false};
   double best_t = -1.0;
   for (int c = 0; c < 4; c++) {
+    if (only_bm && widths[c] != only_bm) continue;
     for (int w = 0; w < 10 && wants[w] <= smax; w++) {
       const int64_t kt_split = (KT + wants[w] - 1) / wants[w];
       const int64_t splits = (KT + kt_split - 1) / kt_split;
       const double t = shape_cost_us(M, N, K, widths[c], splits, kt_split, cus);
       if (best_t < 0 || t < best_t) {
         best_t = t;
-        best = {widths[c], 1, (int)splits, (int)kt_split};
+        best = {widths[c], 1, (int)splits, (int)kt_split, false};
       }
     }
   }
@@ -447,12 +708,18 @@ static PfShape choose_shape_uncached(int64_t M, int64_t N, int64_t K, int cus) {
   return best;
 }
 
-// The same, remembered for the last few shapes of this thread (a GEMM call
-// asks for it twice: the workspace query and the launch).
-static PfShape choose_shape(int64_t M, int64_t N, int64_t K) {
+// The same, with the staging chosen, remembered for the last few shapes of
+// this thread (a GEMM call asks for it twice: the workspace query and the
+// launch).  LDS staging (k_prefill_lds) runs width 128: for packed W it
+// measured 3-9% faster than the register-staged kernel at that width, and
+// for row-major W (the dense baseline) about 40% faster, which also beats
+// the register-staged kernel at 192 and 256, so the dense baseline takes
+// width 128 whenever the model picks 128 or more.
+static PfShape choose_shape(int64_t M, int64_t N, int64_t K, bool rowmajor) {
   struct Entry {
     int64_t M, N, K;
     int cus;
+    bool rowmajor;
     PfShape sh;
   };
   constexpr int kSlots = 8;
@@ -460,9 +727,12 @@ static PfShape choose_shape(int64_t M, int64_t N, int64_t K) {
   thread_local int filled = 0, next = 0;
   const int cus = cu_count();
   for (int i = 0; i < filled; i++)
-    if (cache[i].M == M && cache[i].N == N && cache[i].K == K && cache[i].cus == cus) return cache[i].sh;
-  const PfShape sh = choose_shape_uncached(M, N, K, cus);
-  cache[next] = {M, N, K, cus, sh};
+    if (cache[i].M == M && cache[i].N == N && cache[i].K == K && cache[i].cus == cus && cache[i].rowmajor == rowmajor)
+      return cache[i].sh;
+  PfShape sh = choose_shape_uncached(M, N, K, cus);
+  if (rowmajor && sh.bm > 128) sh = choose_shape_uncached(M, N, K, cus, 128);
+  sh.lds = sh.bm == 128;
+  cache[next] = {M, N, K, cus, rowmajor, sh};
   next = (next + 1) % kSlots;
   if (filled < kSlots) filled++;
   return sh;
@@ -480,7 +750,7 @@ __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ 
   store4<BF16, OUT_F32>(Y, q, sum);
 }
 
-template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, int BM, int DIST>
+template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, int BM, int DIST, bool LDS = false>
 static hipError_t launch_prefill_bm(const void* src, const void* X, int64_t M, int64_t N, int64_t K, void* Y,
                                     const PfShape& sh, float* part, hipStream_t s) {
   PfArgs a;
@@ -500,11 +770,18 @@ static hipError_t launch_prefill_bm(const void* src, const void* X, int64_t M, i
   a.n_blocks = a.n_pairs * a.n_mblk * sh.splits;
   a.per_xcd = (a.n_blocks + 7) / 8;
   if (sh.splits > 1) {
-    hipLaunchKernelGGL((k_prefill<BF16, SRC_ROWMAJOR, true, BM, DIST>), dim3((unsigned)(8 * a.per_xcd)),
-                       dim3(kPfWaves * 64), 0, s, a);
+    if constexpr (LDS)
+      hipLaunchKernelGGL((k_prefill_lds<BF16, SRC_ROWMAJOR, true>), dim3((unsigned)(8 * a.per_xcd)),
+                         dim3(kPfWaves * 64), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_prefill<BF16, SRC_ROWMAJOR, true, BM, DIST>), dim3((unsigned)(8 * a.per_xcd)),
+                         dim3(kPfWaves * 64), 0, s, a);
     const int64_t mn = M * N;
     hipLaunchKernelGGL((k_split_reduce<BF16, OUT_F32>), dim3((unsigned)((mn / 4 + 255) / 256)), dim3(256), 0, s,
                        part, sh.splits, mn, Y);
+  } else if constexpr (LDS) {
+    hipLaunchKernelGGL((k_prefill_lds<BF16, SRC_ROWMAJOR, OUT_F32>), dim3((unsigned)(8 * a.per_xcd)),
+                       dim3(kPfWaves * 64), 0, s, a);
   } else {
     hipLaunchKernelGGL((k_prefill<BF16, SRC_ROWMAJOR, OUT_F32, BM, DIST>), dim3((unsigned)(8 * a.per_xcd)),
                        dim3(kPfWaves * 64), 0, s, a);
@@ -514,8 +791,15 @@ static hipError_t launch_prefill_bm(const void* src, const void* X, int64_t M, i
 
 // The shape for these sizes with the split limited to what the workspace
 // holds (no workspace: no split).
-static PfShape shape_for(int64_t M, int64_t N, int64_t K, uint64_t ws_bytes) {
-  PfShape sh = choose_shape(M, N, K);
+static PfShape shape_for(int64_t M, int64_t N, int64_t K, bool rowmajor, uint64_t ws_bytes, int force_bm = 0,
+                         bool force_lds = false) {
+  PfShape sh;
+  if (force_bm) {
+    sh = choose_shape_uncached(M, N, K, cu_count(), force_bm);
+    sh.lds = force_lds;
+  } else {
+    sh = choose_shape(M, N, K, rowmajor);
+  }
   const uint64_t plane = (uint64_t)M * (uint64_t)N * 4u;
   const int64_t KT = K / kTile;
   if (sh.splits > 1 && (uint64_t)sh.splits * plane > ws_bytes) {
@@ -531,22 +815,23 @@ static PfShape shape_for(int64_t M, int64_t N, int64_t K, uint64_t ws_bytes) {
   return sh;
 }
 
-uint64_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  const PfShape sh = choose_shape(M, N, K);
+uint64_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K, bool rowmajor) {
+  const PfShape sh = choose_shape(M, N, K, rowmajor);
   return sh.splits > 1 ? (uint64_t)sh.splits * (uint64_t)M * (uint64_t)N * 4u : 0u;
 }
 
 // The cost model's time for the shape this workspace allows.
-double prefill_estimate_us(int64_t M, int64_t N, int64_t K, uint64_t ws_bytes) {
-  const PfShape sh = shape_for(M, N, K, ws_bytes);
+double prefill_estimate_us(int64_t M, int64_t N, int64_t K, bool rowmajor, uint64_t ws_bytes) {
+  const PfShape sh = shape_for(M, N, K, rowmajor, ws_bytes);
   return shape_cost_us(M, N, K, sh.bm, sh.splits, sh.kt_split, cu_count());
 }
 
 template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32>
 static hipError_t launch_prefill_t(const void* src, const void* X, int64_t M, int64_t N, int64_t K, void* Y,
-                                   void* ws, uint64_t ws_bytes, hipStream_t s) {
-  const PfShape sh = shape_for(M, N, K, ws ? ws_bytes : 0u);
+                                   void* ws, uint64_t ws_bytes, int force_bm, bool force_lds, hipStream_t s) {
+  const PfShape sh = shape_for(M, N, K, SRC_ROWMAJOR, ws ? ws_bytes : 0u, force_bm, force_lds);
   float* part = reinterpret_cast<float*>(ws);
+  if (sh.lds) return launch_prefill_bm<BF16, SRC_ROWMAJOR, OUT_F32, kLdsBM, 1, true>(src, X, M, N, K, Y, sh, part, s);
   switch (sh.bm) {
     case 64: return launch_prefill_bm<BF16, SRC_ROWMAJOR, OUT_F32, 64, 2>(src, X, M, N, K, Y, sh, part, s);
     case 128: return launch_prefill_bm<BF16, SRC_ROWMAJOR, OUT_F32, 128, 2>(src, X, M, N, K, Y, sh, part, s);
@@ -555,19 +840,22 @@ static hipError_t launch_prefill_t(const void* src, const void* X, int64_t M, in
   }
 }
 
+// force_bm: 0 (the shape the cost model picks) or a width in {64, 128, 192,
+// 256}; force_lds: LDS staging (width 128 only).
 hipError_t launch_prefill(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* X, int64_t M, int64_t N,
-                          int64_t K, void* Y, void* ws, uint64_t ws_bytes, hipStream_t s) {
+                          int64_t K, void* Y, void* ws, uint64_t ws_bytes, int force_bm, bool force_lds,
+                          hipStream_t s) {
   if (K / kTile > kPfMaxKT) return hipErrorInvalidValue;
+  if (force_bm && force_bm != 64 && force_bm != 128 && force_bm != 192 && force_bm != 256) return hipErrorInvalidValue;
+  if (force_lds && force_bm != kLdsBM) return hipErrorInvalidValue;
+#define PATCH_PF(B, R, F) launch_prefill_t<B, R, F>(src, X, M, N, K, Y, ws, ws_bytes, force_bm, force_lds, s)
   if (bf16) {
-    if (rowmajor) return out_f32 ? launch_prefill_t<true, true, true>(src, X, M, N, K, Y, ws, ws_bytes, s)
-                                 : launch_prefill_t<true, true, false>(src, X, M, N, K, Y, ws, ws_bytes, s);
-    return out_f32 ? launch_prefill_t<true, false, true>(src, X, M, N, K, Y, ws, ws_bytes, s)
-                   : launch_prefill_t<true, false, false>(src, X, M, N, K, Y, ws, ws_bytes, s);
+    if (rowmajor) return out_f32 ? PATCH_PF(true, true, true) : PATCH_PF(true, true, false);
+    return out_f32 ? PATCH_PF(true, false, true) : PATCH_PF(true, false, false);
   }
-  if (rowmajor) return out_f32 ? launch_prefill_t<false, true, true>(src, X, M, N, K, Y, ws, ws_bytes, s)
-                               : launch_prefill_t<false, true, false>(src, X, M, N, K, Y, ws, ws_bytes, s);
-  return out_f32 ? launch_prefill_t<false, false, true>(src, X, M, N, K, Y, ws, ws_bytes, s)
-                 : launch_prefill_t<false, false, false>(src, X, M, N, K, Y, ws, ws_bytes, s);
+  if (rowmajor) return out_f32 ? PATCH_PF(false, true, true) : PATCH_PF(false, true, false);
+  return out_f32 ? PATCH_PF(false, false, true) : PATCH_PF(false, false, false);
+#undef PATCH_PF
 }
 
 }  // namespace patch

@@ -15,9 +15,10 @@ hipError_t launch_pack(const void* W, const uint8_t* mask, int64_t N, int64_t K,
 hipError_t launch_decode(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* X, int64_t M, int64_t N,
                          int64_t K, void* Y, hipStream_t s);
 hipError_t launch_prefill(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* X, int64_t M, int64_t N,
-                          int64_t K, void* Y, void* ws, uint64_t ws_bytes, hipStream_t s);
-uint64_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K);
-double prefill_estimate_us(int64_t M, int64_t N, int64_t K, uint64_t ws_bytes);
+                          int64_t K, void* Y, void* ws, uint64_t ws_bytes, int force_bm, bool force_lds,
+                          hipStream_t s);
+uint64_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K, bool rowmajor);
+double prefill_estimate_us(int64_t M, int64_t N, int64_t K, bool rowmajor, uint64_t ws_bytes);
 double decode_estimate_us(int64_t M, int64_t N, int64_t K, double w_bytes);
 }  // namespace patch
 
@@ -235,19 +236,19 @@ patch_status patch_desc_from_header(const void* header_host, uint64_t header_byt
   return PATCH_OK;
 }
 
-static uint64_t workspace_for(int64_t M, int64_t N, int64_t K) {
+static uint64_t workspace_for(int64_t M, int64_t N, int64_t K, bool rowmajor) {
   if (M <= 0 || M > (int64_t)0x7fffffff || N <= 0 || K <= 0 || N % kTile || K % kTile || N > kMaxDim || K > kMaxDim ||
       K / kTile > kMaxKT)
     return 0;
-  return patch::prefill_workspace_bytes(M, N, K);
+  return patch::prefill_workspace_bytes(M, N, K, rowmajor);
 }
 
 uint64_t patch_gemm_workspace_bytes(const patch_packed_desc* desc, int64_t M) {
   if (!desc) return 0;
-  return workspace_for(M, desc->N, desc->K);
+  return workspace_for(M, desc->N, desc->K, false);
 }
 
-uint64_t patch_dense_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) { return workspace_for(M, N, K); }
+uint64_t patch_dense_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) { return workspace_for(M, N, K, true); }
 
 static patch_status gemm_common(bool rowmajor, patch_dtype dt, int64_t M, int64_t N, int64_t K, const void* src,
                                 uint64_t w_bytes, const void* X_dev, void* Y_dev, patch_dtype y_dtype, void* ws,
@@ -255,7 +256,7 @@ static patch_status gemm_common(bool rowmajor, patch_dtype dt, int64_t M, int64_
   patch_status s;
   if ((s = check_ydtype(dt, y_dtype))) return s;
   if (M < 0 || M > (int64_t)0x7fffffff) return fail(PATCH_ERR_INVALID_ARG, "M=%lld out of range", (long long)M);
-  if (variant < PATCH_VARIANT_AUTO || variant > PATCH_VARIANT_PREFILL)
+  if (variant < PATCH_VARIANT_AUTO || variant > PATCH_VARIANT_PREFILL_W128_LDS)
     return fail(PATCH_ERR_INVALID_ARG, "unknown variant %d", (int)variant);
   if (variant == PATCH_VARIANT_DECODE && M > kDecodeMaxM)
     return fail(PATCH_ERR_INVALID_ARG, "decode variant needs M <= %lld (M=%lld)", (long long)kDecodeMaxM, (long long)M);
@@ -272,11 +273,13 @@ static patch_status gemm_common(bool rowmajor, patch_dtype dt, int64_t M, int64_
   bool decode = variant == PATCH_VARIANT_DECODE;
   if (variant == PATCH_VARIANT_AUTO && K <= kDecodeMaxK && M <= kDecodeMaxM)
     decode = M <= kDecodeAutoM || patch::decode_estimate_us(M, N, K, (double)w_bytes) <=
-                                      patch::prefill_estimate_us(M, N, K, ws ? ws_bytes : 0);
+                                      patch::prefill_estimate_us(M, N, K, rowmajor, ws ? ws_bytes : 0);
   const bool bf16 = dt == PATCH_BF16, f32out = y_dtype == PATCH_F32;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  static const int kForceBm[8] = {0, 0, 0, 64, 128, 192, 256, 128};
   hipError_t e = decode ? patch::launch_decode(bf16, rowmajor, f32out, src, X_dev, M, N, K, Y_dev, st)
-                        : patch::launch_prefill(bf16, rowmajor, f32out, src, X_dev, M, N, K, Y_dev, ws, ws_bytes, st);
+                        : patch::launch_prefill(bf16, rowmajor, f32out, src, X_dev, M, N, K, Y_dev, ws, ws_bytes,
+                                                kForceBm[variant], variant == PATCH_VARIANT_PREFILL_W128_LDS, st);
   if (e != hipSuccess) return hip_fail(e, decode ? "launch decode" : "launch prefill");
   return PATCH_OK;
 }

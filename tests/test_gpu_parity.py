@@ -214,6 +214,50 @@ def test_prefill_split_k(N, K, M):
     assert_close(a, ref, f32=True, what=f"auto M={M}")
 
 
+PREFILL_KERNELS = ["prefill_w64", "prefill_w128", "prefill_w192", "prefill_w256", "prefill_w128_lds"]
+
+
+@pytest.mark.parametrize("variant", PREFILL_KERNELS)
+def test_prefill_every_kernel(variant):
+    """Every prefill kernel (M-block width 64/128/192/256 with registers,
+    128 staged through LDS) on the same shape: 640 x 1152 (a lone middle
+    row-block, 9 tile columns so K ranges come out uneven), M from below one
+    block to several, with a workspace of 2 N K bytes (K split as that
+    width's model decides) and with none; packed and dense baseline; every
+    output against the oracle."""
+    N, K = 640, 1152
+    p = inputs.make_custom("bf16", N, K, 24, "bernoulli", 0.5, "uniform")
+    pw, W = _pack(p)
+    pd = inputs.make_custom("bf16", N, K, 24, "dense", 0.0, "top2")
+    ws = torch.empty(2 * N * K, dtype=torch.uint8, device="cuda")
+    for M in (17, 100, 300, 700):
+        Xb = inputs.make_custom_x("bf16", M, K, 25 + M)
+        X = dev_bits(Xb, "bf16")
+        ref, ref_d = _ref(p, Xb), _ref(pd, Xb)
+        for w in (ws, None):
+            tag = f"{variant} M={M} ws={'yes' if w is not None else 'no'}"
+            assert_close(patch.gemm(X, pw, variant=variant, workspace=w), ref, what=tag)
+            assert_close(patch.gemm(X, pw, out_dtype=torch.float32, variant=variant, workspace=w), ref, f32=True,
+                         what=tag + " f32")
+            assert_close(patch.dense_gemm(X, W, variant=variant, workspace=w), ref_d, what="dense " + tag)
+
+
+@pytest.mark.parametrize("variant", PREFILL_KERNELS)
+def test_prefill_every_kernel_f16_exact(variant):
+    """f16, small integers, fp32 output: every kernel equals the oracle
+    exactly (any fp32 summation order is exact here)."""
+    rng = np.random.default_rng(26)
+    N, K, M = 384, 768, 150
+    p = inputs.make_custom("f16", N, K, 27, "bernoulli", 0.5, "uniform")
+    p.w = inputs.to_bits(rng.integers(-2, 3, (N, K)).astype(np.float64), "f16")
+    Xb = inputs.to_bits(rng.integers(-2, 3, (M, K)).astype(np.float64), "f16")
+    pw, W = _pack(p)
+    ref = _ref(p, Xb)
+    ws = torch.empty(2 * N * K, dtype=torch.uint8, device="cuda")
+    y = patch.gemm(dev_bits(Xb, "f16"), pw, out_dtype=torch.float32, variant=variant, workspace=ws)
+    assert np.array_equal(host_f64(y), ref), variant
+
+
 # ------------------------------------------------------------------ exact cases
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_identity_x_gives_masked_weights_exactly(dtype):
