@@ -245,6 +245,35 @@ int oracle_gemm_f64(int dtype, int64_t M, int64_t N, int64_t K, int64_t tn, int6
   return fail ? ORACLE_ERR_ARG : ORACLE_OK;
 }
 
+/* ---------------------------------------------------------------------------
+ * The LLaMA MLP's gated product, the step on either side of the gate and up
+ * projections.  The pages evaluate PATCH on LLaMA-2 models (gist.science
+ * explainer, section 4 "Experimental Results"); the MLP of that architecture
+ * computes H = SiLU(X Wg^T) * (X Wu^T) elementwise before the down
+ * projection, with SiLU(x) = x * sigmoid(x) = x / (1 + e^-x).  Neither formula
+ * is on the pages; both are the architecture's standard definitions.
+ * ------------------------------------------------------------------------- */
+double oracle_silu(double x) { return x / (1.0 + exp(-x)); }
+
+/* H[m][f] = SiLU(Yg[m][f]) * Yu[m][f], Yg = X (Wg o Eg)^T and Yu = X (Wu o Eu)^T
+ * each computed by oracle_gemm_f64; X: M x K, Wg and Wu: F x K, H: M x F. */
+int oracle_swiglu_f64(int dtype, int64_t M, int64_t F, int64_t K, int64_t tn, int64_t tk, const uint16_t* X,
+                      const uint16_t* Wg, const uint16_t* Wu, const uint8_t* map_g, const uint8_t* map_u,
+                      const uint8_t* mask_g, const uint8_t* mask_u, double* H) {
+  if (M < 0 || F < 0) return ORACLE_ERR_ARG;
+  if (M == 0 || F == 0) return ORACLE_OK;
+  double* yg = (double*)malloc(sizeof(double) * (size_t)(M * F));
+  double* yu = (double*)malloc(sizeof(double) * (size_t)(M * F));
+  int rc = (yg && yu) ? ORACLE_OK : ORACLE_ERR_ARG;
+  if (!rc) rc = oracle_gemm_f64(dtype, M, F, K, tn, tk, X, Wg, map_g, mask_g, yg);
+  if (!rc) rc = oracle_gemm_f64(dtype, M, F, K, tn, tk, X, Wu, map_u, mask_u, yu);
+  if (!rc)
+    for (int64_t i = 0; i < M * F; i++) H[i] = oracle_silu(yg[i]) * yu[i];
+  free(yg);
+  free(yu);
+  return rc;
+}
+
 /* Round an fp64 result to the 16-bit output type (RNE) -- used to measure the
  * error floor that any 16-bit output must carry. */
 void oracle_round_f64(int dtype, int64_t n, const double* in, uint16_t* out) {

@@ -63,6 +63,10 @@ def load():
     lib.oracle_packed_bytes.restype = ctypes.c_uint64
     lib.oracle_pack.argtypes = [ctypes.c_int, I64, I64, P, P, P, P, ctypes.c_uint64]
     lib.oracle_pack.restype = ctypes.c_int
+    lib.oracle_silu.argtypes = [ctypes.c_double]
+    lib.oracle_silu.restype = ctypes.c_double
+    lib.oracle_swiglu_f64.argtypes = [ctypes.c_int, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P]
+    lib.oracle_swiglu_f64.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -160,3 +164,37 @@ def pack(dtype, W, tile_map, mask) -> np.ndarray:
     if rc:
         raise OracleError(rc)
     return out
+
+
+def silu(x: float) -> float:
+    return load().oracle_silu(float(x))
+
+
+def swiglu_f64(dtype, X, Wg, Wu, map_g, map_u, mask_g, mask_u, tile_n=128, tile_k=128) -> np.ndarray:
+    """H = SiLU(X (Wg o Eg)^T) * (X (Wu o Eu)^T) in fp64 (the LLaMA MLP's gated
+    product); X (M, K), Wg and Wu (F, K) are 16-bit patterns."""
+    lib = load()
+    X, Wg, Wu = _u16(X), _u16(Wg), _u16(Wu)
+    M, K = X.shape
+    F, K2 = Wg.shape
+    if K != K2 or Wu.shape != Wg.shape:
+        raise ValueError("shape mismatch")
+    H = np.zeros((M, F), dtype=np.float64)
+    rc = lib.oracle_swiglu_f64(_DT[dtype], M, F, K, tile_n, tile_k, _p(X), _p(Wg), _p(Wu), _p(_u8(map_g)),
+                               _p(_u8(map_u)), _p(_u8(mask_g)), _p(_u8(mask_u)), _p(H))
+    if rc:
+        raise OracleError(rc)
+    return H
+
+
+def interleave_gate_up(A_g: np.ndarray, A_u: np.ndarray, rows_per_block: int) -> np.ndarray:
+    """Rows of A_g and A_u interleaved by blocks of rows_per_block: block 2i is
+    A_g's block i, block 2i+1 is A_u's (the row order the fused gate/up blob
+    is packed in).  A pure permutation of rows, used for weights (128-row
+    blocks), tile maps (one row per row-block) and masks."""
+    if A_g.shape != A_u.shape or A_g.shape[0] % rows_per_block:
+        raise ValueError("shape mismatch")
+    nb = A_g.shape[0] // rows_per_block
+    g = A_g.reshape(nb, rows_per_block, *A_g.shape[1:])
+    u = A_u.reshape(nb, rows_per_block, *A_u.shape[1:])
+    return np.stack([g, u], axis=1).reshape(2 * A_g.shape[0], *A_g.shape[1:])

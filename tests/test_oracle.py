@@ -8,6 +8,7 @@ sections "1. Problem Statement", "2. Methodology: PATCH" and
 "4. Experimental Results".
 """
 import itertools
+import math
 import os
 
 import numpy as np
@@ -366,3 +367,79 @@ def test_pack_keeps_negative_zero_bits():
     pieces = blob[512:512 + 8 * 2304].reshape(8, 2304)
     assert np.all(pieces[:, :2048].copy().view(np.uint16) == 0x8000)
     assert np.all(pieces[:, 2048:] == (13 | (13 << 4)))  # code (1,3) = 1 | 3 << 2 = 13
+
+
+# ------------------------------------------------------------------ gated MLP product (SiLU)
+def test_silu_closed_forms():
+    """SiLU(x) = x / (1 + e^-x): zero at zero; SiLU(ln 3) = (3/4) ln 3
+    exactly in the reals; its odd part is x / 2, i.e. SiLU(x) - SiLU(-x) = x
+    (a wrong sign in the exponent or a dropped factor breaks this); it
+    tends to x for large x and to 0 for very negative x."""
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.silu(math.log(3.0)) == pytest.approx(0.75 * math.log(3.0), rel=1e-15)
+    for x in np.linspace(-30.0, 30.0, 121):
+        assert oracle.silu(x) - oracle.silu(-x) == pytest.approx(x, rel=1e-13, abs=1e-13)
+    assert oracle.silu(40.0) == pytest.approx(40.0, rel=1e-15)
+    assert abs(oracle.silu(-40.0)) < 1e-15
+    # sigmoid(1) = e / (1 + e)
+    assert oracle.silu(1.0) == pytest.approx(math.e / (1.0 + math.e), rel=1e-15)
+
+
+def test_swiglu_brute_force_tiny():
+    """8 x 8 gate and up weights with 4 x 4 tiles, different tile maps and
+    2:4 patterns for the two, integer X and W: H = SiLU(yg) * yu with yg, yu
+    summed by hand over the kept positions and SiLU from math.exp."""
+    rng = np.random.default_rng(31)
+    M, F, K = 5, 8, 8
+    Xi = rng.integers(-3, 4, (M, K))
+    Gi = rng.integers(-3, 4, (F, K))
+    Ui = rng.integers(-3, 4, (F, K))
+    maps = [np.array([[1, 0], [0, 1]], np.uint8), np.array([[0, 1], [1, 1]], np.uint8)]
+    pats = [rng.integers(0, 6, (F, K // 4)) for _ in range(2)]
+    masks = []
+    for pt in pats:
+        mk = np.zeros((F, K), np.uint8)
+        for n in range(F):
+            for g in range(K // 4):
+                for d in inputs.PATTERNS[pt[n, g]]:
+                    mk[n, 4 * g + d] = 1
+        masks.append(mk)
+    H = oracle.swiglu_f64("bf16", _int_bits(Xi, "bf16"), _int_bits(Gi, "bf16"), _int_bits(Ui, "bf16"), maps[0],
+                          maps[1], masks[0], masks[1], tile_n=4, tile_k=4)
+
+    def y(Wi, tmap, mk, m, n):
+        return sum(Xi[m, k] * Wi[n, k] for k in range(K) if (not tmap[n // 4, k // 4]) or mk[n, k])
+
+    for m in range(M):
+        for n in range(F):
+            g, u = y(Gi, maps[0], masks[0], m, n), y(Ui, maps[1], masks[1], m, n)
+            ref = g / (1.0 + math.exp(-g)) * u
+            assert H[m, n] == pytest.approx(ref, rel=1e-13, abs=1e-13), (m, n)
+
+
+def test_swiglu_identity_x_is_silu_of_gate_weights_times_up_weights():
+    """X = identity rows: H^T = SiLU(Wg o Eg) * (Wu o Eu) elementwise, with
+    SiLU evaluated by numpy; swapping the roles of gate and up changes it."""
+    pg = _problem(256, 256, "bernoulli", 0.5, seed=12)
+    pu = _problem(256, 256, "bernoulli", 0.5, seed=13)
+    X = inputs.to_bits(np.eye(256), "bf16")
+    H = oracle.swiglu_f64("bf16", X, pg.w, pu.w, pg.tile_map, pu.tile_map, pg.mask, pu.mask)
+    G = inputs.bits_to_f32(pg.w, "bf16").astype(np.float64) * oracle.effective_mask(256, 256, pg.tile_map, pg.mask)
+    U = inputs.bits_to_f32(pu.w, "bf16").astype(np.float64) * oracle.effective_mask(256, 256, pu.tile_map, pu.mask)
+    ref = G / (1.0 + np.exp(-G)) * U
+    np.testing.assert_allclose(H.T, ref, rtol=1e-14, atol=1e-18)
+    Hs = oracle.swiglu_f64("bf16", X, pu.w, pg.w, pu.tile_map, pg.tile_map, pu.mask, pg.mask)
+    assert not np.allclose(Hs, H)
+
+
+def test_interleave_gate_up_rows():
+    """Blocks of rows alternate gate, up, gate, up, ... and nothing else moves."""
+    g = np.arange(6 * 3).reshape(6, 3)
+    u = 100 + np.arange(6 * 3).reshape(6, 3)
+    out = oracle.interleave_gate_up(g, u, 2)
+    assert out.shape == (12, 3)
+    for i in range(3):
+        assert np.array_equal(out[4 * i:4 * i + 2], g[2 * i:2 * i + 2])
+        assert np.array_equal(out[4 * i + 2:4 * i + 4], u[2 * i:2 * i + 2])
+    tm = oracle.interleave_gate_up(np.array([[1, 0]], np.uint8), np.array([[0, 1]], np.uint8), 1)
+    assert np.array_equal(tm, np.array([[1, 0], [0, 1]], np.uint8))
