@@ -187,6 +187,47 @@ patch_status patch_dense_gemm_ex(patch_dtype dtype, int64_t M, int64_t N, int64_
                                  const void* W_dev, void* Y_dev, patch_dtype y_dtype, void* workspace_dev,
                                  uint64_t workspace_bytes, int32_t variant, void* stream);
 
+/*
+ * Fused gate/up projection of the LLaMA MLP (the pages evaluate PATCH on
+ * LLaMA-2 models, gist.science explainer, section 4 "Experimental Results";
+ * that architecture's MLP is down(SiLU(gate(x)) * up(x))):
+ *   H = SiLU(X (Wg o Eg)^T) * (X (Wu o Eu)^T)   elementwise, H is M x F,
+ * SiLU(x) = x / (1 + e^-x), all in fp32 before one rounding of H.
+ *
+ * patch_pack_gate_up packs the two F x K matrices into ONE blob of the
+ * row-block interleave of Wg and Wu (N = 2F: row-block 2i holds Wg's
+ * row-block i, 2i+1 holds Wu's; the same format version 3, tile maps and
+ * masks interleaved the same way), so one GEMM launch reads both and a
+ * workgroup holds matching gate and up sums for its epilogue.  Arguments as
+ * patch_pack, per matrix; F a positive multiple of 128.  A plain patch_gemm
+ * on this blob returns the two projections interleaved by 128 columns.
+ */
+uint64_t patch_packed_bytes_gate_up(patch_dtype dtype, int64_t F, int64_t K, const uint8_t* map_g_host,
+                                    const uint8_t* map_u_host);
+patch_status patch_pack_gate_up(patch_dtype dtype, int64_t F, int64_t K, const void* Wg_dev, const void* Wu_dev,
+                                const uint8_t* map_g_host, const uint8_t* map_u_host, const uint8_t* mask_g_dev,
+                                const uint8_t* mask_u_dev, void* packed_dev, uint64_t packed_bytes,
+                                patch_packed_desc* desc_out, void* stream);
+
+/*
+ * H from a gate/up blob (desc->N = 2F).  H_dev: M x F of h_dtype (the blob's
+ * dtype or PATCH_F32); workspace and variant as patch_gemm_ex (the fused
+ * decode kernel runs twice the waves and so needs M <= 16 or K <= 32768,
+ * else PATCH_ERR_UNSUPPORTED; AUTO then takes the prefill kernel, whose K
+ * split adds the ranges' partial sums before SiLU).  Asynchronous.
+ */
+uint64_t patch_gemm_swiglu_workspace_bytes(const patch_packed_desc* desc, int64_t M);
+patch_status patch_gemm_swiglu(const patch_packed_desc* desc, const void* packed_dev, const void* X_dev, int64_t M,
+                               void* H_dev, patch_dtype h_dtype, void* workspace_dev, uint64_t workspace_bytes,
+                               int32_t variant, void* stream);
+
+/* Same-shape dense baseline of the fused projection from two plain
+ * row-major F x K matrices Wg_dev and Wu_dev (every tile dense). */
+uint64_t patch_dense_gemm_swiglu_workspace_bytes(int64_t M, int64_t F, int64_t K);
+patch_status patch_dense_gemm_swiglu(patch_dtype dtype, int64_t M, int64_t F, int64_t K, const void* X_dev,
+                                     const void* Wg_dev, const void* Wu_dev, void* H_dev, patch_dtype h_dtype,
+                                     void* workspace_dev, uint64_t workspace_bytes, int32_t variant, void* stream);
+
 const char* patch_status_string(patch_status s);
 const char* patch_last_error(void);
 

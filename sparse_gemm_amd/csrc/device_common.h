@@ -95,6 +95,16 @@ constexpr int kSparseMetaOffset = 2048;  // codes after the values in a 2:4 piec
 
 // One tile-table entry of the packed blob.  Band b's piece of the tile
 // starts at offset + b * band_stride.
+// SiLU(x) = x / (1 + e^-x), the gate activation of the LLaMA MLP, and the
+// gated product SiLU(g) * u, in fp32.
+__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+__device__ __forceinline__ f32x4 silu_mul(f32x4 g, f32x4 u) {
+  f32x4 h;
+#pragma unroll
+  for (int c = 0; c < 4; c++) h[c] = silu_f(g[c]) * u[c];
+  return h;
+}
+
 struct TileEntry {
   uint64_t offset;       // byte offset of the tile's band-0 piece from the blob start
   uint32_t kind;         // 0 dense, 1 sparse

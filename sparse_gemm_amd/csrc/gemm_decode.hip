@@ -120,27 +120,42 @@ __device__ __forceinline__ void decode_mma(const DecodeFrag<MB>& f, f32x4 (&acc)
 // WAVES waves per workgroup (tile columns split between them); XCD_MAP puts
 // the 8 bands of a row-block on one XCD (blocks are dealt to the 8 XCDs in
 // turn), so lines they share -- the 2:4 metadata, X -- are fetched into one L2.
-template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, int WAVES, int DEPTH, bool XCD_MAP, int MB>
-__global__ __launch_bounds__(WAVES * 64) void k_decode(const uint8_t* __restrict__ src,
-                                                        const uint16_t* __restrict__ X, int M, int N, int K,
-                                                        void* __restrict__ Y) {
+// FUSE: fused gate/up projection.  W is the row-block interleave of the gate
+// (even row-blocks) and up (odd) matrices -- packed, or, with SRC_ROWMAJOR,
+// two row-major matrices src (gate) and src2 (up); a workgroup takes band b
+// of both row-blocks of pair q with twice the waves (the first WAVES on gate,
+// the others on up) and writes H[m][128 q + ...] = SiLU(gate) * up, H being
+// M x N/2.
+template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, int WAVES, int DEPTH, bool XCD_MAP, int MB, bool FUSE>
+__global__ __launch_bounds__(WAVES * 64 * (FUSE ? 2 : 1)) void k_decode(const uint8_t* __restrict__ src,
+                                                                         const uint8_t* __restrict__ src2,
+                                                                         const uint16_t* __restrict__ X, int M, int N,
+                                                                         int K, void* __restrict__ Y) {
   constexpr int kDecodeWaves = WAVES;
+  constexpr int kAllWaves = WAVES * (FUSE ? 2 : 1);
   const int KT = K / kTile;
   const int bid = blockIdx.x;
-  const int full = (N / kTile / 8) * 64;  // blocks in complete groups of 8 row-blocks
-  int i, b;                               // row-block and 16-row band of W
+  const int NB = FUSE ? N / kTile / 2 : N / kTile;  // row-blocks (fused: gate/up pairs)
+  const int full = (NB / 8) * 64;  // blocks in complete groups of 8 row-blocks
+  int q, b;                        // row-block (fused: pair) and 16-row band of W
   if (XCD_MAP && bid < full) {
-    i = (bid & 7) + 8 * (bid >> 6);
+    q = (bid & 7) + 8 * (bid >> 6);
     b = (bid >> 3) & 7;
   } else {
-    i = bid >> 3;
+    q = bid >> 3;
     b = bid & 7;
   }
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wa = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = FUSE ? wa / WAVES : 0;  // fused: 0 gate, 1 up
+  const int w = wa - g * WAVES;         // wave within its row-block
   const int l = threadIdx.x & 63;
+  const int i = FUSE ? 2 * q + g : q;   // row-block of the (interleaved) matrix
   const TileEntry* table = reinterpret_cast<const TileEntry*>(src + kHeaderBytes) + (int64_t)i * KT;
+  // row-major W: the matrix and row-block this wave reads
+  const uint8_t* wsrc = SRC_ROWMAJOR && FUSE && g ? src2 : src;
+  const int wi = SRC_ROWMAJOR && FUSE ? q : i;
 
-  __shared__ f32x4 s_red[kDecodeWaves * MB][64];
+  __shared__ f32x4 s_red[kAllWaves * MB][64];
 
   // wave w takes tile columns j = w, w + WAVES, ... of its row-block (at
   // most 64 of them, which the launch guarantees).  Their table entries arrive with one
@@ -173,7 +188,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_decode(const uint8_t* __restrict
       uint64_t off;
       uint32_t kind, stride;
       entry(t, off, kind, stride);
-      decode_load<SRC_ROWMAJOR, MB>(f[s], src, off, kind, stride, X, K, M, i, b, w + kDecodeWaves * t, l);
+      decode_load<SRC_ROWMAJOR, MB>(f[s], SRC_ROWMAJOR ? wsrc : src, off, kind, stride, X, K, M, wi, b,
+                                    w + kDecodeWaves * t, l);
     }
     // steady state: compute the DEPTH slots, refilling each with the tile
     // DEPTH further on (clamped to the last tile: a redundant, cached load)
@@ -186,7 +202,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_decode(const uint8_t* __restrict
         uint64_t off;
         uint32_t kind, stride;
         entry(tn, off, kind, stride);
-        decode_load<SRC_ROWMAJOR, MB>(f[s], src, off, kind, stride, X, K, M, i, b, w + kDecodeWaves * tn, l);
+        decode_load<SRC_ROWMAJOR, MB>(f[s], SRC_ROWMAJOR ? wsrc : src, off, kind, stride, X, K, M, wi, b,
+                                      w + kDecodeWaves * tn, l);
       }
     }
     // last round: no refills
@@ -195,57 +212,73 @@ __global__ __launch_bounds__(WAVES * 64) void k_decode(const uint8_t* __restrict
       if (t0 + s < n_mine) decode_mma<BF16, SRC_ROWMAJOR, MB>(f[s], acc, l);
   }
 
-  // ---- fixed-order reduction over waves (wave w adds up M blocks w,
-  // w + WAVES, ...), then round and store
+  // ---- fixed-order reduction over waves (wave wa adds up M blocks wa,
+  // wa + all waves, ...), then round and store
 #pragma unroll
-  for (int mb = 0; mb < MB; mb++) s_red[w * MB + mb][l] = acc[mb];
+  for (int mb = 0; mb < MB; mb++) s_red[wa * MB + mb][l] = acc[mb];
   __syncthreads();
-  for (int mb = w; mb < MB; mb += kDecodeWaves) {
+  for (int mb = wa; mb < MB; mb += kAllWaves) {
     f32x4 sum = s_red[mb][l];
 #pragma unroll
     for (int ww = 1; ww < kDecodeWaves; ww++) sum += s_red[ww * MB + mb][l];
     const int m = 16 * mb + (l & 15);
-    if (m < M) {
+    if constexpr (FUSE) {
+      f32x4 up = s_red[(kDecodeWaves + 0) * MB + mb][l];
+#pragma unroll
+      for (int ww = 1; ww < kDecodeWaves; ww++) up += s_red[(kDecodeWaves + ww) * MB + mb][l];
+      if (m < M) {
+        const int64_t n = (int64_t)q * kTile + 16 * b + 4 * (l >> 4);
+        store4<BF16, OUT_F32>(Y, (int64_t)m * (N / 2) + n, silu_mul(sum, up));
+      }
+    } else if (m < M) {
       const int64_t n = (int64_t)i * kTile + 16 * b + 4 * (l >> 4);
       store4<BF16, OUT_F32>(Y, (int64_t)m * N + n, sum);
     }
   }
 }
 
-template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, int WAVES, int DEPTH, bool XCD_MAP, int MB>
-static hipError_t launch_decode_v(const void* src, const void* X, int64_t M, int64_t N, int64_t K, void* Y,
-                                  hipStream_t s) {
-  const unsigned grid = (unsigned)(N / 16);
-  hipLaunchKernelGGL((k_decode<BF16, SRC_ROWMAJOR, OUT_F32, WAVES, DEPTH, XCD_MAP, MB>), dim3(grid),
-                     dim3(WAVES * 64), 0, s, reinterpret_cast<const uint8_t*>(src),
-                     reinterpret_cast<const uint16_t*>(X), (int)M, (int)N, (int)K, Y);
+template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE, int WAVES, int DEPTH, bool XCD_MAP, int MB>
+static hipError_t launch_decode_v(const void* src, const void* src2, const void* X, int64_t M, int64_t N, int64_t K,
+                                  void* Y, hipStream_t s) {
+  const unsigned grid = (unsigned)(FUSE ? N / 32 : N / 16);
+  hipLaunchKernelGGL((k_decode<BF16, SRC_ROWMAJOR, OUT_F32, WAVES, DEPTH, XCD_MAP, MB, FUSE>), dim3(grid),
+                     dim3(WAVES * 64 * (FUSE ? 2 : 1)), 0, s, reinterpret_cast<const uint8_t*>(src),
+                     reinterpret_cast<const uint8_t*>(src2), reinterpret_cast<const uint16_t*>(X), (int)M, (int)N,
+                     (int)K, Y);
   return hipGetLastError();
 }
 
-template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32>
-static hipError_t launch_decode_t(const void* src, const void* X, int64_t M, int64_t N, int64_t K, void* Y,
-                                  hipStream_t s) {
+template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE>
+static hipError_t launch_decode_t(const void* src, const void* src2, const void* X, int64_t M, int64_t N, int64_t K,
+                                  void* Y, hipStream_t s) {
   // Few waves a workgroup, several tiles in flight a wave: small workgroups
   // fill every CU several times over and keep starting while others drain,
   // which measured faster than 8 or 16 waves on the q_proj, gate_proj and
   // down_proj shapes.  A wave reads its table entries with one vector load,
   // so it may own at most 64 tile columns: larger K takes more waves.
+  // (Fused gate/up: twice the waves, one set per matrix.)
   const int64_t KT = K / kTile;
+#define PATCH_DV(W, D, MBK) launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, FUSE, W, D, true, MBK>(src, src2, X, M, N, K, Y, s)
   if (M <= 16) {
-    if (KT <= 2 * 64) return launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, 2, 4, true, 1>(src, X, M, N, K, Y, s);
-    if (KT <= 4 * 64) return launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, 4, 4, true, 1>(src, X, M, N, K, Y, s);
-    return launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, 8, 2, true, 1>(src, X, M, N, K, Y, s);
+    if (KT <= 2 * 64) return PATCH_DV(2, 4, 1);
+    if (KT <= 4 * 64) return PATCH_DV(4, 4, 1);
+    return PATCH_DV(8, 2, 1);
   }
   // More tokens: MB column blocks of 16 per wave (X is re-read from L2 by
   // every band, which the 16 < M <= 128 range affords).
   if (KT <= 4 * 64) {
-    if (M <= 32) return launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, 4, 2, true, 2>(src, X, M, N, K, Y, s);
-    if (M <= 64) return launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, 4, 1, true, 4>(src, X, M, N, K, Y, s);
-    return launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, 4, 1, true, 8>(src, X, M, N, K, Y, s);
+    if (M <= 32) return PATCH_DV(4, 2, 2);
+    if (M <= 64) return PATCH_DV(4, 1, 4);
+    return PATCH_DV(4, 1, 8);
   }
-  if (M <= 32) return launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, 8, 2, true, 2>(src, X, M, N, K, Y, s);
-  if (M <= 64) return launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, 8, 1, true, 4>(src, X, M, N, K, Y, s);
-  return launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, 8, 1, true, 8>(src, X, M, N, K, Y, s);
+  if constexpr (FUSE) {
+    return hipErrorInvalidValue;  // 16 waves with several blocks of M do not fit the registers
+  } else {
+    if (M <= 32) return PATCH_DV(8, 2, 2);
+    if (M <= 64) return PATCH_DV(8, 1, 4);
+    return PATCH_DV(8, 1, 8);
+  }
+#undef PATCH_DV
 }
 
 // Time model of this kernel for 16 < M <= 128, fitted to its measured times
@@ -257,18 +290,21 @@ double decode_estimate_us(int64_t M, int64_t N, int64_t K, double w_bytes) {
   return 3.13 + w_bytes / 1.543e7 + (double)(N / 16) * mcols * (double)K * 2.0 / 9.30e6;
 }
 
-hipError_t launch_decode(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* X, int64_t M, int64_t N,
-                         int64_t K, void* Y, hipStream_t s) {
+// src2 non-null: fused gate/up (see k_decode); Y is then H, M x N/2.
+hipError_t launch_decode(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* src2, const void* X,
+                         int64_t M, int64_t N, int64_t K, void* Y, hipStream_t s) {
+  const bool fuse = src2 != nullptr;
+  if (fuse && (N % (2 * kTile))) return hipErrorInvalidValue;
+#define PATCH_D(B, R, F, U) launch_decode_t<B, R, F, U>(src, src2, X, M, N, K, Y, s)
+#define PATCH_D2(B, R, F) (fuse ? PATCH_D(B, R, F, true) : PATCH_D(B, R, F, false))
   if (bf16) {
-    if (rowmajor) return out_f32 ? launch_decode_t<true, true, true>(src, X, M, N, K, Y, s)
-                                 : launch_decode_t<true, true, false>(src, X, M, N, K, Y, s);
-    return out_f32 ? launch_decode_t<true, false, true>(src, X, M, N, K, Y, s)
-                   : launch_decode_t<true, false, false>(src, X, M, N, K, Y, s);
+    if (rowmajor) return out_f32 ? PATCH_D2(true, true, true) : PATCH_D2(true, true, false);
+    return out_f32 ? PATCH_D2(true, false, true) : PATCH_D2(true, false, false);
   }
-  if (rowmajor) return out_f32 ? launch_decode_t<false, true, true>(src, X, M, N, K, Y, s)
-                               : launch_decode_t<false, true, false>(src, X, M, N, K, Y, s);
-  return out_f32 ? launch_decode_t<false, false, true>(src, X, M, N, K, Y, s)
-                 : launch_decode_t<false, false, false>(src, X, M, N, K, Y, s);
+  if (rowmajor) return out_f32 ? PATCH_D2(false, true, true) : PATCH_D2(false, true, false);
+  return out_f32 ? PATCH_D2(false, false, true) : PATCH_D2(false, false, false);
+#undef PATCH_D2
+#undef PATCH_D
 }
 
 }  // namespace patch

@@ -93,6 +93,7 @@ struct StepA {
 
 struct PfArgs {
   const uint8_t* src;
+  const uint8_t* src2;  // fused gate/up with row-major W: the up matrix (src is gate)
   const uint16_t* X;
   void* Y;
   int M, N, K, NT, KT, n_mblk, n_pairs;
@@ -102,7 +103,43 @@ struct PfArgs {
   int n_blocks, per_xcd;
 };
 
-template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, int BM, int DIST>
+// Fused gate/up epilogue: the pair is (gate row-block 2p, up row-block 2p+1),
+// waves r = 0 hold gate sums and waves r = 1 the up sums of the same output
+// positions; the up sums go through LDS (scratch, at least 2 KB per wave
+// pair), and the gate waves write H[m][128 p + ...] = SiLU(gate) * up.
+template <bool BF16, bool OUT_F32, int kNMB, int NBR>
+__device__ __forceinline__ void fused_epilogue(const f32x4 (&acc)[4][kNMB], uint8_t* scratch, void* H, int M, int F,
+                                               int p, int m0, int r, int wn, int wm, int l, int half_cols) {
+  constexpr int nbr = NBR;  // bands exchanged per round: scratch holds 4 * NBR KB
+  const int hl = l >> 4;
+  f32x4* sc = reinterpret_cast<f32x4*>(scratch);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of the last stage are done
+  wg_barrier();
+#pragma unroll
+  for (int mblk = 0; mblk < kNMB; mblk++) {
+#pragma unroll
+    for (int b0 = 0; b0 < 4; b0 += nbr) {
+      if (r == 1)
+#pragma unroll
+        for (int bb = 0; bb < nbr; bb++) sc[(((wn * 2 + wm) * nbr) + bb) * 64 + l] = acc[b0 + bb][mblk];
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      wg_barrier();
+      if (r == 0) {
+        const int m = m0 + wm * half_cols + mblk * 16 + (l & 15);
+#pragma unroll
+        for (int bb = 0; bb < nbr; bb++) {
+          const f32x4 u = sc[(((wn * 2 + wm) * nbr) + bb) * 64 + l];
+          const int64_t n = (int64_t)p * kTile + 16 * (4 * wn + b0 + bb) + 4 * hl;
+          if (m < M) store4<BF16, OUT_F32>(H, (int64_t)m * F + n, silu_mul(acc[b0 + bb][mblk], u));
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      wg_barrier();
+    }
+  }
+}
+
+template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, int BM, int DIST, bool FUSE>
 __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
   constexpr int kNMB = BM / 32;                       // 16-column M blocks per wave
   constexpr int kStageBytes = BM * kPfRowBytes;       // one X stage
@@ -135,9 +172,10 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
   const int hl = l >> 4;
   const int KT = P.KT, K = P.K;
   const int m0 = mb * BM;
-  const int i0 = p, i1 = P.NT - 1 - p;
+  // pair: row-blocks p and NT-1-p; fused gate/up: 2p (gate) and 2p+1 (up)
+  const int i0 = FUSE ? 2 * p : p, i1 = FUSE ? 2 * p + 1 : P.NT - 1 - p;
   const int i_mine = r == 0 ? i0 : i1;
-  const bool active = r == 0 || i1 != i0;  // a lone middle row-block has no second half
+  const bool active = r == 0 || i1 != i0;  // a lone middle row-block has no second half (never when fused)
   // this workgroup's tile columns j0 .. j0 + nt - 1 (all of them unless split)
   const int j0 = ks * P.kt_split;
   const int nt = min(P.kt_split, KT - j0);
@@ -166,7 +204,10 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
     const int jl = s >> 1, h = s & 1, j = j0 + jl;
     if constexpr (SRC_ROWMAJOR) {
       // rows 64wn + 16b + (l & 15) of row-block i_mine, columns 128j + 64h + 32qq + 8hl
-      const uint8_t* W = P.src + (((int64_t)i_mine * kTile + 64 * wn) * K + (int64_t)j * kTile + 64 * h) * 2;
+      // (fused: row-block i_mine/2 of the gate or the up matrix)
+      const uint8_t* Wsrc = (FUSE && (i_mine & 1)) ? P.src2 : P.src;
+      const int ib = FUSE ? (i_mine >> 1) : i_mine;
+      const uint8_t* W = Wsrc + (((int64_t)ib * kTile + 64 * wn) * K + (int64_t)j * kTile + 64 * h) * 2;
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(W, 0xffffffffu);
       const uint32_t lane_rm = ((uint32_t)(l & 15) * (uint32_t)K + 8u * (uint32_t)hl) * 2u;
 #pragma unroll
@@ -365,7 +406,15 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
   }
 
   // ---- epilogue: round and store Y[m][n .. n+3] (split: the fp32 partial
-  // of K range ks, at plane ks of the partial buffer)
+  // of K range ks, at plane ks of the partial buffer; fused and unsplit:
+  // H = SiLU(gate) * up)
+  if constexpr (FUSE) {
+    if (P.splits == 1) {
+      fused_epilogue<BF16, OUT_F32, kNMB, (kStageBytes >= 4 * 4096 ? 4 : 2)>(acc, s_x0, P.Y, P.M, P.N / 2, p, m0, r,
+                                                                              wn, wm, l, BM / 2);
+      return;
+    }
+  }
   void* Yp = P.Y;
   if (P.splits > 1) Yp = reinterpret_cast<float*>(P.Y) + (int64_t)ks * P.M * P.N;
   if (active) {
@@ -444,7 +493,7 @@ __device__ __forceinline__ void wait_copies() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32>
+template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE>
 __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   constexpr int BM = kLdsBM;
   constexpr int kNMB = BM / 32;  // 16-column M blocks per wave
@@ -467,8 +516,9 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   const int hl = l >> 4;
   const int KT = P.KT, K = P.K, M = P.M;
   const int m0 = mb * BM;
-  const int i0 = p, i1 = P.NT - 1 - p;
-  const bool active = r == 0 || i1 != i0;  // a lone middle row-block has no second half
+  // pair: row-blocks p and NT-1-p; fused gate/up: 2p (gate) and 2p+1 (up)
+  const int i0 = FUSE ? 2 * p : p, i1 = FUSE ? 2 * p + 1 : P.NT - 1 - p;
+  const bool active = r == 0 || i1 != i0;  // a lone middle row-block has no second half (never when fused)
   const int i_mine = r == 0 ? i0 : i1;
   // a wave with no row-block of its own copies row-block i0's fragments into
   // its own (never read) LDS slots, so every wave issues the same copies
@@ -515,8 +565,11 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
     const uint32_t slot0 = wb + 1024u * (uint32_t)((r * 8 + 4 * wn) * 2);
     if constexpr (SRC_ROWMAJOR) {
       // rows 16 (4wn + b) + l % 16 of row-block i_src, columns 64h + 32wm + 8(l/16) of tile j
-      const uint16_t* W = reinterpret_cast<const uint16_t*>(P.src) +
-                          ((int64_t)i_src * kTile + 64 * wn + (l & 15)) * K + (int64_t)col + 32 * wm + 8 * hl;
+      // (fused: row-block i_src/2 of the gate or the up matrix)
+      const uint8_t* Wsrc = (FUSE && (i_src & 1)) ? P.src2 : P.src;
+      const int ib = FUSE ? (i_src >> 1) : i_src;
+      const uint16_t* W = reinterpret_cast<const uint16_t*>(Wsrc) +
+                          ((int64_t)ib * kTile + 64 * wn + (l & 15)) * K + (int64_t)col + 32 * wm + 8 * hl;
 #pragma unroll
       for (int b = 0; b < 4; b++) dma16(W + (int64_t)16 * b * K, slot0 + 2048u * b + 1024u * wm);
     } else {
@@ -624,6 +677,12 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
     compute(s);
   }
 
+  if constexpr (FUSE) {
+    if (P.splits == 1) {
+      fused_epilogue<BF16, OUT_F32, kNMB, 4>(acc, s_x, P.Y, M, P.N / 2, p, m0, r, wn, wm, l, BM / 2);
+      return;
+    }
+  }
   void* Yp = P.Y;
   if (P.splits > 1) Yp = reinterpret_cast<float*>(P.Y) + (int64_t)ks * P.M * P.N;
   if (active) {
@@ -750,11 +809,32 @@ __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ 
   store4<BF16, OUT_F32>(Y, q, sum);
 }
 
-template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, int BM, int DIST, bool LDS = false>
-static hipError_t launch_prefill_bm(const void* src, const void* X, int64_t M, int64_t N, int64_t K, void* Y,
-                                    const PfShape& sh, float* part, hipStream_t s) {
+// Fused gate/up: H[m][f .. f+3] = SiLU(gate) * up from the partial planes of
+// the interleaved matrix (N = 2F columns: H column f of row-block f/128 is
+// column 256 (f/128) + f%128 for gate and 128 further on for up).
+template <bool BF16, bool OUT_F32>
+__global__ __launch_bounds__(256) void k_split_reduce_fused(const float* __restrict__ part, int splits, int64_t M,
+                                                            int64_t F, void* __restrict__ H) {
+  const int64_t q = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
+  if (q >= M * F) return;
+  const int64_t m = q / F, f = q - (q / F) * F;
+  const int64_t N = 2 * F, mn = M * N;
+  const int64_t gcol = m * N + 2 * kTile * (f / kTile) + f % kTile;
+  f32x4 g = *reinterpret_cast<const f32x4*>(part + gcol);
+  f32x4 u = *reinterpret_cast<const f32x4*>(part + gcol + kTile);
+  for (int k = 1; k < splits; k++) {
+    g += *reinterpret_cast<const f32x4*>(part + (int64_t)k * mn + gcol);
+    u += *reinterpret_cast<const f32x4*>(part + (int64_t)k * mn + gcol + kTile);
+  }
+  store4<BF16, OUT_F32>(H, q, silu_mul(g, u));
+}
+
+template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE, int BM, int DIST, bool LDS = false>
+static hipError_t launch_prefill_bm(const void* src, const void* src2, const void* X, int64_t M, int64_t N, int64_t K,
+                                    void* Y, const PfShape& sh, float* part, hipStream_t s) {
   PfArgs a;
   a.src = reinterpret_cast<const uint8_t*>(src);
+  a.src2 = reinterpret_cast<const uint8_t*>(src2);
   a.X = reinterpret_cast<const uint16_t*>(X);
   a.Y = sh.splits > 1 ? static_cast<void*>(part) : Y;
   a.M = (int)M;
@@ -769,22 +849,27 @@ static hipError_t launch_prefill_bm(const void* src, const void* X, int64_t M, i
   a.kt_split = sh.kt_split;
   a.n_blocks = a.n_pairs * a.n_mblk * sh.splits;
   a.per_xcd = (a.n_blocks + 7) / 8;
+  const dim3 grid((unsigned)(8 * a.per_xcd)), block(kPfWaves * 64);
   if (sh.splits > 1) {
+    // fp32 partials of the K ranges, then the ordered reduction (fused:
+    // SiLU(gate) * up) into Y
     if constexpr (LDS)
-      hipLaunchKernelGGL((k_prefill_lds<BF16, SRC_ROWMAJOR, true>), dim3((unsigned)(8 * a.per_xcd)),
-                         dim3(kPfWaves * 64), 0, s, a);
+      hipLaunchKernelGGL((k_prefill_lds<BF16, SRC_ROWMAJOR, true, FUSE>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((k_prefill<BF16, SRC_ROWMAJOR, true, BM, DIST>), dim3((unsigned)(8 * a.per_xcd)),
-                         dim3(kPfWaves * 64), 0, s, a);
-    const int64_t mn = M * N;
-    hipLaunchKernelGGL((k_split_reduce<BF16, OUT_F32>), dim3((unsigned)((mn / 4 + 255) / 256)), dim3(256), 0, s,
-                       part, sh.splits, mn, Y);
+      hipLaunchKernelGGL((k_prefill<BF16, SRC_ROWMAJOR, true, BM, DIST, FUSE>), grid, block, 0, s, a);
+    if constexpr (FUSE) {
+      const int64_t mf = M * (N / 2);
+      hipLaunchKernelGGL((k_split_reduce_fused<BF16, OUT_F32>), dim3((unsigned)((mf / 4 + 255) / 256)), dim3(256), 0,
+                         s, part, sh.splits, M, N / 2, Y);
+    } else {
+      const int64_t mn = M * N;
+      hipLaunchKernelGGL((k_split_reduce<BF16, OUT_F32>), dim3((unsigned)((mn / 4 + 255) / 256)), dim3(256), 0, s,
+                         part, sh.splits, mn, Y);
+    }
   } else if constexpr (LDS) {
-    hipLaunchKernelGGL((k_prefill_lds<BF16, SRC_ROWMAJOR, OUT_F32>), dim3((unsigned)(8 * a.per_xcd)),
-                       dim3(kPfWaves * 64), 0, s, a);
+    hipLaunchKernelGGL((k_prefill_lds<BF16, SRC_ROWMAJOR, OUT_F32, FUSE>), grid, block, 0, s, a);
   } else {
-    hipLaunchKernelGGL((k_prefill<BF16, SRC_ROWMAJOR, OUT_F32, BM, DIST>), dim3((unsigned)(8 * a.per_xcd)),
-                       dim3(kPfWaves * 64), 0, s, a);
+    hipLaunchKernelGGL((k_prefill<BF16, SRC_ROWMAJOR, OUT_F32, BM, DIST, FUSE>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
@@ -826,35 +911,46 @@ double prefill_estimate_us(int64_t M, int64_t N, int64_t K, bool rowmajor, uint6
   return shape_cost_us(M, N, K, sh.bm, sh.splits, sh.kt_split, cu_count());
 }
 
-template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32>
-static hipError_t launch_prefill_t(const void* src, const void* X, int64_t M, int64_t N, int64_t K, void* Y,
-                                   void* ws, uint64_t ws_bytes, int force_bm, bool force_lds, hipStream_t s) {
+template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE>
+static hipError_t launch_prefill_t(const void* src, const void* src2, const void* X, int64_t M, int64_t N, int64_t K,
+                                   void* Y, void* ws, uint64_t ws_bytes, int force_bm, bool force_lds,
+                                   hipStream_t s) {
   const PfShape sh = shape_for(M, N, K, SRC_ROWMAJOR, ws ? ws_bytes : 0u, force_bm, force_lds);
   float* part = reinterpret_cast<float*>(ws);
-  if (sh.lds) return launch_prefill_bm<BF16, SRC_ROWMAJOR, OUT_F32, kLdsBM, 1, true>(src, X, M, N, K, Y, sh, part, s);
+#define PATCH_BM(W, D, L) \
+  launch_prefill_bm<BF16, SRC_ROWMAJOR, OUT_F32, FUSE, W, D, L>(src, src2, X, M, N, K, Y, sh, part, s)
+  if (sh.lds) return PATCH_BM(kLdsBM, 1, true);
   switch (sh.bm) {
-    case 64: return launch_prefill_bm<BF16, SRC_ROWMAJOR, OUT_F32, 64, 2>(src, X, M, N, K, Y, sh, part, s);
-    case 128: return launch_prefill_bm<BF16, SRC_ROWMAJOR, OUT_F32, 128, 2>(src, X, M, N, K, Y, sh, part, s);
-    case 192: return launch_prefill_bm<BF16, SRC_ROWMAJOR, OUT_F32, 192, 1>(src, X, M, N, K, Y, sh, part, s);
-    default: return launch_prefill_bm<BF16, SRC_ROWMAJOR, OUT_F32, 256, 1>(src, X, M, N, K, Y, sh, part, s);
+    case 64: return PATCH_BM(64, 2, false);
+    case 128: return PATCH_BM(128, 2, false);
+    case 192: return PATCH_BM(192, 1, false);
+    default: return PATCH_BM(256, 1, false);
   }
+#undef PATCH_BM
 }
 
 // force_bm: 0 (the shape the cost model picks) or a width in {64, 128, 192,
-// 256}; force_lds: LDS staging (width 128 only).
-hipError_t launch_prefill(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* X, int64_t M, int64_t N,
-                          int64_t K, void* Y, void* ws, uint64_t ws_bytes, int force_bm, bool force_lds,
-                          hipStream_t s) {
+// 256}; force_lds: LDS staging (width 128 only).  src2 non-null: fused
+// gate/up (src2 = the up matrix when rowmajor; for a packed blob the two are
+// interleaved in src and src2 is src); Y is then H, M x N/2.
+hipError_t launch_prefill(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* src2, const void* X,
+                          int64_t M, int64_t N, int64_t K, void* Y, void* ws, uint64_t ws_bytes, int force_bm,
+                          bool force_lds, hipStream_t s) {
   if (K / kTile > kPfMaxKT) return hipErrorInvalidValue;
   if (force_bm && force_bm != 64 && force_bm != 128 && force_bm != 192 && force_bm != 256) return hipErrorInvalidValue;
   if (force_lds && force_bm != kLdsBM) return hipErrorInvalidValue;
-#define PATCH_PF(B, R, F) launch_prefill_t<B, R, F>(src, X, M, N, K, Y, ws, ws_bytes, force_bm, force_lds, s)
+  const bool fuse = src2 != nullptr;
+  if (fuse && (N % (2 * kTile))) return hipErrorInvalidValue;
+#define PATCH_PF(B, R, F, U) \
+  launch_prefill_t<B, R, F, U>(src, src2, X, M, N, K, Y, ws, ws_bytes, force_bm, force_lds, s)
+#define PATCH_PF2(B, R, F) (fuse ? PATCH_PF(B, R, F, true) : PATCH_PF(B, R, F, false))
   if (bf16) {
-    if (rowmajor) return out_f32 ? PATCH_PF(true, true, true) : PATCH_PF(true, true, false);
-    return out_f32 ? PATCH_PF(true, false, true) : PATCH_PF(true, false, false);
+    if (rowmajor) return out_f32 ? PATCH_PF2(true, true, true) : PATCH_PF2(true, true, false);
+    return out_f32 ? PATCH_PF2(true, false, true) : PATCH_PF2(true, false, false);
   }
-  if (rowmajor) return out_f32 ? PATCH_PF(false, true, true) : PATCH_PF(false, true, false);
-  return out_f32 ? PATCH_PF(false, false, true) : PATCH_PF(false, false, false);
+  if (rowmajor) return out_f32 ? PATCH_PF2(false, true, true) : PATCH_PF2(false, true, false);
+  return out_f32 ? PATCH_PF2(false, false, true) : PATCH_PF2(false, false, false);
+#undef PATCH_PF2
 #undef PATCH_PF
 }
 

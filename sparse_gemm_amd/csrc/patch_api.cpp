@@ -11,12 +11,13 @@
 #include "patch.h"
 
 namespace patch {
-hipError_t launch_pack(const void* W, const uint8_t* mask, int64_t N, int64_t K, uint8_t* blob, hipStream_t s);
-hipError_t launch_decode(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* X, int64_t M, int64_t N,
-                         int64_t K, void* Y, hipStream_t s);
-hipError_t launch_prefill(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* X, int64_t M, int64_t N,
-                          int64_t K, void* Y, void* ws, uint64_t ws_bytes, int force_bm, bool force_lds,
-                          hipStream_t s);
+hipError_t launch_pack(const void* W, const uint8_t* mask, const void* W2, const uint8_t* mask2, int64_t N, int64_t K,
+                       uint8_t* blob, hipStream_t s);
+hipError_t launch_decode(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* src2, const void* X,
+                         int64_t M, int64_t N, int64_t K, void* Y, hipStream_t s);
+hipError_t launch_prefill(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* src2, const void* X,
+                          int64_t M, int64_t N, int64_t K, void* Y, void* ws, uint64_t ws_bytes, int force_bm,
+                          bool force_lds, hipStream_t s);
 uint64_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K, bool rowmajor);
 double prefill_estimate_us(int64_t M, int64_t N, int64_t K, bool rowmajor, uint64_t ws_bytes);
 double decode_estimate_us(int64_t M, int64_t N, int64_t K, double w_bytes);
@@ -125,15 +126,21 @@ uint64_t patch_packed_bytes(patch_dtype dtype, int64_t N, int64_t K, const uint8
   return round_up(256 + 16 * (uint64_t)T, 256) + kDenseBytes * (uint64_t)(T - (int64_t)ns) + kSparseBytes * ns;
 }
 
-patch_status patch_pack(patch_dtype dtype, int64_t N, int64_t K, const void* W_dev, const uint8_t* tile_map_host,
-                        const uint8_t* mask_dev, void* packed_dev, uint64_t packed_bytes,
-                        patch_packed_desc* desc_out, void* stream) {
+}  // extern "C"
+
+// Pack W (or, with W2, the row-block interleave of W and W2: N = 2 F rows,
+// row-block 2i from W, 2i+1 from W2; tile_map_host is already the map of the
+// interleaved matrix).
+static patch_status pack_common(patch_dtype dtype, int64_t N, int64_t K, const void* W_dev, const void* W2_dev,
+                                const uint8_t* tile_map_host, const uint8_t* mask_dev, const uint8_t* mask2_dev,
+                                void* packed_dev, uint64_t packed_bytes, patch_packed_desc* desc_out, void* stream) {
   patch_status s;
   if ((s = check_dtype(dtype))) return s;
   if ((s = check_nk(N, K))) return s;
   if (!W_dev || !tile_map_host || !mask_dev || !packed_dev || !desc_out)
     return fail(PATCH_ERR_INVALID_ARG, "null pointer argument");
-  if (!aligned16(W_dev) || !aligned16(mask_dev) || !aligned16(packed_dev))
+  if (!aligned16(W_dev) || !aligned16(mask_dev) || !aligned16(packed_dev) || (W2_dev && !aligned16(W2_dev)) ||
+      (mask2_dev && !aligned16(mask2_dev)))
     return fail(PATCH_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
   const int64_t NT = N / kTile, KT = K / kTile, T = NT * KT;
   const uint64_t need = patch_packed_bytes(dtype, N, K, tile_map_host);
@@ -182,7 +189,7 @@ patch_status patch_pack(patch_dtype dtype, int64_t N, int64_t K, const void* W_d
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipMemcpyAsync(packed_dev, head.data(), head.size(), hipMemcpyHostToDevice, st);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(header)");
-  e = patch::launch_pack(W_dev, mask_dev, N, K, reinterpret_cast<uint8_t*>(packed_dev), st);
+  e = patch::launch_pack(W_dev, mask_dev, W2_dev, mask2_dev, N, K, reinterpret_cast<uint8_t*>(packed_dev), st);
   if (e != hipSuccess) return hip_fail(e, "launch pack");
   uint32_t flag = 0;
   e = hipMemcpyAsync(&flag, reinterpret_cast<uint8_t*>(packed_dev) + kErrFlagOffset, 4, hipMemcpyDeviceToHost, st);
@@ -205,6 +212,47 @@ patch_status patch_pack(patch_dtype dtype, int64_t N, int64_t K, const void* W_d
   d.total_bytes = need;
   *desc_out = d;
   return PATCH_OK;
+}
+
+// The tile map of the row-block interleave of two F x K matrices.
+static std::vector<uint8_t> interleave_maps(int64_t F, int64_t K, const uint8_t* map_g, const uint8_t* map_u) {
+  const int64_t FT = F / kTile, KT = K / kTile;
+  std::vector<uint8_t> m((size_t)(2 * FT * KT));
+  for (int64_t i = 0; i < FT; i++)
+    for (int64_t j = 0; j < KT; j++) {
+      m[(size_t)((2 * i) * KT + j)] = map_g[i * KT + j];
+      m[(size_t)((2 * i + 1) * KT + j)] = map_u[i * KT + j];
+    }
+  return m;
+}
+
+extern "C" {
+
+patch_status patch_pack(patch_dtype dtype, int64_t N, int64_t K, const void* W_dev, const uint8_t* tile_map_host,
+                        const uint8_t* mask_dev, void* packed_dev, uint64_t packed_bytes,
+                        patch_packed_desc* desc_out, void* stream) {
+  return pack_common(dtype, N, K, W_dev, nullptr, tile_map_host, mask_dev, nullptr, packed_dev, packed_bytes,
+                     desc_out, stream);
+}
+
+uint64_t patch_packed_bytes_gate_up(patch_dtype dtype, int64_t F, int64_t K, const uint8_t* map_g_host,
+                                    const uint8_t* map_u_host) {
+  if (check_dtype(dtype) || F <= 0 || F % kTile || check_nk(2 * F, K) || !map_g_host || !map_u_host) return 0;
+  const std::vector<uint8_t> m = interleave_maps(F, K, map_g_host, map_u_host);
+  return patch_packed_bytes(dtype, 2 * F, K, m.data());
+}
+
+patch_status patch_pack_gate_up(patch_dtype dtype, int64_t F, int64_t K, const void* Wg_dev, const void* Wu_dev,
+                                const uint8_t* map_g_host, const uint8_t* map_u_host, const uint8_t* mask_g_dev,
+                                const uint8_t* mask_u_dev, void* packed_dev, uint64_t packed_bytes,
+                                patch_packed_desc* desc_out, void* stream) {
+  patch_status s;
+  if (F <= 0 || F % kTile) return fail(PATCH_ERR_SHAPE, "F=%lld must be a positive multiple of 128", (long long)F);
+  if ((s = check_nk(2 * F, K))) return s;
+  if (!Wu_dev || !mask_u_dev || !map_g_host || !map_u_host) return fail(PATCH_ERR_INVALID_ARG, "null pointer argument");
+  const std::vector<uint8_t> m = interleave_maps(F, K, map_g_host, map_u_host);
+  return pack_common(dtype, 2 * F, K, Wg_dev, Wu_dev, m.data(), mask_g_dev, mask_u_dev, packed_dev, packed_bytes,
+                     desc_out, stream);
 }
 
 patch_status patch_desc_from_header(const void* header_host, uint64_t header_bytes, patch_packed_desc* desc_out) {
@@ -250,9 +298,12 @@ uint64_t patch_gemm_workspace_bytes(const patch_packed_desc* desc, int64_t M) {
 
 uint64_t patch_dense_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) { return workspace_for(M, N, K, true); }
 
+// src2 non-null: the fused gate/up product H = SiLU(X Wg^T) * (X Wu^T), N = 2F
+// (row-major: src = Wg, src2 = Wu; packed: src2 = src, the interleaved blob);
+// Y is then H, M x F.
 static patch_status gemm_common(bool rowmajor, patch_dtype dt, int64_t M, int64_t N, int64_t K, const void* src,
-                                uint64_t w_bytes, const void* X_dev, void* Y_dev, patch_dtype y_dtype, void* ws,
-                                uint64_t ws_bytes, int32_t variant, void* stream) {
+                                const void* src2, uint64_t w_bytes, const void* X_dev, void* Y_dev,
+                                patch_dtype y_dtype, void* ws, uint64_t ws_bytes, int32_t variant, void* stream) {
   patch_status s;
   if ((s = check_ydtype(dt, y_dtype))) return s;
   if (M < 0 || M > (int64_t)0x7fffffff) return fail(PATCH_ERR_INVALID_ARG, "M=%lld out of range", (long long)M);
@@ -262,8 +313,15 @@ static patch_status gemm_common(bool rowmajor, patch_dtype dt, int64_t M, int64_
     return fail(PATCH_ERR_INVALID_ARG, "decode variant needs M <= %lld (M=%lld)", (long long)kDecodeMaxM, (long long)M);
   if (M == 0) return PATCH_OK;
   if (!src || !X_dev || !Y_dev) return fail(PATCH_ERR_INVALID_ARG, "null pointer argument");
-  if (!aligned16(src) || !aligned16(X_dev) || !aligned16(Y_dev))
+  if (!aligned16(src) || !aligned16(X_dev) || !aligned16(Y_dev) || (src2 && !aligned16(src2)))
     return fail(PATCH_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  const bool fuse = src2 != nullptr;
+  if (fuse && N % (2 * kTile)) return fail(PATCH_ERR_SHAPE, "fused gate/up needs an even number of row-blocks");
+  // the fused decode kernel runs twice the waves: with more than one block of
+  // 16 tokens it needs K <= 32768
+  const bool fused_decode_ok = !fuse || M <= 16 || K <= 32768;
+  if (variant == PATCH_VARIANT_DECODE && !fused_decode_ok)
+    return fail(PATCH_ERR_UNSUPPORTED, "fused decode needs M <= 16 or K <= 32768");
   if (ws_bytes > 0 && (!ws || !aligned16(ws)))
     return fail(PATCH_ERR_INVALID_ARG, "workspace must be non-null and 16-byte aligned when workspace_bytes > 0");
   if (variant == PATCH_VARIANT_DECODE && K > kDecodeMaxK)
@@ -271,15 +329,16 @@ static patch_status gemm_common(bool rowmajor, patch_dtype dt, int64_t M, int64_
   // AUTO: decode for up to 16 tokens; up to 128, whichever kernel's time
   // model is lower (the prefill one for the split the workspace allows).
   bool decode = variant == PATCH_VARIANT_DECODE;
-  if (variant == PATCH_VARIANT_AUTO && K <= kDecodeMaxK && M <= kDecodeMaxM)
+  if (variant == PATCH_VARIANT_AUTO && K <= kDecodeMaxK && M <= kDecodeMaxM && fused_decode_ok)
     decode = M <= kDecodeAutoM || patch::decode_estimate_us(M, N, K, (double)w_bytes) <=
                                       patch::prefill_estimate_us(M, N, K, rowmajor, ws ? ws_bytes : 0);
   const bool bf16 = dt == PATCH_BF16, f32out = y_dtype == PATCH_F32;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   static const int kForceBm[8] = {0, 0, 0, 64, 128, 192, 256, 128};
-  hipError_t e = decode ? patch::launch_decode(bf16, rowmajor, f32out, src, X_dev, M, N, K, Y_dev, st)
-                        : patch::launch_prefill(bf16, rowmajor, f32out, src, X_dev, M, N, K, Y_dev, ws, ws_bytes,
-                                                kForceBm[variant], variant == PATCH_VARIANT_PREFILL_W128_LDS, st);
+  hipError_t e = decode ? patch::launch_decode(bf16, rowmajor, f32out, src, src2, X_dev, M, N, K, Y_dev, st)
+                        : patch::launch_prefill(bf16, rowmajor, f32out, src, src2, X_dev, M, N, K, Y_dev, ws,
+                                                ws_bytes, kForceBm[variant], variant == PATCH_VARIANT_PREFILL_W128_LDS,
+                                                st);
   if (e != hipSuccess) return hip_fail(e, decode ? "launch decode" : "launch prefill");
   return PATCH_OK;
 }
@@ -289,7 +348,7 @@ patch_status patch_gemm_ex(const patch_packed_desc* desc, const void* packed_dev
                            int32_t variant, void* stream) {
   patch_status s = check_desc(desc);
   if (s) return s;
-  return gemm_common(false, (patch_dtype)desc->dtype, M, desc->N, desc->K, packed_dev,
+  return gemm_common(false, (patch_dtype)desc->dtype, M, desc->N, desc->K, packed_dev, nullptr,
                      desc->total_bytes - desc->data_offset, X_dev, Y_dev, y_dtype, workspace_dev, workspace_bytes,
                      variant, stream);
 }
@@ -307,8 +366,8 @@ patch_status patch_dense_gemm_ex(patch_dtype dtype, int64_t M, int64_t N, int64_
   patch_status s;
   if ((s = check_dtype(dtype))) return s;
   if ((s = check_nk(N, K))) return s;
-  return gemm_common(true, dtype, M, N, K, W_dev, (uint64_t)(N * K * 2), X_dev, Y_dev, y_dtype, workspace_dev,
-                     workspace_bytes, variant, stream);
+  return gemm_common(true, dtype, M, N, K, W_dev, nullptr, (uint64_t)(N * K * 2), X_dev, Y_dev, y_dtype,
+                     workspace_dev, workspace_bytes, variant, stream);
 }
 
 patch_status patch_dense_gemm(patch_dtype dtype, int64_t M, int64_t N, int64_t K, const void* X_dev,
@@ -316,6 +375,39 @@ patch_status patch_dense_gemm(patch_dtype dtype, int64_t M, int64_t N, int64_t K
                               uint64_t workspace_bytes, void* stream) {
   return patch_dense_gemm_ex(dtype, M, N, K, X_dev, W_dev, Y_dev, y_dtype, workspace_dev, workspace_bytes,
                              PATCH_VARIANT_AUTO, stream);
+}
+
+uint64_t patch_gemm_swiglu_workspace_bytes(const patch_packed_desc* desc, int64_t M) {
+  if (!desc || desc->nt_n % 2) return 0;
+  return workspace_for(M, desc->N, desc->K, false);
+}
+
+uint64_t patch_dense_gemm_swiglu_workspace_bytes(int64_t M, int64_t F, int64_t K) {
+  if (F <= 0 || F % kTile) return 0;
+  return workspace_for(M, 2 * F, K, true);
+}
+
+patch_status patch_gemm_swiglu(const patch_packed_desc* desc, const void* packed_dev, const void* X_dev, int64_t M,
+                               void* H_dev, patch_dtype h_dtype, void* workspace_dev, uint64_t workspace_bytes,
+                               int32_t variant, void* stream) {
+  patch_status s = check_desc(desc);
+  if (s) return s;
+  if (desc->nt_n % 2) return fail(PATCH_ERR_SHAPE, "a gate/up blob has an even number of row-blocks");
+  return gemm_common(false, (patch_dtype)desc->dtype, M, desc->N, desc->K, packed_dev, packed_dev,
+                     desc->total_bytes - desc->data_offset, X_dev, H_dev, h_dtype, workspace_dev, workspace_bytes,
+                     variant, stream);
+}
+
+patch_status patch_dense_gemm_swiglu(patch_dtype dtype, int64_t M, int64_t F, int64_t K, const void* X_dev,
+                                     const void* Wg_dev, const void* Wu_dev, void* H_dev, patch_dtype h_dtype,
+                                     void* workspace_dev, uint64_t workspace_bytes, int32_t variant, void* stream) {
+  patch_status s;
+  if ((s = check_dtype(dtype))) return s;
+  if (F <= 0 || F % kTile) return fail(PATCH_ERR_SHAPE, "F=%lld must be a positive multiple of 128", (long long)F);
+  if ((s = check_nk(2 * F, K))) return s;
+  if (!Wu_dev) return fail(PATCH_ERR_INVALID_ARG, "null pointer argument");
+  return gemm_common(true, dtype, M, 2 * F, K, Wg_dev, Wu_dev, (uint64_t)(2 * F * K * 2), X_dev, H_dev, h_dtype,
+                     workspace_dev, workspace_bytes, variant, stream);
 }
 
 }  // extern "C"

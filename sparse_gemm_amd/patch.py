@@ -45,7 +45,9 @@ class Desc(ctypes.Structure):
 
 EXPORTS = ("patch_abi_version", "patch_packed_bytes", "patch_pack", "patch_desc_from_header",
            "patch_gemm_workspace_bytes", "patch_dense_gemm_workspace_bytes", "patch_gemm", "patch_gemm_ex",
-           "patch_dense_gemm", "patch_dense_gemm_ex",
+           "patch_dense_gemm", "patch_dense_gemm_ex", "patch_packed_bytes_gate_up", "patch_pack_gate_up",
+           "patch_gemm_swiglu_workspace_bytes", "patch_gemm_swiglu", "patch_dense_gemm_swiglu_workspace_bytes",
+           "patch_dense_gemm_swiglu",
            "patch_status_string", "patch_last_error")
 
 _lib = None
@@ -81,6 +83,18 @@ def load():
     lib.patch_dense_gemm.restype = ctypes.c_int
     lib.patch_dense_gemm_ex.argtypes = [ctypes.c_int, I64, I64, I64, P, P, P, ctypes.c_int, P, U64, I32, P]
     lib.patch_dense_gemm_ex.restype = ctypes.c_int
+    lib.patch_packed_bytes_gate_up.argtypes = [ctypes.c_int, I64, I64, P, P]
+    lib.patch_packed_bytes_gate_up.restype = U64
+    lib.patch_pack_gate_up.argtypes = [ctypes.c_int, I64, I64, P, P, P, P, P, P, P, U64, DP, P]
+    lib.patch_pack_gate_up.restype = ctypes.c_int
+    lib.patch_gemm_swiglu_workspace_bytes.argtypes = [DP, I64]
+    lib.patch_gemm_swiglu_workspace_bytes.restype = U64
+    lib.patch_gemm_swiglu.argtypes = [DP, P, P, I64, P, ctypes.c_int, P, U64, I32, P]
+    lib.patch_gemm_swiglu.restype = ctypes.c_int
+    lib.patch_dense_gemm_swiglu_workspace_bytes.argtypes = [I64, I64, I64]
+    lib.patch_dense_gemm_swiglu_workspace_bytes.restype = U64
+    lib.patch_dense_gemm_swiglu.argtypes = [ctypes.c_int, I64, I64, I64, P, P, P, P, ctypes.c_int, P, U64, I32, P]
+    lib.patch_dense_gemm_swiglu.restype = ctypes.c_int
     lib.patch_status_string.argtypes = [ctypes.c_int]
     lib.patch_status_string.restype = ctypes.c_char_p
     lib.patch_last_error.argtypes = []
@@ -240,4 +254,68 @@ def dense_gemm(X: torch.Tensor, W: torch.Tensor, out_dtype: Optional[torch.dtype
         nb = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.patch_dense_gemm_ex(_dt(X.dtype), M, N, K, X.data_ptr(), W.data_ptr(), out.data_ptr(), _dt(od),
                                    None if ws is None else ws.data_ptr(), nb, VARIANTS[variant], _stream(dev)))
+    return out
+
+
+def pack_gate_up(Wg: torch.Tensor, Wu: torch.Tensor, map_g, map_u, mask_g: torch.Tensor, mask_u: torch.Tensor,
+                 out: Optional[torch.Tensor] = None) -> PackedWeight:
+    """Pack gate and up weights (F x K each, device) into one blob of their
+    row-block interleave (patch_pack_gate_up)."""
+    lib = load()
+    F, K = Wg.shape
+    if tuple(Wu.shape) != (F, K) or Wu.dtype != Wg.dtype:
+        raise ValueError("gate and up weights must have the same shape and dtype")
+    tg, tu = _host_map(map_g), _host_map(map_u)
+    nbytes = int(lib.patch_packed_bytes_gate_up(_dt(Wg.dtype), F, K, tg.ctypes.data_as(ctypes.c_void_p),
+                                                tu.ctypes.data_as(ctypes.c_void_p)))
+    if nbytes == 0:
+        raise PatchError(2, f"invalid shape/dtype for pack_gate_up: {tuple(Wg.shape)} {Wg.dtype}")
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=Wg.device)
+    desc = Desc()
+    _check(lib.patch_pack_gate_up(_dt(Wg.dtype), F, K, _ptr(Wg), _ptr(Wu), tg.ctypes.data_as(ctypes.c_void_p),
+                                  tu.ctypes.data_as(ctypes.c_void_p), _ptr(mask_g), _ptr(mask_u), _ptr(out),
+                                  out.numel(), ctypes.byref(desc), _stream()))
+    return PackedWeight(out, desc)
+
+
+def gemm_swiglu(X: torch.Tensor, packed: PackedWeight, out_dtype: Optional[torch.dtype] = None,
+                variant: str = "auto", out: Optional[torch.Tensor] = None, workspace="auto") -> torch.Tensor:
+    """H = SiLU(X Wg^T) * (X Wu^T) from a gate/up blob (patch_gemm_swiglu)."""
+    lib = _lib or load()
+    M = X.shape[0]
+    F = packed.N // 2
+    od = out_dtype or X.dtype
+    dev = X.get_device()
+    if out is None:
+        out = torch.empty((M, F), dtype=od, device=X.device)
+    ws, nb = None, 0
+    if workspace is not None:
+        nb = _ws_bytes("swiglu", M, packed.N, packed.K, dev,
+                       lambda: lib.patch_gemm_swiglu_workspace_bytes(ctypes.byref(packed.desc), M))
+        ws = _workspace(nb, workspace, X.device)
+        nb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.patch_gemm_swiglu(ctypes.byref(packed.desc), packed.blob.data_ptr(), X.data_ptr(), M, out.data_ptr(),
+                                 _dt(od), None if ws is None else ws.data_ptr(), nb, VARIANTS[variant], _stream(dev)))
+    return out
+
+
+def dense_gemm_swiglu(X: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, out_dtype: Optional[torch.dtype] = None,
+                      variant: str = "auto", out: Optional[torch.Tensor] = None, workspace="auto") -> torch.Tensor:
+    """Same-shape dense baseline of gemm_swiglu from row-major Wg, Wu (patch_dense_gemm_swiglu)."""
+    lib = _lib or load()
+    M, K = X.shape
+    F = Wg.shape[0]
+    od = out_dtype or X.dtype
+    dev = X.get_device()
+    if out is None:
+        out = torch.empty((M, F), dtype=od, device=X.device)
+    ws, nb = None, 0
+    if workspace is not None:
+        nb = _ws_bytes("dense_swiglu", M, F, K, dev, lambda: lib.patch_dense_gemm_swiglu_workspace_bytes(M, F, K))
+        ws = _workspace(nb, workspace, X.device)
+        nb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.patch_dense_gemm_swiglu(_dt(X.dtype), M, F, K, X.data_ptr(), Wg.data_ptr(), Wu.data_ptr(),
+                                       out.data_ptr(), _dt(od), None if ws is None else ws.data_ptr(), nb,
+                                       VARIANTS[variant], _stream(dev)))
     return out
