@@ -188,6 +188,21 @@ patch_status patch_dense_gemm_ex(patch_dtype dtype, int64_t M, int64_t N, int64_
                                  uint64_t workspace_bytes, int32_t variant, void* stream);
 
 /*
+ * Several projections of the same input in one launch (e.g. attention's q,
+ * k and v): pack the row-concatenation of count (1 .. 8) matrices with the
+ * same K -- matrix i is N_host[i] x K (a multiple of 128), with its own tile
+ * map (host) and mask (device), arguments per matrix as patch_pack -- into
+ * one format-3 blob with N = sum of N_host.  patch_gemm on it returns the
+ * projections side by side: Y = [Y_0 | Y_1 | ...], M x N.
+ */
+uint64_t patch_packed_bytes_concat(patch_dtype dtype, int32_t count, const int64_t* N_host, int64_t K,
+                                   const uint8_t* const* tile_maps_host);
+patch_status patch_pack_concat(patch_dtype dtype, int32_t count, const int64_t* N_host, int64_t K,
+                               const void* const* W_dev, const uint8_t* const* tile_maps_host,
+                               const uint8_t* const* masks_dev, void* packed_dev, uint64_t packed_bytes,
+                               patch_packed_desc* desc_out, void* stream);
+
+/*
  * Fused gate/up projection of the LLaMA MLP (the pages evaluate PATCH on
  * LLaMA-2 models, gist.science explainer, section 4 "Experimental Results";
  * that architecture's MLP is down(SiLU(gate(x)) * up(x))):

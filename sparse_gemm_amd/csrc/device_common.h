@@ -19,6 +19,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include "pack_sources.h"
 #include <stdint.h>
 
 namespace patch {

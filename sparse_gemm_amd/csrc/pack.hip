@@ -28,22 +28,26 @@
 namespace patch {
 
 // grid: T * 8 workgroups of 256 threads; workgroup (t, part) packs part of tile t.
-// W2/mask2 non-null: the blob's matrix is the row-block interleave of W (even
-// row-blocks) and W2 (odd row-blocks), as for a fused gate/up projection.
-__global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, const uint8_t* __restrict__ mask,
-                                              const uint16_t* __restrict__ W2, const uint8_t* __restrict__ mask2,
-                                              int K, int KT, uint8_t* __restrict__ blob) {
+// The blob's matrix is assembled from up to kPackMaxSources row-major
+// matrices of K columns (PackSources): concatenated by rows (several
+// projections packed as one), or -- interleave -- row-block ib taken from
+// source ib & 1, row-block ib / 2 (a fused gate/up projection).
+__global__ __launch_bounds__(256) void k_pack(PackSources src, int K, int KT, uint8_t* __restrict__ blob) {
   const int t = blockIdx.x >> 3;
   const int part = blockIdx.x & 7;
   const TileEntry e = reinterpret_cast<const TileEntry*>(blob + kHeaderBytes)[t];
   const int ib = t / KT, j = t - (t / KT) * KT;
   // source matrix and its row-block for blob row-block ib
-  const bool second = W2 != nullptr && (ib & 1);
-  if (second) {
-    W = W2;
-    mask = mask2;
+  int si = 0, i = ib;
+  if (src.interleave) {
+    si = ib & 1;
+    i = ib >> 1;
+  } else {
+    while (si + 1 < src.n && ib >= src.start[si + 1]) si++;
+    i = ib - src.start[si];
   }
-  const int i = W2 != nullptr ? (ib >> 1) : ib;
+  const uint16_t* __restrict__ W = src.W[si];
+  const uint8_t* __restrict__ mask = src.mask[si];
   if (e.kind == 0) {
     if (part >= 4) return;
     const int c = part * 256 + threadIdx.x;  // (q, band, l), 0 .. 1023
@@ -110,12 +114,10 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, co
   if (bad) atomicOr(reinterpret_cast<uint32_t*>(blob + kErrFlagOffset), 1u);
 }
 
-hipError_t launch_pack(const void* W, const uint8_t* mask, const void* W2, const uint8_t* mask2, int64_t N, int64_t K,
-                       uint8_t* blob, hipStream_t s) {
+hipError_t launch_pack(const PackSources& src, int64_t N, int64_t K, uint8_t* blob, hipStream_t s) {
   const int KT = (int)(K / kTile);
   const int64_t T = (N / kTile) * KT;
-  hipLaunchKernelGGL(k_pack, dim3((unsigned)(T * 8)), dim3(256), 0, s, reinterpret_cast<const uint16_t*>(W), mask,
-                     reinterpret_cast<const uint16_t*>(W2), mask2, (int)K, KT, blob);
+  hipLaunchKernelGGL(k_pack, dim3((unsigned)(T * 8)), dim3(256), 0, s, src, (int)K, KT, blob);
   return hipGetLastError();
 }
 

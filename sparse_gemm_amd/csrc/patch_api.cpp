@@ -8,11 +8,11 @@
 #include <string>
 #include <vector>
 
+#include "pack_sources.h"
 #include "patch.h"
 
 namespace patch {
-hipError_t launch_pack(const void* W, const uint8_t* mask, const void* W2, const uint8_t* mask2, int64_t N, int64_t K,
-                       uint8_t* blob, hipStream_t s);
+hipError_t launch_pack(const PackSources& src, int64_t N, int64_t K, uint8_t* blob, hipStream_t s);
 hipError_t launch_decode(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* src2, const void* X,
                          int64_t M, int64_t N, int64_t K, void* Y, hipStream_t s);
 hipError_t launch_prefill(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* src2, const void* X,
@@ -128,20 +128,21 @@ uint64_t patch_packed_bytes(patch_dtype dtype, int64_t N, int64_t K, const uint8
 
 }  // extern "C"
 
-// Pack W (or, with W2, the row-block interleave of W and W2: N = 2 F rows,
-// row-block 2i from W, 2i+1 from W2; tile_map_host is already the map of the
-// interleaved matrix).
-static patch_status pack_common(patch_dtype dtype, int64_t N, int64_t K, const void* W_dev, const void* W2_dev,
-                                const uint8_t* tile_map_host, const uint8_t* mask_dev, const uint8_t* mask2_dev,
-                                void* packed_dev, uint64_t packed_bytes, patch_packed_desc* desc_out, void* stream) {
+// Pack the N x K matrix assembled from the sources (see PackSources);
+// tile_map_host is the map of the assembled matrix.
+static patch_status pack_common(patch_dtype dtype, int64_t N, int64_t K, const patch::PackSources& src,
+                                const uint8_t* tile_map_host, void* packed_dev, uint64_t packed_bytes,
+                                patch_packed_desc* desc_out, void* stream) {
   patch_status s;
   if ((s = check_dtype(dtype))) return s;
   if ((s = check_nk(N, K))) return s;
-  if (!W_dev || !tile_map_host || !mask_dev || !packed_dev || !desc_out)
-    return fail(PATCH_ERR_INVALID_ARG, "null pointer argument");
-  if (!aligned16(W_dev) || !aligned16(mask_dev) || !aligned16(packed_dev) || (W2_dev && !aligned16(W2_dev)) ||
-      (mask2_dev && !aligned16(mask2_dev)))
-    return fail(PATCH_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  if (!tile_map_host || !packed_dev || !desc_out) return fail(PATCH_ERR_INVALID_ARG, "null pointer argument");
+  for (int i = 0; i < src.n; i++) {
+    if (!src.W[i] || !src.mask[i]) return fail(PATCH_ERR_INVALID_ARG, "null pointer argument");
+    if (!aligned16(src.W[i]) || !aligned16(src.mask[i]))
+      return fail(PATCH_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  }
+  if (!aligned16(packed_dev)) return fail(PATCH_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
   const int64_t NT = N / kTile, KT = K / kTile, T = NT * KT;
   const uint64_t need = patch_packed_bytes(dtype, N, K, tile_map_host);
   if (packed_bytes < need)
@@ -189,7 +190,7 @@ static patch_status pack_common(patch_dtype dtype, int64_t N, int64_t K, const v
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipMemcpyAsync(packed_dev, head.data(), head.size(), hipMemcpyHostToDevice, st);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(header)");
-  e = patch::launch_pack(W_dev, mask_dev, W2_dev, mask2_dev, N, K, reinterpret_cast<uint8_t*>(packed_dev), st);
+  e = patch::launch_pack(src, N, K, reinterpret_cast<uint8_t*>(packed_dev), st);
   if (e != hipSuccess) return hip_fail(e, "launch pack");
   uint32_t flag = 0;
   e = hipMemcpyAsync(&flag, reinterpret_cast<uint8_t*>(packed_dev) + kErrFlagOffset, 4, hipMemcpyDeviceToHost, st);
@@ -231,8 +232,61 @@ extern "C" {
 patch_status patch_pack(patch_dtype dtype, int64_t N, int64_t K, const void* W_dev, const uint8_t* tile_map_host,
                         const uint8_t* mask_dev, void* packed_dev, uint64_t packed_bytes,
                         patch_packed_desc* desc_out, void* stream) {
-  return pack_common(dtype, N, K, W_dev, nullptr, tile_map_host, mask_dev, nullptr, packed_dev, packed_bytes,
-                     desc_out, stream);
+  patch::PackSources src{};
+  src.W[0] = reinterpret_cast<const uint16_t*>(W_dev);
+  src.mask[0] = mask_dev;
+  src.start[0] = 0;
+  src.start[1] = (int)(N / kTile);
+  src.n = 1;
+  src.interleave = 0;
+  return pack_common(dtype, N, K, src, tile_map_host, packed_dev, packed_bytes, desc_out, stream);
+}
+
+// Row-concatenation of count matrices with the same K: sizes and the
+// concatenated tile map (empty on invalid arguments).
+static std::vector<uint8_t> concat_maps(int32_t count, const int64_t* N_host, int64_t K,
+                                        const uint8_t* const* maps_host, int64_t* N_total) {
+  std::vector<uint8_t> m;
+  *N_total = 0;
+  if (count < 1 || count > patch::kPackMaxSources || !N_host || !maps_host || K <= 0 || K % kTile) return m;
+  const int64_t KT = K / kTile;
+  for (int32_t i = 0; i < count; i++) {
+    if (N_host[i] <= 0 || N_host[i] % kTile || !maps_host[i]) return std::vector<uint8_t>();
+    *N_total += N_host[i];
+  }
+  if (*N_total > kMaxDim) return std::vector<uint8_t>();
+  for (int32_t i = 0; i < count; i++) m.insert(m.end(), maps_host[i], maps_host[i] + (N_host[i] / kTile) * KT);
+  return m;
+}
+
+uint64_t patch_packed_bytes_concat(patch_dtype dtype, int32_t count, const int64_t* N_host, int64_t K,
+                                   const uint8_t* const* tile_maps_host) {
+  int64_t N = 0;
+  const std::vector<uint8_t> m = concat_maps(count, N_host, K, tile_maps_host, &N);
+  if (m.empty()) return 0;
+  return patch_packed_bytes(dtype, N, K, m.data());
+}
+
+patch_status patch_pack_concat(patch_dtype dtype, int32_t count, const int64_t* N_host, int64_t K,
+                               const void* const* W_dev, const uint8_t* const* tile_maps_host,
+                               const uint8_t* const* masks_dev, void* packed_dev, uint64_t packed_bytes,
+                               patch_packed_desc* desc_out, void* stream) {
+  if (!W_dev || !masks_dev) return fail(PATCH_ERR_INVALID_ARG, "null pointer argument");
+  if (count < 1 || count > patch::kPackMaxSources)
+    return fail(PATCH_ERR_INVALID_ARG, "count=%d must be 1 .. %d", (int)count, patch::kPackMaxSources);
+  int64_t N = 0;
+  const std::vector<uint8_t> m = concat_maps(count, N_host, K, tile_maps_host, &N);
+  if (m.empty()) return fail(PATCH_ERR_SHAPE, "every N must be a positive multiple of 128, K too, sum within range");
+  patch::PackSources src{};
+  src.n = count;
+  src.interleave = 0;
+  src.start[0] = 0;
+  for (int32_t i = 0; i < count; i++) {
+    src.W[i] = reinterpret_cast<const uint16_t*>(W_dev[i]);
+    src.mask[i] = masks_dev[i];
+    src.start[i + 1] = src.start[i] + (int)(N_host[i] / kTile);
+  }
+  return pack_common(dtype, N, K, src, m.data(), packed_dev, packed_bytes, desc_out, stream);
 }
 
 uint64_t patch_packed_bytes_gate_up(patch_dtype dtype, int64_t F, int64_t K, const uint8_t* map_g_host,
@@ -249,10 +303,16 @@ patch_status patch_pack_gate_up(patch_dtype dtype, int64_t F, int64_t K, const v
   patch_status s;
   if (F <= 0 || F % kTile) return fail(PATCH_ERR_SHAPE, "F=%lld must be a positive multiple of 128", (long long)F);
   if ((s = check_nk(2 * F, K))) return s;
-  if (!Wu_dev || !mask_u_dev || !map_g_host || !map_u_host) return fail(PATCH_ERR_INVALID_ARG, "null pointer argument");
+  if (!map_g_host || !map_u_host) return fail(PATCH_ERR_INVALID_ARG, "null pointer argument");
   const std::vector<uint8_t> m = interleave_maps(F, K, map_g_host, map_u_host);
-  return pack_common(dtype, 2 * F, K, Wg_dev, Wu_dev, m.data(), mask_g_dev, mask_u_dev, packed_dev, packed_bytes,
-                     desc_out, stream);
+  patch::PackSources src{};
+  src.n = 2;
+  src.interleave = 1;
+  src.W[0] = reinterpret_cast<const uint16_t*>(Wg_dev);
+  src.W[1] = reinterpret_cast<const uint16_t*>(Wu_dev);
+  src.mask[0] = mask_g_dev;
+  src.mask[1] = mask_u_dev;
+  return pack_common(dtype, 2 * F, K, src, m.data(), packed_dev, packed_bytes, desc_out, stream);
 }
 
 patch_status patch_desc_from_header(const void* header_host, uint64_t header_bytes, patch_packed_desc* desc_out) {

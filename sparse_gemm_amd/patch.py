@@ -47,7 +47,7 @@ EXPORTS = ("patch_abi_version", "patch_packed_bytes", "patch_pack", "patch_desc_
            "patch_gemm_workspace_bytes", "patch_dense_gemm_workspace_bytes", "patch_gemm", "patch_gemm_ex",
            "patch_dense_gemm", "patch_dense_gemm_ex", "patch_packed_bytes_gate_up", "patch_pack_gate_up",
            "patch_gemm_swiglu_workspace_bytes", "patch_gemm_swiglu", "patch_dense_gemm_swiglu_workspace_bytes",
-           "patch_dense_gemm_swiglu",
+           "patch_dense_gemm_swiglu", "patch_packed_bytes_concat", "patch_pack_concat",
            "patch_status_string", "patch_last_error")
 
 _lib = None
@@ -95,6 +95,10 @@ def load():
     lib.patch_dense_gemm_swiglu_workspace_bytes.restype = U64
     lib.patch_dense_gemm_swiglu.argtypes = [ctypes.c_int, I64, I64, I64, P, P, P, P, ctypes.c_int, P, U64, I32, P]
     lib.patch_dense_gemm_swiglu.restype = ctypes.c_int
+    lib.patch_packed_bytes_concat.argtypes = [ctypes.c_int, I32, P, I64, P]
+    lib.patch_packed_bytes_concat.restype = U64
+    lib.patch_pack_concat.argtypes = [ctypes.c_int, I32, P, I64, P, P, P, P, U64, DP, P]
+    lib.patch_pack_concat.restype = ctypes.c_int
     lib.patch_status_string.argtypes = [ctypes.c_int]
     lib.patch_status_string.restype = ctypes.c_char_p
     lib.patch_last_error.argtypes = []
@@ -319,3 +323,30 @@ def dense_gemm_swiglu(X: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, out_d
                                        out.data_ptr(), _dt(od), None if ws is None else ws.data_ptr(), nb,
                                        VARIANTS[variant], _stream(dev)))
     return out
+
+
+def pack_concat(Ws, tile_maps, masks, out: Optional[torch.Tensor] = None) -> PackedWeight:
+    """Pack the row-concatenation of several weights with the same K (device
+    tensors, host tile maps, device masks) into one blob (patch_pack_concat):
+    one GEMM on it returns the projections side by side."""
+    lib = load()
+    n = len(Ws)
+    if not (len(tile_maps) == len(masks) == n) or n < 1:
+        raise ValueError("one tile map and one mask per weight")
+    K = Ws[0].shape[1]
+    if any(W.dtype != Ws[0].dtype or W.shape[1] != K for W in Ws):
+        raise ValueError("the weights must share dtype and K")
+    Ns = (ctypes.c_int64 * n)(*[int(W.shape[0]) for W in Ws])
+    maps = [_host_map(t) for t in tile_maps]
+    mp = (ctypes.c_void_p * n)(*[m.ctypes.data for m in maps])
+    wp = (ctypes.c_void_p * n)(*[W.data_ptr() for W in Ws])
+    kp = (ctypes.c_void_p * n)(*[m.data_ptr() for m in masks])
+    nbytes = int(lib.patch_packed_bytes_concat(_dt(Ws[0].dtype), n, Ns, K, mp))
+    if nbytes == 0:
+        raise PatchError(2, "invalid shapes for pack_concat")
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=Ws[0].device)
+    desc = Desc()
+    _check(lib.patch_pack_concat(_dt(Ws[0].dtype), n, Ns, K, wp, mp, kp, _ptr(out), out.numel(), ctypes.byref(desc),
+                                 _stream()))
+    return PackedWeight(out, desc)

@@ -1,7 +1,8 @@
-"""GPU parity of the fused gate/up projection H = SiLU(X Wg^T) * (X Wu^T)
-(the LLaMA MLP's gated product; the pages evaluate PATCH on LLaMA-2 models,
-gist.science explainer, section 4 "Experimental Results") against the CPU
-oracle, through the C ABI.
+"""GPU parity of the fused projections against the CPU oracle, through the C
+ABI: the gate/up projection H = SiLU(X Wg^T) * (X Wu^T) (the LLaMA MLP's
+gated product; the pages evaluate PATCH on LLaMA-2 models, gist.science
+explainer, section 4 "Experimental Results"), and several projections of
+one input packed as one (attention's q, k, v).
 
 Bars: the packed blob is bit-exact with the oracle's pack of the row-block
 interleave of gate and up.  A 16-bit H is compared with the fp64 oracle
@@ -198,3 +199,51 @@ def test_swiglu_llama7b_mlp(M):
     else:
         rows = np.unique(np.linspace(0, M - 1, 24).astype(np.int64))
         check_h(h[torch.from_numpy(rows).cuda()], _ref(g, u, Xb, rows), "bf16", what=f"M={M} sampled")
+
+
+# ------------------------------------------------------------------ several projections in one blob
+def _concat_oracle_blob(ps):
+    W = np.concatenate([p.w for p in ps])
+    tm = np.concatenate([p.tile_map for p in ps])
+    mk = np.concatenate([p.mask for p in ps])
+    return oracle.pack(ps[0].dtype, W, tm, mk)
+
+
+def _pack_concat(ps):
+    return patch.pack_concat([dev_bits(p.w, p.dtype) for p in ps], [p.tile_map for p in ps],
+                             [dev_u8(p.mask) for p in ps])
+
+
+def test_pack_concat_bit_exact():
+    ps = [inputs.make_custom("bf16", n, 640, 80 + n, "bernoulli", 0.5, "uniform") for n in (128, 384, 256)]
+    pw = _pack_concat(ps)
+    torch.cuda.synchronize()
+    assert pw.N == 768 and np.array_equal(pw.blob.cpu().numpy(), _concat_oracle_blob(ps))
+
+
+def test_pack_concat_llama7b_qkv_bit_exact():
+    cfg = inputs.CONFIGS["sweep"]
+    ps = [inputs.make_weights(cfg, mi, 2) for mi in (0, 1, 2)]  # q_proj, k_proj, v_proj at s = 0.5
+    pw = _pack_concat(ps)
+    torch.cuda.synchronize()
+    assert np.array_equal(pw.blob.cpu().numpy(), _concat_oracle_blob(ps))
+
+
+@pytest.mark.parametrize("M", [1, 16, 64, 300])
+def test_concat_gemm_is_the_projections_side_by_side(M):
+    ps = [inputs.make_custom("bf16", n, 640, 90 + n, "bernoulli", 0.5, "uniform") for n in (256, 128, 384)]
+    pw = _pack_concat(ps)
+    Xb = inputs.make_custom_x("bf16", M, 640, 95 + M)
+    ref = np.concatenate([oracle.gemm_f64("bf16", Xb, p.w, p.tile_map, p.mask) for p in ps], axis=1)
+    X = dev_bits(Xb, "bf16")
+    for v in ["auto", "prefill"] + (["decode"] if M <= 128 else []):
+        assert_close(patch.gemm(X, pw, variant=v), ref, what=f"M={M} {v}")
+
+
+def test_pack_concat_rejects_bad_arguments():
+    p = inputs.make_custom("bf16", 128, 256, 99, "bernoulli", 0.5, "uniform")
+    W, mk = dev_bits(p.w, "bf16"), dev_u8(p.mask)
+    with pytest.raises(ValueError):
+        patch.pack_concat([W], [p.tile_map, p.tile_map], [mk])
+    with pytest.raises(patch.PatchError):
+        patch.pack_concat([W] * 9, [p.tile_map] * 9, [mk] * 9)
