@@ -511,6 +511,106 @@ def run_prefill_workload(args):
                   flush=True)
 
 
+def fused_set(kind, si, Ms, steps, warmup, batches):
+    """Fused projections of the sweep's LLaMA-2-7B weights at sparse-tile
+    fraction index si, one record per M:
+      kind "swiglu": gate_proj + up_proj -> H = SiLU(X Wg^T) * (X Wu^T):
+        fused (patch_gemm_swiglu, one launch) against the two hybrid GEMMs plus
+        torch's elementwise SiLU * mul, the same-shape dense fused kernel
+        (patch_dense_gemm_swiglu) and hipBLASLt (two torch.matmul + SiLU * mul,
+        eager);
+      kind "qkv": q_proj, k_proj, v_proj packed as one blob: one patch_gemm
+        against three, the dense kernel on the concatenated weight and
+        hipBLASLt (three torch.matmul, eager).
+    Our kernels are timed as graph replays (as elsewhere), hipBLASLt eagerly."""
+    import torch
+
+    from sparse_gemm_amd import inputs, patch
+
+    cfg = inputs.CONFIGS["sweep"]
+    mis = (4, 5) if kind == "swiglu" else (0, 1, 2)
+    ps = [inputs.make_weights(cfg, mi, si) for mi in mis]
+    tdt = torch.bfloat16
+    Ws = [dev_bits(p.w, tdt) for p in ps]
+    masks = [torch.from_numpy(p.mask).cuda() for p in ps]
+    singles = [patch.pack(W, p.tile_map, mk) for W, p, mk in zip(Ws, ps, masks)]
+    if kind == "swiglu":
+        fused = patch.pack_gate_up(Ws[0], Ws[1], ps[0].tile_map, ps[1].tile_map, masks[0], masks[1])
+    else:
+        fused = patch.pack_concat(Ws, [p.tile_map for p in ps], masks)
+    del masks
+    K = ps[0].K
+    Ntot = sum(p.N for p in ps)
+    F = ps[0].N
+    blobs = rotate(fused.blob, fused.nbytes)
+    sblobs = [rotate(sp.blob, sp.nbytes) for sp in singles]
+    Wcat = torch.cat(Ws) if kind == "qkv" else None
+    Wrot = rotate(Wcat, Wcat.numel() * 2) if kind == "qkv" else None
+    Wg_rot = rotate(Ws[0], Ws[0].numel() * 2) if kind == "swiglu" else None
+    Wu_rot = rotate(Ws[1], Ws[1].numel() * 2) if kind == "swiglu" else None
+    out = {}
+    for M in Ms:
+        X = dev_bits(inputs.make_x(cfg, M, K, matrix_index=mis[0]), tdt)
+        outw = F if kind == "swiglu" else Ntot
+        Y = torch.empty((M, outw), dtype=tdt, device="cuda")
+        Ys = [torch.empty((M, p.N), dtype=tdt, device="cuda") for p in ps]
+
+        if kind == "swiglu":
+            def f_fused(k):
+                patch.gemm_swiglu(X, patch.PackedWeight(blobs[k % len(blobs)], fused.desc), out=Y)
+
+            def f_unfused(k):
+                for sb, sp, y in zip(sblobs, singles, Ys):
+                    patch.gemm(X, patch.PackedWeight(sb[k % len(sb)], sp.desc), out=y)
+                torch.mul(torch.nn.functional.silu(Ys[0]), Ys[1], out=Y)
+
+            def f_dense(k):
+                patch.dense_gemm_swiglu(X, Wg_rot[k % len(Wg_rot)], Wu_rot[k % len(Wu_rot)], out=Y)
+
+            def f_blas(k):
+                torch.matmul(X, Wg_rot[k % len(Wg_rot)].t(), out=Ys[0])
+                torch.matmul(X, Wu_rot[k % len(Wu_rot)].t(), out=Ys[1])
+                torch.mul(torch.nn.functional.silu(Ys[0]), Ys[1], out=Y)
+        else:
+            def f_fused(k):
+                patch.gemm(X, patch.PackedWeight(blobs[k % len(blobs)], fused.desc), out=Y)
+
+            def f_unfused(k):
+                for sb, sp, y in zip(sblobs, singles, Ys):
+                    patch.gemm(X, patch.PackedWeight(sb[k % len(sb)], sp.desc), out=y)
+
+            def f_dense(k):
+                patch.dense_gemm(X, Wrot[k % len(Wrot)], out=Y)
+
+            def f_blas(k):
+                Wr = Wrot[k % len(Wrot)]
+                for i, y in enumerate(Ys):
+                    torch.matmul(X, Wr[4096 * i:4096 * (i + 1)].t(), out=y)
+
+        _, per_g = time_graphs([("fused", f_fused), ("unfused", f_unfused), ("dense", f_dense)], steps, warmup,
+                               batches)
+        _, per_e = time_launches([("fused", f_fused), ("unfused", f_unfused), ("blas", f_blas)], steps, warmup,
+                                 batches)
+        t = median(per_g["fused"]) * 1e-3
+        ns = sum(int(p.tile_map.sum()) for p in ps)
+        T = sum(int(p.tile_map.size) for p in ps)
+        nbytes = 256 + 16 * T + 32768 * (T - ns) + 18432 * ns + 2 * M * K + 2 * M * outw
+        t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+        t_mma = 2.0 * M * 128 * 128 * ((T - ns) / MFMA_PEAK_BF16_TFLOPS + ns / (2 * MFMA_PEAK_BF16_TFLOPS)) / 1e12
+        out[M] = dict(us=t * 1e6, us_unfused=median(per_g["unfused"]) * 1e3, us_dense=median(per_g["dense"]) * 1e3,
+                      us_eager=median(per_e["fused"]) * 1e3, us_unfused_eager=median(per_e["unfused"]) * 1e3,
+                      hipblaslt_us_eager=median(per_e["blas"]) * 1e3,
+                      speedup_vs_unfused=median(per_g["unfused"]) * 1e-3 / t,
+                      speedup_vs_dense=median(per_g["dense"]) * 1e-3 / t,
+                      speedup_vs_hipblaslt_eager=median(per_e["blas"]) / median(per_e["fused"]),
+                      tflops_dense_equiv=2.0 * M * Ntot * K / t / 1e12, gbps=nbytes / t / 1e9,
+                      roofline_bound="hbm" if t_hbm >= t_mma else "mfma", roofline_frac=max(t_hbm, t_mma) / t,
+                      N_total=Ntot, K=K, sparse_tile_fraction=ns / T)
+    del blobs, sblobs, Wrot, Wg_rot, Wu_rot
+    torch.cuda.empty_cache()
+    return out
+
+
 def write_report(path, steps, warmup, batches):
     """Every workload: decode, prefill MLP, the sparsity sweep and the 13B
     imbalanced shapes; one JSON line per (matrix, s, M).  Each time is the
@@ -543,6 +643,16 @@ def write_report(path, steps, warmup, batches):
         for mi in (0, 4, 6):  # q_proj-like, gate/up-like, down
             for si in range(5):
                 emit("sweep", mi, si, (1, 16, 128, 2048))
+        for kind in ("swiglu", "qkv"):
+            for si in (0, 2, 4):
+                res = fused_set(kind, si, (1, 16, 128, 2048), steps, warmup, batches)
+                for M, rec in res.items():
+                    rec = dict(config="fused_" + kind, matrix=kind, M=M, **rec)
+                    f.write(json.dumps(rec) + "\n")
+                    f.flush()
+                    print(f"[report] fused {kind} s={rec['sparse_tile_fraction']:.2f} M={M}: {rec['us']:.2f} us, "
+                          f"x{rec['speedup_vs_unfused']:.3f} vs unfused, x{rec['speedup_vs_dense']:.3f} vs dense",
+                          flush=True)
 
 
 if __name__ == "__main__":
