@@ -66,7 +66,9 @@ typedef enum {
   PATCH_VARIANT_PREFILL_W128 = 4,     /* registers, 128 */
   PATCH_VARIANT_PREFILL_W192 = 5,     /* registers, 192 */
   PATCH_VARIANT_PREFILL_W256 = 6,     /* registers, 256 */
-  PATCH_VARIANT_PREFILL_W128_LDS = 7  /* W and X staged through LDS, 128 */
+  PATCH_VARIANT_PREFILL_W128_LDS = 7, /* W and X staged through LDS, 128 */
+  PATCH_VARIANT_PREFILL_W192_LDS = 8, /* W and X staged through LDS, 192 */
+  PATCH_VARIANT_PREFILL_W256_LDS = 9  /* W and X staged through LDS, 256 */
 } patch_variant;
 
 /* Host-side mirror of the packed blob's header (format version 3). */
@@ -145,8 +147,8 @@ patch_status patch_desc_from_header(const void* header_host, uint64_t header_byt
  */
 uint64_t patch_gemm_workspace_bytes(const patch_packed_desc* desc, int64_t M);
 
-/* The same for patch_dense_gemm on an N x K weight (its shape choice differs:
- * it takes the LDS-staged kernel wherever the width would be 128 or more). */
+/* The same for patch_dense_gemm on an N x K weight (same kernels and shape
+ * choice as patch_gemm, every tile dense). */
 uint64_t patch_dense_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*

@@ -455,11 +455,10 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
 // LDS: 3 x (32 KB of W + 16 KB of X) + the tile entries = 152 KB, one
 // workgroup per CU.
 // ---------------------------------------------------------------------------
-constexpr int kLdsBM = 128;
-constexpr int kLdsStages = 3;
-constexpr int kLdsWStage = 32768;                // 2 row-blocks x 8 bands x 2 fragments of 1 KB
-constexpr int kLdsXStage = kLdsBM * kPfRowBytes;  // 16 KB
-constexpr int kLdsCopies = 6;                    // copies a wave issues per step
+constexpr int kLdsWStage = 32768;  // 2 row-blocks x 8 bands x 2 fragments of 1 KB
+// stages of the LDS ring for an M-block width: three at 128 (2 x 48 KB in
+// flight), two at 192 and 256 (a third would not fit the 160 KB of LDS)
+constexpr int lds_stages(int bm) { return bm <= 128 ? 3 : 2; }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 
@@ -493,10 +492,14 @@ __device__ __forceinline__ void wait_copies() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE>
+template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE, int BM>
 __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
-  constexpr int BM = kLdsBM;
-  constexpr int kNMB = BM / 32;  // 16-column M blocks per wave
+  constexpr int kNMB = BM / 32;                     // 16-column M blocks per wave
+  constexpr int kLdsStages = lds_stages(BM);
+  constexpr int kLdsXStage = BM * kPfRowBytes;       // X rows of one step
+  constexpr int kXC = BM / 64;                       // 1 KB X chunks a wave copies per step
+  constexpr int kLdsCopies = 4 + kXC;                // copies a wave issues per step
+  static_assert(kXC * 1024 * kPfWaves == kLdsXStage, "X stage split");
   __shared__ __attribute__((aligned(1024))) uint8_t s_w[kLdsStages * kLdsWStage];
   __shared__ __attribute__((aligned(1024))) uint8_t s_x[kLdsStages * kLdsXStage];
   __shared__ uint32_t s_ent[2][kPfMaxKT];
@@ -541,26 +544,26 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   }
   const uint32_t stride = SRC_ROWMAJOR ? 0u : (uint32_t)__builtin_amdgcn_readfirstlane((int)s_stride[r_src]);
 
-  // this wave's two 8-row chunks of each X stage: rows 8 (2w + u) + l/8, the
-  // lane fetching the source chunk whose swizzled position is l % 8; rows
-  // past M read row M - 1 (their outputs are never stored)
-  const uint16_t* xsrc[2];
+  // this wave's kXC 8-row chunks of each X stage: rows 8 (kXC w + u) + l/8,
+  // the lane fetching the source chunk whose swizzled position is l % 8;
+  // rows past M read row M - 1 (their outputs are never stored)
+  const uint16_t* xsrc[kXC];
 #pragma unroll
-  for (int u = 0; u < 2; u++) {
-    const int row = 8 * (2 * w + u) + (l >> 3);
+  for (int u = 0; u < kXC; u++) {
+    const int row = 8 * (kXC * w + u) + (l >> 3);
     const int gm = min(m0 + row, M - 1);
     xsrc[u] = P.X + (int64_t)gm * K + 8 * ((l & 7) ^ swz_f(row));
   }
   const uint32_t w_lds = lds_addr(s_w), x_lds = lds_addr(s_x);
 
-  // the six copies of step s into stage s % 3
+  // the copies of step s into stage s % kLdsStages
   auto issue = [&](int s) {
     const int st = s % kLdsStages;
     const int jl = s >> 1, h = s & 1, j = j0 + jl;
     const uint32_t wb = w_lds + (uint32_t)(st * kLdsWStage), xb = x_lds + (uint32_t)(st * kLdsXStage);
     const int col = j * kTile + 64 * h;
 #pragma unroll
-    for (int u = 0; u < 2; u++) dma16(xsrc[u] + col, xb + 1024u * (uint32_t)(2 * w + u));
+    for (int u = 0; u < kXC; u++) dma16(xsrc[u] + col, xb + 1024u * (uint32_t)(kXC * w + u));
     // fragment slot of band 4wn + b, half e of row-block r: ((r*8 + 4wn + b)*2 + e) KB
     const uint32_t slot0 = wb + 1024u * (uint32_t)((r * 8 + 4 * wn) * 2);
     if constexpr (SRC_ROWMAJOR) {
@@ -664,16 +667,19 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
     }
   };
 
-  // ---- pipeline: copies two steps ahead
-  issue(0);
-  issue(1);  // n_steps >= 2
+  // ---- pipeline: copies kLdsStages - 1 steps ahead
+  constexpr int kAhead = kLdsStages - 1;
+#pragma unroll
+  for (int s = 0; s < kAhead; s++) issue(s);  // n_steps >= 2 >= kAhead
   for (int s = 0; s < n_steps; s++) {
-    if (s + 1 < n_steps)
-      wait_copies<kLdsCopies>();  // this wave's copies of step s have landed
+    // this wave's copies of step s have landed (those of the kAhead - 1
+    // later steps may still be in flight)
+    if (kAhead == 2 && s + 1 < n_steps)
+      wait_copies<kLdsCopies>();
     else
       wait_copies<0>();
-    wg_barrier();  // everyone's have; everyone is done reading stage (s + 2) % 3
-    if (s + 2 < n_steps) issue(s + 2);
+    wg_barrier();  // everyone's have; everyone is done reading the stage step s + kAhead fills
+    if (s + kAhead < n_steps) issue(s + kAhead);
     compute(s);
   }
 
@@ -769,11 +775,11 @@ static PfShape choose_shape_uncached(int64_t M, int64_t N, int64_t K, int cus, i
 
 // The same, with the staging chosen, remembered for the last few shapes of
 // this thread (a GEMM call asks for it twice: the workspace query and the
-// launch).  LDS staging (k_prefill_lds) runs width 128: for packed W it
-// measured 3-9% faster than the register-staged kernel at that width, and
-// for row-major W (the dense baseline) about 40% faster, which also beats
-// the register-staged kernel at 192 and 256, so the dense baseline takes
-// width 128 whenever the model picks 128 or more.
+// launch).  From width 128 up the LDS-staged kernel (k_prefill_lds) runs: on
+// the LLaMA-2 7B/13B prefill shapes it measured as fast as or faster than
+// the register-staged kernel at every width -- 2-12% for packed W, 20-45%
+// for row-major W (the dense baseline) -- so the model's width is kept and
+// only the staging changes.
 static PfShape choose_shape(int64_t M, int64_t N, int64_t K, bool rowmajor) {
   struct Entry {
     int64_t M, N, K;
@@ -789,8 +795,8 @@ static PfShape choose_shape(int64_t M, int64_t N, int64_t K, bool rowmajor) {
     if (cache[i].M == M && cache[i].N == N && cache[i].K == K && cache[i].cus == cus && cache[i].rowmajor == rowmajor)
       return cache[i].sh;
   PfShape sh = choose_shape_uncached(M, N, K, cus);
-  if (rowmajor && sh.bm > 128) sh = choose_shape_uncached(M, N, K, cus, 128);
-  sh.lds = sh.bm == 128;
+  (void)rowmajor;
+  sh.lds = sh.bm >= 128;
   cache[next] = {M, N, K, cus, rowmajor, sh};
   next = (next + 1) % kSlots;
   if (filled < kSlots) filled++;
@@ -854,7 +860,7 @@ static hipError_t launch_prefill_bm(const void* src, const void* src2, const voi
     // fp32 partials of the K ranges, then the ordered reduction (fused:
     // SiLU(gate) * up) into Y
     if constexpr (LDS)
-      hipLaunchKernelGGL((k_prefill_lds<BF16, SRC_ROWMAJOR, true, FUSE>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((k_prefill_lds<BF16, SRC_ROWMAJOR, true, FUSE, BM>), grid, block, 0, s, a);
     else
       hipLaunchKernelGGL((k_prefill<BF16, SRC_ROWMAJOR, true, BM, DIST, FUSE>), grid, block, 0, s, a);
     if constexpr (FUSE) {
@@ -867,7 +873,7 @@ static hipError_t launch_prefill_bm(const void* src, const void* src2, const voi
                          part, sh.splits, mn, Y);
     }
   } else if constexpr (LDS) {
-    hipLaunchKernelGGL((k_prefill_lds<BF16, SRC_ROWMAJOR, OUT_F32, FUSE>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((k_prefill_lds<BF16, SRC_ROWMAJOR, OUT_F32, FUSE, BM>), grid, block, 0, s, a);
   } else {
     hipLaunchKernelGGL((k_prefill<BF16, SRC_ROWMAJOR, OUT_F32, BM, DIST, FUSE>), grid, block, 0, s, a);
   }
@@ -919,7 +925,14 @@ static hipError_t launch_prefill_t(const void* src, const void* src2, const void
   float* part = reinterpret_cast<float*>(ws);
 #define PATCH_BM(W, D, L) \
   launch_prefill_bm<BF16, SRC_ROWMAJOR, OUT_F32, FUSE, W, D, L>(src, src2, X, M, N, K, Y, sh, part, s)
-  if (sh.lds) return PATCH_BM(kLdsBM, 1, true);
+  if (sh.lds) {
+    switch (sh.bm) {
+      case 128: return PATCH_BM(128, 1, true);
+      case 192: return PATCH_BM(192, 1, true);
+      case 256: return PATCH_BM(256, 1, true);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (sh.bm) {
     case 64: return PATCH_BM(64, 2, false);
     case 128: return PATCH_BM(128, 2, false);
@@ -930,7 +943,7 @@ static hipError_t launch_prefill_t(const void* src, const void* src2, const void
 }
 
 // force_bm: 0 (the shape the cost model picks) or a width in {64, 128, 192,
-// 256}; force_lds: LDS staging (width 128 only).  src2 non-null: fused
+// 256}; force_lds: LDS staging (widths 128, 192, 256).  src2 non-null: fused
 // gate/up (src2 = the up matrix when rowmajor; for a packed blob the two are
 // interleaved in src and src2 is src); Y is then H, M x N/2.
 hipError_t launch_prefill(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* src2, const void* X,
@@ -938,7 +951,7 @@ hipError_t launch_prefill(bool bf16, bool rowmajor, bool out_f32, const void* sr
                           bool force_lds, hipStream_t s) {
   if (K / kTile > kPfMaxKT) return hipErrorInvalidValue;
   if (force_bm && force_bm != 64 && force_bm != 128 && force_bm != 192 && force_bm != 256) return hipErrorInvalidValue;
-  if (force_lds && force_bm != kLdsBM) return hipErrorInvalidValue;
+  if (force_lds && force_bm < 128) return hipErrorInvalidValue;
   const bool fuse = src2 != nullptr;
   if (fuse && (N % (2 * kTile))) return hipErrorInvalidValue;
 #define PATCH_PF(B, R, F, U) \

@@ -120,7 +120,8 @@ def test_swiglu_small_ragged(dtype, M):
         check_h(patch.dense_gemm_swiglu(X, Wg, Wu, variant=v), ref_d, dtype, what=f"dense {dtype} M={M} {v}")
 
 
-PREFILL_KERNELS = ["prefill_w64", "prefill_w128", "prefill_w192", "prefill_w256", "prefill_w128_lds"]
+PREFILL_KERNELS = ["prefill_w64", "prefill_w128", "prefill_w192", "prefill_w256", "prefill_w128_lds", "prefill_w192_lds",
+                   "prefill_w256_lds"]
 
 
 @pytest.mark.parametrize("variant", PREFILL_KERNELS)

@@ -214,7 +214,8 @@ def test_prefill_split_k(N, K, M):
     assert_close(a, ref, f32=True, what=f"auto M={M}")
 
 
-PREFILL_KERNELS = ["prefill_w64", "prefill_w128", "prefill_w192", "prefill_w256", "prefill_w128_lds"]
+PREFILL_KERNELS = ["prefill_w64", "prefill_w128", "prefill_w192", "prefill_w256", "prefill_w128_lds", "prefill_w192_lds",
+                   "prefill_w256_lds"]
 
 
 @pytest.mark.parametrize("variant", PREFILL_KERNELS)
