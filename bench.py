@@ -329,7 +329,7 @@ def ingest_counters(dirs):
                     key = "copy"
                 elif "k_decode<" in name:
                     key = "decode_dense" if name.split("<")[1].split(",")[1].strip() == "true" else "decode"
-                elif "k_prefill<" in name:
+                elif "k_prefill<" in name or "k_prefill_lds<" in name:
                     key = "prefill_dense" if name.split("<")[1].split(",")[1].strip() == "true" else "prefill"
                 else:
                     continue

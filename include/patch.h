@@ -52,13 +52,14 @@ typedef enum { PATCH_F16 = 0, PATCH_BF16 = 1, PATCH_F32 = 2 } patch_dtype;
 
 /* GEMM variant selection for patch_gemm_ex (patch_gemm uses PATCH_VARIANT_AUTO). */
 typedef enum {
-  PATCH_VARIANT_AUTO = 0,    /* decode for M <= 16 (K <= 65536), prefill otherwise; for
-                                M <= 128 also decode when the workspace passed is smaller
-                                than the GEMM's workspace query asks for */
+  PATCH_VARIANT_AUTO = 0,    /* decode for M <= 16 (K <= 65536); for 16 < M <= 128 the
+                                kernel whose time model is lower (prefill's for the K
+                                split the workspace passed allows); prefill otherwise */
   PATCH_VARIANT_DECODE = 1,  /* W-streaming kernel; valid for 1 <= M <= 128, K <= 65536
                                 (else PATCH_ERR_INVALID_ARG / PATCH_ERR_UNSUPPORTED) */
-  PATCH_VARIANT_PREFILL = 2, /* output-tiled MFMA kernel; any M >= 1; splits K when the
-                                output blocks cannot fill the GPU and workspace allows */
+  PATCH_VARIANT_PREFILL = 2, /* output-tiled MFMA kernel, W and X staged through LDS;
+                                any M >= 1; splits K when the output blocks cannot fill
+                                the GPU and the workspace allows */
   /* The prefill kernel at one M-block width and staging (K split as its
    * cost model decides for that width, within the workspace passed): for
    * tests and measurements that must run every kernel on the same shapes. */
@@ -68,7 +69,8 @@ typedef enum {
   PATCH_VARIANT_PREFILL_W256 = 6,     /* registers, 256 */
   PATCH_VARIANT_PREFILL_W128_LDS = 7, /* W and X staged through LDS, 128 */
   PATCH_VARIANT_PREFILL_W192_LDS = 8, /* W and X staged through LDS, 192 */
-  PATCH_VARIANT_PREFILL_W256_LDS = 9  /* W and X staged through LDS, 256 */
+  PATCH_VARIANT_PREFILL_W256_LDS = 9, /* W and X staged through LDS, 256 */
+  PATCH_VARIANT_PREFILL_W64_LDS = 10  /* W and X staged through LDS, 64 */
 } patch_variant;
 
 /* Host-side mirror of the packed blob's header (format version 3). */

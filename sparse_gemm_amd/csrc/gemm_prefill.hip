@@ -434,30 +434,31 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
 }
 
 // ---------------------------------------------------------------------------
-// k_prefill_lds: the same output tiling at BM = 128 with W and X staged
-// through LDS by global -> LDS copies, three steps deep.
+// k_prefill_lds: the same output tiling with W and X staged through LDS by
+// global -> LDS copies, two or three steps deep.
 //
-//   * Per step every wave issues exactly six 1 KB copies (16 bytes a lane,
-//     straight into LDS, no registers): two 8-row chunks of the X stage and
-//     four W fragments -- wave (r, wn, wm) copies half wm of bands 4wn..4wn+3
-//     of row-block r (a 2:4 tile: the values if wm = 0, the band's codes if
-//     wm = 1), so each W byte enters the CU once, where the register-staged
-//     kernel loads every W fragment into both M-halves' waves.
-//   * Copies for step s+2 go out while step s computes; a wave waits for its
-//     own copies of step s with vmcnt (six newer copies may stay in flight)
-//     and the barrier after it publishes everyone's.  The copies are inline
-//     asm, so the compiler neither waits for them nor for anything else before
-//     LDS reads; the wait counts are exact because every wave issues the same
-//     six copies every step.
+//   * Per step every wave issues exactly 4 + BM/64 copies of 1 KB (16 bytes
+//     a lane, straight into LDS, no registers): BM/64 8-row chunks of the X
+//     stage and four W fragments -- wave (r, wn, wm) copies half wm of bands
+//     4wn..4wn+3 of row-block r (a 2:4 tile: the values if wm = 0, the
+//     band's codes if wm = 1), so each W byte enters the CU once, where the
+//     register-staged kernel loads every W fragment into both M-halves' waves.
+//   * Copies for the later steps go out while step s computes; a wave waits
+//     for its own copies of step s with vmcnt (the copies of the next step
+//     may stay in flight) and the barrier after it publishes everyone's.  The
+//     copies are inline asm, so the compiler neither waits for them nor for
+//     anything else before LDS reads; the wait counts are exact because every
+//     wave issues the same copies every step.
 //   * Fragments are then read from LDS with one 16-byte read a lane (the
 //     2:4 codes chunk holding the lane's word likewise) and fed to the same
 //     v_smfmac_f32_16x16x64 sequence as the register-staged kernel.
-// LDS: 3 x (32 KB of W + 16 KB of X) + the tile entries = 152 KB, one
-// workgroup per CU.
+// LDS per stage: 32 KB of W + BM * 128 bytes of X; three stages up to width
+// 128 (120 KB at 64, 144 KB at 128), two at 192 and 256 (112 and 128 KB),
+// plus the tile entries: one workgroup per CU.
 // ---------------------------------------------------------------------------
 constexpr int kLdsWStage = 32768;  // 2 row-blocks x 8 bands x 2 fragments of 1 KB
-// stages of the LDS ring for an M-block width: three at 128 (2 x 48 KB in
-// flight), two at 192 and 256 (a third would not fit the 160 KB of LDS)
+// stages of the LDS ring for an M-block width: three up to 128, two at 192
+// and 256 (a third would not fit the 160 KB of LDS)
 constexpr int lds_stages(int bm) { return bm <= 128 ? 3 : 2; }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
@@ -608,7 +609,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
     }
   };
 
-  // step s from stage s % 3: this wave's A fragments from LDS, then the
+  // step s from stage s % kLdsStages: this wave's A fragments from LDS, then the
   // matrix instructions (as in k_prefill)
   auto compute = [&](int s) {
     const int st = s % kLdsStages;
@@ -721,12 +722,12 @@ static int cu_count() {
 }
 
 // Launch shape: the M-block width BM and the number of K ranges, chosen
-// by a cost model of this kernel fitted to its measured times on the
-// LLaMA-2 7B q_proj, gate_proj and down_proj shapes (64 <= M <= 512, every
-// width, 1 to 12 ranges; 4% rms error, and its pick is within 2% of the
-// fastest measured choice on each shape):
-//   t = rounds * (3.0 + tiles * (0.93 + 0.0082 * BM)) us
-//       + with a split: 6.8 us + partial bytes / 3.5 TB/s (second kernel),
+// by a cost model of the LDS-staged kernel fitted to its measured times on
+// the LLaMA-2 7B q_proj, gate_proj and down_proj shapes (32 <= M <= 2048,
+// every width, 1 to 12 ranges; 4% rms error; its pick is the fastest
+// measured choice on 26 of the 30 shapes and 1% slower on average):
+//   t = rounds * (1.9 + tiles * (1.0 + 0.0069 * BM)) us
+//       + with a split: 6.4 us + partial bytes / 3.25 TB/s (second kernel),
 // rounds = ceil(workgroups / CUs), tiles = tile columns per K range.  A K
 // range holds at least two tile columns, and the partial sums (ranges * M *
 // N * 4 bytes) stay within 2 * N * K bytes.  Then the number of M-groups:
@@ -738,14 +739,14 @@ static int cu_count() {
 // least two M-blocks.
 struct PfShape {
   int bm, groups, splits, kt_split;
-  bool lds;  // BM = 128 with W and X staged through LDS (k_prefill_lds)
+  bool lds;  // W and X staged through LDS (k_prefill_lds), else through registers (k_prefill)
 };
 static double shape_cost_us(int64_t M, int64_t N, int64_t K, int bm, int64_t splits, int64_t kt_split, int cus) {
   const int64_t pairs = (N / kTile + 1) / 2;
   const int64_t blocks = pairs * ((M + bm - 1) / bm) * splits;
   const int64_t rounds = (blocks + cus - 1) / cus;
-  double t = (double)rounds * (3.0 + (double)kt_split * (0.93 + 0.0082 * bm));
-  if (splits > 1) t += 6.8 + (double)splits * (double)M * (double)N * 4.0 / 3.5e6;
+  double t = (double)rounds * (1.9 + (double)kt_split * (1.0 + 0.0069 * bm));
+  if (splits > 1) t += 6.4 + (double)splits * (double)M * (double)N * 4.0 / 3.25e6;
   return t;
 }
 // only_bm: consider that width alone (0: every width).
@@ -773,13 +774,12 @@ static PfShape choose_shape_uncached(int64_t M, int64_t N, int64_t K, int cus, i
   return best;
 }
 
-// The same, with the staging chosen, remembered for the last few shapes of
-// this thread (a GEMM call asks for it twice: the workspace query and the
-// launch).  From width 128 up the LDS-staged kernel (k_prefill_lds) runs: on
-// the LLaMA-2 7B/13B prefill shapes it measured as fast as or faster than
-// the register-staged kernel at every width -- 2-12% for packed W, 20-45%
-// for row-major W (the dense baseline) -- so the model's width is kept and
-// only the staging changes.
+// The same, remembered for the last few shapes of this thread (a GEMM call
+// asks for it twice: the workspace query and the launch).  The LDS-staged
+// kernel (k_prefill_lds) runs at every width: on the LLaMA-2 7B/13B prefill
+// shapes it measured as fast as or faster than the register-staged kernel
+// at each width -- 5-10% at width 64, 2-12% from 128 up for packed W, 20-45%
+// for row-major W (the dense baseline).
 static PfShape choose_shape(int64_t M, int64_t N, int64_t K, bool rowmajor) {
   struct Entry {
     int64_t M, N, K;
@@ -796,7 +796,7 @@ static PfShape choose_shape(int64_t M, int64_t N, int64_t K, bool rowmajor) {
       return cache[i].sh;
   PfShape sh = choose_shape_uncached(M, N, K, cus);
   (void)rowmajor;
-  sh.lds = sh.bm >= 128;
+  sh.lds = true;
   cache[next] = {M, N, K, cus, rowmajor, sh};
   next = (next + 1) % kSlots;
   if (filled < kSlots) filled++;
@@ -927,6 +927,7 @@ static hipError_t launch_prefill_t(const void* src, const void* src2, const void
   launch_prefill_bm<BF16, SRC_ROWMAJOR, OUT_F32, FUSE, W, D, L>(src, src2, X, M, N, K, Y, sh, part, s)
   if (sh.lds) {
     switch (sh.bm) {
+      case 64: return PATCH_BM(64, 1, true);
       case 128: return PATCH_BM(128, 1, true);
       case 192: return PATCH_BM(192, 1, true);
       case 256: return PATCH_BM(256, 1, true);
@@ -943,7 +944,7 @@ static hipError_t launch_prefill_t(const void* src, const void* src2, const void
 }
 
 // force_bm: 0 (the shape the cost model picks) or a width in {64, 128, 192,
-// 256}; force_lds: LDS staging (widths 128, 192, 256).  src2 non-null: fused
+// 256}; force_lds: LDS staging (any of those widths).  src2 non-null: fused
 // gate/up (src2 = the up matrix when rowmajor; for a packed blob the two are
 // interleaved in src and src2 is src); Y is then H, M x N/2.
 hipError_t launch_prefill(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* src2, const void* X,
@@ -951,7 +952,7 @@ hipError_t launch_prefill(bool bf16, bool rowmajor, bool out_f32, const void* sr
                           bool force_lds, hipStream_t s) {
   if (K / kTile > kPfMaxKT) return hipErrorInvalidValue;
   if (force_bm && force_bm != 64 && force_bm != 128 && force_bm != 192 && force_bm != 256) return hipErrorInvalidValue;
-  if (force_lds && force_bm < 128) return hipErrorInvalidValue;
+  if (force_lds && force_bm < 64) return hipErrorInvalidValue;
   const bool fuse = src2 != nullptr;
   if (fuse && (N % (2 * kTile))) return hipErrorInvalidValue;
 #define PATCH_PF(B, R, F, U) \

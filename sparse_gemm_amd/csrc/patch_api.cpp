@@ -367,7 +367,7 @@ static patch_status gemm_common(bool rowmajor, patch_dtype dt, int64_t M, int64_
   patch_status s;
   if ((s = check_ydtype(dt, y_dtype))) return s;
   if (M < 0 || M > (int64_t)0x7fffffff) return fail(PATCH_ERR_INVALID_ARG, "M=%lld out of range", (long long)M);
-  if (variant < PATCH_VARIANT_AUTO || variant > PATCH_VARIANT_PREFILL_W256_LDS)
+  if (variant < PATCH_VARIANT_AUTO || variant > PATCH_VARIANT_PREFILL_W64_LDS)
     return fail(PATCH_ERR_INVALID_ARG, "unknown variant %d", (int)variant);
   if (variant == PATCH_VARIANT_DECODE && M > kDecodeMaxM)
     return fail(PATCH_ERR_INVALID_ARG, "decode variant needs M <= %lld (M=%lld)", (long long)kDecodeMaxM, (long long)M);
@@ -394,7 +394,7 @@ static patch_status gemm_common(bool rowmajor, patch_dtype dt, int64_t M, int64_
                                       patch::prefill_estimate_us(M, N, K, rowmajor, ws ? ws_bytes : 0);
   const bool bf16 = dt == PATCH_BF16, f32out = y_dtype == PATCH_F32;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  static const int kForceBm[10] = {0, 0, 0, 64, 128, 192, 256, 128, 192, 256};
+  static const int kForceBm[11] = {0, 0, 0, 64, 128, 192, 256, 128, 192, 256, 64};
   hipError_t e = decode ? patch::launch_decode(bf16, rowmajor, f32out, src, src2, X_dev, M, N, K, Y_dev, st)
                         : patch::launch_prefill(bf16, rowmajor, f32out, src, src2, X_dev, M, N, K, Y_dev, ws,
                                                 ws_bytes, kForceBm[variant], variant >= PATCH_VARIANT_PREFILL_W128_LDS,

@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libpatch.so")
 
 PATCH_F16, PATCH_BF16, PATCH_F32 = 0, 1, 2
 VARIANTS = {"auto": 0, "decode": 1, "prefill": 2, "prefill_w64": 3, "prefill_w128": 4, "prefill_w192": 5,
-            "prefill_w256": 6, "prefill_w128_lds": 7, "prefill_w192_lds": 8, "prefill_w256_lds": 9}
+            "prefill_w256": 6, "prefill_w128_lds": 7, "prefill_w192_lds": 8, "prefill_w256_lds": 9,
+            "prefill_w64_lds": 10}
 STATUS = {0: "PATCH_OK", 1: "PATCH_ERR_INVALID_ARG", 2: "PATCH_ERR_SHAPE", 3: "PATCH_ERR_MASK",
           4: "PATCH_ERR_BUFFER_TOO_SMALL", 5: "PATCH_ERR_UNSUPPORTED", 6: "PATCH_ERR_HIP"}
 

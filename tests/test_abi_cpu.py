@@ -78,7 +78,7 @@ def test_bad_arguments_rejected_before_launch():
         "PATCH_ERR_INVALID_ARG"
     assert patch.STATUS[lib.patch_dense_gemm_ex(1, 129, 256, 256, V(16), V(16), V(16), 1, None, 0, 1, None)] == \
         "PATCH_ERR_INVALID_ARG"
-    for bad_variant in (10, 11, -1):
+    for bad_variant in (11, 12, -1):
         assert patch.STATUS[lib.patch_dense_gemm_ex(1, 4, 256, 256, V(16), V(16), V(16), 1, None, 0, bad_variant,
                                                     None)] == "PATCH_ERR_INVALID_ARG"
     # a workspace size without a workspace, or an unaligned one

@@ -215,7 +215,7 @@ def test_prefill_split_k(N, K, M):
 
 
 PREFILL_KERNELS = ["prefill_w64", "prefill_w128", "prefill_w192", "prefill_w256", "prefill_w128_lds", "prefill_w192_lds",
-                   "prefill_w256_lds"]
+                   "prefill_w256_lds", "prefill_w64_lds"]
 
 
 @pytest.mark.parametrize("variant", PREFILL_KERNELS)
