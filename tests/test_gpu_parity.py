@@ -220,8 +220,8 @@ PREFILL_KERNELS = ["prefill_w64", "prefill_w128", "prefill_w192", "prefill_w256"
 
 @pytest.mark.parametrize("variant", PREFILL_KERNELS)
 def test_prefill_every_kernel(variant):
-    """Every prefill kernel (M-block width 64/128/192/256 with registers,
-    128 staged through LDS) on the same shape: 640 x 1152 (a lone middle
+    """Every prefill kernel (M-block width 64/128/192/256, W and X staged
+    through registers or through LDS) on the same shape: 640 x 1152 (a lone middle
     row-block, 9 tile columns so K ranges come out uneven), M from below one
     block to several, with a workspace of 2 N K bytes (K split as that
     width's model decides) and with none; packed and dense baseline; every
