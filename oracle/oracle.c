@@ -436,3 +436,99 @@ int oracle_pack(int dtype, int64_t N, int64_t K, const uint16_t* W, const uint8_
   }
   return ORACLE_OK;
 }
+
+/* ---------------------------------------------------------------------------
+ * Forward hybrid-mask sampler (gist.science explainer, section 2 "Methodology:
+ * PATCH", "Learnable Distributions"): a learnable two-way distribution per
+ * tile decides dense vs 2:4, sampled with Gumbel-Softmax; inside 2:4 tiles a
+ * second learnable distribution picks one of the six 2:4 patterns per group
+ * of four; the final mask combines the dense option and the 2:4 option with
+ * the tile's weights.
+ *
+ * Definitions used (standard, not on the pages): a Gumbel(0, 1) sample from
+ * a uniform u in (0, 1) is g = -ln(-ln u); the Gumbel-Softmax sample of
+ * logits l_i at temperature tau is y_i = exp((l_i + g_i) / tau) /
+ * sum_j exp((l_j + g_j) / tau), and its hard (straight-through forward)
+ * value is the one-hot of argmax_i (l_i + g_i).
+ *
+ * Readings (not on the pages): the tile classes are (0 dense, 1 sparse); the
+ * six patterns are the kept position pairs in lexicographic order (0,1),
+ * (0,2), (0,3), (1,2), (1,3), (2,3); the soft mask of a weight at position
+ * j of its group in tile t is y_dense(t) + y_sparse(t) * sum over patterns p
+ * holding j of y_p(group); the hard outputs are the tile map (1 where the
+ * sparse class wins) and, in every group (the pack reads it only inside 2:4
+ * tiles), the kept pair of the winning pattern.  The uniforms are inputs (the
+ * caller draws them).  Hard decisions are taken on float32 scores
+ * l + (-logf(-logf(u))), the first index winning a tie -- the precision the
+ * GPU sampler decides in; the soft values are computed in binary64.
+ * ------------------------------------------------------------------------- */
+static const int kPatternPairs[6][2] = {{0, 1}, {0, 2}, {0, 3}, {1, 2}, {1, 3}, {2, 3}};
+
+double oracle_gumbel_f64(double u) { return -log(-log(u)); }
+float oracle_gumbel_f32(float u) { return -logf(-logf(u)); }
+
+/* Gumbel-Softmax over n (1..8) classes: y[0..n) soft (binary64); returns the
+ * hard argmax (float32 scores). */
+int oracle_gumbel_softmax(int n, const float* logit, const float* u, double tau, double* y) {
+  if (n < 1 || n > 8 || !(tau > 0.0)) return -1;
+  int best = 0;
+  float best_s = logit[0] + oracle_gumbel_f32(u[0]);
+  for (int i = 1; i < n; i++) {
+    const float s = logit[i] + oracle_gumbel_f32(u[i]);
+    if (s > best_s) {
+      best_s = s;
+      best = i;
+    }
+  }
+  if (y) {
+    double z[8], zmax = -INFINITY, sum = 0.0;
+    for (int i = 0; i < n; i++) {
+      z[i] = ((double)logit[i] + oracle_gumbel_f64((double)u[i])) / tau;
+      if (z[i] > zmax) zmax = z[i];
+    }
+    for (int i = 0; i < n; i++) {
+      z[i] = exp(z[i] - zmax);
+      sum += z[i];
+    }
+    for (int i = 0; i < n; i++) y[i] = z[i] / sum;
+  }
+  return best;
+}
+
+/* The hybrid mask of an N x K weight with tiles of tn x tk (tk % 4 == 0):
+ *   tile_logits, tile_u: [N/tn][K/tk][2] (class 0 dense, 1 sparse);
+ *   pat_logits, pat_u:   [N][K/4][6] (the six patterns above);
+ * outputs tile_map [N/tn][K/tk] (1 = sparse), mask [N][K] (1 = keep, the
+ * winning pattern of every group), soft [N][K] (binary64; may be NULL). */
+int oracle_sample_mask(int64_t N, int64_t K, int64_t tn, int64_t tk, const float* tile_logits, const float* tile_u,
+                       const float* pat_logits, const float* pat_u, double tau, uint8_t* tile_map, uint8_t* mask,
+                       double* soft) {
+  if (N < 0 || K < 0 || tn <= 0 || tk <= 0 || tk % 4 || N % tn || K % tk || !(tau > 0.0)) return ORACLE_ERR_SHAPE;
+  const int64_t KT = K / tk, G = K / 4;
+  for (int64_t i = 0; i < N / tn; i++)
+    for (int64_t j = 0; j < KT; j++) {
+      const int64_t t = i * KT + j;
+      tile_map[t] = (uint8_t)oracle_gumbel_softmax(2, tile_logits + 2 * t, tile_u + 2 * t, tau, NULL);
+    }
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; n++) {
+    for (int64_t g = 0; g < G; g++) {
+      double yp[6], yt[2];
+      const int64_t o = (n * G + g) * 6;
+      const int p = oracle_gumbel_softmax(6, pat_logits + o, pat_u + o, tau, yp);
+      for (int j = 0; j < 4; j++)
+        mask[n * K + 4 * g + j] = (uint8_t)(j == kPatternPairs[p][0] || j == kPatternPairs[p][1]);
+      if (soft) {
+        const int64_t t = (n / tn) * KT + (4 * g) / tk;
+        oracle_gumbel_softmax(2, tile_logits + 2 * t, tile_u + 2 * t, tau, yt);
+        for (int j = 0; j < 4; j++) {
+          double q = 0.0;
+          for (int c = 0; c < 6; c++)
+            if (j == kPatternPairs[c][0] || j == kPatternPairs[c][1]) q += yp[c];
+          soft[n * K + 4 * g + j] = yt[0] + yt[1] * q;
+        }
+      }
+    }
+  }
+  return ORACLE_OK;
+}

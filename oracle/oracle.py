@@ -67,6 +67,14 @@ def load():
     lib.oracle_silu.restype = ctypes.c_double
     lib.oracle_swiglu_f64.argtypes = [ctypes.c_int, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P]
     lib.oracle_swiglu_f64.restype = ctypes.c_int
+    lib.oracle_gumbel_f64.argtypes = [ctypes.c_double]
+    lib.oracle_gumbel_f64.restype = ctypes.c_double
+    lib.oracle_gumbel_f32.argtypes = [ctypes.c_float]
+    lib.oracle_gumbel_f32.restype = ctypes.c_float
+    lib.oracle_gumbel_softmax.argtypes = [ctypes.c_int, P, P, ctypes.c_double, P]
+    lib.oracle_gumbel_softmax.restype = ctypes.c_int
+    lib.oracle_sample_mask.argtypes = [I64, I64, I64, I64, P, P, P, P, ctypes.c_double, P, P, P]
+    lib.oracle_sample_mask.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -198,3 +206,50 @@ def interleave_gate_up(A_g: np.ndarray, A_u: np.ndarray, rows_per_block: int) ->
     g = A_g.reshape(nb, rows_per_block, *A_g.shape[1:])
     u = A_u.reshape(nb, rows_per_block, *A_u.shape[1:])
     return np.stack([g, u], axis=1).reshape(2 * A_g.shape[0], *A_g.shape[1:])
+
+
+# ---------------------------------------------------------------------------- hybrid-mask sampler
+# Forward Gumbel-Softmax sampler (gist.science explainer, section 2
+# "Methodology: PATCH", "Learnable Distributions"); definitions and readings
+# are restated in oracle.c next to oracle_sample_mask.
+PATTERN_PAIRS = ((0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3))
+
+
+def _f32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def gumbel(u: float) -> float:
+    """-ln(-ln u) in binary64."""
+    return load().oracle_gumbel_f64(float(u))
+
+
+def gumbel_softmax(logits, u, tau: float):
+    """(soft probabilities in binary64, hard argmax on float32 scores)."""
+    logits, u = _f32(logits), _f32(u)
+    y = np.zeros(logits.size, dtype=np.float64)
+    best = load().oracle_gumbel_softmax(int(logits.size), _p(logits), _p(u), float(tau), _p(y))
+    if best < 0:
+        raise OracleError(1)
+    return y, best
+
+
+def sample_mask(tile_logits, tile_u, pat_logits, pat_u, tau: float, tile_n: int = 128, tile_k: int = 128,
+                soft: bool = True):
+    """tile_logits, tile_u: [N/tn, K/tk, 2]; pat_logits, pat_u: [N, K/4, 6].
+    Returns (tile_map uint8 [N/tn, K/tk], mask uint8 [N, K], soft float64
+    [N, K] or None)."""
+    pat_logits, pat_u = _f32(pat_logits), _f32(pat_u)
+    tile_logits, tile_u = _f32(tile_logits), _f32(tile_u)
+    N, G = pat_logits.shape[0], pat_logits.shape[1]
+    K = 4 * G
+    assert pat_logits.shape == (N, G, 6) and pat_u.shape == pat_logits.shape
+    assert tile_logits.shape == (N // tile_n, K // tile_k, 2) and tile_u.shape == tile_logits.shape
+    tmap = np.zeros((N // tile_n, K // tile_k), dtype=np.uint8)
+    mask = np.zeros((N, K), dtype=np.uint8)
+    out = np.zeros((N, K), dtype=np.float64) if soft else None
+    rc = load().oracle_sample_mask(N, K, tile_n, tile_k, _p(tile_logits), _p(tile_u), _p(pat_logits), _p(pat_u),
+                                   float(tau), _p(tmap), _p(mask), _p(out) if soft else None)
+    if rc:
+        raise OracleError(rc)
+    return tmap, mask, out

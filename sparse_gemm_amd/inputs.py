@@ -212,3 +212,39 @@ def make_custom(dtype: str, N: int, K: int, seed: int, map_kind: str, fraction: 
 
 def make_custom_x(dtype: str, M: int, K: int, seed: int, key: int = 99) -> np.ndarray:
     return gen_x(rng_for(seed, key, M, K, ROLE_X), M, K, dtype)
+
+
+# ---------------------------------------------------------------------------- sampler inputs
+ROLE_SAMPLER = 7
+
+
+def gen_uniform_open(rng: np.random.Generator, shape) -> np.ndarray:
+    """float32 uniforms in the open interval (0, 1): k / 2^24, k in [1, 2^24)
+    (every value exactly representable, never 0 or 1)."""
+    return (rng.integers(1, 1 << 24, size=shape, dtype=np.int64).astype(np.float64) / float(1 << 24)).astype(
+        np.float32)
+
+
+@dataclasses.dataclass
+class SamplerInputs:
+    """Logits and uniforms of the forward hybrid-mask sampler for an N x K
+    weight: tile logits / uniforms [N/tn, K/tk, 2] (class 0 dense, 1 sparse),
+    pattern logits / uniforms [N, K/4, 6]; float32."""
+    tile_logits: np.ndarray
+    tile_u: np.ndarray
+    pat_logits: np.ndarray
+    pat_u: np.ndarray
+
+
+def make_sampler_inputs(N: int, K: int, seed: int, tile_n: int = 128, tile_k: int = 128, sparse_bias: float = 0.0,
+                        pattern_scale: float = 1.0) -> SamplerInputs:
+    """Synthetic learnable distributions: logits ~ N(0, 1) (the sparse class
+    shifted by sparse_bias; pattern logits scaled by pattern_scale), and the
+    sampler's uniforms."""
+    rng = rng_for(seed, 40, N, K, ROLE_SAMPLER)
+    NT, KT, G = N // tile_n, K // tile_k, K // 4
+    tl = rng.standard_normal((NT, KT, 2))
+    tl[:, :, 1] += sparse_bias
+    pl = pattern_scale * rng.standard_normal((N, G, 6))
+    return SamplerInputs(tl.astype(np.float32), gen_uniform_open(rng, (NT, KT, 2)), pl.astype(np.float32),
+                         gen_uniform_open(rng, (N, G, 6)))

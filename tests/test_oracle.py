@@ -443,3 +443,132 @@ def test_interleave_gate_up_rows():
         assert np.array_equal(out[4 * i + 2:4 * i + 4], u[2 * i:2 * i + 2])
     tm = oracle.interleave_gate_up(np.array([[1, 0]], np.uint8), np.array([[0, 1]], np.uint8), 1)
     assert np.array_equal(tm, np.array([[1, 0], [0, 1]], np.uint8))
+
+
+# ---------------------------------------------------------------- hybrid-mask sampler (Gumbel-Softmax forward)
+# gist.science explainer, section 2 "Methodology: PATCH", "Learnable
+# Distributions": tile selection (dense vs 2:4) and pattern selection (one of
+# six) are learnable distributions sampled with Gumbel-Softmax.
+def test_gumbel_transform_is_the_gumbel_inverse_cdf():
+    """g(u) = -ln(-ln u) is the standard Gumbel quantile function: it matches
+    scipy.stats.gumbel_r.ppf (library routine) and inverts the textbook CDF
+    F(g) = exp(-exp(-g)); g(1/e) = 0 and g(exp(-exp(-2))) = 2."""
+    from scipy import stats
+
+    us = np.concatenate([np.linspace(1e-6, 1 - 1e-6, 97), [2.0 ** -24, 0.5, 1 - 2.0 ** -24]])
+    got = np.array([oracle.gumbel(u) for u in us])
+    np.testing.assert_allclose(got, stats.gumbel_r.ppf(us), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(np.exp(-np.exp(-got)), us, rtol=1e-12)
+    assert abs(oracle.gumbel(math.exp(-1.0))) < 1e-15
+    assert abs(oracle.gumbel(math.exp(-math.exp(-2.0))) - 2.0) < 1e-14
+
+
+@pytest.mark.parametrize("tau", [0.1, 0.5, 1.0, 2.0])
+def test_gumbel_softmax_is_softmax_of_perturbed_logits(tau):
+    """The soft sample equals scipy.special.softmax((l + g) / tau) with g the
+    library's Gumbel quantiles of the same uniforms (library routines), and
+    with u = 1/e (g = 0 up to float32 rounding of u) it is softmax(l / tau)."""
+    from scipy import special, stats
+
+    rng = np.random.default_rng(5)
+    for n in (2, 6):
+        l = rng.standard_normal(n).astype(np.float32)
+        u = inputs.gen_uniform_open(rng, n)
+        y, best = oracle.gumbel_softmax(l, u, tau)
+        g = stats.gumbel_r.ppf(u.astype(np.float64))
+        np.testing.assert_allclose(y, special.softmax((l.astype(np.float64) + g) / tau), rtol=1e-12, atol=1e-15)
+        assert best == int(np.argmax(l.astype(np.float64) + g))
+        y0, _ = oracle.gumbel_softmax(l, np.full(n, math.exp(-1.0), np.float32), tau)
+        np.testing.assert_allclose(y0, special.softmax(l.astype(np.float64) / tau), rtol=2e-6, atol=1e-9)
+
+
+def test_gumbel_max_frequencies_follow_softmax():
+    """Gumbel-max trick: the hard sample argmax(l + g) is distributed as
+    softmax(l).  Over ~303k groups with one set of six pattern logits and
+    ~76k tiles of 4 x 4 with one pair of tile logits, each class frequency is
+    within 5 binomial standard deviations of softmax(l) -- a wrong sign or
+    form of the Gumbel transform moves them by far more."""
+    from scipy import special
+
+    N, K, tn, tk = 128, 9472, 4, 4
+    G = K // 4
+    rng = np.random.default_rng(7)
+    lp = np.array([0.3, -1.0, 2.0, 0.5, 0.0, -0.2], dtype=np.float32)
+    lt = np.array([0.7, -0.4], dtype=np.float32)
+    pl = np.broadcast_to(lp, (N, G, 6))
+    tl = np.broadcast_to(lt, (N // tn, K // tk, 2))
+    tmap, mask, _ = oracle.sample_mask(tl, inputs.gen_uniform_open(rng, tl.shape), pl,
+                                       inputs.gen_uniform_open(rng, pl.shape), 1.0, tn, tk, soft=False)
+    groups = mask.reshape(N, G, 4)
+    counts = np.zeros(6)
+    for p, (a, b) in enumerate(oracle.PATTERN_PAIRS):
+        counts[p] = np.count_nonzero(groups[:, :, a] & groups[:, :, b])
+    assert counts.sum() == N * G
+    for freq, prob, n in ((counts / (N * G), special.softmax(lp.astype(np.float64)), N * G),
+                          (np.bincount(tmap.ravel(), minlength=2) / tmap.size,
+                           special.softmax(lt.astype(np.float64)), tmap.size)):
+        sd = np.sqrt(prob * (1 - prob) / n)
+        assert np.all(np.abs(freq - prob) < 5 * sd), (freq, prob)
+
+
+def test_soft_mask_invariants_and_hard_mask_validity():
+    """Soft mask: values in [0, 1]; in a group the four values sum to
+    4 y_dense + 2 y_sparse = 2 + 2 y_dense, so the sum is the same in every
+    group of a tile; no value is below y_dense.  Hard outputs: every group keeps
+    exactly two positions, so the sampled map and mask pass the pack's
+    validation and have sparsity 0.5 x (fraction of 2:4 tiles)."""
+    N, K = 256, 384
+    s = inputs.make_sampler_inputs(N, K, 3)
+    tmap, mask, soft = oracle.sample_mask(s.tile_logits, s.tile_u, s.pat_logits, s.pat_u, 0.7)
+    assert soft.min() >= 0.0 and soft.max() <= 1.0 + 1e-15
+    sums = soft.reshape(N, K // 4, 4).sum(axis=2)
+    for i in range(N // 128):
+        for j in range(K // 128):
+            blk = sums[128 * i:128 * (i + 1), 32 * j:32 * (j + 1)]
+            y_dense = blk.mean() / 2 - 1
+            np.testing.assert_allclose(blk, blk.mean(), rtol=0, atol=1e-12)
+            assert soft[128 * i:128 * (i + 1), 128 * j:128 * (j + 1)].min() >= y_dense - 1e-12
+    assert np.all(mask.reshape(N, K // 4, 4).sum(axis=2) == 2)
+    oracle.validate(N, K, tmap, mask)
+    E = oracle.effective_mask(N, K, tmap, mask)
+    assert (E == 0).sum() * tmap.size * 2 == N * K * int(tmap.sum())
+
+
+@pytest.mark.parametrize("p", range(6))
+def test_degenerate_distributions_give_the_pure_options(p):
+    """A tile whose dense logit dominates has soft mask 1 and map byte 0; one
+    whose sparse logit and pattern-p logit dominate has map byte 1 and soft
+    mask = hard mask = the indicator of pattern p's pair (lexicographic order
+    of the six pairs)."""
+    N, K = 128, 256
+    rng = np.random.default_rng(11 + p)
+    tl = np.zeros((1, 2, 2), np.float32)
+    tl[0, 0] = (60.0, 0.0)
+    tl[0, 1] = (0.0, 60.0)
+    pl = np.zeros((N, K // 4, 6), np.float32)
+    pl[:, :, p] = 60.0
+    tmap, mask, soft = oracle.sample_mask(tl, inputs.gen_uniform_open(rng, tl.shape), pl,
+                                          inputs.gen_uniform_open(rng, pl.shape), 1.0)
+    assert tmap.tolist() == [[0, 1]]
+    pair = np.zeros(4)
+    pair[list(oracle.PATTERN_PAIRS[p])] = 1
+    assert oracle.PATTERN_PAIRS[p] == tuple(int(v) for v in inputs.PATTERNS[p])
+    np.testing.assert_allclose(soft[:, :128], 1.0, atol=1e-12)
+    np.testing.assert_allclose(soft[:, 128:], np.tile(pair, (N, 32)), atol=1e-12)
+    assert np.array_equal(mask, np.tile(pair, (N, K // 4)).astype(np.uint8))
+
+
+def test_temperature_limits():
+    """tau -> 0: the soft sample tends to the one-hot hard sample; tau -> inf:
+    to the uniform distribution."""
+    rng = np.random.default_rng(13)
+    for n in (2, 6):
+        for _ in range(20):
+            l = rng.standard_normal(n).astype(np.float32)
+            u = inputs.gen_uniform_open(rng, n)
+            y, best = oracle.gumbel_softmax(l, u, 1e-4)
+            scores = np.sort(l.astype(np.float64) + np.array([oracle.gumbel(v) for v in u]))
+            if scores[-1] - scores[-2] > 0.01:
+                assert y[best] > 1 - 1e-12
+            y, _ = oracle.gumbel_softmax(l, u, 1e7)
+            np.testing.assert_allclose(y, 1.0 / n, atol=1e-5)
