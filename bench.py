@@ -392,8 +392,9 @@ def main():
     ap.add_argument("--report", default=None, help="also write the full sweep as JSON lines to this path")
     ap.add_argument("--report-steps", type=int, default=100, help="launches per timed batch in the report")
     ap.add_argument("--report-batches", type=int, default=10, help="timed batches per point in the report (median)")
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill_mlp", "imbalanced_13b"],
-                    help="decode (default: the q_proj decode GEMM) or a prefill workload, for profiling")
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill_mlp", "imbalanced_13b", "sampler"],
+                    help="decode (default: the q_proj decode GEMM), a prefill workload or the mask sampler, "
+                         "for profiling")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for rocprofv3 byte counters)")
     ap.add_argument("--ingest-counters", nargs="+", metavar="DIR", default=None,
@@ -424,6 +425,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration_copy_bytes": src.numel(), "copies": 3}), file=sys.stderr, flush=True)
         del src, dst
+    if args.workload == "sampler":
+        for rec in sampler_set(args.steps, args.warmup, 1):
+            print(json.dumps(rec), flush=True)
+        return
     if args.workload != "decode":
         run_prefill_workload(args)
         return
@@ -509,6 +514,39 @@ def run_prefill_workload(args):
                                   traffic_counters_bytes=traffic_for("prefill", M) if args.workload == "prefill_mlp"
                                   else None, **summ[M])),
                   flush=True)
+
+
+def sampler_set(steps, warmup, batches):
+    """The forward hybrid-mask sampler (patch_sample_mask) on the LLaMA-2-7B
+    q_proj and gate_proj shapes, with and without the soft mask: graph
+    replays of `steps` launches.  Inputs (float32 logits and uniforms, ~6 +
+    6 bytes per weight) exceed the Infinity Cache on gate_proj and nearly on
+    q_proj; HBM roofline on the algorithmic bytes: logits + uniforms read,
+    tile map + mask (+ soft mask) written."""
+    import torch
+
+    from sparse_gemm_amd import inputs, patch
+
+    out = []
+    for name, N, K in (("q_proj", 4096, 4096), ("gate_proj", 11008, 4096)):
+        s = inputs.make_sampler_inputs(N, K, 0, sparse_bias=0.4)
+        dev = [torch.from_numpy(a).cuda() for a in (s.tile_logits, s.tile_u, s.pat_logits, s.pat_u)]
+        bufs = (torch.empty((N // 128, K // 128), dtype=torch.uint8, device="cuda"),
+                torch.empty((N, K), dtype=torch.uint8, device="cuda"),
+                torch.empty((N, K), dtype=torch.float32, device="cuda"))
+        T = (N // 128) * (K // 128)
+        for soft in (True, False):
+            fn = (lambda k, soft=soft: patch.sample_mask(*dev, 0.5, soft=soft, out=bufs))
+            _, per = time_graphs([("s", fn)], steps, warmup, batches)
+            us = median(per["s"]) * 1e3
+            nbytes = N * (K // 4) * 6 * 4 * 2 + T * 2 * 4 * 2 + T + N * K + (4 * N * K if soft else 0)
+            gbps = nbytes / (us * 1e-6) / 1e9
+            out.append(dict(config="sampler", matrix=name, N=N, K=K, soft=soft, us=us, gbps=gbps,
+                            algorithmic_bytes=nbytes, sparse_tile_fraction=float(bufs[0].float().mean().item()),
+                            roofline_bound="hbm", roofline_frac=gbps / HBM_PEAK_GBS))
+        del dev, bufs
+        torch.cuda.empty_cache()
+    return out
 
 
 def fused_set(kind, si, Ms, steps, warmup, batches):
@@ -643,6 +681,11 @@ def write_report(path, steps, warmup, batches):
         for mi in (0, 4, 6):  # q_proj-like, gate/up-like, down
             for si in range(5):
                 emit("sweep", mi, si, (1, 16, 128, 2048))
+        for rec in sampler_set(steps, warmup, batches):
+            f.write(json.dumps(rec) + "\n")
+            f.flush()
+            print(f"[report] sampler {rec['matrix']} soft={rec['soft']}: {rec['us']:.2f} us, {rec['gbps']:.0f} GB/s, "
+                  f"roofline {rec['roofline_frac']:.2f}", flush=True)
         for kind in ("swiglu", "qkv"):
             for si in (0, 2, 4):
                 res = fused_set(kind, si, (1, 16, 128, 2048), steps, warmup, batches)

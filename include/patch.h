@@ -247,6 +247,39 @@ patch_status patch_dense_gemm_swiglu(patch_dtype dtype, int64_t M, int64_t F, in
                                      const void* Wg_dev, const void* Wu_dev, void* H_dev, patch_dtype h_dtype,
                                      void* workspace_dev, uint64_t workspace_bytes, int32_t variant, void* stream);
 
+/*
+ * Forward hybrid-mask sampler (gist.science explainer, section 2
+ * "Methodology: PATCH": tile selection and pattern selection are learnable
+ * distributions sampled with Gumbel-Softmax; the final mask combines the
+ * dense and the 2:4 option).  For an N x K weight with 128 x 128 tiles
+ * (N, K positive multiples of 128):
+ *   tile_logits_dev, tile_u_dev: float32 [N/128][K/128][2], class 0 dense,
+ *     class 1 sparse (8-byte aligned);
+ *   pat_logits_dev, pat_u_dev: float32 [N][K/4][6], the six kept position
+ *     pairs of a group in lexicographic order (0,1) (0,2) (0,3) (1,2) (1,3)
+ *     (2,3) (16-byte aligned);
+ *   the u arrays hold the sampler's uniforms, each in the open interval
+ *     (0, 1) (the caller draws them; other values give IEEE inf/NaN scores);
+ *   tau: the temperature, finite and > 0.
+ * With g = -ln(-ln u) per class (float32), outputs (caller-owned device
+ * memory, row-major):
+ *   tile_map_dev uint8 [N/128][K/128]: 1 where l_sparse + g > l_dense + g'
+ *     (a 2:4 tile), else 0 -- the tile map patch_pack takes (after a copy
+ *     to the host);
+ *   mask_dev uint8 [N][K] (4-byte aligned): 1 at the two positions of the
+ *     pattern with the largest l_p + g_p (first on a tie) in every group --
+ *     the 2:4 mask patch_pack takes;
+ *   soft_dev float32 [N][K] (16-byte aligned) or NULL: y_dense + y_sparse *
+ *     (sum of y_p over the patterns keeping the position), y = softmax of
+ *     (l + g) / tau over the tile's two classes and over the group's six
+ *     patterns.
+ * Asynchronous on `stream`.  Errors: PATCH_ERR_SHAPE (N, K), PATCH_ERR_INVALID_ARG
+ * (null or misaligned pointers, tau not finite and positive).
+ */
+patch_status patch_sample_mask(int64_t N, int64_t K, const float* tile_logits_dev, const float* tile_u_dev,
+                               const float* pat_logits_dev, const float* pat_u_dev, float tau, uint8_t* tile_map_dev,
+                               uint8_t* mask_dev, float* soft_dev, void* stream);
+
 const char* patch_status_string(patch_status s);
 const char* patch_last_error(void);
 

@@ -2,6 +2,7 @@
 // argument validation, the packed header and tile table, kernel selection.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -21,6 +22,9 @@ hipError_t launch_prefill(bool bf16, bool rowmajor, bool out_f32, const void* sr
 uint64_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K, bool rowmajor);
 double prefill_estimate_us(int64_t M, int64_t N, int64_t K, bool rowmajor, uint64_t ws_bytes);
 double decode_estimate_us(int64_t M, int64_t N, int64_t K, double w_bytes);
+hipError_t launch_sample_mask(int64_t N, int64_t K, const float* tile_logits, const float* tile_u,
+                              const float* pat_logits, const float* pat_u, float tau, uint8_t* tile_map,
+                              uint8_t* mask, float* soft, hipStream_t s);
 }  // namespace patch
 
 namespace {
@@ -102,6 +106,26 @@ void put64(uint8_t* p, uint64_t v) { std::memcpy(p, &v, 8); }
 extern "C" {
 
 int32_t patch_abi_version(void) { return 3; }
+
+patch_status patch_sample_mask(int64_t N, int64_t K, const float* tile_logits_dev, const float* tile_u_dev,
+                               const float* pat_logits_dev, const float* pat_u_dev, float tau, uint8_t* tile_map_dev,
+                               uint8_t* mask_dev, float* soft_dev, void* stream) {
+  patch_status s;
+  if ((s = check_nk(N, K))) return s;
+  if (!tile_logits_dev || !tile_u_dev || !pat_logits_dev || !pat_u_dev || !tile_map_dev || !mask_dev)
+    return fail(PATCH_ERR_INVALID_ARG, "null pointer argument");
+  auto aligned = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; };
+  if (!aligned(tile_logits_dev, 8) || !aligned(tile_u_dev, 8) || !aligned16(pat_logits_dev) ||
+      !aligned16(pat_u_dev) || !aligned(mask_dev, 4) || (soft_dev && !aligned16(soft_dev)))
+    return fail(PATCH_ERR_INVALID_ARG,
+                "tile logits and uniforms must be 8-byte, pattern logits, uniforms and soft 16-byte, and the mask "
+                "4-byte aligned");
+  if (!std::isfinite(tau) || !(tau > 0.0f)) return fail(PATCH_ERR_INVALID_ARG, "tau must be finite and > 0");
+  hipError_t e = patch::launch_sample_mask(N, K, tile_logits_dev, tile_u_dev, pat_logits_dev, pat_u_dev, tau,
+                                           tile_map_dev, mask_dev, soft_dev, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "launch sampler");
+  return PATCH_OK;
+}
 
 const char* patch_status_string(patch_status s) {
   switch (s) {

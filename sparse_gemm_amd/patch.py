@@ -48,7 +48,7 @@ EXPORTS = ("patch_abi_version", "patch_packed_bytes", "patch_pack", "patch_desc_
            "patch_gemm_workspace_bytes", "patch_dense_gemm_workspace_bytes", "patch_gemm", "patch_gemm_ex",
            "patch_dense_gemm", "patch_dense_gemm_ex", "patch_packed_bytes_gate_up", "patch_pack_gate_up",
            "patch_gemm_swiglu_workspace_bytes", "patch_gemm_swiglu", "patch_dense_gemm_swiglu_workspace_bytes",
-           "patch_dense_gemm_swiglu", "patch_packed_bytes_concat", "patch_pack_concat",
+           "patch_dense_gemm_swiglu", "patch_packed_bytes_concat", "patch_pack_concat", "patch_sample_mask",
            "patch_status_string", "patch_last_error")
 
 _lib = None
@@ -100,6 +100,8 @@ def load():
     lib.patch_packed_bytes_concat.restype = U64
     lib.patch_pack_concat.argtypes = [ctypes.c_int, I32, P, I64, P, P, P, P, U64, DP, P]
     lib.patch_pack_concat.restype = ctypes.c_int
+    lib.patch_sample_mask.argtypes = [I64, I64, P, P, P, P, ctypes.c_float, P, P, P, P]
+    lib.patch_sample_mask.restype = ctypes.c_int
     lib.patch_status_string.argtypes = [ctypes.c_int]
     lib.patch_status_string.restype = ctypes.c_char_p
     lib.patch_last_error.argtypes = []
@@ -351,3 +353,29 @@ def pack_concat(Ws, tile_maps, masks, out: Optional[torch.Tensor] = None) -> Pac
     _check(lib.patch_pack_concat(_dt(Ws[0].dtype), n, Ns, K, wp, mp, kp, _ptr(out), out.numel(), ctypes.byref(desc),
                                  _stream()))
     return PackedWeight(out, desc)
+
+
+def sample_mask(tile_logits: torch.Tensor, tile_u: torch.Tensor, pat_logits: torch.Tensor, pat_u: torch.Tensor,
+                tau: float, soft: bool = True, out=None):
+    """Forward hybrid-mask sampler (patch_sample_mask) on device float32
+    tensors: tile_logits, tile_u [N/128, K/128, 2]; pat_logits, pat_u
+    [N, K/4, 6].  Returns (tile_map uint8 [N/128, K/128], mask uint8 [N, K],
+    soft float32 [N, K] or None); out = (tile_map, mask, soft) reuses
+    buffers."""
+    lib = load()
+    N, G = int(pat_logits.shape[0]), int(pat_logits.shape[1])
+    K = 4 * G
+    for t, shape in ((tile_logits, (N // 128, K // 128, 2)), (tile_u, (N // 128, K // 128, 2)),
+                     (pat_logits, (N, G, 6)), (pat_u, (N, G, 6))):
+        if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"expected a contiguous float32 device tensor of shape {shape}")
+    dev = pat_logits.device
+    if out is None:
+        out = (torch.empty((N // 128, K // 128), dtype=torch.uint8, device=dev),
+               torch.empty((N, K), dtype=torch.uint8, device=dev),
+               torch.empty((N, K), dtype=torch.float32, device=dev) if soft else None)
+    tmap, mask, sf = out
+    _check(lib.patch_sample_mask(N, K, _ptr(tile_logits), _ptr(tile_u), _ptr(pat_logits), _ptr(pat_u), float(tau),
+                                 _ptr(tmap), _ptr(mask), _ptr(sf) if soft else ctypes.c_void_p(0),
+                                 _stream(dev.index)))
+    return tmap, mask, (sf if soft else None)
