@@ -12,5 +12,5 @@ computes and which passage of the pages it follows.
 from .oracle import (  # noqa: F401
     F16, BF16, OracleError, build, lib_path, load, validate, effective_mask, gemm_f64, packed_bytes, pack,
     round_f64, f16_to_double, bf16_to_double, num_threads, silu, swiglu_f64, interleave_gate_up, PATTERN_PAIRS,
-    gumbel, gumbel_softmax, sample_mask,
+    gumbel, gumbel_softmax, sample_mask, exec_map, apply_fine_mask,
 )

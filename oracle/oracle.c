@@ -532,3 +532,47 @@ int oracle_sample_mask(int64_t N, int64_t K, int64_t tn, int64_t tk, const float
   }
   return ORACLE_OK;
 }
+
+/* ---------------------------------------------------------------------------
+ * Mask tiles finer than the execution tile (gist.science explainer, section 4
+ * "Ablation Studies", "Tile Size": PATCH works across tile sizes, 4 x 4 being
+ * the finest control, while the hardware executes larger tiles, 128 x 128).
+ *
+ * Reading (not on the pages): the model was trained with the fine effective
+ * mask E_fine (oracle_effective_mask at the fine tile size), so inference
+ * must compute X (W o E_fine)^T exactly.  An execution tile runs as 2:4 only
+ * if every fine tile inside it is 2:4 (then its 2:4 mask is the fine one);
+ * otherwise it runs dense on W o E_fine -- the weights its 2:4 fine tiles
+ * pruned stored as +0.
+ * ------------------------------------------------------------------------- */
+
+/* exec_map[i][j] (N/en x K/ek) = 1 iff every fine tile (b1 x b2) inside
+ * execution tile (i, j) is 2:4 in fine_map (N/b1 x K/b2). */
+int oracle_exec_map(int64_t N, int64_t K, int64_t b1, int64_t b2, int64_t en, int64_t ek, const uint8_t* fine_map,
+                    uint8_t* exec_map) {
+  if (check_shape(N, K, b1, b2) || check_shape(N, K, en, ek) || en % b1 || ek % b2) return ORACLE_ERR_SHAPE;
+  const int64_t fKT = K / b2, eKT = K / ek;
+  for (int64_t i = 0; i < N / en; i++)
+    for (int64_t j = 0; j < eKT; j++) {
+      int all = 1;
+      for (int64_t fi = i * (en / b1); fi < (i + 1) * (en / b1); fi++)
+        for (int64_t fj = j * (ek / b2); fj < (j + 1) * (ek / b2); fj++) all &= fine_map[fi * fKT + fj] != 0;
+      exec_map[i * eKT + j] = (uint8_t)all;
+    }
+  return ORACLE_OK;
+}
+
+/* W_out = W o E_fine as element bits: a kept weight's bits unchanged, a
+ * pruned one +0 (bits 0). */
+int oracle_apply_fine_mask(int64_t N, int64_t K, int64_t b1, int64_t b2, const uint16_t* W, const uint8_t* fine_map,
+                           const uint8_t* mask, uint16_t* W_out) {
+  int rc = check_shape(N, K, b1, b2);
+  if (rc) return rc;
+  uint8_t* E = (uint8_t*)malloc((size_t)(N * K));
+  if (!E) return ORACLE_ERR_ARG;
+  rc = oracle_effective_mask(N, K, b1, b2, fine_map, mask, E);
+  if (!rc)
+    for (int64_t i = 0; i < N * K; i++) W_out[i] = E[i] ? W[i] : (uint16_t)0;
+  free(E);
+  return rc;
+}

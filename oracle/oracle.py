@@ -75,6 +75,10 @@ def load():
     lib.oracle_gumbel_softmax.restype = ctypes.c_int
     lib.oracle_sample_mask.argtypes = [I64, I64, I64, I64, P, P, P, P, ctypes.c_double, P, P, P]
     lib.oracle_sample_mask.restype = ctypes.c_int
+    lib.oracle_exec_map.argtypes = [I64, I64, I64, I64, I64, I64, P, P]
+    lib.oracle_exec_map.restype = ctypes.c_int
+    lib.oracle_apply_fine_mask.argtypes = [I64, I64, I64, I64, P, P, P, P]
+    lib.oracle_apply_fine_mask.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -253,3 +257,30 @@ def sample_mask(tile_logits, tile_u, pat_logits, pat_u, tau: float, tile_n: int 
     if rc:
         raise OracleError(rc)
     return tmap, mask, out
+
+
+# ---------------------------------------------------------------------------- fine mask tiles
+# Mask tiles finer than the 128 x 128 execution tile (gist.science explainer,
+# section 4 "Ablation Studies", "Tile Size"); the reading is restated in
+# oracle.c next to oracle_exec_map.
+def exec_map(N, K, fine_map, b1, b2, en=128, ek=128) -> np.ndarray:
+    """Execution tile map: 1 iff every fine tile inside is 2:4."""
+    fm = _u8(fine_map)
+    assert fm.shape == (N // b1, K // b2)
+    out = np.zeros((N // en, K // ek), dtype=np.uint8)
+    rc = load().oracle_exec_map(N, K, b1, b2, en, ek, _p(fm), _p(out))
+    if rc:
+        raise OracleError(rc)
+    return out
+
+
+def apply_fine_mask(W, fine_map, mask, b1, b2) -> np.ndarray:
+    """W o E_fine as element bits (pruned weights +0)."""
+    W = _u16(W)
+    N, K = W.shape
+    fm, mk = _u8(fine_map), _u8(mask)
+    out = np.zeros_like(W)
+    rc = load().oracle_apply_fine_mask(N, K, b1, b2, _p(W), _p(fm), _p(mk), _p(out))
+    if rc:
+        raise OracleError(rc)
+    return out

@@ -248,3 +248,31 @@ def make_sampler_inputs(N: int, K: int, seed: int, tile_n: int = 128, tile_k: in
     pl = pattern_scale * rng.standard_normal((N, G, 6))
     return SamplerInputs(tl.astype(np.float32), gen_uniform_open(rng, (NT, KT, 2)), pl.astype(np.float32),
                          gen_uniform_open(rng, (N, G, 6)))
+
+
+# ---------------------------------------------------------------------------- fine mask tiles
+ROLE_FINE = 8
+
+
+def gen_fine_map(rng: np.random.Generator, N: int, K: int, b1: int, b2: int, s_exec: float,
+                 p_sub: float) -> np.ndarray:
+    """Fine tile map (N/b1 x K/b2) of mask tiles b1 x b2: each 128 x 128
+    execution tile is, with probability s_exec, 2:4 in every fine tile, else
+    each of its fine tiles is 2:4 with probability p_sub."""
+    NT, KT = N // TILE, K // TILE
+    fn, fk = TILE // b1, TILE // b2
+    whole = rng.random((NT, KT)) < s_exec
+    sub = rng.random((NT, fn, KT, fk)) < p_sub
+    sub |= whole[:, None, :, None]
+    return sub.reshape(N // b1, K // b2).astype(np.uint8)
+
+
+def make_fine(dtype: str, N: int, K: int, b1: int, b2: int, seed: int, s_exec: float = 0.4,
+              p_sub: float = 0.6) -> Problem:
+    """Weights with a fine tile map (tile_map holds the N/b1 x K/b2 fine map)
+    and a mask with one of the six patterns in every group (read only inside
+    2:4 fine tiles)."""
+    rng = rng_for(seed, 41, N, K, ROLE_FINE)
+    w = gen_w(rng, N, K, dtype)
+    fmap = gen_fine_map(rng, N, K, b1, b2, s_exec, p_sub)
+    return Problem(dtype, N, K, w, fmap, gen_mask_uniform(rng, N, K), {"seed": seed, "b1": b1, "b2": b2})

@@ -572,3 +572,66 @@ def test_temperature_limits():
                 assert y[best] > 1 - 1e-12
             y, _ = oracle.gumbel_softmax(l, u, 1e7)
             np.testing.assert_allclose(y, 1.0 / n, atol=1e-5)
+
+
+# ---------------------------------------------------------------- mask tiles finer than execution tiles
+# gist.science explainer, section 4 "Ablation Studies", "Tile Size": the mask
+# can be learnt on tiles as fine as 4 x 4 while the hardware executes
+# 128 x 128 tiles.
+@pytest.mark.parametrize("en,ek", [(8, 8), (8, 4), (4, 8)])
+def test_exec_map_brute_force(en, ek):
+    """8 x 8 weight, 4 x 4 fine tiles, every one of the 16 fine maps: an
+    execution tile is 2:4 exactly when all fine tiles inside it are."""
+    for bits in range(16):
+        fm = np.array([(bits >> i) & 1 for i in range(4)], dtype=np.uint8).reshape(2, 2)
+        got = oracle.exec_map(8, 8, fm, 4, 4, en, ek)
+        for i in range(8 // en):
+            for j in range(8 // ek):
+                sub = [fm[a, b] for a in range(2) for b in range(2)
+                       if i * en <= 4 * a < (i + 1) * en and j * ek <= 4 * b < (j + 1) * ek]
+                assert got[i, j] == int(all(sub)), (bits, i, j)
+
+
+def test_exec_map_identity_and_monotone():
+    """Fine tiles of the execution size map to themselves; coarser execution
+    tiles never hold more 2:4 tiles' worth of area than the fine map."""
+    rng = np.random.default_rng(3)
+    fm = inputs.gen_fine_map(rng, 384, 512, 128, 128, 0.3, 0.5)
+    assert np.array_equal(oracle.exec_map(384, 512, fm, 128, 128), fm)
+    for b1, b2 in ((4, 4), (32, 16), (64, 128)):
+        fm = inputs.gen_fine_map(rng, 384, 512, b1, b2, 0.3, 0.7)
+        em = oracle.exec_map(384, 512, fm, b1, b2)
+        assert em.sum() * 128 * 128 <= fm.sum() * b1 * b2
+
+
+def test_apply_fine_mask_bits():
+    """Kept weights keep their bits (-0 included); pruned ones become +0;
+    dense fine tiles are untouched."""
+    p = inputs.make_fine("bf16", 256, 256, 16, 32, 4)
+    p.w[0, :8] = 0x8000  # -0
+    p.tile_map[0, 0] = 1
+    out = oracle.apply_fine_mask(p.w, p.tile_map, p.mask, 16, 32)
+    E = oracle.effective_mask(256, 256, p.tile_map, p.mask, 16, 32)
+    assert np.array_equal(out[E == 1], p.w[E == 1])
+    assert np.all(out[E == 0] == 0)
+    dense = np.repeat(np.repeat(p.tile_map == 0, 16, axis=0), 32, axis=1)
+    assert np.array_equal(out[dense], p.w[dense])
+
+
+@pytest.mark.parametrize("b1,b2", [(4, 4), (16, 16), (32, 64), (128, 128)])
+def test_fine_policy_preserves_the_product(b1, b2):
+    """Executing on 128 x 128 tiles with the policy's map and the masked
+    weight gives exactly the fine-tiled product X (W o E_fine)^T (binary64,
+    same terms in the same order)."""
+    N, K, M = 256, 384, 9
+    p = inputs.make_fine("f16", N, K, b1, b2, 5)
+    X = inputs.make_custom_x("f16", M, K, 6)
+    em = oracle.exec_map(N, K, p.tile_map, b1, b2)
+    W2 = oracle.apply_fine_mask(p.w, p.tile_map, p.mask, b1, b2)
+    fine = oracle.gemm_f64("f16", X, p.w, p.tile_map, p.mask, tile_n=b1, tile_k=b2)
+    execd = oracle.gemm_f64("f16", X, W2, em, p.mask)
+    assert np.array_equal(fine, execd)
+    assert 0 < em.sum() < em.size  # both execution kinds occur
+    if (b1, b2) != (128, 128):
+        # some dense execution tiles hold pruned (2:4) fine tiles
+        assert (p.tile_map.sum() * b1 * b2) > em.sum() * 128 * 128
