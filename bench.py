@@ -392,7 +392,8 @@ def main():
     ap.add_argument("--report", default=None, help="also write the full sweep as JSON lines to this path")
     ap.add_argument("--report-steps", type=int, default=100, help="launches per timed batch in the report")
     ap.add_argument("--report-batches", type=int, default=10, help="timed batches per point in the report (median)")
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill_mlp", "imbalanced_13b", "sampler"],
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill_mlp", "imbalanced_13b", "sampler", "fine_mask"],
                     help="decode (default: the q_proj decode GEMM), a prefill workload or the mask sampler, "
                          "for profiling")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -425,8 +426,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration_copy_bytes": src.numel(), "copies": 3}), file=sys.stderr, flush=True)
         del src, dst
-    if args.workload == "sampler":
-        for rec in sampler_set(args.steps, args.warmup, 1):
+    if args.workload in ("sampler", "fine_mask"):
+        for rec in (sampler_set if args.workload == "sampler" else fine_set)(args.steps, args.warmup, 1):
             print(json.dumps(rec), flush=True)
         return
     if args.workload != "decode":
@@ -545,6 +546,38 @@ def sampler_set(steps, warmup, batches):
                             algorithmic_bytes=nbytes, sparse_tile_fraction=float(bufs[0].float().mean().item()),
                             roofline_bound="hbm", roofline_frac=gbps / HBM_PEAK_GBS))
         del dev, bufs
+        torch.cuda.empty_cache()
+    return out
+
+
+def fine_set(steps, warmup, batches):
+    """patch_apply_fine_mask (W o E_fine for the dense execution tiles of a
+    mask learnt on finer tiles) on the LLaMA-2-7B gate_proj shape with 32 x 32
+    and 4 x 4 mask tiles: graph replays; HBM roofline on W read (2 B), mask
+    read (1 B) and W_out written (2 B) per weight."""
+    import torch
+
+    from sparse_gemm_amd import inputs, patch
+
+    out = []
+    N, K = 11008, 4096
+    for b1, b2 in ((32, 32), (4, 4)):
+        p = inputs.make_fine("bf16", N, K, b1, b2, 0)
+        W = torch.from_numpy(p.w.view(np.int16)).view(torch.bfloat16).cuda()
+        fm = torch.from_numpy(p.tile_map).cuda()
+        mk = torch.from_numpy(p.mask).cuda()
+        Wo = torch.empty_like(W)
+        fn = (lambda k: patch.apply_fine_mask(W, fm, mk, b1, b2, out=Wo))
+        _, per = time_graphs([("f", fn)], steps, warmup, batches)
+        us = median(per["f"]) * 1e3
+        nbytes = 5 * N * K + p.tile_map.size
+        gbps = nbytes / (us * 1e-6) / 1e9
+        emap = patch.exec_tile_map(N, K, p.tile_map, b1, b2)
+        out.append(dict(config="fine_mask", matrix="gate_proj", N=N, K=K, b1=b1, b2=b2, us=us, gbps=gbps,
+                        algorithmic_bytes=nbytes, fine_sparse_fraction=float(p.tile_map.mean()),
+                        exec_sparse_fraction=float(emap.mean()), roofline_bound="hbm",
+                        roofline_frac=gbps / HBM_PEAK_GBS))
+        del W, fm, mk, Wo
         torch.cuda.empty_cache()
     return out
 
@@ -681,6 +714,11 @@ def write_report(path, steps, warmup, batches):
         for mi in (0, 4, 6):  # q_proj-like, gate/up-like, down
             for si in range(5):
                 emit("sweep", mi, si, (1, 16, 128, 2048))
+        for rec in fine_set(steps, warmup, batches):
+            f.write(json.dumps(rec) + "\n")
+            f.flush()
+            print(f"[report] fine mask {rec['b1']}x{rec['b2']}: {rec['us']:.2f} us, {rec['gbps']:.0f} GB/s, "
+                  f"roofline {rec['roofline_frac']:.2f}", flush=True)
         for rec in sampler_set(steps, warmup, batches):
             f.write(json.dumps(rec) + "\n")
             f.flush()

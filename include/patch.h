@@ -280,6 +280,36 @@ patch_status patch_sample_mask(int64_t N, int64_t K, const float* tile_logits_de
                                const float* pat_logits_dev, const float* pat_u_dev, float tau, uint8_t* tile_map_dev,
                                uint8_t* mask_dev, float* soft_dev, void* stream);
 
+/*
+ * Mask tiles finer than the 128 x 128 execution tile (gist.science
+ * explainer, section 4 "Ablation Studies", "Tile Size": the mask can be
+ * learnt on tiles as fine as 4 x 4; the hardware executes 128 x 128).  The
+ * result must stay X (W o E_fine)^T, E_fine the effective mask at the fine
+ * tile size (1 in dense fine tiles, the 2:4 mask in 2:4 ones).  Policy: an
+ * execution tile runs as 2:4 only if every fine tile in it is 2:4 (its 2:4
+ * mask is then the fine one); otherwise it runs dense on W o E_fine.
+ *
+ * Fine tiles are b1 x b2 (rows x columns), b1 and b2 dividing 128, b2 a
+ * multiple of 4; the fine map is uint8 [N/b1][K/b2], nonzero = 2:4.
+ *
+ * patch_exec_tile_map (host only): exec_map_host uint8 [N/128][K/128] = 1
+ * where every fine tile is 2:4; *n_sparse_out (may be NULL) receives their
+ * number.  Errors: PATCH_ERR_SHAPE, PATCH_ERR_INVALID_ARG (null maps).
+ *
+ * patch_apply_fine_mask: W_out_dev = W o E_fine as element bits (kept weights
+ * unchanged, pruned ones +0), N x K row-major 16-bit elements of dtype; W_dev
+ * and W_out_dev 16-byte aligned (they may be the same buffer), mask_dev uint8
+ * [N][K] 8-byte aligned, fine_map_dev the fine map in device memory.  The
+ * groups of the 2:4 fine tiles are applied as given (patch_pack validates
+ * the ones its 2:4 execution tiles store).  Asynchronous.  Then
+ * patch_pack(W_out, exec map, mask) packs the layer.
+ */
+patch_status patch_exec_tile_map(int64_t N, int64_t K, int64_t b1, int64_t b2, const uint8_t* fine_map_host,
+                                 uint8_t* exec_map_host, int64_t* n_sparse_out);
+patch_status patch_apply_fine_mask(patch_dtype dtype, int64_t N, int64_t K, int64_t b1, int64_t b2, const void* W_dev,
+                                   const uint8_t* fine_map_dev, const uint8_t* mask_dev, void* W_out_dev,
+                                   void* stream);
+
 const char* patch_status_string(patch_status s);
 const char* patch_last_error(void);
 

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpatch.so")
-SOURCES = ["pack.hip", "gemm_decode.hip", "gemm_prefill.hip", "sampler.hip", "patch_api.cpp"]
+SOURCES = ["pack.hip", "gemm_decode.hip", "gemm_prefill.hip", "sampler.hip", "fine_mask.hip", "patch_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -25,6 +25,8 @@ double decode_estimate_us(int64_t M, int64_t N, int64_t K, double w_bytes);
 hipError_t launch_sample_mask(int64_t N, int64_t K, const float* tile_logits, const float* tile_u,
                               const float* pat_logits, const float* pat_u, float tau, uint8_t* tile_map,
                               uint8_t* mask, float* soft, hipStream_t s);
+hipError_t launch_apply_fine_mask(int64_t N, int64_t K, int b1, int b2, const void* W, const uint8_t* fine_map,
+                                  const uint8_t* mask, void* out, hipStream_t s);
 }  // namespace patch
 
 namespace {
@@ -124,6 +126,57 @@ patch_status patch_sample_mask(int64_t N, int64_t K, const float* tile_logits_de
   hipError_t e = patch::launch_sample_mask(N, K, tile_logits_dev, tile_u_dev, pat_logits_dev, pat_u_dev, tau,
                                            tile_map_dev, mask_dev, soft_dev, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "launch sampler");
+  return PATCH_OK;
+}
+
+namespace {
+patch_status check_fine(int64_t N, int64_t K, int64_t b1, int64_t b2) {
+  patch_status s = check_nk(N, K);
+  if (s) return s;
+  if (b1 <= 0 || b2 <= 0 || kTile % b1 || kTile % b2 || b2 % 4)
+    return fail(PATCH_ERR_SHAPE, "fine tiles %lld x %lld must divide 128 (columns a multiple of 4)", (long long)b1,
+                (long long)b2);
+  return PATCH_OK;
+}
+}  // namespace
+
+patch_status patch_exec_tile_map(int64_t N, int64_t K, int64_t b1, int64_t b2, const uint8_t* fine_map_host,
+                                 uint8_t* exec_map_host, int64_t* n_sparse_out) {
+  patch_status s = check_fine(N, K, b1, b2);
+  if (s) return s;
+  if (!fine_map_host || !exec_map_host) return fail(PATCH_ERR_INVALID_ARG, "null tile map");
+  const int64_t fKT = K / b2, KT = K / kTile, rn = kTile / b1, rk = kTile / b2;
+  int64_t n_sparse = 0;
+  for (int64_t i = 0; i < N / kTile; i++)
+    for (int64_t j = 0; j < KT; j++) {
+      bool all = true;
+      for (int64_t a = 0; a < rn && all; a++) {
+        const uint8_t* row = fine_map_host + (i * rn + a) * fKT + j * rk;
+        for (int64_t b = 0; b < rk; b++)
+          if (!row[b]) {
+            all = false;
+            break;
+          }
+      }
+      exec_map_host[i * KT + j] = all ? 1 : 0;
+      n_sparse += all;
+    }
+  if (n_sparse_out) *n_sparse_out = n_sparse;
+  return PATCH_OK;
+}
+
+patch_status patch_apply_fine_mask(patch_dtype dtype, int64_t N, int64_t K, int64_t b1, int64_t b2, const void* W_dev,
+                                   const uint8_t* fine_map_dev, const uint8_t* mask_dev, void* W_out_dev,
+                                   void* stream) {
+  patch_status s;
+  if ((s = check_dtype(dtype))) return s;
+  if ((s = check_fine(N, K, b1, b2))) return s;
+  if (!W_dev || !fine_map_dev || !mask_dev || !W_out_dev) return fail(PATCH_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(W_dev) || !aligned16(W_out_dev) || (reinterpret_cast<uintptr_t>(mask_dev) & 7u))
+    return fail(PATCH_ERR_INVALID_ARG, "W and W_out must be 16-byte and the mask 8-byte aligned");
+  hipError_t e = patch::launch_apply_fine_mask(N, K, (int)b1, (int)b2, W_dev, fine_map_dev, mask_dev, W_out_dev,
+                                               reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "launch apply_fine_mask");
   return PATCH_OK;
 }
 

@@ -49,7 +49,7 @@ EXPORTS = ("patch_abi_version", "patch_packed_bytes", "patch_pack", "patch_desc_
            "patch_dense_gemm", "patch_dense_gemm_ex", "patch_packed_bytes_gate_up", "patch_pack_gate_up",
            "patch_gemm_swiglu_workspace_bytes", "patch_gemm_swiglu", "patch_dense_gemm_swiglu_workspace_bytes",
            "patch_dense_gemm_swiglu", "patch_packed_bytes_concat", "patch_pack_concat", "patch_sample_mask",
-           "patch_status_string", "patch_last_error")
+           "patch_exec_tile_map", "patch_apply_fine_mask", "patch_status_string", "patch_last_error")
 
 _lib = None
 
@@ -102,6 +102,10 @@ def load():
     lib.patch_pack_concat.restype = ctypes.c_int
     lib.patch_sample_mask.argtypes = [I64, I64, P, P, P, P, ctypes.c_float, P, P, P, P]
     lib.patch_sample_mask.restype = ctypes.c_int
+    lib.patch_exec_tile_map.argtypes = [I64, I64, I64, I64, P, P, ctypes.POINTER(I64)]
+    lib.patch_exec_tile_map.restype = ctypes.c_int
+    lib.patch_apply_fine_mask.argtypes = [ctypes.c_int, I64, I64, I64, I64, P, P, P, P, P]
+    lib.patch_apply_fine_mask.restype = ctypes.c_int
     lib.patch_status_string.argtypes = [ctypes.c_int]
     lib.patch_status_string.restype = ctypes.c_char_p
     lib.patch_last_error.argtypes = []
@@ -379,3 +383,37 @@ def sample_mask(tile_logits: torch.Tensor, tile_u: torch.Tensor, pat_logits: tor
                                  _ptr(tmap), _ptr(mask), _ptr(sf) if soft else ctypes.c_void_p(0),
                                  _stream(dev.index)))
     return tmap, mask, (sf if soft else None)
+
+
+def exec_tile_map(N: int, K: int, fine_map, b1: int, b2: int) -> np.ndarray:
+    """128 x 128 execution tile map from a fine tile map of b1 x b2 tiles
+    (patch_exec_tile_map): 1 where every fine tile is 2:4."""
+    fm = _host_map(fine_map)
+    if fm.shape != (N // b1, K // b2):
+        raise ValueError(f"fine map must be {(N // b1, K // b2)}")
+    out = np.zeros((N // 128, K // 128), dtype=np.uint8)
+    n = ctypes.c_int64(0)
+    _check(load().patch_exec_tile_map(N, K, b1, b2, fm.ctypes.data, out.ctypes.data, ctypes.byref(n)))
+    return out
+
+
+def apply_fine_mask(W: torch.Tensor, fine_map: torch.Tensor, mask: torch.Tensor, b1: int, b2: int,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """W o E_fine on the device (patch_apply_fine_mask): fine_map uint8
+    [N/b1, K/b2] and mask uint8 [N, K] device tensors."""
+    N, K = W.shape
+    if out is None:
+        out = torch.empty_like(W)
+    _check(load().patch_apply_fine_mask(_dt(W.dtype), N, K, b1, b2, _ptr(W), _ptr(fine_map), _ptr(mask), _ptr(out),
+                                        _stream(W.device.index)))
+    return out
+
+
+def pack_fine(W: torch.Tensor, fine_map, mask: torch.Tensor, b1: int, b2: int) -> PackedWeight:
+    """Pack a layer whose mask was learnt on b1 x b2 tiles: execution map by
+    the all-2:4 policy, dense execution tiles from W o E_fine."""
+    N, K = W.shape
+    fm_host = _host_map(fine_map)
+    emap = exec_tile_map(N, K, fm_host, b1, b2)
+    Wm = apply_fine_mask(W, torch.from_numpy(fm_host).to(W.device), mask, b1, b2)
+    return pack(Wm, emap, mask)

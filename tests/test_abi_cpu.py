@@ -131,3 +131,25 @@ def test_workspace_query_host_logic():
         assert b // (M * N * 4) <= K // 256  # at least two tile columns a range
     for bad in [(0, 4096, 4096), (-1, 4096, 4096), (16, 100, 4096), (16, 4096, 100), (16, 4096, 128 * 1025)]:
         assert ws(*bad) == 0, bad
+
+
+@pytest.mark.parametrize("b1,b2", [(1, 4), (4, 4), (16, 16), (32, 64), (64, 128), (128, 128)])
+def test_exec_tile_map_matches_oracle(b1, b2):
+    """Host logic of patch_exec_tile_map (no GPU): the execution map of a
+    fine map equals the oracle's, byte for byte."""
+    rng = np.random.default_rng(b1 * 1000 + b2)
+    N, K = 384, 512
+    fm = inputs.gen_fine_map(rng, N, K, b1, b2, 0.4, 0.8)
+    got = patch.exec_tile_map(N, K, fm, b1, b2)
+    assert np.array_equal(got, oracle.exec_map(N, K, fm, b1, b2))
+
+
+def test_exec_tile_map_rejects_bad_tiles():
+    lib = patch.load()
+    fm = np.ones(4096, dtype=np.uint8)
+    out = np.zeros(16, dtype=np.uint8)
+    P = ctypes.c_void_p
+    for b1, b2, want in ((3, 4, 2), (4, 2, 2), (4, 6, 2), (256, 128, 2), (0, 4, 2), (4, 4, 0)):
+        assert lib.patch_exec_tile_map(256, 256, b1, b2, P(fm.ctypes.data), P(out.ctypes.data), None) == want
+    assert lib.patch_exec_tile_map(256, 256, 4, 4, None, P(out.ctypes.data), None) == 1
+    assert lib.patch_exec_tile_map(200, 256, 4, 4, P(fm.ctypes.data), P(out.ctypes.data), None) == 2
