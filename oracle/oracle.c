@@ -162,30 +162,43 @@ static int check_shape(int64_t N, int64_t K, int64_t tn, int64_t tk) {
   return ORACLE_OK;
 }
 
-/* Returns ORACLE_ERR_MASK if a group of four inside a sparse tile does not
- * keep exactly two positions; *bad_row / *bad_group receive the first one. */
+/* Tile kinds (tile-map bytes): 0 dense, 1 2:4 (two kept in every group of
+ * four consecutive weights along K), 2 4:8 (four kept in every group of
+ * eight).  4:8 is one of the "other N:M patterns" the explainer's section 5
+ * "Significance" names as future work (the framework is pattern-agnostic);
+ * any other byte is an error (ORACLE_ERR_ARG).
+ * Returns ORACLE_ERR_MASK if a group inside a 2:4 or 4:8 tile does not keep
+ * exactly half its positions; *bad_row / *bad_group receive the first one
+ * (the group index counts groups of that tile's kind from column 0). */
 int oracle_validate(int64_t N, int64_t K, int64_t tn, int64_t tk, const uint8_t* tile_map,
                     const uint8_t* mask, int64_t* bad_row, int64_t* bad_group) {
   int rc = check_shape(N, K, tn, tk);
   if (rc) return rc;
   int64_t KT = K / tk;
+  for (int64_t t = 0; t < (N / tn) * KT; t++) {
+    if (tile_map[t] > 2) return ORACLE_ERR_ARG;
+    if (tile_map[t] == 2 && tk % 8) return ORACLE_ERR_SHAPE;
+  }
   for (int64_t n = 0; n < N; n++) {
-    for (int64_t g = 0; g < K / 4; g++) {
-      int64_t k0 = 4 * g;
-      if (!tile_map[(n / tn) * KT + k0 / tk]) continue; /* dense tile: mask not read */
-      int kept = 0;
-      for (int d = 0; d < 4; d++) kept += mask[n * K + k0 + d] != 0;
-      if (kept != 2) {
-        if (bad_row) *bad_row = n;
-        if (bad_group) *bad_group = g;
-        return ORACLE_ERR_MASK;
+    for (int64_t k0 = 0; k0 < K;) {
+      const int kind = tile_map[(n / tn) * KT + k0 / tk];
+      const int gs = kind == 2 ? 8 : 4; /* group size */
+      if (kind) {                       /* dense tile: mask not read */
+        int kept = 0;
+        for (int d = 0; d < gs; d++) kept += mask[n * K + k0 + d] != 0;
+        if (kept != gs / 2) {
+          if (bad_row) *bad_row = n;
+          if (bad_group) *bad_group = k0 / gs;
+          return ORACLE_ERR_MASK;
+        }
       }
+      k0 += gs;
     }
   }
   return ORACLE_OK;
 }
 
-/* E[n][k] = 1 in dense tiles, (mask != 0) in sparse tiles. */
+/* E[n][k] = 1 in dense tiles, (mask != 0) in 2:4 and 4:8 tiles. */
 int oracle_effective_mask(int64_t N, int64_t K, int64_t tn, int64_t tk, const uint8_t* tile_map,
                           const uint8_t* mask, uint8_t* E) {
   int rc = check_shape(N, K, tn, tk);
@@ -290,8 +303,9 @@ void oracle_round_f64(int dtype, int64_t n, const double* in, uint16_t* out) {
  * Header, 256 bytes at offset 0:
  *   u32 magic 0x48435450, u32 version 3, u32 dtype (0 f16, 1 bf16),
  *   u32 tile_n 128, u32 tile_k 128, u32 N, u32 K, u32 NT, u32 KT,
- *   u32 n_sparse, u64 table_offset (= 256), u64 data_offset,
- *   u64 data_bytes, u64 total_bytes.
+ *   u32 n_sparse (2:4 and 4:8 tiles), u64 table_offset (= 256),
+ *   u64 data_offset, u64 data_bytes, u64 total_bytes, u32 n_48 (the 4:8
+ *   tiles among them) at byte 72.
  * Data at data_offset = round_up(256 + 16*T, 256).
  *
  * A "band" is 16 consecutive rows of a row-block (b = 0..7); a "piece" is
@@ -302,7 +316,7 @@ void oracle_round_f64(int dtype, int64_t n, const double* in, uint16_t* out) {
  * starts S_i bytes after band b-1.
  * Tile table at 256: T entries of 16 bytes, tile (i, j) at index i*KT + j:
  *   u64 byte offset (from the start of the blob) of the tile's band-0 piece,
- *   u32 kind (0 dense, 1 sparse), u32 S_i.
+ *   u32 kind (0 dense, 1 2:4, 2 4:8), u32 S_i.
  * So band b's piece of tile (i, j) starts at entry offset + b * S_i.
  *
  * Inside a piece a "lane" is a number l = 0..63 with row-in-band
@@ -316,7 +330,17 @@ void oracle_round_f64(int dtype, int64_t n, const double* in, uint16_t* out) {
  *   2*g + u (u = 0, 1) is column 64*q + 16*h + 4*g + 2*e + u.  (Each half is
  *   a 2:4 operand with the fixed pattern (0,1) or (2,3), so a dense tile runs
  *   on the same sparse matrix instruction as a 2:4 tile.)
- * Sparse piece: groups of four columns g = 0..31 (columns 4g..4g+3).
+ * 4:8 piece (2304 bytes, like a 2:4 one): the tile's columns form four
+ *   32-column slices c = 0..3; lane l owns, in slice c, the group of eight
+ *   columns 32*c + 8*h .. +7 of row 16*band + r.  Values: block q (q = 0, 1)
+ *   at byte 1024*q; lane l's 16 bytes at 1024*q + 16*l hold the four kept
+ *   elements (ascending column) of its group in slice 2*q, then the four of
+ *   its group in slice 2*q + 1.  Masks at byte 2048: a u32 per lane at
+ *   2048 + 4*l whose byte c has bit p set iff column 32*c + 8*h + p of the
+ *   row is kept.  (Lane l's group of a slice is exactly the eight elements
+ *   that lane holds of the A operand of v_mfma_f32_16x16x32, so a kernel can
+ *   rebuild the dense operand from them without moving data between lanes.)
+ * Sparse (2:4) piece: groups of four columns g = 0..31 (columns 4g..4g+3).
  *   Values: block q (q = 0, 1) at byte 1024*q; lane l holds, for p = 0..3
  *   and group g = 16*q + 4*h + p, the two kept elements of row 16*band + r in
  *   ascending column order -- 8 elements, 16 bytes.
@@ -364,8 +388,11 @@ int oracle_pack(int dtype, int64_t N, int64_t K, const uint16_t* W, const uint8_
   if (out_bytes < total) return ORACLE_ERR_SMALL;
   memset(out, 0, (size_t)total);
   int64_t NT = N / PT_B, KT = K / PT_B, T = NT * KT;
-  uint32_t ns = 0;
-  for (int64_t t = 0; t < T; t++) ns += tile_map[t] != 0;
+  uint32_t ns = 0, n48 = 0;
+  for (int64_t t = 0; t < T; t++) {
+    ns += tile_map[t] != 0;
+    n48 += tile_map[t] == 2;
+  }
   uint64_t data_off = round_up(256 + 16 * (uint64_t)T, 256);
   put32(out + 0, 0x48435450u);
   put32(out + 4, 3);
@@ -381,6 +408,7 @@ int oracle_pack(int dtype, int64_t N, int64_t K, const uint16_t* W, const uint8_
   put64(out + 48, data_off);
   put64(out + 56, total - data_off);
   put64(out + 64, total);
+  put32(out + 72, n48);
 
   uint64_t rb = data_off;  /* start of the current row-block */
   for (int64_t i = 0; i < NT; i++) {
@@ -391,7 +419,7 @@ int oracle_pack(int dtype, int64_t N, int64_t K, const uint16_t* W, const uint8_
       int64_t t = i * KT + j;
       int sparse = tile_map[t] != 0;
       put64(out + 256 + 16 * t, rb + prefix);
-      put32(out + 256 + 16 * t + 8, (uint32_t)sparse);
+      put32(out + 256 + 16 * t + 8, (uint32_t)tile_map[t]);
       put32(out + 256 + 16 * t + 12, (uint32_t)stride);
       for (int band = 0; band < 8; band++) {
         uint8_t* piece = out + rb + (uint64_t)band * stride + prefix;
@@ -405,6 +433,22 @@ int oracle_pack(int dtype, int64_t N, int64_t K, const uint16_t* W, const uint8_
                     int64_t col = j * PT_B + 64 * q + 16 * (l / 16) + 4 * g + 2 * e + u;
                     put16(piece + 2048 * q + 1024 * e + 16 * l + 2 * (2 * g + u), W[row * K + col]);
                   }
+        } else if (tile_map[t] == 2) {
+          for (int l = 0; l < 64; l++) {
+            int64_t row = i * PT_B + 16 * band + (l % 16);
+            for (int c = 0; c < 4; c++) {
+              int64_t c0 = j * PT_B + 32 * c + 8 * (l / 16);
+              int s = 0;
+              uint8_t bits = 0;
+              for (int p = 0; p < 8; p++)
+                if (mask[row * K + c0 + p]) {
+                  put16(piece + 1024 * (c / 2) + 16 * l + 8 * (c % 2) + 2 * s, W[row * K + c0 + p]);
+                  bits |= (uint8_t)(1u << p);
+                  s++;
+                }
+              piece[2048 + 4 * l + c] = bits;
+            }
+          }
         } else {
           for (int q = 0; q < 2; q++)
             for (int l = 0; l < 64; l++) {

@@ -276,3 +276,47 @@ def make_fine(dtype: str, N: int, K: int, b1: int, b2: int, seed: int, s_exec: f
     w = gen_w(rng, N, K, dtype)
     fmap = gen_fine_map(rng, N, K, b1, b2, s_exec, p_sub)
     return Problem(dtype, N, K, w, fmap, gen_mask_uniform(rng, N, K), {"seed": seed, "b1": b1, "b2": b2})
+
+
+# ---------------------------------------------------------------------------- 4:8 tiles
+ROLE_48 = 9
+KIND_DENSE, KIND_24, KIND_48 = 0, 1, 2
+
+
+def gen_mask_top4of8(w_bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Keep the four largest |w| of each group of eight along K (stored
+    values), ties toward the lower column."""
+    N, K = w_bits.shape
+    a = np.abs(bits_to_f32(w_bits, dtype)).reshape(N, K // 8, 8)
+    order = np.argsort(-a, axis=-1, kind="stable")
+    mask = np.zeros((N, K // 8, 8), dtype=np.uint8)
+    np.put_along_axis(mask, order[..., :4], 1, axis=-1)
+    return mask.reshape(N, K)
+
+
+def gen_mask_uniform48(rng: np.random.Generator, N: int, K: int) -> np.ndarray:
+    """One of the 70 patterns of four kept in eight per group, uniformly."""
+    keys = rng.random((N, K // 8, 8))
+    order = np.argsort(keys, axis=-1)
+    mask = np.zeros((N, K // 8, 8), dtype=np.uint8)
+    np.put_along_axis(mask, order[..., :4], 1, axis=-1)
+    return mask.reshape(N, K)
+
+
+def make_mixed(dtype: str, N: int, K: int, seed: int, frac24: float, frac48: float, mask_kind: str = "top") -> Problem:
+    """Tiles of all three kinds: each 128 x 128 tile 2:4 with probability
+    frac24, 4:8 with probability frac48, else dense; the mask keeps the top-2
+    of 4 (2:4 tiles) / top-4 of 8 (4:8 tiles) by |w|, or (mask_kind
+    "uniform") a uniformly drawn pattern."""
+    rng = rng_for(seed, 42, N, K, ROLE_48)
+    w = gen_w(rng, N, K, dtype)
+    NT, KT = N // TILE, K // TILE
+    u = rng.random((NT, KT))
+    tmap = np.where(u < frac24, KIND_24, np.where(u < frac24 + frac48, KIND_48, KIND_DENSE)).astype(np.uint8)
+    if mask_kind == "top":
+        m24, m48 = gen_mask_top2(w, dtype), gen_mask_top4of8(w, dtype)
+    else:
+        m24, m48 = gen_mask_uniform(rng, N, K), gen_mask_uniform48(rng, N, K)
+    sel48 = np.repeat(np.repeat(tmap == KIND_48, TILE, axis=0), TILE, axis=1)
+    mask = np.where(sel48, m48, m24).astype(np.uint8)
+    return Problem(dtype, N, K, w, tmap, mask, {"seed": seed, "frac24": frac24, "frac48": frac48})

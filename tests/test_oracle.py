@@ -326,6 +326,19 @@ def _unpack(blob, N, K):
                                     for u in range(2):
                                         c = j * 128 + 64 * q + 16 * (l // 16) + 4 * g + 2 * half + u
                                         W[r, c] = ch[q, half, l, 2 * g + u]
+                elif kind == 2:
+                    # 4:8: block q holds lane l's four kept values of slices 2q and 2q+1;
+                    # byte c of the lane's mask word: positions kept in slice c
+                    vals = piece[:2048].view(np.uint16).reshape(2, 64, 8)
+                    masks = piece[2048:2304].reshape(64, 4)
+                    for l in range(64):
+                        r = i * 128 + band * 16 + l % 16
+                        for c in range(4):
+                            m = int(masks[l, c])
+                            codes.append(m)
+                            kept = [pp for pp in range(8) if (m >> pp) & 1]
+                            for s_, pp in enumerate(kept[:4]):
+                                W[r, j * 128 + 32 * c + 8 * (l // 16) + pp] = vals[c // 2, l, 4 * (c % 2) + s_]
                 else:
                     vals = piece[:2048].view(np.uint16).reshape(2, 64, 8)
                     meta = piece[2048:2304].view(np.uint32)
@@ -635,3 +648,100 @@ def test_fine_policy_preserves_the_product(b1, b2):
     if (b1, b2) != (128, 128):
         # some dense execution tiles hold pruned (2:4) fine tiles
         assert (p.tile_map.sum() * b1 * b2) > em.sum() * 128 * 128
+
+
+
+# ---------------------------------------------------------------- 4:8 tiles (another N:M pattern)
+# gist.science explainer, section 5 "Significance", "Future Direction": the
+# framework is pattern-agnostic and extends to other N:M patterns, e.g. 4:8.
+def test_pack_48_hand_worked_example():
+    g = _golden("pack_48_example.txt")
+    N = K = 128
+    W = np.full((N, K), 0x3F80, np.uint16)
+    W[g["value.row"], g["value.col"]] = g["value.bits"]
+    mask = np.zeros((N, K), np.uint8)
+    for p in range(4):
+        mask[:, p::8] = 1
+    mask[37, 72:80] = [0, 1, 0, 0, 1, 1, 0, 1]
+    blob = oracle.pack("bf16", W, np.array([[2]], np.uint8), mask)
+    u64 = lambda o: int.from_bytes(blob[o:o + 8].tobytes(), "little")
+    u32 = lambda o: int.from_bytes(blob[o:o + 4].tobytes(), "little")
+    u16 = lambda o: int.from_bytes(blob[o:o + 2].tobytes(), "little")
+    assert blob.size == g["header.total_bytes"] and u64(64) == g["header.total_bytes"]
+    assert u32(36) == g["header.n_sparse"] and u32(72) == g["header.n_48"]
+    assert (u64(256), u32(264), u32(268)) == (g["table.0.offset"], g["table.0.kind"], g["table.0.stride"])
+    assert u16(g["value.byte_offset"]) == g["value.bits"]
+    assert u16(g["value0.byte_offset"]) == g["value0.bits"]
+    assert blob[g["mask.byte_offset"]] == g["mask.value"]
+    assert blob[g["mask0.byte_offset"]] == g["mask0.value"]
+
+
+@pytest.mark.parametrize("mask_kind", ["top", "uniform"])
+def test_pack_mixed_kinds_round_trip(mask_kind):
+    """Dense, 2:4 and 4:8 tiles in one blob: unpack(pack(W)) == W o E
+    bit-exactly; every 4:8 mask byte keeps exactly four positions; sizes as
+    the closed form (a 4:8 tile takes as many bytes as a 2:4 one)."""
+    p = inputs.make_mixed("bf16", 384, 640, 14, 0.35, 0.35, mask_kind)
+    assert set(np.unique(p.tile_map)) == {0, 1, 2}
+    blob = oracle.pack("bf16", p.w, p.tile_map, p.mask)
+    T, ns = p.tile_map.size, int((p.tile_map != 0).sum())
+    assert blob.size == -(-(256 + 16 * T) // 256) * 256 + 32768 * (T - ns) + 18432 * ns
+    W2, _ = _unpack(blob, p.N, p.K)
+    E = oracle.effective_mask(p.N, p.K, p.tile_map, p.mask)
+    assert np.array_equal(W2, np.where(E != 0, p.w, 0).astype(np.uint16))
+    tiles48 = np.repeat(np.repeat(p.tile_map == 2, 128, 0), 128, 1)
+    assert np.all(p.mask[tiles48].reshape(-1, 8).sum(axis=1) == 4)
+    # sparsity: half of every 2:4 and 4:8 tile
+    assert (E == 0).sum() * 2 == ns * 128 * 128
+
+
+def test_validate_48_groups():
+    """A 4:8 tile's group keeping 3 or 5 of 8 is an error; map bytes other
+    than 0, 1, 2 are rejected; a 4:8 group need not be 2:4 within it."""
+    N = K = 128
+    W = np.zeros((N, K), np.uint16)
+    mask = np.zeros((N, K), np.uint8)
+    mask[:, 0:4] = 1  # positions 0..3 of the first group: 4 of 8, not 2 of 4 in each half
+    for p in range(4):
+        mask[:, p::8] = 1
+    assert oracle.validate(N, K, np.array([[2]], np.uint8), mask) is None
+    assert oracle.validate(N, K, np.array([[1]], np.uint8), mask) == (0, 0)  # as 2:4: 4 of 4 kept
+    for bad in (3, 5):
+        m = mask.copy()
+        m[9, 16:24] = 0
+        m[9, 16:16 + bad] = 1
+        assert oracle.validate(N, K, np.array([[2]], np.uint8), m) == (9, 2)
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.validate(N, K, np.array([[3]], np.uint8), mask)
+    assert e.value.code == 1
+
+
+def test_gemm_48_brute_force_tiny():
+    """16 x 16 weight with 8 x 8 tiles of all kinds, small integers: the GEMM
+    equals a second formulation that sums only the kept positions of each
+    group (exact in binary64)."""
+    rng = np.random.default_rng(21)
+    N = K = 16
+    M = 5
+    for tmap in (np.array([[2, 0], [1, 2]], np.uint8), np.array([[2, 2], [2, 2]], np.uint8)):
+        Wv = rng.integers(-3, 4, (N, K)).astype(np.float64)
+        Xv = rng.integers(-3, 4, (M, K)).astype(np.float64)
+        W, X = inputs.to_bits(Wv, "f16"), inputs.to_bits(Xv, "f16")
+        mask = np.zeros((N, K), np.uint8)
+        for n in range(N):
+            for g in range(K // 8):
+                mask[n, 8 * g + rng.permutation(8)[:4]] = 1
+            for g in range(K // 4):
+                blk = mask[n, 4 * g:4 * g + 4]
+                if tmap[n // 8, (4 * g) // 8] == 1:
+                    blk[:] = 0
+                    blk[rng.permutation(4)[:2]] = 1
+        Y = oracle.gemm_f64("f16", X, W, tmap, mask, tile_n=8, tile_k=8)
+        ref = np.zeros((M, N))
+        for m in range(M):
+            for n in range(N):
+                for k in range(K):
+                    kind = tmap[n // 8, k // 8]
+                    if kind == 0 or mask[n, k]:
+                        ref[m, n] += Xv[m, k] * Wv[n, k]
+        assert np.array_equal(Y, ref)
