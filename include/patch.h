@@ -62,7 +62,9 @@ typedef enum {
                                 the GPU and the workspace allows */
   /* The prefill kernel at one M-block width and staging (K split as its
    * cost model decides for that width, within the workspace passed): for
-   * tests and measurements that must run every kernel on the same shapes. */
+   * tests and measurements that must run every kernel on the same shapes;
+   * the register-staged ones run dense and 2:4 tiles only (a blob with 4:8
+   * tiles: PATCH_ERR_UNSUPPORTED). */
   PATCH_VARIANT_PREFILL_W64 = 3,      /* registers, 64 columns of M a workgroup */
   PATCH_VARIANT_PREFILL_W128 = 4,     /* registers, 128 */
   PATCH_VARIANT_PREFILL_W192 = 5,     /* registers, 192 */
@@ -82,7 +84,8 @@ typedef struct {
   uint32_t N, K;      /* matrix shape */
   uint32_t nt_n;      /* N / 128 */
   uint32_t nt_k;      /* K / 128 */
-  uint32_t n_sparse;  /* number of 2:4 tiles */
+  uint32_t n_sparse;  /* number of compressed (2:4 and 4:8) tiles */
+  uint32_t n_48;      /* number of 4:8 tiles among them (header byte 72) */
   uint64_t table_offset; /* 256 */
   uint64_t data_offset;  /* round_up(256 + 16 * nt_n * nt_k, 256) */
   uint64_t total_bytes;  /* size of the whole blob */
@@ -95,9 +98,10 @@ int32_t patch_abi_version(void);
  * Size in bytes of the packed blob for a tile map (PATCH "tile-level
  * assignment", gist.science explainer, section 2 "Core Mechanism"):
  *   round_up(256 + 16*T, 256) + 32768 * n_dense + 18432 * n_sparse,
- * T = (N/128)*(K/128).  tile_map_host: T bytes, row-block-major (tile (i, j)
- * at i*(K/128) + j), nonzero = 2:4 sparse.  Returns 0 if the arguments are
- * invalid (dtype, shape, null map).
+ * T = (N/128)*(K/128), n_sparse the 2:4 and 4:8 tiles.  tile_map_host: T
+ * bytes, row-block-major (tile (i, j) at i*(K/128) + j): 0 dense, 1 2:4,
+ * 2 4:8.  Returns 0 if the arguments are invalid (dtype, shape, null map, a
+ * map byte above 2).
  */
 uint64_t patch_packed_bytes(patch_dtype dtype, int64_t N, int64_t K, const uint8_t* tile_map_host);
 
@@ -117,14 +121,25 @@ uint64_t patch_packed_bytes(patch_dtype dtype, int64_t N, int64_t K, const uint8
  * fixed code).  The 2:4 rule: gist.science explainer, section 1 "Problem
  * Statement"; the six patterns: section 2 "Pattern Selection".
  *
+ * A 4:8 tile (another N:M pattern, explainer section 5 "Significance",
+ * "Future Direction") keeps four of every eight consecutive weights along K:
+ * per band piece (2304 bytes, as a 2:4 one) each lane holds, for each
+ * 32-column slice, the four kept values of its group of eight and an 8-bit
+ * mask of their positions -- the group it holds of the dense 16x16x32
+ * matrix instruction's operand, which the GEMM kernels rebuild in
+ * registers: 4:8 tiles take a 2:4 tile's bytes and a dense tile's
+ * matrix-core time.
+ *
  *   W_dev          N x K elements of `dtype`, row-major, device.
- *   tile_map_host  T bytes on the host, nonzero = sparse tile.
+ *   tile_map_host  T bytes on the host: 0 dense, 1 2:4, 2 4:8 (other
+ *                  values: PATCH_ERR_INVALID_ARG).
  *   mask_dev       N x K bytes on the device, nonzero = keep.  Read only
- *                  inside sparse tiles (ignored in dense tiles).
+ *                  inside 2:4 and 4:8 tiles (ignored in dense tiles).
  *   packed_dev     output, device, at least patch_packed_bytes() bytes.
  *   desc_out       host descriptor of the result (written on success only).
  *
- * Synchronises `stream` (to report PATCH_ERR_MASK).  On PATCH_ERR_MASK the
+ * Synchronises `stream` (to report PATCH_ERR_MASK: a 2:4 group not keeping
+ * two of four, or a 4:8 group not keeping four of eight).  On PATCH_ERR_MASK the
  * blob contents are undefined.  The blob is immutable afterwards and may be
  * shared by any number of concurrent GEMM calls.
  */

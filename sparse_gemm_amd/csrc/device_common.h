@@ -107,6 +107,24 @@ __device__ __forceinline__ f32x4 silu_mul(f32x4 g, f32x4 u) {
   return h;
 }
 
+// A 4:8 group (four of eight consecutive weights kept): its four kept 16-bit
+// values in ascending column order (v01 = values 0 and 1, v23 = values 2
+// and 3) and the 8-bit mask m of their positions -> the group's eight
+// elements with zeros at the dropped positions, i.e. the 16-byte A chunk a
+// lane holds of v_mfma_f32_16x16x32 (row l % 16, K 8*(l/16) .. +7).  Kept
+// position p takes the lowest value not yet placed.
+__device__ __forceinline__ u32x4 expand48(uint32_t v01, uint32_t v23, uint32_t m) {
+  uint64_t q = (uint64_t)v01 | ((uint64_t)v23 << 32);
+  uint32_t e[8];
+#pragma unroll
+  for (int p = 0; p < 8; p++) {
+    const bool kept = (m >> p) & 1u;
+    e[p] = kept ? (uint32_t)(q & 0xffffu) : 0u;
+    q = kept ? (q >> 16) : q;
+  }
+  return (u32x4){e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+}
+
 struct TileEntry {
   uint64_t offset;       // byte offset of the tile's band-0 piece from the blob start
   uint32_t kind;         // 0 dense, 1 sparse

@@ -37,7 +37,9 @@ namespace patch {
 //           the row-major chunk of columns 32c + 8*(l/16) (dense baseline);
 //   sparse: a[0], a[1] = value fragments of slices 0 and 1, a[2] = the
 //           16 bytes of the band's codes holding this lane's word (word l & 3),
-//           a[3] = the same chunk again (unused).
+//           a[3] = the same chunk again (unused); 4:8 tiles alike, the
+//           fragments holding the four kept values per 32-column group and
+//           the word its four 8-bit position masks.
 template <int MB>
 struct DecodeFrag {
   u32x4 x[MB][4];  // B operand chunks of M block mb: X[16mb + m][k0 + 32c + 8h .. +7], c = 0..3
@@ -107,6 +109,19 @@ __device__ __forceinline__ void decode_mma(const DecodeFrag<MB>& f, f32x4 (&acc)
     const u32x4 mc = f.a[2];
     const uint32_t lo = (l & 1) ? mc[1] : mc[0], hi = (l & 1) ? mc[3] : mc[2];
     const uint32_t meta = (l & 2) ? hi : lo;
+    if (f.kind == 2) {
+      // 4:8: rebuild the lane's group of each 32-column slice c (values in
+      // a[c / 2], words 2(c % 2) and 2(c % 2) + 1; mask = byte c of the word)
+      // and run the dense instruction on it
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        const u32x4 v = f.a[c >> 1];
+        const u32x4 A = expand48(v[2 * (c & 1)], v[2 * (c & 1) + 1], (meta >> (8 * c)) & 0xffu);
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++) acc[mb] = mma_dense<BF16>(A, f.x[mb][c], acc[mb]);
+      }
+      return;
+    }
 #pragma unroll
     for (int mb = 0; mb < MB; mb++) {
       // slice 0: logical K 0..63 of the tile -> B chunks 0 (K 8h..) and 1 (K 32+8h..)

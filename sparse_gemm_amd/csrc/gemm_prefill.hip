@@ -150,7 +150,8 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
   __shared__ __attribute__((aligned(16))) uint8_t s_x0[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_x1[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_x2[DIST == 2 ? kStageBytes : 16];
-  // per row-block of the pair and tile column: (byte offset >> 8) | kind << 31
+  // per row-block of the pair and tile column: (byte offset >> 8) | kind << 30
+  // (kind 0 dense, 1 2:4, 2 4:8; blobs stay below 2^38 bytes)
   __shared__ uint32_t s_ent[2][kPfMaxKT];
   __shared__ uint32_t s_stride[2];  // band stride of each row-block of the pair
 
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
       const int rr = e >= nt ? 1 : 0;
       const int j = e - rr * nt;
       const TileEntry te = table[(int64_t)(rr ? i1 : i0) * KT + j0 + j];
-      s_ent[rr][j] = (uint32_t)(te.offset >> 8) | (te.kind ? 0x80000000u : 0u);
+      s_ent[rr][j] = (uint32_t)(te.offset >> 8) | (te.kind << 30);
       if (j == 0) s_stride[rr] = te.band_stride;
     }
     __syncthreads();
@@ -217,14 +218,16 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
       return 0u;
     } else {
       const uint32_t e = __builtin_amdgcn_readfirstlane(s_ent[r][jl]);
-      const uint32_t kind = e >> 31;
+      const uint32_t kind = e >> 30;
       // the wave's first band piece; band 4wn+b is b * stride further on
-      const uint8_t* piece = P.src + ((uint64_t)(e & 0x7fffffffu) << 8) + (uint64_t)(4 * wn) * stride;
+      const uint8_t* piece = P.src + ((uint64_t)(e & 0x3fffffffu) << 8) + (uint64_t)(4 * wn) * stride;
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(piece, 3u * stride + (uint32_t)kDensePieceBytes);
       // dense: a[e][b] = half e of band 4wn+b in 64-column slice h, at
       //        2048h + 1024e in its piece;
       // 2:4  : a[0][b] = values of band 4wn+b in slice h, at 1024h;
       //        a[1][b] = its codes chunk 16 * (l/4) past the values.
+      // (This kernel runs dense and 2:4 tiles only; the host routes blobs
+      // with 4:8 tiles to k_prefill_lds.)
       const uint32_t v1 = kind ? 16u * (uint32_t)(l >> 2) : lane16;
       const uint32_t o0 = kind ? 1024u * (uint32_t)h : 2048u * (uint32_t)h;
       const uint32_t o1 = kind ? (uint32_t)kSparseMetaOffset : 2048u * (uint32_t)h + 1024u;
@@ -538,7 +541,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
       const int rr = e >= nt ? 1 : 0;
       const int j = e - rr * nt;
       const TileEntry te = table[(int64_t)(rr ? i1 : i0) * KT + j0 + j];
-      s_ent[rr][j] = (uint32_t)(te.offset >> 8) | (te.kind ? 0x80000000u : 0u);
+      s_ent[rr][j] = (uint32_t)(te.offset >> 8) | (te.kind << 30);
       if (j == 0) s_stride[rr] = te.band_stride;
     }
     __syncthreads();
@@ -578,8 +581,8 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
       for (int b = 0; b < 4; b++) dma16(W + (int64_t)16 * b * K, slot0 + 2048u * b + 1024u * wm);
     } else {
       const uint32_t e = __builtin_amdgcn_readfirstlane(s_ent[r_src][jl]);
-      const uint8_t* piece = P.src + ((uint64_t)(e & 0x7fffffffu) << 8) + (uint64_t)(4 * wn) * stride;
-      if ((e >> 31) == 0) {
+      const uint8_t* piece = P.src + ((uint64_t)(e & 0x3fffffffu) << 8) + (uint64_t)(4 * wn) * stride;
+      if ((e >> 30) == 0) {
 #pragma unroll
         for (int b = 0; b < 4; b++)
           dma16(piece + (uint64_t)b * stride + 2048 * h + 1024 * wm + 16 * l, slot0 + 2048u * b + 1024u * wm);
@@ -617,7 +620,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
     const uint8_t* ws = s_w + st * kLdsWStage + 1024 * ((r * 8 + 4 * wn) * 2);
     const uint8_t* xs = s_x + st * kLdsXStage;
     uint32_t kind = 0;
-    if constexpr (!SRC_ROWMAJOR) kind = __builtin_amdgcn_readfirstlane(s_ent[r_src][jl]) >> 31;
+    if constexpr (!SRC_ROWMAJOR) kind = (uint32_t)__builtin_amdgcn_readfirstlane((int)s_ent[r_src][jl]) >> 30;
     u32x4 a0[4], a1[4];
     const int off1 = kind ? 16 * (l >> 2) : 16 * l;
 #pragma unroll
@@ -637,6 +640,32 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
         for (int mblk = 0; mblk < kNMB; mblk++)
 #pragma unroll
           for (int b = 0; b < 4; b++) acc[b][mblk] = mma_dense<BF16>(qq ? a1[b] : a0[b], bf[mblk], acc[b][mblk]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if (kind == 2) {
+      // 4:8: groups of eight rebuilt in registers (slices 2h, 2h+1), dense
+      // instruction with the B fragments of K 8hl.. and 32+8hl..
+      u32x4 a_lo[4], a_hi[4];
+#pragma unroll
+      for (int b = 0; b < 4; b++) {
+        const u32x4 mc = a1[b], v = a0[b];
+        const uint32_t lo = (l & 1) ? mc[1] : mc[0], hi = (l & 1) ? mc[3] : mc[2];
+        const uint32_t meta = ((l & 2) ? hi : lo) >> (16 * h);
+        a_lo[b] = expand48(v[0], v[1], meta & 0xffu);
+        a_hi[b] = expand48(v[2], v[3], (meta >> 8) & 0xffu);
+      }
+      constexpr int kGroups = kNMB / kPfMGroup;
+#pragma unroll
+      for (int g = 0; g < kGroups; g++) {
+        u32x4 blo[kPfMGroup], bhi[kPfMGroup];
+        read_b(xs, g, blo, bhi);
+#pragma unroll
+        for (int mm = 0; mm < kPfMGroup; mm++)
+#pragma unroll
+          for (int b = 0; b < 4; b++) {
+            acc[b][kPfMGroup * g + mm] = mma_dense<BF16>(a_lo[b], blo[mm], acc[b][kPfMGroup * g + mm]);
+            acc[b][kPfMGroup * g + mm] = mma_dense<BF16>(a_hi[b], bhi[mm], acc[b][kPfMGroup * g + mm]);
+          }
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {

@@ -44,6 +44,8 @@ constexpr int64_t kDecodeMaxK = 65536;        // decode kernel: <= 64 tile colum
 constexpr int64_t kDecodeMaxM = 128;          // decode kernel: <= 8 blocks of 16 columns of M
 constexpr int64_t kDecodeAutoM = 16;          // AUTO: always decode up to here
 constexpr uint64_t kErrFlagOffset = 252;
+// the prefill kernels keep a tile's piece offset / 256 in 30 bits
+constexpr uint64_t kMaxBlobBytes = uint64_t(1) << 38;
 
 thread_local std::string g_err;
 
@@ -93,10 +95,14 @@ patch_status check_desc(const patch_packed_desc* d) {
   patch_status s = check_nk(d->N, d->K);
   if (s) return s;
   const uint64_t T = (uint64_t)d->nt_n * d->nt_k;
-  if (d->nt_n != d->N / kTile || d->nt_k != d->K / kTile || d->n_sparse > T || d->table_offset != 256 ||
+  if (d->nt_n != d->N / kTile || d->nt_k != d->K / kTile || d->n_sparse > T || d->n_48 > d->n_sparse ||
+      d->table_offset != 256 ||
       d->data_offset != round_up(256 + 16 * T, 256) ||
       d->total_bytes != d->data_offset + kDenseBytes * (T - d->n_sparse) + kSparseBytes * d->n_sparse)
     return fail(PATCH_ERR_INVALID_ARG, "inconsistent descriptor");
+  if (d->total_bytes >= kMaxBlobBytes)
+    return fail(PATCH_ERR_UNSUPPORTED, "blob of %llu bytes exceeds the supported %llu",
+                (unsigned long long)d->total_bytes, (unsigned long long)kMaxBlobBytes);
   return PATCH_OK;
 }
 
@@ -107,7 +113,7 @@ void put64(uint8_t* p, uint64_t v) { std::memcpy(p, &v, 8); }
 
 extern "C" {
 
-int32_t patch_abi_version(void) { return 3; }
+int32_t patch_abi_version(void) { return 4; }
 
 patch_status patch_sample_mask(int64_t N, int64_t K, const float* tile_logits_dev, const float* tile_u_dev,
                                const float* pat_logits_dev, const float* pat_u_dev, float tau, uint8_t* tile_map_dev,
@@ -199,7 +205,10 @@ uint64_t patch_packed_bytes(patch_dtype dtype, int64_t N, int64_t K, const uint8
   if (check_dtype(dtype) || check_nk(N, K) || !tile_map_host) return 0;
   const int64_t T = (N / kTile) * (K / kTile);
   uint64_t ns = 0;
-  for (int64_t t = 0; t < T; t++) ns += tile_map_host[t] != 0;
+  for (int64_t t = 0; t < T; t++) {
+    if (tile_map_host[t] > 2) return 0;  // 0 dense, 1 2:4, 2 4:8
+    ns += tile_map_host[t] != 0;
+  }
   return round_up(256 + 16 * (uint64_t)T, 256) + kDenseBytes * (uint64_t)(T - (int64_t)ns) + kSparseBytes * ns;
 }
 
@@ -221,7 +230,12 @@ static patch_status pack_common(patch_dtype dtype, int64_t N, int64_t K, const p
   }
   if (!aligned16(packed_dev)) return fail(PATCH_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
   const int64_t NT = N / kTile, KT = K / kTile, T = NT * KT;
+  for (int64_t t = 0; t < T; t++)
+    if (tile_map_host[t] > 2)
+      return fail(PATCH_ERR_INVALID_ARG, "tile map byte %d at tile %lld (0 dense, 1 2:4, 2 4:8)", (int)tile_map_host[t],
+                  (long long)t);
   const uint64_t need = patch_packed_bytes(dtype, N, K, tile_map_host);
+  if (need >= kMaxBlobBytes) return fail(PATCH_ERR_UNSUPPORTED, "blob of %llu bytes too large", (unsigned long long)need);
   if (packed_bytes < need)
     return fail(PATCH_ERR_BUFFER_TOO_SMALL, "packed buffer %llu < %llu bytes", (unsigned long long)packed_bytes,
                 (unsigned long long)need);
@@ -232,7 +246,7 @@ static patch_status pack_common(patch_dtype dtype, int64_t N, int64_t K, const p
   // Row-block i: 8 bands of S_i bytes, band b holding its piece of every
   // tile in order; an entry holds the offset of the tile's band-0 piece, its
   // kind and S_i.
-  uint32_t ns = 0;
+  uint32_t ns = 0, n48 = 0;
   uint64_t rb = data_off;
   for (int64_t i = 0; i < NT; i++) {
     uint64_t stride = 0;
@@ -240,12 +254,13 @@ static patch_status pack_common(patch_dtype dtype, int64_t N, int64_t K, const p
     uint64_t prefix = 0;
     for (int64_t j = 0; j < KT; j++) {
       const int64_t t = i * KT + j;
-      const uint32_t kind = tile_map_host[t] != 0;
+      const uint32_t kind = tile_map_host[t];  // 0 dense, 1 2:4, 2 4:8
       put64(&head[256 + 16 * t], rb + prefix);
       put32(&head[256 + 16 * t + 8], kind);
       put32(&head[256 + 16 * t + 12], (uint32_t)stride);
       prefix += kind ? kSparsePiece : kDensePiece;
-      ns += kind;
+      ns += kind != 0;
+      n48 += kind == 2;
     }
     rb += 8 * stride;
   }
@@ -263,6 +278,7 @@ static patch_status pack_common(patch_dtype dtype, int64_t N, int64_t K, const p
   put64(&head[48], data_off);
   put64(&head[56], need - data_off);
   put64(&head[64], need);
+  put32(&head[72], n48);
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipMemcpyAsync(packed_dev, head.data(), head.size(), hipMemcpyHostToDevice, st);
@@ -274,7 +290,9 @@ static patch_status pack_common(patch_dtype dtype, int64_t N, int64_t K, const p
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(flag)");
   e = hipStreamSynchronize(st);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-  if (flag) return fail(PATCH_ERR_MASK, "a group of four inside a sparse tile does not keep exactly two weights");
+  if (flag)
+    return fail(PATCH_ERR_MASK,
+                "a group inside a 2:4 (4:8) tile does not keep exactly two of four (four of eight) weights");
 
   patch_packed_desc d;
   d.version = kVersion;
@@ -285,6 +303,7 @@ static patch_status pack_common(patch_dtype dtype, int64_t N, int64_t K, const p
   d.nt_n = (uint32_t)NT;
   d.nt_k = (uint32_t)KT;
   d.n_sparse = ns;
+  d.n_48 = n48;
   d.table_offset = 256;
   d.data_offset = data_off;
   d.total_bytes = need;
@@ -411,6 +430,7 @@ patch_status patch_desc_from_header(const void* header_host, uint64_t header_byt
   d.nt_n = u[7];
   d.nt_k = u[8];
   d.n_sparse = u[9];
+  std::memcpy(&d.n_48, h + 72, 4);
   d.table_offset = v[0];
   d.data_offset = v[1];
   d.total_bytes = v[3];
@@ -440,12 +460,15 @@ uint64_t patch_dense_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) { ret
 // Y is then H, M x F.
 static patch_status gemm_common(bool rowmajor, patch_dtype dt, int64_t M, int64_t N, int64_t K, const void* src,
                                 const void* src2, uint64_t w_bytes, const void* X_dev, void* Y_dev,
-                                patch_dtype y_dtype, void* ws, uint64_t ws_bytes, int32_t variant, void* stream) {
+                                patch_dtype y_dtype, void* ws, uint64_t ws_bytes, int32_t variant, void* stream,
+                                bool has48 = false) {
   patch_status s;
   if ((s = check_ydtype(dt, y_dtype))) return s;
   if (M < 0 || M > (int64_t)0x7fffffff) return fail(PATCH_ERR_INVALID_ARG, "M=%lld out of range", (long long)M);
   if (variant < PATCH_VARIANT_AUTO || variant > PATCH_VARIANT_PREFILL_W64_LDS)
     return fail(PATCH_ERR_INVALID_ARG, "unknown variant %d", (int)variant);
+  if (has48 && variant >= PATCH_VARIANT_PREFILL_W64 && variant <= PATCH_VARIANT_PREFILL_W256)
+    return fail(PATCH_ERR_UNSUPPORTED, "the register-staged prefill variants run dense and 2:4 tiles only");
   if (variant == PATCH_VARIANT_DECODE && M > kDecodeMaxM)
     return fail(PATCH_ERR_INVALID_ARG, "decode variant needs M <= %lld (M=%lld)", (long long)kDecodeMaxM, (long long)M);
   if (M == 0) return PATCH_OK;
@@ -487,7 +510,7 @@ patch_status patch_gemm_ex(const patch_packed_desc* desc, const void* packed_dev
   if (s) return s;
   return gemm_common(false, (patch_dtype)desc->dtype, M, desc->N, desc->K, packed_dev, nullptr,
                      desc->total_bytes - desc->data_offset, X_dev, Y_dev, y_dtype, workspace_dev, workspace_bytes,
-                     variant, stream);
+                     variant, stream, desc->n_48 > 0);
 }
 
 patch_status patch_gemm(const patch_packed_desc* desc, const void* packed_dev, const void* X_dev, int64_t M,
@@ -532,7 +555,7 @@ patch_status patch_gemm_swiglu(const patch_packed_desc* desc, const void* packed
   if (desc->nt_n % 2) return fail(PATCH_ERR_SHAPE, "a gate/up blob has an even number of row-blocks");
   return gemm_common(false, (patch_dtype)desc->dtype, M, desc->N, desc->K, packed_dev, packed_dev,
                      desc->total_bytes - desc->data_offset, X_dev, H_dev, h_dtype, workspace_dev, workspace_bytes,
-                     variant, stream);
+                     variant, stream, desc->n_48 > 0);
 }
 
 patch_status patch_dense_gemm_swiglu(patch_dtype dtype, int64_t M, int64_t F, int64_t K, const void* X_dev,

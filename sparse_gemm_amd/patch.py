@@ -40,7 +40,7 @@ class Desc(ctypes.Structure):
     _fields_ = [("version", ctypes.c_uint32), ("dtype", ctypes.c_uint32), ("tile_n", ctypes.c_uint32),
                 ("tile_k", ctypes.c_uint32), ("N", ctypes.c_uint32), ("K", ctypes.c_uint32),
                 ("nt_n", ctypes.c_uint32), ("nt_k", ctypes.c_uint32), ("n_sparse", ctypes.c_uint32),
-                ("table_offset", ctypes.c_uint64), ("data_offset", ctypes.c_uint64),
+                ("n_48", ctypes.c_uint32), ("table_offset", ctypes.c_uint64), ("data_offset", ctypes.c_uint64),
                 ("total_bytes", ctypes.c_uint64)]
 
 
@@ -177,14 +177,18 @@ def packed_bytes(dtype: torch.dtype, N: int, K: int, tile_map) -> int:
 
 
 def pack(W: torch.Tensor, tile_map, mask: torch.Tensor, out: Optional[torch.Tensor] = None) -> PackedWeight:
-    """Pack W (N x K, f16/bf16, device), a host tile map (nonzero = 2:4 tile)
-    and a device byte mask (nonzero = keep) into a blob (patch_pack)."""
+    """Pack W (N x K, f16/bf16, device), a host tile map (0 dense, 1 2:4,
+    2 4:8) and a device byte mask (nonzero = keep) into a blob (patch_pack)."""
     lib = load()
     N, K = W.shape
     tm = _host_map(tile_map)
     nbytes = packed_bytes(W.dtype, N, K, tm)
     if nbytes == 0:
-        raise PatchError(2, f"invalid shape/dtype for pack: {tuple(W.shape)} {W.dtype}")
+        # let the library name what is wrong (it checks before the buffer size)
+        probe = torch.empty(16, dtype=torch.uint8, device=W.device)
+        _check(lib.patch_pack(_dt(W.dtype), N, K, _ptr(W), tm.ctypes.data_as(ctypes.c_void_p), _ptr(mask),
+                              _ptr(probe), 0, ctypes.byref(Desc()), _stream()))
+        raise PatchError(2, f"invalid arguments for pack: {tuple(W.shape)} {W.dtype}")
     if out is None:
         out = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
     desc = Desc()

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(patch.EXPORTS)
-    assert patch.load().patch_abi_version() == 3
+    assert patch.load().patch_abi_version() == 4
 
 
 def test_packed_bytes_matches_oracle_closed_form():
