@@ -330,16 +330,16 @@ void oracle_round_f64(int dtype, int64_t n, const double* in, uint16_t* out) {
  *   2*g + u (u = 0, 1) is column 64*q + 16*h + 4*g + 2*e + u.  (Each half is
  *   a 2:4 operand with the fixed pattern (0,1) or (2,3), so a dense tile runs
  *   on the same sparse matrix instruction as a 2:4 tile.)
- * 4:8 piece (2304 bytes, like a 2:4 one): the tile's columns form four
- *   32-column slices c = 0..3; lane l owns, in slice c, the group of eight
- *   columns 32*c + 8*h .. +7 of row 16*band + r.  Values: block q (q = 0, 1)
- *   at byte 1024*q; lane l's 16 bytes at 1024*q + 16*l hold the four kept
- *   elements (ascending column) of its group in slice 2*q, then the four of
- *   its group in slice 2*q + 1.  Masks at byte 2048: a u32 per lane at
- *   2048 + 4*l whose byte c has bit p set iff column 32*c + 8*h + p of the
- *   row is kept.  (Lane l's group of a slice is exactly the eight elements
- *   that lane holds of the A operand of v_mfma_f32_16x16x32, so a kernel can
- *   rebuild the dense operand from them without moving data between lanes.)
+ * 4:8 piece (2304 bytes, like a 2:4 one): lane l owns, in 64-column slice
+ *   q (q = 0, 1), columns 64*q + 16*h .. +15 of row 16*band + r -- two
+ *   groups of eight, u = 0 (columns 64*q + 16*h + 0..7) and u = 1 (+8..15).
+ *   Values: block q at byte 1024*q; lane l's 16 bytes at 1024*q + 16*l hold
+ *   the four kept elements (ascending column) of group u = 0, then the four
+ *   of group u = 1.  Masks at byte 2048: a u32 per lane at 2048 + 4*l whose
+ *   byte 2*q + u has bit p set iff column 64*q + 16*h + 8*u + p of the row
+ *   is kept.  (Lane l's sixteen columns are those it holds of a dense
+ *   piece's two halves, so a kernel rebuilds a dense tile's operands from
+ *   them without moving data between lanes.)
  * Sparse (2:4) piece: groups of four columns g = 0..31 (columns 4g..4g+3).
  *   Values: block q (q = 0, 1) at byte 1024*q; lane l holds, for p = 0..3
  *   and group g = 16*q + 4*h + p, the two kept elements of row 16*band + r in
@@ -436,18 +436,19 @@ int oracle_pack(int dtype, int64_t N, int64_t K, const uint16_t* W, const uint8_
         } else if (tile_map[t] == 2) {
           for (int l = 0; l < 64; l++) {
             int64_t row = i * PT_B + 16 * band + (l % 16);
-            for (int c = 0; c < 4; c++) {
-              int64_t c0 = j * PT_B + 32 * c + 8 * (l / 16);
-              int s = 0;
-              uint8_t bits = 0;
-              for (int p = 0; p < 8; p++)
-                if (mask[row * K + c0 + p]) {
-                  put16(piece + 1024 * (c / 2) + 16 * l + 8 * (c % 2) + 2 * s, W[row * K + c0 + p]);
-                  bits |= (uint8_t)(1u << p);
-                  s++;
-                }
-              piece[2048 + 4 * l + c] = bits;
-            }
+            for (int q = 0; q < 2; q++)
+              for (int u = 0; u < 2; u++) {
+                int64_t c0 = j * PT_B + 64 * q + 16 * (l / 16) + 8 * u;
+                int s = 0;
+                uint8_t bits = 0;
+                for (int p = 0; p < 8; p++)
+                  if (mask[row * K + c0 + p]) {
+                    put16(piece + 1024 * q + 16 * l + 8 * u + 2 * s, W[row * K + c0 + p]);
+                    bits |= (uint8_t)(1u << p);
+                    s++;
+                  }
+                piece[2048 + 4 * l + 2 * q + u] = bits;
+              }
           }
         } else {
           for (int q = 0; q < 2; q++)

@@ -327,18 +327,20 @@ def _unpack(blob, N, K):
                                         c = j * 128 + 64 * q + 16 * (l // 16) + 4 * g + 2 * half + u
                                         W[r, c] = ch[q, half, l, 2 * g + u]
                 elif kind == 2:
-                    # 4:8: block q holds lane l's four kept values of slices 2q and 2q+1;
-                    # byte c of the lane's mask word: positions kept in slice c
+                    # 4:8: block q holds lane l's four kept values of its groups u = 0, 1
+                    # (columns 64q + 16(l/16) + 8u ..); byte 2q + u of the lane's mask
+                    # word: positions kept in that group
                     vals = piece[:2048].view(np.uint16).reshape(2, 64, 8)
                     masks = piece[2048:2304].reshape(64, 4)
                     for l in range(64):
                         r = i * 128 + band * 16 + l % 16
-                        for c in range(4):
-                            m = int(masks[l, c])
-                            codes.append(m)
-                            kept = [pp for pp in range(8) if (m >> pp) & 1]
-                            for s_, pp in enumerate(kept[:4]):
-                                W[r, j * 128 + 32 * c + 8 * (l // 16) + pp] = vals[c // 2, l, 4 * (c % 2) + s_]
+                        for q in range(2):
+                            for u in range(2):
+                                m = int(masks[l, 2 * q + u])
+                                codes.append(m)
+                                kept = [pp for pp in range(8) if (m >> pp) & 1]
+                                for s_, pp in enumerate(kept[:4]):
+                                    W[r, j * 128 + 64 * q + 16 * (l // 16) + 8 * u + pp] = vals[q, l, 4 * u + s_]
                 else:
                     vals = piece[:2048].view(np.uint16).reshape(2, 64, 8)
                     meta = piece[2048:2304].view(np.uint32)
