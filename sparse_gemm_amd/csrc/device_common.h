@@ -107,22 +107,46 @@ __device__ __forceinline__ f32x4 silu_mul(f32x4 g, f32x4 u) {
   return h;
 }
 
-// A 4:8 group (four of eight consecutive weights kept): its four kept 16-bit
-// values in ascending column order (v01 = values 0 and 1, v23 = values 2
-// and 3) and the 8-bit mask m of their positions -> the group's eight
-// elements with zeros at the dropped positions, i.e. the 16-byte A chunk a
-// lane holds of v_mfma_f32_16x16x32 (row l % 16, K 8*(l/16) .. +7).  Kept
-// position p takes the lowest value not yet placed.
-__device__ __forceinline__ u32x4 expand48(uint32_t v01, uint32_t v23, uint32_t m) {
-  uint64_t q = (uint64_t)v01 | ((uint64_t)v23 << 32);
-  uint32_t e[8];
+// Rebuilding a 4:8 group (four of eight consecutive weights kept): its four
+// kept 16-bit values in ascending column order sit in two words (v01 =
+// values 0 and 1, v23 = values 2 and 3), i.e. value k in bytes 2k, 2k+1 of
+// the byte pool {v23 : v01} that v_perm_b32 selects from (selector bytes
+// 0-3 pick v01's bytes, 4-7 v23's, 0x0c a zero byte).  sel48(m) are the four
+// selector words that turn the pool into the group's eight elements in
+// column order for the position mask m: element p takes the lowest value
+// not yet placed if bit p is set, else zero.  Kernels keep sel48 of every
+// byte in a 4 KB LDS table, so a group costs one LDS read and four perms.
+__device__ __forceinline__ u32x4 sel48(uint32_t m) {
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  uint32_t k = 0;
 #pragma unroll
   for (int p = 0; p < 8; p++) {
-    const bool kept = (m >> p) & 1u;
-    e[p] = kept ? (uint32_t)(q & 0xffffu) : 0u;
-    q = kept ? (q >> 16) : q;
+    const uint32_t kept = (m >> p) & 1u;
+    const uint32_t s = kept ? ((2u * k) | ((2u * k + 1u) << 8)) : 0x0c0cu;
+    w[p >> 1] |= s << (16 * (p & 1));
+    k += kept;
   }
-  return (u32x4){e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+  return (u32x4){w[0], w[1], w[2], w[3]};
+}
+__device__ __forceinline__ u32x4 expand48(uint32_t v01, uint32_t v23, u32x4 sel) {
+  return (u32x4){__builtin_amdgcn_perm(v23, v01, sel[0]), __builtin_amdgcn_perm(v23, v01, sel[1]),
+                 __builtin_amdgcn_perm(v23, v01, sel[2]), __builtin_amdgcn_perm(v23, v01, sel[3])};
+}
+// Fill a 256-entry selector table (every thread of the workgroup calls it;
+// the caller synchronises before reading).
+__device__ __forceinline__ void fill_sel48(u32x4* table, int tid, int nthreads) {
+  for (int m = tid; m < 256; m += nthreads) table[m] = sel48((uint32_t)m);
+}
+
+// A lane's sixteen columns of a 4:8 tile's 64-column slice (two groups of
+// eight: values v = group 0's four then group 1's four, masks m16 = group 0
+// in bits 0-7, group 1 in bits 8-15) -> the lane's chunks of a dense
+// piece's two halves: h0 = positions (0,1), h1 = positions (2,3) of each
+// group of four, the fixed-pattern operands a dense tile runs on.
+__device__ __forceinline__ void dense_halves48(u32x4 v, uint32_t m16, const u32x4* table, u32x4& h0, u32x4& h1) {
+  const u32x4 x0 = expand48(v[0], v[1], table[m16 & 0xffu]), x1 = expand48(v[2], v[3], table[(m16 >> 8) & 0xffu]);
+  h0 = (u32x4){x0[0], x0[2], x1[0], x1[2]};
+  h1 = (u32x4){x0[1], x0[3], x1[1], x1[3]};
 }
 
 struct TileEntry {

@@ -37,9 +37,10 @@ namespace patch {
 //           the row-major chunk of columns 32c + 8*(l/16) (dense baseline);
 //   sparse: a[0], a[1] = value fragments of slices 0 and 1, a[2] = the
 //           16 bytes of the band's codes holding this lane's word (word l & 3),
-//           a[3] = the same chunk again (unused); 4:8 tiles alike, the
-//           fragments holding the four kept values per 32-column group and
-//           the word its four 8-bit position masks.
+//           a[3] = the same chunk again (unused); 4:8 tiles alike (the
+//           value fragments hold four kept values per group of eight, the
+//           word four 8-bit position masks), rebuilt into a dense tile's
+//           halves before the matrix instructions.
 template <int MB>
 struct DecodeFrag {
   u32x4 x[MB][4];  // B operand chunks of M block mb: X[16mb + m][k0 + 32c + 8h .. +7], c = 0..3
@@ -87,14 +88,31 @@ __device__ __forceinline__ void decode_load(DecodeFrag<MB>& f, const uint8_t* __
   for (int c = 0; c < 4; c++) f.a[c] = ld16(ap[c]);
 }
 
-template <bool BF16, bool SRC_ROWMAJOR, int MB>
-__device__ __forceinline__ void decode_mma(const DecodeFrag<MB>& f, f32x4 (&acc)[MB], int l) {
+// N48: the blob holds 4:8 tiles (their rebuild lives only in this
+// instantiation: it costs the other kinds registers and occupancy).
+template <bool BF16, bool SRC_ROWMAJOR, int MB, bool N48>
+__device__ __forceinline__ void decode_mma(DecodeFrag<MB>& f, f32x4 (&acc)[MB], int l, const u32x4* sel) {
   if constexpr (SRC_ROWMAJOR) {
 #pragma unroll
     for (int mb = 0; mb < MB; mb++)
 #pragma unroll
       for (int c = 0; c < 4; c++) acc[mb] = mma_dense<BF16>(f.a[c], f.x[mb][c], acc[mb]);
-  } else if (f.kind == 0) {
+  } else if (f.kind == 0 || (N48 && f.kind == 2)) {
+    // dense, or 4:8 rebuilt in place into a dense piece's halves (values of
+    // slice q in a[q], its two groups' masks in bits 16q .. 16q+15 of the
+    // lane's word in the codes chunk a[2]); the slot is reloaded afterwards
+    if constexpr (N48) {
+      if (f.kind == 2) {
+        // the mask word is read from a[3] (the same codes chunk as a[2]):
+        // it is the slot's last load, so reading it makes the wait cover
+        // every load of the slot before its registers are rewritten here
+        const u32x4 mc = f.a[3], v0 = f.a[0], v1 = f.a[1];
+        const uint32_t lo = (l & 1) ? mc[1] : mc[0], hi = (l & 1) ? mc[3] : mc[2];
+        const uint32_t meta = (l & 2) ? hi : lo;
+        dense_halves48(v0, meta & 0xffffu, sel, f.a[0], f.a[1]);
+        dense_halves48(v1, meta >> 16, sel, f.a[2], f.a[3]);
+      }
+    }
     // slice q: halves with positions (0,1) (code 4) and (2,3) (code 14)
 #pragma unroll
     for (int mb = 0; mb < MB; mb++)
@@ -109,19 +127,6 @@ __device__ __forceinline__ void decode_mma(const DecodeFrag<MB>& f, f32x4 (&acc)
     const u32x4 mc = f.a[2];
     const uint32_t lo = (l & 1) ? mc[1] : mc[0], hi = (l & 1) ? mc[3] : mc[2];
     const uint32_t meta = (l & 2) ? hi : lo;
-    if (f.kind == 2) {
-      // 4:8: rebuild the lane's group of each 32-column slice c (values in
-      // a[c / 2], words 2(c % 2) and 2(c % 2) + 1; mask = byte c of the word)
-      // and run the dense instruction on it
-#pragma unroll
-      for (int c = 0; c < 4; c++) {
-        const u32x4 v = f.a[c >> 1];
-        const u32x4 A = expand48(v[2 * (c & 1)], v[2 * (c & 1) + 1], (meta >> (8 * c)) & 0xffu);
-#pragma unroll
-        for (int mb = 0; mb < MB; mb++) acc[mb] = mma_dense<BF16>(A, f.x[mb][c], acc[mb]);
-      }
-      return;
-    }
 #pragma unroll
     for (int mb = 0; mb < MB; mb++) {
       // slice 0: logical K 0..63 of the tile -> B chunks 0 (K 8h..) and 1 (K 32+8h..)
@@ -141,7 +146,7 @@ __device__ __forceinline__ void decode_mma(const DecodeFrag<MB>& f, f32x4 (&acc)
 // of both row-blocks of pair q with twice the waves (the first WAVES on gate,
 // the others on up) and writes H[m][128 q + ...] = SiLU(gate) * up, H being
 // M x N/2.
-template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, int WAVES, int DEPTH, bool XCD_MAP, int MB, bool FUSE>
+template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, int WAVES, int DEPTH, bool XCD_MAP, int MB, bool FUSE, bool N48>
 __global__ __launch_bounds__(WAVES * 64 * (FUSE ? 2 : 1)) void k_decode(const uint8_t* __restrict__ src,
                                                                          const uint8_t* __restrict__ src2,
                                                                          const uint16_t* __restrict__ X, int M, int N,
@@ -171,6 +176,12 @@ __global__ __launch_bounds__(WAVES * 64 * (FUSE ? 2 : 1)) void k_decode(const ui
   const int wi = SRC_ROWMAJOR && FUSE ? q : i;
 
   __shared__ f32x4 s_red[kAllWaves * MB][64];
+  // 4:8 rebuild selectors (only in the instantiation for blobs with 4:8 tiles)
+  __shared__ u32x4 s_sel[N48 ? 256 : 1];
+  if constexpr (N48) {
+    fill_sel48(s_sel, (int)threadIdx.x, kAllWaves * 64);
+    __syncthreads();
+  }
 
   // wave w takes tile columns j = w, w + WAVES, ... of its row-block (at
   // most 64 of them, which the launch guarantees).  Their table entries arrive with one
@@ -212,7 +223,7 @@ __global__ __launch_bounds__(WAVES * 64 * (FUSE ? 2 : 1)) void k_decode(const ui
     for (; t0 + DEPTH < n_mine; t0 += DEPTH) {
 #pragma unroll
       for (int s = 0; s < DEPTH; s++) {
-        decode_mma<BF16, SRC_ROWMAJOR, MB>(f[s], acc, l);
+        decode_mma<BF16, SRC_ROWMAJOR, MB, N48>(f[s], acc, l, s_sel);
         const int tn = min(t0 + s + DEPTH, n_mine - 1);
         uint64_t off;
         uint32_t kind, stride;
@@ -224,7 +235,7 @@ __global__ __launch_bounds__(WAVES * 64 * (FUSE ? 2 : 1)) void k_decode(const ui
     // last round: no refills
 #pragma unroll
     for (int s = 0; s < DEPTH; s++)
-      if (t0 + s < n_mine) decode_mma<BF16, SRC_ROWMAJOR, MB>(f[s], acc, l);
+      if (t0 + s < n_mine) decode_mma<BF16, SRC_ROWMAJOR, MB, N48>(f[s], acc, l, s_sel);
   }
 
   // ---- fixed-order reduction over waves (wave wa adds up M blocks wa,
@@ -252,18 +263,18 @@ __global__ __launch_bounds__(WAVES * 64 * (FUSE ? 2 : 1)) void k_decode(const ui
   }
 }
 
-template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE, int WAVES, int DEPTH, bool XCD_MAP, int MB>
+template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE, bool N48, int WAVES, int DEPTH, bool XCD_MAP, int MB>
 static hipError_t launch_decode_v(const void* src, const void* src2, const void* X, int64_t M, int64_t N, int64_t K,
                                   void* Y, hipStream_t s) {
   const unsigned grid = (unsigned)(FUSE ? N / 32 : N / 16);
-  hipLaunchKernelGGL((k_decode<BF16, SRC_ROWMAJOR, OUT_F32, WAVES, DEPTH, XCD_MAP, MB, FUSE>), dim3(grid),
+  hipLaunchKernelGGL((k_decode<BF16, SRC_ROWMAJOR, OUT_F32, WAVES, DEPTH, XCD_MAP, MB, FUSE, N48>), dim3(grid),
                      dim3(WAVES * 64 * (FUSE ? 2 : 1)), 0, s, reinterpret_cast<const uint8_t*>(src),
                      reinterpret_cast<const uint8_t*>(src2), reinterpret_cast<const uint16_t*>(X), (int)M, (int)N,
                      (int)K, Y);
   return hipGetLastError();
 }
 
-template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE>
+template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE, bool N48>
 static hipError_t launch_decode_t(const void* src, const void* src2, const void* X, int64_t M, int64_t N, int64_t K,
                                   void* Y, hipStream_t s) {
   // Few waves a workgroup, several tiles in flight a wave: small workgroups
@@ -273,7 +284,8 @@ static hipError_t launch_decode_t(const void* src, const void* src2, const void*
   // so it may own at most 64 tile columns: larger K takes more waves.
   // (Fused gate/up: twice the waves, one set per matrix.)
   const int64_t KT = K / kTile;
-#define PATCH_DV(W, D, MBK) launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, FUSE, W, D, true, MBK>(src, src2, X, M, N, K, Y, s)
+#define PATCH_DV(W, D, MBK) \
+  launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, FUSE, N48, W, D, true, MBK>(src, src2, X, M, N, K, Y, s)
   if (M <= 16) {
     if (KT <= 2 * 64) return PATCH_DV(2, 4, 1);
     if (KT <= 4 * 64) return PATCH_DV(4, 4, 1);
@@ -306,18 +318,25 @@ double decode_estimate_us(int64_t M, int64_t N, int64_t K, double w_bytes) {
 }
 
 // src2 non-null: fused gate/up (see k_decode); Y is then H, M x N/2.
+// n48: the packed blob holds 4:8 tiles.
 hipError_t launch_decode(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* src2, const void* X,
-                         int64_t M, int64_t N, int64_t K, void* Y, hipStream_t s) {
+                         int64_t M, int64_t N, int64_t K, void* Y, bool n48, hipStream_t s) {
   const bool fuse = src2 != nullptr;
   if (fuse && (N % (2 * kTile))) return hipErrorInvalidValue;
-#define PATCH_D(B, R, F, U) launch_decode_t<B, R, F, U>(src, src2, X, M, N, K, Y, s)
-#define PATCH_D2(B, R, F) (fuse ? PATCH_D(B, R, F, true) : PATCH_D(B, R, F, false))
+#define PATCH_D(B, R, F, U, Q) launch_decode_t<B, R, F, U, Q>(src, src2, X, M, N, K, Y, s)
+#define PATCH_D2(B, R, F) (fuse ? PATCH_D(B, R, F, true, false) : PATCH_D(B, R, F, false, false))
+#define PATCH_D48(B, F) (fuse ? PATCH_D(B, false, F, true, true) : PATCH_D(B, false, F, false, true))
+  if (!rowmajor && n48) {
+    if (bf16) return out_f32 ? PATCH_D48(true, true) : PATCH_D48(true, false);
+    return out_f32 ? PATCH_D48(false, true) : PATCH_D48(false, false);
+  }
   if (bf16) {
     if (rowmajor) return out_f32 ? PATCH_D2(true, true, true) : PATCH_D2(true, true, false);
     return out_f32 ? PATCH_D2(true, false, true) : PATCH_D2(true, false, false);
   }
   if (rowmajor) return out_f32 ? PATCH_D2(false, true, true) : PATCH_D2(false, true, false);
   return out_f32 ? PATCH_D2(false, false, true) : PATCH_D2(false, false, false);
+#undef PATCH_D48
 #undef PATCH_D2
 #undef PATCH_D
 }

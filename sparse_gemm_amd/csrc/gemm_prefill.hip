@@ -508,6 +508,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_x[kLdsStages * kLdsXStage];
   __shared__ uint32_t s_ent[2][kPfMaxKT];
   __shared__ uint32_t s_stride[2];
+  __shared__ u32x4 s_sel[SRC_ROWMAJOR ? 1 : 256];  // 4:8 rebuild selectors
 
   const int t = (blockIdx.x & 7) * P.per_xcd + (blockIdx.x >> 3);
   if (t >= P.n_blocks) return;  // whole workgroup
@@ -544,6 +545,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
       s_ent[rr][j] = (uint32_t)(te.offset >> 8) | (te.kind << 30);
       if (j == 0) s_stride[rr] = te.band_stride;
     }
+    fill_sel48(s_sel, (int)threadIdx.x, kPfWaves * 64);
     __syncthreads();
   }
   const uint32_t stride = SRC_ROWMAJOR ? 0u : (uint32_t)__builtin_amdgcn_readfirstlane((int)s_stride[r_src]);
@@ -642,33 +644,19 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
           for (int b = 0; b < 4; b++) acc[b][mblk] = mma_dense<BF16>(qq ? a1[b] : a0[b], bf[mblk], acc[b][mblk]);
         __builtin_amdgcn_sched_barrier(0);
       }
-    } else if (kind == 2) {
-      // 4:8: groups of eight rebuilt in registers (slices 2h, 2h+1), dense
-      // instruction with the B fragments of K 8hl.. and 32+8hl..
-      u32x4 a_lo[4], a_hi[4];
-#pragma unroll
-      for (int b = 0; b < 4; b++) {
-        const u32x4 mc = a1[b], v = a0[b];
-        const uint32_t lo = (l & 1) ? mc[1] : mc[0], hi = (l & 1) ? mc[3] : mc[2];
-        const uint32_t meta = ((l & 2) ? hi : lo) >> (16 * h);
-        a_lo[b] = expand48(v[0], v[1], meta & 0xffu);
-        a_hi[b] = expand48(v[2], v[3], (meta >> 8) & 0xffu);
-      }
-      constexpr int kGroups = kNMB / kPfMGroup;
-#pragma unroll
-      for (int g = 0; g < kGroups; g++) {
-        u32x4 blo[kPfMGroup], bhi[kPfMGroup];
-        read_b(xs, g, blo, bhi);
-#pragma unroll
-        for (int mm = 0; mm < kPfMGroup; mm++)
-#pragma unroll
-          for (int b = 0; b < 4; b++) {
-            acc[b][kPfMGroup * g + mm] = mma_dense<BF16>(a_lo[b], blo[mm], acc[b][kPfMGroup * g + mm]);
-            acc[b][kPfMGroup * g + mm] = mma_dense<BF16>(a_hi[b], bhi[mm], acc[b][kPfMGroup * g + mm]);
-          }
-        __builtin_amdgcn_sched_barrier(0);
-      }
     } else {
+      if (kind == 2) {
+        // 4:8: each band's sixteen columns rebuilt into a dense piece's two
+        // halves (values in a0, the lane's masks in the codes chunk a1),
+        // then run as a dense tile
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+          const u32x4 mc = a1[b];
+          const uint32_t lo = (l & 1) ? mc[1] : mc[0], hi = (l & 1) ? mc[3] : mc[2];
+          dense_halves48(a0[b], (((l & 2) ? hi : lo) >> (16 * h)) & 0xffffu, s_sel, a0[b], a1[b]);
+        }
+        kind = 0;
+      }
       const int nsub = kind == 0 ? 2 : 1;
       uint32_t idx0[4];
 #pragma unroll

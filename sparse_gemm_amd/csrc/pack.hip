@@ -19,11 +19,12 @@
 //       (ascending column) of groups g = 16*q + 4*(l/16) + p, p = 0..3; then
 //       at 2048 + 4*l the lane's word of codes i0 | i1 << 2 (bits 16*q + 4*p);
 //   4:8 piece (2304 B; other N:M patterns, explainer section 5 "Future
-//       Direction"): lane l's group of eight in 32-column slice c is columns
-//       32*c + 8*(l/16) .. +7; block q at 1024*q holds its four kept values
-//       (ascending column) in slice 2q, then in slice 2q+1; at 2048 + 4*l the
-//       lane's word whose byte c is the group's kept-position mask in slice c
-//       (the A-operand group of v_mfma_f32_16x16x32 a lane rebuilds in place).
+//       Direction"): lane l's columns 64*q + 16*(l/16) .. +15 of slice q are
+//       two groups of eight u = 0, 1; block q at 1024*q holds the four kept
+//       values (ascending column) of group 0, then of group 1; at 2048 + 4*l
+//       the lane's word whose byte 2q + u is group u's kept-position mask
+//       (the sixteen columns a lane holds of a dense piece's two halves, which
+//       the GEMM kernels rebuild in place).
 // These are the lane orders of the A operand and index of
 // v_smfmac_f32_16x16x64, for both tile kinds, so the GEMM kernels load each
 // 1 KB fragment with one coalesced 16-byte load a lane, run dense and 2:4
@@ -78,33 +79,33 @@ __global__ __launch_bounds__(256) void k_pack(PackSources src, int K, int KT, ui
   uint32_t meta = 0;
   bool bad = false;
   if (e.kind == 2) {
-    // four 32-column slices; this lane's group of eight in slice c
-    uint32_t vals[8];  // value words: slices 0..3, two words each
-#pragma unroll
-    for (int c = 0; c < 4; c++) {
-      const int64_t col0 = (int64_t)j * kTile + 32 * c + 8 * (l >> 4);
-      const u32x4 w = ld16(W + row * K + col0);
-      const uint2 mk = *reinterpret_cast<const uint2*>(mask + row * K + col0);
-      uint32_t kept[4] = {0u, 0u, 0u, 0u}, bits = 0;
-      int n = 0;
-#pragma unroll
-      for (int p = 0; p < 8; p++) {
-        const uint32_t mb = ((p < 4 ? mk.x : mk.y) >> (8 * (p & 3))) & 0xffu;
-        const uint32_t v = (w[p >> 1] >> (16 * (p & 1))) & 0xffffu;
-        if (mb) {
-          if (n < 4) kept[n] = v;
-          bits |= 1u << p;
-          n++;
-        }
-      }
-      bad |= (n != 4);
-      vals[2 * c] = kept[0] | (kept[1] << 16);
-      vals[2 * c + 1] = kept[2] | (kept[3] << 16);
-      meta |= bits << (8 * c);
-    }
+    // 64-column slice q: this lane's sixteen columns, groups u = 0, 1 of eight
 #pragma unroll
     for (int q = 0; q < 2; q++) {
-      const u32x4 o = {vals[4 * q], vals[4 * q + 1], vals[4 * q + 2], vals[4 * q + 3]};
+      uint32_t vals[4];
+#pragma unroll
+      for (int u = 0; u < 2; u++) {
+        const int64_t col0 = (int64_t)j * kTile + 64 * q + 16 * (l >> 4) + 8 * u;
+        const u32x4 w = ld16(W + row * K + col0);
+        const uint2 mk = *reinterpret_cast<const uint2*>(mask + row * K + col0);
+        uint32_t kept[4] = {0u, 0u, 0u, 0u}, bits = 0;
+        int n = 0;
+#pragma unroll
+        for (int p = 0; p < 8; p++) {
+          const uint32_t mb = ((p < 4 ? mk.x : mk.y) >> (8 * (p & 3))) & 0xffu;
+          const uint32_t v = (w[p >> 1] >> (16 * (p & 1))) & 0xffffu;
+          if (mb) {
+            if (n < 4) kept[n] = v;
+            bits |= 1u << p;
+            n++;
+          }
+        }
+        bad |= (n != 4);
+        vals[2 * u] = kept[0] | (kept[1] << 16);
+        vals[2 * u + 1] = kept[2] | (kept[3] << 16);
+        meta |= bits << (8 * (2 * q + u));
+      }
+      const u32x4 o = {vals[0], vals[1], vals[2], vals[3]};
       st16(piece + 1024 * q + 16 * l, o);
     }
     reinterpret_cast<uint32_t*>(piece + kSparseMetaOffset)[l] = meta;

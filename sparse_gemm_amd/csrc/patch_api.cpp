@@ -15,7 +15,7 @@
 namespace patch {
 hipError_t launch_pack(const PackSources& src, int64_t N, int64_t K, uint8_t* blob, hipStream_t s);
 hipError_t launch_decode(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* src2, const void* X,
-                         int64_t M, int64_t N, int64_t K, void* Y, hipStream_t s);
+                         int64_t M, int64_t N, int64_t K, void* Y, bool n48, hipStream_t s);
 hipError_t launch_prefill(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* src2, const void* X,
                           int64_t M, int64_t N, int64_t K, void* Y, void* ws, uint64_t ws_bytes, int force_bm,
                           bool force_lds, hipStream_t s);
@@ -495,7 +495,7 @@ static patch_status gemm_common(bool rowmajor, patch_dtype dt, int64_t M, int64_
   const bool bf16 = dt == PATCH_BF16, f32out = y_dtype == PATCH_F32;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   static const int kForceBm[11] = {0, 0, 0, 64, 128, 192, 256, 128, 192, 256, 64};
-  hipError_t e = decode ? patch::launch_decode(bf16, rowmajor, f32out, src, src2, X_dev, M, N, K, Y_dev, st)
+  hipError_t e = decode ? patch::launch_decode(bf16, rowmajor, f32out, src, src2, X_dev, M, N, K, Y_dev, has48, st)
                         : patch::launch_prefill(bf16, rowmajor, f32out, src, src2, X_dev, M, N, K, Y_dev, ws,
                                                 ws_bytes, kForceBm[variant], variant >= PATCH_VARIANT_PREFILL_W128_LDS,
                                                 st);
