@@ -457,7 +457,12 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
 //     v_smfmac_f32_16x16x64 sequence as the register-staged kernel.
 // LDS per stage: 32 KB of W + BM * 128 bytes of X; three stages up to width
 // 128 (120 KB at 64, 144 KB at 128), two at 192 and 256 (112 and 128 KB),
-// plus the tile entries: one workgroup per CU.
+// plus the tile entries and, for packed W, the 4 KB table that rebuilds 4:8
+// tiles: one workgroup per CU.
+//   * Tile kinds: dense and 2:4 as above; a 4:8 tile's band is copied like a
+//     2:4 one (values, then the chunk holding the lane's position masks) and
+//     rebuilt in registers into a dense piece's two halves (one table read
+//     and four byte permutes per group of eight), then runs as a dense tile.
 // ---------------------------------------------------------------------------
 constexpr int kLdsWStage = 32768;  // 2 row-blocks x 8 bands x 2 fragments of 1 KB
 // stages of the LDS ring for an M-block width: three up to 128, two at 192
