@@ -106,14 +106,14 @@ int32_t patch_abi_version(void);
 uint64_t patch_packed_bytes(patch_dtype dtype, int64_t N, int64_t K, const uint8_t* tile_map_host);
 
 /*
- * Pack dense W plus a tile map and a 2:4 mask into the blob (format
- * version 3): a 256-byte header, a 16-byte-per-tile table (data offset,
- * kind, band stride) and the tile data.  A sparse tile keeps, for every
+ * Pack dense W plus a tile map and a 2:4 (or 4:8) mask into the blob
+ * (format version 3): a 256-byte header, a 16-byte-per-tile table (data
+ * offset, kind, band stride) and the tile data.  A 2:4 tile keeps, for every
  * group of four consecutive weights along K, the two kept values plus a
  * 4-bit code i0 | i1 << 2 (2 bits per kept value); a dense tile keeps all
  * 128 x 128 values, each 64-column slice stored as two halves holding
  * positions (0,1) and (2,3) of every group of four.  A tile is stored as
- * eight pieces, one per 16-row band (4096 bytes dense, 2304 bytes 2:4);
+ * eight pieces, one per 16-row band (4096 bytes dense, 2304 bytes 2:4 or 4:8);
  * within a row-block the pieces of one band for all its tiles lie back to
  * back, so band b of a tile sits at the tile's offset + b * band stride.
  * Pieces are laid out in the lane order of the sparse matrix instruction's

@@ -164,7 +164,13 @@ class PackedWeight:
 
     @property
     def n_sparse(self) -> int:
+        """Compressed (2:4 and 4:8) tiles."""
         return self.desc.n_sparse
+
+    @property
+    def n_48(self) -> int:
+        """4:8 tiles among the compressed ones."""
+        return self.desc.n_48
 
     @property
     def nbytes(self) -> int:
