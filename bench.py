@@ -393,7 +393,7 @@ def main():
     ap.add_argument("--report-steps", type=int, default=100, help="launches per timed batch in the report")
     ap.add_argument("--report-batches", type=int, default=10, help="timed batches per point in the report (median)")
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill_mlp", "imbalanced_13b", "sampler", "fine_mask"],
+                    choices=["decode", "prefill_mlp", "imbalanced_13b", "sampler", "fine_mask", "n48"],
                     help="decode (default: the q_proj decode GEMM), a prefill workload or the mask sampler, "
                          "for profiling")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -426,8 +426,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration_copy_bytes": src.numel(), "copies": 3}), file=sys.stderr, flush=True)
         del src, dst
-    if args.workload in ("sampler", "fine_mask"):
-        for rec in (sampler_set if args.workload == "sampler" else fine_set)(args.steps, args.warmup, 1):
+    if args.workload in ("sampler", "fine_mask", "n48"):
+        fn = {"sampler": sampler_set, "fine_mask": fine_set, "n48": n48_set}[args.workload]
+        for rec in fn(args.steps, args.warmup, 1):
             print(json.dumps(rec), flush=True)
         return
     if args.workload != "decode":
@@ -546,6 +547,43 @@ def sampler_set(steps, warmup, batches):
                             algorithmic_bytes=nbytes, sparse_tile_fraction=float(bufs[0].float().mean().item()),
                             roofline_bound="hbm", roofline_frac=gbps / HBM_PEAK_GBS))
         del dev, bufs
+        torch.cuda.empty_cache()
+    return out
+
+
+def n48_set(steps, warmup, batches, Ms=(1, 16, 128, 2048)):
+    """4:8 tiles (the third tile kind) on the LLaMA-2-7B q_proj, gate_proj
+    and down_proj shapes: every tile 4:8, every tile 2:4 and every tile
+    dense (the dense kernel on row-major W), top-4-of-8 / top-2-of-4
+    masks; graph replays, rotated copies as elsewhere."""
+    import torch
+
+    from sparse_gemm_amd import inputs, patch
+
+    out = []
+    for name, N, K in (("q_proj", 4096, 4096), ("gate_proj", 11008, 4096), ("down_proj", 4096, 11008)):
+        p48 = inputs.make_mixed("bf16", N, K, 0, 0.0, 1.0)
+        p24 = inputs.make_mixed("bf16", N, K, 0, 1.0, 0.0)
+        W = dev_bits(p48.w, torch.bfloat16)
+        packs = {}
+        for tag, p in (("48", p48), ("24", p24)):
+            pw = patch.pack(W, p.tile_map, torch.from_numpy(p.mask).cuda())
+            packs[tag] = (rotate(pw.blob, pw.nbytes), pw.desc)
+        Ws = rotate(W, W.numel() * 2)
+        for M in Ms:
+            X = dev_bits(inputs.make_x(inputs.CONFIGS["sweep"], M, K), torch.bfloat16)
+            Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            calls = [(tag, (lambda k, b=b, d=d: patch.gemm(X, patch.PackedWeight(b[k % len(b)], d), out=Y)))
+                     for tag, (b, d) in packs.items()]
+            calls.append(("dense", lambda k: patch.dense_gemm(X, Ws[k % len(Ws)], out=Y)))
+            _, per = time_graphs(calls, steps, warmup, batches)
+            us = {t: median(v) * 1e3 for t, v in per.items()}
+            out.append(dict(config="n48", matrix=name, N=N, K=K, M=M, us_48=us["48"], us_24=us["24"],
+                            us_dense=us["dense"], speedup_48_vs_dense=us["dense"] / us["48"],
+                            speedup_24_vs_dense=us["dense"] / us["24"],
+                            tflops_dense_equiv_48=2.0 * M * N * K / (us["48"] * 1e-6) / 1e12,
+                            gbps_48=algo_bytes(N, K, M, (N // 128) * (K // 128)) / (us["48"] * 1e-6) / 1e9))
+        del packs, Ws, W
         torch.cuda.empty_cache()
     return out
 
@@ -714,6 +752,11 @@ def write_report(path, steps, warmup, batches):
         for mi in (0, 4, 6):  # q_proj-like, gate/up-like, down
             for si in range(5):
                 emit("sweep", mi, si, (1, 16, 128, 2048))
+        for rec in n48_set(steps, warmup, batches):
+            f.write(json.dumps(rec) + "\n")
+            f.flush()
+            print(f"[report] 4:8 {rec['matrix']} M={rec['M']}: {rec['us_48']:.2f} us (2:4 {rec['us_24']:.2f}, dense "
+                  f"{rec['us_dense']:.2f}), x{rec['speedup_48_vs_dense']:.3f} vs dense", flush=True)
         for rec in fine_set(steps, warmup, batches):
             f.write(json.dumps(rec) + "\n")
             f.flush()
