@@ -23,6 +23,8 @@
 #include "pack_sources.h"
 #include <stdint.h>
 
+#include <atomic>
+
 namespace patch {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -154,5 +156,19 @@ struct TileEntry {
   uint32_t kind;         // 0 dense, 1 sparse
   uint32_t band_stride;  // bytes from one band's pieces to the next in this row-block
 };
+
+// Number of compute units of the current device, read once per device (the
+// cache is atomic: GEMM calls may come from several host threads).
+inline int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 }  // namespace patch

@@ -6,7 +6,7 @@
 // kernel streams each tile's packed bytes exactly once:
 //
 //   * one workgroup per 16-row band of W (N/16 workgroups) and all of K;
-//     wave w of the workgroup's WAVES (2 to 8, fewer where K allows) takes
+//     wave w of the workgroup's WAVES (1 to 8, by K and the grid) takes
 //     the tile columns j = w, w+WAVES, ... of the band's row-block; its
 //     tile-table entries arrive with one vector load and are read with
 //     v_readlane (no list building, no barrier before the first weight
@@ -287,6 +287,11 @@ static hipError_t launch_decode_t(const void* src, const void* src2, const void*
 #define PATCH_DV(W, D, MBK) \
   launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, FUSE, N48, W, D, true, MBK>(src, src2, X, M, N, K, Y, s)
   if (M <= 16) {
+    // Wide matrices, whose bands cover every CU at least twice: one wave a
+    // band (gate_proj of LLaMA-2 7B, 11008 x 4096: 1-6% faster than two
+    // waves; q_proj, 4096 x 4096 with one band a CU, is 30% slower so).
+    if constexpr (!FUSE)
+      if (KT <= 64 && N / 16 >= 2 * (int64_t)cu_count()) return PATCH_DV(1, 4, 1);
     if (KT <= 2 * 64) return PATCH_DV(2, 4, 1);
     if (KT <= 4 * 64) return PATCH_DV(4, 4, 1);
     return PATCH_DV(8, 2, 1);

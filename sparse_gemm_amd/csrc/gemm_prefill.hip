@@ -730,19 +730,6 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   }
 }
 
-// Number of compute units, read once per device.
-static int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 // Launch shape: the M-block width BM and the number of K ranges, chosen
 // by a cost model of the LDS-staged kernel fitted to its measured times on
 // the LLaMA-2 7B q_proj, gate_proj and down_proj shapes (32 <= M <= 2048,
