@@ -454,7 +454,12 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
 //     wave issues the same copies every step.
 //   * Fragments are then read from LDS with one 16-byte read a lane (the
 //     2:4 codes chunk holding the lane's word likewise) and fed to the same
-//     v_smfmac_f32_16x16x64 sequence as the register-staged kernel.
+//     v_smfmac_f32_16x16x64 sequence as the register-staged kernel.  The
+//     barrier of step s + 1 sits before the last group of step s's matrix
+//     instructions, and step s + 1's A fragments and first B fragments are
+//     read right after it, so those reads run under that group and a step
+//     starts with operands in registers (two sets of A fragments; B
+//     fragments alternate between two buffers by group).
 // LDS per stage: 32 KB of W + BM * 128 bytes of X; three stages up to width
 // 128 (120 KB at 64, 144 KB at 128), two at 192 and 256 (112 and 128 KB),
 // plus the tile entries and, for packed W, the 4 KB table that rebuilds 4:8
@@ -508,6 +513,9 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   constexpr int kLdsXStage = BM * kPfRowBytes;       // X rows of one step
   constexpr int kXC = BM / 64;                       // 1 KB X chunks a wave copies per step
   constexpr int kLdsCopies = 4 + kXC;                // copies a wave issues per step
+  // 16-column M blocks whose B fragments are read together (one at width
+  // 256, where two steps' A fragments and the accumulators leave no room)
+  constexpr int kMG = BM == 256 ? 1 : kPfMGroup;
   static_assert(kXC * 1024 * kPfWaves == kLdsXStage, "X stage split");
   __shared__ __attribute__((aligned(1024))) uint8_t s_w[kLdsStages * kLdsWStage];
   __shared__ __attribute__((aligned(1024))) uint8_t s_x[kLdsStages * kLdsXStage];
@@ -610,100 +618,164 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
 #pragma unroll
     for (int c = 0; c < kNMB; c++) acc[a][c] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  auto read_b = [&](const uint8_t* xs, int g, u32x4 (&blo)[kPfMGroup], u32x4 (&bhi)[kPfMGroup]) {
+  auto read_b = [&](const uint8_t* xs, int g, u32x4 (&blo)[kMG], u32x4 (&bhi)[kMG]) {
 #pragma unroll
-    for (int mm = 0; mm < kPfMGroup; mm++) {
-      const int row = wm * (BM / 2) + (kPfMGroup * g + mm) * 16 + (l & 15);
+    for (int mm = 0; mm < kMG; mm++) {
+      const int row = wm * (BM / 2) + (kMG * g + mm) * 16 + (l & 15);
       blo[mm] = *reinterpret_cast<const u32x4*>(xs + swz(row, hl));
       bhi[mm] = *reinterpret_cast<const u32x4*>(xs + swz(row, 4 + hl));
     }
   };
-
-  // step s from stage s % kLdsStages: this wave's A fragments from LDS, then the
-  // matrix instructions (as in k_prefill)
-  auto compute = [&](int s) {
-    const int st = s % kLdsStages;
-    const int jl = s >> 1, h = s & 1;
-    const uint8_t* ws = s_w + st * kLdsWStage + 1024 * ((r * 8 + 4 * wn) * 2);
-    const uint8_t* xs = s_x + st * kLdsXStage;
-    uint32_t kind = 0;
-    if constexpr (!SRC_ROWMAJOR) kind = (uint32_t)__builtin_amdgcn_readfirstlane((int)s_ent[r_src][jl]) >> 30;
-    u32x4 a0[4], a1[4];
+  // row-major W: B fragments of K half qq (32 columns), M blocks kRG p .. kRG p + kRG - 1
+  // (parts at the larger widths: registers)
+  constexpr int kRG = BM == 256 ? (FUSE ? kNMB / 4 : kNMB / 2) : (BM == 192 && FUSE ? kNMB / 2 : kNMB);
+  constexpr int kRParts = kNMB / kRG;
+  auto read_bq = [&](const uint8_t* xs, int qq, int part, u32x4 (&bf)[kRG]) {
+#pragma unroll
+    for (int mm = 0; mm < kRG; mm++)
+      bf[mm] = *reinterpret_cast<const u32x4*>(xs + swz(wm * (BM / 2) + (kRG * part + mm) * 16 + (l & 15), 4 * qq + hl));
+  };
+  auto x_stage = [&](int s) { return s_x + (s % kLdsStages) * kLdsXStage; };
+  // this wave's A fragments of step s (and the step's tile kind) from its stage
+  auto read_a = [&](int s, u32x4 (&a0)[4], u32x4 (&a1)[4], uint32_t& kind) {
+    const uint8_t* ws = s_w + (s % kLdsStages) * kLdsWStage + 1024 * ((r * 8 + 4 * wn) * 2);
+    kind = 0;
+    if constexpr (!SRC_ROWMAJOR) kind = (uint32_t)__builtin_amdgcn_readfirstlane((int)s_ent[r_src][s >> 1]) >> 30;
     const int off1 = kind ? 16 * (l >> 2) : 16 * l;
 #pragma unroll
     for (int b = 0; b < 4; b++) {
       a0[b] = *reinterpret_cast<const u32x4*>(ws + 2048 * b + 16 * l);
       a1[b] = *reinterpret_cast<const u32x4*>(ws + 2048 * b + 1024 + off1);
     }
-    if (!active) return;
-    if constexpr (SRC_ROWMAJOR) {
-#pragma unroll
-      for (int qq = 0; qq < 2; qq++) {
-        u32x4 bf[kNMB];
-#pragma unroll
-        for (int mblk = 0; mblk < kNMB; mblk++)
-          bf[mblk] = *reinterpret_cast<const u32x4*>(xs + swz(wm * (BM / 2) + mblk * 16 + (l & 15), 4 * qq + hl));
-#pragma unroll
-        for (int mblk = 0; mblk < kNMB; mblk++)
-#pragma unroll
-          for (int b = 0; b < 4; b++) acc[b][mblk] = mma_dense<BF16>(qq ? a1[b] : a0[b], bf[mblk], acc[b][mblk]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    } else {
-      if (kind == 2) {
-        // 4:8: each band's sixteen columns rebuilt into a dense piece's two
-        // halves (values in a0, the lane's masks in the codes chunk a1),
-        // then run as a dense tile
-#pragma unroll
-        for (int b = 0; b < 4; b++) {
-          const u32x4 mc = a1[b];
-          const uint32_t lo = (l & 1) ? mc[1] : mc[0], hi = (l & 1) ? mc[3] : mc[2];
-          dense_halves48(a0[b], (((l & 2) ? hi : lo) >> (16 * h)) & 0xffffu, s_sel, a0[b], a1[b]);
-        }
-        kind = 0;
-      }
-      const int nsub = kind == 0 ? 2 : 1;
-      uint32_t idx0[4];
+  };
+
+  // ---- pipeline: copies kLdsStages - 1 steps ahead; the fragments of step
+  // s + 1 are read from LDS while the last group of step s's matrix
+  // instructions runs, so a step starts with its first operands in registers
+  constexpr int kAhead = kLdsStages - 1;
+  // called in step s (s + 1 < n_steps) once this wave's reads of stage s
+  // are issued: step s + 1's copies have landed everywhere and nobody reads
+  // stage s any more, which the copies of step s + 1 + kAhead then refill
+  auto advance = [&](int s) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage s are done
+    if (kAhead == 2 && s + 2 < n_steps)
+      wait_copies<kLdsCopies>();  // step s + 2's copies may stay in flight
+    else
+      wait_copies<0>();
+    wg_barrier();
+    if (s + 1 + kAhead < n_steps) issue(s + 1 + kAhead);
+  };
+
+  // packed W, step s: A fragments a0/a1 (kind), B group 0 in buffer par * G & 1
+  // (the buffers alternate by group across steps; par = s & 1); reads step
+  // s + 1's A fragments into na0/na1 and its B group 0 into the next buffer
+  constexpr int kGroups = kNMB / kMG;
+  auto step_packed = [&](int s, int par, u32x4 (&a0)[4], u32x4 (&a1)[4], uint32_t kind, u32x4 (&na0)[4],
+                         u32x4 (&na1)[4], uint32_t& nkind, u32x4 (&blo)[2][kMG],
+                         u32x4 (&bhi)[2][kMG]) {
+    const int h = s & 1;
+    if (kind == 2) {
+      // 4:8: each band's sixteen columns rebuilt into a dense piece's two
+      // halves (values in a0, the lane's masks in the codes chunk a1),
+      // then run as a dense tile
 #pragma unroll
       for (int b = 0; b < 4; b++) {
         const u32x4 mc = a1[b];
         const uint32_t lo = (l & 1) ? mc[1] : mc[0], hi = (l & 1) ? mc[3] : mc[2];
-        idx0[b] = kind == 0 ? 0x4444u : (((l & 2) ? hi : lo) >> (16 * h));
+        dense_halves48(a0[b], (((l & 2) ? hi : lo) >> (16 * h)) & 0xffffu, s_sel, a0[b], a1[b]);
       }
-      constexpr int kGroups = kNMB / kPfMGroup;
-      u32x4 blo[2][kPfMGroup], bhi[2][kPfMGroup];
-      read_b(xs, 0, blo[0], bhi[0]);
+      kind = 0;
+    }
+    const int nsub = kind == 0 ? 2 : 1;
+    uint32_t idx0[4];
 #pragma unroll
-      for (int g = 0; g < kGroups; g++) {
-        if (g + 1 < kGroups) read_b(xs, g + 1, blo[(g + 1) & 1], bhi[(g + 1) & 1]);
+    for (int b = 0; b < 4; b++) {
+      const u32x4 mc = a1[b];
+      const uint32_t lo = (l & 1) ? mc[1] : mc[0], hi = (l & 1) ? mc[3] : mc[2];
+      idx0[b] = kind == 0 ? 0x4444u : (((l & 2) ? hi : lo) >> (16 * h));
+    }
+    const uint8_t* xs = x_stage(s);
+#pragma unroll
+    for (int g = 0; g < kGroups; g++) {
+      const int cb = (g + par * kGroups) & 1, nb = (g + 1 + par * kGroups) & 1;
+      if (g + 1 < kGroups) {
+        read_b(xs, g + 1, blo[nb], bhi[nb]);
+      } else {
+        // (after the last step: its own stage again, never used)
+        if (s + 1 < n_steps) advance(s);
+        const int sn = min(s + 1, n_steps - 1);
+        read_a(sn, na0, na1, nkind);
+        read_b(x_stage(sn), 0, blo[nb], bhi[nb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (active) {
         for (int sub = 0; sub < nsub; sub++) {
 #pragma unroll
-          for (int mm = 0; mm < kPfMGroup; mm++)
+          for (int mm = 0; mm < kMG; mm++)
 #pragma unroll
             for (int b = 0; b < 4; b++)
-              acc[b][kPfMGroup * g + mm] =
-                  mma_sparse<BF16, 0>(sub ? a1[b] : a0[b], blo[g & 1][mm], bhi[g & 1][mm],
-                                      acc[b][kPfMGroup * g + mm], sub ? 0xEEEEu : idx0[b]);
+              acc[b][kMG * g + mm] = mma_sparse<BF16, 0>(sub ? a1[b] : a0[b], blo[cb][mm], bhi[cb][mm],
+                                                               acc[b][kMG * g + mm], sub ? 0xEEEEu : idx0[b]);
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // row-major W (the dense baseline), step s: K halves qq = 0, 1 on
+  // v_mfma_f32_16x16x32, in groups g = (qq, part) whose B fragments
+  // alternate between bq[0] and bq[1] (an even number of groups a step)
+  auto step_rowmajor = [&](int s, u32x4 (&a0)[4], u32x4 (&a1)[4], u32x4 (&na0)[4], u32x4 (&na1)[4],
+                           u32x4 (&bq)[2][kRG]) {
+    const uint8_t* xs = x_stage(s);
+#pragma unroll
+    for (int g = 0; g < 2 * kRParts; g++) {
+      const int qq = g / kRParts, part = g % kRParts;
+      if (g + 1 < 2 * kRParts) {
+        read_bq(xs, (g + 1) / kRParts, (g + 1) % kRParts, bq[(g + 1) & 1]);
+      } else {
+        uint32_t unused;
+        if (s + 1 < n_steps) advance(s);
+        const int sn = min(s + 1, n_steps - 1);
+        read_a(sn, na0, na1, unused);
+        read_bq(x_stage(sn), 0, 0, bq[0]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (active) {
+#pragma unroll
+        for (int mm = 0; mm < kRG; mm++)
+#pragma unroll
+          for (int b = 0; b < 4; b++)
+            acc[b][kRG * part + mm] = mma_dense<BF16>(qq ? a1[b] : a0[b], bq[g & 1][mm], acc[b][kRG * part + mm]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // ---- pipeline: copies kLdsStages - 1 steps ahead
-  constexpr int kAhead = kLdsStages - 1;
 #pragma unroll
   for (int s = 0; s < kAhead; s++) issue(s);  // n_steps >= 2 >= kAhead
-  for (int s = 0; s < n_steps; s++) {
-    // this wave's copies of step s have landed (those of the kAhead - 1
-    // later steps may still be in flight)
-    if (kAhead == 2 && s + 1 < n_steps)
-      wait_copies<kLdsCopies>();
-    else
-      wait_copies<0>();
-    wg_barrier();  // everyone's have; everyone is done reading the stage step s + kAhead fills
-    if (s + kAhead < n_steps) issue(s + kAhead);
-    compute(s);
+  if (kAhead == 2)
+    wait_copies<kLdsCopies>();
+  else
+    wait_copies<0>();
+  wg_barrier();
+  if (kAhead < n_steps) issue(kAhead);
+  u32x4 fa0[4], fa1[4], fb0[4], fb1[4];
+  uint32_t ka, kb;
+  read_a(0, fa0, fa1, ka);
+  if constexpr (SRC_ROWMAJOR) {
+    u32x4 bq[2][kRG];
+    read_bq(x_stage(0), 0, 0, bq[0]);
+    for (int s = 0; s < n_steps; s += 2) {  // n_steps is even
+      step_rowmajor(s, fa0, fa1, fb0, fb1, bq);
+      step_rowmajor(s + 1, fb0, fb1, fa0, fa1, bq);
+    }
+  } else {
+    u32x4 blo[2][kMG], bhi[2][kMG];
+    read_b(x_stage(0), 0, blo[0], bhi[0]);
+    for (int s = 0; s < n_steps; s += 2) {  // n_steps is even
+      step_packed(s, 0, fa0, fa1, ka, fb0, fb1, kb, blo, bhi);
+      step_packed(s + 1, 1, fb0, fb1, kb, fa0, fa1, ka, blo, bhi);
+    }
   }
 
   if constexpr (FUSE) {
@@ -734,9 +806,9 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
 // by a cost model of the LDS-staged kernel fitted to its measured times on
 // the LLaMA-2 7B q_proj, gate_proj and down_proj shapes (32 <= M <= 2048,
 // every width, 1 to 12 ranges; 4% rms error; its pick is the fastest
-// measured choice on 26 of the 30 shapes and 1% slower on average):
-//   t = rounds * (1.9 + tiles * (1.0 + 0.0069 * BM)) us
-//       + with a split: 6.4 us + partial bytes / 3.25 TB/s (second kernel),
+// measured choice on 25 of the 30 shapes and 1% slower on average):
+//   t = rounds * (2.47 + tiles * (0.90 + 0.0075 * BM)) us
+//       + with a split: 6.3 us + partial bytes / 3.28 TB/s (second kernel),
 // rounds = ceil(workgroups / CUs), tiles = tile columns per K range.  A K
 // range holds at least two tile columns, and the partial sums (ranges * M *
 // N * 4 bytes) stay within 2 * N * K bytes.  Then the number of M-groups:
@@ -754,8 +826,8 @@ static double shape_cost_us(int64_t M, int64_t N, int64_t K, int bm, int64_t spl
   const int64_t pairs = (N / kTile + 1) / 2;
   const int64_t blocks = pairs * ((M + bm - 1) / bm) * splits;
   const int64_t rounds = (blocks + cus - 1) / cus;
-  double t = (double)rounds * (1.9 + (double)kt_split * (1.0 + 0.0069 * bm));
-  if (splits > 1) t += 6.4 + (double)splits * (double)M * (double)N * 4.0 / 3.25e6;
+  double t = (double)rounds * (2.47 + (double)kt_split * (0.90 + 0.0075 * bm));
+  if (splits > 1) t += 6.3 + (double)splits * (double)M * (double)N * 4.0 / 3.28e6;
   return t;
 }
 // only_bm: consider that width alone (0: every width).
