@@ -459,7 +459,10 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
 //     instructions, and step s + 1's A fragments and first B fragments are
 //     read right after it, so those reads run under that group and a step
 //     starts with operands in registers (two sets of A fragments; B
-//     fragments alternate between two buffers by group).
+//     fragments alternate between two buffers by group).  Within a group
+//     the next group's reads are spread between the matrix instructions
+//     (one or two after each), so the waves sharing a SIMD do not all
+//     queue at the LDS and then all at the matrix core.
 // LDS per stage: 32 KB of W + BM * 128 bytes of X; three stages up to width
 // 128 (120 KB at 64, 144 KB at 128), two at 192 and 256 (112 and 128 KB),
 // plus the tile entries and, for packed W, the 4 KB table that rebuilds 4:8
@@ -628,7 +631,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   };
   // row-major W: B fragments of K half qq (32 columns), M blocks kRG p .. kRG p + kRG - 1
   // (parts at the larger widths: registers)
-  constexpr int kRG = BM == 256 ? (FUSE ? kNMB / 4 : kNMB / 2) : (BM == 192 && FUSE ? kNMB / 2 : kNMB);
+  constexpr int kRG = BM == 256 ? kNMB / 4 : (BM == 192 ? kNMB / 2 : kNMB);
   constexpr int kRParts = kNMB / kRG;
   auto read_bq = [&](const uint8_t* xs, int qq, int part, u32x4 (&bf)[kRG]) {
 #pragma unroll
@@ -636,11 +639,14 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
       bf[mm] = *reinterpret_cast<const u32x4*>(xs + swz(wm * (BM / 2) + (kRG * part + mm) * 16 + (l & 15), 4 * qq + hl));
   };
   auto x_stage = [&](int s) { return s_x + (s % kLdsStages) * kLdsXStage; };
-  // this wave's A fragments of step s (and the step's tile kind) from its stage
-  auto read_a = [&](int s, u32x4 (&a0)[4], u32x4 (&a1)[4], uint32_t& kind) {
+  // the tile kind of step s (0 for row-major W)
+  auto step_kind = [&](int s) -> uint32_t {
+    if constexpr (SRC_ROWMAJOR) return 0u;
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)s_ent[r_src][s >> 1]) >> 30;
+  };
+  // this wave's A fragments of step s (tile kind `kind`) from its stage
+  auto read_a = [&](int s, uint32_t kind, u32x4 (&a0)[4], u32x4 (&a1)[4]) {
     const uint8_t* ws = s_w + (s % kLdsStages) * kLdsWStage + 1024 * ((r * 8 + 4 * wn) * 2);
-    kind = 0;
-    if constexpr (!SRC_ROWMAJOR) kind = (uint32_t)__builtin_amdgcn_readfirstlane((int)s_ent[r_src][s >> 1]) >> 30;
     const int off1 = kind ? 16 * (l >> 2) : 16 * l;
 #pragma unroll
     for (int b = 0; b < 4; b++) {
@@ -674,6 +680,8 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
                          u32x4 (&na1)[4], uint32_t& nkind, u32x4 (&blo)[2][kMG],
                          u32x4 (&bhi)[2][kMG]) {
     const int h = s & 1;
+    // step s + 1's kind, read early (its fragments' addresses depend on it)
+    nkind = step_kind(min(s + 1, n_steps - 1));
     if (kind == 2) {
       // 4:8: each band's sixteen columns rebuilt into a dense piece's two
       // halves (values in a0, the lane's masks in the codes chunk a1),
@@ -686,7 +694,6 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
       }
       kind = 0;
     }
-    const int nsub = kind == 0 ? 2 : 1;
     uint32_t idx0[4];
 #pragma unroll
     for (int b = 0; b < 4; b++) {
@@ -698,25 +705,49 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
 #pragma unroll
     for (int g = 0; g < kGroups; g++) {
       const int cb = (g + par * kGroups) & 1, nb = (g + 1 + par * kGroups) & 1;
-      if (g + 1 < kGroups) {
+      const bool last = g + 1 == kGroups;
+      if (last && s + 1 < n_steps) advance(s);
+      __builtin_amdgcn_sched_barrier(0);
+      // the first half (a 2:4 tile's only one) with the next group's reads
+      // -- or, in the last group, step s + 1's first fragments -- spread
+      // between its matrix instructions.  (Waves without a row-block of
+      // their own compute on row-block i0's copy and store nothing.)
+#pragma unroll
+      for (int mm = 0; mm < kMG; mm++)
+#pragma unroll
+        for (int b = 0; b < 4; b++)
+          acc[b][kMG * g + mm] = mma_sparse<BF16, 0>(a0[b], blo[cb][mm], bhi[cb][mm], acc[b][kMG * g + mm], idx0[b]);
+      if (!last) {
         read_b(xs, g + 1, blo[nb], bhi[nb]);
       } else {
         // (after the last step: its own stage again, never used)
-        if (s + 1 < n_steps) advance(s);
         const int sn = min(s + 1, n_steps - 1);
-        read_a(sn, na0, na1, nkind);
+        read_a(sn, nkind, na0, na1);
         read_b(x_stage(sn), 0, blo[nb], bhi[nb]);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      if (active) {
-        for (int sub = 0; sub < nsub; sub++) {
+      constexpr int kMma = 4 * kMG;
+      constexpr int kPerMid = (2 * kMG + kMma - 1) / kMma, kPerLast = (8 + 2 * kMG + kMma - 1) / kMma;
+      if (last) {
 #pragma unroll
-          for (int mm = 0; mm < kMG; mm++)
-#pragma unroll
-            for (int b = 0; b < 4; b++)
-              acc[b][kMG * g + mm] = mma_sparse<BF16, 0>(sub ? a1[b] : a0[b], blo[cb][mm], bhi[cb][mm],
-                                                               acc[b][kMG * g + mm], sub ? 0xEEEEu : idx0[b]);
+        for (int i = 0; i < kMma; i++) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // one matrix instruction
+          __builtin_amdgcn_sched_group_barrier(0x100, kPerLast, 0);  // then LDS reads
         }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kMma; i++) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, kPerMid, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (kind == 0) {
+        // dense tile: the second half (positions 2, 3 of each group of four)
+#pragma unroll
+        for (int mm = 0; mm < kMG; mm++)
+#pragma unroll
+          for (int b = 0; b < 4; b++)
+            acc[b][kMG * g + mm] = mma_sparse<BF16, 0>(a1[b], blo[cb][mm], bhi[cb][mm], acc[b][kMG * g + mm], 0xEEEEu);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -730,22 +761,36 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
 #pragma unroll
     for (int g = 0; g < 2 * kRParts; g++) {
       const int qq = g / kRParts, part = g % kRParts;
-      if (g + 1 < 2 * kRParts) {
+      const bool last = g + 1 == 2 * kRParts;
+      if (last && s + 1 < n_steps) advance(s);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int mm = 0; mm < kRG; mm++)
+#pragma unroll
+        for (int b = 0; b < 4; b++)
+          acc[b][kRG * part + mm] = mma_dense<BF16>(qq ? a1[b] : a0[b], bq[g & 1][mm], acc[b][kRG * part + mm]);
+      if (!last) {
         read_bq(xs, (g + 1) / kRParts, (g + 1) % kRParts, bq[(g + 1) & 1]);
       } else {
-        uint32_t unused;
-        if (s + 1 < n_steps) advance(s);
         const int sn = min(s + 1, n_steps - 1);
-        read_a(sn, na0, na1, unused);
+        read_a(sn, 0u, na0, na1);
         read_bq(x_stage(sn), 0, 0, bq[0]);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      if (active) {
+      // the reads spread between the matrix instructions
+      constexpr int kMma = 4 * kRG;
+      constexpr int kPerMid = (kRG + kMma - 1) / kMma, kPerLast = (8 + kRG + kMma - 1) / kMma;
+      if (last) {
 #pragma unroll
-        for (int mm = 0; mm < kRG; mm++)
+        for (int i = 0; i < kMma; i++) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, kPerLast, 0);
+        }
+      } else {
 #pragma unroll
-          for (int b = 0; b < 4; b++)
-            acc[b][kRG * part + mm] = mma_dense<BF16>(qq ? a1[b] : a0[b], bq[g & 1][mm], acc[b][kRG * part + mm]);
+        for (int i = 0; i < kMma; i++) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, kPerMid, 0);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -760,8 +805,8 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   wg_barrier();
   if (kAhead < n_steps) issue(kAhead);
   u32x4 fa0[4], fa1[4], fb0[4], fb1[4];
-  uint32_t ka, kb;
-  read_a(0, fa0, fa1, ka);
+  uint32_t ka = step_kind(0), kb;
+  read_a(0, ka, fa0, fa1);
   if constexpr (SRC_ROWMAJOR) {
     u32x4 bq[2][kRG];
     read_bq(x_stage(0), 0, 0, bq[0]);
@@ -805,10 +850,10 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
 // Launch shape: the M-block width BM and the number of K ranges, chosen
 // by a cost model of the LDS-staged kernel fitted to its measured times on
 // the LLaMA-2 7B q_proj, gate_proj and down_proj shapes (32 <= M <= 2048,
-// every width, 1 to 12 ranges; 4% rms error; its pick is the fastest
-// measured choice on 25 of the 30 shapes and 1% slower on average):
-//   t = rounds * (2.47 + tiles * (0.90 + 0.0075 * BM)) us
-//       + with a split: 6.3 us + partial bytes / 3.28 TB/s (second kernel),
+// every width, 1 to 12 ranges; 5% rms error; its pick is the fastest
+// measured choice on 24 of the 30 shapes and 1.5% slower on average):
+//   t = rounds * (2.42 + tiles * (0.835 + 0.0071 * BM)) us
+//       + with a split: 6.3 us + partial bytes / 3.16 TB/s (second kernel),
 // rounds = ceil(workgroups / CUs), tiles = tile columns per K range.  A K
 // range holds at least two tile columns, and the partial sums (ranges * M *
 // N * 4 bytes) stay within 2 * N * K bytes.  Then the number of M-groups:
@@ -826,8 +871,8 @@ static double shape_cost_us(int64_t M, int64_t N, int64_t K, int bm, int64_t spl
   const int64_t pairs = (N / kTile + 1) / 2;
   const int64_t blocks = pairs * ((M + bm - 1) / bm) * splits;
   const int64_t rounds = (blocks + cus - 1) / cus;
-  double t = (double)rounds * (2.47 + (double)kt_split * (0.90 + 0.0075 * bm));
-  if (splits > 1) t += 6.3 + (double)splits * (double)M * (double)N * 4.0 / 3.28e6;
+  double t = (double)rounds * (2.42 + (double)kt_split * (0.835 + 0.0071 * bm));
+  if (splits > 1) t += 6.3 + (double)splits * (double)M * (double)N * 4.0 / 3.16e6;
   return t;
 }
 // only_bm: consider that width alone (0: every width).

@@ -259,6 +259,26 @@ def test_prefill_every_kernel_f16_exact(variant):
     assert np.array_equal(host_f64(y), ref), variant
 
 
+@pytest.mark.parametrize("variant", [v for v in PREFILL_KERNELS if v.endswith("_lds")])
+def test_prefill_lds_short_k(variant):
+    """The LDS-staged kernels at one to three tile columns (two to six
+    64-column steps: the pipeline's first step is also its last-but-one or
+    last), with and without a K split, packed and row-major W."""
+    for K in (128, 256, 384):
+        N = 384
+        p = inputs.make_custom("bf16", N, K, 40 + K, "bernoulli", 0.5, "uniform")
+        pw, W = _pack(p)
+        pd = inputs.make_custom("bf16", N, K, 40 + K, "dense", 0.0, "top2")
+        ws = torch.empty(2 * N * K, dtype=torch.uint8, device="cuda")
+        for M in (40, 300):
+            Xb = inputs.make_custom_x("bf16", M, K, 50 + M)
+            X = dev_bits(Xb, "bf16")
+            for w in (ws, None):
+                tag = f"{variant} K={K} M={M} ws={'yes' if w is not None else 'no'}"
+                assert_close(patch.gemm(X, pw, variant=variant, workspace=w), _ref(p, Xb), what=tag)
+                assert_close(patch.dense_gemm(X, W, variant=variant, workspace=w), _ref(pd, Xb), what="dense " + tag)
+
+
 # ------------------------------------------------------------------ exact cases
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_identity_x_gives_masked_weights_exactly(dtype):
