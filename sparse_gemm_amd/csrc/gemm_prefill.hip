@@ -851,10 +851,12 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
 // by a cost model of the LDS-staged kernel fitted to its measured times on
 // the LLaMA-2 7B q_proj, gate_proj and down_proj shapes (32 <= M <= 2048,
 // every width, 1 to 12 ranges; 5% rms error; its pick is the fastest
-// measured choice on 24 of the 30 shapes and 1.5% slower on average):
-//   t = rounds * (2.42 + tiles * (0.835 + 0.0071 * BM)) us
-//       + with a split: 6.3 us + partial bytes / 3.16 TB/s (second kernel),
-// rounds = ceil(workgroups / CUs), tiles = tile columns per K range.  A K
+// measured choice on 25 of the 30 shapes and 1% slower on average):
+//   t = rounds * (2.33 + tiles * (0.79 * (1 + 0.086 * fill) + 0.0072 * BM)) us
+//       + with a split: 6.4 us + partial bytes / 3.24 TB/s (second kernel),
+// rounds = ceil(workgroups / CUs), fill = the busy fraction of the CUs in a
+// full round (a tile's W copy costs more when every CU streams at once),
+// tiles = tile columns per K range.  A K
 // range holds at least two tile columns, and the partial sums (ranges * M *
 // N * 4 bytes) stay within 2 * N * K bytes.  Then the number of M-groups:
 // each XCD (one L2) works on about 1/8 of the output blocks in the
@@ -871,8 +873,9 @@ static double shape_cost_us(int64_t M, int64_t N, int64_t K, int bm, int64_t spl
   const int64_t pairs = (N / kTile + 1) / 2;
   const int64_t blocks = pairs * ((M + bm - 1) / bm) * splits;
   const int64_t rounds = (blocks + cus - 1) / cus;
-  double t = (double)rounds * (2.42 + (double)kt_split * (0.835 + 0.0071 * bm));
-  if (splits > 1) t += 6.3 + (double)splits * (double)M * (double)N * 4.0 / 3.16e6;
+  const double fill = (double)std::min<int64_t>(blocks, cus) / (double)cus;
+  double t = (double)rounds * (2.33 + (double)kt_split * (0.79 * (1.0 + 0.086 * fill) + 0.0072 * bm));
+  if (splits > 1) t += 6.4 + (double)splits * (double)M * (double)N * 4.0 / 3.24e6;
   return t;
 }
 // only_bm: consider that width alone (0: every width).
