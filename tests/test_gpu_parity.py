@@ -116,6 +116,20 @@ def test_gemm_small_ragged(dtype, M):
         assert_close(y32, ref, f32=True, what=f"{dtype} M={M} {v} f32")
 
 
+def test_empty_m():
+    """M = 0: every variant returns an empty product and launches nothing
+    (the boundary accepts it before looking at the pointers)."""
+    p = inputs.make_custom("bf16", 384, 640, 7, "bernoulli", 0.5, "top2")
+    pw, W = _pack(p)
+    X = torch.empty((0, 640), dtype=torch.bfloat16, device="cuda")
+    for v in ("auto", "decode", "prefill", "prefill_w64_lds", "prefill_w256"):
+        for od in (None, torch.float32):
+            y = patch.gemm(X, pw, out_dtype=od, variant=v)
+            assert tuple(y.shape) == (0, 384), v
+    assert tuple(patch.dense_gemm(X, W).shape) == (0, 384)
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("M", [1, 16, 17, 300])
 def test_dense_baseline_small(dtype, M):
