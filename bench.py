@@ -7,13 +7,16 @@ end-to-end numbers (1.18x-1.38x over dense, LLaMA-2 7B on an A6000, section 4
 "Speedup & Efficiency"), so there is no published kernel figure to compare
 with and vs_baseline is null.
 
-Default workload: the LLaMA-2-7B q_proj decode GEMM -- W 4096 x 4096 bf16,
-half of the 1024 tiles 2:4 (25% sparsity), top-2-of-4 masks, X with
-M = 1, 4 and 16 rows.  One step = one patch_gemm call for each M (every
-kernel of the hot path at inference: the decode hybrid GEMM with its
+Default workload (the headline line): the LLaMA-2-7B MLP prefill GEMMs --
+gate/up 11008 x 4096 and down 4096 x 11008, bf16, 2202 of their 2752
+128 x 128 tiles 2:4 (40% sparsity), top-2-of-4 masks, X of 2048 tokens.
+One step = one patch_gemm on each matrix (the hybrid GEMM with its
 epilogue; packing is offline and timed separately).  Inputs are resident in
-HBM; 40 copies of the packed weight are rotated so the 256 MB Infinity Cache
-cannot serve them.
+HBM; every launch reads its own copy of the packed weight (>= 1 GiB rotated
+per matrix) so the 256 MB Infinity Cache cannot serve them.  The line also
+carries the decode workload (q_proj 4096 x 4096, M = 1, 4, 16), a sparsity
+sweep on three shapes, ceilings measured in the same run and the CPU
+oracle's rate.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--report out.jsonl]
 
@@ -76,23 +79,28 @@ def _event():
 
 
 def time_launches(calls, steps, warmup, batches=1):
-    """calls: list of (key, fn(k)).  Returns
+    """calls: list of (key, fn(i)); fn(i) issues launch i of that call (it
+    picks its weight copy from i).  Returns
       * ms per step, a step running every call once, back to back (one event
-        pair around all `steps` steps), and
+        pair around all `steps` steps; step k gives call c the index
+        (warmup + k) * len(calls) + c, so no two launches of a step share a
+        copy), and
       * {key: [ms per launch of each batch]}, each call timed on its own:
-        `batches` batches of `steps` launches back to back, one event pair
-        around each batch, divided by `steps`.
+        `batches` batches of `steps` launches back to back (indices warmup,
+        warmup + 1, ...), one event pair around each batch, divided by
+        `steps`.
     Events are recorded on the current stream, the one the launches use."""
     import torch
 
+    n = len(calls)
     for k in range(warmup):
-        for _, fn in calls:
-            fn(k)
+        for c, (_, fn) in enumerate(calls):
+            fn(k * n + c)
     torch.cuda.synchronize()
     a = _event()
     for k in range(steps):
-        for _, fn in calls:
-            fn(warmup + k)
+        for c, (_, fn) in enumerate(calls):
+            fn((warmup + k) * n + c)
     b = _event()
     torch.cuda.synchronize()
     ms_step = a.elapsed_time(b) / steps
@@ -109,6 +117,37 @@ def time_launches(calls, steps, warmup, batches=1):
             torch.cuda.synchronize()
             per[key].append(a.elapsed_time(b) / steps)
     return ms_step, per
+
+
+def time_steps_events(calls, steps, warmup):
+    """The timed region of the headline: `steps` steps, each running every
+    call once (call c of step k gets index (warmup + k) * len(calls) + c),
+    issued back to back on the current stream with a HIP event recorded
+    before every launch and one after the last.  Returns ms per step (first
+    to last event / steps) and {key: [ms of each of its launches]} (event to
+    next event), so the launches' durations add up to the step time exactly.
+    Every launch here is long against its host cost, so the stream never
+    waits for the host."""
+    import torch
+
+    n = len(calls)
+    for k in range(warmup):
+        for c, (_, fn) in enumerate(calls):
+            fn(k * n + c)
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps * n + 1)]
+    i = 0
+    for k in range(steps):
+        for c, (_, fn) in enumerate(calls):
+            evs[i].record()
+            fn((warmup + k) * n + c)
+            i += 1
+    evs[i].record()
+    torch.cuda.synchronize()
+    per = {key: [] for key, _ in calls}
+    for j in range(steps * n):
+        per[calls[j % n][0]].append(evs[j].elapsed_time(evs[j + 1]))
+    return evs[0].elapsed_time(evs[-1]) / steps, per
 
 
 def _capture(fns):
@@ -133,20 +172,22 @@ def _capture(fns):
 
 
 def time_graphs(calls, steps, warmup, batches=1):
-    """As time_launches, but the launches are captured in HIP graphs and the
-    graphs replayed, so host launch overhead is out of the timed region:
+    """As time_launches (same launch indices), but the launches are captured
+    in HIP graphs and the graphs replayed, so host launch overhead is out of
+    the timed region:
       * ms per step: one graph of `steps` steps (every call once a step, back
         to back), replayed once untimed and once between one event pair;
       * {key: [ms per launch of each batch]}: per call, one graph of `steps`
-        launches, replayed `batches` times, each between one event pair.
-    Step k of either uses rotation index warmup + k, as the eager timing."""
+        launches, replayed `batches` times, each between one event pair."""
     import torch
 
+    n = len(calls)
     for k in range(warmup):
-        for _, fn in calls:
-            fn(k)
+        for c, (_, fn) in enumerate(calls):
+            fn(k * n + c)
     torch.cuda.synchronize()
-    g = _capture([(lambda fn=fn, k=k: fn(warmup + k)) for k in range(steps) for _, fn in calls])
+    g = _capture([(lambda fn=fn, i=(warmup + k) * n + c: fn(i)) for k in range(steps)
+                  for c, (_, fn) in enumerate(calls)])
     g.replay()
     torch.cuda.synchronize()
     a = _event()
@@ -173,9 +214,13 @@ def time_graphs(calls, steps, warmup, batches=1):
 
 
 def rotate(t, nbytes_each):
-    import torch
-
-    n = max(2, min(64, int(np.ceil(ROTATE_BYTES / max(1, nbytes_each)))))
+    """t and copies of it, >= ROTATE_BYTES in all (so the 256 MB Infinity
+    Cache cannot hold them); the count is prime to 2 and 3, so launches that
+    index the copies with a stride of 2 or 3 (a step's calls) still visit
+    every copy."""
+    n = max(5, min(65, int(np.ceil(ROTATE_BYTES / max(1, nbytes_each)))))
+    while n % 2 == 0 or n % 3 == 0:
+        n += 1
     return [t] + [t.clone() for _ in range(n - 1)]
 
 
@@ -218,19 +263,20 @@ def gemm_set(cfg_name, mi, si, Ms, steps, warmup, with_hipblaslt=True, fraction=
     Ys = {M: torch.empty((M, p.N), dtype=tdt, device="cuda") for M in Ms}
     desc = pw.desc
 
+    # f(i): launch i on weight copy i mod the copies
     def hyb(M):
-        def f(k):
-            patch.gemm(Xs[M], patch.PackedWeight(blobs[k % len(blobs)], desc), out=Ys[M])
+        def f(i):
+            patch.gemm(Xs[M], patch.PackedWeight(blobs[i % len(blobs)], desc), out=Ys[M])
         return f
 
     def dense(M):
-        def f(k):
-            patch.dense_gemm(Xs[M], Ws[k % len(Ws)], out=Ys[M])
+        def f(i):
+            patch.dense_gemm(Xs[M], Ws[i % len(Ws)], out=Ys[M])
         return f
 
     def blas(M):
-        def f(k):
-            torch.matmul(Xs[M], Ws[k % len(Ws)].t(), out=Ys[M])
+        def f(i):
+            torch.matmul(Xs[M], Ws[i % len(Ws)].t(), out=Ys[M])
         return f
 
     # our kernels: graph replays (launch overhead out of the timed region)
@@ -362,39 +408,303 @@ def ingest_counters(dirs):
     print(json.dumps(out))
 
 
-def cpu_baseline(p, Ms, cfg):
-    """The oracle, as it stands, on a bounded sample of the same step."""
+def cpu_baseline(problems, Ms, sample_rows, budget_s=10.0):
+    """The oracle, as it stands, on a bounded sample of the same step: the
+    first `sample_rows` rows of each call's X against the full weights
+    (every output column, every tile), repeated for about `budget_s`
+    seconds; reported as dense-equivalent TFLOP/s of the rows it did."""
     import oracle
     from sparse_gemm_amd import inputs
 
-    Xb = {M: inputs.make_x(cfg, M, p.K) for M in Ms}
-    flops = sum(2.0 * M * p.N * p.K for M in Ms)
+    work = []
+    for (p, cfg, mi), M in zip(problems, Ms):
+        rows = min(M, sample_rows)
+        work.append((p, inputs.make_x(cfg, M, p.K, matrix_index=mi)[:rows], rows))
+    flops = sum(2.0 * rows * p.N * p.K for p, _, rows in work)
     reps, t0 = 0, time.perf_counter()
     while True:
-        for M in Ms:
-            oracle.gemm_f64(p.dtype, Xb[M], p.w, p.tile_map, p.mask)
+        for p, xb, _ in work:
+            oracle.gemm_f64(p.dtype, xb, p.w, p.tile_map, p.mask)
         reps += 1
         el = time.perf_counter() - t0
-        if el > 10.0 or reps >= 5000:
+        if el > budget_s or reps >= 5000:
             break
+    desc = "; ".join(f"{rows} of {M} rows of X against the full {p.N}x{p.K} weight" for (p, _, rows), M in
+                     zip(work, Ms))
     return dict(value=flops * reps / el / 1e12, unit="TFLOP/s (dense-equivalent)", cores=oracle.num_threads(),
                 kind="oracle",
-                sample=f"{reps} full step(s): oracle_gemm_f64 (fp64) for M in {list(Ms)} on the same "
-                       f"{p.N}x{p.K} weights, tile map and masks; {el:.1f} s wall")
+                sample=f"{reps} repetition(s) of oracle_gemm_f64 (fp64, plain C) on a row sample of the step "
+                       f"({desc}; same weights, tile maps and masks); {el:.1f} s wall")
+
+
+def measure_ceilings(read_bytes, steps=20):
+    """What one launch can reach on this device, measured in this run:
+    streaming reads of each byte count in `read_bytes` (distinct buffers
+    rotated past the Infinity Cache, as the GEMM weights are) and the
+    sustained rate of each matrix instruction the kernels use."""
+    import torch
+
+    from sparse_gemm_amd import patch
+
+    out = {"hbm_read": {}, "matrix_core_tflops": {}}
+    sink = torch.zeros(1 << 16, dtype=torch.uint8, device="cuda")
+    for nb in read_bytes:
+        nb = int(nb) // 16 * 16
+        bufs = rotate(torch.ones(nb, dtype=torch.uint8, device="cuda"), nb)
+        _, per = time_graphs([("r", lambda i: patch.probe_stream_read(bufs[i % len(bufs)], sink))], steps, 5, 3)
+        t = median(per["r"]) * 1e-3
+        out["hbm_read"][str(nb)] = dict(us=t * 1e6, gbps=nb / t / 1e9, frac_of_peak=nb / t / 1e9 / HBM_PEAK_GBS)
+        del bufs
+        torch.cuda.empty_cache()
+    names = {0: "mfma_f32_16x16x32_bf16", 1: "smfmac_f32_16x16x64_bf16", 2: "mfma_f32_32x32x16_bf16",
+             3: "smfmac_f32_32x32x32_bf16"}
+    wgs = 2 * 256  # two workgroups of four waves a CU
+    for kind, name in names.items():
+        flops = patch.probe_matrix_rate(kind, 64, wgs, sink)  # warm-up
+        iters = 4000
+        torch.cuda.synchronize()
+        a = _event()
+        flops = patch.probe_matrix_rate(kind, iters, wgs, sink)
+        b = _event()
+        torch.cuda.synchronize()
+        out["matrix_core_tflops"][name] = flops / (a.elapsed_time(b) * 1e-3) / 1e12
+    out["note"] = ("hbm_read: patch_probe_stream_read over that many bytes (16-byte loads, one pass), median of 3 "
+                   "graph replays of 20 launches on rotated buffers; matrix_core_tflops: patch_probe_matrix_rate, "
+                   "2 workgroups of 4 waves a CU, independent accumulator chains, dense-equivalent flops for the "
+                   "sparse instructions; datasheet peaks: 8000 GB/s, 2516.6 TFLOP/s dense bf16 (x2 with 2:4)")
+    return out
+
+
+def t_mfma_s(M, T, ns):
+    """Matrix-core time of one launch at the blended datasheet peak: dense
+    tiles at the dense bf16 peak, 2:4 tiles' dense-equivalent work at twice
+    it (the sparse instruction's rate)."""
+    return 2.0 * M * 128 * 128 * ((T - ns) / MFMA_PEAK_BF16_TFLOPS + ns / (2 * MFMA_PEAK_BF16_TFLOPS)) / 1e12
+
+
+def eff_flops(M, T, ns):
+    """Work the hybrid GEMM actually does: 32768 flop per token per dense
+    tile, 16384 per 2:4 tile."""
+    return 2.0 * M * 128 * 128 * ((T - ns) + 0.5 * ns)
+
+
+def headline_prefill(args):
+    """The prefill MLP workload (LLaMA-2-7B gate/up 11008 x 4096 and down
+    4096 x 11008, bf16, 80% of tiles 2:4 (2202 of 2752), top-2-of-4 masks,
+    X 2048 x K): one step = one hybrid GEMM on each matrix."""
+    import torch
+
+    from sparse_gemm_amd import inputs, patch
+
+    cfg = inputs.CONFIGS["prefill_mlp"]
+    M = cfg.Ms[0]
+    mats = []
+    for mi in range(len(cfg.matrices)):
+        p = inputs.make_weights(cfg, mi, 0)
+        W = dev_bits(p.w, torch.bfloat16)
+        mk = torch.from_numpy(p.mask).cuda()
+        pw, pack_ms = pack_timed(W, p.tile_map, mk)
+        p0 = patch.pack(W, np.zeros_like(p.tile_map), mk)  # the same weights with every tile dense
+        del mk
+        X = dev_bits(inputs.make_x(cfg, M, p.K, matrix_index=mi), torch.bfloat16)
+        mats.append(dict(name=cfg.matrices[mi].name, p=p, pw=pw, pack_ms=pack_ms, blobs=rotate(pw.blob, pw.nbytes),
+                         blobs0=rotate(p0.blob, p0.nbytes), desc0=p0.desc, Ws=rotate(W, W.numel() * 2), X=X,
+                         Y=torch.empty((M, p.N), dtype=torch.bfloat16, device="cuda")))
+        del p0, W
+
+    def hyb(m):
+        return lambda i: patch.gemm(m["X"], patch.PackedWeight(m["blobs"][i % len(m["blobs"])], m["pw"].desc),
+                                    out=m["Y"])
+
+    def hyb0(m):
+        return lambda i: patch.gemm(m["X"], patch.PackedWeight(m["blobs0"][i % len(m["blobs0"])], m["desc0"]),
+                                    out=m["Y"])
+
+    def dense(m):
+        return lambda i: patch.dense_gemm(m["X"], m["Ws"][i % len(m["Ws"])], out=m["Y"])
+
+    def blas(m):
+        return lambda i: torch.matmul(m["X"], m["Ws"][i % len(m["Ws"])].t(), out=m["Y"])
+
+    steps, warmup = args.steps, args.warmup
+    ms_step, per = time_steps_events([(m["name"], hyb(m)) for m in mats], steps, warmup)
+    ms_step_graph, _ = time_graphs([(m["name"], hyb(m)) for m in mats], steps, warmup)
+    ms_dense, per_dense = time_steps_events([(m["name"], dense(m)) for m in mats], steps, warmup)
+    ms_s0, per_s0 = time_steps_events([(m["name"], hyb0(m)) for m in mats], steps, warmup)
+    ms_blas, per_blas = time_steps_events([(m["name"], blas(m)) for m in mats], steps, warmup)
+
+    flops_step = sum(2.0 * M * m["p"].N * m["p"].K for m in mats)
+    per_matrix = {}
+    eff_sum, t_sum, n_launch, tm_sum = 0.0, 0.0, 0, 0.0
+    for m in mats:
+        p = m["p"]
+        T, ns = int(p.tile_map.size), int(p.tile_map.sum())
+        t = mean(per[m["name"]]) * 1e-3
+        tm = t_mfma_s(M, T, ns)
+        per_matrix[m["name"]] = dict(
+            N=p.N, K=p.K, M=M, sparse_tiles=ns, tiles=T, us=t * 1e6, us_min=min(per[m["name"]]) * 1e3,
+            us_max=max(per[m["name"]]) * 1e3, tflops_dense_equiv=2.0 * M * p.N * p.K / t / 1e12,
+            tflops_effective=eff_flops(M, T, ns) / t / 1e12, roofline_us=tm * 1e6, roofline_frac=tm / t,
+            dense_us=mean(per_dense[m["name"]]) * 1e3, hybrid_all_dense_us=mean(per_s0[m["name"]]) * 1e3,
+            hipblaslt_us=mean(per_blas[m["name"]]) * 1e3,
+            speedup_vs_dense=mean(per_dense[m["name"]]) * 1e-3 / t,
+            speedup_vs_hybrid_all_dense=mean(per_s0[m["name"]]) * 1e-3 / t,
+            speedup_vs_hipblaslt=mean(per_blas[m["name"]]) * 1e-3 / t,
+            pack_us=m["pack_ms"] * 1e3, pack_gbps=(3 * p.N * p.K + m["pw"].nbytes) / (m["pack_ms"] * 1e-3) / 1e9,
+            weight_copies_rotated=len(m["blobs"]))
+        eff_sum += eff_flops(M, T, ns) * len(per[m["name"]])
+        t_sum += sum(per[m["name"]]) * 1e-3
+        tm_sum += tm * len(per[m["name"]])
+        n_launch += len(per[m["name"]])
+    avg_t = t_sum / n_launch
+    achieved = eff_sum / t_sum / 1e12
+    traffic = traffic_for("prefill", M)
+    line = {
+        "metric": "hybrid GEMM TFLOP/s (dense-equiv) + speedup vs dense, LLaMA-2-7B shapes",
+        "value": flops_step / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) X, N(0,0.02) W; LLaMA-2-7B MLP shapes, no weights)",
+        "config": {
+            "workload": "prefill_mlp: LLaMA-2-7B MLP GEMMs gate/up 11008x4096 and down 4096x11008, bf16, "
+                        "2202 of 2752 128x128 tiles 2:4 (40% sparsity), top-2-of-4 masks, X 2048 tokens; "
+                        "one step = patch_gemm on each of the two matrices",
+            "M": M, "matrices": [dict(name=m["name"], N=m["p"].N, K=m["p"].K) for m in mats],
+            "weight_copies_rotated": [len(m["blobs"]) for m in mats],
+        },
+        "timing": "one event before every launch and one after the last, on the launch stream; the K steps issued "
+                  "back to back (each launch on its own weight copy, >= 1 GiB rotated per matrix); ms_per_step = "
+                  "first to last event / K; per-launch times = event to next event",
+        "ms_per_step_graph": ms_step_graph,
+        "speedup_vs_dense_step": ms_dense / ms_step,
+        "speedup_vs_hybrid_all_dense_step": ms_s0 / ms_step,
+        "speedup_vs_hipblaslt_step": ms_blas / ms_step,
+        "per_matrix": per_matrix,
+        "roofline": {
+            "kernel": "prefill hybrid GEMM (packed W), both matrices' launches",
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": MFMA_PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / MFMA_PEAK_BF16_TFLOPS,
+            "traffic": traffic,
+            "flops_per_launch_effective": eff_sum / n_launch,
+            "avg_launch_us": avg_t * 1e6,
+            "roofline_us_per_launch": tm_sum / n_launch * 1e6,
+            "note": "achieved = effective flops (32768 a token a dense tile, 16384 a 2:4 tile) / launch time; "
+                    "effective work at the blended matrix-core peak (dense tiles at 2516.6, 2:4 tiles at twice "
+                    "that, dense-equivalent) runs at exactly 2516.6 TFLOP/s, so frac = roofline time / time",
+        },
+    }
+    return line, mats
+
+
+def decode_extra(args):
+    """The decode workload (LLaMA-2-7B q_proj 4096 x 4096, half the tiles
+    2:4, M = 1, 4, 16): graph replays, each launch on its own weight copy."""
+    import torch
+
+    from sparse_gemm_amd import inputs, patch
+
+    cfg = inputs.CONFIGS["decode"]
+    Ms = cfg.Ms
+    res = gemm_set("decode", 0, 0, Ms, args.steps, args.warmup, batches=3)
+    p = res["p"]
+    ns, T = int(p.tile_map.sum()), int(p.tile_map.size)
+    summ = summarize(res, Ms)
+    t_sum = sum(median(res["per"][M]) for M in Ms) * 1e-3
+    b_sum = sum(algo_bytes(p.N, p.K, M, ns) for M in Ms)
+    tr = [traffic_for("decode", M) for M in Ms]
+    return {
+        "workload": "decode: q_proj W 4096x4096 bf16, 512 of 1024 tiles 2:4 (25% sparsity), top-2-of-4 masks, "
+                    "X M in {1,4,16}; one step = patch_gemm at each M, each launch on its own weight copy",
+        "ms_per_step": res["ms_step"],
+        "tflops_dense_equiv_step": sum(2.0 * M * p.N * p.K for M in Ms) / (res["ms_step"] * 1e-3) / 1e12,
+        "sum_of_per_M_launches_ms": t_sum * 1e3,
+        "speedup_vs_dense_step": res["ms_step_dense"] / res["ms_step"],
+        "per_M": {str(M): summ[M] for M in Ms},
+        "roofline": {"kernel": "decode hybrid GEMM", "bound": "hbm", "achieved": b_sum / t_sum / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": b_sum / t_sum / 1e9 / HBM_PEAK_GBS,
+                     "traffic": (sum(tr) / len(tr)) if all(x is not None for x in tr) else None,
+                     "bytes_per_launch_algorithmic": b_sum / len(Ms), "avg_launch_us": t_sum / len(Ms) * 1e6},
+        "blob_bytes": res["pw"].nbytes,
+        "weight_copies_rotated": res["n_copies"],
+    }
+
+
+def sweep_compact(steps, warmup, Ms=(1, 2048)):
+    """The sparsity sweep on three LLaMA-2-7B shapes (q_proj, gate_proj,
+    down_proj) at s = 0, .25, .5, .75, 1 and M in Ms: hybrid time, the
+    same-shape dense kernel, and speedups; `monotone` says whether the
+    speedup over the dense kernel rises strictly with s."""
+    import torch
+
+    from sparse_gemm_amd import inputs, patch
+
+    cfg = inputs.CONFIGS["sweep"]
+    out = []
+    for mi in (0, 4, 6):
+        p = inputs.make_weights(cfg, mi, 0)
+        W = dev_bits(p.w, torch.bfloat16)
+        mk = torch.from_numpy(p.mask).cuda()
+        Ws = rotate(W, W.numel() * 2)
+        Xs = {M: dev_bits(inputs.make_x(cfg, M, p.K, matrix_index=mi), torch.bfloat16) for M in Ms}
+        Y = {M: torch.empty((M, p.N), dtype=torch.bfloat16, device="cuda") for M in Ms}
+        _, per_d = time_graphs([(M, (lambda i, M=M: patch.dense_gemm(Xs[M], Ws[i % len(Ws)], out=Y[M])))
+                                for M in Ms], steps, warmup, 3)
+        del Ws
+        rec = {M: dict(matrix=cfg.matrices[mi].name, N=p.N, K=p.K, M=M, s=[], us=[], dense_us=median(per_d[M]) * 1e3,
+                       roofline_frac=[]) for M in Ms}
+        for si, frac in enumerate(cfg.fractions):
+            q = inputs.make_weights(cfg, mi, si, reuse=p)
+            pw = patch.pack(W, q.tile_map, mk)
+            blobs = rotate(pw.blob, pw.nbytes)
+            _, per = time_graphs([(M, (lambda i, M=M: patch.gemm(Xs[M], patch.PackedWeight(blobs[i % len(blobs)],
+                                                                                            pw.desc), out=Y[M])))
+                                  for M in Ms], steps, warmup, 3)
+            ns, T = int(q.tile_map.sum()), int(q.tile_map.size)
+            for M in Ms:
+                t = median(per[M]) * 1e-3
+                r = rec[M]
+                r["s"].append(ns / T)
+                r["us"].append(t * 1e6)
+                t_hbm = algo_bytes(p.N, p.K, M, ns) / (HBM_PEAK_GBS * 1e9)
+                r["roofline_frac"].append(max(t_hbm, t_mfma_s(M, T, ns)) / t)
+            del blobs, pw
+            torch.cuda.empty_cache()
+        for M in Ms:
+            r = rec[M]
+            r["speedup_vs_dense"] = [r["dense_us"] / u for u in r["us"]]
+            r["speedup_vs_hybrid_s0"] = [r["us"][0] / u for u in r["us"]]
+            sp = r["speedup_vs_dense"]
+            r["monotone"] = all(b > a for a, b in zip(sp, sp[1:]))
+            out.append(r)
+        del W, mk, Xs, Y
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="headline only (no decode workload, sweep or ceilings): for profiling")
     ap.add_argument("--report", default=None, help="also write the full sweep as JSON lines to this path")
     ap.add_argument("--report-steps", type=int, default=100, help="launches per timed batch in the report")
     ap.add_argument("--report-batches", type=int, default=10, help="timed batches per point in the report (median)")
-    ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill_mlp", "imbalanced_13b", "sampler", "fine_mask", "n48"],
-                    help="decode (default: the q_proj decode GEMM), a prefill workload or the mask sampler, "
+    ap.add_argument("--workload", default="prefill_mlp",
+                    choices=["prefill_mlp", "decode", "imbalanced_13b", "sampler", "fine_mask", "n48"],
+                    help="prefill_mlp (default: the headline line); the others print that workload's lines, "
                          "for profiling")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for rocprofv3 byte counters)")
@@ -431,68 +741,36 @@ def main():
         for rec in fn(args.steps, args.warmup, 1):
             print(json.dumps(rec), flush=True)
         return
-    if args.workload != "decode":
+    if args.workload == "imbalanced_13b":
         run_prefill_workload(args)
         return
-    cfg = inputs.CONFIGS["decode"]
-    Ms = cfg.Ms
-    res = gemm_set("decode", 0, 0, Ms, args.steps, args.warmup)
-    p = res["p"]
-    ns = int(p.tile_map.sum())
-    summ = summarize(res, Ms)
-    flops_step = sum(2.0 * M * p.N * p.K for M in Ms)
-    value = flops_step / (res["ms_step"] * 1e-3) / 1e12
+    if args.workload == "decode":
+        print(json.dumps(decode_extra(args)), flush=True)
+        return
 
-    # dominant kernel: the decode hybrid GEMM (all three launches of a step)
-    t_sum = sum(mean(res["per"][M]) for M in Ms) * 1e-3
-    b_sum = sum(algo_bytes(p.N, p.K, M, ns) for M in Ms)
-    achieved = b_sum / t_sum / 1e9
-    traffic = None
-    tr = [traffic_for("decode", M) for M in Ms]
-    if all(x is not None for x in tr):
-        traffic = sum(tr) / len(tr)
-    line = {
-        "metric": "hybrid GEMM TFLOP/s (dense-equiv) + speedup vs dense, LLaMA-2-7B shapes",
-        "value": value,
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": res["ms_step"],
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) X, N(0,0.02) W; LLaMA-2-7B q_proj shape, no weights)",
-        "config": {
-            "workload": "decode: q_proj W 4096x4096 bf16, 512 of 1024 128x128 tiles 2:4 (25% sparsity), "
-                        "top-2-of-4 masks, X M in {1,4,16}; one step = patch_gemm at each M",
-            "N": p.N, "K": p.K, "Ms": list(Ms), "sparse_tiles": ns, "tiles": int(p.tile_map.size),
-            "weight_copies_rotated": res["n_copies"],
-        },
-        "ms_per_step_eager": res["ms_step_eager"],
-        "timing": "value and ms_per_step: one HIP graph of the K steps (3 patch_gemm launches each, cycling the "
-                  "weight copies), replayed between one event pair; ms_per_step_eager: the same launches issued "
-                  "from Python back to back",
-        "speedup_vs_dense_step": res["ms_step_dense"] / res["ms_step"],
-        "per_M": {str(M): summ[M] for M in Ms},
-        "pack": {"us": res["pack_ms"] * 1e3,
-                 "gbps": (2 * p.N * p.K + p.N * p.K + res["pw"].nbytes) / (res["pack_ms"] * 1e-3) / 1e9,
-                 "note": "patch_pack incl. host header upload and stream sync; bytes = W + mask + blob"},
-        "roofline": {
-            "kernel": "k_decode (hybrid, packed W)",
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
-            "traffic": traffic,
-            "bytes_per_launch_algorithmic": b_sum / len(Ms),
-            "avg_launch_us": t_sum / len(Ms) * 1e6,
-        },
-    }
+    print("[bench] prefill MLP headline", file=sys.stderr, flush=True)
+    line, mats = headline_prefill(args)
+    problems = [(m["p"], inputs.CONFIGS["prefill_mlp"], i) for i, m in enumerate(mats)]
+    Ms = [line["config"]["M"]] * len(mats)
+    blob_sizes = [m["pw"].nbytes for m in mats]
+    del mats
+    torch.cuda.empty_cache()
+    if not args.no_extras:
+        print("[bench] decode workload", file=sys.stderr, flush=True)
+        line["decode"] = decode_extra(args)
+        print("[bench] ceilings", file=sys.stderr, flush=True)
+        line["ceilings"] = measure_ceilings([line["decode"]["blob_bytes"], blob_sizes[0]])
+        dec_b = str(line["decode"]["blob_bytes"] // 16 * 16)
+        line["decode"]["roofline"]["measured_read_ceiling_gbps"] = line["ceilings"]["hbm_read"][dec_b]["gbps"]
+        line["decode"]["roofline"]["frac_of_measured_ceiling"] = (line["decode"]["roofline"]["achieved"] /
+                                                                  line["ceilings"]["hbm_read"][dec_b]["gbps"])
+        sm = line["ceilings"]["matrix_core_tflops"]
+        line["roofline"]["measured_ceilings_tflops"] = {k: sm[k] for k in sm}
+        print("[bench] sparsity sweep", file=sys.stderr, flush=True)
+        line["sweep"] = sweep_compact(max(10, args.steps), args.warmup)
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(p, Ms, cfg)
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(problems, Ms, sample_rows=32)
     print(json.dumps(line), flush=True)
 
     if args.report:

@@ -72,7 +72,17 @@ typedef enum {
   PATCH_VARIANT_PREFILL_W128_LDS = 7, /* W and X staged through LDS, 128 */
   PATCH_VARIANT_PREFILL_W192_LDS = 8, /* W and X staged through LDS, 192 */
   PATCH_VARIANT_PREFILL_W256_LDS = 9, /* W and X staged through LDS, 256 */
-  PATCH_VARIANT_PREFILL_W64_LDS = 10  /* W and X staged through LDS, 64 */
+  PATCH_VARIANT_PREFILL_W64_LDS = 10, /* W and X staged through LDS, 64 */
+  /* The prefill kernel whose waves each hold a 128-row register tile of
+   * both row-blocks of their pair (W and X staged through LDS), with 4
+   * waves (one a SIMD): its own choice of width, or 128, 192 or 256
+   * columns of M a workgroup; with 8 waves (two a SIMD): 128 or 256. */
+  PATCH_VARIANT_PREFILL_BIG = 11,
+  PATCH_VARIANT_PREFILL_BIG_W128 = 12,
+  PATCH_VARIANT_PREFILL_BIG_W192 = 13,
+  PATCH_VARIANT_PREFILL_BIG_W256 = 14,
+  PATCH_VARIANT_PREFILL_BIG8_W128 = 15,
+  PATCH_VARIANT_PREFILL_BIG8_W256 = 16
 } patch_variant;
 
 /* Host-side mirror of the packed blob's header (format version 3). */
@@ -122,13 +132,16 @@ uint64_t patch_packed_bytes(patch_dtype dtype, int64_t N, int64_t K, const uint8
  * Statement"; the six patterns: section 2 "Pattern Selection".
  *
  * A 4:8 tile (another N:M pattern, explainer section 5 "Significance",
- * "Future Direction") keeps four of every eight consecutive weights along K:
- * per band piece (2304 bytes, as a 2:4 one) each lane holds, for each
- * 32-column slice, the four kept values of its group of eight and an 8-bit
- * mask of their positions -- the group it holds of the dense 16x16x32
- * matrix instruction's operand, which the GEMM kernels rebuild in
- * registers: 4:8 tiles take a 2:4 tile's bytes and a dense tile's
- * matrix-core time.
+ * "Future Direction") keeps four of every eight consecutive weights along K.
+ * A band piece takes 2304 bytes, as a 2:4 one.  In each 64-column slice q a
+ * lane l owns columns 64q + 16(l/16) .. +15, which are two groups of eight
+ * u = 0, 1: the 1 KB block at 1024q holds, at 16l, the four kept values
+ * (ascending column) of group 0 and then of group 1; the lane's 32-bit word
+ * at 2048 + 4l holds group u's 8-bit position mask in byte 2q + u.  Those
+ * sixteen columns are exactly the lane's share of a dense piece's two
+ * halves, so the GEMM kernels rebuild the halves in registers and run them
+ * on the sparse instruction with the dense tile's fixed codes: 4:8 tiles
+ * take a 2:4 tile's bytes and a dense tile's matrix-core time.
  *
  *   W_dev          N x K elements of `dtype`, row-major, device.
  *   tile_map_host  T bytes on the host: 0 dense, 1 2:4, 2 4:8 (other
@@ -148,7 +161,9 @@ patch_status patch_pack(patch_dtype dtype, int64_t N, int64_t K, const void* W_d
                         patch_packed_desc* desc_out, void* stream);
 
 /* Parse a blob header already copied to the host (for reloading a saved blob).
- * Checks magic, version, dtype, tile shape and that the sizes agree. */
+ * header_bytes must be at least 76 (the descriptor's fields end with n_48 at
+ * bytes 72..75; else PATCH_ERR_BUFFER_TOO_SMALL).  Checks magic, version,
+ * dtype, tile shape and that the sizes agree. */
 patch_status patch_desc_from_header(const void* header_host, uint64_t header_bytes, patch_packed_desc* desc_out);
 
 /*
@@ -169,10 +184,14 @@ uint64_t patch_gemm_workspace_bytes(const patch_packed_desc* desc, int64_t M);
 uint64_t patch_dense_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
- * Hybrid GEMM: Y = X * (W o E)^T from the packed blob.  Both tile kinds run
- * on v_smfmac_f32_16x16x64 (bf16/f16): a 2:4 slice once with its packed
- * codes, a dense slice as its two fixed-pattern halves; accumulation is
- * fp32; a 16-bit Y is rounded to nearest even.
+ * Hybrid GEMM: Y = X * (W o E)^T from the packed blob -- the inference-time
+ * product of a PATCH layer, whose dense tiles run on dense matrix units and
+ * whose 2:4 tiles run on the sparse path (gist.science explainer, section 2
+ * "Methodology: PATCH", "Inference & Deployment"; E as in "Core
+ * Mechanism": 1 in dense tiles, the 2:4 mask in sparse ones).  Both tile
+ * kinds run on v_smfmac_f32_16x16x64 (bf16/f16): a 2:4 slice once with its
+ * packed codes, a dense slice as its two fixed-pattern halves; accumulation
+ * is fp32; a 16-bit Y is rounded to nearest even.
  *
  *   desc        descriptor from patch_pack / patch_desc_from_header.
  *   packed_dev  the blob (device).
@@ -193,9 +212,12 @@ patch_status patch_gemm_ex(const patch_packed_desc* desc, const void* packed_dev
                            int32_t variant, void* stream);
 
 /*
- * Same-shape dense baseline: Y = X * W^T from plain row-major W (N x K), with
- * the same kernels and tiling as patch_gemm, every tile dense, on
- * v_mfma_f32_16x16x32.
+ * Same-shape dense baseline: Y = X * W^T from plain row-major W (N x K) --
+ * the dense layer PATCH's speedups are measured against (gist.science
+ * explainer, section 4 "Experimental Results", "Speedup & Efficiency"), with
+ * the same kernels and tiling as patch_gemm, every tile dense, on the dense
+ * matrix instruction.  Arguments as patch_gemm, with W_dev N x K elements of
+ * `dtype` in place of the blob.
  */
 patch_status patch_dense_gemm(patch_dtype dtype, int64_t M, int64_t N, int64_t K, const void* X_dev,
                               const void* W_dev, void* Y_dev, patch_dtype y_dtype, void* workspace_dev,
@@ -324,6 +346,35 @@ patch_status patch_exec_tile_map(int64_t N, int64_t K, int64_t b1, int64_t b2, c
 patch_status patch_apply_fine_mask(patch_dtype dtype, int64_t N, int64_t K, int64_t b1, int64_t b2, const void* W_dev,
                                    const uint8_t* fine_map_dev, const uint8_t* mask_dev, void* W_out_dev,
                                    void* stream);
+
+/*
+ * Measurement probes.  They compute nothing of the method; they measure, on
+ * the device the GEMMs run on, the ceilings the GEMM kernels are compared
+ * with (the datasheet peaks -- 8 TB/s HBM, 2.5 PFLOP/s dense bf16 matrix
+ * math, twice that for 2:4 sparse instructions -- are upper bounds that one
+ * launch of a given size does not reach).  Both are asynchronous on
+ * `stream`; the caller times them.
+ *
+ * patch_probe_stream_read: reads `bytes` (a multiple of 16) of src_dev once
+ * with 16-byte loads and writes at most a few words of sink_dev (scratch of
+ * sink_bytes, at least 4; it bounds the grid: sink_bytes / 4 workgroups).
+ * Errors: PATCH_ERR_INVALID_ARG (null or unaligned pointers, bytes not a
+ * positive multiple of 16, sink_bytes < 4).
+ *
+ * patch_probe_matrix_rate: `workgroups` workgroups of 4 waves, each wave
+ * issuing `iters` rounds of independent matrix instructions of one kind on
+ * register operands: kind 0 v_mfma_f32_16x16x32_bf16, 1
+ * v_smfmac_f32_16x16x64_bf16, 2 v_mfma_f32_32x32x16_bf16, 3
+ * v_smfmac_f32_32x32x32_bf16.  sink_dev: scratch of 4 * workgroups bytes.
+ * patch_probe_matrix_flops returns the flops one such launch executes
+ * (dense-equivalent for the sparse kinds: 2 x rows x columns x logical K per
+ * instruction), 0 for bad arguments.  Errors: PATCH_ERR_INVALID_ARG (kind
+ * outside 0..3, iters or workgroups < 1, null sink).
+ */
+patch_status patch_probe_stream_read(const void* src_dev, uint64_t bytes, void* sink_dev, uint64_t sink_bytes,
+                                     void* stream);
+patch_status patch_probe_matrix_rate(int32_t kind, int32_t iters, int32_t workgroups, void* sink_dev, void* stream);
+uint64_t patch_probe_matrix_flops(int32_t kind, int32_t iters, int32_t workgroups);
 
 const char* patch_status_string(patch_status s);
 const char* patch_last_error(void);

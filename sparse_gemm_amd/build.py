@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpatch.so")
-SOURCES = ["pack.hip", "gemm_decode.hip", "gemm_prefill.hip", "sampler.hip", "fine_mask.hip", "patch_api.cpp"]
+SOURCES = ["pack.hip", "gemm_decode.hip", "gemm_prefill.hip", "gemm_prefill_big.hip", "sampler.hip", "fine_mask.hip", "probe.hip", "patch_api.cpp"]
 ARCH = "gfx950"
 
 
@@ -46,7 +46,7 @@ def _compile(src: str) -> str:
 
 
 def build(verbose: bool = True) -> str:
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs

@@ -48,39 +48,14 @@
 //
 // With SRC_ROWMAJOR the same kernel reads plain row-major W with every tile
 // dense, on v_mfma_f32_16x16x32: the same-shape dense baseline.
-#include "device_common.h"
+#include "prefill_common.h"
 
 #include <algorithm>
 
 namespace patch {
 
 constexpr int kPfWaves = 8;
-constexpr int kPfRowBytes = 128;  // one staged X row: 64 elements
-constexpr int kPfMaxKT = 1024;
 constexpr int kPfMGroup = 2;      // 16-column blocks of M whose B fragments are read together
-
-// Chunk position of 16-byte chunk c (0..7) of staged row r.  The XOR keeps the
-// 16 rows read by one B-fragment load on distinct bank groups for both 32- and
-// 64-bank LDS: bits (r0 ^ r3, r2, r1) of r.
-__device__ __forceinline__ int swz_f(int r) { return (((r ^ (r >> 3)) & 1) << 2) | ((r >> 1) & 3); }
-__device__ __forceinline__ int swz(int r, int c) { return r * kPfRowBytes + ((c ^ swz_f(r)) << 4); }
-
-// Workgroup barrier without the fences __syncthreads adds (they would wait
-// for every load in flight); callers wait for what they need first.
-__device__ __forceinline__ void wg_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Raw buffer descriptor: byte addressing from `base`, loads at offsets >=
-// `bytes` return zero (word 3 = the gfx9-family raw-buffer format).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
-}
 
 // A operands of one step, [.][band]: packed dense tile: a[e] = half e
 // (positions 2e, 2e+1 of every group of four); 2:4 tile: a[0] = values,
@@ -89,18 +64,6 @@ __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff
 // v_mfma_f32_16x16x32 layout.
 struct StepA {
   u32x4 a[2][4];
-};
-
-struct PfArgs {
-  const uint8_t* src;
-  const uint8_t* src2;  // fused gate/up with row-major W: the up matrix (src is gate)
-  const uint16_t* X;
-  void* Y;
-  int M, N, K, NT, KT, n_mblk, n_pairs;
-  int mg;       // M-blocks per group (the output blocks are ordered group-major)
-  int splits;   // K ranges; above 1, Y is the fp32 partial buffer [splits][M][N]
-  int kt_split; // tile columns per K range
-  int n_blocks, per_xcd;
 };
 
 // Fused gate/up epilogue: the pair is (gate row-block 2p, up row-block 2p+1),
@@ -477,38 +440,6 @@ constexpr int kLdsWStage = 32768;  // 2 row-blocks x 8 bands x 2 fragments of 1 
 // and 256 (a third would not fit the 160 KB of LDS)
 constexpr int lds_stages(int bm) { return bm <= 128 ? 3 : 2; }
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
-
-// 16 bytes a lane, global -> LDS: lane l's bytes land at LDS byte lds + 16 l
-// (M0 holds the LDS base; it is saved and restored around the copy).
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %2, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(g)
-      : "memory");
-}
-// 4 bytes a lane, global -> LDS: lane l's bytes land at LDS byte lds + 4 l.
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dword %2, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(g)
-      : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_copies() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE, int BM>
 __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   constexpr int kNMB = BM / 32;                     // 16-column M blocks per wave
@@ -868,6 +799,8 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
 struct PfShape {
   int bm, groups, splits, kt_split;
   bool lds;  // W and X staged through LDS (k_prefill_lds), else through registers (k_prefill)
+  bool big;  // the kernel whose waves hold 128-row register tiles (k_prefill_big)
+  int waves; // its waves a workgroup: 4 or 8
 };
 static double shape_cost_us(int64_t M, int64_t N, int64_t K, int bm, int64_t splits, int64_t kt_split, int cus) {
   const int64_t pairs = (N / kTile + 1) / 2;
@@ -884,7 +817,7 @@ static PfShape choose_shape_uncached(int64_t M, int64_t N, int64_t K, int cus, i
   const int widths[4] = {256, 192, 128, 64};
   const int wants[10] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
   const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(KT / 2, K / (2 * M)));
-  PfShape best = {256, 1, 1, (int)KT, false};
+  PfShape best = {256, 1, 1, (int)KT, false, false, 4};
   double best_t = -1.0;
   for (int c = 0; c < 4; c++) {
     if (only_bm && widths[c] != only_bm) continue;
@@ -894,7 +827,7 @@ static PfShape choose_shape_uncached(int64_t M, int64_t N, int64_t K, int cus, i
       const double t = shape_cost_us(M, N, K, widths[c], splits, kt_split, cus);
       if (best_t < 0 || t < best_t) {
         best_t = t;
-        best = {widths[c], 1, (int)splits, (int)kt_split, false};
+        best = {widths[c], 1, (int)splits, (int)kt_split, false, false, 4};
       }
     }
   }
@@ -964,6 +897,55 @@ __global__ __launch_bounds__(256) void k_split_reduce_fused(const float* __restr
   store4<BF16, OUT_F32>(H, q, silu_mul(g, u));
 }
 
+hipError_t launch_prefill_big(bool bf16, bool rowmajor, bool out_f32, bool fuse, int bm, int waves, const PfArgs& a,
+                              hipStream_t s);
+
+// The fp32 partials of sh.splits K ranges in part -> Y (fused: H).
+template <bool BF16, bool OUT_F32, bool FUSE>
+static hipError_t launch_split_reduce(const float* part, int splits, int64_t M, int64_t N, void* Y, hipStream_t s) {
+  if constexpr (FUSE) {
+    const int64_t mf = M * (N / 2);
+    hipLaunchKernelGGL((k_split_reduce_fused<BF16, OUT_F32>), dim3((unsigned)((mf / 4 + 255) / 256)), dim3(256), 0, s,
+                       part, splits, M, N / 2, Y);
+  } else {
+    const int64_t mn = M * N;
+    hipLaunchKernelGGL((k_split_reduce<BF16, OUT_F32>), dim3((unsigned)((mn / 4 + 255) / 256)), dim3(256), 0, s, part,
+                       splits, mn, Y);
+  }
+  return hipGetLastError();
+}
+
+static PfArgs prefill_args(const void* src, const void* src2, const void* X, int64_t M, int64_t N, int64_t K, void* Y,
+                           const PfShape& sh, float* part, int bm) {
+  PfArgs a;
+  a.src = reinterpret_cast<const uint8_t*>(src);
+  a.src2 = reinterpret_cast<const uint8_t*>(src2);
+  a.X = reinterpret_cast<const uint16_t*>(X);
+  a.Y = sh.splits > 1 ? static_cast<void*>(part) : Y;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.NT = (int)(N / kTile);
+  a.KT = (int)(K / kTile);
+  a.n_mblk = (int)((M + bm - 1) / bm);
+  a.n_pairs = (a.NT + 1) / 2;
+  a.mg = (a.n_mblk + sh.groups - 1) / sh.groups;
+  a.splits = sh.splits;
+  a.kt_split = sh.kt_split;
+  a.n_blocks = a.n_pairs * a.n_mblk * sh.splits;
+  a.per_xcd = (a.n_blocks + 7) / 8;
+  return a;
+}
+
+template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE>
+static hipError_t launch_big_t(const void* src, const void* src2, const void* X, int64_t M, int64_t N, int64_t K,
+                               void* Y, const PfShape& sh, float* part, hipStream_t s) {
+  const PfArgs a = prefill_args(src, src2, X, M, N, K, Y, sh, part, sh.bm);
+  hipError_t e = launch_prefill_big(BF16, SRC_ROWMAJOR, OUT_F32, FUSE, sh.bm, sh.waves, a, s);
+  if (e != hipSuccess || sh.splits == 1) return e;
+  return launch_split_reduce<BF16, OUT_F32, FUSE>(part, sh.splits, M, N, Y, s);
+}
+
 template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE, int BM, int DIST, bool LDS = false>
 static hipError_t launch_prefill_bm(const void* src, const void* src2, const void* X, int64_t M, int64_t N, int64_t K,
                                     void* Y, const PfShape& sh, float* part, hipStream_t s) {
@@ -1009,12 +991,55 @@ static hipError_t launch_prefill_bm(const void* src, const void* src2, const voi
   return hipGetLastError();
 }
 
+// Launch shape of the big-tile kernel (k_prefill_big): the token-block
+// width BM in {128, 192, 256} and the K split, from its time model
+//   t = rounds * (c0 + tiles * c1 * BM / 256) + split cost (as above),
+// rounds = ceil(workgroups / CUs): a 256 x BM block of output per
+// workgroup, one workgroup per CU.  only_bm: that width alone.
+static double big_cost_us(int64_t M, int64_t N, int64_t K, int bm, int64_t splits, int64_t kt_split, int cus) {
+  const int64_t pairs = (N / kTile + 1) / 2;
+  const int64_t blocks = pairs * ((M + bm - 1) / bm) * splits;
+  const int64_t rounds = (blocks + cus - 1) / cus;
+  double t = (double)rounds * (3.0 + (double)kt_split * 1.6 * (double)bm / 256.0);
+  if (splits > 1) t += 6.4 + (double)splits * (double)M * (double)N * 4.0 / 3.24e6;
+  return t;
+}
+constexpr int64_t kBigMaxKT = 256;  // tile columns a workgroup of the big-tile kernel keeps entries of
+static PfShape choose_shape_big(int64_t M, int64_t N, int64_t K, int cus, int only_bm = 0, int waves = 4) {
+  const int64_t KT = K / kTile;
+  const int widths[3] = {256, 192, 128};
+  const int wants[10] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
+  const int64_t smin = (KT + kBigMaxKT - 1) / kBigMaxKT;
+  const int64_t smax = std::max<int64_t>(smin, std::min<int64_t>(KT / 2, K / (2 * M)));
+  PfShape best = {256, 1, (int)smin, (int)((KT + smin - 1) / smin), true, true, waves};
+  double best_t = -1.0;
+  for (int c = 0; c < 3; c++) {
+    if (only_bm && widths[c] != only_bm) continue;
+    if (waves == 8 && widths[c] == 192) continue;
+    for (int w = 0; w < 10 && wants[w] <= smax; w++) {
+      const int64_t kt_split = (KT + wants[w] - 1) / wants[w];
+      const int64_t splits = (KT + kt_split - 1) / kt_split;
+      if (kt_split > kBigMaxKT) continue;
+      const double t = big_cost_us(M, N, K, widths[c], splits, kt_split, cus);
+      if (best_t < 0 || t < best_t) {
+        best_t = t;
+        best = {widths[c], 1, (int)splits, (int)kt_split, true, true, waves};
+      }
+    }
+  }
+  const int64_t mblk = (M + best.bm - 1) / best.bm;
+  while (best.groups < 4 && 2 * best.groups * 2 <= mblk) best.groups *= 2;
+  return best;
+}
+
 // The shape for these sizes with the split limited to what the workspace
 // holds (no workspace: no split).
 static PfShape shape_for(int64_t M, int64_t N, int64_t K, bool rowmajor, uint64_t ws_bytes, int force_bm = 0,
-                         bool force_lds = false) {
+                         bool force_lds = false, int force_big = 0) {
   PfShape sh;
-  if (force_bm) {
+  if (force_big) {
+    sh = choose_shape_big(M, N, K, cu_count(), force_bm, force_big);
+  } else if (force_bm) {
     sh = choose_shape_uncached(M, N, K, cu_count(), force_bm);
     sh.lds = force_lds;
   } else {
@@ -1032,6 +1057,15 @@ static PfShape shape_for(int64_t M, int64_t N, int64_t K, bool rowmajor, uint64_
       sh.splits = (int)((KT + sh.kt_split - 1) / sh.kt_split);
     }
   }
+  if (sh.big && sh.kt_split > kBigMaxKT) {
+    // the big-tile kernel keeps at most kBigMaxKT tile columns a range and
+    // the workspace allows no split that short: the 8-wave kernel
+    PfShape lds = choose_shape(M, N, K, rowmajor);
+    lds.lds = true;
+    lds.splits = 1;
+    lds.kt_split = (int)KT;
+    return lds;
+  }
   return sh;
 }
 
@@ -1048,10 +1082,11 @@ double prefill_estimate_us(int64_t M, int64_t N, int64_t K, bool rowmajor, uint6
 
 template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE>
 static hipError_t launch_prefill_t(const void* src, const void* src2, const void* X, int64_t M, int64_t N, int64_t K,
-                                   void* Y, void* ws, uint64_t ws_bytes, int force_bm, bool force_lds,
+                                   void* Y, void* ws, uint64_t ws_bytes, int force_bm, bool force_lds, int force_big,
                                    hipStream_t s) {
-  const PfShape sh = shape_for(M, N, K, SRC_ROWMAJOR, ws ? ws_bytes : 0u, force_bm, force_lds);
+  const PfShape sh = shape_for(M, N, K, SRC_ROWMAJOR, ws ? ws_bytes : 0u, force_bm, force_lds, force_big);
   float* part = reinterpret_cast<float*>(ws);
+  if (sh.big) return launch_big_t<BF16, SRC_ROWMAJOR, OUT_F32, FUSE>(src, src2, X, M, N, K, Y, sh, part, s);
 #define PATCH_BM(W, D, L) \
   launch_prefill_bm<BF16, SRC_ROWMAJOR, OUT_F32, FUSE, W, D, L>(src, src2, X, M, N, K, Y, sh, part, s)
   if (sh.lds) {
@@ -1078,14 +1113,16 @@ static hipError_t launch_prefill_t(const void* src, const void* src2, const void
 // interleaved in src and src2 is src); Y is then H, M x N/2.
 hipError_t launch_prefill(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* src2, const void* X,
                           int64_t M, int64_t N, int64_t K, void* Y, void* ws, uint64_t ws_bytes, int force_bm,
-                          bool force_lds, hipStream_t s) {
+                          bool force_lds, int force_big, hipStream_t s) {
   if (K / kTile > kPfMaxKT) return hipErrorInvalidValue;
   if (force_bm && force_bm != 64 && force_bm != 128 && force_bm != 192 && force_bm != 256) return hipErrorInvalidValue;
   if (force_lds && force_bm < 64) return hipErrorInvalidValue;
+  if (force_big && force_bm != 0 && force_bm < 128) return hipErrorInvalidValue;
+  if (force_big == 8 && force_bm == 192) return hipErrorInvalidValue;
   const bool fuse = src2 != nullptr;
   if (fuse && (N % (2 * kTile))) return hipErrorInvalidValue;
 #define PATCH_PF(B, R, F, U) \
-  launch_prefill_t<B, R, F, U>(src, src2, X, M, N, K, Y, ws, ws_bytes, force_bm, force_lds, s)
+  launch_prefill_t<B, R, F, U>(src, src2, X, M, N, K, Y, ws, ws_bytes, force_bm, force_lds, force_big, s)
 #define PATCH_PF2(B, R, F) (fuse ? PATCH_PF(B, R, F, true) : PATCH_PF(B, R, F, false))
   if (bf16) {
     if (rowmajor) return out_f32 ? PATCH_PF2(true, true, true) : PATCH_PF2(true, true, false);

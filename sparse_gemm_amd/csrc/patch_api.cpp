@@ -18,7 +18,7 @@ hipError_t launch_decode(bool bf16, bool rowmajor, bool out_f32, const void* src
                          int64_t M, int64_t N, int64_t K, void* Y, bool n48, hipStream_t s);
 hipError_t launch_prefill(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* src2, const void* X,
                           int64_t M, int64_t N, int64_t K, void* Y, void* ws, uint64_t ws_bytes, int force_bm,
-                          bool force_lds, hipStream_t s);
+                          bool force_lds, int force_big, hipStream_t s);
 uint64_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K, bool rowmajor);
 double prefill_estimate_us(int64_t M, int64_t N, int64_t K, bool rowmajor, uint64_t ws_bytes);
 double decode_estimate_us(int64_t M, int64_t N, int64_t K, double w_bytes);
@@ -27,6 +27,9 @@ hipError_t launch_sample_mask(int64_t N, int64_t K, const float* tile_logits, co
                               uint8_t* mask, float* soft, hipStream_t s);
 hipError_t launch_apply_fine_mask(int64_t N, int64_t K, int b1, int b2, const void* W, const uint8_t* fine_map,
                                   const uint8_t* mask, void* out, hipStream_t s);
+hipError_t launch_probe_read(const void* src, uint64_t bytes, void* sink, uint64_t sink_bytes, hipStream_t s);
+hipError_t launch_probe_mma(int kind, int iters, int workgroups, void* sink, hipStream_t s);
+uint64_t probe_mma_flops(int kind, int iters, int workgroups);
 }  // namespace patch
 
 namespace {
@@ -200,6 +203,30 @@ const char* patch_status_string(patch_status s) {
 }
 
 const char* patch_last_error(void) { return g_err.c_str(); }
+
+patch_status patch_probe_stream_read(const void* src_dev, uint64_t bytes, void* sink_dev, uint64_t sink_bytes,
+                                     void* stream) {
+  if (!src_dev || !sink_dev || !aligned16(src_dev)) return fail(PATCH_ERR_INVALID_ARG, "null or unaligned pointer");
+  if (bytes == 0 || bytes % 16) return fail(PATCH_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+  if (sink_bytes < 4) return fail(PATCH_ERR_INVALID_ARG, "sink needs at least 4 bytes");
+  hipError_t e = patch::launch_probe_read(src_dev, bytes, sink_dev, sink_bytes, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "launch stream-read probe");
+  return PATCH_OK;
+}
+
+uint64_t patch_probe_matrix_flops(int32_t kind, int32_t iters, int32_t workgroups) {
+  if (kind < 0 || kind > 3 || iters < 1 || workgroups < 1) return 0;
+  return patch::probe_mma_flops(kind, iters, workgroups);
+}
+
+patch_status patch_probe_matrix_rate(int32_t kind, int32_t iters, int32_t workgroups, void* sink_dev, void* stream) {
+  if (kind < 0 || kind > 3) return fail(PATCH_ERR_INVALID_ARG, "kind %d outside 0..3", (int)kind);
+  if (iters < 1 || workgroups < 1) return fail(PATCH_ERR_INVALID_ARG, "iters and workgroups must be >= 1");
+  if (!sink_dev) return fail(PATCH_ERR_INVALID_ARG, "null sink");
+  hipError_t e = patch::launch_probe_mma(kind, iters, workgroups, sink_dev, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "launch matrix-rate probe");
+  return PATCH_OK;
+}
 
 uint64_t patch_packed_bytes(patch_dtype dtype, int64_t N, int64_t K, const uint8_t* tile_map_host) {
   if (check_dtype(dtype) || check_nk(N, K) || !tile_map_host) return 0;
@@ -413,7 +440,8 @@ patch_status patch_pack_gate_up(patch_dtype dtype, int64_t F, int64_t K, const v
 
 patch_status patch_desc_from_header(const void* header_host, uint64_t header_bytes, patch_packed_desc* desc_out) {
   if (!header_host || !desc_out) return fail(PATCH_ERR_INVALID_ARG, "null pointer argument");
-  if (header_bytes < 72) return fail(PATCH_ERR_BUFFER_TOO_SMALL, "header needs at least 72 bytes");
+  // the descriptor's fields end with n_48 at bytes 72..75
+  if (header_bytes < 76) return fail(PATCH_ERR_BUFFER_TOO_SMALL, "header needs at least 76 bytes");
   const uint8_t* h = reinterpret_cast<const uint8_t*>(header_host);
   uint32_t u[10];
   uint64_t v[4];
@@ -465,7 +493,7 @@ static patch_status gemm_common(bool rowmajor, patch_dtype dt, int64_t M, int64_
   patch_status s;
   if ((s = check_ydtype(dt, y_dtype))) return s;
   if (M < 0 || M > (int64_t)0x7fffffff) return fail(PATCH_ERR_INVALID_ARG, "M=%lld out of range", (long long)M);
-  if (variant < PATCH_VARIANT_AUTO || variant > PATCH_VARIANT_PREFILL_W64_LDS)
+  if (variant < PATCH_VARIANT_AUTO || variant > PATCH_VARIANT_PREFILL_BIG8_W256)
     return fail(PATCH_ERR_INVALID_ARG, "unknown variant %d", (int)variant);
   if (has48 && variant >= PATCH_VARIANT_PREFILL_W64 && variant <= PATCH_VARIANT_PREFILL_W256)
     return fail(PATCH_ERR_UNSUPPORTED, "the register-staged prefill variants run dense and 2:4 tiles only");
@@ -494,11 +522,12 @@ static patch_status gemm_common(bool rowmajor, patch_dtype dt, int64_t M, int64_
                                       patch::prefill_estimate_us(M, N, K, rowmajor, ws ? ws_bytes : 0);
   const bool bf16 = dt == PATCH_BF16, f32out = y_dtype == PATCH_F32;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  static const int kForceBm[11] = {0, 0, 0, 64, 128, 192, 256, 128, 192, 256, 64};
+  static const int kForceBm[17] = {0, 0, 0, 64, 128, 192, 256, 128, 192, 256, 64, 0, 128, 192, 256, 128, 256};
+  const int big = variant >= PATCH_VARIANT_PREFILL_BIG8_W128 ? 8 : variant >= PATCH_VARIANT_PREFILL_BIG ? 4 : 0;
+  const bool lds = variant >= PATCH_VARIANT_PREFILL_W128_LDS && variant <= PATCH_VARIANT_PREFILL_W64_LDS;
   hipError_t e = decode ? patch::launch_decode(bf16, rowmajor, f32out, src, src2, X_dev, M, N, K, Y_dev, has48, st)
                         : patch::launch_prefill(bf16, rowmajor, f32out, src, src2, X_dev, M, N, K, Y_dev, ws,
-                                                ws_bytes, kForceBm[variant], variant >= PATCH_VARIANT_PREFILL_W128_LDS,
-                                                st);
+                                                ws_bytes, kForceBm[variant], lds, big, st);
   if (e != hipSuccess) return hip_fail(e, decode ? "launch decode" : "launch prefill");
   return PATCH_OK;
 }

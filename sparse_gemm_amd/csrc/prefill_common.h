@@ -1,0 +1,80 @@
+// prefill_common.h -- pieces shared by the prefill (many-token) kernels:
+// launch arguments, the swizzled LDS layout of staged rows, global -> LDS
+// copies and barriers.
+#pragma once
+
+#include "device_common.h"
+
+namespace patch {
+
+constexpr int kPfRowBytes = 128;  // one staged row of X (or row-major W): 64 elements
+constexpr int kPfMaxKT = 1024;    // tile columns a workgroup keeps entries of
+
+// Chunk position of 16-byte chunk c (0..7) of staged row r.  The XOR keeps the
+// 16 rows read by one B-fragment load on distinct bank groups for both 32- and
+// 64-bank LDS: bits (r0 ^ r3, r2, r1) of r.
+__device__ __forceinline__ int swz_f(int r) { return (((r ^ (r >> 3)) & 1) << 2) | ((r >> 1) & 3); }
+__device__ __forceinline__ int swz(int r, int c) { return r * kPfRowBytes + ((c ^ swz_f(r)) << 4); }
+
+// Workgroup barrier without the fences __syncthreads adds (they would wait
+// for every load in flight); callers wait for what they need first.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Raw buffer descriptor: byte addressing from `base`, loads at offsets >=
+// `bytes` return zero (word 3 = the gfx9-family raw-buffer format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+struct PfArgs {
+  const uint8_t* src;
+  const uint8_t* src2;  // fused gate/up with row-major W: the up matrix (src is gate)
+  const uint16_t* X;
+  void* Y;
+  int M, N, K, NT, KT, n_mblk, n_pairs;
+  int mg;       // M-blocks per group (the output blocks are ordered group-major)
+  int splits;   // K ranges; above 1, Y is the fp32 partial buffer [splits][M][N]
+  int kt_split; // tile columns per K range
+  int n_blocks, per_xcd;
+};
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+// 16 bytes a lane, global -> LDS: lane l's bytes land at LDS byte lds + 16 l
+// (M0 holds the LDS base; it is saved and restored around the copy).
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(g)
+      : "memory");
+}
+// 4 bytes a lane, global -> LDS: lane l's bytes land at LDS byte lds + 4 l.
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dword %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(g)
+      : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+}  // namespace patch

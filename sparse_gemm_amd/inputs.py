@@ -178,17 +178,26 @@ class Problem:
 
 
 def make_weights(cfg: Config, matrix_index: int, s_index: int, seed: int = 0,
-                 map_kind: str | None = None, fraction: float | None = None) -> Problem:
+                 map_kind: str | None = None, fraction: float | None = None, reuse: Problem | None = None) -> Problem:
+    """reuse: a Problem made by this function for the same config, matrix and
+    seed; its weights and mask (which do not depend on s_index) are taken
+    as they are instead of being drawn again."""
     mat = cfg.matrices[matrix_index]
     N, K = mat.N, mat.K
     frac = cfg.fractions[s_index] if fraction is None else fraction
     kind = cfg.map_kind if map_kind is None else map_kind
-    w = gen_w(rng_for(seed, cfg.cid, matrix_index, 0, ROLE_W), N, K, cfg.dtype)
     tmap = gen_tile_map(rng_for(seed, cfg.cid, matrix_index, s_index, ROLE_MAP), N // TILE, K // TILE, kind, frac)
-    if cfg.mask_kind == "top2":
-        mask = gen_mask_top2(w, cfg.dtype)
+    if reuse is not None:
+        sd = reuse.seeds
+        if (sd.get("config"), sd.get("matrix"), sd.get("seed")) != (cfg.cid, matrix_index, seed):
+            raise ValueError("reuse must come from the same config, matrix and seed")
+        w, mask = reuse.w, reuse.mask
     else:
-        mask = gen_mask_uniform(rng_for(seed, cfg.cid, matrix_index, 0, ROLE_MASK), N, K)
+        w = gen_w(rng_for(seed, cfg.cid, matrix_index, 0, ROLE_W), N, K, cfg.dtype)
+        if cfg.mask_kind == "top2":
+            mask = gen_mask_top2(w, cfg.dtype)
+        else:
+            mask = gen_mask_uniform(rng_for(seed, cfg.cid, matrix_index, 0, ROLE_MASK), N, K)
     return Problem(cfg.dtype, N, K, w, tmap, mask,
                    dict(seed=seed, config=cfg.cid, matrix=matrix_index, s_index=s_index, map_kind=kind,
                         fraction=frac))

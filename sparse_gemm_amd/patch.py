@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(_HERE, "libpatch.so")
 PATCH_F16, PATCH_BF16, PATCH_F32 = 0, 1, 2
 VARIANTS = {"auto": 0, "decode": 1, "prefill": 2, "prefill_w64": 3, "prefill_w128": 4, "prefill_w192": 5,
             "prefill_w256": 6, "prefill_w128_lds": 7, "prefill_w192_lds": 8, "prefill_w256_lds": 9,
-            "prefill_w64_lds": 10}
+            "prefill_w64_lds": 10, "prefill_big": 11, "prefill_big_w128": 12, "prefill_big_w192": 13,
+            "prefill_big_w256": 14, "prefill_big8_w128": 15, "prefill_big8_w256": 16}
 STATUS = {0: "PATCH_OK", 1: "PATCH_ERR_INVALID_ARG", 2: "PATCH_ERR_SHAPE", 3: "PATCH_ERR_MASK",
           4: "PATCH_ERR_BUFFER_TOO_SMALL", 5: "PATCH_ERR_UNSUPPORTED", 6: "PATCH_ERR_HIP"}
 
@@ -49,7 +50,8 @@ EXPORTS = ("patch_abi_version", "patch_packed_bytes", "patch_pack", "patch_desc_
            "patch_dense_gemm", "patch_dense_gemm_ex", "patch_packed_bytes_gate_up", "patch_pack_gate_up",
            "patch_gemm_swiglu_workspace_bytes", "patch_gemm_swiglu", "patch_dense_gemm_swiglu_workspace_bytes",
            "patch_dense_gemm_swiglu", "patch_packed_bytes_concat", "patch_pack_concat", "patch_sample_mask",
-           "patch_exec_tile_map", "patch_apply_fine_mask", "patch_status_string", "patch_last_error")
+           "patch_exec_tile_map", "patch_apply_fine_mask", "patch_probe_stream_read", "patch_probe_matrix_rate",
+           "patch_probe_matrix_flops", "patch_status_string", "patch_last_error")
 
 _lib = None
 
@@ -106,6 +108,12 @@ def load():
     lib.patch_exec_tile_map.restype = ctypes.c_int
     lib.patch_apply_fine_mask.argtypes = [ctypes.c_int, I64, I64, I64, I64, P, P, P, P, P]
     lib.patch_apply_fine_mask.restype = ctypes.c_int
+    lib.patch_probe_stream_read.argtypes = [P, U64, P, U64, P]
+    lib.patch_probe_stream_read.restype = ctypes.c_int
+    lib.patch_probe_matrix_rate.argtypes = [I32, I32, I32, P, P]
+    lib.patch_probe_matrix_rate.restype = ctypes.c_int
+    lib.patch_probe_matrix_flops.argtypes = [I32, I32, I32]
+    lib.patch_probe_matrix_flops.restype = U64
     lib.patch_status_string.argtypes = [ctypes.c_int]
     lib.patch_status_string.restype = ctypes.c_char_p
     lib.patch_last_error.argtypes = []
@@ -137,6 +145,39 @@ def _dt(dtype: torch.dtype) -> int:
     if dtype not in _TORCH_DT:
         raise TypeError(f"unsupported dtype {dtype}")
     return _TORCH_DT[dtype]
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_dev(t: torch.Tensor, name: str, dtype=None, shape=None, on_device: bool = True):
+    """A contiguous (device) tensor of the given dtype and shape: the C ABI
+    takes raw pointers and cannot check any of this itself.  Type, dtype,
+    shape and layout are checked before the device, so every one of these
+    errors can be raised without a GPU."""
+    _need(isinstance(t, torch.Tensor), f"{name} must be a torch tensor")
+    if dtype is not None:
+        _need(t.dtype == dtype, f"{name} must be {dtype}, not {t.dtype}")
+    if shape is not None:
+        _need(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    if on_device:
+        _need(t.is_cuda, f"{name} must be a device tensor")
+
+
+def _check_out(out: Optional[torch.Tensor], shape, dtype):
+    if out is not None:
+        _check_dev(out, "out", dtype, shape, on_device=False)
+
+
+def _same_device(X: torch.Tensor, *others):
+    """Every tensor on X's device (after the shape checks)."""
+    _need(X.is_cuda, "X must be a device tensor")
+    for name, t in others:
+        if t is not None:
+            _need(t.is_cuda and t.device == X.device, f"{name} must be on the same device as X")
 
 
 def _host_map(tile_map) -> np.ndarray:
@@ -186,8 +227,16 @@ def pack(W: torch.Tensor, tile_map, mask: torch.Tensor, out: Optional[torch.Tens
     """Pack W (N x K, f16/bf16, device), a host tile map (0 dense, 1 2:4,
     2 4:8) and a device byte mask (nonzero = keep) into a blob (patch_pack)."""
     lib = load()
+    _need(isinstance(W, torch.Tensor) and W.dim() == 2, "W must be a 2-D tensor (N x K)")
+    _need(W.dtype in (torch.float16, torch.bfloat16), "W must be float16 or bfloat16")
     N, K = W.shape
+    _check_dev(W, "W", on_device=False)
+    _check_dev(mask, "mask", torch.uint8, (N, K), on_device=False)
     tm = _host_map(tile_map)
+    _need(tm.shape == (N // 128, K // 128) or N % 128 or K % 128, f"tile map must have shape {(N // 128, K // 128)}")
+    if out is not None:
+        _check_dev(out, "out", torch.uint8, on_device=False)
+    _need(W.is_cuda and mask.is_cuda and (out is None or out.is_cuda), "W, mask and out must be device tensors")
     nbytes = packed_bytes(W.dtype, N, K, tm)
     if nbytes == 0:
         # let the library name what is wrong (it checks before the buffer size)
@@ -226,6 +275,16 @@ def _ws_bytes(kind: str, M: int, N: int, K: int, dev: int, query) -> int:
     return nb
 
 
+def _check_x(X: torch.Tensor, dtype: torch.dtype, K: int):
+    _need(isinstance(X, torch.Tensor) and X.dim() == 2, "X must be a 2-D tensor (M x K)")
+    _need(X.shape[1] == K, f"X must have K = {K} columns, not {X.shape[1]}")
+    _check_dev(X, "X", dtype, on_device=False)
+
+
+def _check_out_dtype(od: torch.dtype, xd: torch.dtype):
+    _need(od in (xd, torch.float32), f"out_dtype must be {xd} or torch.float32, not {od}")
+
+
 def _workspace(nbytes: int, workspace, device):
     """workspace="auto": a fresh buffer of the size the library asks for
     (from torch's caching allocator); None: no workspace; a tensor: used as
@@ -234,6 +293,9 @@ def _workspace(nbytes: int, workspace, device):
         if workspace != "auto":
             raise ValueError(f"workspace must be 'auto', None or a tensor, not {workspace!r}")
         return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes > 0 else None
+    if workspace is not None:
+        _check_dev(workspace, "workspace")
+        _need(workspace.device == device, "workspace must be on the same device as X")
     return workspace
 
 
@@ -241,8 +303,14 @@ def gemm(X: torch.Tensor, packed: PackedWeight, out_dtype: Optional[torch.dtype]
          out: Optional[torch.Tensor] = None, workspace="auto") -> torch.Tensor:
     """Y = X (W o E)^T from a packed blob (patch_gemm_ex)."""
     lib = _lib or load()
+    _check_x(X, packed.dtype, packed.K)
+    _check_dev(packed.blob, "packed blob", torch.uint8, on_device=False)
+    _need(packed.blob.numel() >= packed.nbytes, "packed blob is smaller than its descriptor's total_bytes")
     M = X.shape[0]
     od = out_dtype or X.dtype
+    _check_out_dtype(od, X.dtype)
+    _check_out(out, (M, packed.N), od)
+    _same_device(X, ("packed blob", packed.blob), ("out", out))
     dev = X.get_device()
     if out is None:
         out = torch.empty((M, packed.N), dtype=od, device=X.device)
@@ -262,9 +330,15 @@ def dense_gemm(X: torch.Tensor, W: torch.Tensor, out_dtype: Optional[torch.dtype
                out: Optional[torch.Tensor] = None, workspace="auto") -> torch.Tensor:
     """Same-shape dense baseline Y = X W^T from row-major W (patch_dense_gemm_ex)."""
     lib = _lib or load()
+    _need(W.dim() == 2, "W must be 2-D (N x K)")
+    _check_x(X, W.dtype, W.shape[1])
+    _check_dev(W, "W", X.dtype, on_device=False)
     M, K = X.shape
     N = W.shape[0]
     od = out_dtype or X.dtype
+    _check_out_dtype(od, X.dtype)
+    _check_out(out, (M, N), od)
+    _same_device(X, ("W", W), ("out", out))
     dev = X.get_device()
     if out is None:
         out = torch.empty((M, N), dtype=od, device=X.device)
@@ -304,9 +378,15 @@ def gemm_swiglu(X: torch.Tensor, packed: PackedWeight, out_dtype: Optional[torch
                 variant: str = "auto", out: Optional[torch.Tensor] = None, workspace="auto") -> torch.Tensor:
     """H = SiLU(X Wg^T) * (X Wu^T) from a gate/up blob (patch_gemm_swiglu)."""
     lib = _lib or load()
+    _check_x(X, packed.dtype, packed.K)
+    _check_dev(packed.blob, "packed blob", torch.uint8, on_device=False)
+    _need(packed.blob.numel() >= packed.nbytes, "packed blob is smaller than its descriptor's total_bytes")
     M = X.shape[0]
     F = packed.N // 2
     od = out_dtype or X.dtype
+    _check_out_dtype(od, X.dtype)
+    _check_out(out, (M, F), od)
+    _same_device(X, ("packed blob", packed.blob), ("out", out))
     dev = X.get_device()
     if out is None:
         out = torch.empty((M, F), dtype=od, device=X.device)
@@ -325,9 +405,16 @@ def dense_gemm_swiglu(X: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, out_d
                       variant: str = "auto", out: Optional[torch.Tensor] = None, workspace="auto") -> torch.Tensor:
     """Same-shape dense baseline of gemm_swiglu from row-major Wg, Wu (patch_dense_gemm_swiglu)."""
     lib = _lib or load()
+    _need(Wg.dim() == 2, "Wg must be 2-D (F x K)")
+    _check_x(X, Wg.dtype, Wg.shape[1])
+    _check_dev(Wg, "Wg", X.dtype, on_device=False)
+    _check_dev(Wu, "Wu", X.dtype, tuple(Wg.shape), on_device=False)
     M, K = X.shape
     F = Wg.shape[0]
     od = out_dtype or X.dtype
+    _check_out_dtype(od, X.dtype)
+    _check_out(out, (M, F), od)
+    _same_device(X, ("Wg", Wg), ("Wu", Wu), ("out", out))
     dev = X.get_device()
     if out is None:
         out = torch.empty((M, F), dtype=od, device=X.device)
@@ -427,3 +514,23 @@ def pack_fine(W: torch.Tensor, fine_map, mask: torch.Tensor, b1: int, b2: int) -
     emap = exec_tile_map(N, K, fm_host, b1, b2)
     Wm = apply_fine_mask(W, torch.from_numpy(fm_host).to(W.device), mask, b1, b2)
     return pack(Wm, emap, mask)
+
+
+def probe_stream_read(src: torch.Tensor, sink: torch.Tensor) -> None:
+    """Read every byte of src once (patch_probe_stream_read); time it around
+    the call.  sink: a device scratch tensor (its bytes bound the grid)."""
+    _check_dev(src, "src")
+    _check_dev(sink, "sink")
+    nb = src.numel() * src.element_size()
+    _check(load().patch_probe_stream_read(_ptr(src), nb - nb % 16, _ptr(sink), sink.numel() * sink.element_size(),
+                                          _stream(src.device.index)))
+
+
+def probe_matrix_rate(kind: int, iters: int, workgroups: int, sink: torch.Tensor) -> int:
+    """Launch the matrix-instruction rate probe (patch_probe_matrix_rate);
+    returns the flops it executes (dense-equivalent for the sparse kinds)."""
+    _check_dev(sink, "sink")
+    _need(sink.numel() * sink.element_size() >= 4 * workgroups, "sink needs 4 bytes a workgroup")
+    lib = load()
+    _check(lib.patch_probe_matrix_rate(kind, iters, workgroups, _ptr(sink), _stream(sink.device.index)))
+    return int(lib.patch_probe_matrix_flops(kind, iters, workgroups))

@@ -78,7 +78,7 @@ def test_bad_arguments_rejected_before_launch():
         "PATCH_ERR_INVALID_ARG"
     assert patch.STATUS[lib.patch_dense_gemm_ex(1, 129, 256, 256, V(16), V(16), V(16), 1, None, 0, 1, None)] == \
         "PATCH_ERR_INVALID_ARG"
-    for bad_variant in (11, 12, -1):
+    for bad_variant in (17, 18, -1):
         assert patch.STATUS[lib.patch_dense_gemm_ex(1, 4, 256, 256, V(16), V(16), V(16), 1, None, 0, bad_variant,
                                                     None)] == "PATCH_ERR_INVALID_ARG"
     # a workspace size without a workspace, or an unaligned one
@@ -153,3 +153,67 @@ def test_exec_tile_map_rejects_bad_tiles():
         assert lib.patch_exec_tile_map(256, 256, b1, b2, P(fm.ctypes.data), P(out.ctypes.data), None) == want
     assert lib.patch_exec_tile_map(256, 256, 4, 4, None, P(out.ctypes.data), None) == 1
     assert lib.patch_exec_tile_map(200, 256, 4, 4, P(fm.ctypes.data), P(out.ctypes.data), None) == 2
+
+
+def test_desc_from_header_needs_76_bytes():
+    """The descriptor's last field (n_48) is at header bytes 72..75: a shorter
+    buffer is rejected instead of read past its end."""
+    p = inputs.make_custom("bf16", 256, 384, 3, "bernoulli", 0.5, "top2")
+    blob = oracle.pack("bf16", p.w, p.tile_map, p.mask)
+    assert patch.desc_from_header(bytes(blob[:76].tobytes())).N == 256
+    for n in (72, 75):
+        with pytest.raises(patch.PatchError) as e:
+            patch.desc_from_header(bytes(blob[:n].tobytes()))
+        assert e.value.name == "PATCH_ERR_BUFFER_TOO_SMALL"
+
+
+def _fake_packed(N=256, K=384, dtype=1):
+    d = patch.Desc()
+    d.version, d.dtype, d.tile_n, d.tile_k, d.N, d.K = 3, dtype, 128, 128, N, K
+    d.nt_n, d.nt_k = N // 128, K // 128
+    d.table_offset, d.data_offset = 256, 256 + 256
+    d.total_bytes = 512 + 32768 * d.nt_n * d.nt_k
+    return patch.PackedWeight(torch.zeros(d.total_bytes, dtype=torch.uint8), d)
+
+
+def test_binding_rejects_bad_tensors_before_any_call():
+    """The C ABI takes raw pointers, so the binding checks shapes, dtypes,
+    layout and device before calling it (no GPU is touched here: every case
+    fails in the binding)."""
+    pw = _fake_packed()
+    bf = torch.bfloat16
+    X = torch.zeros(4, 384, dtype=bf)
+    cases = [
+        (lambda: patch.gemm(torch.zeros(4, 256, dtype=bf), pw), "K = 384"),          # X has the wrong K
+        (lambda: patch.gemm(torch.zeros(4, 384, dtype=torch.float16), pw), "bfloat16"),  # X dtype != blob dtype
+        (lambda: patch.gemm(torch.zeros(384, 8, dtype=bf).t(), pw), "contiguous"),   # transposed view
+        (lambda: patch.gemm(torch.zeros(4, 768, dtype=bf)[:, ::2], pw), "contiguous"),  # strided view
+        (lambda: patch.gemm(torch.zeros(384, dtype=bf), pw), "2-D"),
+        (lambda: patch.gemm(X, pw, out_dtype=torch.float32, out=torch.zeros(4, 256, dtype=bf)), "float32"),
+        (lambda: patch.gemm(X, pw, out=torch.zeros(4, 128, dtype=bf)), "shape"),
+        (lambda: patch.gemm(X, pw, out=torch.zeros(256, 4, dtype=bf).t()), "contiguous"),
+        (lambda: patch.gemm(X, pw, out_dtype=torch.float16), "out_dtype"),
+        (lambda: patch.gemm(X, pw), "device"),                                       # all checks pass but the device
+        (lambda: patch.gemm(X, patch.PackedWeight(pw.blob[:100], pw.desc)), "smaller"),
+        (lambda: patch.dense_gemm(X, torch.zeros(256, 256, dtype=bf)), "K = 256"),
+        (lambda: patch.dense_gemm(X, torch.zeros(256, 384, dtype=torch.float16)), "bfloat16"),
+        (lambda: patch.dense_gemm(X, torch.zeros(384, 256, dtype=bf).t()), "contiguous"),
+        (lambda: patch.dense_gemm(X, torch.zeros(256, 384, dtype=bf), out=torch.zeros(4, 255, dtype=bf)), "shape"),
+        (lambda: patch.gemm_swiglu(X, pw, out=torch.zeros(4, 256, dtype=bf)), "shape"),  # H is M x N/2
+        (lambda: patch.dense_gemm_swiglu(X, torch.zeros(128, 384, dtype=bf), torch.zeros(256, 384, dtype=bf)),
+         "shape"),
+        (lambda: patch.pack(torch.zeros(256, 384, dtype=bf), np.zeros((2, 3), np.uint8),
+                            torch.zeros(256, 384, dtype=torch.int8)), "uint8"),
+        (lambda: patch.pack(torch.zeros(256, 384, dtype=bf), np.zeros((2, 3), np.uint8),
+                            torch.zeros(256, 383, dtype=torch.uint8)), "shape"),
+        (lambda: patch.pack(torch.zeros(256, 384, dtype=bf), np.zeros((3, 2), np.uint8),
+                            torch.zeros(256, 384, dtype=torch.uint8)), "tile map"),
+        (lambda: patch.pack(torch.zeros(256, 384, dtype=torch.float32), np.zeros((2, 3), np.uint8),
+                            torch.zeros(256, 384, dtype=torch.uint8)), "float16 or bfloat16"),
+        (lambda: patch.pack(torch.zeros(256, 384, dtype=bf), np.zeros((2, 3), np.uint8),
+                            torch.zeros(256, 384, dtype=torch.uint8)), "device"),
+    ]
+    for fn, text in cases:
+        with pytest.raises(ValueError) as e:
+            fn()
+        assert text in str(e.value), (text, str(e.value))

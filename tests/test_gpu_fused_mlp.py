@@ -121,7 +121,7 @@ def test_swiglu_small_ragged(dtype, M):
 
 
 PREFILL_KERNELS = ["prefill_w64", "prefill_w128", "prefill_w192", "prefill_w256", "prefill_w128_lds", "prefill_w192_lds",
-                   "prefill_w256_lds", "prefill_w64_lds"]
+                   "prefill_w256_lds", "prefill_w64_lds", "prefill_big_w128", "prefill_big_w192", "prefill_big_w256", "prefill_big8_w128", "prefill_big8_w256"]
 
 
 @pytest.mark.parametrize("variant", PREFILL_KERNELS)

@@ -20,7 +20,8 @@ from tests.gpu_util import assert_close, dev_bits, dev_u8, host_f64
 
 pytestmark = pytest.mark.gpu
 
-LDS_KERNELS = ["prefill_w64_lds", "prefill_w128_lds", "prefill_w192_lds", "prefill_w256_lds"]
+LDS_KERNELS = ["prefill_w64_lds", "prefill_w128_lds", "prefill_w192_lds", "prefill_w256_lds", "prefill_big_w128",
+               "prefill_big_w192", "prefill_big_w256", "prefill_big8_w128", "prefill_big8_w256"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -123,8 +124,9 @@ def test_gemm_48_identity_x():
     E = oracle.effective_mask(N, K, p.tile_map, p.mask)
     WE = inputs.bits_to_f32(np.where(E != 0, p.w, 0).astype(np.uint16), "bf16").astype(np.float64)
     eye = inputs.to_bits(np.eye(K), "bf16")
-    y = patch.gemm(dev_bits(eye, "bf16"), pw, out_dtype=torch.float32, variant="prefill")
-    assert np.array_equal(host_f64(y), WE.T)
+    for v in ["prefill"] + LDS_KERNELS:
+        y = patch.gemm(dev_bits(eye, "bf16"), pw, out_dtype=torch.float32, variant=v)
+        assert np.array_equal(host_f64(y), WE.T), v
     for rows in (16, 128):
         for k0 in range(0, K, rows):
             y = patch.gemm(dev_bits(eye[k0:k0 + rows], "bf16"), pw, out_dtype=torch.float32, variant="decode")

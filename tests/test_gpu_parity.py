@@ -229,7 +229,8 @@ def test_prefill_split_k(N, K, M):
 
 
 PREFILL_KERNELS = ["prefill_w64", "prefill_w128", "prefill_w192", "prefill_w256", "prefill_w128_lds", "prefill_w192_lds",
-                   "prefill_w256_lds", "prefill_w64_lds"]
+                   "prefill_w256_lds", "prefill_w64_lds", "prefill_big_w128", "prefill_big_w192", "prefill_big_w256", "prefill_big8_w128", "prefill_big8_w256"]
+BIG_KERNELS = ["prefill_big_w128", "prefill_big_w192", "prefill_big_w256", "prefill_big8_w128", "prefill_big8_w256"]
 
 
 @pytest.mark.parametrize("variant", PREFILL_KERNELS)
@@ -273,7 +274,7 @@ def test_prefill_every_kernel_f16_exact(variant):
     assert np.array_equal(host_f64(y), ref), variant
 
 
-@pytest.mark.parametrize("variant", [v for v in PREFILL_KERNELS if v.endswith("_lds")])
+@pytest.mark.parametrize("variant", [v for v in PREFILL_KERNELS if v.endswith("_lds") or "big" in v])
 def test_prefill_lds_short_k(variant):
     """The LDS-staged kernels at one to three tile columns (two to six
     64-column steps: the pipeline's first step is also its last-but-one or
@@ -304,9 +305,10 @@ def test_identity_x_gives_masked_weights_exactly(dtype):
     E = oracle.effective_mask(p.N, p.K, p.tile_map, p.mask)
     Weff = np.where(E != 0, inputs.bits_to_f32(p.w, dtype), 0.0).astype(np.float64)
     eye = inputs.to_bits(np.eye(p.K), dtype)
-    # prefill: all K rows at once
-    y = patch.gemm(dev_bits(eye, dtype), pw, variant="prefill")
-    assert np.array_equal(host_f64(y).T, Weff)
+    # prefill: all K rows at once, every prefill kernel staged through LDS
+    for v in ["prefill", "prefill_w64_lds"] + BIG_KERNELS:
+        y = patch.gemm(dev_bits(eye, dtype), pw, variant=v)
+        assert np.array_equal(host_f64(y).T, Weff), v
     # decode: 16 rows at a time (one block of M), then 128 (eight blocks)
     for rows in (16, 128):
         for k0 in range(0, p.K, rows):
@@ -326,7 +328,7 @@ def test_small_integers_exact_in_f32(dtype, M):
     Xb = inputs.to_bits(rng.integers(-2, 3, (M, K)).astype(np.float64), dtype)
     pw, _ = _pack(p)
     ref = _ref(p, Xb)
-    for v in ["prefill"] + (["decode"] if M <= 128 else []):
+    for v in ["prefill"] + BIG_KERNELS + (["decode"] if M <= 128 else []):
         y = patch.gemm(dev_bits(Xb, dtype), pw, out_dtype=torch.float32, variant=v)
         assert np.array_equal(host_f64(y), ref), v
 
@@ -345,8 +347,9 @@ def test_six_patterns_every_lane_slot():
     pw = patch.pack(dev_bits(w, "bf16"), tm, dev_u8(mask))
     eye = inputs.to_bits(np.eye(K), "bf16")
     ref = oracle.gemm_f64("bf16", eye, w, tm, mask)
-    y = patch.gemm(dev_bits(eye, "bf16"), pw, out_dtype=torch.float32, variant="prefill")
-    assert np.array_equal(host_f64(y), ref)
+    for v in ["prefill"] + BIG_KERNELS:
+        y = patch.gemm(dev_bits(eye, "bf16"), pw, out_dtype=torch.float32, variant=v)
+        assert np.array_equal(host_f64(y), ref), v
     for rows in (16, 32, 64, 128):
         for k0 in range(0, K, rows):
             y = patch.gemm(dev_bits(eye[k0:k0 + rows], "bf16"), pw, out_dtype=torch.float32, variant="decode")
@@ -491,15 +494,22 @@ def test_config_imbalanced_13b_sampled(mi):
     assert_close(y[torch.from_numpy(rows).cuda()], _ref(p, Xb, rows), what=f"13b {cfg.matrices[mi].name}")
 
 
-@pytest.mark.parametrize("mi", [0, 4, 6])
+@pytest.mark.parametrize("mi", range(7))
 def test_config_sweep_sampled(mi):
-    """Sparsity sweep (q_proj, gate_proj, down_proj) at every sparse-tile
-    fraction and every M of the sweep, on sampled output rows."""
+    """Sparsity sweep, every one of its seven independently seeded
+    LLaMA-2-7B matrices (q, k, v, o, gate, up, down), at every sparse-tile
+    fraction: the packed blob equals the oracle's byte for byte, and the GEMM
+    at every M of the sweep is within tolerance on sampled output rows."""
     cfg = inputs.CONFIGS["sweep"]
+    base = None
     for si, frac in enumerate(cfg.fractions):
-        p = inputs.make_weights(cfg, mi, si)
+        p = inputs.make_weights(cfg, mi, si, reuse=base)
+        base = base or p
         assert p.tile_map.sum() == int(np.round(frac * p.tile_map.size))
         pw, _ = _pack(p)
+        blob = pw.blob.cpu().numpy()
+        want = oracle.pack("bf16", p.w, p.tile_map, p.mask)
+        assert blob.size == want.size and np.array_equal(blob, want), f"sweep {cfg.matrices[mi].name} s={frac} blob"
         for M in cfg.Ms:
             Xb = inputs.make_x(cfg, M, p.K, matrix_index=mi)
             y = patch.gemm(dev_bits(Xb, "bf16"), pw)
