@@ -49,6 +49,7 @@ namespace patch {
 constexpr int kBgWStage = 32768;  // 2 row-blocks x 8 bands x 2 slots of 1 KB (row-major W: 256 rows x 128 B)
 constexpr int kBgEntRegs = 4;                 // tile-entry registers a row-block (64 tile columns each)
 constexpr int kBgMaxKT = 64 * kBgEntRegs;     // tile columns a workgroup can hold entries of
+static_assert(kBgMaxKT == 256, "the launcher gives this kernel K ranges of at most 256 tile columns");
 
 // WAVES = 4 (one a SIMD: waves = 2 band halves x 2 token halves) or 8 (two
 // a SIMD: 2 band halves x 4 token quarters).  Every wave holds its band
