@@ -348,6 +348,26 @@ patch_status patch_apply_fine_mask(patch_dtype dtype, int64_t N, int64_t K, int6
                                    void* stream);
 
 /*
+ * patch_gemm without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The prefill kernel's K split -- the
+ * only scratch the GEMM path uses: fp32 partial sums of the K ranges,
+ * written in full before they are read, nothing to clear -- goes to a
+ * device array of patch_noalloc_scratch_bytes() bytes (64 MiB) that the
+ * library holds on every device it runs on until the process ends.
+ * Arguments and results as patch_gemm, same kernels and launch shapes.
+ * Errors: as patch_gemm; PATCH_ERR_BUFFER_TOO_SMALL if this shape's launch
+ * wants more scratch than the array holds (patch_gemm_workspace_bytes(desc,
+ * M) > patch_noalloc_scratch_bytes()), checked on the host before anything
+ * is launched; PATCH_ERR_HIP if the array's address cannot be had.  Calls
+ * that overlap on one device share the array and race: serialize them.
+ * The call allocates nothing (no hipMalloc, no library allocation).
+ */
+uint64_t patch_noalloc_scratch_bytes(void);
+patch_status patch_gemm_noalloc(const patch_packed_desc* desc, const void* packed_dev, const void* X_dev, int64_t M,
+                                void* Y_dev, patch_dtype y_dtype, void* stream);
+
+/*
  * Measurement probes.  They compute nothing of the method; they measure, on
  * the device the GEMMs run on, the ceilings the GEMM kernels are compared
  * with (the datasheet peaks -- 8 TB/s HBM, 2.5 PFLOP/s dense bf16 matrix

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpatch.so")
-SOURCES = ["pack.hip", "gemm_decode.hip", "gemm_prefill.hip", "gemm_prefill_big.hip", "sampler.hip", "fine_mask.hip", "probe.hip", "patch_api.cpp"]
+SOURCES = ["pack.hip", "gemm_decode.hip", "gemm_prefill.hip", "gemm_prefill_big.hip", "sampler.hip", "fine_mask.hip", "probe.hip", "noalloc.hip", "patch_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -62,6 +62,17 @@ patch_status fail(patch_status s, const char* fmt, ...) {
   return s;
 }
 
+}  // namespace
+
+namespace patch {
+patch_status set_last_error(patch_status s, const char* msg) {
+  g_err = msg;
+  return s;
+}
+}  // namespace patch
+
+namespace {
+
 patch_status hip_fail(hipError_t e, const char* what) {
   return fail(PATCH_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
 }

@@ -51,7 +51,8 @@ EXPORTS = ("patch_abi_version", "patch_packed_bytes", "patch_pack", "patch_desc_
            "patch_gemm_swiglu_workspace_bytes", "patch_gemm_swiglu", "patch_dense_gemm_swiglu_workspace_bytes",
            "patch_dense_gemm_swiglu", "patch_packed_bytes_concat", "patch_pack_concat", "patch_sample_mask",
            "patch_exec_tile_map", "patch_apply_fine_mask", "patch_probe_stream_read", "patch_probe_matrix_rate",
-           "patch_probe_matrix_flops", "patch_status_string", "patch_last_error")
+           "patch_probe_matrix_flops", "patch_noalloc_scratch_bytes", "patch_gemm_noalloc", "patch_status_string",
+           "patch_last_error")
 
 _lib = None
 
@@ -114,6 +115,10 @@ def load():
     lib.patch_probe_matrix_rate.restype = ctypes.c_int
     lib.patch_probe_matrix_flops.argtypes = [I32, I32, I32]
     lib.patch_probe_matrix_flops.restype = U64
+    lib.patch_noalloc_scratch_bytes.argtypes = []
+    lib.patch_noalloc_scratch_bytes.restype = U64
+    lib.patch_gemm_noalloc.argtypes = [DP, P, P, I64, P, ctypes.c_int, P]
+    lib.patch_gemm_noalloc.restype = ctypes.c_int
     lib.patch_status_string.argtypes = [ctypes.c_int]
     lib.patch_status_string.restype = ctypes.c_char_p
     lib.patch_last_error.argtypes = []
@@ -323,6 +328,24 @@ def gemm(X: torch.Tensor, packed: PackedWeight, out_dtype: Optional[torch.dtype]
     _check(lib.patch_gemm_ex(ctypes.byref(packed.desc), packed.blob.data_ptr(), X.data_ptr(), M, out.data_ptr(),
                              _dt(od), None if ws is None else ws.data_ptr(), nb, VARIANTS[variant],
                              _stream(dev)))
+    return out
+
+
+def gemm_noalloc(X: torch.Tensor, packed: PackedWeight, out: torch.Tensor,
+                 out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    """Y = X (W o E)^T into a caller-supplied `out` with the library's own
+    device scratch (patch_gemm_noalloc): nothing is allocated, by the
+    library or here."""
+    lib = _lib or load()
+    _check_x(X, packed.dtype, packed.K)
+    _check_dev(packed.blob, "packed blob", torch.uint8, on_device=False)
+    _need(packed.blob.numel() >= packed.nbytes, "packed blob is smaller than its descriptor's total_bytes")
+    od = out_dtype or out.dtype
+    _check_out_dtype(od, X.dtype)
+    _check_out(out, (X.shape[0], packed.N), od)
+    _same_device(X, ("packed blob", packed.blob), ("out", out))
+    _check(lib.patch_gemm_noalloc(ctypes.byref(packed.desc), packed.blob.data_ptr(), X.data_ptr(), X.shape[0],
+                                  out.data_ptr(), _dt(od), _stream(X.get_device())))
     return out
 
 
