@@ -48,15 +48,15 @@ struct DecodeFrag {
   uint32_t kind;
 };
 
-// Lanes whose X row is >= M only feed output columns >= M, which are never
-// stored, so they need no X at all: they re-read their own W chunk (same
-// cache lines as the A load) instead of a predicated load (which would make
-// the compiler wait for it right away) or all hitting row 0 of X (a hot spot
-// when M is 1).
+// X is read through a buffer descriptor whose range ends with row M - 1:
+// lanes whose X row is >= M (they only feed output columns that are never
+// stored) get zeros from the range check, with no memory access, no
+// predication (which would make the compiler wait for the load at once) and
+// no hot spot on row 0 when M is 1.
 template <bool SRC_ROWMAJOR, int MB>
 __device__ __forceinline__ void decode_load(DecodeFrag<MB>& f, const uint8_t* __restrict__ src, uint64_t off,
-                                            uint32_t kind, uint32_t stride, const uint16_t* __restrict__ X, int K,
-                                            int M, int i, int b, int j, int l) {
+                                            uint32_t kind, uint32_t stride, __amdgpu_buffer_rsrc_t xr, int K,
+                                            int i, int b, int j, int l) {
   const int h = l >> 4;
   const uint8_t* ap[4];
   if constexpr (SRC_ROWMAJOR) {
@@ -79,10 +79,10 @@ __device__ __forceinline__ void decode_load(DecodeFrag<MB>& f, const uint8_t* __
   }
 #pragma unroll
   for (int mb = 0; mb < MB; mb++) {
-    const int m = 16 * mb + (l & 15);
-    const uint8_t* xr = reinterpret_cast<const uint8_t*>(X + (int64_t)m * K + (int64_t)j * kTile + 8 * h);
+    const uint32_t xo = ((uint32_t)(16 * mb + (l & 15)) * (uint32_t)K + (uint32_t)(j * kTile + 8 * h)) * 2u;
 #pragma unroll
-    for (int c = 0; c < 4; c++) f.x[mb][c] = ld16(m < M ? xr + 64 * c : ap[c]);
+    for (int c = 0; c < 4; c++)
+      f.x[mb][c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (int)xo, 64 * c, 0));
   }
 #pragma unroll
   for (int c = 0; c < 4; c++) f.a[c] = ld16(ap[c]);
@@ -176,6 +176,9 @@ __global__ __launch_bounds__(WAVES * 64 * (FUSE ? 2 : 1)) void k_decode(const ui
   const int wi = SRC_ROWMAJOR && FUSE ? q : i;
 
   __shared__ f32x4 s_red[kAllWaves * MB][64];
+  // X rows 0 .. M-1 (byte range M K 2, below 2^31 for M <= 128, K <= 65536)
+  const __amdgpu_buffer_rsrc_t xr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X), (short)0, M * K * 2, 0x00020000);
   // 4:8 rebuild selectors (only in the instantiation for blobs with 4:8 tiles)
   __shared__ u32x4 s_sel[N48 ? 256 : 1];
   if constexpr (N48) {
@@ -214,7 +217,7 @@ __global__ __launch_bounds__(WAVES * 64 * (FUSE ? 2 : 1)) void k_decode(const ui
       uint64_t off;
       uint32_t kind, stride;
       entry(t, off, kind, stride);
-      decode_load<SRC_ROWMAJOR, MB>(f[s], SRC_ROWMAJOR ? wsrc : src, off, kind, stride, X, K, M, wi, b,
+      decode_load<SRC_ROWMAJOR, MB>(f[s], SRC_ROWMAJOR ? wsrc : src, off, kind, stride, xr, K, wi, b,
                                     w + kDecodeWaves * t, l);
     }
     // steady state: compute the DEPTH slots, refilling each with the tile
@@ -228,7 +231,7 @@ __global__ __launch_bounds__(WAVES * 64 * (FUSE ? 2 : 1)) void k_decode(const ui
         uint64_t off;
         uint32_t kind, stride;
         entry(tn, off, kind, stride);
-        decode_load<SRC_ROWMAJOR, MB>(f[s], SRC_ROWMAJOR ? wsrc : src, off, kind, stride, X, K, M, wi, b,
+        decode_load<SRC_ROWMAJOR, MB>(f[s], SRC_ROWMAJOR ? wsrc : src, off, kind, stride, xr, K, wi, b,
                                       w + kDecodeWaves * tn, l);
       }
     }

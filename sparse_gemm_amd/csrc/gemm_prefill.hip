@@ -509,8 +509,10 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   }
   const uint32_t w_lds = lds_addr(s_w), x_lds = lds_addr(s_x);
 
-  // the copies of step s into stage s % kLdsStages
-  auto issue = [&](int s) {
+  // the copies of step s into stage s % kLdsStages; e_v: the tile entry of
+  // step s for this wave's row-block (a VGPR loaded from LDS earlier, so no
+  // LDS round trip sits between the step's barrier and its copies)
+  auto issue = [&](int s, uint32_t e_v) {
     const int st = s % kLdsStages;
     const int jl = s >> 1, h = s & 1, j = j0 + jl;
     const uint32_t wb = w_lds + (uint32_t)(st * kLdsWStage), xb = x_lds + (uint32_t)(st * kLdsXStage);
@@ -529,7 +531,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
 #pragma unroll
       for (int b = 0; b < 4; b++) dma16(W + (int64_t)16 * b * K, slot0 + 2048u * b + 1024u * wm);
     } else {
-      const uint32_t e = __builtin_amdgcn_readfirstlane(s_ent[r_src][jl]);
+      const uint32_t e = (uint32_t)__builtin_amdgcn_readfirstlane((int)e_v);
       const uint8_t* piece = P.src + ((uint64_t)(e & 0x3fffffffu) << 8) + (uint64_t)(4 * wn) * stride;
       if ((e >> 30) == 0) {
 #pragma unroll
@@ -575,6 +577,12 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
     if constexpr (SRC_ROWMAJOR) return 0u;
     return (uint32_t)__builtin_amdgcn_readfirstlane((int)s_ent[r_src][s >> 1]) >> 30;
   };
+  // this wave's tile entry of step s as a VGPR (an LDS load nobody waits
+  // for until the value is used)
+  auto ent_v = [&](int s) -> uint32_t {
+    if constexpr (SRC_ROWMAJOR) return 0u;
+    return s_ent[r_src][min(s, n_steps - 1) >> 1];
+  };
   // this wave's A fragments of step s (tile kind `kind`) from its stage
   auto read_a = [&](int s, uint32_t kind, u32x4 (&a0)[4], u32x4 (&a1)[4]) {
     const uint8_t* ws = s_w + (s % kLdsStages) * kLdsWStage + 1024 * ((r * 8 + 4 * wn) * 2);
@@ -593,14 +601,14 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   // called in step s (s + 1 < n_steps) once this wave's reads of stage s
   // are issued: step s + 1's copies have landed everywhere and nobody reads
   // stage s any more, which the copies of step s + 1 + kAhead then refill
-  auto advance = [&](int s) {
+  auto advance = [&](int s, uint32_t e_copy) {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage s are done
     if (kAhead == 2 && s + 2 < n_steps)
       wait_copies<kLdsCopies>();  // step s + 2's copies may stay in flight
     else
       wait_copies<0>();
     wg_barrier();
-    if (s + 1 + kAhead < n_steps) issue(s + 1 + kAhead);
+    if (s + 1 + kAhead < n_steps) issue(s + 1 + kAhead, e_copy);
   };
 
   // packed W, step s: A fragments a0/a1 (kind), B group 0 in buffer par * G & 1
@@ -611,8 +619,10 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
                          u32x4 (&na1)[4], uint32_t& nkind, u32x4 (&blo)[2][kMG],
                          u32x4 (&bhi)[2][kMG]) {
     const int h = s & 1;
-    // step s + 1's kind, read early (its fragments' addresses depend on it)
-    nkind = step_kind(min(s + 1, n_steps - 1));
+    // step s + 1's entry (its kind: its fragments' addresses depend on it)
+    // and that of the step whose copies this step issues, loaded now and
+    // read after the step's barrier
+    const uint32_t nk_v = ent_v(s + 1), ecopy_v = ent_v(s + 1 + kAhead);
     if (kind == 2) {
       // 4:8: each band's sixteen columns rebuilt into a dense piece's two
       // halves (values in a0, the lane's masks in the codes chunk a1),
@@ -637,7 +647,8 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
     for (int g = 0; g < kGroups; g++) {
       const int cb = (g + par * kGroups) & 1, nb = (g + 1 + par * kGroups) & 1;
       const bool last = g + 1 == kGroups;
-      if (last && s + 1 < n_steps) advance(s);
+      if (last && s + 1 < n_steps) advance(s, ecopy_v);
+      if (last) nkind = (uint32_t)__builtin_amdgcn_readfirstlane((int)nk_v) >> 30;
       __builtin_amdgcn_sched_barrier(0);
       // the first half (a 2:4 tile's only one) with the next group's reads
       // -- or, in the last group, step s + 1's first fragments -- spread
@@ -693,7 +704,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
     for (int g = 0; g < 2 * kRParts; g++) {
       const int qq = g / kRParts, part = g % kRParts;
       const bool last = g + 1 == 2 * kRParts;
-      if (last && s + 1 < n_steps) advance(s);
+      if (last && s + 1 < n_steps) advance(s, 0u);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int mm = 0; mm < kRG; mm++)
@@ -728,13 +739,13 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   };
 
 #pragma unroll
-  for (int s = 0; s < kAhead; s++) issue(s);  // n_steps >= 2 >= kAhead
+  for (int s = 0; s < kAhead; s++) issue(s, ent_v(s));  // n_steps >= 2 >= kAhead
   if (kAhead == 2)
     wait_copies<kLdsCopies>();
   else
     wait_copies<0>();
   wg_barrier();
-  if (kAhead < n_steps) issue(kAhead);
+  if (kAhead < n_steps) issue(kAhead, ent_v(kAhead));
   u32x4 fa0[4], fa1[4], fb0[4], fb1[4];
   uint32_t ka = step_kind(0), kb;
   read_a(0, ka, fa0, fa1);
