@@ -36,11 +36,13 @@
  * ascending order in binary64, so the result does not depend on the number
  * of threads (OpenMP splits the work over output rows n only).
  *
- * The packed format is the repository's own (format version 3): the pages fix
- * only the tile shape (128 x 128 execution tiles, gist.science explainer,
- * section 4 "Ablation Studies"), the six 2:4 patterns (section 2, "Pattern
- * Selection") and nothing about bytes.  oracle_pack() writes it from its
- * written definition, restated next to the function.
+ * The packed formats are the repository's own (version 3: 128 x 128
+ * execution tiles; version 4: 64 x 64 ones): the pages fix only the tile
+ * shape (128 x 128 execution tiles, gist.science explainer, section 4
+ * "Ablation Studies", which also finds smaller tiles give finer control),
+ * the six 2:4 patterns (section 2, "Pattern Selection") and nothing about
+ * bytes.  oracle_pack() and oracle_pack_q64() write them from their written
+ * definitions, restated next to each function.
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -478,6 +480,160 @@ int oracle_pack(int dtype, int64_t N, int64_t K, const uint16_t* W, const uint8_
       prefix += sparse ? PT_SPARSE_PIECE : PT_DENSE_PIECE;
     }
     rb += 8 * stride;
+  }
+  return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * Packed format version 4: 64 x 64 execution tiles (the repository's own
+ * layout).  The explainer's section 4 "Ablation Studies" ("Tile Size") finds
+ * the method robust across tile sizes, the smaller ones giving finer
+ * control, while execution wants large tiles; this format lets every 64 x 64
+ * quadrant of a 128 x 128 tile be dense or 2:4 on its own.  Only dense and
+ * 2:4 (no 4:8).  N and K multiples of 128.  Little-endian; all bytes not
+ * written below are zero.
+ *
+ * Input: a quadrant map of (N/64) x (K/64) bytes, quadrant (R, C) -- rows
+ * 64R .. 64R+63, columns 64C .. 64C+63 -- at R*(K/64) + C: 0 dense, 1 2:4.
+ *
+ * Header, 256 bytes at offset 0, as in version 3 except: version 4,
+ *   tile_n = tile_k = 64, NT = N/64, KT = K/64 (the quadrant map's shape),
+ *   n_sparse = the 2:4 quadrants, n_48 = 0.
+ * A "half-row-block" r (r = 0 .. N/64 - 1) is rows 64r .. 64r+63; with
+ * KC = K/128 tile columns, a "cell" (r, j) is its columns 128j .. 128j+127:
+ * two quadrants, slice q = 0, 1 being quadrant (r, 2j + q).  Its kind bits
+ * are k = sparse(r, 2j) | sparse(r, 2j+1) << 1.
+ * Table at 256: N/64 * KC entries of 16 bytes, cell (r, j) at r*KC + j:
+ *   u64 byte offset of the cell's band-0 piece, u32 kind bits k, u32 S_r.
+ * Data at data_offset = round_up(256 + 16 * (N/64) * KC, 256).
+ *
+ * A "band" is 16 rows of a half-row-block (b = 0..3, rows 64r + 16b ..);
+ * a "piece" is one band of one cell.  A piece holds the cell's two slices
+ * in order, a dense slice taking 2048 bytes and a 2:4 slice 1024, followed,
+ * if either slice is 2:4, by a 256-byte codes block: piece size
+ * P(k) = (k&1 ? 1024 : 2048) + (k&2 ? 1024 : 2048) + (k ? 256 : 0), i.e.
+ * 4096 (both dense), 3328 (one of each), 2304 (both 2:4).  Slice 1 starts at
+ * A1 = (k&1 ? 1024 : 2048), the codes block at A1 + (k&2 ? 1024 : 2048).
+ * S_r = sum over j of P(k(r, j)); half-row-block r takes 4 * S_r bytes,
+ * half-row-blocks follow each other; inside r, band b's pieces of cells
+ * j = 0 .. KC-1 lie back to back and band b starts S_r bytes after band b-1.
+ *
+ * Lanes l = 0..63 as in version 3 (row-in-band l mod 16, column group
+ * h = l / 16, 16 bytes at 16 l of a 1 KB block).  For a slice q at byte A
+ * of the piece:
+ *   dense: blocks e = 0, 1 at A + 1024 e; lane l holds, of the row's four
+ *     groups of four at columns 128j + 64q + 16h .. +15, the elements at
+ *     positions 2e and 2e+1 (element 2g + u = column 128j + 64q + 16h +
+ *     4g + 2e + u) -- version 3's dense block (q, e);
+ *   2:4: the block at A; lane l holds, for p = 0..3, the two kept elements
+ *     (ascending column) of group G = 16q + 4h + p (columns 128j + 4G ..
+ *     +3) -- version 3's 2:4 value block q -- and the lane's u32 at
+ *     codes + 4 l holds, in bits 16q + 4p .. +3, that group's code
+ *     i0 | i1 << 2 (bits of a dense slice stay zero).
+ * So a piece with k = 0 or 3 is byte for byte a version-3 dense or 2:4
+ * piece, and a quadrant map constant on every 128 x 128 tile gives the same
+ * data bytes as version 3 (only the header and table differ).
+ * ------------------------------------------------------------------------- */
+#define PQ_B 64
+
+static uint64_t q64_piece(int k) { return (k & 1 ? 1024u : 2048u) + (k & 2 ? 1024u : 2048u) + (k ? 256u : 0u); }
+
+uint64_t oracle_packed_bytes_q64(int64_t N, int64_t K, const uint8_t* quad_map) {
+  if (N <= 0 || K <= 0 || N % PT_B || K % PT_B) return 0;
+  int64_t R = N / PQ_B, KC = K / PT_B, KQ = K / PQ_B;
+  uint64_t total = round_up(256 + 16 * (uint64_t)(R * KC), 256);
+  for (int64_t r = 0; r < R; r++)
+    for (int64_t j = 0; j < KC; j++) {
+      int k = (quad_map[r * KQ + 2 * j] != 0) | ((quad_map[r * KQ + 2 * j + 1] != 0) << 1);
+      total += 4 * q64_piece(k);
+    }
+  return total;
+}
+
+int oracle_pack_q64(int dtype, int64_t N, int64_t K, const uint16_t* W, const uint8_t* quad_map,
+                    const uint8_t* mask, uint8_t* out, uint64_t out_bytes) {
+  if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return ORACLE_ERR_ARG;
+  if (N <= 0 || K <= 0) return ORACLE_ERR_ARG;
+  if (N % PT_B || K % PT_B) return ORACLE_ERR_SHAPE;
+  int64_t R = N / PQ_B, KC = K / PT_B, KQ = K / PQ_B;
+  for (int64_t t = 0; t < R * KQ; t++)
+    if (quad_map[t] > 1) return ORACLE_ERR_ARG; /* dense and 2:4 only */
+  int rc = oracle_validate(N, K, PQ_B, PQ_B, quad_map, mask, NULL, NULL);
+  if (rc) return rc;
+  uint64_t total = oracle_packed_bytes_q64(N, K, quad_map);
+  if (out_bytes < total) return ORACLE_ERR_SMALL;
+  memset(out, 0, (size_t)total);
+  uint32_t ns = 0;
+  for (int64_t t = 0; t < R * KQ; t++) ns += quad_map[t] != 0;
+  uint64_t data_off = round_up(256 + 16 * (uint64_t)(R * KC), 256);
+  put32(out + 0, 0x48435450u);
+  put32(out + 4, 4);
+  put32(out + 8, (uint32_t)dtype);
+  put32(out + 12, PQ_B);
+  put32(out + 16, PQ_B);
+  put32(out + 20, (uint32_t)N);
+  put32(out + 24, (uint32_t)K);
+  put32(out + 28, (uint32_t)R);
+  put32(out + 32, (uint32_t)KQ);
+  put32(out + 36, ns);
+  put64(out + 40, 256);
+  put64(out + 48, data_off);
+  put64(out + 56, total - data_off);
+  put64(out + 64, total);
+  put32(out + 72, 0);
+
+  uint64_t hb = data_off; /* start of the current half-row-block */
+  for (int64_t r = 0; r < R; r++) {
+    uint64_t stride = 0; /* S_r */
+    for (int64_t j = 0; j < KC; j++)
+      stride += q64_piece((quad_map[r * KQ + 2 * j] != 0) | ((quad_map[r * KQ + 2 * j + 1] != 0) << 1));
+    uint64_t prefix = 0; /* offset of cell j's piece inside a band */
+    for (int64_t j = 0; j < KC; j++) {
+      int kb = (quad_map[r * KQ + 2 * j] != 0) | ((quad_map[r * KQ + 2 * j + 1] != 0) << 1);
+      uint8_t* ent = out + 256 + 16 * (r * KC + j);
+      put64(ent, hb + prefix);
+      put32(ent + 8, (uint32_t)kb);
+      put32(ent + 12, (uint32_t)stride);
+      uint64_t a1 = kb & 1 ? 1024 : 2048;
+      uint64_t codes = a1 + (kb & 2 ? 1024 : 2048);
+      for (int band = 0; band < 4; band++) {
+        uint8_t* piece = out + hb + (uint64_t)band * stride + prefix;
+        for (int q = 0; q < 2; q++) {
+          uint8_t* part = piece + (q ? a1 : 0);
+          int sparse = (kb >> q) & 1;
+          for (int l = 0; l < 64; l++) {
+            int64_t row = r * PQ_B + 16 * band + (l % 16);
+            int h = l / 16;
+            if (!sparse) {
+              for (int e = 0; e < 2; e++)
+                for (int g = 0; g < 4; g++)
+                  for (int u = 0; u < 2; u++) {
+                    int64_t col = j * PT_B + 64 * q + 16 * h + 4 * g + 2 * e + u;
+                    put16(part + 1024 * e + 16 * l + 2 * (2 * g + u), W[row * K + col]);
+                  }
+            } else {
+              for (int p = 0; p < 4; p++) {
+                int G = 16 * q + 4 * h + p;
+                int64_t c0 = j * PT_B + 4 * G;
+                int s = 0, pos[2] = {0, 0};
+                for (int d = 0; d < 4; d++)
+                  if (mask[row * K + c0 + d]) {
+                    put16(part + 16 * l + 2 * (2 * p + s), W[row * K + c0 + d]);
+                    pos[s++] = d;
+                  }
+                uint8_t* cw = piece + codes + 4 * l;
+                uint32_t word = (uint32_t)cw[0] | ((uint32_t)cw[1] << 8) | ((uint32_t)cw[2] << 16) |
+                                ((uint32_t)cw[3] << 24);
+                word |= ((uint32_t)pos[0] | ((uint32_t)pos[1] << 2)) << (16 * q + 4 * p);
+                put32(cw, word);
+              }
+            }
+          }
+        }
+      }
+      prefix += q64_piece(kb);
+    }
+    hb += 4 * stride;
   }
   return ORACLE_OK;
 }

@@ -63,6 +63,10 @@ def load():
     lib.oracle_packed_bytes.restype = ctypes.c_uint64
     lib.oracle_pack.argtypes = [ctypes.c_int, I64, I64, P, P, P, P, ctypes.c_uint64]
     lib.oracle_pack.restype = ctypes.c_int
+    lib.oracle_packed_bytes_q64.argtypes = [I64, I64, P]
+    lib.oracle_packed_bytes_q64.restype = ctypes.c_uint64
+    lib.oracle_pack_q64.argtypes = [ctypes.c_int, I64, I64, P, P, P, P, ctypes.c_uint64]
+    lib.oracle_pack_q64.restype = ctypes.c_int
     lib.oracle_silu.argtypes = [ctypes.c_double]
     lib.oracle_silu.restype = ctypes.c_double
     lib.oracle_swiglu_f64.argtypes = [ctypes.c_int, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P]
@@ -173,6 +177,33 @@ def pack(dtype, W, tile_map, mask) -> np.ndarray:
         raise OracleError(2)
     out = np.zeros(nbytes, dtype=np.uint8)
     rc = lib.oracle_pack(_DT[dtype], N, K, _p(W), _p(tm), _p(mk), _p(out), nbytes)
+    if rc:
+        raise OracleError(rc)
+    return out
+
+
+def packed_bytes_q64(N, K, quad_map) -> int:
+    """Size of the format-4 blob (64 x 64 execution tiles) for a (N/64, K/64) quadrant map."""
+    qm = _u8(quad_map)
+    if N % 128 or K % 128 or qm.shape != (N // 64, K // 64):
+        return 0
+    return int(load().oracle_packed_bytes_q64(N, K, _p(qm)))
+
+
+def pack_q64(dtype, W, quad_map, mask) -> np.ndarray:
+    """The format-4 blob (64 x 64 execution tiles, quadrant map 0 dense / 1
+    2:4) as a uint8 array."""
+    lib = load()
+    W = _u16(W)
+    N, K = W.shape
+    qm, mk = _u8(quad_map), _u8(mask)
+    if qm.shape != (N // 64, K // 64):
+        raise OracleError(2)
+    nbytes = lib.oracle_packed_bytes_q64(N, K, _p(qm))
+    if nbytes == 0:
+        raise OracleError(2)
+    out = np.zeros(nbytes, dtype=np.uint8)
+    rc = lib.oracle_pack_q64(_DT[dtype], N, K, _p(W), _p(qm), _p(mk), _p(out), nbytes)
     if rc:
         raise OracleError(rc)
     return out

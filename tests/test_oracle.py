@@ -384,6 +384,184 @@ def test_pack_keeps_negative_zero_bits():
     assert np.all(pieces[:, 2048:] == (13 | (13 << 4)))  # code (1,3) = 1 | 3 << 2 = 13
 
 
+# ------------------------------------------------------- format 4: 64 x 64 execution tiles
+def test_pack_q64_hand_worked_example():
+    g = _golden("pack_q64_example.txt")
+    N, K = 128, 256
+    W = np.full((N, K), 0x3F80, np.uint16)
+    for x in "abcdef":
+        W[g[x + ".row"], g[x + ".col"]] = g[x + ".bits"]
+    mask = np.zeros((N, K), np.uint8)
+    mask[:, 0::4] = 1
+    mask[:, 1::4] = 1
+    for x, keep in (("b", [1, 0, 0, 1]), ("c", [0, 1, 1, 0]), ("e", [0, 0, 1, 1])):
+        r, c = g[x + ".row"], g[x + ".col"]
+        mask[r, c - c % 4:c - c % 4 + 4] = keep
+    qmap = np.array([[0, 1, 1, 1], [1, 0, 0, 0]], np.uint8)
+    blob = oracle.pack_q64("bf16", W, qmap, mask)
+    u64 = lambda o: int.from_bytes(blob[o:o + 8].tobytes(), "little")
+    u32 = lambda o: int.from_bytes(blob[o:o + 4].tobytes(), "little")
+    u16 = lambda o: int.from_bytes(blob[o:o + 2].tobytes(), "little")
+    assert blob.size == g["header.total_bytes"] == oracle.packed_bytes_q64(N, K, qmap)
+    assert u32(0) == 0x48435450 and u32(4) == g["header.version"] and u32(8) == 1
+    assert u32(12) == u32(16) == g["header.tile"]
+    assert (u32(20), u32(24), u32(28), u32(32)) == (N, K, g["header.nt_n"], g["header.nt_k"])
+    assert u32(36) == g["header.n_sparse"] and u32(72) == 0
+    assert u64(40) == 256 and u64(48) == g["header.data_offset"] and u64(64) == g["header.total_bytes"]
+    assert u64(56) == g["header.total_bytes"] - g["header.data_offset"]
+    for t in range(4):
+        e = 256 + 16 * t
+        assert (u64(e), u32(e + 8), u32(e + 12)) == (g[f"table.{t}.offset"], g[f"table.{t}.kind"],
+                                                     g[f"table.{t}.stride"])
+    for x in "abcdef":
+        assert u16(g[x + ".byte_offset"]) == g[x + ".bits"], x
+    for x in "bce":
+        assert blob[g[x + ".code_byte_offset"]] == g[x + ".code_byte_value"], x
+    for x in "bc":
+        assert blob[g[x + ".zero_code_byte_offset"]] == 0, x
+
+
+def _unpack_q64(blob, N, K):
+    """Independent reader of format 4 (written from its definition): W o E
+    and the codes of every 2:4 group."""
+    R, KC = N // 64, K // 128
+    W = np.zeros((N, K), np.uint16)
+    codes = []
+    u64 = lambda o: int.from_bytes(blob[o:o + 8].tobytes(), "little")
+    u32 = lambda o: int.from_bytes(blob[o:o + 4].tobytes(), "little")
+    for r in range(R):
+        for j in range(KC):
+            e = 256 + 16 * (r * KC + j)
+            off, kb, stride = u64(e), u32(e + 8), u32(e + 12)
+            starts = [0, 1024 if kb & 1 else 2048]
+            code_at = starts[1] + (1024 if kb & 2 else 2048)
+            for band in range(4):
+                base = off + band * stride
+                for q in range(2):
+                    part = base + starts[q]
+                    for l in range(64):
+                        row = 64 * r + 16 * band + l % 16
+                        h = l // 16
+                        if (kb >> q) & 1:
+                            word = u32(base + code_at + 4 * l)
+                            vals = blob[part + 16 * l:part + 16 * l + 16].view(np.uint16)
+                            for p in range(4):
+                                G = 16 * q + 4 * h + p
+                                code = (word >> (16 * q + 4 * p)) & 15
+                                codes.append(code)
+                                W[row, 128 * j + 4 * G + (code & 3)] = vals[2 * p]
+                                W[row, 128 * j + 4 * G + (code >> 2)] = vals[2 * p + 1]
+                        else:
+                            if kb:  # a dense slice leaves its code bits zero
+                                assert (u32(base + code_at + 4 * l) >> (16 * q)) & 0xFFFF == 0
+                            for half in range(2):
+                                vals = blob[part + 1024 * half + 16 * l:part + 1024 * half + 16 * l + 16].view(np.uint16)
+                                for gg in range(4):
+                                    for u in range(2):
+                                        W[row, 128 * j + 64 * q + 16 * h + 4 * gg + 2 * half + u] = vals[2 * gg + u]
+    return W, np.array(codes)
+
+
+def _quad_problem(N, K, frac, seed, mask="uniform"):
+    rng = np.random.default_rng(seed)
+    qmap = (rng.random((N // 64, K // 64)) < frac).astype(np.uint8)
+    w = rng.integers(0, 1 << 16, (N, K), dtype=np.uint16)
+    # a random pair of the four positions in every group
+    pick = rng.integers(0, 6, (N, K // 4))
+    pairs = np.array([[0, 1], [0, 2], [0, 3], [1, 2], [1, 3], [2, 3]])
+    mk = np.zeros((N, K // 4, 4), np.uint8)
+    sel = pairs[pick]
+    np.put_along_axis(mk, sel, 1, axis=2)
+    if mask == "top2":
+        mk[:] = 0
+        mk[:, :, :2] = 1
+    return qmap, w, mk.reshape(N, K)
+
+
+@pytest.mark.parametrize("frac", [0.0, 0.4, 1.0])
+def test_pack_q64_round_trip_and_legal_codes(frac):
+    """unpack(pack(W)) == W o E for E from the 64 x 64 quadrant map,
+    bit-exactly; the codes are the six 2:4 patterns."""
+    N, K = 256, 384
+    qmap, w, mk = _quad_problem(N, K, frac, seed=41)
+    blob = oracle.pack_q64("bf16", w, qmap, mk)
+    W2, codes = _unpack_q64(blob, N, K)
+    E = oracle.effective_mask(N, K, qmap, mk, tile_n=64, tile_k=64)
+    assert np.array_equal(W2, np.where(E != 0, w, 0).astype(np.uint16))
+    if frac > 0:
+        assert set(np.unique(codes)) == {4, 8, 12, 9, 13, 14}
+
+
+def test_pack_q64_size_closed_form():
+    """total = data offset + 8192 per dense quadrant + 4096 per 2:4 quadrant
+    + 1024 per cell (pair of quadrants) holding any 2:4 quadrant."""
+    N, K = 384, 640
+    for frac in (0.0, 0.3, 1.0):
+        qmap, w, mk = _quad_problem(N, K, frac, seed=42)
+        ns = int(qmap.sum())
+        nq = qmap.size
+        cells = qmap.reshape(N // 64, K // 128, 2).max(axis=2)
+        E = (N // 64) * (K // 128)
+        expect = -(-(256 + 16 * E) // 256) * 256 + 8192 * (nq - ns) + 4096 * ns + 1024 * int(cells.sum())
+        assert oracle.packed_bytes_q64(N, K, qmap) == expect
+        assert oracle.pack_q64("f16", w, qmap, mk).size == expect
+
+
+def test_pack_q64_tile_constant_map_has_the_128_tile_data_bytes():
+    """A quadrant map constant on every 128 x 128 tile stores the same data
+    bytes as the 128 x 128 format (pieces of both-dense and both-2:4 cells
+    are the 128 x 128 format's pieces, in the same order)."""
+    N, K = 256, 512
+    rng = np.random.default_rng(43)
+    tmap = (rng.random((N // 128, K // 128)) < 0.5).astype(np.uint8)
+    qmap = np.kron(tmap, np.ones((2, 2), np.uint8))
+    _, w, mk = _quad_problem(N, K, 0.5, seed=44)
+    b3 = oracle.pack("bf16", w, tmap, mk)
+    b4 = oracle.pack_q64("bf16", w, qmap, mk)
+    d3 = int.from_bytes(b3[48:56].tobytes(), "little")
+    d4 = int.from_bytes(b4[48:56].tobytes(), "little")
+    assert np.array_equal(b3[d3:], b4[d4:])
+
+
+def test_pack_q64_rejects_bad_input():
+    N, K = 128, 256
+    qmap, w, mk = _quad_problem(N, K, 1.0, seed=45)
+    bad = qmap.copy()
+    bad[0, 0] = 2  # 4:8 is not a quadrant kind
+    with pytest.raises(oracle.OracleError) as ei:
+        oracle.pack_q64("bf16", w, bad, mk)
+    assert ei.value.code == 1
+    mk2 = mk.copy()
+    mk2[3, 64:68] = [1, 1, 1, 0]  # three kept in a 2:4 quadrant
+    with pytest.raises(oracle.OracleError) as ei:
+        oracle.pack_q64("bf16", w, qmap, mk2)
+    assert ei.value.code == 3
+    with pytest.raises(oracle.OracleError):
+        oracle.pack_q64("bf16", w[:, :192], qmap[:, :3], mk[:, :192])  # K not a multiple of 128
+
+
+def test_gemm_q64_brute_force_tiny():
+    """The product with a 64 x 64 tile map, against sums written out over
+    the kept weights (fp64, exact for these small integers)."""
+    N, K, M = 128, 128, 3
+    rng = np.random.default_rng(46)
+    qmap = np.array([[1, 0], [0, 1]], np.uint8)
+    _, _, mk = _quad_problem(N, K, 0.5, seed=47)
+    wv = rng.integers(-4, 5, (N, K)).astype(np.float32)
+    xv = rng.integers(-4, 5, (M, K)).astype(np.float32)
+    w = (wv.view(np.uint32) >> 16).astype(np.uint16)
+    x = (xv.view(np.uint32) >> 16).astype(np.uint16)
+    Y = oracle.gemm_f64("bf16", x, w, qmap, mk, tile_n=64, tile_k=64)
+    for m in range(M):
+        for n in range(N):
+            s = 0.0
+            for k in range(K):
+                sparse = qmap[n // 64, k // 64] == 1
+                if not sparse or mk[n, k]:
+                    s += float(xv[m, k]) * float(wv[n, k])
+            assert Y[m, n] == s
+
+
 # ------------------------------------------------------------------ gated MLP product (SiLU)
 def test_silu_closed_forms():
     """SiLU(x) = x / (1 + e^-x): zero at zero; SiLU(ln 3) = (3/4) ln 3
