@@ -42,8 +42,13 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, datasheet
 MFMA_PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 matrix peak, datasheet
 ROTATE_BYTES = 1 << 30          # >= 1 GiB of distinct weights per timed loop
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+# --hybrid-only: time the hybrid launches alone (no dense, all-dense-packed or
+# hipBLASLt references; the headline without its graph-replay figure), so
+# that a profiler's per-kernel figures cover the headline's timed launches
+# alone -- the all-dense packed reference runs the same kernels
+HYBRID_ONLY = False
 KERNEL_SOURCES = ("sparse_gemm_amd/csrc/gemm_decode.hip", "sparse_gemm_amd/csrc/gemm_prefill.hip",
-                  "sparse_gemm_amd/csrc/device_common.h")
+                  "sparse_gemm_amd/csrc/prefill_common.h", "sparse_gemm_amd/csrc/device_common.h")
 
 
 def kernel_sha() -> str:
@@ -256,10 +261,11 @@ def gemm_set(cfg_name, mi, si, Ms, steps, warmup, with_hipblaslt=True, fraction=
     W = dev_bits(p.w, tdt)
     mask = torch.from_numpy(p.mask).cuda()
     pw, pack_ms = pack_timed(W, p.tile_map, mask)
-    p0 = patch.pack(W, np.zeros_like(p.tile_map), mask)  # the same weights, every tile dense
+    refs = not HYBRID_ONLY
+    p0 = patch.pack(W, np.zeros_like(p.tile_map), mask) if refs else None  # the same weights, every tile dense
     del mask
     blobs = rotate(pw.blob, pw.nbytes)
-    blobs0 = rotate(p0.blob, p0.nbytes)
+    blobs0 = rotate(p0.blob, p0.nbytes) if refs else None
     Ws = rotate(W, W.numel() * 2)
     Xs = {M: dev_bits(inputs.make_x(cfg, M, p.K, matrix_index=mi), tdt) for M in Ms}
     Ys = {M: torch.empty((M, p.N), dtype=tdt, device="cuda") for M in Ms}
@@ -291,11 +297,12 @@ def gemm_set(cfg_name, mi, si, Ms, steps, warmup, with_hipblaslt=True, fraction=
     # since a library call may record work that graph replays do not repeat
     # faithfully
     ms_h, per_h = time_graphs([(M, hyb(M)) for M in Ms], steps, warmup, batches)
-    ms_0, per_0 = time_graphs([(M, hyb0(M)) for M in Ms], steps, warmup, batches)
-    ms_d, per_d = time_graphs([(M, dense(M)) for M in Ms], steps, warmup, batches)
+    ms_0 = per_0 = ms_d = per_d = per_b = None
+    if refs:
+        ms_0, per_0 = time_graphs([(M, hyb0(M)) for M in Ms], steps, warmup, batches)
+        ms_d, per_d = time_graphs([(M, dense(M)) for M in Ms], steps, warmup, batches)
     ms_he, per_he = time_launches([(M, hyb(M)) for M in Ms], steps, warmup, batches)
-    per_b = None
-    if with_hipblaslt:
+    if with_hipblaslt and refs:
         _, per_b = time_launches([(M, blas(M)) for M in Ms], steps, warmup, batches)
     res = dict(p=p, pw=pw, pack_ms=pack_ms, ms_step=ms_h, ms_step_dense=ms_0, per=per_h, per_dense=per_0,
                ms_step_rowmajor=ms_d, per_rowmajor=per_d, ms_step_eager=ms_he, per_eager=per_he, per_blas=per_b,
@@ -321,14 +328,17 @@ def summarize(res, Ms):
     out = {}
     for M in Ms:
         t = median(res["per"][M]) * 1e-3
-        td = median(res["per_dense"][M]) * 1e-3  # the same weights packed all-dense, same kernels
-        tr = median(res["per_rowmajor"][M]) * 1e-3  # patch_dense_gemm on row-major W
         fl = 2.0 * M * N * K
         eff = 2.0 * M * N * K * (1 - 0.5 * s)
         e = dict(us=t * 1e6, us_min=min(res["per"][M]) * 1e3, us_max=max(res["per"][M]) * 1e3,
-                 batches=len(res["per"][M]), us_eager=median(res["per_eager"][M]) * 1e3, dense_us=td * 1e6, tflops_dense_equiv=fl / t / 1e12, tflops_effective=eff / t / 1e12,
-                 gbps=algo_bytes(N, K, M, ns) / t / 1e9, speedup_vs_dense=td / t, rowmajor_dense_us=tr * 1e6,
-                 speedup_vs_rowmajor_dense=tr / t)
+                 batches=len(res["per"][M]), us_eager=median(res["per_eager"][M]) * 1e3,
+                 tflops_dense_equiv=fl / t / 1e12, tflops_effective=eff / t / 1e12,
+                 gbps=algo_bytes(N, K, M, ns) / t / 1e9)
+        if res["per_dense"] is not None:
+            td = median(res["per_dense"][M]) * 1e-3  # the same weights packed all-dense, same kernels
+            tr = median(res["per_rowmajor"][M]) * 1e-3  # patch_dense_gemm on row-major W
+            e.update(dense_us=td * 1e6, speedup_vs_dense=td / t, rowmajor_dense_us=tr * 1e6,
+                     speedup_vs_rowmajor_dense=tr / t)
         if res["per_blas"] is not None:
             # eager against eager: both include the host's launch cost
             tb = median(res["per_blas"][M]) * 1e-3
@@ -515,11 +525,14 @@ def headline_prefill(args):
         W = dev_bits(p.w, torch.bfloat16)
         mk = torch.from_numpy(p.mask).cuda()
         pw, pack_ms = pack_timed(W, p.tile_map, mk)
-        p0 = patch.pack(W, np.zeros_like(p.tile_map), mk)  # the same weights with every tile dense
+        # the same weights with every tile dense
+        p0 = patch.pack(W, np.zeros_like(p.tile_map), mk) if not HYBRID_ONLY else None
         del mk
         X = dev_bits(inputs.make_x(cfg, M, p.K, matrix_index=mi), torch.bfloat16)
+        refs = p0 is not None
         mats.append(dict(name=cfg.matrices[mi].name, p=p, pw=pw, pack_ms=pack_ms, blobs=rotate(pw.blob, pw.nbytes),
-                         blobs0=rotate(p0.blob, p0.nbytes), desc0=p0.desc, Ws=rotate(W, W.numel() * 2), X=X,
+                         blobs0=rotate(p0.blob, p0.nbytes) if refs else None, desc0=p0.desc if refs else None,
+                         Ws=rotate(W, W.numel() * 2) if refs else None, X=X,
                          Y=torch.empty((M, p.N), dtype=torch.bfloat16, device="cuda")))
         del p0, W
 
@@ -539,10 +552,21 @@ def headline_prefill(args):
 
     steps, warmup = args.steps, args.warmup
     ms_step, per = time_steps_events([(m["name"], hyb(m)) for m in mats], steps, warmup)
-    ms_step_graph, _ = time_graphs([(m["name"], hyb(m)) for m in mats], steps, warmup)
-    ms_dense, per_dense = time_steps_events([(m["name"], dense(m)) for m in mats], steps, warmup)
-    ms_s0, per_s0 = time_steps_events([(m["name"], hyb0(m)) for m in mats], steps, warmup)
-    ms_blas, per_blas = time_steps_events([(m["name"], blas(m)) for m in mats], steps, warmup)
+    ms_step_graph = None
+    if not HYBRID_ONLY:
+        ms_step_graph, _ = time_graphs([(m["name"], hyb(m)) for m in mats], steps, warmup)
+    refs = not HYBRID_ONLY
+    ms_dense = per_dense = ms_s0 = per_s0 = ms_blas = per_blas = None
+    if refs:
+        ms_dense, per_dense = time_steps_events([(m["name"], dense(m)) for m in mats], steps, warmup)
+        ms_s0, per_s0 = time_steps_events([(m["name"], hyb0(m)) for m in mats], steps, warmup)
+        ms_blas, per_blas = time_steps_events([(m["name"], blas(m)) for m in mats], steps, warmup)
+
+    def ref_us(per_ref, name):
+        return mean(per_ref[name]) * 1e3 if refs else None
+
+    def ref_speedup(per_ref, name, t):
+        return mean(per_ref[name]) * 1e-3 / t if refs else None
 
     flops_step = sum(2.0 * M * m["p"].N * m["p"].K for m in mats)
     per_matrix = {}
@@ -556,11 +580,12 @@ def headline_prefill(args):
             N=p.N, K=p.K, M=M, sparse_tiles=ns, tiles=T, us=t * 1e6, us_min=min(per[m["name"]]) * 1e3,
             us_max=max(per[m["name"]]) * 1e3, tflops_dense_equiv=2.0 * M * p.N * p.K / t / 1e12,
             tflops_effective=eff_flops(M, T, ns) / t / 1e12, roofline_us=tm * 1e6, roofline_frac=tm / t,
-            dense_us=mean(per_s0[m["name"]]) * 1e3, rowmajor_dense_us=mean(per_dense[m["name"]]) * 1e3,
-            hipblaslt_us=mean(per_blas[m["name"]]) * 1e3,
-            speedup_vs_dense=mean(per_s0[m["name"]]) * 1e-3 / t,
-            speedup_vs_rowmajor_dense=mean(per_dense[m["name"]]) * 1e-3 / t,
-            speedup_vs_hipblaslt=mean(per_blas[m["name"]]) * 1e-3 / t,
+            dense_us=ref_us(per_s0, m["name"]),
+            rowmajor_dense_us=ref_us(per_dense, m["name"]),
+            hipblaslt_us=ref_us(per_blas, m["name"]),
+            speedup_vs_dense=ref_speedup(per_s0, m["name"], t),
+            speedup_vs_rowmajor_dense=ref_speedup(per_dense, m["name"], t),
+            speedup_vs_hipblaslt=ref_speedup(per_blas, m["name"], t),
             pack_us=m["pack_ms"] * 1e3, pack_gbps=(3 * p.N * p.K + m["pw"].nbytes) / (m["pack_ms"] * 1e-3) / 1e9,
             weight_copies_rotated=len(m["blobs"]))
         eff_sum += eff_flops(M, T, ns) * len(per[m["name"]])
@@ -597,9 +622,9 @@ def headline_prefill(args):
                            "dense, run by the same kernels (the sparsity gain alone); speedup_vs_rowmajor_dense: "
                            "patch_dense_gemm on row-major W; speedup_vs_hipblaslt: torch.matmul (hipBLASLt)",
         "ms_per_step_graph": ms_step_graph,
-        "speedup_vs_dense_step": ms_s0 / ms_step,
-        "speedup_vs_rowmajor_dense_step": ms_dense / ms_step,
-        "speedup_vs_hipblaslt_step": ms_blas / ms_step,
+        "speedup_vs_dense_step": ms_s0 / ms_step if refs else None,
+        "speedup_vs_rowmajor_dense_step": ms_dense / ms_step if refs else None,
+        "speedup_vs_hipblaslt_step": ms_blas / ms_step if refs else None,
         "per_matrix": per_matrix,
         "roofline": {
             "kernel": "prefill hybrid GEMM (packed W), both matrices' launches",
@@ -642,8 +667,9 @@ def decode_extra(args):
         "ms_per_step": res["ms_step"],
         "tflops_dense_equiv_step": sum(2.0 * M * p.N * p.K for M in Ms) / (res["ms_step"] * 1e-3) / 1e12,
         "sum_of_per_M_launches_ms": t_sum * 1e3,
-        "speedup_vs_dense_step": res["ms_step_dense"] / res["ms_step"],
-        "speedup_vs_rowmajor_dense_step": res["ms_step_rowmajor"] / res["ms_step"],
+        "speedup_vs_dense_step": res["ms_step_dense"] / res["ms_step"] if res["ms_step_dense"] else None,
+        "speedup_vs_rowmajor_dense_step": (res["ms_step_rowmajor"] / res["ms_step"] if res["ms_step_rowmajor"]
+                                           else None),
         "per_M": {str(M): summ[M] for M in Ms},
         "roofline": {"kernel": "decode hybrid GEMM", "bound": "hbm", "achieved": b_sum / t_sum / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": b_sum / t_sum / 1e9 / HBM_PEAK_GBS,
@@ -722,12 +748,17 @@ def main():
                     choices=["prefill_mlp", "decode", "imbalanced_13b", "sampler", "fine_mask", "n48"],
                     help="prefill_mlp (default: the headline line); the others print that workload's lines, "
                          "for profiling")
+    ap.add_argument("--hybrid-only", action="store_true",
+                    help="time the hybrid launches alone, no reference GEMMs (for profiler and counter runs, whose "
+                         "per-kernel figures then cover the hybrid launches alone)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for rocprofv3 byte counters)")
     ap.add_argument("--ingest-counters", nargs="+", metavar="DIR", default=None,
                     help="FETCH_DIR WRITE_DIR [FETCH_DIR WRITE_DIR ...]: write profiles/traffic_counters.json from "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE runs and exit")
     args = ap.parse_args()
+    global HYBRID_ONLY
+    HYBRID_ONLY = args.hybrid_only
     if args.ingest_counters:
         ingest_counters(args.ingest_counters)
         return

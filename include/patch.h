@@ -87,17 +87,18 @@ typedef enum {
 
 /* Host-side mirror of the packed blob's header (format version 3). */
 typedef struct {
-  uint32_t version;   /* 3 */
+  uint32_t version;   /* 3 (128 x 128 execution tiles) or 4 (64 x 64, patch_pack_q64) */
   uint32_t dtype;     /* PATCH_F16 or PATCH_BF16 */
-  uint32_t tile_n;    /* 128 */
-  uint32_t tile_k;    /* 128 */
+  uint32_t tile_n;    /* 128 (version 4: 64) */
+  uint32_t tile_k;    /* 128 (version 4: 64) */
   uint32_t N, K;      /* matrix shape */
-  uint32_t nt_n;      /* N / 128 */
-  uint32_t nt_k;      /* K / 128 */
-  uint32_t n_sparse;  /* number of compressed (2:4 and 4:8) tiles */
-  uint32_t n_48;      /* number of 4:8 tiles among them (header byte 72) */
+  uint32_t nt_n;      /* N / tile_n */
+  uint32_t nt_k;      /* K / tile_k */
+  uint32_t n_sparse;  /* number of compressed tiles (2:4 and 4:8; version 4: 2:4 quadrants) */
+  uint32_t n_48;      /* number of 4:8 tiles among them (header byte 72; version 4: 0) */
   uint64_t table_offset; /* 256 */
-  uint64_t data_offset;  /* round_up(256 + 16 * nt_n * nt_k, 256) */
+  uint64_t data_offset;  /* round_up(256 + 16 * entries, 256); entries = nt_n * nt_k
+                            (version 4: (N / 64) * (K / 128)) */
   uint64_t total_bytes;  /* size of the whole blob */
 } patch_packed_desc;
 
@@ -159,6 +160,42 @@ uint64_t patch_packed_bytes(patch_dtype dtype, int64_t N, int64_t K, const uint8
 patch_status patch_pack(patch_dtype dtype, int64_t N, int64_t K, const void* W_dev, const uint8_t* tile_map_host,
                         const uint8_t* mask_dev, void* packed_dev, uint64_t packed_bytes,
                         patch_packed_desc* desc_out, void* stream);
+
+/*
+ * 64 x 64 execution tiles (format version 4).  The explainer's section 4
+ * "Ablation Studies" ("Tile Size") finds the method robust across tile
+ * sizes, smaller tiles giving finer control, while execution wants larger
+ * tiles.  Here every 64 x 64 quadrant of a 128 x 128 tile is dense or 2:4 on
+ * its own, so a mask chosen on 64 x 64 tiles runs as it is (where the
+ * 128 x 128 policy, patch_exec_tile_map, runs a tile as 2:4 only if all its
+ * quadrants are).  Dense and 2:4 only (no 4:8); N and K multiples of 128.
+ *
+ *   quad_map_host  (N/64) x (K/64) bytes on the host, quadrant (R, C) --
+ *                  rows 64R.., columns 64C.. -- at R*(K/64) + C: 0 dense,
+ *                  1 2:4 (other values: PATCH_ERR_INVALID_ARG).
+ *
+ * Layout: a table entry per 64-row half-row-block r and 128-column tile
+ * column j (at r*(K/128) + j): u64 offset of its band-0 piece, u32 kind bits
+ * k (bit q set: the 64-column slice q, quadrant (r, 2j + q), is 2:4), u32
+ * the half-row-block's band stride.  A piece (16 rows) holds slice 0 then
+ * slice 1 -- 2048 bytes dense (version 3's dense blocks), 1024 bytes 2:4
+ * (version 3's value block) -- then, if k != 0, a 256-byte codes block (lane
+ * l's u32 at 4l, slice q's codes in bits 16q..16q+15): 4096, 3328 or 2304
+ * bytes.  Size: round_up(256 + 16 * entries, 256) + 8192 per dense quadrant
+ * + 4096 per 2:4 quadrant + 1024 per entry with k != 0.
+ *
+ * patch_packed_bytes_q64 returns that size (0 for invalid arguments);
+ * patch_pack_q64 takes W and the mask as patch_pack does (the mask read only
+ * inside 2:4 quadrants), synchronises `stream`, and reports PATCH_ERR_MASK
+ * for a 2:4-quadrant group not keeping two of four.  patch_gemm,
+ * patch_gemm_ex (AUTO, DECODE, PREFILL and the LDS-staged PREFILL_W*_LDS
+ * variants; the others return PATCH_ERR_UNSUPPORTED) and
+ * patch_gemm_noalloc run such a blob; the fused gate/up product does not.
+ */
+uint64_t patch_packed_bytes_q64(patch_dtype dtype, int64_t N, int64_t K, const uint8_t* quad_map_host);
+patch_status patch_pack_q64(patch_dtype dtype, int64_t N, int64_t K, const void* W_dev,
+                            const uint8_t* quad_map_host, const uint8_t* mask_dev, void* packed_dev,
+                            uint64_t packed_bytes, patch_packed_desc* desc_out, void* stream);
 
 /* Parse a blob header already copied to the host (for reloading a saved blob).
  * header_bytes must be at least 76 (the descriptor's fields end with n_48 at

@@ -53,7 +53,13 @@ struct DecodeFrag {
 // stored) get zeros from the range check, with no memory access, no
 // predication (which would make the compiler wait for the load at once) and
 // no hot spot on row 0 when M is 1.
-template <bool SRC_ROWMAJOR, int MB>
+// Q64 (64 x 64 execution tiles, format 4): `b` is the band within the
+// entry's 64-row half and `kind` the entry's kind bits (bit q: 64-column
+// slice q is 2:4); the piece holds slice 0, then slice 1 (2048 bytes dense,
+// 1024 bytes 2:4), then the codes block if either slice is 2:4.  Slot
+// registers: a[2q] = slice q's first fragment, a[2q + 1] = its second dense
+// half, or, for a 2:4 slice, the codes chunk holding the lane's word.
+template <bool SRC_ROWMAJOR, int MB, bool Q64 = false>
 __device__ __forceinline__ void decode_load(DecodeFrag<MB>& f, const uint8_t* __restrict__ src, uint64_t off,
                                             uint32_t kind, uint32_t stride, __amdgpu_buffer_rsrc_t xr, int K,
                                             int i, int b, int j, int l) {
@@ -66,6 +72,15 @@ __device__ __forceinline__ void decode_load(DecodeFrag<MB>& f, const uint8_t* __
 #pragma unroll
     for (int c = 0; c < 4; c++) ap[c] = wr + 64 * c;
     f.kind = 0;
+  } else if constexpr (Q64) {
+    const uint8_t* pb = src + off + (uint64_t)b * stride;
+    const uint32_t a1 = (kind & 1u) ? 1024u : 2048u;
+    const uint8_t* mp = pb + a1 + ((kind & 2u) ? 1024u : 2048u) + 16 * (l >> 2);
+    ap[0] = pb + 16 * l;
+    ap[1] = (kind & 1u) ? mp : pb + 1024 + 16 * l;
+    ap[2] = pb + a1 + 16 * l;
+    ap[3] = (kind & 2u) ? mp : pb + a1 + 1024 + 16 * l;
+    f.kind = kind;
   } else {
     // band b's piece of the tile: dense = blocks (slice 0, half 0/1), (slice
     // 1, half 0/1); 2:4 = value blocks of slices 0 and 1, then the codes
@@ -90,9 +105,32 @@ __device__ __forceinline__ void decode_load(DecodeFrag<MB>& f, const uint8_t* __
 
 // N48: the blob holds 4:8 tiles (their rebuild lives only in this
 // instantiation: it costs the other kinds registers and occupancy).
-template <bool BF16, bool SRC_ROWMAJOR, int MB, bool N48>
+template <bool BF16, bool SRC_ROWMAJOR, int MB, bool N48, bool Q64 = false>
 __device__ __forceinline__ void decode_mma(DecodeFrag<MB>& f, f32x4 (&acc)[MB], int l, const u32x4* sel) {
-  if constexpr (SRC_ROWMAJOR) {
+  if constexpr (Q64) {
+    // each 64-column slice on its own kind (f.kind is wave-uniform)
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      if ((f.kind >> q) & 1u) {
+        const u32x4 mc = f.a[2 * q + 1];
+        const uint32_t lo = (l & 1) ? mc[1] : mc[0], hi = (l & 1) ? mc[3] : mc[2];
+        const uint32_t meta = (l & 2) ? hi : lo;
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++) {
+          if (q == 0)
+            acc[mb] = mma_sparse<BF16, 0>(f.a[0], f.x[mb][0], f.x[mb][1], acc[mb], meta);
+          else
+            acc[mb] = mma_sparse<BF16, 1>(f.a[2], f.x[mb][2], f.x[mb][3], acc[mb], meta);
+        }
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++) {
+          acc[mb] = mma_sparse<BF16, 0>(f.a[2 * q], f.x[mb][2 * q], f.x[mb][2 * q + 1], acc[mb], 0x4444u);
+          acc[mb] = mma_sparse<BF16, 0>(f.a[2 * q + 1], f.x[mb][2 * q], f.x[mb][2 * q + 1], acc[mb], 0xEEEEu);
+        }
+      }
+    }
+  } else if constexpr (SRC_ROWMAJOR) {
 #pragma unroll
     for (int mb = 0; mb < MB; mb++)
 #pragma unroll
@@ -146,7 +184,10 @@ __device__ __forceinline__ void decode_mma(DecodeFrag<MB>& f, f32x4 (&acc)[MB], 
 // of both row-blocks of pair q with twice the waves (the first WAVES on gate,
 // the others on up) and writes H[m][128 q + ...] = SiLU(gate) * up, H being
 // M x N/2.
-template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, int WAVES, int DEPTH, bool XCD_MAP, int MB, bool FUSE, bool N48>
+// Q64: a blob of 64 x 64 execution tiles (format 4; not fused): band b of
+// row-block i reads the entries of half-row-block 2i + b/4, band b mod 4.
+template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, int WAVES, int DEPTH, bool XCD_MAP, int MB, bool FUSE, bool N48,
+          bool Q64 = false>
 __global__ __launch_bounds__(WAVES * 64 * (FUSE ? 2 : 1)) void k_decode(const uint8_t* __restrict__ src,
                                                                          const uint8_t* __restrict__ src2,
                                                                          const uint16_t* __restrict__ X, int M, int N,
@@ -170,7 +211,10 @@ __global__ __launch_bounds__(WAVES * 64 * (FUSE ? 2 : 1)) void k_decode(const ui
   const int w = wa - g * WAVES;         // wave within its row-block
   const int l = threadIdx.x & 63;
   const int i = FUSE ? 2 * q + g : q;   // row-block of the (interleaved) matrix
-  const TileEntry* table = reinterpret_cast<const TileEntry*>(src + kHeaderBytes) + (int64_t)i * KT;
+  static_assert(!Q64 || (!SRC_ROWMAJOR && !FUSE && !N48), "64 x 64 execution tiles: packed W, not fused");
+  const TileEntry* table =
+      reinterpret_cast<const TileEntry*>(src + kHeaderBytes) + (int64_t)(Q64 ? 2 * i + (b >> 2) : i) * KT;
+  const int bp = Q64 ? (b & 3) : b;  // the band's index inside its entries' pieces
   // row-major W: the matrix and row-block this wave reads
   const uint8_t* wsrc = SRC_ROWMAJOR && FUSE && g ? src2 : src;
   const int wi = SRC_ROWMAJOR && FUSE ? q : i;
@@ -217,8 +261,8 @@ __global__ __launch_bounds__(WAVES * 64 * (FUSE ? 2 : 1)) void k_decode(const ui
       uint64_t off;
       uint32_t kind, stride;
       entry(t, off, kind, stride);
-      decode_load<SRC_ROWMAJOR, MB>(f[s], SRC_ROWMAJOR ? wsrc : src, off, kind, stride, xr, K, wi, b,
-                                    w + kDecodeWaves * t, l);
+      decode_load<SRC_ROWMAJOR, MB, Q64>(f[s], SRC_ROWMAJOR ? wsrc : src, off, kind, stride, xr, K, wi, bp,
+                                         w + kDecodeWaves * t, l);
     }
     // steady state: compute the DEPTH slots, refilling each with the tile
     // DEPTH further on (clamped to the last tile: a redundant, cached load)
@@ -226,19 +270,19 @@ __global__ __launch_bounds__(WAVES * 64 * (FUSE ? 2 : 1)) void k_decode(const ui
     for (; t0 + DEPTH < n_mine; t0 += DEPTH) {
 #pragma unroll
       for (int s = 0; s < DEPTH; s++) {
-        decode_mma<BF16, SRC_ROWMAJOR, MB, N48>(f[s], acc, l, s_sel);
+        decode_mma<BF16, SRC_ROWMAJOR, MB, N48, Q64>(f[s], acc, l, s_sel);
         const int tn = min(t0 + s + DEPTH, n_mine - 1);
         uint64_t off;
         uint32_t kind, stride;
         entry(tn, off, kind, stride);
-        decode_load<SRC_ROWMAJOR, MB>(f[s], SRC_ROWMAJOR ? wsrc : src, off, kind, stride, xr, K, wi, b,
-                                      w + kDecodeWaves * tn, l);
+        decode_load<SRC_ROWMAJOR, MB, Q64>(f[s], SRC_ROWMAJOR ? wsrc : src, off, kind, stride, xr, K, wi, bp,
+                                           w + kDecodeWaves * tn, l);
       }
     }
     // last round: no refills
 #pragma unroll
     for (int s = 0; s < DEPTH; s++)
-      if (t0 + s < n_mine) decode_mma<BF16, SRC_ROWMAJOR, MB, N48>(f[s], acc, l, s_sel);
+      if (t0 + s < n_mine) decode_mma<BF16, SRC_ROWMAJOR, MB, N48, Q64>(f[s], acc, l, s_sel);
   }
 
   // ---- fixed-order reduction over waves (wave wa adds up M blocks wa,
@@ -266,18 +310,19 @@ __global__ __launch_bounds__(WAVES * 64 * (FUSE ? 2 : 1)) void k_decode(const ui
   }
 }
 
-template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE, bool N48, int WAVES, int DEPTH, bool XCD_MAP, int MB>
+template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE, bool N48, int WAVES, int DEPTH, bool XCD_MAP, int MB,
+          bool Q64>
 static hipError_t launch_decode_v(const void* src, const void* src2, const void* X, int64_t M, int64_t N, int64_t K,
                                   void* Y, hipStream_t s) {
   const unsigned grid = (unsigned)(FUSE ? N / 32 : N / 16);
-  hipLaunchKernelGGL((k_decode<BF16, SRC_ROWMAJOR, OUT_F32, WAVES, DEPTH, XCD_MAP, MB, FUSE, N48>), dim3(grid),
+  hipLaunchKernelGGL((k_decode<BF16, SRC_ROWMAJOR, OUT_F32, WAVES, DEPTH, XCD_MAP, MB, FUSE, N48, Q64>), dim3(grid),
                      dim3(WAVES * 64 * (FUSE ? 2 : 1)), 0, s, reinterpret_cast<const uint8_t*>(src),
                      reinterpret_cast<const uint8_t*>(src2), reinterpret_cast<const uint16_t*>(X), (int)M, (int)N,
                      (int)K, Y);
   return hipGetLastError();
 }
 
-template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE, bool N48>
+template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE, bool N48, bool Q64 = false>
 static hipError_t launch_decode_t(const void* src, const void* src2, const void* X, int64_t M, int64_t N, int64_t K,
                                   void* Y, hipStream_t s) {
   // Few waves a workgroup, several tiles in flight a wave: small workgroups
@@ -288,7 +333,7 @@ static hipError_t launch_decode_t(const void* src, const void* src2, const void*
   // (Fused gate/up: twice the waves, one set per matrix.)
   const int64_t KT = K / kTile;
 #define PATCH_DV(W, D, MBK) \
-  launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, FUSE, N48, W, D, true, MBK>(src, src2, X, M, N, K, Y, s)
+  launch_decode_v<BF16, SRC_ROWMAJOR, OUT_F32, FUSE, N48, W, D, true, MBK, Q64>(src, src2, X, M, N, K, Y, s)
   if (M <= 16) {
     // Wide matrices, whose bands cover every CU at least twice: one wave a
     // band (gate_proj of LLaMA-2 7B, 11008 x 4096: 1-6% faster than two
@@ -326,11 +371,20 @@ double decode_estimate_us(int64_t M, int64_t N, int64_t K, double w_bytes) {
 }
 
 // src2 non-null: fused gate/up (see k_decode); Y is then H, M x N/2.
-// n48: the packed blob holds 4:8 tiles.
+// n48: the packed blob holds 4:8 tiles; q64: it is a blob of 64 x 64
+// execution tiles (format 4; packed, not fused).
 hipError_t launch_decode(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* src2, const void* X,
-                         int64_t M, int64_t N, int64_t K, void* Y, bool n48, hipStream_t s) {
+                         int64_t M, int64_t N, int64_t K, void* Y, bool n48, bool q64, hipStream_t s) {
   const bool fuse = src2 != nullptr;
   if (fuse && (N % (2 * kTile))) return hipErrorInvalidValue;
+  if (q64) {
+    if (rowmajor || fuse || n48) return hipErrorInvalidValue;
+    if (bf16)
+      return out_f32 ? launch_decode_t<true, false, true, false, false, true>(src, src2, X, M, N, K, Y, s)
+                     : launch_decode_t<true, false, false, false, false, true>(src, src2, X, M, N, K, Y, s);
+    return out_f32 ? launch_decode_t<false, false, true, false, false, true>(src, src2, X, M, N, K, Y, s)
+                   : launch_decode_t<false, false, false, false, false, true>(src, src2, X, M, N, K, Y, s);
+  }
 #define PATCH_D(B, R, F, U, Q) launch_decode_t<B, R, F, U, Q>(src, src2, X, M, N, K, Y, s)
 #define PATCH_D2(B, R, F) (fuse ? PATCH_D(B, R, F, true, false) : PATCH_D(B, R, F, false, false))
 #define PATCH_D48(B, F) (fuse ? PATCH_D(B, false, F, true, true) : PATCH_D(B, false, F, false, true))

@@ -440,8 +440,17 @@ constexpr int kLdsWStage = 32768;  // 2 row-blocks x 8 bands x 2 fragments of 1 
 // and 256 (a third would not fit the 160 KB of LDS)
 constexpr int lds_stages(int bm) { return bm <= 128 ? 3 : 2; }
 
-template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE, int BM>
+// Q64: a blob of 64 x 64 execution tiles (format 4).  Its table has one
+// entry per 64-row half of a row-block and 128-column tile column, whose
+// kind bits give each 64-column slice's kind (bit q set: slice q is 2:4) and
+// whose pieces hold the slices back to back (a dense slice 2048 bytes, a 2:4
+// one 1024) and then, if either is 2:4, the 256-byte codes block.  A wave
+// (r, wn, wm) works on half wn of row-block r, so it reads that half's
+// entries and, per step (one slice), that slice's kind: the waves of one
+// workgroup may run different kinds in the same step.
+template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE, int BM, bool Q64 = false>
 __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
+  static_assert(!Q64 || (!SRC_ROWMAJOR && !FUSE), "64 x 64 execution tiles: packed W, not fused");
   constexpr int kNMB = BM / 32;                     // 16-column M blocks per wave
   constexpr int kLdsStages = lds_stages(BM);
   constexpr int kLdsXStage = BM * kPfRowBytes;       // X rows of one step
@@ -453,9 +462,10 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   static_assert(kXC * 1024 * kPfWaves == kLdsXStage, "X stage split");
   __shared__ __attribute__((aligned(1024))) uint8_t s_w[kLdsStages * kLdsWStage];
   __shared__ __attribute__((aligned(1024))) uint8_t s_x[kLdsStages * kLdsXStage];
-  __shared__ uint32_t s_ent[2][kPfMaxKT];
-  __shared__ uint32_t s_stride[2];
-  __shared__ u32x4 s_sel[SRC_ROWMAJOR ? 1 : 256];  // 4:8 rebuild selectors
+  constexpr int kEntRows = Q64 ? 4 : 2;  // row-blocks (Q64: their 64-row halves) of a workgroup
+  __shared__ uint32_t s_ent[kEntRows][kPfMaxKT];
+  __shared__ uint32_t s_stride[Q64 ? 1 : 2];  // (Q64: each wave reads its own from the table)
+  __shared__ u32x4 s_sel[SRC_ROWMAJOR || Q64 ? 1 : 256];  // 4:8 rebuild selectors
 
   const int t = (blockIdx.x & 7) * P.per_xcd + (blockIdx.x >> 3);
   if (t >= P.n_blocks) return;  // whole workgroup
@@ -483,7 +493,17 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   const int nt = min(P.kt_split, KT - j0);
   const int n_steps = 2 * nt;
 
-  if constexpr (!SRC_ROWMAJOR) {
+  if constexpr (Q64) {
+    // entry rows 2 rr + hh: half hh of row-block i0 (rr = 0) or i1 (rr = 1)
+    const TileEntry* table = reinterpret_cast<const TileEntry*>(P.src + kHeaderBytes);
+    for (int e = threadIdx.x; e < 4 * nt; e += kPfWaves * 64) {
+      const int rh = e / nt;
+      const int j = e - rh * nt;
+      const TileEntry te = table[(int64_t)(2 * ((rh >> 1) ? i1 : i0) + (rh & 1)) * KT + j0 + j];
+      s_ent[rh][j] = (uint32_t)(te.offset >> 8) | (te.kind << 30);
+    }
+    __syncthreads();
+  } else if constexpr (!SRC_ROWMAJOR) {
     const TileEntry* table = reinterpret_cast<const TileEntry*>(P.src + kHeaderBytes);
     for (int e = threadIdx.x; e < 2 * nt; e += kPfWaves * 64) {
       const int rr = e >= nt ? 1 : 0;
@@ -495,7 +515,13 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
     fill_sel48(s_sel, (int)threadIdx.x, kPfWaves * 64);
     __syncthreads();
   }
-  const uint32_t stride = SRC_ROWMAJOR ? 0u : (uint32_t)__builtin_amdgcn_readfirstlane((int)s_stride[r_src]);
+  const int er = Q64 ? 2 * r_src + wn : r_src;  // this wave's entry row
+  uint32_t stride = 0u;
+  if constexpr (Q64)
+    stride = (uint32_t)__builtin_amdgcn_readfirstlane((int)reinterpret_cast<const TileEntry*>(
+        P.src + kHeaderBytes)[(int64_t)(2 * (r_src ? i1 : i0) + wn) * KT + j0].band_stride);
+  else if constexpr (!SRC_ROWMAJOR)
+    stride = (uint32_t)__builtin_amdgcn_readfirstlane((int)s_stride[er]);
 
   // this wave's kXC 8-row chunks of each X stage: rows 8 (kXC w + u) + l/8,
   // the lane fetching the source chunk whose swizzled position is l % 8;
@@ -532,18 +558,29 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
       for (int b = 0; b < 4; b++) dma16(W + (int64_t)16 * b * K, slot0 + 2048u * b + 1024u * wm);
     } else {
       const uint32_t e = (uint32_t)__builtin_amdgcn_readfirstlane((int)e_v);
-      const uint8_t* piece = P.src + ((uint64_t)(e & 0x3fffffffu) << 8) + (uint64_t)(4 * wn) * stride;
-      if ((e >> 30) == 0) {
+      // the slice's kind, where its part starts in the band piece, where the codes are
+      uint32_t sparse, part, codes;
+      if constexpr (Q64) {
+        const uint32_t kb = e >> 30, a1 = (kb & 1u) ? 1024u : 2048u;
+        sparse = (kb >> h) & 1u;
+        part = h ? a1 : 0u;
+        codes = a1 + ((kb & 2u) ? 1024u : 2048u);
+      } else {
+        sparse = (e >> 30) != 0u;
+        part = sparse ? 1024u * h : 2048u * h;
+        codes = kSparseMetaOffset;
+      }
+      const uint8_t* piece = P.src + ((uint64_t)(e & 0x3fffffffu) << 8) + (Q64 ? 0 : (uint64_t)(4 * wn) * stride);
+      if (!sparse) {
 #pragma unroll
         for (int b = 0; b < 4; b++)
-          dma16(piece + (uint64_t)b * stride + 2048 * h + 1024 * wm + 16 * l, slot0 + 2048u * b + 1024u * wm);
+          dma16(piece + (uint64_t)b * stride + part + 1024 * wm + 16 * l, slot0 + 2048u * b + 1024u * wm);
       } else if (wm == 0) {
 #pragma unroll
-        for (int b = 0; b < 4; b++) dma16(piece + (uint64_t)b * stride + 1024 * h + 16 * l, slot0 + 2048u * b);
+        for (int b = 0; b < 4; b++) dma16(piece + (uint64_t)b * stride + part + 16 * l, slot0 + 2048u * b);
       } else {
 #pragma unroll
-        for (int b = 0; b < 4; b++)
-          dma4(piece + (uint64_t)b * stride + kSparseMetaOffset + 4 * l, slot0 + 2048u * b + 1024u);
+        for (int b = 0; b < 4; b++) dma4(piece + (uint64_t)b * stride + codes + 4 * l, slot0 + 2048u * b + 1024u);
       }
     }
   };
@@ -573,15 +610,20 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   };
   auto x_stage = [&](int s) { return s_x + (s % kLdsStages) * kLdsXStage; };
   // the tile kind of step s (0 for row-major W)
+  // (Q64: the kind of slice s & 1 of the entry's two)
+  auto kind_of = [&](uint32_t ent, int s) -> uint32_t {
+    if constexpr (Q64) return ((ent >> 30) >> (s & 1)) & 1u;
+    return ent >> 30;
+  };
   auto step_kind = [&](int s) -> uint32_t {
     if constexpr (SRC_ROWMAJOR) return 0u;
-    return (uint32_t)__builtin_amdgcn_readfirstlane((int)s_ent[r_src][s >> 1]) >> 30;
+    return kind_of((uint32_t)__builtin_amdgcn_readfirstlane((int)s_ent[er][s >> 1]), s);
   };
   // this wave's tile entry of step s as a VGPR (an LDS load nobody waits
   // for until the value is used)
   auto ent_v = [&](int s) -> uint32_t {
     if constexpr (SRC_ROWMAJOR) return 0u;
-    return s_ent[r_src][min(s, n_steps - 1) >> 1];
+    return s_ent[er][min(s, n_steps - 1) >> 1];
   };
   // this wave's A fragments of step s (tile kind `kind`) from its stage
   auto read_a = [&](int s, uint32_t kind, u32x4 (&a0)[4], u32x4 (&a1)[4]) {
@@ -623,7 +665,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
     // and that of the step whose copies this step issues, loaded now and
     // read after the step's barrier
     const uint32_t nk_v = ent_v(s + 1), ecopy_v = ent_v(s + 1 + kAhead);
-    if (kind == 2) {
+    if (!Q64 && kind == 2) {
       // 4:8: each band's sixteen columns rebuilt into a dense piece's two
       // halves (values in a0, the lane's masks in the codes chunk a1),
       // then run as a dense tile
@@ -648,7 +690,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
       const int cb = (g + par * kGroups) & 1, nb = (g + 1 + par * kGroups) & 1;
       const bool last = g + 1 == kGroups;
       if (last && s + 1 < n_steps) advance(s, ecopy_v);
-      if (last) nkind = (uint32_t)__builtin_amdgcn_readfirstlane((int)nk_v) >> 30;
+      if (last) nkind = kind_of((uint32_t)__builtin_amdgcn_readfirstlane((int)nk_v), s + 1);
       __builtin_amdgcn_sched_barrier(0);
       // the first half (a 2:4 tile's only one) with the next group's reads
       // -- or, in the last group, step s + 1's first fragments -- spread
@@ -957,9 +999,10 @@ static hipError_t launch_big_t(const void* src, const void* src2, const void* X,
   return launch_split_reduce<BF16, OUT_F32, FUSE>(part, sh.splits, M, N, Y, s);
 }
 
-template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE, int BM, int DIST, bool LDS = false>
+template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE, int BM, int DIST, bool LDS = false, bool Q64 = false>
 static hipError_t launch_prefill_bm(const void* src, const void* src2, const void* X, int64_t M, int64_t N, int64_t K,
                                     void* Y, const PfShape& sh, float* part, hipStream_t s) {
+  static_assert(!Q64 || LDS, "64 x 64 execution tiles run on the LDS-staged kernel");
   PfArgs a;
   a.src = reinterpret_cast<const uint8_t*>(src);
   a.src2 = reinterpret_cast<const uint8_t*>(src2);
@@ -982,7 +1025,7 @@ static hipError_t launch_prefill_bm(const void* src, const void* src2, const voi
     // fp32 partials of the K ranges, then the ordered reduction (fused:
     // SiLU(gate) * up) into Y
     if constexpr (LDS)
-      hipLaunchKernelGGL((k_prefill_lds<BF16, SRC_ROWMAJOR, true, FUSE, BM>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((k_prefill_lds<BF16, SRC_ROWMAJOR, true, FUSE, BM, Q64>), grid, block, 0, s, a);
     else
       hipLaunchKernelGGL((k_prefill<BF16, SRC_ROWMAJOR, true, BM, DIST, FUSE>), grid, block, 0, s, a);
     if constexpr (FUSE) {
@@ -995,7 +1038,7 @@ static hipError_t launch_prefill_bm(const void* src, const void* src2, const voi
                          part, sh.splits, mn, Y);
     }
   } else if constexpr (LDS) {
-    hipLaunchKernelGGL((k_prefill_lds<BF16, SRC_ROWMAJOR, OUT_F32, FUSE, BM>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((k_prefill_lds<BF16, SRC_ROWMAJOR, OUT_F32, FUSE, BM, Q64>), grid, block, 0, s, a);
   } else {
     hipLaunchKernelGGL((k_prefill<BF16, SRC_ROWMAJOR, OUT_F32, BM, DIST, FUSE>), grid, block, 0, s, a);
   }
@@ -1118,14 +1161,43 @@ static hipError_t launch_prefill_t(const void* src, const void* src2, const void
 #undef PATCH_BM
 }
 
+// A blob of 64 x 64 execution tiles: the LDS-staged kernel at the width the
+// cost model picks (or force_bm), its per-half entries and per-slice kinds.
+template <bool BF16, bool OUT_F32>
+static hipError_t launch_prefill_q64_t(const void* src, const void* X, int64_t M, int64_t N, int64_t K, void* Y,
+                                       void* ws, uint64_t ws_bytes, int force_bm, hipStream_t s) {
+  const PfShape sh = shape_for(M, N, K, false, ws ? ws_bytes : 0u, force_bm, true, 0);
+  float* part = reinterpret_cast<float*>(ws);
+#define PATCH_BQ(W) launch_prefill_bm<BF16, false, OUT_F32, false, W, 1, true, true>(src, nullptr, X, M, N, K, Y, sh, part, s)
+  switch (sh.bm) {
+    case 64: return PATCH_BQ(64);
+    case 128: return PATCH_BQ(128);
+    case 192: return PATCH_BQ(192);
+    case 256: return PATCH_BQ(256);
+    default: return hipErrorInvalidValue;
+  }
+#undef PATCH_BQ
+}
+
 // force_bm: 0 (the shape the cost model picks) or a width in {64, 128, 192,
 // 256}; force_lds: LDS staging (any of those widths).  src2 non-null: fused
 // gate/up (src2 = the up matrix when rowmajor; for a packed blob the two are
-// interleaved in src and src2 is src); Y is then H, M x N/2.
+// interleaved in src and src2 is src); Y is then H, M x N/2.  q64: a blob of
+// 64 x 64 execution tiles (packed, not fused; LDS-staged kernel only).
 hipError_t launch_prefill(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* src2, const void* X,
                           int64_t M, int64_t N, int64_t K, void* Y, void* ws, uint64_t ws_bytes, int force_bm,
-                          bool force_lds, int force_big, hipStream_t s) {
+                          bool force_lds, int force_big, bool q64, hipStream_t s) {
   if (K / kTile > kPfMaxKT) return hipErrorInvalidValue;
+  if (q64) {
+    if (rowmajor || src2 || force_big) return hipErrorInvalidValue;
+    if (force_bm && force_bm != 64 && force_bm != 128 && force_bm != 192 && force_bm != 256)
+      return hipErrorInvalidValue;
+    if (bf16)
+      return out_f32 ? launch_prefill_q64_t<true, true>(src, X, M, N, K, Y, ws, ws_bytes, force_bm, s)
+                     : launch_prefill_q64_t<true, false>(src, X, M, N, K, Y, ws, ws_bytes, force_bm, s);
+    return out_f32 ? launch_prefill_q64_t<false, true>(src, X, M, N, K, Y, ws, ws_bytes, force_bm, s)
+                   : launch_prefill_q64_t<false, false>(src, X, M, N, K, Y, ws, ws_bytes, force_bm, s);
+  }
   if (force_bm && force_bm != 64 && force_bm != 128 && force_bm != 192 && force_bm != 256) return hipErrorInvalidValue;
   if (force_lds && force_bm < 64) return hipErrorInvalidValue;
   if (force_big && force_bm != 0 && force_bm < 128) return hipErrorInvalidValue;

@@ -1,4 +1,6 @@
-// pack.hip -- dense W + tile map + 2:4 / 4:8 mask -> packed blob (format version 3).
+// pack.hip -- dense W + tile map + 2:4 / 4:8 mask -> packed blob (format
+// version 3, 128 x 128 execution tiles); dense W + quadrant map + 2:4 mask ->
+// format version 4 (64 x 64 execution tiles, k_pack_q64 below).
 //
 // PATCH (arXiv 2509.23410), gist.science explainer, section 2 "Core
 // Mechanism": every 128 x 128 tile of W is dense or 2:4 sparse; section 1
@@ -153,6 +155,78 @@ __global__ __launch_bounds__(256) void k_pack(PackSources src, int K, int KT, ui
   }
   reinterpret_cast<uint32_t*>(piece + kSparseMetaOffset)[l] = meta;
   if (bad) atomicOr(reinterpret_cast<uint32_t*>(blob + kErrFlagOffset), 1u);
+}
+
+// Format 4 (64 x 64 execution tiles): grid = one workgroup of 256 threads
+// per table entry (a 64-row half-row-block r and a tile column j); thread
+// (band, l) writes lane l's share of band `band` (0..3) of the entry's
+// piece: each 64-column slice q in order -- dense: two 1 KB halves holding
+// positions (0,1) and (2,3) of each group of four (2048 bytes); 2:4: the kept
+// values (1024 bytes) -- then, if either slice is 2:4, the lane's codes word
+// (slice q's codes in bits 16q .. 16q+15) in the 256-byte block after them.
+__global__ __launch_bounds__(256) void k_pack_q64(const uint16_t* __restrict__ W, const uint8_t* __restrict__ mask,
+                                                  int K, int KC, uint8_t* __restrict__ blob) {
+  const int t = blockIdx.x;
+  const TileEntry e = reinterpret_cast<const TileEntry*>(blob + kHeaderBytes)[t];
+  const int r = t / KC, j = t - (t / KC) * KC;
+  const int band = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int64_t row = (int64_t)r * 64 + 16 * band + (l & 15);
+  uint8_t* piece = blob + e.offset + (uint64_t)band * e.band_stride;
+  const uint32_t a1 = (e.kind & 1u) ? 1024u : 2048u;
+  uint32_t meta = 0;
+  bool bad = false;
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    const int64_t col = (int64_t)j * kTile + 64 * q + 16 * (l >> 4);
+    const u32x4 w0 = ld16(W + row * K + col), w1 = ld16(W + row * K + col + 8);
+    uint8_t* part = piece + (q ? a1 : 0u);
+    if (!((e.kind >> q) & 1u)) {
+      const u32x4 h0 = {w0[0], w0[2], w1[0], w1[2]};
+      const u32x4 h1 = {w0[1], w0[3], w1[1], w1[3]};
+      st16(part + 16 * l, h0);
+      st16(part + 1024 + 16 * l, h1);
+      continue;
+    }
+    const u32x4 m4 = ld16(mask + row * K + col);
+    uint32_t outv[4];
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+      const uint32_t mword = m4[p];  // mask bytes of group p (4 columns)
+      const u32x4& wsrc = p < 2 ? w0 : w1;
+      const uint32_t wlo = wsrc[2 * (p & 1)], whi = wsrc[2 * (p & 1) + 1];  // positions 0,1 and 2,3
+      uint32_t kept[2] = {0u, 0u}, pos[2] = {0u, 0u};
+      int n = 0;
+#pragma unroll
+      for (int d = 0; d < 4; d++) {
+        if ((mword >> (8 * d)) & 0xffu) {
+          const uint32_t v = ((d < 2 ? wlo : whi) >> (16 * (d & 1))) & 0xffffu;
+          if (n < 2) {
+            kept[n] = v;
+            pos[n] = (uint32_t)d;
+          }
+          n++;
+        }
+      }
+      bad |= (n != 2);
+      outv[p] = kept[0] | (kept[1] << 16);
+      meta |= (pos[0] | (pos[1] << 2)) << (16 * q + 4 * p);
+    }
+    const u32x4 o = {outv[0], outv[1], outv[2], outv[3]};
+    st16(part + 16 * l, o);
+  }
+  if (e.kind) {
+    const uint32_t codes = a1 + ((e.kind & 2u) ? 1024u : 2048u);
+    reinterpret_cast<uint32_t*>(piece + codes)[l] = meta;
+  }
+  if (bad) atomicOr(reinterpret_cast<uint32_t*>(blob + kErrFlagOffset), 1u);
+}
+
+hipError_t launch_pack_q64(const void* W, const uint8_t* mask, int64_t N, int64_t K, uint8_t* blob, hipStream_t s) {
+  const int KC = (int)(K / kTile);
+  const int64_t E = (N / 64) * KC;
+  hipLaunchKernelGGL(k_pack_q64, dim3((unsigned)E), dim3(256), 0, s, reinterpret_cast<const uint16_t*>(W), mask,
+                     (int)K, KC, blob);
+  return hipGetLastError();
 }
 
 hipError_t launch_pack(const PackSources& src, int64_t N, int64_t K, uint8_t* blob, hipStream_t s) {

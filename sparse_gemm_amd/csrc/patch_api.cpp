@@ -2,6 +2,7 @@
 // argument validation, the packed header and tile table, kernel selection.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -14,11 +15,12 @@
 
 namespace patch {
 hipError_t launch_pack(const PackSources& src, int64_t N, int64_t K, uint8_t* blob, hipStream_t s);
+hipError_t launch_pack_q64(const void* W, const uint8_t* mask, int64_t N, int64_t K, uint8_t* blob, hipStream_t s);
 hipError_t launch_decode(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* src2, const void* X,
-                         int64_t M, int64_t N, int64_t K, void* Y, bool n48, hipStream_t s);
+                         int64_t M, int64_t N, int64_t K, void* Y, bool n48, bool q64, hipStream_t s);
 hipError_t launch_prefill(bool bf16, bool rowmajor, bool out_f32, const void* src, const void* src2, const void* X,
                           int64_t M, int64_t N, int64_t K, void* Y, void* ws, uint64_t ws_bytes, int force_bm,
-                          bool force_lds, int force_big, hipStream_t s);
+                          bool force_lds, int force_big, bool q64, hipStream_t s);
 uint64_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K, bool rowmajor);
 double prefill_estimate_us(int64_t M, int64_t N, int64_t K, bool rowmajor, uint64_t ws_bytes);
 double decode_estimate_us(int64_t M, int64_t N, int64_t K, double w_bytes);
@@ -35,7 +37,9 @@ uint64_t probe_mma_flops(int kind, int iters, int workgroups);
 namespace {
 
 constexpr uint32_t kMagic = 0x48435450u;  // "PTCH"
-constexpr uint32_t kVersion = 3;
+constexpr uint32_t kVersion = 3;     // 128 x 128 execution tiles
+constexpr uint32_t kVersionQ64 = 4;  // 64 x 64 execution tiles
+constexpr int64_t kQuad = 64;        // their edge
 constexpr int64_t kTile = 128;
 constexpr uint64_t kDenseBytes = 32768;
 constexpr uint64_t kSparseBytes = 18432;
@@ -101,8 +105,32 @@ patch_status check_ydtype(patch_dtype in, patch_dtype y) {
   return PATCH_OK;
 }
 
+// Format 4: bytes of one band piece of a table entry with kind bits kb
+// (bit q: 64-column slice q is 2:4), and of the whole blob for a quadrant map.
+uint64_t q64_piece(uint32_t kb) { return (kb & 1u ? 1024u : 2048u) + (kb & 2u ? 1024u : 2048u) + (kb ? 256u : 0u); }
+
+patch_status check_desc_q64(const patch_packed_desc* d) {
+  if (d->tile_n != kQuad || d->tile_k != kQuad) return fail(PATCH_ERR_INVALID_ARG, "descriptor version/tile mismatch");
+  if (check_dtype((patch_dtype)d->dtype)) return PATCH_ERR_INVALID_ARG;
+  patch_status s = check_nk(d->N, d->K);
+  if (s) return s;
+  const uint64_t Tq = (uint64_t)d->nt_n * d->nt_k, E = (uint64_t)(d->N / kQuad) * (uint64_t)(d->K / kTile);
+  // the data take 8192 bytes a dense quadrant, 4096 a 2:4 one and 1024 a
+  // table entry with a 2:4 slice (at most one per 2:4 quadrant)
+  const uint64_t base = d->data_offset + 8192u * (Tq - d->n_sparse) + 4096u * d->n_sparse;
+  if (d->nt_n != d->N / kQuad || d->nt_k != d->K / kQuad || d->n_sparse > Tq || d->n_48 != 0 ||
+      d->table_offset != 256 || d->data_offset != round_up(256 + 16 * E, 256) || d->total_bytes < base ||
+      d->total_bytes > base + 1024u * std::min<uint64_t>(d->n_sparse, E) || (d->total_bytes - base) % 1024u)
+    return fail(PATCH_ERR_INVALID_ARG, "inconsistent descriptor");
+  if (d->total_bytes >= kMaxBlobBytes)
+    return fail(PATCH_ERR_UNSUPPORTED, "blob of %llu bytes exceeds the supported %llu",
+                (unsigned long long)d->total_bytes, (unsigned long long)kMaxBlobBytes);
+  return PATCH_OK;
+}
+
 patch_status check_desc(const patch_packed_desc* d) {
   if (!d) return fail(PATCH_ERR_INVALID_ARG, "null descriptor");
+  if (d->version == kVersionQ64) return check_desc_q64(d);
   if (d->version != kVersion || d->tile_n != kTile || d->tile_k != kTile)
     return fail(PATCH_ERR_INVALID_ARG, "descriptor version/tile mismatch");
   if (check_dtype((patch_dtype)d->dtype)) return PATCH_ERR_INVALID_ARG;
@@ -127,7 +155,7 @@ void put64(uint8_t* p, uint64_t v) { std::memcpy(p, &v, 8); }
 
 extern "C" {
 
-int32_t patch_abi_version(void) { return 4; }
+int32_t patch_abi_version(void) { return 5; }
 
 patch_status patch_sample_mask(int64_t N, int64_t K, const float* tile_logits_dev, const float* tile_u_dev,
                                const float* pat_logits_dev, const float* pat_u_dev, float tau, uint8_t* tile_map_dev,
@@ -252,6 +280,19 @@ uint64_t patch_packed_bytes(patch_dtype dtype, int64_t N, int64_t K, const uint8
 
 }  // extern "C"
 
+extern "C" uint64_t patch_packed_bytes_q64(patch_dtype dtype, int64_t N, int64_t K, const uint8_t* quad_map_host) {
+  if (check_dtype(dtype) || check_nk(N, K) || !quad_map_host) return 0;
+  const int64_t R = N / kQuad, KQ = K / kQuad, KC = K / kTile;
+  uint64_t total = round_up(256 + 16 * (uint64_t)(R * KC), 256);
+  for (int64_t r = 0; r < R; r++)
+    for (int64_t j = 0; j < KC; j++) {
+      const uint8_t a = quad_map_host[r * KQ + 2 * j], b = quad_map_host[r * KQ + 2 * j + 1];
+      if (a > 1 || b > 1) return 0;  // 0 dense, 1 2:4
+      total += 4 * q64_piece((uint32_t)a | ((uint32_t)b << 1));
+    }
+  return total;
+}
+
 // Pack the N x K matrix assembled from the sources (see PackSources);
 // tile_map_host is the map of the assembled matrix.
 static patch_status pack_common(patch_dtype dtype, int64_t N, int64_t K, const patch::PackSources& src,
@@ -342,6 +383,94 @@ static patch_status pack_common(patch_dtype dtype, int64_t N, int64_t K, const p
   d.nt_k = (uint32_t)KT;
   d.n_sparse = ns;
   d.n_48 = n48;
+  d.table_offset = 256;
+  d.data_offset = data_off;
+  d.total_bytes = need;
+  *desc_out = d;
+  return PATCH_OK;
+}
+
+extern "C" patch_status patch_pack_q64(patch_dtype dtype, int64_t N, int64_t K, const void* W_dev,
+                                      const uint8_t* quad_map_host, const uint8_t* mask_dev, void* packed_dev,
+                                      uint64_t packed_bytes, patch_packed_desc* desc_out, void* stream) {
+  patch_status s;
+  if ((s = check_dtype(dtype))) return s;
+  if ((s = check_nk(N, K))) return s;
+  if (!W_dev || !quad_map_host || !mask_dev || !packed_dev || !desc_out)
+    return fail(PATCH_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(W_dev) || !aligned16(mask_dev) || !aligned16(packed_dev))
+    return fail(PATCH_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  const int64_t R = N / kQuad, KQ = K / kQuad, KC = K / kTile;
+  for (int64_t t = 0; t < R * KQ; t++)
+    if (quad_map_host[t] > 1)
+      return fail(PATCH_ERR_INVALID_ARG, "quadrant map byte %d at quadrant %lld (0 dense, 1 2:4)",
+                  (int)quad_map_host[t], (long long)t);
+  const uint64_t need = patch_packed_bytes_q64(dtype, N, K, quad_map_host);
+  if (need >= kMaxBlobBytes) return fail(PATCH_ERR_UNSUPPORTED, "blob of %llu bytes too large", (unsigned long long)need);
+  if (packed_bytes < need)
+    return fail(PATCH_ERR_BUFFER_TOO_SMALL, "packed buffer %llu < %llu bytes", (unsigned long long)packed_bytes,
+                (unsigned long long)need);
+
+  // header + table, built on the host: half-row-block r takes 4 bands of
+  // S_r bytes, band b holding its piece of every tile column in order
+  const uint64_t data_off = round_up(256 + 16 * (uint64_t)(R * KC), 256);
+  std::vector<uint8_t> head(data_off, 0);
+  uint32_t ns = 0;
+  uint64_t hb = data_off;
+  for (int64_t r = 0; r < R; r++) {
+    uint64_t stride = 0;
+    for (int64_t j = 0; j < KC; j++)
+      stride += q64_piece((uint32_t)quad_map_host[r * KQ + 2 * j] | ((uint32_t)quad_map_host[r * KQ + 2 * j + 1] << 1));
+    uint64_t prefix = 0;
+    for (int64_t j = 0; j < KC; j++) {
+      const int64_t t = r * KC + j;
+      const uint32_t kb = (uint32_t)quad_map_host[r * KQ + 2 * j] | ((uint32_t)quad_map_host[r * KQ + 2 * j + 1] << 1);
+      put64(&head[256 + 16 * t], hb + prefix);
+      put32(&head[256 + 16 * t + 8], kb);
+      put32(&head[256 + 16 * t + 12], (uint32_t)stride);
+      prefix += q64_piece(kb);
+      ns += (kb & 1u) + (kb >> 1);
+    }
+    hb += 4 * stride;
+  }
+  put32(&head[0], kMagic);
+  put32(&head[4], kVersionQ64);
+  put32(&head[8], (uint32_t)dtype);
+  put32(&head[12], (uint32_t)kQuad);
+  put32(&head[16], (uint32_t)kQuad);
+  put32(&head[20], (uint32_t)N);
+  put32(&head[24], (uint32_t)K);
+  put32(&head[28], (uint32_t)R);
+  put32(&head[32], (uint32_t)KQ);
+  put32(&head[36], ns);
+  put64(&head[40], 256);
+  put64(&head[48], data_off);
+  put64(&head[56], need - data_off);
+  put64(&head[64], need);
+  put32(&head[72], 0);
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(packed_dev, head.data(), head.size(), hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(header)");
+  e = patch::launch_pack_q64(W_dev, mask_dev, N, K, reinterpret_cast<uint8_t*>(packed_dev), st);
+  if (e != hipSuccess) return hip_fail(e, "launch pack_q64");
+  uint32_t flag = 0;
+  e = hipMemcpyAsync(&flag, reinterpret_cast<uint8_t*>(packed_dev) + kErrFlagOffset, 4, hipMemcpyDeviceToHost, st);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(flag)");
+  e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  if (flag) return fail(PATCH_ERR_MASK, "a group inside a 2:4 quadrant does not keep exactly two of four weights");
+
+  patch_packed_desc d;
+  d.version = kVersionQ64;
+  d.dtype = (uint32_t)dtype;
+  d.tile_n = d.tile_k = (uint32_t)kQuad;
+  d.N = (uint32_t)N;
+  d.K = (uint32_t)K;
+  d.nt_n = (uint32_t)R;
+  d.nt_k = (uint32_t)KQ;
+  d.n_sparse = ns;
+  d.n_48 = 0;
   d.table_offset = 256;
   d.data_offset = data_off;
   d.total_bytes = need;
@@ -500,7 +629,7 @@ uint64_t patch_dense_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) { ret
 static patch_status gemm_common(bool rowmajor, patch_dtype dt, int64_t M, int64_t N, int64_t K, const void* src,
                                 const void* src2, uint64_t w_bytes, const void* X_dev, void* Y_dev,
                                 patch_dtype y_dtype, void* ws, uint64_t ws_bytes, int32_t variant, void* stream,
-                                bool has48 = false) {
+                                bool has48 = false, bool q64 = false) {
   patch_status s;
   if ((s = check_ydtype(dt, y_dtype))) return s;
   if (M < 0 || M > (int64_t)0x7fffffff) return fail(PATCH_ERR_INVALID_ARG, "M=%lld out of range", (long long)M);
@@ -508,6 +637,11 @@ static patch_status gemm_common(bool rowmajor, patch_dtype dt, int64_t M, int64_
     return fail(PATCH_ERR_INVALID_ARG, "unknown variant %d", (int)variant);
   if (has48 && variant >= PATCH_VARIANT_PREFILL_W64 && variant <= PATCH_VARIANT_PREFILL_W256)
     return fail(PATCH_ERR_UNSUPPORTED, "the register-staged prefill variants run dense and 2:4 tiles only");
+  if (q64 && ((variant >= PATCH_VARIANT_PREFILL_W64 && variant <= PATCH_VARIANT_PREFILL_W256) ||
+              variant >= PATCH_VARIANT_PREFILL_BIG))
+    return fail(PATCH_ERR_UNSUPPORTED,
+                "a blob of 64 x 64 execution tiles runs on the decode and LDS-staged prefill kernels only");
+  if (q64 && src2) return fail(PATCH_ERR_UNSUPPORTED, "the fused gate/up product takes 128 x 128 execution tiles");
   if (variant == PATCH_VARIANT_DECODE && M > kDecodeMaxM)
     return fail(PATCH_ERR_INVALID_ARG, "decode variant needs M <= %lld (M=%lld)", (long long)kDecodeMaxM, (long long)M);
   if (M == 0) return PATCH_OK;
@@ -536,9 +670,10 @@ static patch_status gemm_common(bool rowmajor, patch_dtype dt, int64_t M, int64_
   static const int kForceBm[17] = {0, 0, 0, 64, 128, 192, 256, 128, 192, 256, 64, 0, 128, 192, 256, 128, 256};
   const int big = variant >= PATCH_VARIANT_PREFILL_BIG8_W128 ? 8 : variant >= PATCH_VARIANT_PREFILL_BIG ? 4 : 0;
   const bool lds = variant >= PATCH_VARIANT_PREFILL_W128_LDS && variant <= PATCH_VARIANT_PREFILL_W64_LDS;
-  hipError_t e = decode ? patch::launch_decode(bf16, rowmajor, f32out, src, src2, X_dev, M, N, K, Y_dev, has48, st)
+  hipError_t e = decode ? patch::launch_decode(bf16, rowmajor, f32out, src, src2, X_dev, M, N, K, Y_dev, has48, q64,
+                                               st)
                         : patch::launch_prefill(bf16, rowmajor, f32out, src, src2, X_dev, M, N, K, Y_dev, ws,
-                                                ws_bytes, kForceBm[variant], lds, big, st);
+                                                ws_bytes, kForceBm[variant], lds, big, q64, st);
   if (e != hipSuccess) return hip_fail(e, decode ? "launch decode" : "launch prefill");
   return PATCH_OK;
 }
@@ -550,7 +685,7 @@ patch_status patch_gemm_ex(const patch_packed_desc* desc, const void* packed_dev
   if (s) return s;
   return gemm_common(false, (patch_dtype)desc->dtype, M, desc->N, desc->K, packed_dev, nullptr,
                      desc->total_bytes - desc->data_offset, X_dev, Y_dev, y_dtype, workspace_dev, workspace_bytes,
-                     variant, stream, desc->n_48 > 0);
+                     variant, stream, desc->n_48 > 0, desc->version == kVersionQ64);
 }
 
 patch_status patch_gemm(const patch_packed_desc* desc, const void* packed_dev, const void* X_dev, int64_t M,
@@ -592,6 +727,8 @@ patch_status patch_gemm_swiglu(const patch_packed_desc* desc, const void* packed
                                int32_t variant, void* stream) {
   patch_status s = check_desc(desc);
   if (s) return s;
+  if (desc->version == kVersionQ64)
+    return fail(PATCH_ERR_UNSUPPORTED, "the fused gate/up product takes 128 x 128 execution tiles");
   if (desc->nt_n % 2) return fail(PATCH_ERR_SHAPE, "a gate/up blob has an even number of row-blocks");
   return gemm_common(false, (patch_dtype)desc->dtype, M, desc->N, desc->K, packed_dev, packed_dev,
                      desc->total_bytes - desc->data_offset, X_dev, H_dev, h_dtype, workspace_dev, workspace_bytes,

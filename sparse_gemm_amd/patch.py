@@ -45,7 +45,8 @@ class Desc(ctypes.Structure):
                 ("total_bytes", ctypes.c_uint64)]
 
 
-EXPORTS = ("patch_abi_version", "patch_packed_bytes", "patch_pack", "patch_desc_from_header",
+EXPORTS = ("patch_abi_version", "patch_packed_bytes", "patch_pack", "patch_packed_bytes_q64", "patch_pack_q64",
+           "patch_desc_from_header",
            "patch_gemm_workspace_bytes", "patch_dense_gemm_workspace_bytes", "patch_gemm", "patch_gemm_ex",
            "patch_dense_gemm", "patch_dense_gemm_ex", "patch_packed_bytes_gate_up", "patch_pack_gate_up",
            "patch_gemm_swiglu_workspace_bytes", "patch_gemm_swiglu", "patch_dense_gemm_swiglu_workspace_bytes",
@@ -73,6 +74,10 @@ def load():
     lib.patch_packed_bytes.restype = U64
     lib.patch_pack.argtypes = [ctypes.c_int, I64, I64, P, P, P, P, U64, DP, P]
     lib.patch_pack.restype = ctypes.c_int
+    lib.patch_packed_bytes_q64.argtypes = [ctypes.c_int, I64, I64, P]
+    lib.patch_packed_bytes_q64.restype = U64
+    lib.patch_pack_q64.argtypes = [ctypes.c_int, I64, I64, P, P, P, P, U64, DP, P]
+    lib.patch_pack_q64.restype = ctypes.c_int
     lib.patch_desc_from_header.argtypes = [P, U64, DP]
     lib.patch_desc_from_header.restype = ctypes.c_int
     lib.patch_gemm_workspace_bytes.argtypes = [DP, I64]
@@ -254,6 +259,44 @@ def pack(W: torch.Tensor, tile_map, mask: torch.Tensor, out: Optional[torch.Tens
     desc = Desc()
     _check(lib.patch_pack(_dt(W.dtype), N, K, _ptr(W), tm.ctypes.data_as(ctypes.c_void_p), _ptr(mask), _ptr(out),
                           out.numel(), ctypes.byref(desc), _stream()))
+    return PackedWeight(out, desc)
+
+
+def packed_bytes_q64(dtype: torch.dtype, N: int, K: int, quad_map) -> int:
+    """Blob size for 64 x 64 execution tiles (format 4) and a (N/64, K/64)
+    quadrant map (0 dense, 1 2:4); 0 for invalid arguments."""
+    qm = _host_map(quad_map)
+    if qm.shape != (N // 64, K // 64):
+        return 0
+    return int(load().patch_packed_bytes_q64(_dt(dtype), N, K, qm.ctypes.data_as(ctypes.c_void_p)))
+
+
+def pack_q64(W: torch.Tensor, quad_map, mask: torch.Tensor, out: Optional[torch.Tensor] = None) -> PackedWeight:
+    """Pack W (N x K, f16/bf16, device), a host quadrant map ((N/64) x (K/64):
+    0 dense, 1 2:4) and a device byte mask into a blob of 64 x 64 execution
+    tiles (patch_pack_q64)."""
+    lib = load()
+    _need(isinstance(W, torch.Tensor) and W.dim() == 2, "W must be a 2-D tensor (N x K)")
+    _need(W.dtype in (torch.float16, torch.bfloat16), "W must be float16 or bfloat16")
+    N, K = W.shape
+    _check_dev(W, "W", on_device=False)
+    _check_dev(mask, "mask", torch.uint8, (N, K), on_device=False)
+    qm = _host_map(quad_map)
+    _need(qm.shape == (N // 64, K // 64) or N % 128 or K % 128, f"quadrant map must have shape {(N // 64, K // 64)}")
+    if out is not None:
+        _check_dev(out, "out", torch.uint8, on_device=False)
+    _need(W.is_cuda and mask.is_cuda and (out is None or out.is_cuda), "W, mask and out must be device tensors")
+    nbytes = packed_bytes_q64(W.dtype, N, K, qm)
+    if nbytes == 0:
+        probe = torch.empty(16, dtype=torch.uint8, device=W.device)
+        _check(lib.patch_pack_q64(_dt(W.dtype), N, K, _ptr(W), qm.ctypes.data_as(ctypes.c_void_p), _ptr(mask),
+                                  _ptr(probe), 0, ctypes.byref(Desc()), _stream()))
+        raise PatchError(2, f"invalid arguments for pack_q64: {tuple(W.shape)} {W.dtype}")
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
+    desc = Desc()
+    _check(lib.patch_pack_q64(_dt(W.dtype), N, K, _ptr(W), qm.ctypes.data_as(ctypes.c_void_p), _ptr(mask),
+                              _ptr(out), out.numel(), ctypes.byref(desc), _stream()))
     return PackedWeight(out, desc)
 
 

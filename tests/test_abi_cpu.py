@@ -12,12 +12,13 @@ import oracle
 from sparse_gemm_amd import inputs, patch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+V = ctypes.c_void_p
 
 
 def _declared():
     src = open(os.path.join(ROOT, "include", "patch.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(patch_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(patch_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -27,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(patch.EXPORTS)
-    assert patch.load().patch_abi_version() == 4
+    assert patch.load().patch_abi_version() == 5
 
 
 def test_packed_bytes_matches_oracle_closed_form():
@@ -217,3 +218,61 @@ def test_binding_rejects_bad_tensors_before_any_call():
         with pytest.raises(ValueError) as e:
             fn()
         assert text in str(e.value), (text, str(e.value))
+
+
+# ---------------------------------------------------------------- 64 x 64 execution tiles (format 4)
+def test_packed_bytes_q64_matches_oracle():
+    lib = patch.load()
+    for seed, (s_exec, p_sub) in enumerate(((0.0, 0.0), (0.3, 0.5), (1.0, 1.0), (0.0, 0.7))):
+        p = inputs.make_fine("bf16", 384, 640, 64, 64, 30 + seed, s_exec=s_exec, p_sub=p_sub)
+        want = oracle.packed_bytes_q64(384, 640, p.tile_map)
+        assert patch.packed_bytes_q64(torch.bfloat16, 384, 640, p.tile_map) == want
+        qm = np.ascontiguousarray(p.tile_map)
+        assert lib.patch_packed_bytes_q64(0, 384, 640, qm.ctypes.data_as(ctypes.c_void_p)) == want
+    bad = np.zeros((6, 10), np.uint8)
+    bad[1, 3] = 2  # 4:8 is not a quadrant kind
+    assert lib.patch_packed_bytes_q64(1, 384, 640, bad.ctypes.data_as(ctypes.c_void_p)) == 0
+    assert patch.packed_bytes_q64(torch.bfloat16, 384, 640, np.zeros((3, 5), np.uint8)) == 0  # wrong map shape
+    assert lib.patch_packed_bytes_q64(1, 320, 640, np.zeros((5, 10), np.uint8).ctypes.data_as(ctypes.c_void_p)) == 0
+
+
+def test_pack_q64_host_checks_before_any_device_work():
+    lib = patch.load()
+    qm = np.zeros((4, 4), np.uint8)
+    qm[0, 0] = 3
+    d = patch.Desc()
+    rc = lib.patch_pack_q64(1, 256, 256, V(16), qm.ctypes.data_as(ctypes.c_void_p), V(16), V(16), 1 << 40,
+                            ctypes.byref(d), None)
+    assert patch.STATUS[rc] == "PATCH_ERR_INVALID_ARG"
+    qm[0, 0] = 1
+    rc = lib.patch_pack_q64(1, 256, 256, V(16), qm.ctypes.data_as(ctypes.c_void_p), V(16), V(16), 1024,
+                            ctypes.byref(d), None)
+    assert patch.STATUS[rc] == "PATCH_ERR_BUFFER_TOO_SMALL"
+    rc = lib.patch_pack_q64(1, 256, 256, V(8), qm.ctypes.data_as(ctypes.c_void_p), V(16), V(16), 1 << 40,
+                            ctypes.byref(d), None)
+    assert patch.STATUS[rc] == "PATCH_ERR_INVALID_ARG"  # unaligned W
+
+
+def test_desc_from_oracle_q64_header_and_gemm_checks():
+    p = inputs.make_fine("bf16", 256, 384, 64, 64, 33, s_exec=0.3, p_sub=0.5)
+    blob = oracle.pack_q64("bf16", p.w, p.tile_map, p.mask)
+    d = patch.desc_from_header(blob[:256].tobytes())
+    assert (d.version, d.dtype, d.tile_n, d.tile_k, d.N, d.K, d.nt_n, d.nt_k, d.n_48) == (4, 1, 64, 64, 256, 384,
+                                                                                           4, 6, 0)
+    assert d.n_sparse == int(p.tile_map.sum()) and d.total_bytes == blob.size
+    lib = patch.load()
+    assert lib.patch_gemm(ctypes.byref(d), V(16), V(16), 0, V(16), 1, None, 0, None) == 0  # M = 0 no-op
+    # the register-staged and big-tile variants and the fused product reject it before any device work
+    for v in (3, 6, 11, 16):
+        assert patch.STATUS[lib.patch_gemm_ex(ctypes.byref(d), V(16), V(16), 64, V(16), 1, None, 0, v,
+                                              None)] == "PATCH_ERR_UNSUPPORTED"
+    assert patch.STATUS[lib.patch_gemm_swiglu(ctypes.byref(d), V(16), V(16), 64, V(16), 1, None, 0, 0,
+                                              None)] == "PATCH_ERR_UNSUPPORTED"
+    bad = bytearray(blob[:256].tobytes())
+    bad[64] ^= 0x04  # total_bytes off by 1 KiB * 4: no longer a multiple of the step or out of range
+    bad[56] ^= 0x04
+    with pytest.raises(patch.PatchError):
+        patch.desc_from_header(bytes(bad))
+    d.n_48 = 1
+    assert patch.STATUS[lib.patch_gemm(ctypes.byref(d), V(16), V(16), 4, V(16), 1, None, 0,
+                                       None)] == "PATCH_ERR_INVALID_ARG"
