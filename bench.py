@@ -745,7 +745,7 @@ def main():
     ap.add_argument("--report-steps", type=int, default=100, help="launches per timed batch in the report")
     ap.add_argument("--report-batches", type=int, default=10, help="timed batches per point in the report (median)")
     ap.add_argument("--workload", default="prefill_mlp",
-                    choices=["prefill_mlp", "decode", "imbalanced_13b", "sampler", "fine_mask", "n48"],
+                    choices=["prefill_mlp", "decode", "imbalanced_13b", "sampler", "fine_mask", "n48", "tile64"],
                     help="prefill_mlp (default: the headline line); the others print that workload's lines, "
                          "for profiling")
     ap.add_argument("--hybrid-only", action="store_true",
@@ -783,6 +783,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration_copy_bytes": src.numel(), "copies": 3}), file=sys.stderr, flush=True)
         del src, dst
+    if args.workload == "tile64":
+        for rec in q64_set(args.steps, args.warmup):
+            print(json.dumps(rec), flush=True)
+        return
     if args.workload in ("sampler", "fine_mask", "n48"):
         fn = {"sampler": sampler_set, "fine_mask": fine_set, "n48": n48_set}[args.workload]
         for rec in fn(args.steps, args.warmup, 1):
@@ -815,6 +819,8 @@ def main():
         line["roofline"]["measured_ceilings_tflops"] = {k: sm[k] for k in sm}
         print("[bench] sparsity sweep", file=sys.stderr, flush=True)
         line["sweep"] = sweep_compact(max(10, args.steps), args.warmup)
+        print("[bench] 64 x 64 execution tiles", file=sys.stderr, flush=True)
+        line["tile64"] = q64_set(max(10, args.steps), args.warmup)
     if not args.no_cpu:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(problems, Ms, sample_rows=32)
@@ -909,6 +915,58 @@ def n48_set(steps, warmup, batches, Ms=(1, 16, 128, 2048)):
                             tflops_dense_equiv_48=2.0 * M * N * K / (us["48"] * 1e-6) / 1e12,
                             gbps_48=algo_bytes(N, K, M, (N // 128) * (K // 128)) / (us["48"] * 1e-6) / 1e9))
         del packs, Ws, W
+        torch.cuda.empty_cache()
+    return out
+
+
+def q64_set(steps, warmup, batches=3):
+    """64 x 64 against 128 x 128 execution tiles for one mask learnt on
+    64 x 64 tiles (LLaMA-2-7B q_proj 4096 x 4096 and gate_proj 11008 x 4096,
+    bf16; a 128 x 128 tile is 2:4 in all four quadrants with probability 0.4,
+    else each quadrant is 2:4 with probability 0.6; uniformly drawn 2:4
+    patterns), at M = 1, 16 and 2048, each launch on its own weight copy,
+    graph replays (median of batches):
+      * q64: the 64 x 64 blob (patch_pack_q64), every 2:4 quadrant on the
+        sparse path;
+      * t128: the 128 x 128 blob under the all-2:4 policy (a tile runs 2:4
+        only if its four quadrants are; dense tiles on W o E_fine:
+        patch_exec_tile_map + patch_apply_fine_mask + patch_pack) -- the same
+        product X (W o E_fine)^T;
+      * dense: the same weights packed with every tile dense (same kernels)."""
+    import torch
+
+    from sparse_gemm_amd import inputs, patch
+
+    out = []
+    for name, N, K in (("q_proj", 4096, 4096), ("gate_proj", 11008, 4096)):
+        p = inputs.make_fine("bf16", N, K, 64, 64, 0)
+        W = dev_bits(p.w, torch.bfloat16)
+        mk = torch.from_numpy(p.mask).cuda()
+        packs = {"q64": patch.pack_q64(W, p.tile_map, mk), "t128": patch.pack_fine(W, p.tile_map, mk, 64, 64),
+                 "dense": patch.pack(W, np.zeros((N // 128, K // 128), np.uint8), mk)}
+        del mk
+        emap = patch.exec_tile_map(N, K, p.tile_map, 64, 64)
+        rec = dict(config="tile64", matrix=name, N=N, K=K, quadrant_sparse_fraction=float(p.tile_map.mean()),
+                   tile128_sparse_fraction=float(emap.mean()),
+                   blob_bytes={k: v.nbytes for k, v in packs.items()}, us={})
+        Ms = (1, 16, 2048)
+        Xs = {M: dev_bits(inputs.make_x(inputs.CONFIGS["decode"], M, K), torch.bfloat16) for M in Ms}
+        Ys = {M: torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for M in Ms}
+        for k, pw in packs.items():
+            blobs = rotate(pw.blob, pw.nbytes)
+
+            def mk_fn(M, blobs=blobs, desc=pw.desc):
+                return lambda i: patch.gemm(Xs[M], patch.PackedWeight(blobs[i % len(blobs)], desc), out=Ys[M])
+
+            _, per = time_graphs([(M, mk_fn(M)) for M in Ms], steps, warmup, batches)
+            rec["us"][k] = {str(M): median(per[M]) * 1e3 for M in Ms}
+            del blobs
+            torch.cuda.empty_cache()
+        rec["speedup_q64_vs_t128"] = {str(M): rec["us"]["t128"][str(M)] / rec["us"]["q64"][str(M)] for M in Ms}
+        rec["speedup_q64_vs_dense"] = {str(M): rec["us"]["dense"][str(M)] / rec["us"]["q64"][str(M)] for M in Ms}
+        rec["speedup_t128_vs_dense"] = {str(M): rec["us"]["dense"][str(M)] / rec["us"]["t128"][str(M)] for M in Ms}
+        out.append(rec)
+        del W, packs, Xs, Ys
         torch.cuda.empty_cache()
     return out
 
