@@ -47,6 +47,12 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 # that a profiler's per-kernel figures cover the headline's timed launches
 # alone -- the all-dense packed reference runs the same kernels
 HYBRID_ONLY = False
+# Untimed settle phase before every timed measurement: the calls are repeated
+# back to back for this long first.  From idle, the GPU's power management
+# takes some 20-40 ms of sustained load to settle; launches timed before that
+# ran up to 25% slower (the prefill MLP step: 0.34 ms in its first 14 ms, then
+# 0.29-0.30 ms).  --settle-ms sets it.
+SETTLE_MS = 150.0
 KERNEL_SOURCES = ("sparse_gemm_amd/csrc/gemm_decode.hip", "sparse_gemm_amd/csrc/gemm_prefill.hip",
                   "sparse_gemm_amd/csrc/prefill_common.h", "sparse_gemm_amd/csrc/device_common.h")
 
@@ -83,6 +89,26 @@ def _event():
     return e
 
 
+def settle(calls, ms=None):
+    """Untimed: run the calls back to back (launch index k * len(calls) + c,
+    so the weight copies keep rotating) until `ms` of host time has passed,
+    synchronising every few steps so the GPU is busy for about that long."""
+    import torch
+
+    ms = SETTLE_MS if ms is None else ms
+    if ms <= 0:
+        return
+    n, k = len(calls), 0
+    t_end = time.perf_counter() + ms * 1e-3
+    while time.perf_counter() < t_end:
+        for c, (_, fn) in enumerate(calls):
+            fn(k * n + c)
+        k += 1
+        if k % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def time_launches(calls, steps, warmup, batches=1):
     """calls: list of (key, fn(i)); fn(i) issues launch i of that call (it
     picks its weight copy from i).  Returns
@@ -94,9 +120,11 @@ def time_launches(calls, steps, warmup, batches=1):
         `batches` batches of `steps` launches back to back (indices warmup,
         warmup + 1, ...), one event pair around each batch, divided by
         `steps`.
-    Events are recorded on the current stream, the one the launches use."""
+    Events are recorded on the current stream, the one the launches use.
+    An untimed settle phase (settle()) comes first."""
     import torch
 
+    settle(calls)
     n = len(calls)
     for k in range(warmup):
         for c, (_, fn) in enumerate(calls):
@@ -132,9 +160,10 @@ def time_steps_events(calls, steps, warmup):
     to last event / steps) and {key: [ms of each of its launches]} (event to
     next event), so the launches' durations add up to the step time exactly.
     Every launch here is long against its host cost, so the stream never
-    waits for the host."""
+    waits for the host.  An untimed settle phase (settle()) comes first."""
     import torch
 
+    settle(calls)
     n = len(calls)
     for k in range(warmup):
         for c, (_, fn) in enumerate(calls):
@@ -183,9 +212,11 @@ def time_graphs(calls, steps, warmup, batches=1):
       * ms per step: one graph of `steps` steps (every call once a step, back
         to back), replayed once untimed and once between one event pair;
       * {key: [ms per launch of each batch]}: per call, one graph of `steps`
-        launches, replayed `batches` times, each between one event pair."""
+        launches, replayed `batches` times, each between one event pair.
+    An untimed settle phase (settle()) comes first."""
     import torch
 
+    settle(calls)
     n = len(calls)
     for k in range(warmup):
         for c, (_, fn) in enumerate(calls):
@@ -556,11 +587,16 @@ def headline_prefill(args):
     if not HYBRID_ONLY:
         ms_step_graph, _ = time_graphs([(m["name"], hyb(m)) for m in mats], steps, warmup)
     refs = not HYBRID_ONLY
-    ms_dense = per_dense = ms_s0 = per_s0 = ms_blas = per_blas = None
+    ms_dense = per_dense = ms_s0 = per_s0 = ms_blas = per_blas = per_hb = per_bb = None
     if refs:
         ms_dense, per_dense = time_steps_events([(m["name"], dense(m)) for m in mats], steps, warmup)
         ms_s0, per_s0 = time_steps_events([(m["name"], hyb0(m)) for m in mats], steps, warmup)
         ms_blas, per_blas = time_steps_events([(m["name"], blas(m)) for m in mats], steps, warmup)
+        # like for like against the library: batches of back-to-back launches
+        # between one event pair, no event between launches (an event between
+        # two torch.matmul launches costs them more than it costs ours)
+        _, per_hb = time_launches([(m["name"], hyb(m)) for m in mats], steps, warmup, 3)
+        _, per_bb = time_launches([(m["name"], blas(m)) for m in mats], steps, warmup, 3)
 
     def ref_us(per_ref, name):
         return mean(per_ref[name]) * 1e3 if refs else None
@@ -582,10 +618,13 @@ def headline_prefill(args):
             tflops_effective=eff_flops(M, T, ns) / t / 1e12, roofline_us=tm * 1e6, roofline_frac=tm / t,
             dense_us=ref_us(per_s0, m["name"]),
             rowmajor_dense_us=ref_us(per_dense, m["name"]),
-            hipblaslt_us=ref_us(per_blas, m["name"]),
+            hipblaslt_us=median(per_bb[m["name"]]) * 1e3 if refs else None,
+            hybrid_us_batched=median(per_hb[m["name"]]) * 1e3 if refs else None,
+            hipblaslt_us_events=ref_us(per_blas, m["name"]),
             speedup_vs_dense=ref_speedup(per_s0, m["name"], t),
             speedup_vs_rowmajor_dense=ref_speedup(per_dense, m["name"], t),
-            speedup_vs_hipblaslt=ref_speedup(per_blas, m["name"], t),
+            speedup_vs_hipblaslt=median(per_bb[m["name"]]) / median(per_hb[m["name"]]) if refs else None,
+            speedup_vs_hipblaslt_events=ref_speedup(per_blas, m["name"], t),
             pack_us=m["pack_ms"] * 1e3, pack_gbps=(3 * p.N * p.K + m["pw"].nbytes) / (m["pack_ms"] * 1e-3) / 1e9,
             weight_copies_rotated=len(m["blobs"]))
         eff_sum += eff_flops(M, T, ns) * len(per[m["name"]])
@@ -615,16 +654,23 @@ def headline_prefill(args):
             "M": M, "matrices": [dict(name=m["name"], N=m["p"].N, K=m["p"].K) for m in mats],
             "weight_copies_rotated": [len(m["blobs"]) for m in mats],
         },
-        "timing": "one event before every launch and one after the last, on the launch stream; the K steps issued "
-                  "back to back (each launch on its own weight copy, >= 1 GiB rotated per matrix); ms_per_step = "
-                  "first to last event / K; per-launch times = event to next event",
+        "timing": "an untimed settle phase (the step repeated for settle_ms: the GPU's power management takes "
+                  "20-40 ms of sustained load to settle), W untimed warm-up steps, then one event before every "
+                  "launch and one after the last, on the launch stream; the K steps issued back to back (each "
+                  "launch on its own weight copy, >= 1 GiB rotated per matrix); ms_per_step = first to last "
+                  "event / K; per-launch times = event to next event",
+        "settle_ms": SETTLE_MS,
         "dense_reference": "speedup_vs_dense: the same-shape dense GEMM = the same weights packed with every tile "
                            "dense, run by the same kernels (the sparsity gain alone); speedup_vs_rowmajor_dense: "
-                           "patch_dense_gemm on row-major W; speedup_vs_hipblaslt: torch.matmul (hipBLASLt)",
+                           "patch_dense_gemm on row-major W; speedup_vs_hipblaslt: torch.matmul (hipBLASLt) against "
+                           "the hybrid GEMM, both as 3 batches of K back-to-back launches between one event pair "
+                           "(median; _events: with the headline's per-launch events)",
         "ms_per_step_graph": ms_step_graph,
         "speedup_vs_dense_step": ms_s0 / ms_step if refs else None,
         "speedup_vs_rowmajor_dense_step": ms_dense / ms_step if refs else None,
-        "speedup_vs_hipblaslt_step": ms_blas / ms_step if refs else None,
+        "speedup_vs_hipblaslt_step": (sum(median(per_bb[m["name"]]) for m in mats) /
+                                      sum(median(per_hb[m["name"]]) for m in mats)) if refs else None,
+        "speedup_vs_hipblaslt_step_events": ms_blas / ms_step if refs else None,
         "per_matrix": per_matrix,
         "roofline": {
             "kernel": "prefill hybrid GEMM (packed W), both matrices' launches",
@@ -734,6 +780,7 @@ def sweep_compact(steps, warmup, Ms=(1, 2048)):
 
 
 def main():
+    global HYBRID_ONLY, SETTLE_MS
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -751,14 +798,16 @@ def main():
     ap.add_argument("--hybrid-only", action="store_true",
                     help="time the hybrid launches alone, no reference GEMMs (for profiler and counter runs, whose "
                          "per-kernel figures then cover the hybrid launches alone)")
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="untimed settle phase before every timed measurement, ms (0: none)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for rocprofv3 byte counters)")
     ap.add_argument("--ingest-counters", nargs="+", metavar="DIR", default=None,
                     help="FETCH_DIR WRITE_DIR [FETCH_DIR WRITE_DIR ...]: write profiles/traffic_counters.json from "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE runs and exit")
     args = ap.parse_args()
-    global HYBRID_ONLY
     HYBRID_ONLY = args.hybrid_only
+    SETTLE_MS = args.settle_ms
     if args.ingest_counters:
         ingest_counters(args.ingest_counters)
         return
