@@ -439,6 +439,11 @@ constexpr int kLdsWStage = 32768;  // 2 row-blocks x 8 bands x 2 fragments of 1 
 // stages of the LDS ring for an M-block width: three up to 128, two at 192
 // and 256 (a third would not fit the 160 KB of LDS)
 constexpr int lds_stages(int bm) { return bm <= 128 ? 3 : 2; }
+// W stages: three also at width 192 (two X stages of 24 KB beside three W
+// stages of 32 KB and 8 KB of tile entries fill the 160 KB exactly; not with
+// the 16 KB of entries of 64 x 64 tiles), so W copies run two steps ahead
+// there while X copies run one
+constexpr int lds_w_stages(int bm, bool q64) { return bm <= 128 || (bm == 192 && !q64) ? 3 : 2; }
 
 // Q64: a blob of 64 x 64 execution tiles (format 4).  Its table has one
 // entry per 64-row half of a row-block and 128-column tile column, whose
@@ -452,7 +457,8 @@ template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE, int BM, bool Q6
 __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   static_assert(!Q64 || (!SRC_ROWMAJOR && !FUSE), "64 x 64 execution tiles: packed W, not fused");
   constexpr int kNMB = BM / 32;                     // 16-column M blocks per wave
-  constexpr int kLdsStages = lds_stages(BM);
+  constexpr int kXStages = lds_stages(BM);
+  constexpr int kWStages = lds_w_stages(BM, Q64);
   constexpr int kLdsXStage = BM * kPfRowBytes;       // X rows of one step
   constexpr int kXC = BM / 64;                       // 1 KB X chunks a wave copies per step
   constexpr int kLdsCopies = 4 + kXC;                // copies a wave issues per step
@@ -460,11 +466,10 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   // 256, where two steps' A fragments and the accumulators leave no room)
   constexpr int kMG = BM == 256 ? 1 : kPfMGroup;
   static_assert(kXC * 1024 * kPfWaves == kLdsXStage, "X stage split");
-  __shared__ __attribute__((aligned(1024))) uint8_t s_w[kLdsStages * kLdsWStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t s_x[kLdsStages * kLdsXStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_w[kWStages * kLdsWStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_x[kXStages * kLdsXStage];
   constexpr int kEntRows = Q64 ? 4 : 2;  // row-blocks (Q64: their 64-row halves) of a workgroup
   __shared__ uint32_t s_ent[kEntRows][kPfMaxKT];
-  __shared__ uint32_t s_stride[Q64 ? 1 : 2];  // (Q64: each wave reads its own from the table)
   __shared__ u32x4 s_sel[SRC_ROWMAJOR || Q64 ? 1 : 256];  // 4:8 rebuild selectors
 
   const int t = (blockIdx.x & 7) * P.per_xcd + (blockIdx.x >> 3);
@@ -510,18 +515,17 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
       const int j = e - rr * nt;
       const TileEntry te = table[(int64_t)(rr ? i1 : i0) * KT + j0 + j];
       s_ent[rr][j] = (uint32_t)(te.offset >> 8) | (te.kind << 30);
-      if (j == 0) s_stride[rr] = te.band_stride;
     }
     fill_sel48(s_sel, (int)threadIdx.x, kPfWaves * 64);
     __syncthreads();
   }
   const int er = Q64 ? 2 * r_src + wn : r_src;  // this wave's entry row
+  // the band stride of this wave's row-block (Q64: of its half), read by
+  // each wave from its first table entry
   uint32_t stride = 0u;
-  if constexpr (Q64)
+  if constexpr (!SRC_ROWMAJOR)
     stride = (uint32_t)__builtin_amdgcn_readfirstlane((int)reinterpret_cast<const TileEntry*>(
-        P.src + kHeaderBytes)[(int64_t)(2 * (r_src ? i1 : i0) + wn) * KT + j0].band_stride);
-  else if constexpr (!SRC_ROWMAJOR)
-    stride = (uint32_t)__builtin_amdgcn_readfirstlane((int)s_stride[er]);
+        P.src + kHeaderBytes)[(int64_t)(Q64 ? 2 * (r_src ? i1 : i0) + wn : i_src) * KT + j0].band_stride);
 
   // this wave's kXC 8-row chunks of each X stage: rows 8 (kXC w + u) + l/8,
   // the lane fetching the source chunk whose swizzled position is l % 8;
@@ -535,16 +539,20 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   }
   const uint32_t w_lds = lds_addr(s_w), x_lds = lds_addr(s_x);
 
-  // the copies of step s into stage s % kLdsStages; e_v: the tile entry of
-  // step s for this wave's row-block (a VGPR loaded from LDS earlier, so no
-  // LDS round trip sits between the step's barrier and its copies)
-  auto issue = [&](int s, uint32_t e_v) {
-    const int st = s % kLdsStages;
-    const int jl = s >> 1, h = s & 1, j = j0 + jl;
-    const uint32_t wb = w_lds + (uint32_t)(st * kLdsWStage), xb = x_lds + (uint32_t)(st * kLdsXStage);
-    const int col = j * kTile + 64 * h;
+  // the X copies of step s into X stage s % kXStages
+  auto issue_x = [&](int s) {
+    const int col = (j0 + (s >> 1)) * kTile + 64 * (s & 1);
+    const uint32_t xb = x_lds + (uint32_t)((s % kXStages) * kLdsXStage);
 #pragma unroll
     for (int u = 0; u < kXC; u++) dma16(xsrc[u] + col, xb + 1024u * (uint32_t)(kXC * w + u));
+  };
+  // the W copies of step s into W stage s % kWStages; e_v: the tile entry of
+  // step s for this wave's row-block (a VGPR loaded from LDS earlier, so no
+  // LDS round trip sits between the step's barrier and its copies)
+  auto issue_w = [&](int s, uint32_t e_v) {
+    const int jl = s >> 1, h = s & 1, j = j0 + jl;
+    const uint32_t wb = w_lds + (uint32_t)((s % kWStages) * kLdsWStage);
+    const int col = j * kTile + 64 * h;
     // fragment slot of band 4wn + b, half e of row-block r: ((r*8 + 4wn + b)*2 + e) KB
     const uint32_t slot0 = wb + 1024u * (uint32_t)((r * 8 + 4 * wn) * 2);
     if constexpr (SRC_ROWMAJOR) {
@@ -608,7 +616,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
     for (int mm = 0; mm < kRG; mm++)
       bf[mm] = *reinterpret_cast<const u32x4*>(xs + swz(wm * (BM / 2) + (kRG * part + mm) * 16 + (l & 15), 4 * qq + hl));
   };
-  auto x_stage = [&](int s) { return s_x + (s % kLdsStages) * kLdsXStage; };
+  auto x_stage = [&](int s) { return s_x + (s % kXStages) * kLdsXStage; };
   // the tile kind of step s (0 for row-major W)
   // (Q64: the kind of slice s & 1 of the entry's two)
   auto kind_of = [&](uint32_t ent, int s) -> uint32_t {
@@ -627,7 +635,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   };
   // this wave's A fragments of step s (tile kind `kind`) from its stage
   auto read_a = [&](int s, uint32_t kind, u32x4 (&a0)[4], u32x4 (&a1)[4]) {
-    const uint8_t* ws = s_w + (s % kLdsStages) * kLdsWStage + 1024 * ((r * 8 + 4 * wn) * 2);
+    const uint8_t* ws = s_w + (s % kWStages) * kLdsWStage + 1024 * ((r * 8 + 4 * wn) * 2);
     const int off1 = kind ? 16 * (l >> 2) : 16 * l;
 #pragma unroll
     for (int b = 0; b < 4; b++) {
@@ -636,21 +644,29 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
     }
   };
 
-  // ---- pipeline: copies kLdsStages - 1 steps ahead; the fragments of step
-  // s + 1 are read from LDS while the last group of step s's matrix
-  // instructions runs, so a step starts with its first operands in registers
-  constexpr int kAhead = kLdsStages - 1;
+  // ---- pipeline: X copies kXStages - 1 steps ahead, W copies kWStages - 1;
+  // the fragments of step s + 1 are read from LDS while the last group of
+  // step s's matrix instructions runs, so a step starts with its first
+  // operands in registers
+  constexpr int kXAhead = kXStages - 1, kWAhead = kWStages - 1;
+  // Every advance issues X copies, then W copies (of the step kXAhead, resp.
+  // kWAhead, ahead); kLater = the copies issued after step s + 1's last one
+  // (step s + 2's), which may stay in flight at step s's barrier
+  constexpr int kLater = (kXAhead == 2 ? kXC : 0) + (kWAhead == 2 ? 4 : 0);
+  static_assert(kXAhead <= kWAhead && kWAhead <= 2 && kLater <= kLdsCopies, "copy pipeline");
   // called in step s (s + 1 < n_steps) once this wave's reads of stage s
   // are issued: step s + 1's copies have landed everywhere and nobody reads
-  // stage s any more, which the copies of step s + 1 + kAhead then refill
+  // stage s any more, which the copies of step s + 1 + kXAhead (X) and
+  // s + 1 + kWAhead (W) then refill
   auto advance = [&](int s, uint32_t e_copy) {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage s are done
-    if (kAhead == 2 && s + 2 < n_steps)
-      wait_copies<kLdsCopies>();  // step s + 2's copies may stay in flight
+    if (kLater > 0 && s + 2 < n_steps)
+      wait_copies<kLater>();  // step s + 2's copies may stay in flight
     else
       wait_copies<0>();
     wg_barrier();
-    if (s + 1 + kAhead < n_steps) issue(s + 1 + kAhead, e_copy);
+    if (s + 1 + kXAhead < n_steps) issue_x(s + 1 + kXAhead);
+    if (s + 1 + kWAhead < n_steps) issue_w(s + 1 + kWAhead, e_copy);
   };
 
   // packed W, step s: A fragments a0/a1 (kind), B group 0 in buffer par * G & 1
@@ -664,7 +680,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
     // step s + 1's entry (its kind: its fragments' addresses depend on it)
     // and that of the step whose copies this step issues, loaded now and
     // read after the step's barrier
-    const uint32_t nk_v = ent_v(s + 1), ecopy_v = ent_v(s + 1 + kAhead);
+    const uint32_t nk_v = ent_v(s + 1), ecopy_v = ent_v(s + 1 + kWAhead);
     if (!Q64 && kind == 2) {
       // 4:8: each band's sixteen columns rebuilt into a dense piece's two
       // halves (values in a0, the lane's masks in the codes chunk a1),
@@ -780,14 +796,18 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
     }
   };
 
+  // before step 0: the copies the advances of steps -kWAhead - 1 .. -2 would
+  // have issued (all exist: n_steps >= 2 >= kWAhead), then step 0's wait and
+  // barrier and what the advance of step -1 issues
 #pragma unroll
-  for (int s = 0; s < kAhead; s++) issue(s, ent_v(s));  // n_steps >= 2 >= kAhead
-  if (kAhead == 2)
-    wait_copies<kLdsCopies>();
-  else
-    wait_copies<0>();
+  for (int t = -(kWAhead + 1); t <= -2; t++) {
+    if (t + 1 + kXAhead >= 0) issue_x(t + 1 + kXAhead);
+    issue_w(t + 1 + kWAhead, ent_v(t + 1 + kWAhead));
+  }
+  wait_copies<kLater>();
   wg_barrier();
-  if (kAhead < n_steps) issue(kAhead, ent_v(kAhead));
+  if (kXAhead < n_steps) issue_x(kXAhead);
+  if (kWAhead < n_steps) issue_w(kWAhead, ent_v(kWAhead));
   u32x4 fa0[4], fa1[4], fb0[4], fb1[4];
   uint32_t ka = step_kind(0), kb;
   read_a(0, ka, fa0, fa1);
