@@ -201,3 +201,50 @@ def test_q64_unsupported_paths():
     rc = lib.patch_gemm_swiglu(ctypes.byref(pw.desc), pw.blob.data_ptr(), X.data_ptr(), 256, H.data_ptr(),
                                1, None, 0, 0, None)
     assert rc == 5  # PATCH_ERR_UNSUPPORTED
+
+
+def test_q64_deterministic_and_graph_replays_match_eager():
+    """64 x 64 tiles through decode, the split-K prefill and the unsplit
+    prefill: two eager runs are bitwise equal, and the same calls captured in
+    a HIP graph and replayed three times (eager work and synchronisations in
+    between) equal the eager results bit for bit."""
+    p = _problem("bf16", 512, 4096, 18)
+    pw, _ = _pack(p)
+    X4 = dev_bits(inputs.make_custom_x("bf16", 4, 4096, 21), "bf16")
+    X128 = dev_bits(inputs.make_custom_x("bf16", 128, 4096, 22), "bf16")
+    X600 = dev_bits(inputs.make_custom_x("bf16", 600, 4096, 23), "bf16")
+    outs = [torch.empty((4, 512), dtype=torch.bfloat16, device="cuda"),
+            torch.empty((128, 512), dtype=torch.float32, device="cuda"),
+            torch.empty((600, 512), dtype=torch.bfloat16, device="cuda")]
+
+    def run():
+        patch.gemm(X4, pw, out=outs[0])
+        patch.gemm(X128, pw, out_dtype=torch.float32, variant="prefill", out=outs[1])
+        patch.gemm(X600, pw, variant="prefill_w192_lds", out=outs[2], workspace=None)
+
+    run()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    run()
+    torch.cuda.synchronize()
+    for a, b in zip(outs, eager):
+        assert torch.equal(a, b), "repeat"
+    assert int(patch.load().patch_gemm_workspace_bytes(ctypes.byref(pw.desc), 128)) > 0  # the split path
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(7.0)
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, eager):
+            assert torch.equal(a, b), f"replay {rep}"
+        other = patch.gemm(X128, pw)  # eager work between replays
+        torch.cuda.synchronize()
+        assert other.shape == (128, 512)
