@@ -864,11 +864,14 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
 // range holds at least two tile columns, and the partial sums (ranges * M *
 // N * 4 bytes) stay within 2 * N * K bytes.  Then the number of M-groups:
 // each XCD (one L2) works on about 1/8 of the output blocks in the
-// group-major order.  Four groups (so an XCD holds some 2/8 of W's
-// row-blocks and 1/4 of X) measured fastest or within 2% of it on the
-// LLaMA-2 7B and 13B prefill shapes, against 3-10% slower with one group
-// (every XCD reading all of X); with fewer than 8 M-blocks, groups of at
-// least two M-blocks.
+// group-major order, i.e. on about (its share / M-blocks a group) row-block
+// pairs times the M-blocks of one group, and its L2 fetches that many pairs'
+// W and that many M-blocks' X.  Two groups come closest to the fewest bytes
+// for such a split on the LLaMA-2 7B prefill shapes (gate/up: ~10 pairs x 6
+// M-blocks an XCD; down: 8 pairs x 4 M-blocks), and measured as fast as four
+// (within 1% on the 7B and 13B prefill shapes) with 30-40% fewer bytes
+// fetched past the L2s; one group (every XCD reading all of X) was 3-10%
+// slower.  With fewer than 4 M-blocks, one group.
 struct PfShape {
   int bm, groups, splits, kt_split;
   bool lds;  // W and X staged through LDS (k_prefill_lds), else through registers (k_prefill)
@@ -905,7 +908,7 @@ static PfShape choose_shape_uncached(int64_t M, int64_t N, int64_t K, int cus, i
     }
   }
   const int64_t mblk = (M + best.bm - 1) / best.bm;
-  while (best.groups < 4 && 2 * best.groups * 2 <= mblk) best.groups *= 2;
+  while (best.groups < 2 && 2 * best.groups * 2 <= mblk) best.groups *= 2;
   return best;
 }
 
