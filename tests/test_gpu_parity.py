@@ -183,9 +183,10 @@ def test_decode_long_k(K):
 
 @pytest.mark.parametrize("M", [520, 1061, 1500])
 def test_prefill_m_groups(M):
-    """Prefill orders its output blocks by groups of M-blocks (2 to 4 groups
-    at these M, the last one short) over an odd number of row-blocks (a lone
-    middle row-block): every output against the oracle."""
+    """Prefill orders its output blocks by groups of M-blocks (two groups at
+    these M, the last one short when the M-blocks are odd) over an odd
+    number of row-blocks (a lone middle row-block): every output against the
+    oracle."""
     p = inputs.make_custom("bf16", 640, 384, 16, "bernoulli", 0.5, "uniform")
     pw, _ = _pack(p)
     Xb = inputs.make_custom_x("bf16", M, 384, 17)
