@@ -529,41 +529,55 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
 
   // this wave's kXC 8-row chunks of each X stage: rows 8 (kXC w + u) + l/8,
   // the lane fetching the source chunk whose swizzled position is l % 8;
-  // rows past M read row M - 1 (their outputs are never stored)
-  const uint16_t* xsrc[kXC];
+  // rows past M read row M - 1 (their outputs are never stored).  Lane byte
+  // offsets from row m0 of X (at most 256 K elements: 32 bits suffice).
+  const uint8_t* const xrow0 = reinterpret_cast<const uint8_t*>(P.X + (int64_t)m0 * K);
+  uint32_t xoff[kXC];
 #pragma unroll
   for (int u = 0; u < kXC; u++) {
     const int row = 8 * (kXC * w + u) + (l >> 3);
     const int gm = min(m0 + row, M - 1);
-    xsrc[u] = P.X + (int64_t)gm * K + 8 * ((l & 7) ^ swz_f(row));
+    xoff[u] = 2u * (uint32_t)((gm - m0) * K + 8 * ((l & 7) ^ swz_f(row)));
   }
   const uint32_t w_lds = lds_addr(s_w), x_lds = lds_addr(s_x);
+  // lane byte offsets of the W copies: a dense fragment half wm (or a 2:4
+  // band's values, wm = 0) 16 bytes a lane, a 2:4 band's codes 4 bytes a lane;
+  // row-major W: rows 64 wn + l % 16 (+ 16 b), columns 32 wm + 8 (l / 16) of
+  // the step's 64 from the row-block's first row (at most 128 K elements)
+  const uint32_t vw16 = 1024u * (uint32_t)wm + 16u * (uint32_t)l, vw4 = 4u * (uint32_t)l;
+  const uint32_t vrm = 2u * (uint32_t)((64 * wn + (l & 15)) * K + 32 * wm + 8 * hl);
+  const uint32_t vw16s[4] = {vw16, vw16, vw16, vw16}, vw4s[4] = {vw4, vw4, vw4, vw4};
+  const uint32_t vrms[4] = {vrm, vrm, vrm, vrm};
 
-  // the X copies of step s into X stage s % kXStages
-  auto issue_x = [&](int s) {
+  // the X copies of step s into X stage xst (= s % kXStages)
+  auto issue_x = [&](int s, int xst) {
     const int col = (j0 + (s >> 1)) * kTile + 64 * (s & 1);
-    const uint32_t xb = x_lds + (uint32_t)((s % kXStages) * kLdsXStage);
+    const uint8_t* const base = xrow0 + 2 * (int64_t)col;
+    const uint8_t* srcs[kXC];
 #pragma unroll
-    for (int u = 0; u < kXC; u++) dma16(xsrc[u] + col, xb + 1024u * (uint32_t)(kXC * w + u));
+    for (int u = 0; u < kXC; u++) srcs[u] = base;
+    dma_n<kXC, 1024, true>(srcs, xoff, x_lds + (uint32_t)(xst * kLdsXStage) + 1024u * (uint32_t)(kXC * w));
   };
-  // the W copies of step s into W stage s % kWStages; e_v: the tile entry of
-  // step s for this wave's row-block (a VGPR loaded from LDS earlier, so no
-  // LDS round trip sits between the step's barrier and its copies)
-  auto issue_w = [&](int s, uint32_t e_v) {
+  // the W copies of step s into W stage wst (= s % kWStages); e_v: the tile
+  // entry of step s for this wave's row-block (a VGPR loaded from LDS
+  // earlier, so no LDS round trip sits between the step's barrier and its
+  // copies)
+  auto issue_w = [&](int s, int wst, uint32_t e_v) {
     const int jl = s >> 1, h = s & 1, j = j0 + jl;
-    const uint32_t wb = w_lds + (uint32_t)((s % kWStages) * kLdsWStage);
+    const uint32_t wb = w_lds + (uint32_t)(wst * kLdsWStage);
     const int col = j * kTile + 64 * h;
     // fragment slot of band 4wn + b, half e of row-block r: ((r*8 + 4wn + b)*2 + e) KB
     const uint32_t slot0 = wb + 1024u * (uint32_t)((r * 8 + 4 * wn) * 2);
+    const uint8_t* srcs[4];
     if constexpr (SRC_ROWMAJOR) {
       // rows 16 (4wn + b) + l % 16 of row-block i_src, columns 64h + 32wm + 8(l/16) of tile j
       // (fused: row-block i_src/2 of the gate or the up matrix)
       const uint8_t* Wsrc = (FUSE && (i_src & 1)) ? P.src2 : P.src;
       const int ib = FUSE ? (i_src >> 1) : i_src;
-      const uint16_t* W = reinterpret_cast<const uint16_t*>(Wsrc) +
-                          ((int64_t)ib * kTile + 64 * wn + (l & 15)) * K + (int64_t)col + 32 * wm + 8 * hl;
+      const uint8_t* const base = Wsrc + 2 * ((int64_t)ib * kTile * K + col);
 #pragma unroll
-      for (int b = 0; b < 4; b++) dma16(W + (int64_t)16 * b * K, slot0 + 2048u * b + 1024u * wm);
+      for (int b = 0; b < 4; b++) srcs[b] = base + (int64_t)32 * b * K;
+      dma_n<4, 2048, true>(srcs, vrms, slot0 + 1024u * (uint32_t)wm);
     } else {
       const uint32_t e = (uint32_t)__builtin_amdgcn_readfirstlane((int)e_v);
       // the slice's kind, where its part starts in the band piece, where the codes are
@@ -578,17 +592,16 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
         part = sparse ? 1024u * h : 2048u * h;
         codes = kSparseMetaOffset;
       }
-      const uint8_t* piece = P.src + ((uint64_t)(e & 0x3fffffffu) << 8) + (Q64 ? 0 : (uint64_t)(4 * wn) * stride);
-      if (!sparse) {
+      const uint8_t* const piece = P.src + ((uint64_t)(e & 0x3fffffffu) << 8) + (Q64 ? 0 : (uint64_t)(4 * wn) * stride);
+      if (!sparse || wm == 0) {
+        // a dense fragment half wm, or a 2:4 band's values
 #pragma unroll
-        for (int b = 0; b < 4; b++)
-          dma16(piece + (uint64_t)b * stride + part + 1024 * wm + 16 * l, slot0 + 2048u * b + 1024u * wm);
-      } else if (wm == 0) {
-#pragma unroll
-        for (int b = 0; b < 4; b++) dma16(piece + (uint64_t)b * stride + part + 16 * l, slot0 + 2048u * b);
+        for (int b = 0; b < 4; b++) srcs[b] = piece + (uint64_t)b * stride + part;
+        dma_n<4, 2048, true>(srcs, vw16s, slot0 + 1024u * (uint32_t)wm);
       } else {
 #pragma unroll
-        for (int b = 0; b < 4; b++) dma4(piece + (uint64_t)b * stride + codes + 4 * l, slot0 + 2048u * b + 1024u);
+        for (int b = 0; b < 4; b++) srcs[b] = piece + (uint64_t)b * stride + codes;
+        dma_n<4, 2048, false>(srcs, vw4s, slot0 + 1024u);
       }
     }
   };
@@ -616,7 +629,10 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
     for (int mm = 0; mm < kRG; mm++)
       bf[mm] = *reinterpret_cast<const u32x4*>(xs + swz(wm * (BM / 2) + (kRG * part + mm) * 16 + (l & 15), 4 * qq + hl));
   };
-  auto x_stage = [&](int s) { return s_x + (s % kXStages) * kLdsXStage; };
+  auto x_stage = [&](int xi) { return s_x + xi * kLdsXStage; };
+  // stage indices of the next step
+  auto next_x = [](int xi) { return xi + 1 == kXStages ? 0 : xi + 1; };
+  auto next_w = [](int wi) { return wi + 1 == kWStages ? 0 : wi + 1; };
   // the tile kind of step s (0 for row-major W)
   // (Q64: the kind of slice s & 1 of the entry's two)
   auto kind_of = [&](uint32_t ent, int s) -> uint32_t {
@@ -633,14 +649,23 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
     if constexpr (SRC_ROWMAJOR) return 0u;
     return s_ent[er][min(s, n_steps - 1) >> 1];
   };
-  // this wave's A fragments of step s (tile kind `kind`) from its stage
-  auto read_a = [&](int s, uint32_t kind, u32x4 (&a0)[4], u32x4 (&a1)[4]) {
-    const uint8_t* ws = s_w + (s % kWStages) * kLdsWStage + 1024 * ((r * 8 + 4 * wn) * 2);
-    const int off1 = kind ? 16 * (l >> 2) : 16 * l;
+  // this wave's A fragments of a step in W stage wi, 64-column half h, tile
+  // kind `kind`: the first fragment a0 (a dense tile's first half, a 2:4 or
+  // 4:8 tile's values); cw = the lane's 16-bit half h of word l of the band's
+  // codes (mask) chunk, read whatever the kind (128 bytes a wave); a dense
+  // tile's second half a1 only for a dense tile (a1 is written on that path
+  // alone, so no wait for a read that did not happen lands on it)
+  auto read_a = [&](int wi, int h, uint32_t kind, u32x4 (&a0)[4], u32x4 (&a1)[4], uint32_t (&cw)[4]) {
+    const uint8_t* ws = s_w + wi * kLdsWStage + 1024 * ((r * 8 + 4 * wn) * 2);
 #pragma unroll
-    for (int b = 0; b < 4; b++) {
-      a0[b] = *reinterpret_cast<const u32x4*>(ws + 2048 * b + 16 * l);
-      a1[b] = *reinterpret_cast<const u32x4*>(ws + 2048 * b + 1024 + off1);
+    for (int b = 0; b < 4; b++) a0[b] = *reinterpret_cast<const u32x4*>(ws + 2048 * b + 16 * l);
+    if constexpr (!SRC_ROWMAJOR) {
+#pragma unroll
+      for (int b = 0; b < 4; b++) cw[b] = *reinterpret_cast<const uint16_t*>(ws + 2048 * b + 1024 + 4 * l + 2 * h);
+    }
+    if (kind == 0) {
+#pragma unroll
+      for (int b = 0; b < 4; b++) a1[b] = *reinterpret_cast<const u32x4*>(ws + 2048 * b + 1024 + 16 * l);
     }
   };
 
@@ -658,24 +683,25 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   // are issued: step s + 1's copies have landed everywhere and nobody reads
   // stage s any more, which the copies of step s + 1 + kXAhead (X) and
   // s + 1 + kWAhead (W) then refill
-  auto advance = [&](int s, uint32_t e_copy) {
+  // (xi, wi: the X and W stages of step s, which the copies refill)
+  auto advance = [&](int s, int xi, int wi, uint32_t e_copy) {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage s are done
     if (kLater > 0 && s + 2 < n_steps)
       wait_copies<kLater>();  // step s + 2's copies may stay in flight
     else
       wait_copies<0>();
     wg_barrier();
-    if (s + 1 + kXAhead < n_steps) issue_x(s + 1 + kXAhead);
-    if (s + 1 + kWAhead < n_steps) issue_w(s + 1 + kWAhead, e_copy);
+    if (s + 1 + kXAhead < n_steps) issue_x(s + 1 + kXAhead, xi);
+    if (s + 1 + kWAhead < n_steps) issue_w(s + 1 + kWAhead, wi, e_copy);
   };
 
   // packed W, step s: A fragments a0/a1 (kind), B group 0 in buffer par * G & 1
   // (the buffers alternate by group across steps; par = s & 1); reads step
   // s + 1's A fragments into na0/na1 and its B group 0 into the next buffer
   constexpr int kGroups = kNMB / kMG;
-  auto step_packed = [&](int s, int par, u32x4 (&a0)[4], u32x4 (&a1)[4], uint32_t kind, u32x4 (&na0)[4],
-                         u32x4 (&na1)[4], uint32_t& nkind, u32x4 (&blo)[2][kMG],
-                         u32x4 (&bhi)[2][kMG]) {
+  auto step_packed = [&](int s, int par, int xi, int wi, u32x4 (&a0)[4], u32x4 (&a1)[4], uint32_t (&cw)[4],
+                         uint32_t kind, u32x4 (&na0)[4], u32x4 (&na1)[4], uint32_t (&ncw)[4], uint32_t& nkind,
+                         u32x4 (&blo)[2][kMG], u32x4 (&bhi)[2][kMG]) {
     const int h = s & 1;
     // step s + 1's entry (its kind: its fragments' addresses depend on it)
     // and that of the step whose copies this step issues, loaded now and
@@ -686,27 +712,25 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
       // halves (values in a0, the lane's masks in the codes chunk a1),
       // then run as a dense tile
 #pragma unroll
-      for (int b = 0; b < 4; b++) {
-        const u32x4 mc = a1[b];
-        const uint32_t lo = (l & 1) ? mc[1] : mc[0], hi = (l & 1) ? mc[3] : mc[2];
-        dense_halves48(a0[b], (((l & 2) ? hi : lo) >> (16 * h)) & 0xffffu, s_sel, a0[b], a1[b]);
-      }
+      for (int b = 0; b < 4; b++) dense_halves48(a0[b], cw[b], s_sel, a0[b], a1[b]);
       kind = 0;
     }
     uint32_t idx0[4];
 #pragma unroll
-    for (int b = 0; b < 4; b++) {
-      const u32x4 mc = a1[b];
-      const uint32_t lo = (l & 1) ? mc[1] : mc[0], hi = (l & 1) ? mc[3] : mc[2];
-      idx0[b] = kind == 0 ? 0x4444u : (((l & 2) ? hi : lo) >> (16 * h));
-    }
-    const uint8_t* xs = x_stage(s);
+    for (int b = 0; b < 4; b++) idx0[b] = kind == 0 ? 0x4444u : cw[b];
+    const uint8_t* xs = x_stage(xi);
+    const int xn = next_x(xi), wn1 = next_w(wi);
 #pragma unroll
     for (int g = 0; g < kGroups; g++) {
       const int cb = (g + par * kGroups) & 1, nb = (g + 1 + par * kGroups) & 1;
       const bool last = g + 1 == kGroups;
-      if (last && s + 1 < n_steps) advance(s, ecopy_v);
-      if (last) nkind = kind_of((uint32_t)__builtin_amdgcn_readfirstlane((int)nk_v), s + 1);
+      if (last && s + 1 < n_steps) advance(s, xi, wi, ecopy_v);
+      if (last) {
+        nkind = kind_of((uint32_t)__builtin_amdgcn_readfirstlane((int)nk_v), s + 1);
+        // step s + 1's A fragments first: the next step waits for them
+        // (after the last step: a stage never used again)
+        read_a(wn1, h ^ 1, nkind, na0, na1, ncw);
+      }
       __builtin_amdgcn_sched_barrier(0);
       // the first half (a 2:4 tile's only one) with the next group's reads
       // -- or, in the last group, step s + 1's first fragments -- spread
@@ -720,13 +744,10 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
       if (!last) {
         read_b(xs, g + 1, blo[nb], bhi[nb]);
       } else {
-        // (after the last step: its own stage again, never used)
-        const int sn = min(s + 1, n_steps - 1);
-        read_a(sn, nkind, na0, na1);
-        read_b(x_stage(sn), 0, blo[nb], bhi[nb]);
+        read_b(x_stage(xn), 0, blo[nb], bhi[nb]);
       }
       constexpr int kMma = 4 * kMG;
-      constexpr int kPerMid = (2 * kMG + kMma - 1) / kMma, kPerLast = (8 + 2 * kMG + kMma - 1) / kMma;
+      constexpr int kPerMid = (2 * kMG + kMma - 1) / kMma, kPerLast = (2 * kMG + kMma - 1) / kMma;
       if (last) {
 #pragma unroll
         for (int i = 0; i < kMma; i++) {
@@ -755,14 +776,16 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   // row-major W (the dense baseline), step s: K halves qq = 0, 1 on
   // v_mfma_f32_16x16x32, in groups g = (qq, part) whose B fragments
   // alternate between bq[0] and bq[1] (an even number of groups a step)
-  auto step_rowmajor = [&](int s, u32x4 (&a0)[4], u32x4 (&a1)[4], u32x4 (&na0)[4], u32x4 (&na1)[4],
-                           u32x4 (&bq)[2][kRG]) {
-    const uint8_t* xs = x_stage(s);
+  auto step_rowmajor = [&](int s, int xi, int wi, u32x4 (&a0)[4], u32x4 (&a1)[4], u32x4 (&na0)[4],
+                           u32x4 (&na1)[4], u32x4 (&bq)[2][kRG]) {
+    const uint8_t* xs = x_stage(xi);
+    uint32_t cw_unused[4];
 #pragma unroll
     for (int g = 0; g < 2 * kRParts; g++) {
       const int qq = g / kRParts, part = g % kRParts;
       const bool last = g + 1 == 2 * kRParts;
-      if (last && s + 1 < n_steps) advance(s, 0u);
+      if (last && s + 1 < n_steps) advance(s, xi, wi, 0u);
+      if (last) read_a(next_w(wi), 0, 0u, na0, na1, cw_unused);  // step s + 1's A fragments first
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int mm = 0; mm < kRG; mm++)
@@ -772,13 +795,11 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
       if (!last) {
         read_bq(xs, (g + 1) / kRParts, (g + 1) % kRParts, bq[(g + 1) & 1]);
       } else {
-        const int sn = min(s + 1, n_steps - 1);
-        read_a(sn, 0u, na0, na1);
-        read_bq(x_stage(sn), 0, 0, bq[0]);
+        read_bq(x_stage(next_x(xi)), 0, 0, bq[0]);
       }
       // the reads spread between the matrix instructions
       constexpr int kMma = 4 * kRG;
-      constexpr int kPerMid = (kRG + kMma - 1) / kMma, kPerLast = (8 + kRG + kMma - 1) / kMma;
+      constexpr int kPerMid = (kRG + kMma - 1) / kMma, kPerLast = (kRG + kMma - 1) / kMma;
       if (last) {
 #pragma unroll
         for (int i = 0; i < kMma; i++) {
@@ -801,29 +822,36 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   // barrier and what the advance of step -1 issues
 #pragma unroll
   for (int t = -(kWAhead + 1); t <= -2; t++) {
-    if (t + 1 + kXAhead >= 0) issue_x(t + 1 + kXAhead);
-    issue_w(t + 1 + kWAhead, ent_v(t + 1 + kWAhead));
+    if (t + 1 + kXAhead >= 0) issue_x(t + 1 + kXAhead, (t + 1 + kXAhead) % kXStages);
+    issue_w(t + 1 + kWAhead, (t + 1 + kWAhead) % kWStages, ent_v(t + 1 + kWAhead));
   }
   wait_copies<kLater>();
   wg_barrier();
-  if (kXAhead < n_steps) issue_x(kXAhead);
-  if (kWAhead < n_steps) issue_w(kWAhead, ent_v(kWAhead));
+  if (kXAhead < n_steps) issue_x(kXAhead, kXAhead);
+  if (kWAhead < n_steps) issue_w(kWAhead, kWAhead, ent_v(kWAhead));
   u32x4 fa0[4], fa1[4], fb0[4], fb1[4];
+  uint32_t fac[4], fbc[4];
   uint32_t ka = step_kind(0), kb;
-  read_a(0, ka, fa0, fa1);
+  read_a(0, 0, ka, fa0, fa1, fac);
+  // stage indices of step s (X and W rings)
+  int xi = 0, wi = 0;
   if constexpr (SRC_ROWMAJOR) {
     u32x4 bq[2][kRG];
     read_bq(x_stage(0), 0, 0, bq[0]);
     for (int s = 0; s < n_steps; s += 2) {  // n_steps is even
-      step_rowmajor(s, fa0, fa1, fb0, fb1, bq);
-      step_rowmajor(s + 1, fb0, fb1, fa0, fa1, bq);
+      step_rowmajor(s, xi, wi, fa0, fa1, fb0, fb1, bq);
+      xi = next_x(xi), wi = next_w(wi);
+      step_rowmajor(s + 1, xi, wi, fb0, fb1, fa0, fa1, bq);
+      xi = next_x(xi), wi = next_w(wi);
     }
   } else {
     u32x4 blo[2][kMG], bhi[2][kMG];
     read_b(x_stage(0), 0, blo[0], bhi[0]);
     for (int s = 0; s < n_steps; s += 2) {  // n_steps is even
-      step_packed(s, 0, fa0, fa1, ka, fb0, fb1, kb, blo, bhi);
-      step_packed(s + 1, 1, fb0, fb1, kb, fa0, fa1, ka, blo, bhi);
+      step_packed(s, 0, xi, wi, fa0, fa1, fac, ka, fb0, fb1, fbc, kb, blo, bhi);
+      xi = next_x(xi), wi = next_w(wi);
+      step_packed(s + 1, 1, xi, wi, fb0, fb1, fbc, kb, fa0, fa1, fac, ka, blo, bhi);
+      xi = next_x(xi), wi = next_w(wi);
     }
   }
 

@@ -72,6 +72,85 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
       : "s"(lds), "v"(g)
       : "memory");
 }
+// N copies global -> LDS issued back to back in one block (M0 saved once):
+// copy k moves lane l's 16 bytes (W16) or 4 bytes from the global address
+// src[k] + voff[k] (src[k] wave-uniform, in SGPRs; voff[k] the lane's byte
+// offset) to LDS byte lds + k * LS + 16 l (4 l).  The address arithmetic
+// stays scalar: one 64-bit scalar add per copy where a per-lane pointer
+// would cost two vector adds.  M0 is only ever moved into (s_mov leaves
+// SCC alone, which the compiler may keep live across the block).
+template <int N, int LS, bool W16>
+__device__ __forceinline__ void dma_n(const uint8_t* const (&src)[N], const uint32_t (&voff)[N], uint32_t lds) {
+  static_assert(N >= 1 && N <= 4, "1 to 4 copies");
+  const uint32_t m1 = lds + (uint32_t)LS, m2 = lds + 2u * (uint32_t)LS, m3 = lds + 3u * (uint32_t)LS;
+  uint32_t saved;
+  if constexpr (N == 1) {
+    if constexpr (W16)
+      asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+                   : "=&s"(saved) : "s"(lds), "v"(voff[0]), "s"(src[0]) : "memory");
+    else
+      asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
+                   : "=&s"(saved) : "s"(lds), "v"(voff[0]), "s"(src[0]) : "memory");
+  } else if constexpr (N == 2) {
+    if constexpr (W16)
+      asm volatile(
+          "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\t"
+          "global_load_lds_dwordx4 %3, %5\n\ts_mov_b32 m0, %2\n\t"
+          "global_load_lds_dwordx4 %4, %6\n\ts_mov_b32 m0, %0"
+          : "=&s"(saved) : "s"(lds), "s"(m1), "v"(voff[0]), "v"(voff[1]), "s"(src[0]), "s"(src[1]) : "memory");
+    else
+      asm volatile(
+          "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\t"
+          "global_load_lds_dword %3, %5\n\ts_mov_b32 m0, %2\n\t"
+          "global_load_lds_dword %4, %6\n\ts_mov_b32 m0, %0"
+          : "=&s"(saved) : "s"(lds), "s"(m1), "v"(voff[0]), "v"(voff[1]), "s"(src[0]), "s"(src[1]) : "memory");
+  } else if constexpr (N == 3) {
+    if constexpr (W16)
+      asm volatile(
+          "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\t"
+          "global_load_lds_dwordx4 %4, %7\n\ts_mov_b32 m0, %2\n\t"
+          "global_load_lds_dwordx4 %5, %8\n\ts_mov_b32 m0, %3\n\t"
+          "global_load_lds_dwordx4 %6, %9\n\ts_mov_b32 m0, %0"
+          : "=&s"(saved)
+          : "s"(lds), "s"(m1), "s"(m2), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "s"(src[0]), "s"(src[1]),
+            "s"(src[2])
+          : "memory");
+    else
+      asm volatile(
+          "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\t"
+          "global_load_lds_dword %4, %7\n\ts_mov_b32 m0, %2\n\t"
+          "global_load_lds_dword %5, %8\n\ts_mov_b32 m0, %3\n\t"
+          "global_load_lds_dword %6, %9\n\ts_mov_b32 m0, %0"
+          : "=&s"(saved)
+          : "s"(lds), "s"(m1), "s"(m2), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "s"(src[0]), "s"(src[1]),
+            "s"(src[2])
+          : "memory");
+  } else {
+    if constexpr (W16)
+      asm volatile(
+          "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\t"
+          "global_load_lds_dwordx4 %5, %9\n\ts_mov_b32 m0, %2\n\t"
+          "global_load_lds_dwordx4 %6, %10\n\ts_mov_b32 m0, %3\n\t"
+          "global_load_lds_dwordx4 %7, %11\n\ts_mov_b32 m0, %4\n\t"
+          "global_load_lds_dwordx4 %8, %12\n\ts_mov_b32 m0, %0"
+          : "=&s"(saved)
+          : "s"(lds), "s"(m1), "s"(m2), "s"(m3), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]),
+            "s"(src[0]), "s"(src[1]), "s"(src[2]), "s"(src[3])
+          : "memory");
+    else
+      asm volatile(
+          "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\t"
+          "global_load_lds_dword %5, %9\n\ts_mov_b32 m0, %2\n\t"
+          "global_load_lds_dword %6, %10\n\ts_mov_b32 m0, %3\n\t"
+          "global_load_lds_dword %7, %11\n\ts_mov_b32 m0, %4\n\t"
+          "global_load_lds_dword %8, %12\n\ts_mov_b32 m0, %0"
+          : "=&s"(saved)
+          : "s"(lds), "s"(m1), "s"(m2), "s"(m3), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]),
+            "s"(src[0]), "s"(src[1]), "s"(src[2]), "s"(src[3])
+          : "memory");
+  }
+}
+
 template <int N>
 __device__ __forceinline__ void wait_copies() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
