@@ -407,25 +407,28 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
 //     a lane, straight into LDS, no registers): BM/64 8-row chunks of the X
 //     stage and four W fragments -- wave (r, wn, wm) copies half wm of bands
 //     4wn..4wn+3 of row-block r (a 2:4 tile: the values if wm = 0, the
-//     band's codes if wm = 1), so each W byte enters the CU once, where the
-//     register-staged kernel loads every W fragment into both M-halves' waves.
+//     band's codes, 4 bytes a lane, if wm = 1), so each W byte enters the CU
+//     once, where the register-staged kernel loads every W fragment into
+//     both M-halves' waves.  A step's copies go out as a few blocks of
+//     back-to-back copies whose addresses are scalar (one scalar add a copy).
 //   * Copies for the later steps go out while step s computes; a wave waits
 //     for its own copies of step s with vmcnt (the copies of the next step
 //     may stay in flight) and the barrier after it publishes everyone's.  The
 //     copies are inline asm, so the compiler neither waits for them nor for
 //     anything else before LDS reads; the wait counts are exact because every
 //     wave issues the same copies every step.
-//   * Fragments are then read from LDS with one 16-byte read a lane (the
-//     2:4 codes chunk holding the lane's word likewise) and fed to the same
-//     v_smfmac_f32_16x16x64 sequence as the register-staged kernel.  The
-//     barrier of step s + 1 sits before the last group of step s's matrix
-//     instructions, and step s + 1's A fragments and first B fragments are
-//     read right after it, so those reads run under that group and a step
-//     starts with operands in registers (two sets of A fragments; B
-//     fragments alternate between two buffers by group).  Within a group
-//     the next group's reads are spread between the matrix instructions
-//     (one or two after each), so the waves sharing a SIMD do not all
-//     queue at the LDS and then all at the matrix core.
+//   * Fragments are then read from LDS with one 16-byte read a lane (a 2:4
+//     or 4:8 tile's codes: one 16-bit read a lane, its half of its word) and
+//     fed to the same v_smfmac_f32_16x16x64 sequence as the register-staged
+//     kernel.  The barrier of step s + 1 sits before the last group of step
+//     s's matrix instructions; right after it each wave reads step s + 1's
+//     A fragments and first B fragments, then issues its copies, then runs
+//     that group, so the reads the next step waits for go out first and run
+//     under the group (two sets of A fragments; B fragments alternate
+//     between two buffers by group).  Within the other groups the next
+//     group's reads are spread between the matrix instructions (one or two
+//     after each), so the waves sharing a SIMD do not all queue at the LDS
+//     and then all at the matrix core.
 // LDS per stage: 32 KB of W + BM * 128 bytes of X; three stages up to width
 // 128 (120 KB at 64, 144 KB at 128), two at 192 and 256 (112 and 128 KB),
 // plus the tile entries and, for packed W, the 4 KB table that rebuilds 4:8
@@ -437,7 +440,8 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill(PfArgs P) {
 // ---------------------------------------------------------------------------
 constexpr int kLdsWStage = 32768;  // 2 row-blocks x 8 bands x 2 fragments of 1 KB
 // stages of the LDS ring for an M-block width: three up to 128, two at 192
-// and 256 (a third would not fit the 160 KB of LDS)
+// and 256 (a third would not fit the 160 KB of LDS; at 192 three X stages
+// beside two W stages measured 2-4% slower than two beside three)
 constexpr int lds_stages(int bm) { return bm <= 128 ? 3 : 2; }
 // W stages: three also at width 192 (two X stages of 24 KB beside three W
 // stages of 32 KB and 8 KB of tile entries fill the 160 KB exactly; not with
@@ -674,25 +678,32 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   // step s's matrix instructions runs, so a step starts with its first
   // operands in registers
   constexpr int kXAhead = kXStages - 1, kWAhead = kWStages - 1;
-  // Every advance issues X copies, then W copies (of the step kXAhead, resp.
-  // kWAhead, ahead); kLater = the copies issued after step s + 1's last one
-  // (step s + 2's), which may stay in flight at step s's barrier
+  constexpr int kAhead = kXAhead > kWAhead ? kXAhead : kWAhead;
+  // Every advance issues the copies of the ring that runs fewer steps ahead
+  // first (X, also when both run as far), then the other's; kLater = the
+  // copies issued after step s + 1's last one (step s + 2's), which may stay
+  // in flight at step s's barrier
+  constexpr bool kXFirst = kXAhead <= kWAhead;
   constexpr int kLater = (kXAhead == 2 ? kXC : 0) + (kWAhead == 2 ? 4 : 0);
-  static_assert(kXAhead <= kWAhead && kWAhead <= 2 && kLater <= kLdsCopies, "copy pipeline");
+  static_assert(kXAhead >= 1 && kWAhead >= 1 && kAhead <= 2 && kLater <= kLdsCopies, "copy pipeline");
   // called in step s (s + 1 < n_steps) once this wave's reads of stage s
   // are issued: step s + 1's copies have landed everywhere and nobody reads
   // stage s any more, which the copies of step s + 1 + kXAhead (X) and
   // s + 1 + kWAhead (W) then refill
   // (xi, wi: the X and W stages of step s, which the copies refill)
-  auto advance = [&](int s, int xi, int wi, uint32_t e_copy) {
+  // advance_wait: the wait and the barrier; advance_issue: the copies
+  auto advance_wait = [&](int s) {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage s are done
     if (kLater > 0 && s + 2 < n_steps)
       wait_copies<kLater>();  // step s + 2's copies may stay in flight
     else
       wait_copies<0>();
     wg_barrier();
-    if (s + 1 + kXAhead < n_steps) issue_x(s + 1 + kXAhead, xi);
+  };
+  auto advance_issue = [&](int s, int xi, int wi, uint32_t e_copy) {
+    if (kXFirst && s + 1 + kXAhead < n_steps) issue_x(s + 1 + kXAhead, xi);
     if (s + 1 + kWAhead < n_steps) issue_w(s + 1 + kWAhead, wi, e_copy);
+    if (!kXFirst && s + 1 + kXAhead < n_steps) issue_x(s + 1 + kXAhead, xi);
   };
 
   // packed W, step s: A fragments a0/a1 (kind), B group 0 in buffer par * G & 1
@@ -724,13 +735,16 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
     for (int g = 0; g < kGroups; g++) {
       const int cb = (g + par * kGroups) & 1, nb = (g + 1 + par * kGroups) & 1;
       const bool last = g + 1 == kGroups;
-      if (last && s + 1 < n_steps) advance(s, xi, wi, ecopy_v);
+      if (last && s + 1 < n_steps) advance_wait(s);
       if (last) {
+        // step s + 1's A fragments and first B fragments right after the
+        // barrier, before this step's copies go out: the next step waits
+        // for them (after the last step: a stage never used again)
         nkind = kind_of((uint32_t)__builtin_amdgcn_readfirstlane((int)nk_v), s + 1);
-        // step s + 1's A fragments first: the next step waits for them
-        // (after the last step: a stage never used again)
         read_a(wn1, h ^ 1, nkind, na0, na1, ncw);
+        read_b(x_stage(xn), 0, blo[nb], bhi[nb]);
       }
+      if (last && s + 1 < n_steps) advance_issue(s, xi, wi, ecopy_v);
       __builtin_amdgcn_sched_barrier(0);
       // the first half (a 2:4 tile's only one) with the next group's reads
       // -- or, in the last group, step s + 1's first fragments -- spread
@@ -741,11 +755,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
 #pragma unroll
         for (int b = 0; b < 4; b++)
           acc[b][kMG * g + mm] = mma_sparse<BF16, 0>(a0[b], blo[cb][mm], bhi[cb][mm], acc[b][kMG * g + mm], idx0[b]);
-      if (!last) {
-        read_b(xs, g + 1, blo[nb], bhi[nb]);
-      } else {
-        read_b(x_stage(xn), 0, blo[nb], bhi[nb]);
-      }
+      if (!last) read_b(xs, g + 1, blo[nb], bhi[nb]);
       constexpr int kMma = 4 * kMG;
       constexpr int kPerMid = (2 * kMG + kMma - 1) / kMma, kPerLast = (2 * kMG + kMma - 1) / kMma;
       if (last) {
@@ -784,7 +794,10 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
     for (int g = 0; g < 2 * kRParts; g++) {
       const int qq = g / kRParts, part = g % kRParts;
       const bool last = g + 1 == 2 * kRParts;
-      if (last && s + 1 < n_steps) advance(s, xi, wi, 0u);
+      if (last && s + 1 < n_steps) {
+        advance_wait(s);
+        advance_issue(s, xi, wi, 0u);
+      }
       if (last) read_a(next_w(wi), 0, 0u, na0, na1, cw_unused);  // step s + 1's A fragments first
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -817,18 +830,20 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
     }
   };
 
-  // before step 0: the copies the advances of steps -kWAhead - 1 .. -2 would
-  // have issued (all exist: n_steps >= 2 >= kWAhead), then step 0's wait and
+  // before step 0: the copies the advances of steps -kAhead - 1 .. -2 would
+  // have issued (all exist: n_steps >= 2 >= kAhead), then step 0's wait and
   // barrier and what the advance of step -1 issues
 #pragma unroll
-  for (int t = -(kWAhead + 1); t <= -2; t++) {
-    if (t + 1 + kXAhead >= 0) issue_x(t + 1 + kXAhead, (t + 1 + kXAhead) % kXStages);
-    issue_w(t + 1 + kWAhead, (t + 1 + kWAhead) % kWStages, ent_v(t + 1 + kWAhead));
+  for (int t = -(kAhead + 1); t <= -2; t++) {
+    if (kXFirst && t + 1 + kXAhead >= 0) issue_x(t + 1 + kXAhead, (t + 1 + kXAhead) % kXStages);
+    if (t + 1 + kWAhead >= 0) issue_w(t + 1 + kWAhead, (t + 1 + kWAhead) % kWStages, ent_v(t + 1 + kWAhead));
+    if (!kXFirst && t + 1 + kXAhead >= 0) issue_x(t + 1 + kXAhead, (t + 1 + kXAhead) % kXStages);
   }
   wait_copies<kLater>();
   wg_barrier();
-  if (kXAhead < n_steps) issue_x(kXAhead, kXAhead);
+  if (kXFirst && kXAhead < n_steps) issue_x(kXAhead, kXAhead);
   if (kWAhead < n_steps) issue_w(kWAhead, kWAhead, ent_v(kWAhead));
+  if (!kXFirst && kXAhead < n_steps) issue_x(kXAhead, kXAhead);
   u32x4 fa0[4], fa1[4], fb0[4], fb1[4];
   uint32_t fac[4], fbc[4];
   uint32_t ka = step_kind(0), kb;
