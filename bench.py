@@ -520,10 +520,36 @@ def measure_ceilings(read_bytes, steps=20):
         b = _event()
         torch.cuda.synchronize()
         out["matrix_core_tflops"][name] = flops / (a.elapsed_time(b) * 1e-3) / 1e12
+    # global -> LDS copies (the prefill kernels' copy instruction and ring), one
+    # workgroup of 8 waves a CU: 16 windows of 256 KB (held by the L2s after
+    # the first pass) and one 512 KB window a workgroup (128 MB in all: past
+    # the L2s, Infinity Cache resident)
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    src = torch.ones(256 * (512 << 10), dtype=torch.uint8, device="cuda")
+    out["lds_copy_tbs"] = {}
+    for name, nbytes, win, iters in (("l2_resident", 16 * (256 << 10), 256 << 10, 3000),
+                                     ("past_l2", 256 * (512 << 10), 512 << 10, 3000)):
+        view = src[:nbytes]
+        patch.probe_copy_rate(view, win, 10, ncu, sink)  # warm-up (and first touch)
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(3):
+            a = _event()
+            nb = patch.probe_copy_rate(view, win, iters, ncu, sink)
+            b = _event()
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) * 1e-3
+            best = t if best is None or t < best else best
+        out["lds_copy_tbs"][name] = nb / best / 1e12
+    del src
+    torch.cuda.empty_cache()
     out["note"] = ("hbm_read: patch_probe_stream_read over that many bytes (16-byte loads, one pass), median of 3 "
                    "graph replays of 20 launches on rotated buffers; matrix_core_tflops: patch_probe_matrix_rate, "
                    "2 workgroups of 4 waves a CU, independent accumulator chains, dense-equivalent flops for the "
-                   "sparse instructions; datasheet peaks: 8000 GB/s, 2516.6 TFLOP/s dense bf16 (x2 with 2:4)")
+                   "sparse instructions; lds_copy_tbs: patch_probe_copy_rate (global -> LDS with the prefill "
+                   "kernels' copy instruction, 8 waves a CU, 7 KB a wave per iteration, two-slot ring), L2-resident "
+                   "windows and windows past the L2s, best of 3; datasheet peaks: 8000 GB/s, 2516.6 TFLOP/s dense "
+                   "bf16 (x2 with 2:4)")
     return out
 
 

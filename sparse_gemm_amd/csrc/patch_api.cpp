@@ -32,6 +32,9 @@ hipError_t launch_apply_fine_mask(int64_t N, int64_t K, int b1, int b2, const vo
 hipError_t launch_probe_read(const void* src, uint64_t bytes, void* sink, uint64_t sink_bytes, hipStream_t s);
 hipError_t launch_probe_mma(int kind, int iters, int workgroups, void* sink, hipStream_t s);
 uint64_t probe_mma_flops(int kind, int iters, int workgroups);
+hipError_t launch_probe_copy(const void* src, uint64_t src_bytes, uint64_t window, int iters, int workgroups,
+                             void* sink, hipStream_t s);
+uint64_t probe_copy_bytes(int iters, int workgroups);
 }  // namespace patch
 
 namespace {
@@ -251,6 +254,24 @@ patch_status patch_probe_stream_read(const void* src_dev, uint64_t bytes, void* 
   hipError_t e = patch::launch_probe_read(src_dev, bytes, sink_dev, sink_bytes, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "launch stream-read probe");
   return PATCH_OK;
+}
+
+patch_status patch_probe_copy_rate(const void* src_dev, uint64_t src_bytes, uint64_t window_bytes, int32_t iters,
+                                   int32_t workgroups, void* sink_dev, uint64_t sink_bytes, void* stream) {
+  if (!src_dev || !sink_dev || !aligned16(src_dev) || iters < 1 || workgroups < 1)
+    return fail(PATCH_ERR_INVALID_ARG, "probe_copy_rate: null or unaligned pointer, iters or workgroups < 1");
+  if (window_bytes < 1024 || window_bytes % 1024 || src_bytes < window_bytes || src_bytes % window_bytes)
+    return fail(PATCH_ERR_INVALID_ARG, "probe_copy_rate: window must be a positive multiple of 1 KB dividing src_bytes");
+  if (sink_bytes < 4ull * (uint64_t)workgroups) return fail(PATCH_ERR_INVALID_ARG, "probe_copy_rate: sink too small");
+  hipError_t e = patch::launch_probe_copy(src_dev, src_bytes, window_bytes, iters, workgroups, sink_dev,
+                                          reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "launch copy probe");
+  return PATCH_OK;
+}
+
+uint64_t patch_probe_copy_bytes(int32_t iters, int32_t workgroups) {
+  if (iters < 1 || workgroups < 1) return 0;
+  return patch::probe_copy_bytes(iters, workgroups);
 }
 
 uint64_t patch_probe_matrix_flops(int32_t kind, int32_t iters, int32_t workgroups) {

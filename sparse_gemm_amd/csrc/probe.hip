@@ -4,6 +4,7 @@
 // of a given size can reach is lower and is what these kernels measure).
 // They compute nothing of the method and are not called by the GEMM path.
 #include "device_common.h"
+#include "prefill_common.h"
 
 namespace patch {
 
@@ -102,6 +103,48 @@ __global__ __launch_bounds__(256) void k_probe_mma(int iters, float* __restrict_
       for (int c = 0; c < 16; c++) s += acc[j][c];
   }
   if (s == 1234.5f) sink[blockIdx.x] = s;
+}
+
+// Global -> LDS copy rate with the copy instruction the prefill kernels use:
+// 8 waves a workgroup, each issuing 7 copies of 1 KB an iteration (16 bytes a
+// lane) into one of two LDS slots, waiting for the previous iteration's
+// copies (vmcnt) and meeting at a barrier, as the prefill kernels' copy ring
+// does.  Workgroup g copies from its window of `window` bytes at offset
+// (g * window) mod src_bytes, cycling through it: a few windows in all stay
+// in the L2s after the first pass, windows that add up to more than the L2s
+// are served from past them.  The LDS is read once at the end (a word
+// stored only if it equals a constant), so the copies cannot be dropped.
+constexpr int kProbeCopies = 7;
+__global__ __launch_bounds__(512) void k_probe_copy(const uint8_t* __restrict__ src, int64_t src_bytes,
+                                                    int64_t window, int iters, uint32_t* __restrict__ sink) {
+  __shared__ __attribute__((aligned(1024))) uint8_t buf[2 * kProbeCopies * 8 * 1024];
+  const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const uint8_t* win = src + ((int64_t)blockIdx.x * window) % src_bytes;
+  const uint32_t base = lds_addr(buf);
+  for (int it = 0; it < iters; it++) {
+    const uint32_t slot = base + (uint32_t)((it & 1) * kProbeCopies * 8 * 1024);
+#pragma unroll
+    for (int j = 0; j < kProbeCopies; j++) {
+      const int64_t c = ((int64_t)it * kProbeCopies + j) * 8 + w;
+      dma16(win + (c * 1024) % window + 16 * l, slot + (uint32_t)((j * 8 + w) * 1024));
+    }
+    wait_copies<kProbeCopies>();  // the previous iteration's copies have landed
+    wg_barrier();
+  }
+  wait_copies<0>();
+  __syncthreads();
+  if (buf[threadIdx.x] == 0x77 && buf[threadIdx.x + 1] == 0x78) sink[blockIdx.x] = 1u;
+}
+
+uint64_t probe_copy_bytes(int iters, int workgroups) {
+  return (uint64_t)kProbeCopies * 8u * 1024u * (uint64_t)iters * (uint64_t)workgroups;
+}
+
+hipError_t launch_probe_copy(const void* src, uint64_t src_bytes, uint64_t window, int iters, int workgroups,
+                             void* sink, hipStream_t s) {
+  hipLaunchKernelGGL(k_probe_copy, dim3((unsigned)workgroups), dim3(512), 0, s, reinterpret_cast<const uint8_t*>(src),
+                     (int64_t)src_bytes, (int64_t)window, iters, reinterpret_cast<uint32_t*>(sink));
+  return hipGetLastError();
 }
 
 // Flops (dense-equivalent for the sparse instructions) one launch executes.

@@ -51,7 +51,7 @@ EXPORTS = ("patch_abi_version", "patch_packed_bytes", "patch_pack", "patch_packe
            "patch_dense_gemm", "patch_dense_gemm_ex", "patch_packed_bytes_gate_up", "patch_pack_gate_up",
            "patch_gemm_swiglu_workspace_bytes", "patch_gemm_swiglu", "patch_dense_gemm_swiglu_workspace_bytes",
            "patch_dense_gemm_swiglu", "patch_packed_bytes_concat", "patch_pack_concat", "patch_sample_mask",
-           "patch_exec_tile_map", "patch_apply_fine_mask", "patch_probe_stream_read", "patch_probe_matrix_rate",
+           "patch_exec_tile_map", "patch_apply_fine_mask", "patch_probe_stream_read", "patch_probe_matrix_rate", "patch_probe_copy_rate", "patch_probe_copy_bytes",
            "patch_probe_matrix_flops", "patch_noalloc_scratch_bytes", "patch_gemm_noalloc", "patch_status_string",
            "patch_last_error")
 
@@ -120,6 +120,10 @@ def load():
     lib.patch_probe_matrix_rate.restype = ctypes.c_int
     lib.patch_probe_matrix_flops.argtypes = [I32, I32, I32]
     lib.patch_probe_matrix_flops.restype = U64
+    lib.patch_probe_copy_rate.argtypes = [P, U64, U64, I32, I32, P, U64, P]
+    lib.patch_probe_copy_rate.restype = ctypes.c_int
+    lib.patch_probe_copy_bytes.argtypes = [I32, I32]
+    lib.patch_probe_copy_bytes.restype = U64
     lib.patch_noalloc_scratch_bytes.argtypes = []
     lib.patch_noalloc_scratch_bytes.restype = U64
     lib.patch_gemm_noalloc.argtypes = [DP, P, P, I64, P, ctypes.c_int, P]
@@ -600,3 +604,14 @@ def probe_matrix_rate(kind: int, iters: int, workgroups: int, sink: torch.Tensor
     lib = load()
     _check(lib.patch_probe_matrix_rate(kind, iters, workgroups, _ptr(sink), _stream(sink.device.index)))
     return int(lib.patch_probe_matrix_flops(kind, iters, workgroups))
+
+
+def probe_copy_rate(src: torch.Tensor, window_bytes: int, iters: int, workgroups: int, sink: torch.Tensor) -> int:
+    """Launch the global -> LDS copy-rate probe (patch_probe_copy_rate) over
+    src (its size a multiple of window_bytes); returns the bytes it copies."""
+    _check_dev(src, "src")
+    _check_dev(sink, "sink")
+    lib = load()
+    _check(lib.patch_probe_copy_rate(_ptr(src), src.numel() * src.element_size(), window_bytes, iters, workgroups,
+                                     _ptr(sink), sink.numel() * sink.element_size(), _stream(src.device.index)))
+    return int(lib.patch_probe_copy_bytes(iters, workgroups))

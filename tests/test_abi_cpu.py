@@ -276,3 +276,26 @@ def test_desc_from_oracle_q64_header_and_gemm_checks():
     d.n_48 = 1
     assert patch.STATUS[lib.patch_gemm(ctypes.byref(d), V(16), V(16), 4, V(16), 1, None, 0,
                                        None)] == "PATCH_ERR_INVALID_ARG"
+
+
+def test_probe_copy_rate_host_checks():
+    """The global -> LDS copy probe: its byte count in closed form (7 copies of
+    1 KB a wave, 8 waves a workgroup, per iteration) and every argument check
+    taken before any launch."""
+    lib = patch.load()
+    V = ctypes.c_void_p
+    assert lib.patch_probe_copy_bytes(3, 5) == 7 * 8 * 1024 * 3 * 5
+    assert lib.patch_probe_copy_bytes(0, 5) == 0 and lib.patch_probe_copy_bytes(3, 0) == 0
+    bad = [
+        (None, 1 << 20, 1 << 18, 10, 4, V(16), 64),        # null source
+        (V(16), 1 << 20, 1 << 18, 10, 4, None, 64),        # null sink
+        (V(24), 1 << 20, 1 << 18, 10, 4, V(16), 64),       # unaligned source
+        (V(16), 1 << 20, 1000, 10, 4, V(16), 64),          # window not a multiple of 1 KB
+        (V(16), 3 << 18, 1 << 19, 10, 4, V(16), 64),       # window does not divide the source
+        (V(16), 1 << 20, 1 << 21, 10, 4, V(16), 64),       # window larger than the source
+        (V(16), 1 << 20, 1 << 18, 0, 4, V(16), 64),        # no iterations
+        (V(16), 1 << 20, 1 << 18, 10, 0, V(16), 64),       # no workgroups
+        (V(16), 1 << 20, 1 << 18, 10, 32, V(16), 64),      # sink smaller than 4 bytes a workgroup
+    ]
+    for args in bad:
+        assert patch.STATUS[lib.patch_probe_copy_rate(*args, None)] == "PATCH_ERR_INVALID_ARG", args
