@@ -432,15 +432,16 @@ patch_status patch_gemm_noalloc(const patch_packed_desc* desc, const void* packe
  * copy instruction (global_load_lds, 16 bytes a lane): `workgroups`
  * workgroups of 8 waves, each wave copying 7 KB an iteration for `iters`
  * iterations into a two-slot LDS ring (wait for the previous iteration's
- * copies, then a barrier).  Workgroup g reads its window of window_bytes at
- * offset (g * window_bytes) mod src_bytes of src_dev, cycling through it:
- * few distinct windows (src_bytes within the L2s) measure copies from L2,
- * windows adding up to more than the L2s copies from past them.  sink_dev:
+ * copies, then a barrier).  Workgroup g reads its window of window_bytes (a
+ * power of two) at offset (g * window_bytes) mod src_bytes of src_dev,
+ * cycling through it: few distinct windows (src_bytes within the L2s)
+ * measure copies from L2, windows adding up to more than the L2s copies
+ * from past them.  sink_dev:
  * scratch of at least 4 * workgroups bytes.  patch_probe_copy_bytes returns
  * the bytes one launch copies (0 for bad arguments).  Errors:
  * PATCH_ERR_INVALID_ARG (null or unaligned pointers, iters or workgroups <
- * 1, window_bytes not a positive multiple of 1024 dividing src_bytes, sink
- * too small).
+ * 1, window_bytes not a power of two of at least 1024 dividing src_bytes,
+ * sink too small).
  */
 patch_status patch_probe_stream_read(const void* src_dev, uint64_t bytes, void* sink_dev, uint64_t sink_bytes,
                                      void* stream);

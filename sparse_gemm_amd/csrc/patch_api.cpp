@@ -260,8 +260,9 @@ patch_status patch_probe_copy_rate(const void* src_dev, uint64_t src_bytes, uint
                                    int32_t workgroups, void* sink_dev, uint64_t sink_bytes, void* stream) {
   if (!src_dev || !sink_dev || !aligned16(src_dev) || iters < 1 || workgroups < 1)
     return fail(PATCH_ERR_INVALID_ARG, "probe_copy_rate: null or unaligned pointer, iters or workgroups < 1");
-  if (window_bytes < 1024 || window_bytes % 1024 || src_bytes < window_bytes || src_bytes % window_bytes)
-    return fail(PATCH_ERR_INVALID_ARG, "probe_copy_rate: window must be a positive multiple of 1 KB dividing src_bytes");
+  if (window_bytes < 1024 || (window_bytes & (window_bytes - 1)) || src_bytes < window_bytes ||
+      src_bytes % window_bytes)
+    return fail(PATCH_ERR_INVALID_ARG, "probe_copy_rate: window must be a power of two >= 1 KB dividing src_bytes");
   if (sink_bytes < 4ull * (uint64_t)workgroups) return fail(PATCH_ERR_INVALID_ARG, "probe_copy_rate: sink too small");
   hipError_t e = patch::launch_probe_copy(src_dev, src_bytes, window_bytes, iters, workgroups, sink_dev,
                                           reinterpret_cast<hipStream_t>(stream));

@@ -109,8 +109,8 @@ __global__ __launch_bounds__(256) void k_probe_mma(int iters, float* __restrict_
 // 8 waves a workgroup, each issuing 7 copies of 1 KB an iteration (16 bytes a
 // lane) into one of two LDS slots, waiting for the previous iteration's
 // copies (vmcnt) and meeting at a barrier, as the prefill kernels' copy ring
-// does.  Workgroup g copies from its window of `window` bytes at offset
-// (g * window) mod src_bytes, cycling through it: a few windows in all stay
+// does.  Workgroup g copies from its window of `window` bytes (a power of
+// two) at offset (g * window) mod src_bytes, cycling through it: a few windows in all stay
 // in the L2s after the first pass, windows that add up to more than the L2s
 // are served from past them.  The LDS is read once at the end (a word
 // stored only if it equals a constant), so the copies cannot be dropped.
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(512) void k_probe_copy(const uint8_t* __restrict__ 
 #pragma unroll
     for (int j = 0; j < kProbeCopies; j++) {
       const int64_t c = ((int64_t)it * kProbeCopies + j) * 8 + w;
-      dma16(win + (c * 1024) % window + 16 * l, slot + (uint32_t)((j * 8 + w) * 1024));
+      dma16(win + ((c << 10) & (window - 1)) + 16 * l, slot + (uint32_t)((j * 8 + w) * 1024));
     }
     wait_copies<kProbeCopies>();  // the previous iteration's copies have landed
     wg_barrier();

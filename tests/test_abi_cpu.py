@@ -291,6 +291,7 @@ def test_probe_copy_rate_host_checks():
         (V(16), 1 << 20, 1 << 18, 10, 4, None, 64),        # null sink
         (V(24), 1 << 20, 1 << 18, 10, 4, V(16), 64),       # unaligned source
         (V(16), 1 << 20, 1000, 10, 4, V(16), 64),          # window not a multiple of 1 KB
+        (V(16), 3 << 20, 3 << 10, 10, 4, V(16), 64),       # window not a power of two
         (V(16), 3 << 18, 1 << 19, 10, 4, V(16), 64),       # window does not divide the source
         (V(16), 1 << 20, 1 << 21, 10, 4, V(16), 64),       # window larger than the source
         (V(16), 1 << 20, 1 << 18, 0, 4, V(16), 64),        # no iterations
