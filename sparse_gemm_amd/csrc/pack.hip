@@ -36,14 +36,18 @@
 
 namespace patch {
 
-// grid: T * 8 workgroups of 256 threads; workgroup (t, part) packs part of tile t.
+// grid: T * 4 workgroups of 256 threads; thread c = 256 * (blockIdx.x & 3)
+// + threadIdx.x of tile t = blockIdx.x / 4 (c = 0 .. 1023) writes lane
+// l = c & 63's share of 64-column slice q = c >> 9 of band (c >> 6) & 7, so
+// every thread has work for every tile kind.
 // The blob's matrix is assembled from up to kPackMaxSources row-major
 // matrices of K columns (PackSources): concatenated by rows (several
 // projections packed as one), or -- interleave -- row-block ib taken from
 // source ib & 1, row-block ib / 2 (a fused gate/up projection).
 __global__ __launch_bounds__(256) void k_pack(PackSources src, int K, int KT, uint8_t* __restrict__ blob) {
-  const int t = blockIdx.x >> 3;
-  const int part = blockIdx.x & 7;
+  const int t = blockIdx.x >> 2;
+  const int c = ((blockIdx.x & 3) << 8) | threadIdx.x;
+  const int q = c >> 9, band = (c >> 6) & 7, l = c & 63;
   const TileEntry e = reinterpret_cast<const TileEntry*>(blob + kHeaderBytes)[t];
   const int ib = t / KT, j = t - (t / KT) * KT;
   // source matrix and its row-block for blob row-block ib
@@ -57,70 +61,52 @@ __global__ __launch_bounds__(256) void k_pack(PackSources src, int K, int KT, ui
   }
   const uint16_t* __restrict__ W = src.W[si];
   const uint8_t* __restrict__ mask = src.mask[si];
+  const int64_t row = (int64_t)i * kTile + 16 * band + (l & 15);
+  const int64_t col = (int64_t)j * kTile + 64 * q + 16 * (l >> 4);
+  uint8_t* piece = blob + e.offset + (uint64_t)band * e.band_stride;
   if (e.kind == 0) {
-    if (part >= 4) return;
-    const int c = part * 256 + threadIdx.x;  // (q, band, l), 0 .. 1023
-    const int q = c >> 9, band = (c >> 6) & 7, l = c & 63;
-    const int64_t row = (int64_t)i * kTile + 16 * band + (l & 15);
-    const int64_t col = (int64_t)j * kTile + 64 * q + 16 * (l >> 4);
     // 16 elements = 8 words of two; group g is words 2g (positions 0, 1) and
     // 2g+1 (positions 2, 3)
     const u32x4 w0 = ld16(W + row * K + col), w1 = ld16(W + row * K + col + 8);
     const u32x4 h0 = {w0[0], w0[2], w1[0], w1[2]};
     const u32x4 h1 = {w0[1], w0[3], w1[1], w1[3]};
-    uint8_t* dst = blob + e.offset + (uint64_t)band * e.band_stride + 2048 * q + 16 * l;
+    uint8_t* dst = piece + 2048 * q + 16 * l;
     st16(dst, h0);
     st16(dst + 1024, h1);
     return;
   }
-  if (part >= 2) return;
-  const int pair = part * 256 + threadIdx.x;  // (band, l), 0 .. 511
-  const int band = pair >> 6, l = pair & 63;
-  const int64_t row = (int64_t)i * kTile + 16 * band + (l & 15);
-  uint8_t* piece = blob + e.offset + (uint64_t)band * e.band_stride;
+  // slice q's half of the lane's codes word (bits 16q .. 16q+15)
   uint32_t meta = 0;
   bool bad = false;
   if (e.kind == 2) {
-    // 64-column slice q: this lane's sixteen columns, groups u = 0, 1 of eight
+    // this lane's sixteen columns of slice q: groups u = 0, 1 of eight
+    uint32_t vals[4];
 #pragma unroll
-    for (int q = 0; q < 2; q++) {
-      uint32_t vals[4];
+    for (int u = 0; u < 2; u++) {
+      const u32x4 w = ld16(W + row * K + col + 8 * u);
+      const uint2 mk = *reinterpret_cast<const uint2*>(mask + row * K + col + 8 * u);
+      uint32_t kept[4] = {0u, 0u, 0u, 0u}, bits = 0;
+      int n = 0;
 #pragma unroll
-      for (int u = 0; u < 2; u++) {
-        const int64_t col0 = (int64_t)j * kTile + 64 * q + 16 * (l >> 4) + 8 * u;
-        const u32x4 w = ld16(W + row * K + col0);
-        const uint2 mk = *reinterpret_cast<const uint2*>(mask + row * K + col0);
-        uint32_t kept[4] = {0u, 0u, 0u, 0u}, bits = 0;
-        int n = 0;
-#pragma unroll
-        for (int p = 0; p < 8; p++) {
-          const uint32_t mb = ((p < 4 ? mk.x : mk.y) >> (8 * (p & 3))) & 0xffu;
-          const uint32_t v = (w[p >> 1] >> (16 * (p & 1))) & 0xffffu;
-          if (mb) {
-            if (n < 4) kept[n] = v;
-            bits |= 1u << p;
-            n++;
-          }
+      for (int p = 0; p < 8; p++) {
+        const uint32_t mb = ((p < 4 ? mk.x : mk.y) >> (8 * (p & 3))) & 0xffu;
+        const uint32_t v = (w[p >> 1] >> (16 * (p & 1))) & 0xffffu;
+        if (mb) {
+          if (n < 4) kept[n] = v;
+          bits |= 1u << p;
+          n++;
         }
-        bad |= (n != 4);
-        vals[2 * u] = kept[0] | (kept[1] << 16);
-        vals[2 * u + 1] = kept[2] | (kept[3] << 16);
-        meta |= bits << (8 * (2 * q + u));
       }
-      const u32x4 o = {vals[0], vals[1], vals[2], vals[3]};
-      st16(piece + 1024 * q + 16 * l, o);
+      bad |= (n != 4);
+      vals[2 * u] = kept[0] | (kept[1] << 16);
+      vals[2 * u + 1] = kept[2] | (kept[3] << 16);
+      meta |= bits << (8 * u);
     }
-    reinterpret_cast<uint32_t*>(piece + kSparseMetaOffset)[l] = meta;
-    if (bad) atomicOr(reinterpret_cast<uint32_t*>(blob + kErrFlagOffset), 1u);
-    return;
-  }
-#pragma unroll
-  for (int q = 0; q < 2; q++) {
-    const int64_t col0 = (int64_t)j * kTile + 64 * q + 16 * (l >> 4);
-    const uint16_t* wp = W + row * K + col0;
-    const uint8_t* mp = mask + row * K + col0;
-    u32x4 w0 = ld16(wp), w1 = ld16(wp + 8);
-    u32x4 m4 = ld16(mp);
+    const u32x4 o = {vals[0], vals[1], vals[2], vals[3]};
+    st16(piece + 1024 * q + 16 * l, o);
+  } else {
+    const u32x4 w0 = ld16(W + row * K + col), w1 = ld16(W + row * K + col + 8);
+    const u32x4 m4 = ld16(mask + row * K + col);
     uint16_t wv[16];
 #pragma unroll
     for (int d = 0; d < 4; d++) {
@@ -148,12 +134,13 @@ __global__ __launch_bounds__(256) void k_pack(PackSources src, int K, int KT, ui
       }
       bad |= (n != 2);
       outv[p] = kept[0] | (kept[1] << 16);
-      meta |= (pos[0] | (pos[1] << 2)) << (16 * q + 4 * p);
+      meta |= (pos[0] | (pos[1] << 2)) << (4 * p);
     }
-    u32x4 o = {outv[0], outv[1], outv[2], outv[3]};
+    const u32x4 o = {outv[0], outv[1], outv[2], outv[3]};
     st16(piece + 1024 * q + 16 * l, o);
   }
-  reinterpret_cast<uint32_t*>(piece + kSparseMetaOffset)[l] = meta;
+  // the two slices' threads write the two halves of the lane's word
+  reinterpret_cast<uint16_t*>(piece + kSparseMetaOffset)[2 * l + q] = (uint16_t)meta;
   if (bad) atomicOr(reinterpret_cast<uint32_t*>(blob + kErrFlagOffset), 1u);
 }
 
@@ -232,7 +219,7 @@ hipError_t launch_pack_q64(const void* W, const uint8_t* mask, int64_t N, int64_
 hipError_t launch_pack(const PackSources& src, int64_t N, int64_t K, uint8_t* blob, hipStream_t s) {
   const int KT = (int)(K / kTile);
   const int64_t T = (N / kTile) * KT;
-  hipLaunchKernelGGL(k_pack, dim3((unsigned)(T * 8)), dim3(256), 0, s, src, (int)K, KT, blob);
+  hipLaunchKernelGGL(k_pack, dim3((unsigned)(T * 4)), dim3(256), 0, s, src, (int)K, KT, blob);
   return hipGetLastError();
 }
 
