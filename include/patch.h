@@ -209,10 +209,14 @@ patch_status patch_desc_from_header(const void* header_host, uint64_t header_byt
  * splits K into ranges, writes each range's fp32 partial sums to the
  * workspace ([splits][M][N] floats) and adds them in range order in a
  * second kernel on the same stream, so results do not depend on timing.
+ * When the blocks fill whole rounds of the GPU with a few left over (the
+ * tail split), only those few are cut into K ranges, which hand their fp32
+ * sums (256 x width floats a block and range) and a flag each through the
+ * workspace to the block's first range, which adds them in range order.
  * 0 when no split is wanted.  A smaller workspace only means fewer ranges
- * (none below two planes of M*N floats).  The workspace is scratch owned by
- * the call: its contents need no initialisation and are undefined after;
- * calls that run concurrently need distinct workspaces.
+ * (none below two planes of M*N floats) or no tail split.  The workspace is
+ * scratch owned by the call: its contents need no initialisation and are
+ * undefined after; calls that run concurrently need distinct workspaces.
  */
 uint64_t patch_gemm_workspace_bytes(const patch_packed_desc* desc, int64_t M);
 

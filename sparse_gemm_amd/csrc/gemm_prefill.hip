@@ -457,6 +457,13 @@ constexpr int lds_w_stages(int bm, bool q64) { return bm <= 128 || (bm == 192 &&
 // (r, wn, wm) works on half wn of row-block r, so it reads that half's
 // entries and, per step (one slice), that slice's kind: the waves of one
 // workgroup may run different kinds in the same step.
+// Polls of a tail range's flag (each a round trip to the L2 plus 256
+// cycles of sleep) before range 0 gives up on it: a second or more, far
+// beyond any range's run time.
+constexpr int kTailSpinLimit = 1 << 20;
+// Cache-policy operand of the buffer loads and stores: sc1, agent scope.
+constexpr int kCoherent = 16;
+
 template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE, int BM, bool Q64 = false>
 __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   static_assert(!Q64 || (!SRC_ROWMAJOR && !FUSE), "64 x 64 execution tiles: packed W, not fused");
@@ -476,10 +483,32 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   __shared__ uint32_t s_ent[kEntRows][kPfMaxKT];
   __shared__ u32x4 s_sel[SRC_ROWMAJOR || Q64 ? 1 : 256];  // 4:8 rebuild selectors
 
-  const int t = (blockIdx.x & 7) * P.per_xcd + (blockIdx.x >> 3);
-  if (t >= P.n_blocks) return;  // whole workgroup
-  const int per_split = P.n_pairs * P.n_mblk;
-  const int ks = t / per_split, tk = t - (t / per_split) * per_split;
+  // block tk, K range ks; tb: the tail block (tail split), else -1
+  int ks, tk, tb = -1;
+  if (!FUSE && P.tail_s > 1) {
+    // an XCD runs its share of the whole blocks first, then its tail blocks,
+    // each block's ranges back to back with range 0 -- the one that waits --
+    // last, so it is dispatched after the ranges it waits for
+    const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
+    const int full_per = P.n_full >> 3;
+    if (i < full_per) {
+      tk = x * full_per + i;
+      ks = 0;
+    } else {
+      const int j = i - full_per;
+      const int tl = j / P.tail_s;
+      tb = x * P.tail_per + tl;
+      if (tl >= P.tail_per || tb >= P.n_tail) return;  // whole workgroup
+      ks = P.tail_s - 1 - (j - tl * P.tail_s);
+      tk = P.n_full + tb;
+    }
+  } else {
+    const int t = (blockIdx.x & 7) * P.per_xcd + (blockIdx.x >> 3);
+    if (t >= P.n_blocks) return;  // whole workgroup
+    const int per_split = P.n_pairs * P.n_mblk;
+    ks = t / per_split;
+    tk = t - ks * per_split;
+  }
   const int grp = P.n_pairs * P.mg;
   const int gi = tk / grp, rem = tk - (tk / grp) * grp;
   const int m_cnt = min(P.mg, P.n_mblk - gi * P.mg);
@@ -499,7 +528,8 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   const int r_src = active ? r : 0;
   const int i_src = active ? i_mine : i0;
   const int j0 = ks * P.kt_split;
-  const int nt = min(P.kt_split, KT - j0);
+  // (a whole block of a tail split: all of K)
+  const int nt = !FUSE && P.tail_s > 1 && tb < 0 ? KT : min(P.kt_split, KT - j0);
   const int n_steps = 2 * nt;
 
   if constexpr (Q64) {
@@ -876,6 +906,73 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
       return;
     }
   }
+  if (!FUSE && tb >= 0) {
+    // A tail block's ranges: lane l of wave w keeps its sums at f32x4 index
+    // ((w * 4 + b) * kNMB + mblk) * 64 + l of a slot.  The slots are written
+    // and read with the agent-coherent cache policy (sc1: the value every
+    // XCD's L2 sees), so the hand-over needs no cache-wide write-back or
+    // invalidation -- which would also evict what the other workgroups of
+    // the XCD are streaming.  Order: a range's stores complete (vmcnt 0)
+    // before its barrier and flag; range 0 loads after it has seen the
+    // flags.
+    const int slot0 = tb * (P.tail_s - 1);
+    constexpr uint32_t kSlotBytes = 256u * BM * 4u;
+    if (ks > 0) {
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(P.part + (int64_t)(slot0 + ks - 1) * (256 * BM), kSlotBytes);
+#pragma unroll
+      for (int b = 0; b < 4; b++)
+#pragma unroll
+        for (int mblk = 0; mblk < kNMB; mblk++)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[b][mblk]), rs,
+                                                 16 * (((w * 4 + b) * kNMB + mblk) * 64 + l), 0, kCoherent);
+      wait_copies<0>();
+      __syncthreads();
+      if (threadIdx.x == 0) __hip_atomic_store(P.flags + slot0 + ks - 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    // range 0: a bounded wait (one thread) that marks the block when it runs
+    // out, so a missing range shows as NaN outputs rather than a hang; the
+    // first barrier: every wave is done with the tile entries, whose first
+    // word then carries the mark
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t late = 0;
+      for (int q = 1; q < P.tail_s; q++) {
+        int spins = 0;
+        while (__hip_atomic_load(P.flags + slot0 + q - 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+          if (++spins > kTailSpinLimit) {
+            late = 1;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(4);
+        }
+      }
+      s_ent[0][0] = late;
+    }
+    __syncthreads();
+    const bool late = s_ent[0][0] != 0;
+    // the ranges' sums in range order, one band at a time (the loads of all
+    // four at once would need as many registers again as the sums)
+    for (int q = 1; q < P.tail_s; q++) {
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(P.part + (int64_t)(slot0 + q - 1) * (256 * BM), kSlotBytes);
+#pragma unroll
+      for (int b = 0; b < 4; b++) {
+#pragma unroll
+        for (int mblk = 0; mblk < kNMB; mblk++)
+          acc[b][mblk] += __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * (((w * 4 + b) * kNMB + mblk) * 64 + l), 0,
+                                                           kCoherent));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (late) {
+#pragma unroll
+      for (int b = 0; b < 4; b++)
+#pragma unroll
+        for (int mblk = 0; mblk < kNMB; mblk++)
+          acc[b][mblk] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+    }
+  }
   void* Yp = P.Y;
   if (P.splits > 1) Yp = reinterpret_cast<float*>(P.Y) + (int64_t)ks * P.M * P.N;
   if (active) {
@@ -892,6 +989,13 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+}
+
+// Clears the tail split's flags before its launch (a kernel rather than a
+// memset, so the pair can be captured in a graph).
+__global__ __launch_bounds__(256) void k_tail_clear(int* __restrict__ flags, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) flags[i] = 0;
 }
 
 // Launch shape: the M-block width BM and the number of K ranges, chosen
@@ -920,6 +1024,9 @@ struct PfShape {
   bool lds;  // W and X staged through LDS (k_prefill_lds), else through registers (k_prefill)
   bool big;  // the kernel whose waves hold 128-row register tiles (k_prefill_big)
   int waves; // its waves a workgroup: 4 or 8
+  // tail split (k_prefill_lds, splits = 1): n_full blocks whole, the rest
+  // in tail_s K ranges (0: none)
+  int tail_s = 0, n_full = 0;
 };
 static double shape_cost_us(int64_t M, int64_t N, int64_t K, int bm, int64_t splits, int64_t kt_split, int cus) {
   const int64_t pairs = (N / kTile + 1) / 2;
@@ -931,7 +1038,47 @@ static double shape_cost_us(int64_t M, int64_t N, int64_t K, int bm, int64_t spl
   return t;
 }
 // only_bm: consider that width alone (0: every width).
-static PfShape choose_shape_uncached(int64_t M, int64_t N, int64_t K, int cus, int only_bm = 0) {
+// The tail split at width bm: whole rounds of blocks as usual (R = the CUs
+// rounded down to a multiple of 8 blocks a round), the blocks left over (too
+// few to fill a round) each cut into S K ranges so that they fill one short
+// round; a range hands its fp32 sums to the block's range 0 (the cost: the
+// flags cleared, the slots written, range 0 reading them).  Returns -1 where
+// it does not apply (no left-over blocks, or too many to cut in two).
+static double tail_cost_us(int64_t M, int64_t N, int64_t K, int bm, int cus, int* n_full, int* tail_s,
+                           int* kt_split) {
+  const int64_t KT = K / kTile;
+  const int64_t R = cus - cus % 8;
+  const int64_t blocks = ((N / kTile + 1) / 2) * ((M + bm - 1) / bm);
+  if (R < 8 || blocks <= R || blocks % R == 0) return -1.0;
+  const int64_t full = blocks / R * R, tail = blocks - full;
+  int64_t S = std::min<int64_t>(R / tail, KT / 2);
+  if (S < 2) return -1.0;
+  const int64_t kt = (KT + S - 1) / S;
+  S = (KT + kt - 1) / kt;
+  const double fill = (double)(tail * S) / (double)cus;
+  // range 0 reads the other ranges' slots (256 x bm fp32 each) at about
+  // 150 GB/s a CU
+  const double t = (double)(full / R) * (2.33 + (double)KT * (0.79 * 1.086 + 0.0072 * bm)) + 2.33 +
+                   (double)kt * (0.79 * (1.0 + 0.086 * fill) + 0.0072 * bm) + 1.0 +
+                   (double)(S - 1) * 256.0 * bm * 4.0 / 1.5e5;
+  *n_full = (int)full;
+  *tail_s = (int)S;
+  *kt_split = (int)kt;
+  return t;
+}
+
+// Workspace bytes of a tail split: a slot of 256 x bm fp32 sums for every
+// range but the first of every tail block, then their flags (rounded to 256
+// bytes).
+static uint64_t tail_ws_bytes(int64_t M, int64_t N, int bm, int n_full, int tail_s) {
+  const int64_t blocks = ((N / kTile + 1) / 2) * ((M + bm - 1) / bm);
+  const uint64_t slots = (uint64_t)(blocks - n_full) * (uint64_t)(tail_s - 1);
+  return slots * 256u * (uint64_t)bm * 4u + (slots * 4u + 255u) / 256u * 256u;
+}
+
+// tail_ok: the tail split may be chosen (the LDS-staged kernel, not fused).
+static PfShape choose_shape_uncached(int64_t M, int64_t N, int64_t K, int cus, int only_bm = 0,
+                                     bool tail_ok = false) {
   const int64_t KT = K / kTile;
   const int widths[4] = {256, 192, 128, 64};
   const int wants[10] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
@@ -949,6 +1096,14 @@ static PfShape choose_shape_uncached(int64_t M, int64_t N, int64_t K, int cus, i
         best = {widths[c], 1, (int)splits, (int)kt_split, false, false, 4};
       }
     }
+    if (tail_ok) {
+      int n_full = 0, tail_s = 0, kt = 0;
+      const double t = tail_cost_us(M, N, K, widths[c], cus, &n_full, &tail_s, &kt);
+      if (t >= 0 && t < best_t) {
+        best_t = t;
+        best = {widths[c], 1, 1, kt, false, false, 4, tail_s, n_full};
+      }
+    }
   }
   const int64_t mblk = (M + best.bm - 1) / best.bm;
   while (best.groups < 2 && 2 * best.groups * 2 <= mblk) best.groups *= 2;
@@ -961,11 +1116,11 @@ static PfShape choose_shape_uncached(int64_t M, int64_t N, int64_t K, int cus, i
 // shapes it measured as fast as or faster than the register-staged kernel
 // at each width -- 5-10% at width 64, 2-12% from 128 up for packed W, 20-45%
 // for row-major W (the dense baseline).
-static PfShape choose_shape(int64_t M, int64_t N, int64_t K, bool rowmajor) {
+static PfShape choose_shape(int64_t M, int64_t N, int64_t K, bool rowmajor, bool tail_ok = true) {
   struct Entry {
     int64_t M, N, K;
     int cus;
-    bool rowmajor;
+    bool rowmajor, tail_ok;
     PfShape sh;
   };
   constexpr int kSlots = 8;
@@ -973,12 +1128,12 @@ static PfShape choose_shape(int64_t M, int64_t N, int64_t K, bool rowmajor) {
   thread_local int filled = 0, next = 0;
   const int cus = cu_count();
   for (int i = 0; i < filled; i++)
-    if (cache[i].M == M && cache[i].N == N && cache[i].K == K && cache[i].cus == cus && cache[i].rowmajor == rowmajor)
+    if (cache[i].M == M && cache[i].N == N && cache[i].K == K && cache[i].cus == cus &&
+        cache[i].rowmajor == rowmajor && cache[i].tail_ok == tail_ok)
       return cache[i].sh;
-  PfShape sh = choose_shape_uncached(M, N, K, cus);
-  (void)rowmajor;
+  PfShape sh = choose_shape_uncached(M, N, K, cus, 0, tail_ok);
   sh.lds = true;
-  cache[next] = {M, N, K, cus, rowmajor, sh};
+  cache[next] = {M, N, K, cus, rowmajor, tail_ok, sh};
   next = (next + 1) % kSlots;
   if (filled < kSlots) filled++;
   return sh;
@@ -1053,6 +1208,9 @@ static PfArgs prefill_args(const void* src, const void* src2, const void* X, int
   a.kt_split = sh.kt_split;
   a.n_blocks = a.n_pairs * a.n_mblk * sh.splits;
   a.per_xcd = (a.n_blocks + 7) / 8;
+  a.n_full = a.n_tail = a.tail_s = a.tail_per = 0;
+  a.part = nullptr;
+  a.flags = nullptr;
   return a;
 }
 
@@ -1086,6 +1244,25 @@ static hipError_t launch_prefill_bm(const void* src, const void* src2, const voi
   a.kt_split = sh.kt_split;
   a.n_blocks = a.n_pairs * a.n_mblk * sh.splits;
   a.per_xcd = (a.n_blocks + 7) / 8;
+  a.n_full = a.n_tail = a.tail_s = a.tail_per = 0;
+  a.part = nullptr;
+  a.flags = nullptr;
+  if constexpr (LDS && !FUSE) {
+    if (sh.tail_s > 1) {
+      // tail split: the slots, then the flags, in the workspace
+      a.n_full = sh.n_full;
+      a.n_tail = a.n_pairs * a.n_mblk - sh.n_full;
+      a.tail_s = sh.tail_s;
+      a.tail_per = (a.n_tail + 7) / 8;
+      a.part = part;
+      const int nf = a.n_tail * (sh.tail_s - 1);
+      a.flags = reinterpret_cast<int*>(part + (int64_t)nf * 256 * BM);
+      hipLaunchKernelGGL(k_tail_clear, dim3((unsigned)((nf + 255) / 256)), dim3(256), 0, s, a.flags, nf);
+      hipLaunchKernelGGL((k_prefill_lds<BF16, SRC_ROWMAJOR, OUT_F32, false, BM, Q64>),
+                         dim3((unsigned)(8 * (sh.n_full / 8 + a.tail_per * sh.tail_s))), dim3(kPfWaves * 64), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   const dim3 grid((unsigned)(8 * a.per_xcd)), block(kPfWaves * 64);
   if (sh.splits > 1) {
     // fp32 partials of the K ranges, then the ordered reduction (fused:
@@ -1155,15 +1332,21 @@ static PfShape choose_shape_big(int64_t M, int64_t N, int64_t K, int cus, int on
 // The shape for these sizes with the split limited to what the workspace
 // holds (no workspace: no split).
 static PfShape shape_for(int64_t M, int64_t N, int64_t K, bool rowmajor, uint64_t ws_bytes, int force_bm = 0,
-                         bool force_lds = false, int force_big = 0) {
+                         bool force_lds = false, int force_big = 0, bool fuse = false) {
   PfShape sh;
   if (force_big) {
     sh = choose_shape_big(M, N, K, cu_count(), force_bm, force_big);
   } else if (force_bm) {
-    sh = choose_shape_uncached(M, N, K, cu_count(), force_bm);
+    sh = choose_shape_uncached(M, N, K, cu_count(), force_bm, force_lds && !fuse);
     sh.lds = force_lds;
   } else {
-    sh = choose_shape(M, N, K, rowmajor);
+    sh = choose_shape(M, N, K, rowmajor, !fuse);
+  }
+  if (sh.tail_s > 1 && tail_ws_bytes(M, N, sh.bm, sh.n_full, sh.tail_s) > ws_bytes) {
+    // no room for the tail split's slots: the best shape without it
+    const bool lds = sh.lds;
+    sh = force_bm ? choose_shape_uncached(M, N, K, cu_count(), force_bm, false) : choose_shape(M, N, K, rowmajor, false);
+    sh.lds = lds;
   }
   const uint64_t plane = (uint64_t)M * (uint64_t)N * 4u;
   const int64_t KT = K / kTile;
@@ -1180,7 +1363,7 @@ static PfShape shape_for(int64_t M, int64_t N, int64_t K, bool rowmajor, uint64_
   if (sh.big && sh.kt_split > kBigMaxKT) {
     // the big-tile kernel keeps at most kBigMaxKT tile columns a range and
     // the workspace allows no split that short: the 8-wave kernel
-    PfShape lds = choose_shape(M, N, K, rowmajor);
+    PfShape lds = choose_shape(M, N, K, rowmajor, false);
     lds.lds = true;
     lds.splits = 1;
     lds.kt_split = (int)KT;
@@ -1189,14 +1372,25 @@ static PfShape shape_for(int64_t M, int64_t N, int64_t K, bool rowmajor, uint64_
   return sh;
 }
 
+// Room for the shape with the tail split and for the one without (the
+// fused product runs without it).
 uint64_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K, bool rowmajor) {
-  const PfShape sh = choose_shape(M, N, K, rowmajor);
-  return sh.splits > 1 ? (uint64_t)sh.splits * (uint64_t)M * (uint64_t)N * 4u : 0u;
+  uint64_t b = 0;
+  for (int tail_ok = 0; tail_ok < 2; tail_ok++) {
+    const PfShape sh = choose_shape(M, N, K, rowmajor, tail_ok != 0);
+    if (sh.splits > 1) b = std::max<uint64_t>(b, (uint64_t)sh.splits * (uint64_t)M * (uint64_t)N * 4u);
+    if (sh.tail_s > 1) b = std::max<uint64_t>(b, tail_ws_bytes(M, N, sh.bm, sh.n_full, sh.tail_s));
+  }
+  return b;
 }
 
 // The cost model's time for the shape this workspace allows.
 double prefill_estimate_us(int64_t M, int64_t N, int64_t K, bool rowmajor, uint64_t ws_bytes) {
   const PfShape sh = shape_for(M, N, K, rowmajor, ws_bytes);
+  if (sh.tail_s > 1) {
+    int n_full = 0, tail_s = 0, kt = 0;
+    return tail_cost_us(M, N, K, sh.bm, cu_count(), &n_full, &tail_s, &kt);
+  }
   return shape_cost_us(M, N, K, sh.bm, sh.splits, sh.kt_split, cu_count());
 }
 
@@ -1204,7 +1398,7 @@ template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE>
 static hipError_t launch_prefill_t(const void* src, const void* src2, const void* X, int64_t M, int64_t N, int64_t K,
                                    void* Y, void* ws, uint64_t ws_bytes, int force_bm, bool force_lds, int force_big,
                                    hipStream_t s) {
-  const PfShape sh = shape_for(M, N, K, SRC_ROWMAJOR, ws ? ws_bytes : 0u, force_bm, force_lds, force_big);
+  const PfShape sh = shape_for(M, N, K, SRC_ROWMAJOR, ws ? ws_bytes : 0u, force_bm, force_lds, force_big, FUSE);
   float* part = reinterpret_cast<float*>(ws);
   if (sh.big) return launch_big_t<BF16, SRC_ROWMAJOR, OUT_F32, FUSE>(src, src2, X, M, N, K, Y, sh, part, s);
 #define PATCH_BM(W, D, L) \

@@ -43,6 +43,15 @@ struct PfArgs {
   int splits;   // K ranges; above 1, Y is the fp32 partial buffer [splits][M][N]
   int kt_split; // tile columns per K range
   int n_blocks, per_xcd;
+  // Tail split (tail_s > 1; splits = 1): the first n_full blocks (8 * an
+  // XCD's share) run whole; the n_tail blocks after them run in tail_s K
+  // ranges of kt_split tile columns, tail_per of them an XCD.  Range k > 0
+  // of tail block b hands its fp32 sums to range 0 through slot
+  // b * (tail_s - 1) + k - 1 of part (256 x BM floats each, in the lanes'
+  // order) and the flag of the same index (cleared before the launch).
+  int n_full, n_tail, tail_s, tail_per;
+  float* part;
+  int* flags;
 };
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }

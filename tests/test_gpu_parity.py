@@ -295,6 +295,55 @@ def test_prefill_lds_short_k(variant):
                 assert_close(patch.dense_gemm(X, W, variant=variant, workspace=w), _ref(pd, Xb), what="dense " + tag)
 
 
+# Shapes with a little over 256 output blocks at one width, so that the
+# LDS-staged kernel at that width runs a round of whole blocks and cuts the
+# few left over into K ranges (the tail split): (variant, N, K, M).  N = 640
+# has a lone middle row-block; the M values leave a ragged last M-block.
+TAIL_CASES = [("prefill_w64_lds", 640, 1152, 5750),     # 270 blocks: 14 left over, 3 ranges
+              ("prefill_w128_lds", 1536, 1152, 5450),   # 258: 2 left over, 3 ranges
+              ("prefill_w192_lds", 1536, 2048, 8371),   # 264: 8 left over, 8 ranges
+              ("prefill_w256_lds", 1536, 1152, 14800)]  # 348: 92 left over, 2 ranges
+
+
+@pytest.mark.parametrize("variant,N,K,M", TAIL_CASES)
+def test_prefill_tail_split(variant, N, K, M):
+    """The tail split: the blocks left over after the whole rounds run in K
+    ranges, each range handing its fp32 sums to the block's first range
+    through the workspace.  2:4 + dense blob, row-major dense W, a 2:4 + 4:8
+    + dense blob and a 64 x 64 tile blob, bf16 and fp32 outputs, on sampled
+    rows against the oracle (every output column, so every block of the
+    sampled rows); a workspace with room for the slots (64 MB); repeated
+    calls equal bit for bit; without a workspace the data-parallel launch
+    runs."""
+    rows = _sampled_rows(M, n=32, seed=M)
+    # rows in the last M-blocks too, where the left-over blocks are
+    rows = np.unique(np.concatenate([rows, np.arange(M - 300, M, 37)]))
+    sel = torch.from_numpy(rows).cuda()
+    Xb = inputs.make_custom_x("bf16", M, K, 70 + M)
+    X = dev_bits(Xb, "bf16")
+    p = inputs.make_custom("bf16", N, K, 71, "bernoulli", 0.5, "uniform")
+    pw, W = _pack(p)
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    ref = _ref(p, Xb, rows)
+    tag = f"{variant} N={N} K={K} M={M}"
+    a = patch.gemm(X, pw, out_dtype=torch.float32, variant=variant, workspace=ws)
+    b = patch.gemm(X, pw, out_dtype=torch.float32, variant=variant, workspace=ws)
+    assert torch.equal(a, b), tag
+    assert_close(a[sel], ref, f32=True, what=tag + " f32")
+    assert_close(patch.gemm(X, pw, variant=variant, workspace=ws)[sel], ref, what=tag)
+    assert_close(patch.gemm(X, pw, variant=variant, workspace=None)[sel], ref, what=tag + " no workspace")
+    pd = inputs.make_custom("bf16", N, K, 71, "dense", 0.0, "top2")
+    assert_close(patch.dense_gemm(X, W, variant=variant, workspace=ws)[sel], _ref(pd, Xb, rows), what="dense " + tag)
+    pm = inputs.make_mixed("bf16", N, K, 72, 0.3, 0.4, "uniform")
+    pwm, _ = _pack(pm)
+    assert_close(patch.gemm(X, pwm, variant=variant, workspace=ws)[sel], _ref(pm, Xb, rows), what="4:8 " + tag)
+    pq = inputs.make_fine("bf16", N, K, 64, 64, 73, s_exec=0.3, p_sub=0.5)
+    pwq = patch.pack_q64(dev_bits(pq.w, "bf16"), pq.tile_map, dev_u8(pq.mask))
+    assert_close(patch.gemm(X, pwq, variant=variant, workspace=ws)[sel],
+                 oracle.gemm_f64("bf16", Xb[rows], pq.w, pq.tile_map, pq.mask, tile_n=64, tile_k=64),
+                 what="64x64 tiles " + tag)
+
+
 # ------------------------------------------------------------------ exact cases
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_identity_x_gives_masked_weights_exactly(dtype):
