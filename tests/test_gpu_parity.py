@@ -297,12 +297,15 @@ def test_prefill_lds_short_k(variant):
 
 # Shapes with a little over 256 output blocks at one width, so that the
 # LDS-staged kernel at that width runs a round of whole blocks and cuts the
-# few left over into K ranges (the tail split): (variant, N, K, M).  N = 640
-# has a lone middle row-block; the M values leave a ragged last M-block.
+# few left over into K ranges (the tail split), and one with fewer blocks
+# than a round and a long K, all of whose blocks run in two ranges:
+# (variant, N, K, M).  N = 640 has a lone middle row-block; the M values
+# leave a ragged last M-block.
 TAIL_CASES = [("prefill_w64_lds", 640, 1152, 5750),     # 270 blocks: 14 left over, 3 ranges
               ("prefill_w128_lds", 1536, 1152, 5450),   # 258: 2 left over, 3 ranges
               ("prefill_w192_lds", 1536, 2048, 8371),   # 264: 8 left over, 8 ranges
-              ("prefill_w256_lds", 1536, 1152, 14800)]  # 348: 92 left over, 2 ranges
+              ("prefill_w256_lds", 1536, 1152, 14800),  # 348: 92 left over, 2 ranges
+              ("prefill_w256_lds", 1536, 8192, 2000)]   # 48: no whole round, 2 ranges of 32 tile columns
 
 
 @pytest.mark.parametrize("variant,N,K,M", TAIL_CASES)
