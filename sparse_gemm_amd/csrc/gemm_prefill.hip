@@ -51,6 +51,8 @@
 #include "prefill_common.h"
 
 #include <algorithm>
+#include <atomic>
+#include <random>
 
 namespace patch {
 
@@ -927,7 +929,8 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
                                                  16 * (((w * 4 + b) * kNMB + mblk) * 64 + l), 0, kCoherent);
       wait_copies<0>();
       __syncthreads();
-      if (threadIdx.x == 0) __hip_atomic_store(P.flags + slot0 + ks - 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (threadIdx.x == 0)
+        __hip_atomic_store(P.flags + slot0 + ks - 1, P.token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return;
     }
     // range 0: a bounded wait (one thread) that marks the block when it runs
@@ -938,14 +941,18 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
     if (threadIdx.x == 0) {
       uint32_t late = 0;
       for (int q = 1; q < P.tail_s; q++) {
+        uint64_t* f = P.flags + slot0 + q - 1;
         int spins = 0;
-        while (__hip_atomic_load(P.flags + slot0 + q - 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+        while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != P.token) {
           if (++spins > kTailSpinLimit) {
             late = 1;
             break;
           }
           __builtin_amdgcn_s_sleep(4);
         }
+        // back to 0 for the next launch (the sums are read below; the flag
+        // is no longer needed)
+        __hip_atomic_store(f, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       s_ent[0][0] = late;
     }
@@ -991,12 +998,6 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   }
 }
 
-// Clears the tail split's flags before its launch (a kernel rather than a
-// memset, so the pair can be captured in a graph).
-__global__ __launch_bounds__(256) void k_tail_clear(int* __restrict__ flags, int n) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) flags[i] = 0;
-}
 
 // Launch shape: the M-block width BM and the number of K ranges, chosen
 // by a cost model of the LDS-staged kernel fitted to its measured times on
@@ -1076,13 +1077,30 @@ static double tail_cost_us(int64_t M, int64_t N, int64_t K, int bm, int cus, int
   return t;
 }
 
+// This launch's tail-split token: a counter mixed with a random salt
+// drawn once per process (splitmix64's finaliser), never 0.  Stale or
+// uninitialised flag words would have to equal a fresh 64-bit value to pass
+// for it.
+static uint64_t tail_token() {
+  static const uint64_t salt = [] {
+    std::random_device rd;
+    return ((uint64_t)rd() << 32) ^ (uint64_t)rd();
+  }();
+  static std::atomic<uint64_t> counter{1};
+  uint64_t z = salt + 0x9e3779b97f4a7c15ull * counter.fetch_add(1, std::memory_order_relaxed);
+  z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+  z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+  z ^= z >> 31;
+  return z ? z : 1;
+}
+
 // Workspace bytes of a tail split: a slot of 256 x bm fp32 sums for every
-// range but the first of every tail block, then their flags (rounded to 256
-// bytes).
+// range but the first of every tail block, then their 8-byte flags
+// (rounded to 256 bytes).
 static uint64_t tail_ws_bytes(int64_t M, int64_t N, int bm, int n_full, int tail_s) {
   const int64_t blocks = ((N / kTile + 1) / 2) * ((M + bm - 1) / bm);
   const uint64_t slots = (uint64_t)(blocks - n_full) * (uint64_t)(tail_s - 1);
-  return slots * 256u * (uint64_t)bm * 4u + (slots * 4u + 255u) / 256u * 256u;
+  return slots * 256u * (uint64_t)bm * 4u + (slots * 8u + 255u) / 256u * 256u;
 }
 
 // tail_ok: the tail split may be chosen (the LDS-staged kernel, not fused).
@@ -1220,6 +1238,7 @@ static PfArgs prefill_args(const void* src, const void* src2, const void* X, int
   a.n_full = a.n_tail = a.tail_s = a.tail_per = 0;
   a.part = nullptr;
   a.flags = nullptr;
+  a.token = 0;
   return a;
 }
 
@@ -1256,6 +1275,7 @@ static hipError_t launch_prefill_bm(const void* src, const void* src2, const voi
   a.n_full = a.n_tail = a.tail_s = a.tail_per = 0;
   a.part = nullptr;
   a.flags = nullptr;
+  a.token = 0;
   if constexpr (LDS && !FUSE) {
     if (sh.tail_s > 1) {
       // tail split: the slots, then the flags, in the workspace
@@ -1265,8 +1285,8 @@ static hipError_t launch_prefill_bm(const void* src, const void* src2, const voi
       a.tail_per = (a.n_tail + 7) / 8;
       a.part = part;
       const int nf = a.n_tail * (sh.tail_s - 1);
-      a.flags = reinterpret_cast<int*>(part + (int64_t)nf * 256 * BM);
-      hipLaunchKernelGGL(k_tail_clear, dim3((unsigned)((nf + 255) / 256)), dim3(256), 0, s, a.flags, nf);
+      a.flags = reinterpret_cast<uint64_t*>(part + (int64_t)nf * 256 * BM);
+      a.token = tail_token();
       hipLaunchKernelGGL((k_prefill_lds<BF16, SRC_ROWMAJOR, OUT_F32, false, BM, Q64>),
                          dim3((unsigned)(8 * (sh.n_full / 8 + a.tail_per * sh.tail_s))), dim3(kPfWaves * 64), 0, s, a);
       return hipGetLastError();

@@ -48,10 +48,14 @@ struct PfArgs {
   // ranges of kt_split tile columns, tail_per of them an XCD.  Range k > 0
   // of tail block b hands its fp32 sums to range 0 through slot
   // b * (tail_s - 1) + k - 1 of part (256 x BM floats each, in the lanes'
-  // order) and the flag of the same index (cleared before the launch).
+  // order) and the flag of the same index: it stores token there, which
+  // is this launch's own (nonzero) value; range 0 waits for the token and
+  // sets the flag back to 0, so every completed launch leaves its flags at
+  // 0 and no other launch's value can pass for its own.
   int n_full, n_tail, tail_s, tail_per;
   float* part;
-  int* flags;
+  uint64_t* flags;
+  uint64_t token;
 };
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }

@@ -129,8 +129,8 @@ def test_workspace_query_host_logic():
     ws = lambda M, N, K: int(lib.patch_dense_gemm_workspace_bytes(M, N, K))
     # 43 row-block pairs x 8 M-blocks of 256: a round of 256 blocks, the 88
     # left over in two K ranges (the tail split): a slot of 256 x 256 fp32
-    # sums for each, then their flags (rounded to 256 bytes)
-    assert ws(2048, 11008, 4096) == 88 * 256 * 256 * 4 + 512
+    # sums for each, then their 8-byte flags (rounded to 256 bytes)
+    assert ws(2048, 11008, 4096) == 88 * 256 * 256 * 4 + 768
     for M, N, K in [(128, 4096, 4096), (64, 4096, 11008), (17, 512, 4096), (300, 384, 4096)]:
         b = ws(M, N, K)
         assert b > 0 and b % (M * N * 4) == 0 and b <= 2 * N * K, (M, N, K, b)

@@ -315,9 +315,10 @@ def test_prefill_tail_split(variant, N, K, M):
     through the workspace.  2:4 + dense blob, row-major dense W, a 2:4 + 4:8
     + dense blob and a 64 x 64 tile blob, bf16 and fp32 outputs, on sampled
     rows against the oracle (every output column, so every block of the
-    sampled rows); a workspace with room for the slots (64 MB); repeated
-    calls equal bit for bit; without a workspace the data-parallel launch
-    runs."""
+    sampled rows); a workspace with room for the slots (64 MB of arbitrary
+    bytes: each launch's flags carry its own token, and the first range
+    sets them back to 0); repeated calls equal bit for bit; without a
+    workspace the data-parallel launch runs."""
     rows = _sampled_rows(M, n=32, seed=M)
     # rows in the last M-blocks too, where the left-over blocks are
     rows = np.unique(np.concatenate([rows, np.arange(M - 300, M, 37)]))
@@ -326,7 +327,8 @@ def test_prefill_tail_split(variant, N, K, M):
     X = dev_bits(Xb, "bf16")
     p = inputs.make_custom("bf16", N, K, 71, "bernoulli", 0.5, "uniform")
     pw, W = _pack(p)
-    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    # a workspace of arbitrary bytes: the flags need no initialisation
+    ws = torch.randint(0, 256, (64 << 20,), dtype=torch.uint8, device="cuda")
     ref = _ref(p, Xb, rows)
     tag = f"{variant} N={N} K={K} M={M}"
     a = patch.gemm(X, pw, out_dtype=torch.float32, variant=variant, workspace=ws)
@@ -345,6 +347,49 @@ def test_prefill_tail_split(variant, N, K, M):
     assert_close(patch.gemm(X, pwq, variant=variant, workspace=ws)[sel],
                  oracle.gemm_f64("bf16", Xb[rows], pq.w, pq.tile_map, pq.mask, tile_n=64, tile_k=64),
                  what="64x64 tiles " + tag)
+
+
+def test_tail_split_graph_replays():
+    """Tail-split launches captured in a HIP graph (the graph holds one token
+    per launch, so every replay relies on the previous one having set its
+    flags back to 0): one with a whole round and left-over blocks, one
+    without, replayed four times with eager tail-split launches on the same
+    workspace and synchronisations in between; every replay equals the eager
+    result bit for bit."""
+    cases = []
+    for variant, N, K, M in (TAIL_CASES[3], TAIL_CASES[4]):
+        p = inputs.make_custom("bf16", N, K, 74, "bernoulli", 0.5, "uniform")
+        pw, _ = _pack(p)
+        X = dev_bits(inputs.make_custom_x("bf16", M, K, 75 + M), "bf16")
+        cases.append((variant, pw, X, torch.empty((M, N), dtype=torch.float32, device="cuda")))
+    ws = torch.randint(0, 256, (64 << 20,), dtype=torch.uint8, device="cuda")
+
+    def run():
+        for variant, pw, X, out in cases:
+            patch.gemm(X, pw, out_dtype=torch.float32, variant=variant, workspace=ws, out=out)
+
+    run()
+    torch.cuda.synchronize()
+    eager = [c[3].clone() for c in cases]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(4):
+        for c in cases:
+            c[3].fill_(7.0)
+        g.replay()
+        torch.cuda.synchronize()
+        for c, e in zip(cases, eager):
+            assert torch.equal(c[3], e), f"replay {rep} {c[0]}"
+        run()  # eager tail-split launches (fresh tokens) on the same workspace
+        torch.cuda.synchronize()
+        for c, e in zip(cases, eager):
+            assert torch.equal(c[3], e), f"eager after replay {rep} {c[0]}"
 
 
 # ------------------------------------------------------------------ exact cases
