@@ -26,6 +26,7 @@ Prints one JSON line.  --report also writes the sweep over all workloads
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -152,6 +153,30 @@ def time_launches(calls, steps, warmup, batches=1):
     return ms_step, per
 
 
+def time_steps(calls, steps, warmup):
+    """The timed region of the headline: `steps` steps, each running every
+    call once (call c of step k gets index (warmup + k) * len(calls) + c),
+    issued back to back on the current stream between one pair of HIP
+    events.  Returns ms per step.  An untimed settle phase (settle()) and
+    `warmup` untimed steps come first."""
+    import torch
+
+    settle(calls)
+    n = len(calls)
+    for k in range(warmup):
+        for c, (_, fn) in enumerate(calls):
+            fn(k * n + c)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for k in range(steps):
+        for c, (_, fn) in enumerate(calls):
+            fn((warmup + k) * n + c)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
 def time_steps_events(calls, steps, warmup):
     """The timed region of the headline: `steps` steps, each running every
     call once (call c of step k gets index (warmup + k) * len(calls) + c),
@@ -260,6 +285,41 @@ def rotate(t, nbytes_each):
     return [t] + [t.clone() for _ in range(n - 1)]
 
 
+_WS = {}
+
+
+def ws_for(key, nbytes_fn):
+    """The workspace of one call site (key), allocated on its first call --
+    in the untimed settle phase that starts every timed region -- at the
+    size the library asks for, then reused: the timed launches carry no
+    allocator work, as in a serving loop or a captured graph."""
+    import torch
+
+    w = _WS.get(key)
+    if w is None:
+        w = _WS[key] = torch.empty(max(16, int(nbytes_fn())), dtype=torch.uint8, device="cuda")
+    return w
+
+
+def ws_gemm(desc, M):
+    from sparse_gemm_amd import patch
+
+    return ws_for(("gemm", id(desc), M), lambda: patch.load().patch_gemm_workspace_bytes(ctypes.byref(desc), M))
+
+
+def ws_dense(M, N, K):
+    from sparse_gemm_amd import patch
+
+    return ws_for(("dense", M, N, K), lambda: patch.load().patch_dense_gemm_workspace_bytes(M, N, K))
+
+
+def ws_swiglu(desc, M):
+    from sparse_gemm_amd import patch
+
+    return ws_for(("swiglu", id(desc), M),
+                  lambda: patch.load().patch_gemm_swiglu_workspace_bytes(ctypes.byref(desc), M))
+
+
 def pack_timed(W, tile_map, mask):
     import torch
 
@@ -305,17 +365,18 @@ def gemm_set(cfg_name, mi, si, Ms, steps, warmup, with_hipblaslt=True, fraction=
     # f(i): launch i on weight copy i mod the copies
     def hyb(M):
         def f(i):
-            patch.gemm(Xs[M], patch.PackedWeight(blobs[i % len(blobs)], desc), out=Ys[M])
+            patch.gemm(Xs[M], patch.PackedWeight(blobs[i % len(blobs)], desc), out=Ys[M], workspace=ws_gemm(desc, M))
         return f
 
     def hyb0(M):
         def f(i):
-            patch.gemm(Xs[M], patch.PackedWeight(blobs0[i % len(blobs0)], p0.desc), out=Ys[M])
+            patch.gemm(Xs[M], patch.PackedWeight(blobs0[i % len(blobs0)], p0.desc), out=Ys[M],
+                       workspace=ws_gemm(p0.desc, M))
         return f
 
     def dense(M):
         def f(i):
-            patch.dense_gemm(Xs[M], Ws[i % len(Ws)], out=Ys[M])
+            patch.dense_gemm(Xs[M], Ws[i % len(Ws)], out=Ys[M], workspace=ws_dense(M, p.N, p.K))
         return f
 
     def blas(M):
@@ -595,29 +656,35 @@ def headline_prefill(args):
 
     def hyb(m):
         return lambda i: patch.gemm(m["X"], patch.PackedWeight(m["blobs"][i % len(m["blobs"])], m["pw"].desc),
-                                    out=m["Y"])
+                                    out=m["Y"], workspace=ws_gemm(m["pw"].desc, M))
 
     def hyb0(m):
         return lambda i: patch.gemm(m["X"], patch.PackedWeight(m["blobs0"][i % len(m["blobs0"])], m["desc0"]),
-                                    out=m["Y"])
+                                    out=m["Y"], workspace=ws_gemm(m["desc0"], M))
 
     def dense(m):
-        return lambda i: patch.dense_gemm(m["X"], m["Ws"][i % len(m["Ws"])], out=m["Y"])
+        return lambda i: patch.dense_gemm(m["X"], m["Ws"][i % len(m["Ws"])], out=m["Y"],
+                                          workspace=ws_dense(M, m["p"].N, m["p"].K))
 
     def blas(m):
         return lambda i: torch.matmul(m["X"], m["Ws"][i % len(m["Ws"])].t(), out=m["Y"])
 
     steps, warmup = args.steps, args.warmup
-    ms_step, per = time_steps_events([(m["name"], hyb(m)) for m in mats], steps, warmup)
+    ms_step = time_steps([(m["name"], hyb(m)) for m in mats], steps, warmup)
+    # the per-launch breakdown: the same steps with an event before every launch
+    ms_step_ev, per = time_steps_events([(m["name"], hyb(m)) for m in mats], steps, warmup)
     ms_step_graph = None
     if not HYBRID_ONLY:
         ms_step_graph, _ = time_graphs([(m["name"], hyb(m)) for m in mats], steps, warmup)
     refs = not HYBRID_ONLY
-    ms_dense = per_dense = ms_s0 = per_s0 = ms_blas = per_blas = per_hb = per_bb = None
+    ms_dense = per_dense = ms_s0 = per_s0 = ms_blas = ms_blas_ev = per_blas = per_hb = per_bb = None
     if refs:
-        ms_dense, per_dense = time_steps_events([(m["name"], dense(m)) for m in mats], steps, warmup)
-        ms_s0, per_s0 = time_steps_events([(m["name"], hyb0(m)) for m in mats], steps, warmup)
-        ms_blas, per_blas = time_steps_events([(m["name"], blas(m)) for m in mats], steps, warmup)
+        ms_dense = time_steps([(m["name"], dense(m)) for m in mats], steps, warmup)
+        ms_s0 = time_steps([(m["name"], hyb0(m)) for m in mats], steps, warmup)
+        ms_blas = time_steps([(m["name"], blas(m)) for m in mats], steps, warmup)
+        _, per_dense = time_steps_events([(m["name"], dense(m)) for m in mats], steps, warmup)
+        _, per_s0 = time_steps_events([(m["name"], hyb0(m)) for m in mats], steps, warmup)
+        ms_blas_ev, per_blas = time_steps_events([(m["name"], blas(m)) for m in mats], steps, warmup)
         # like for like against the library: batches of back-to-back launches
         # between one event pair, no event between launches (an event between
         # two torch.matmul launches costs them more than it costs ours)
@@ -653,12 +720,13 @@ def headline_prefill(args):
             speedup_vs_hipblaslt_events=ref_speedup(per_blas, m["name"], t),
             pack_us=m["pack_ms"] * 1e3, pack_gbps=(3 * p.N * p.K + m["pw"].nbytes) / (m["pack_ms"] * 1e-3) / 1e9,
             weight_copies_rotated=len(m["blobs"]))
-        eff_sum += eff_flops(M, T, ns) * len(per[m["name"]])
-        t_sum += sum(per[m["name"]]) * 1e-3
-        tm_sum += tm * len(per[m["name"]])
-        n_launch += len(per[m["name"]])
-    avg_t = t_sum / n_launch
-    achieved = eff_sum / t_sum / 1e12
+        eff_sum += eff_flops(M, T, ns)
+        tm_sum += tm
+        n_launch += 1
+    # the roofline's launch time: the headline's step time (one event pair
+    # over the K steps) over the step's launches
+    avg_t = ms_step * 1e-3 / n_launch
+    achieved = eff_sum / (ms_step * 1e-3) / 1e12
     traffic = traffic_for("prefill", M)
     line = {
         "metric": "hybrid GEMM TFLOP/s (dense-equiv) + speedup vs dense, LLaMA-2-7B shapes",
@@ -681,22 +749,25 @@ def headline_prefill(args):
             "weight_copies_rotated": [len(m["blobs"]) for m in mats],
         },
         "timing": "an untimed settle phase (the step repeated for settle_ms: the GPU's power management takes "
-                  "20-40 ms of sustained load to settle), W untimed warm-up steps, then one event before every "
-                  "launch and one after the last, on the launch stream; the K steps issued back to back (each "
-                  "launch on its own weight copy, >= 1 GiB rotated per matrix); ms_per_step = first to last "
-                  "event / K; per-launch times = event to next event",
+                  "20-40 ms of sustained load to settle), W untimed warm-up steps, then the K steps issued back "
+                  "to back between one pair of events on the launch stream (each launch on its own weight copy, "
+                  ">= 1 GiB rotated per matrix; each call's workspace allocated once before the timed region); "
+                  "ms_per_step = the event pair's time / K; roofline.avg_launch_us = ms_per_step / the step's "
+                  "launches; per_matrix.us: a second run of the same steps with an event before every launch "
+                  "(event to next event; each event adds a gap of a few us, ms_per_step_events)",
         "settle_ms": SETTLE_MS,
         "dense_reference": "speedup_vs_dense: the same-shape dense GEMM = the same weights packed with every tile "
                            "dense, run by the same kernels (the sparsity gain alone); speedup_vs_rowmajor_dense: "
                            "patch_dense_gemm on row-major W; speedup_vs_hipblaslt: torch.matmul (hipBLASLt) against "
                            "the hybrid GEMM, both as 3 batches of K back-to-back launches between one event pair "
-                           "(median; _events: with the headline's per-launch events)",
+                           "(median; _events: the steps with an event before every launch)",
         "ms_per_step_graph": ms_step_graph,
+        "ms_per_step_events": ms_step_ev,
         "speedup_vs_dense_step": ms_s0 / ms_step if refs else None,
         "speedup_vs_rowmajor_dense_step": ms_dense / ms_step if refs else None,
         "speedup_vs_hipblaslt_step": (sum(median(per_bb[m["name"]]) for m in mats) /
                                       sum(median(per_hb[m["name"]]) for m in mats)) if refs else None,
-        "speedup_vs_hipblaslt_step_events": ms_blas / ms_step if refs else None,
+        "speedup_vs_hipblaslt_step_events": ms_blas_ev / ms_step_ev if refs else None,
         "per_matrix": per_matrix,
         "roofline": {
             "kernel": "prefill hybrid GEMM (packed W), both matrices' launches",
@@ -707,9 +778,11 @@ def headline_prefill(args):
             "frac": achieved / MFMA_PEAK_BF16_TFLOPS,
             "traffic": traffic,
             "flops_per_launch_effective": eff_sum / n_launch,
+            "launches_per_step": n_launch,
             "avg_launch_us": avg_t * 1e6,
             "roofline_us_per_launch": tm_sum / n_launch * 1e6,
-            "note": "achieved = effective flops (32768 a token a dense tile, 16384 a 2:4 tile) / launch time; "
+            "note": "achieved = effective flops (32768 a token a dense tile, 16384 a 2:4 tile) of a step / "
+                    "ms_per_step; "
                     "effective work at the blended matrix-core peak (dense tiles at 2516.6, 2:4 tiles at twice "
                     "that, dense-equivalent) runs at exactly 2516.6 TFLOP/s, so frac = roofline time / time",
         },
@@ -770,7 +843,8 @@ def sweep_compact(steps, warmup, Ms=(1, 2048)):
         Ws = rotate(W, W.numel() * 2)
         Xs = {M: dev_bits(inputs.make_x(cfg, M, p.K, matrix_index=mi), torch.bfloat16) for M in Ms}
         Y = {M: torch.empty((M, p.N), dtype=torch.bfloat16, device="cuda") for M in Ms}
-        _, per_d = time_graphs([(M, (lambda i, M=M: patch.dense_gemm(Xs[M], Ws[i % len(Ws)], out=Y[M])))
+        _, per_d = time_graphs([(M, (lambda i, M=M: patch.dense_gemm(Xs[M], Ws[i % len(Ws)], out=Y[M],
+                                                                     workspace=ws_dense(M, p.N, p.K))))
                                 for M in Ms], steps, warmup, 3)
         del Ws
         rec = {M: dict(matrix=cfg.matrices[mi].name, N=p.N, K=p.K, M=M, s=[], us=[],
@@ -780,7 +854,8 @@ def sweep_compact(steps, warmup, Ms=(1, 2048)):
             pw = patch.pack(W, q.tile_map, mk)
             blobs = rotate(pw.blob, pw.nbytes)
             _, per = time_graphs([(M, (lambda i, M=M: patch.gemm(Xs[M], patch.PackedWeight(blobs[i % len(blobs)],
-                                                                                            pw.desc), out=Y[M])))
+                                                                                            pw.desc), out=Y[M],
+                                                                 workspace=ws_gemm(pw.desc, M))))
                                   for M in Ms], steps, warmup, 3)
             ns, T = int(q.tile_map.sum()), int(q.tile_map.size)
             for M in Ms:
@@ -979,9 +1054,11 @@ def n48_set(steps, warmup, batches, Ms=(1, 16, 128, 2048)):
         for M in Ms:
             X = dev_bits(inputs.make_x(inputs.CONFIGS["sweep"], M, K), torch.bfloat16)
             Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-            calls = [(tag, (lambda k, b=b, d=d: patch.gemm(X, patch.PackedWeight(b[k % len(b)], d), out=Y)))
+            calls = [(tag, (lambda k, b=b, d=d, M=M: patch.gemm(X, patch.PackedWeight(b[k % len(b)], d), out=Y,
+                                                                workspace=ws_gemm(d, M))))
                      for tag, (b, d) in packs.items()]
-            calls.append(("dense", lambda k: patch.dense_gemm(X, Ws[k % len(Ws)], out=Y)))
+            calls.append(("dense", lambda k, M=M: patch.dense_gemm(X, Ws[k % len(Ws)], out=Y,
+                                                                   workspace=ws_dense(M, N, K))))
             _, per = time_graphs(calls, steps, warmup, batches)
             us = {t: median(v) * 1e3 for t, v in per.items()}
             out.append(dict(config="n48", matrix=name, N=N, K=K, M=M, us_48=us["48"], us_24=us["24"],
@@ -1031,7 +1108,8 @@ def q64_set(steps, warmup, batches=3):
             blobs = rotate(pw.blob, pw.nbytes)
 
             def mk_fn(M, blobs=blobs, desc=pw.desc):
-                return lambda i: patch.gemm(Xs[M], patch.PackedWeight(blobs[i % len(blobs)], desc), out=Ys[M])
+                return lambda i: patch.gemm(Xs[M], patch.PackedWeight(blobs[i % len(blobs)], desc), out=Ys[M],
+                                            workspace=ws_gemm(desc, M))
 
             _, per = time_graphs([(M, mk_fn(M)) for M in Ms], steps, warmup, batches)
             rec["us"][k] = {str(M): median(per[M]) * 1e3 for M in Ms}
@@ -1124,11 +1202,12 @@ def fused_set(kind, si, Ms, steps, warmup, batches):
 
         if kind == "swiglu":
             def f_fused(k):
-                patch.gemm_swiglu(X, patch.PackedWeight(blobs[k % len(blobs)], fused.desc), out=Y)
+                patch.gemm_swiglu(X, patch.PackedWeight(blobs[k % len(blobs)], fused.desc), out=Y,
+                                  workspace=ws_swiglu(fused.desc, M))
 
             def f_unfused(k):
                 for sb, sp, y in zip(sblobs, singles, Ys):
-                    patch.gemm(X, patch.PackedWeight(sb[k % len(sb)], sp.desc), out=y)
+                    patch.gemm(X, patch.PackedWeight(sb[k % len(sb)], sp.desc), out=y, workspace=ws_gemm(sp.desc, M))
                 torch.mul(torch.nn.functional.silu(Ys[0]), Ys[1], out=Y)
 
             def f_dense(k):
@@ -1140,14 +1219,15 @@ def fused_set(kind, si, Ms, steps, warmup, batches):
                 torch.mul(torch.nn.functional.silu(Ys[0]), Ys[1], out=Y)
         else:
             def f_fused(k):
-                patch.gemm(X, patch.PackedWeight(blobs[k % len(blobs)], fused.desc), out=Y)
+                patch.gemm(X, patch.PackedWeight(blobs[k % len(blobs)], fused.desc), out=Y,
+                           workspace=ws_gemm(fused.desc, M))
 
             def f_unfused(k):
                 for sb, sp, y in zip(sblobs, singles, Ys):
-                    patch.gemm(X, patch.PackedWeight(sb[k % len(sb)], sp.desc), out=y)
+                    patch.gemm(X, patch.PackedWeight(sb[k % len(sb)], sp.desc), out=y, workspace=ws_gemm(sp.desc, M))
 
             def f_dense(k):
-                patch.dense_gemm(X, Wrot[k % len(Wrot)], out=Y)
+                patch.dense_gemm(X, Wrot[k % len(Wrot)], out=Y, workspace=ws_dense(M, Ntot, K))
 
             def f_blas(k):
                 Wr = Wrot[k % len(Wrot)]

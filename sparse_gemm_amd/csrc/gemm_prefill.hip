@@ -487,7 +487,18 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
 
   // block tk, K range ks; tb: the tail block (tail split), else -1
   int ks, tk, tb = -1;
-  if (!FUSE && P.tail_s > 1) {
+  if (!FUSE && P.tail_s > 1 && P.n_full == 0) {
+    // no whole blocks: range-major, as the K split (an XCD streams one K
+    // range of its blocks), the waiting range 0 last -- on the XCDs after
+    // the writers', so the waiting workgroups never hold the CUs that the
+    // ranges they wait for need
+    const int t = (blockIdx.x & 7) * P.per_xcd + (blockIdx.x >> 3);
+    if (t >= P.tail_s * P.n_tail) return;  // whole workgroup
+    const int r = t / P.n_tail;
+    tb = t - r * P.n_tail;
+    ks = P.tail_s - 1 - r;
+    tk = tb;
+  } else if (!FUSE && P.tail_s > 1) {
     // an XCD runs its share of the whole blocks first, then its tail blocks,
     // each block's ranges back to back with range 0 -- the one that waits --
     // last, so it is dispatched after the ranges it waits for
@@ -1287,8 +1298,12 @@ static hipError_t launch_prefill_bm(const void* src, const void* src2, const voi
       const int nf = a.n_tail * (sh.tail_s - 1);
       a.flags = reinterpret_cast<uint64_t*>(part + (int64_t)nf * 256 * BM);
       a.token = tail_token();
-      hipLaunchKernelGGL((k_prefill_lds<BF16, SRC_ROWMAJOR, OUT_F32, false, BM, Q64>),
-                         dim3((unsigned)(8 * (sh.n_full / 8 + a.tail_per * sh.tail_s))), dim3(kPfWaves * 64), 0, s, a);
+      // no whole blocks: range-major over per_xcd workgroups an XCD
+      a.per_xcd = (sh.tail_s * a.n_tail + 7) / 8;
+      const unsigned grid =
+          (unsigned)(sh.n_full > 0 ? 8 * (sh.n_full / 8 + a.tail_per * sh.tail_s) : 8 * a.per_xcd);
+      hipLaunchKernelGGL((k_prefill_lds<BF16, SRC_ROWMAJOR, OUT_F32, false, BM, Q64>), dim3(grid),
+                         dim3(kPfWaves * 64), 0, s, a);
       return hipGetLastError();
     }
   }
