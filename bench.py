@@ -304,7 +304,10 @@ def ws_for(key, nbytes_fn):
 def ws_gemm(desc, M):
     from sparse_gemm_amd import patch
 
-    return ws_for(("gemm", id(desc), M), lambda: patch.load().patch_gemm_workspace_bytes(ctypes.byref(desc), M))
+    # keyed by what the size depends on (not by the descriptor object, whose
+    # id a later one may reuse)
+    return ws_for(("gemm", desc.version, desc.N, desc.K, M),
+                  lambda: patch.load().patch_gemm_workspace_bytes(ctypes.byref(desc), M))
 
 
 def ws_dense(M, N, K):
@@ -316,7 +319,7 @@ def ws_dense(M, N, K):
 def ws_swiglu(desc, M):
     from sparse_gemm_amd import patch
 
-    return ws_for(("swiglu", id(desc), M),
+    return ws_for(("swiglu", desc.version, desc.N, desc.K, M),
                   lambda: patch.load().patch_gemm_swiglu_workspace_bytes(ctypes.byref(desc), M))
 
 
