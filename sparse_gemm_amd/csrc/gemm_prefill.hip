@@ -450,6 +450,12 @@ constexpr int lds_stages(int bm) { return bm <= 128 ? 3 : 2; }
 // the 16 KB of entries of 64 x 64 tiles), so W copies run two steps ahead
 // there while X copies run one
 constexpr int lds_w_stages(int bm, bool q64) { return bm <= 128 || (bm == 192 && !q64) ? 3 : 2; }
+// Polls of a tail range's flag (each a round trip to the L2 plus 256
+// cycles of sleep) before range 0 gives up on it: a second or more, far
+// beyond any range's run time.
+constexpr int kTailSpinLimit = 1 << 20;
+// Cache-policy operand of the buffer loads and stores: sc1, agent scope.
+constexpr int kCoherent = 16;
 
 // Q64: a blob of 64 x 64 execution tiles (format 4).  Its table has one
 // entry per 64-row half of a row-block and 128-column tile column, whose
@@ -459,13 +465,6 @@ constexpr int lds_w_stages(int bm, bool q64) { return bm <= 128 || (bm == 192 &&
 // (r, wn, wm) works on half wn of row-block r, so it reads that half's
 // entries and, per step (one slice), that slice's kind: the waves of one
 // workgroup may run different kinds in the same step.
-// Polls of a tail range's flag (each a round trip to the L2 plus 256
-// cycles of sleep) before range 0 gives up on it: a second or more, far
-// beyond any range's run time.
-constexpr int kTailSpinLimit = 1 << 20;
-// Cache-policy operand of the buffer loads and stores: sc1, agent scope.
-constexpr int kCoherent = 16;
-
 template <bool BF16, bool SRC_ROWMAJOR, bool OUT_F32, bool FUSE, int BM, bool Q64 = false>
 __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   static_assert(!Q64 || (!SRC_ROWMAJOR && !FUSE), "64 x 64 execution tiles: packed W, not fused");
@@ -1009,7 +1008,6 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
   }
 }
 
-
 // Launch shape: the M-block width BM and the number of K ranges, chosen
 // by a cost model of the LDS-staged kernel fitted to its measured times on
 // the LLaMA-2 7B q_proj, gate_proj and down_proj shapes (32 <= M <= 2048,
@@ -1054,8 +1052,8 @@ static double shape_cost_us(int64_t M, int64_t N, int64_t K, int bm, int64_t spl
 // rounded down to a multiple of 8 blocks a round), the blocks left over (too
 // few to fill a round, or all of them when there are too few for one) each
 // cut into S K ranges so that they fill one short round; a range hands its
-// fp32 sums to the block's range 0 (the cost: the flags cleared, the slots
-// written, range 0 reading them).  Returns -1 where it does not apply (no
+// fp32 sums to the block's range 0 (the cost: the slots written and range 0
+// reading them).  Returns -1 where it does not apply (no
 // left-over blocks, too many to cut in two, or short ranges without a
 // whole round).
 static double tail_cost_us(int64_t M, int64_t N, int64_t K, int bm, int cus, int* n_full, int* tail_s,
