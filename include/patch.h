@@ -391,10 +391,11 @@ patch_status patch_apply_fine_mask(patch_dtype dtype, int64_t N, int64_t K, int6
 /*
  * patch_gemm without a workspace argument, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,
- * harnesses that forbid allocation).  The prefill kernel's K split -- the
- * only scratch the GEMM path uses: fp32 partial sums of the K ranges,
- * written in full before they are read, nothing to clear -- goes to a
- * device array of patch_noalloc_scratch_bytes() bytes (64 MiB) that the
+ * harnesses that forbid allocation).  The prefill kernel's K split and tail
+ * split -- the only scratch the GEMM path uses: fp32 partial sums of the K
+ * ranges, written before they are read, and the tail split's flags, which
+ * each launch leaves at 0; nothing to clear -- go to a device array of
+ * patch_noalloc_scratch_bytes() bytes (64 MiB) that the
  * library holds on every device it runs on until the process ends.
  * Arguments and results as patch_gemm, same kernels and launch shapes.
  * Errors: as patch_gemm; PATCH_ERR_BUFFER_TOO_SMALL if this shape's launch
@@ -407,6 +408,19 @@ patch_status patch_apply_fine_mask(patch_dtype dtype, int64_t N, int64_t K, int6
 uint64_t patch_noalloc_scratch_bytes(void);
 patch_status patch_gemm_noalloc(const patch_packed_desc* desc, const void* packed_dev, const void* X_dev, int64_t M,
                                 void* Y_dev, patch_dtype y_dtype, void* stream);
+
+/*
+ * For tests of the prefill kernel's bounded wait.  In the tail split (the
+ * output blocks left over after whole rounds of the GPU, cut into K ranges
+ * that hand their fp32 sums to the block's first range through the
+ * workspace) the first range polls a flag per range a bounded number of
+ * times.  polls > 0: in the launches that follow, the first range waits for
+ * a flag value that no range stores and gives up after that many polls,
+ * marking its block's outputs NaN -- the path a range that never arrives
+ * would take, forced from the host so a test can see the launch end;
+ * polls <= 0: back to normal (the default).  Process-wide, for tests only.
+ */
+void patch_debug_tail_wait(int32_t polls);
 
 /*
  * Measurement probes.  They compute nothing of the method; they measure, on

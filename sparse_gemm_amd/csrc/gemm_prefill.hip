@@ -953,8 +953,8 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_prefill_lds(PfArgs P) {
       for (int q = 1; q < P.tail_s; q++) {
         uint64_t* f = P.flags + slot0 + q - 1;
         int spins = 0;
-        while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != P.token) {
-          if (++spins > kTailSpinLimit) {
+        while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != P.wait_token) {
+          if (++spins > P.wait_polls) {
             late = 1;
             break;
           }
@@ -1086,6 +1086,13 @@ static double tail_cost_us(int64_t M, int64_t N, int64_t K, int bm, int cus, int
   return t;
 }
 
+// Tests of the tail split's bounded wait (tail_wait_test): above 0, range 0
+// of the launches that follow waits for a value no range stores, this many
+// polls, and marks its block's outputs NaN.
+static std::atomic<int> g_tail_test_polls{0};
+
+void tail_wait_test(int polls) { g_tail_test_polls.store(polls > 0 ? polls : 0, std::memory_order_relaxed); }
+
 // This launch's tail-split token: a counter mixed with a random salt
 // drawn once per process (splitmix64's finaliser), never 0.  Stale or
 // uninitialised flag words would have to equal a fresh 64-bit value to pass
@@ -1100,7 +1107,7 @@ static uint64_t tail_token() {
   z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
   z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
   z ^= z >> 31;
-  return z ? z : 1;
+  return z == 0 || z == ~0ull ? 1 : z;  // neither 0 (a cleared flag) nor ~0 (~token: the tests' value)
 }
 
 // Workspace bytes of a tail split: a slot of 256 x bm fp32 sums for every
@@ -1247,7 +1254,8 @@ static PfArgs prefill_args(const void* src, const void* src2, const void* X, int
   a.n_full = a.n_tail = a.tail_s = a.tail_per = 0;
   a.part = nullptr;
   a.flags = nullptr;
-  a.token = 0;
+  a.token = a.wait_token = 0;
+  a.wait_polls = 0;
   return a;
 }
 
@@ -1284,7 +1292,8 @@ static hipError_t launch_prefill_bm(const void* src, const void* src2, const voi
   a.n_full = a.n_tail = a.tail_s = a.tail_per = 0;
   a.part = nullptr;
   a.flags = nullptr;
-  a.token = 0;
+  a.token = a.wait_token = 0;
+  a.wait_polls = 0;
   if constexpr (LDS && !FUSE) {
     if (sh.tail_s > 1) {
       // tail split: the slots, then the flags, in the workspace
@@ -1296,6 +1305,11 @@ static hipError_t launch_prefill_bm(const void* src, const void* src2, const voi
       const int nf = a.n_tail * (sh.tail_s - 1);
       a.flags = reinterpret_cast<uint64_t*>(part + (int64_t)nf * 256 * BM);
       a.token = tail_token();
+      // a test of the bounded wait makes range 0 wait for a value no range
+      // stores, with a short limit (tail_wait_test)
+      const int test_polls = g_tail_test_polls.load(std::memory_order_relaxed);
+      a.wait_token = test_polls > 0 ? ~a.token : a.token;
+      a.wait_polls = test_polls > 0 ? test_polls : kTailSpinLimit;
       // no whole blocks: range-major over per_xcd workgroups an XCD
       a.per_xcd = (sh.tail_s * a.n_tail + 7) / 8;
       const unsigned grid =

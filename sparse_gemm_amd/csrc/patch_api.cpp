@@ -23,6 +23,7 @@ hipError_t launch_prefill(bool bf16, bool rowmajor, bool out_f32, const void* sr
                           bool force_lds, int force_big, bool q64, hipStream_t s);
 uint64_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K, bool rowmajor);
 double prefill_estimate_us(int64_t M, int64_t N, int64_t K, bool rowmajor, uint64_t ws_bytes);
+void tail_wait_test(int polls);
 double decode_estimate_us(int64_t M, int64_t N, int64_t K, double w_bytes);
 hipError_t launch_sample_mask(int64_t N, int64_t K, const float* tile_logits, const float* tile_u,
                               const float* pat_logits, const float* pat_u, float tau, uint8_t* tile_map,
@@ -255,6 +256,8 @@ patch_status patch_probe_stream_read(const void* src_dev, uint64_t bytes, void* 
   if (e != hipSuccess) return hip_fail(e, "launch stream-read probe");
   return PATCH_OK;
 }
+
+void patch_debug_tail_wait(int32_t polls) { patch::tail_wait_test((int)polls); }
 
 patch_status patch_probe_copy_rate(const void* src_dev, uint64_t src_bytes, uint64_t window_bytes, int32_t iters,
                                    int32_t workgroups, void* sink_dev, uint64_t sink_bytes, void* stream) {

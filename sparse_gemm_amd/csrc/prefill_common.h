@@ -56,6 +56,10 @@ struct PfArgs {
   float* part;
   uint64_t* flags;
   uint64_t token;
+  // what range 0 waits for (token, except in tests of the bounded wait) and
+  // how many polls it makes before it gives up
+  uint64_t wait_token;
+  int wait_polls;
 };
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }

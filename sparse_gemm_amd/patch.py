@@ -52,6 +52,7 @@ EXPORTS = ("patch_abi_version", "patch_packed_bytes", "patch_pack", "patch_packe
            "patch_gemm_swiglu_workspace_bytes", "patch_gemm_swiglu", "patch_dense_gemm_swiglu_workspace_bytes",
            "patch_dense_gemm_swiglu", "patch_packed_bytes_concat", "patch_pack_concat", "patch_sample_mask",
            "patch_exec_tile_map", "patch_apply_fine_mask", "patch_probe_stream_read", "patch_probe_matrix_rate", "patch_probe_copy_rate", "patch_probe_copy_bytes",
+           "patch_debug_tail_wait",
            "patch_probe_matrix_flops", "patch_noalloc_scratch_bytes", "patch_gemm_noalloc", "patch_status_string",
            "patch_last_error")
 
@@ -124,6 +125,8 @@ def load():
     lib.patch_probe_copy_rate.restype = ctypes.c_int
     lib.patch_probe_copy_bytes.argtypes = [I32, I32]
     lib.patch_probe_copy_bytes.restype = U64
+    lib.patch_debug_tail_wait.argtypes = [I32]
+    lib.patch_debug_tail_wait.restype = None
     lib.patch_noalloc_scratch_bytes.argtypes = []
     lib.patch_noalloc_scratch_bytes.restype = U64
     lib.patch_gemm_noalloc.argtypes = [DP, P, P, I64, P, ctypes.c_int, P]
@@ -604,6 +607,14 @@ def probe_matrix_rate(kind: int, iters: int, workgroups: int, sink: torch.Tensor
     lib = load()
     _check(lib.patch_probe_matrix_rate(kind, iters, workgroups, _ptr(sink), _stream(sink.device.index)))
     return int(lib.patch_probe_matrix_flops(kind, iters, workgroups))
+
+
+def debug_tail_wait(polls: int) -> None:
+    """For tests of the tail split's bounded wait (patch_debug_tail_wait):
+    polls > 0 makes the first K range of every left-over block wait for a
+    flag value no range stores, give up after that many polls and mark its
+    block's outputs NaN; polls <= 0 restores normal launches."""
+    (_lib or load()).patch_debug_tail_wait(int(polls))
 
 
 def probe_copy_rate(src: torch.Tensor, window_bytes: int, iters: int, workgroups: int, sink: torch.Tensor) -> int:

@@ -349,6 +349,47 @@ def test_prefill_tail_split(variant, N, K, M):
                  what="64x64 tiles " + tag)
 
 
+def test_tail_split_bounded_wait():
+    """The tail split's bounded wait, forced from the host: with
+    patch_debug_tail_wait(64) the first K range of every left-over block
+    waits for a flag value no range stores, gives up after 64 polls and
+    marks its block's outputs NaN.  The launch ends; the NaN outputs are
+    exactly the left-over blocks (whole 256-column M-blocks x 128-row
+    row-blocks, two row-blocks a block: 2 x 92 of them here); every other
+    output matches the oracle; and the next launch, back to normal on the
+    same workspace, is correct everywhere."""
+    variant, N, K, M = TAIL_CASES[3]  # 348 blocks: a round of 256, 92 left over in two ranges
+    p = inputs.make_custom("bf16", N, K, 76, "bernoulli", 0.5, "uniform")
+    pw, _ = _pack(p)
+    Xb = inputs.make_custom_x("bf16", M, K, 77)
+    X = dev_bits(Xb, "bf16")
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    rows = np.unique(np.concatenate([_sampled_rows(M, n=40, seed=7), np.arange(0, M, 256)]))
+    ref = _ref(p, Xb, rows)
+    try:
+        patch.debug_tail_wait(64)
+        y = patch.gemm(X, pw, out_dtype=torch.float32, variant=variant, workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        patch.debug_tail_wait(0)
+    nan = torch.isnan(y).cpu().numpy()
+    n_mb, nt = (M + 255) // 256, N // 128
+    cells = np.zeros((n_mb, nt))
+    for mb in range(n_mb):
+        for i in range(nt):
+            cells[mb, i] = nan[mb * 256:(mb + 1) * 256, i * 128:(i + 1) * 128].mean()
+    assert set(np.unique(cells)) <= {0.0, 1.0}, "NaN outputs must form whole blocks"
+    assert int(cells.sum()) == 2 * 92, int(cells.sum())
+    got = host_f64(y[torch.from_numpy(rows).cuda()])
+    fin = ~np.isnan(got)
+    assert fin.any()
+    scale = float(np.abs(ref).max())
+    assert float(np.abs(got[fin] - ref[fin]).max()) <= 1e-2 * scale
+    y2 = patch.gemm(X, pw, out_dtype=torch.float32, variant=variant, workspace=ws)
+    assert not bool(torch.isnan(y2).any())
+    assert_close(y2[torch.from_numpy(rows).cuda()], ref, f32=True, what="after the forced wait")
+
+
 def test_tail_split_graph_replays():
     """Tail-split launches captured in a HIP graph (the graph holds one token
     per launch, so every replay relies on the previous one having set its
