@@ -342,8 +342,11 @@ def _check_out_dtype(od: torch.dtype, xd: torch.dtype):
 
 def _workspace(nbytes: int, workspace, device):
     """workspace="auto": a fresh buffer of the size the library asks for
-    (from torch's caching allocator); None: no workspace; a tensor: used as
-    given."""
+    (from torch's caching allocator) on every call; None: no workspace; a
+    tensor: used as given.  Callers that run the same shapes repeatedly keep
+    one buffer per call site (sized by patch_gemm_workspace_bytes) and pass
+    it: with the per-call allocation a step of two tail-split GEMMs measured
+    up to 3% slower."""
     if isinstance(workspace, str):
         if workspace != "auto":
             raise ValueError(f"workspace must be 'auto', None or a tensor, not {workspace!r}")
